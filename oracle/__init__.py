@@ -1,0 +1,12 @@
+"""fp64 CPU oracle for the Falcon forward pass (test infrastructure only).
+
+Only the tests, the smoke check and the CPU-baseline leg of the benchmark
+import this package; the HIP library never does.
+"""
+from .falcon_oracle import (F1, F2, F3, F1A, F3A, VARIANTS, WINDOW_VARIANTS,
+                            PHI_RMSNORM, PHI_IDENTITY, OracleState, OracleTrace,
+                            falcon_forward, phi, window_lambda_max)
+
+__all__ = ["F1", "F2", "F3", "F1A", "F3A", "VARIANTS", "WINDOW_VARIANTS",
+           "PHI_RMSNORM", "PHI_IDENTITY", "OracleState", "OracleTrace",
+           "falcon_forward", "phi", "window_lambda_max"]

@@ -1,0 +1,466 @@
+"""Pins for the fp64 oracle: every check here compares the oracle with
+something other than itself — hand-worked values, closed forms, textbook
+special cases, library routines, or an independently written masked /
+renormalised / chunked form (tests/pin_forms.py).  CPU only."""
+from __future__ import annotations
+
+import json
+import math
+import pathlib
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import OracleState, falcon_forward
+from linear_recurrent_weight_amd.inputs import round_to_bf16
+import pin_forms as pf
+
+GOLDEN = pathlib.Path(__file__).parent / "golden"
+
+
+def _num(s):
+    s = str(s)
+    if "sqrt" in s:
+        return float(eval(s, {"__builtins__": {}}, {"sqrt": math.sqrt}))
+    return float(Fraction(s))
+
+
+def _arr(x):
+    return np.array(x, dtype=np.float64)
+
+
+def _head(a, T, d):
+    return np.asarray(a, np.float64).reshape(1, 1, T, d)
+
+
+def _rand(rng, B, H, T, dk, dv, variant="F1", beta=(0.1, 0.9), lam=(0.0, 0.3)):
+    q = rng.standard_normal((B, H, T, dk))
+    k = rng.standard_normal((B, H, T, dk))
+    v = rng.standard_normal((B, H, T, dv))
+    bshape = (B, H, T, dv) if variant == "F2" else (B, H, T)
+    b = rng.uniform(*beta, bshape)
+    lm = rng.uniform(*lam, (B, H, T))
+    return q, k, v, b, lm
+
+
+# --------------------------------------------------------------------------
+# hand-worked examples (tests/golden)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["f1_scalar_by_hand", "f1a_scalar_by_hand"])
+def test_golden_scalar(name):
+    g = json.loads((GOLDEN / f"{name}.json").read_text())
+    T = len(g["q"])
+    o, st = falcon_forward(g["variant"], _head(g["q"], T, 1), _head(g["k"], T, 1),
+                           _head(g["v"], T, 1), _arr(g["beta"]).reshape(1, 1, T),
+                           _arr(g["lam"]).reshape(1, 1, T), eps=g["eps"],
+                           eps_gamma=g["eps_gamma"], phi_kind=oracle.PHI_IDENTITY)
+    exp_o = [_num(s) for s in g["expected_o"]]
+    np.testing.assert_allclose(o.ravel(), exp_o, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(st.S.ravel(), [_num(g["expected_S"])], atol=1e-14)
+    np.testing.assert_allclose(st.x_next.ravel(), [_num(g["expected_x_next"])], atol=0)
+
+
+def test_golden_f1_2x2_transpose_sensitive():
+    g = json.loads((GOLDEN / "f1_2x2_by_hand.json").read_text())
+    T = len(g["q"])
+    o, st = falcon_forward("F1", _head(g["q"], T, 2), _head(g["k"], T, 2), _head(g["v"], T, 2),
+                           _arr(g["beta"]).reshape(1, 1, T), _arr(g["lam"]).reshape(1, 1, T),
+                           eps=g["eps"], eps_gamma=g["eps_gamma"], phi_kind=oracle.PHI_IDENTITY)
+    exp_o = np.array([[_num(s) for s in row] for row in g["expected_o"]])
+    exp_S = np.array([[_num(s) for s in row] for row in g["expected_S"]])
+    np.testing.assert_allclose(o[0, 0], exp_o, atol=1e-14)
+    np.testing.assert_allclose(st.S[0], exp_S, atol=1e-14)
+    np.testing.assert_allclose(st.x_next[0], [_num(s) for s in g["expected_x_next"]])
+
+
+@pytest.mark.parametrize("variant", ["F3", "F3A"])
+def test_golden_window2(variant):
+    g = json.loads((GOLDEN / "f3_f3a_window2_by_hand.json").read_text())
+    T = len(g["q"])
+    o, st = falcon_forward(variant, _head(g["q"], T, 2), _head(g["k"], T, 2), _head(g["v"], T, 1),
+                           _arr(g["beta"]).reshape(1, 1, T), _arr(g["lam"]).reshape(1, 1, T),
+                           window=g["window"], eps=g["eps"], eps_gamma=g["eps_gamma"],
+                           phi_kind=oracle.PHI_IDENTITY)
+    e = g["expected"][variant]
+    np.testing.assert_allclose(o.ravel(), [_num(s) for s in e["o"]], atol=1e-13)
+    np.testing.assert_allclose(st.S[0].ravel(), [_num(r[0]) for r in e["S"]], atol=1e-13)
+    np.testing.assert_allclose(st.tail_x[0], _arr(g["expected_tail_x"]))
+    np.testing.assert_allclose(st.tail_y[0], _arr(g["expected_tail_y"]))
+
+
+# --------------------------------------------------------------------------
+# closed forms and textbook special cases
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("variant", ["F1", "F2"])
+@pytest.mark.parametrize("phi_kind", [oracle.PHI_RMSNORM, oracle.PHI_IDENTITY])
+def test_projection_reads_back_current_value(variant, phi_kind):
+    """beta = 1, lambda = eps = 0: the step is the orthogonal projection
+    eta = 1/||x||^2 (summary §2.3), so S_t^T x_t = y_t.  Reading with
+    q_t := k_{t-1} (so phi(q_t) = x_t) must return v_t exactly for t >= 2:
+    this pins the one-step key shift, the residual sign, read-after-write and
+    the orientation of S."""
+    rng = np.random.default_rng(7)
+    T, dk, dv = 9, 5, 3
+    k = rng.standard_normal((1, 2, T, dk))
+    q = np.zeros_like(k)
+    q[:, :, 1:] = k[:, :, :-1]
+    v = rng.standard_normal((1, 2, T, dv))
+    beta = np.ones((1, 2, T, dv)) if variant == "F2" else np.ones((1, 2, T))
+    lam = np.zeros((1, 2, T))
+    o, _ = falcon_forward(variant, q, k, v, beta, lam, eps=0.0, phi_kind=phi_kind)
+    np.testing.assert_allclose(o[:, :, 1:], v[:, :, 1:], rtol=1e-12, atol=1e-12)
+
+
+def test_classical_nlms_columns():
+    """lambda = eps = 0 reduces Falcon-1 to classical NLMS (summary §3.1;
+    blog): every value column j is an adaptive linear filter w_j updated by
+    w_j <- w_j + beta e_j x / ||x||^2 with e_j = y_j - w_j . x, and no update
+    when x = 0.  Written here as the textbook filter loop on the features."""
+    rng = np.random.default_rng(11)
+    T, dk, dv = 12, 4, 3
+    q, k, v, beta, _ = _rand(rng, 1, 1, T, dk, dv, beta=(0.2, 1.8))
+    lam = np.zeros((1, 1, T))
+    o, st = falcon_forward("F1", q, k, v, beta, lam, eps=0.0)
+    kh = pf.rms_feature(k[0, 0], 1e-6)
+    qh = pf.rms_feature(q[0, 0], 1e-6)
+    w = np.zeros((dv, dk))
+    outs = []
+    for t in range(T):
+        x = kh[t - 1] if t > 0 else np.zeros(dk)
+        nx = x @ x
+        for j in range(dv):
+            if nx > 0:
+                e = v[0, 0, t, j] - w[j] @ x
+                w[j] = w[j] + beta[0, 0, t] * e * x / nx
+        outs.append(w @ qh[t])
+    np.testing.assert_allclose(o[0, 0], np.array(outs), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(st.S[0], w.T, rtol=1e-11, atol=1e-12)
+
+
+def test_transition_spectrum():
+    """eps = 0, y = 0: one step maps S to (gamma I - eta x x^T) S, whose
+    eigenvalue along x is 1 - beta and on x-perp is gamma (summary §C.6)."""
+    rng = np.random.default_rng(3)
+    dk, dv = 6, 4
+    x = rng.standard_normal(dk)
+    z = rng.standard_normal(dk)
+    z -= (z @ x) / (x @ x) * x            # z orthogonal to x
+    e = rng.standard_normal(dv)
+    beta, lam = 0.7, 0.4
+    for vec, factor in [(x, None), (z, None)]:
+        S0 = np.outer(vec, e)[None]
+        st_in = OracleState(S=S0, fresh=False, x_next=x[None], tail_x=np.zeros((1, 0, dk)),
+                            tail_y=np.zeros((1, 0, dv)))
+        q = rng.standard_normal((1, 1, 1, dk))
+        k = rng.standard_normal((1, 1, 1, dk))
+        v = np.zeros((1, 1, 1, dv))
+        _, st = falcon_forward("F1", q, k, v, np.full((1, 1, 1), beta), np.full((1, 1, 1), lam),
+                               eps=0.0, eps_gamma=1e-3, state_in=st_in, phi_kind=oracle.PHI_IDENTITY)
+        eta = beta / (x @ x + lam)
+        gamma = 1 - eta * lam
+        want = (1 - beta) if vec is x else gamma
+        np.testing.assert_allclose(st.S[0], want * S0[0], rtol=1e-12, atol=1e-13)
+
+
+def test_f1a_no_ridge_is_shifted_linear_attention():
+    """lambda = 0: Falcon-1A is additive, o_t = sum_{j<=t} eta_j (qh_t.x_j) v_j
+    with x_j = phi(k_{j-1}) (summary §4.3, §4.5): a causal masked product."""
+    rng = np.random.default_rng(5)
+    T, dk, dv = 10, 4, 3
+    q, k, v, beta, _ = _rand(rng, 1, 1, T, dk, dv)
+    lam = np.zeros((1, 1, T))
+    o, _ = falcon_forward("F1A", q, k, v, beta, lam, eps=1e-6)
+    qh = pf.rms_feature(q[0, 0], 1e-6)
+    kh = pf.rms_feature(k[0, 0], 1e-6)
+    X = np.vstack([np.zeros(dk), kh[:-1]])
+    eta = beta[0, 0] / ((X * X).sum(1) + 1e-6)
+    eta[0] = 0.0
+    want = np.tril(qh @ X.T) @ (eta[:, None] * v[0, 0])
+    np.testing.assert_allclose(o[0, 0], want, rtol=1e-12, atol=1e-12)
+
+
+def test_clamp_keeps_eta_and_floors_gamma():
+    """alpha = min(eta lambda, 1 - eps_gamma) (summary §4.6; blog): eta lambda
+    < beta, so with beta in (1, 2) and a huge ridge the clamp binds; the carry
+    then sits exactly at eps_gamma and eta keeps its unclamped value."""
+    rng = np.random.default_rng(9)
+    T, dk, dv = 6, 3, 2
+    q, k, v, beta, _ = _rand(rng, 1, 1, T, dk, dv, beta=(1.5, 1.9))
+    lam = np.full((1, 1, T), 50.0)
+    _, _, tr = falcon_forward("F1", q, k, v, beta, lam, eps_gamma=0.01, trace=True)
+    x = tr.x[0]
+    eta = beta[0, 0] / ((x * x).sum(1) + 50.0 + 1e-6)
+    np.testing.assert_allclose(tr.eta[0, 1:], eta[1:], rtol=1e-14)
+    assert np.all(eta[1:] * 50.0 > 0.99)
+    np.testing.assert_allclose(tr.gamma[0, 1:], 0.01, rtol=1e-12)
+    assert tr.gamma[0, 0] == 1.0 and tr.eta[0, 0] == 0.0
+
+
+def test_zero_denominator_gives_zero_step():
+    """x = 0, lambda = eps = 0: the denominator vanishes and eta := 0
+    (summary Appendix) — no NaN, state unchanged."""
+    T, dk, dv = 4, 3, 2
+    k = np.zeros((1, 1, T, dk))
+    q = np.ones((1, 1, T, dk))
+    v = np.ones((1, 1, T, dv))
+    o, st, tr = falcon_forward("F1", q, k, v, np.full((1, 1, T), 0.5), np.zeros((1, 1, T)),
+                               eps=0.0, trace=True)
+    assert np.all(tr.eta == 0) and np.all(np.isfinite(o)) and np.all(st.S == 0)
+
+
+# --------------------------------------------------------------------------
+# descent and invariants
+# --------------------------------------------------------------------------
+
+def _loss(variant, S, xw, yw, lam):
+    if variant in ("F1", "F3"):
+        r = yw - xw @ S
+        return 0.5 * np.mean(np.sum(r * r, -1)) + 0.5 * lam * np.sum(S * S)
+    return -np.mean(np.sum(yw * (xw @ S), -1)) + 0.5 * lam * np.sum(S * S)
+
+
+@pytest.mark.parametrize("variant,window", [("F1", 1), ("F3", 3), ("F1A", 1), ("F3A", 3)])
+def test_per_step_descent(variant, window):
+    """Unclamped, beta in (0, 2): one step does not increase the instantaneous
+    regularised objective it descends (summary §3.2, §4.5)."""
+    rng = np.random.default_rng(21)
+    T, dk, dv = 8, 4, 3
+    q, k, v, beta, lam = _rand(rng, 1, 1, T, dk, dv, beta=(0.2, 1.9), lam=(0.05, 0.5))
+    _, _, tr = falcon_forward(variant, q, k, v, beta, lam, window=window, eps=0.0,
+                              eps_gamma=1e-6, trace=True)
+    prev = np.zeros((dk, dv))
+    for t in range(1, T + 1):
+        _, st = falcon_forward(variant, q[:, :, :t], k[:, :, :t], v[:, :, :t], beta[:, :, :t],
+                               lam[:, :, :t], window=window, eps=0.0, eps_gamma=1e-6)
+        if t >= 2:
+            lo = max(0, t - window)
+            xw = tr.x[0, lo:t]
+            yw = v[0, 0, lo:t]
+            l0 = _loss(variant, prev, xw, yw, lam[0, 0, t - 1])
+            l1 = _loss(variant, st.S[0], xw, yw, lam[0, 0, t - 1])
+            assert l1 <= l0 + 1e-12, (t, l0, l1)
+        prev = st.S[0]
+
+
+def test_linearity_in_v():
+    rng = np.random.default_rng(2)
+    for variant in ["F1", "F2", "F3", "F1A", "F3A"]:
+        q, k, v, beta, lam = _rand(rng, 1, 2, 7, 3, 4, variant)
+        w = 3 if variant in ("F3", "F3A") else 1
+        o1, s1 = falcon_forward(variant, q, k, v, beta, lam, window=w)
+        o2, s2 = falcon_forward(variant, q, k, -2.5 * v, beta, lam, window=w)
+        np.testing.assert_allclose(o2, -2.5 * o1, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(s2.S, -2.5 * s1.S, rtol=1e-12, atol=1e-13)
+
+
+def test_columns_and_heads_independent():
+    rng = np.random.default_rng(4)
+    for variant in ["F1", "F2", "F3", "F1A", "F3A"]:
+        q, k, v, beta, lam = _rand(rng, 2, 2, 6, 3, 6, variant)
+        w = 2 if variant in ("F3", "F3A") else 1
+        o, st = falcon_forward(variant, q, k, v, beta, lam, window=w)
+        for sl in (slice(0, 2), slice(2, 6)):
+            b = beta[..., sl] if variant == "F2" else beta
+            oh, sh = falcon_forward(variant, q, k, v[..., sl], b, lam, window=w)
+            np.testing.assert_allclose(oh, o[..., sl], rtol=1e-13, atol=1e-14)
+        o1, _ = falcon_forward(variant, q[1:, :1], k[1:, :1], v[1:, :1], beta[1:, :1], lam[1:, :1], window=w)
+        np.testing.assert_allclose(o1, o[1:, :1], rtol=1e-13, atol=1e-14)
+
+
+def test_rmsnorm_scale_invariance():
+    rng = np.random.default_rng(6)
+    q, k, v, beta, lam = _rand(rng, 1, 1, 9, 8, 4)
+    o1, _ = falcon_forward("F1", q, k, v, beta, lam, eps_rms=1e-12)
+    o2, _ = falcon_forward("F1", 7.0 * q, 0.3 * k, v, beta, lam, eps_rms=1e-12)
+    np.testing.assert_allclose(o2, o1, rtol=1e-9, atol=1e-10)
+
+
+# --------------------------------------------------------------------------
+# cross-variant reductions
+# --------------------------------------------------------------------------
+
+def test_f2_equal_gains_is_f1():
+    rng = np.random.default_rng(8)
+    q, k, v, beta, lam = _rand(rng, 2, 1, 11, 4, 5)
+    o1, s1 = falcon_forward("F1", q, k, v, beta, lam)
+    b2 = np.repeat(beta[..., None], 5, -1)
+    o2, s2 = falcon_forward("F2", q, k, v, b2, lam)
+    np.testing.assert_allclose(o2, o1, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(s2.S, s1.S, rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("pair", [("F3", "F1"), ("F3A", "F1A")])
+def test_window_one_reduces(pair):
+    """W = 1: lambda_max of x x^T is ||x||^2, so F3 -> F1 and F3A -> F1A
+    (summary §4.5; explainer; blog)."""
+    rng = np.random.default_rng(12)
+    q, k, v, beta, lam = _rand(rng, 2, 2, 10, 5, 3)
+    o3, s3 = falcon_forward(pair[0], q, k, v, beta, lam, window=1)
+    o1, s1 = falcon_forward(pair[1], q, k, v, beta, lam)
+    np.testing.assert_allclose(o3, o1, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(s3.S, s1.S, rtol=1e-12, atol=1e-13)
+
+
+def test_window_lambda_max_three_ways():
+    """Exact Gram eigenvalue (oracle) = top eigenvalue of the d x d covariance
+    = converged power iteration = the 2-vector closed form."""
+    rng = np.random.default_rng(13)
+    xw = rng.standard_normal((5, 4, 7))
+    lm = oracle.window_lambda_max(xw)
+    for n in range(5):
+        assert abs(lm[n] - pf.cov_top_eig(xw[n])) < 1e-12 * lm[n]
+        c = xw[n].T @ xw[n] / 4
+        u = np.ones(7)
+        for _ in range(2000):
+            u = c @ u
+            u /= np.linalg.norm(u)
+        assert abs(u @ c @ u - lm[n]) < 1e-9 * lm[n]
+    a, b = xw[0, 0], xw[0, 1]
+    na, nb, ab = a @ a, b @ b, a @ b
+    closed = (na + nb + math.sqrt((na - nb) ** 2 + 4 * ab * ab)) / 4
+    assert abs(oracle.window_lambda_max(xw[:1, :2])[0] - closed) < 1e-12 * closed
+
+
+# --------------------------------------------------------------------------
+# equivalent forms (independent code in pin_forms.py)
+# --------------------------------------------------------------------------
+
+VARIANT_CASES = [("F1", 1), ("F2", 1), ("F1A", 1), ("F3A", 3), ("F3", 3), ("F3A", 1), ("F3", 2)]
+
+
+@pytest.mark.parametrize("variant,window", VARIANT_CASES)
+def test_masked_form_equals_recurrence(variant, window):
+    rng = np.random.default_rng(100 + window)
+    T, dk, dv = 11, 4, 3
+    q, k, v, beta, lam = _rand(rng, 1, 1, T, dk, dv, variant)
+    o, st = falcon_forward(variant, q, k, v, beta, lam, window=window)
+    seg = pf.Segment(q[0, 0], k[0, 0], v[0, 0], beta[0, 0], lam[0, 0])
+    om, sm = pf.masked_segment(pf.NAMES[variant], seg, window)
+    np.testing.assert_allclose(om, o[0, 0], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(sm, st.S[0], rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("variant,window", VARIANT_CASES)
+@pytest.mark.parametrize("C", [1, 2, 4, 5, 13])
+def test_chunk_form_equals_recurrence(variant, window, C):
+    """Chunk-local restart of the log-prefix is exact (summary §D.1)."""
+    rng = np.random.default_rng(200 + C)
+    T, dk, dv = 13, 4, 3
+    q, k, v, beta, lam = _rand(rng, 1, 1, T, dk, dv, variant, lam=(0.0, 2.0))
+    o, st = falcon_forward(variant, q, k, v, beta, lam, window=window, eps_gamma=0.05)
+    oc, sc = pf.chunked(pf.NAMES[variant], q[0, 0], k[0, 0], v[0, 0], beta[0, 0], lam[0, 0], C,
+                        window=window, eps_gamma=0.05)
+    np.testing.assert_allclose(oc, o[0, 0], rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(sc, st.S[0], rtol=1e-10, atol=1e-11)
+
+
+def test_renormalized_form_equals_recurrence():
+    """Dividing state, step and target by the running decay removes the ridge
+    (summary §C.6, §E, §G.1) and gives the same outputs, clamp included."""
+    rng = np.random.default_rng(17)
+    T, dk, dv = 12, 4, 3
+    q, k, v, beta, lam = _rand(rng, 1, 1, T, dk, dv, lam=(0.0, 20.0))
+    o, st = falcon_forward("F1", q, k, v, beta, lam, eps_gamma=0.2)
+    seg = pf.Segment(q[0, 0], k[0, 0], v[0, 0], beta[0, 0], lam[0, 0])
+    orr, srr = pf.renormalized_f1(seg, eps_gamma=0.2)
+    np.testing.assert_allclose(orr, o[0, 0], rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(srr, st.S[0], rtol=1e-10, atol=1e-11)
+
+
+# --------------------------------------------------------------------------
+# continuation
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("variant,window", [("F1", 1), ("F2", 1), ("F3", 4), ("F1A", 1), ("F3A", 4)])
+def test_continuation_is_exact(variant, window):
+    """Splitting anywhere and carrying (S, x_next, last W-1 pairs) gives the
+    single-run outputs and state (summary §C.7, §4.4; blog)."""
+    rng = np.random.default_rng(31)
+    T = 14
+    q, k, v, beta, lam = _rand(rng, 2, 1, T, 3, 4, variant)
+    o, st = falcon_forward(variant, q, k, v, beta, lam, window=window)
+    for p in (0, 1, 2, 5, 13, 14):
+        oa, sa = falcon_forward(variant, q[:, :, :p], k[:, :, :p], v[:, :, :p], beta[:, :, :p],
+                                lam[:, :, :p], window=window)
+        ob, sb = falcon_forward(variant, q[:, :, p:], k[:, :, p:], v[:, :, p:], beta[:, :, p:],
+                                lam[:, :, p:], window=window, state_in=sa)
+        np.testing.assert_allclose(np.concatenate([oa, ob], 2), o, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(sb.S, st.S, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(sb.tail_x, st.tail_x)
+
+
+@pytest.mark.parametrize("drop", ["x_next", "tail"])
+def test_continuation_needs_its_state(drop):
+    """Negative check: passing only S (no x_next, or no tail) changes the
+    result (summary §C.7)."""
+    rng = np.random.default_rng(32)
+    q, k, v, beta, lam = _rand(rng, 1, 1, 12, 3, 4)
+    o, _ = falcon_forward("F3A", q, k, v, beta, lam, window=4)
+    oa, sa = falcon_forward("F3A", q[:, :, :6], k[:, :, :6], v[:, :, :6], beta[:, :, :6],
+                            lam[:, :, :6], window=4)
+    if drop == "x_next":
+        sa = OracleState(S=sa.S, fresh=True, x_next=None, tail_x=sa.tail_x[:, :0], tail_y=sa.tail_y[:, :0])
+    else:
+        sa = OracleState(S=sa.S, fresh=False, x_next=sa.x_next, tail_x=sa.tail_x[:, :0],
+                         tail_y=sa.tail_y[:, :0])
+    ob, _ = falcon_forward("F3A", q[:, :, 6:], k[:, :, 6:], v[:, :, 6:], beta[:, :, 6:],
+                           lam[:, :, 6:], window=4, state_in=sa)
+    assert np.max(np.abs(ob - o[:, :, 6:])) > 1e-3
+
+
+# --------------------------------------------------------------------------
+# exact arithmetic on tiny inputs
+# --------------------------------------------------------------------------
+
+def test_exact_rational_recurrence():
+    """Identity feature map and rational inputs: the recurrence needs no
+    transcendental function (gamma = 1 - alpha), so it runs exactly in
+    Fractions; the fp64 oracle must agree to rounding."""
+    rng = np.random.default_rng(41)
+    T, dk, dv = 7, 3, 2
+
+    def rat(shape, lo, hi, den):
+        return rng.integers(lo, hi, shape) / den
+
+    q = rat((T, dk), -4, 5, 2)
+    k = rat((T, dk), -4, 5, 2)
+    v = rat((T, dv), -6, 7, 3)
+    beta = rat((T,), 1, 8, 4)
+    lam = rat((T,), 0, 5, 8)
+    eps = Fraction(1, 64)
+    F = lambda a: [[Fraction(x).limit_denominator(1000) for x in row] for row in a]
+    Fq, Fk, Fv = F(q), F(k), F(v)
+    Fb = [Fraction(x).limit_denominator(1000) for x in beta]
+    Fl = [Fraction(x).limit_denominator(1000) for x in lam]
+    S = [[Fraction(0)] * dv for _ in range(dk)]
+    outs = []
+    for t in range(T):
+        x = [Fraction(0)] * dk if t == 0 else Fk[t - 1]
+        if t > 0:
+            den = sum(xi * xi for xi in x) + Fl[t] + eps
+            eta = Fb[t] / den
+            alpha = min(eta * Fl[t], 1 - Fraction(1, 1000))
+            gamma = 1 - alpha
+            pred = [sum(S[i][j] * x[i] for i in range(dk)) for j in range(dv)]
+            S = [[gamma * S[i][j] + eta * x[i] * (Fv[t][j] - pred[j]) for j in range(dv)]
+                 for i in range(dk)]
+        outs.append([sum(S[i][j] * Fq[t][i] for i in range(dk)) for j in range(dv)])
+    o, st = falcon_forward("F1", q.reshape(1, 1, T, dk), k.reshape(1, 1, T, dk),
+                           v.reshape(1, 1, T, dv), beta.reshape(1, 1, T), lam.reshape(1, 1, T),
+                           eps=float(eps), eps_gamma=1e-3, phi_kind=oracle.PHI_IDENTITY)
+    np.testing.assert_allclose(o[0, 0], np.array(outs, dtype=float), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(st.S[0], np.array(S, dtype=float), rtol=1e-13, atol=1e-14)
+
+
+def test_bf16_rounding_helper():
+    """Input recipe: RNE rounding to bfloat16 (checked against torch)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal(4096).astype(np.float32) * 10
+    ours = round_to_bf16(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(ours, ref)
