@@ -1,0 +1,171 @@
+/*
+ * falcon.h — C ABI of the MI355X (gfx950) Falcon fast-weight forward pass.
+ *
+ * The operation is the forward pass of "Fast Weight Attention for Continual
+ * Learning" (arXiv 2608.27763v1).  Per (batch, head) a fast-weight state S
+ * with d_k rows and d_v columns is written once per token with the
+ * prefix-aligned pair x_t = phi(k_{t-1}), y_t = v_t, and read after the write
+ * with o_t = S_t^T phi(q_t):
+ *   - the pair, the sentinel x_1 = 0 and the strict no-op first step:
+ *     paperlayer.ai summary, §3 "Autoregressive Next-Latent Prediction",
+ *     Appendix, §4.6 and §H.3 "Identification of Drivers";
+ *   - the step eta_t = beta_t / (mu_t + lambda_t + eps) (0 if the
+ *     denominator is 0), the carry gamma_t = 1 - min(eta_t lambda_t,
+ *     1 - eps_gamma): summary §3.1, §C.3, §4.6; agihunt.info explainer
+ *     "Method"; sungsoo.github.io post (clamp and log1p paragraph);
+ *   - the writes of Falcon-1 (scalar NLMS), Falcon-2 (per value column),
+ *     Falcon-3 (window mini-batch, mu_t = lambda_max of the window
+ *     covariance), Falcon-1A / Falcon-3A (inner-product writes):
+ *     summary §1, §4, §4.3-§4.5, App. F; explainer "Method";
+ *   - the feature map phi = QK-RMSNorm (default) or the identity:
+ *     summary §5 and §H.3 "The Falcon-3 Recurrence";
+ *   - the recurrent and chunk-parallel forms and the chunk-local log-decay:
+ *     summary Figure 2, Figure 4, §D.1 "Chunk-Local Evaluation", §G.1;
+ *   - the boundary state for exact continuation (S, the next pair's
+ *     feature, the last W-1 pairs): summary §C.7, §4.4; sungsoo.github.io.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers inside the structs are DEVICE pointers owned by
+ *     the caller; the library keeps none of them after a call returns.
+ *     The structs themselves (falcon_fwd_args, falcon_state) live in host
+ *     memory and are read during the call only.
+ *   - Layouts are contiguous row-major with batch, then head, then token,
+ *     then feature: q, k [B,H,T,d_k]; v, o [B,H,T,d_v]; beta [B,H,T]
+ *     ([B,H,T,d_v] for Falcon-2); lambda [B,H,T]; S [B,H,d_k,d_v].
+ *   - Errors are returned as negative status codes (falcon_status_str gives
+ *     the text).  On any error except FALCON_ERR_HIP nothing is launched.
+ *   - falcon_fwd enqueues work on the given stream and returns without
+ *     synchronising, allocating or freeing memory.  It is reentrant.
+ *   - Data preconditions that are documented, not checked on the device:
+ *     beta >= 0 and lambda >= 0 (the pages require non-negative steps and
+ *     ridge; the NLMS gain is meant to lie in (0, 2)), finite inputs.
+ *   - The same inputs give bitwise-identical outputs (no atomics).
+ */
+#ifndef FALCON_H
+#define FALCON_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FALCON_ABI_VERSION 1
+#define FALCON_MAX_WINDOW 8
+
+/* status codes */
+#define FALCON_OK 0
+#define FALCON_ERR_INVALID_ARG (-1) /* a malformed argument                        */
+#define FALCON_ERR_UNSUPPORTED (-2) /* well formed but not implemented (sizes...)  */
+#define FALCON_ERR_WORKSPACE (-3)   /* workspace missing or smaller than required  */
+#define FALCON_ERR_HIP (-4)         /* a kernel launch failed (hipGetLastError)    */
+
+/* variants: 1/2/3 = scalar, per-column, sliding-window regression;
+ * 11/13 = scalar and sliding-window inner-product writes (2A = 12 is not
+ * provided) */
+#define FALCON_V1 1
+#define FALCON_V2 2
+#define FALCON_V3 3
+#define FALCON_V1A 11
+#define FALCON_V3A 13
+
+/* storage type of q, k, v and o */
+#define FALCON_BF16 0
+#define FALCON_F32 1
+
+/* feature map phi applied to q and k */
+#define FALCON_PHI_RMSNORM 0  /* z / sqrt(mean(z^2) + eps_rms); 0 if that is 0/0 */
+#define FALCON_PHI_IDENTITY 1 /* the "unkernelized" case                        */
+
+/*
+ * Boundary state of a segment (summary §C.7, §4.4).
+ *   S       [B,H,d_k,d_v] fp32, device.
+ *   x_next  [B,H,d_k] fp32, device: phi(k_T) of the previous segment, the
+ *           write feature of this segment's first pair.  Ignored when fresh.
+ *   tail_x  [B,H,W-1,d_k] fp32, device; tail_y [B,H,W-1,d_v] fp32, device:
+ *           the last pairs, right-aligned and oldest first: slot s holds the
+ *           pair that lies W-1-s pairs before this segment's first pair.
+ *           Only the last n_tail slots are meaningful.  Unused when W == 1.
+ *   n_tail  host int, 0..W-1 (input); written by the library on output as
+ *           min(W-1, n_tail_in + T).  Output slots before the valid ones are
+ *           zero-filled.
+ *   fresh   host int.  Input: nonzero means a new sequence (x_1 = 0 and the
+ *           first step is a strict no-op); then x_next is ignored and n_tail
+ *           must be 0.  Output: set to 1 only when T == 0 and the input was
+ *           fresh, else 0.
+ */
+typedef struct falcon_state {
+    float *S;
+    float *x_next;
+    float *tail_x;
+    float *tail_y;
+    int n_tail;
+    int fresh;
+} falcon_state;
+
+/*
+ * Arguments of one forward call.
+ *   abi_version  must equal FALCON_ABI_VERSION.
+ *   variant      FALCON_V1, _V2, _V3, _V1A or _V3A.
+ *   dtype        FALCON_BF16 or FALCON_F32 (q, k, v, o).  State, beta and
+ *                lambda are always fp32; all arithmetic accumulates in fp32.
+ *   phi          FALCON_PHI_RMSNORM or FALCON_PHI_IDENTITY.
+ *   batch, heads >= 1; seqlen >= 0; dk, dv in {16, 32, 64, 128}.
+ *   chunk        0 = token-recurrent form (every variant);
+ *                64 = chunk-parallel form.  A combination that has no
+ *                chunk-parallel kernel returns FALCON_ERR_UNSUPPORTED.
+ *   window       W >= 1; must be 1 for V1, V2, V1A; at most FALCON_MAX_WINDOW.
+ *   eps >= 0, eps_rms >= 0, 0 < eps_gamma < 1 (defaults 1e-6, 1e-6, 1e-3).
+ *   q, k, v      device inputs, 16-byte aligned.
+ *   beta, lambda device fp32 inputs, 16-byte aligned.
+ *   state_in     NULL: S_0 = 0 and a fresh sequence.
+ *   state_out    NULL: the final state is not written.  Must not overlap
+ *                state_in.
+ *   o            device output [B,H,T,d_v] in dtype.
+ *   workspace    device scratch of at least falcon_fwd_workspace_size(args)
+ *                bytes, 256-byte aligned; may be NULL when that size is 0.
+ */
+typedef struct falcon_fwd_args {
+    int abi_version;
+    int variant;
+    int dtype;
+    int phi;
+    int batch, heads, seqlen, dk, dv;
+    int chunk;
+    int window;
+    float eps, eps_gamma, eps_rms;
+    const void *q, *k, *v;
+    const float *beta, *lambda;
+    const falcon_state *state_in;
+    falcon_state *state_out;
+    void *o;
+    void *workspace;
+    size_t workspace_bytes;
+} falcon_fwd_args;
+
+/* Bytes of device workspace falcon_fwd needs for these arguments (pointer
+ * fields are not read).  Pure host code, no HIP call.  Returns 0 for a
+ * malformed or unsupported argument set (falcon_fwd_validate says which). */
+size_t falcon_fwd_workspace_size(const falcon_fwd_args *args);
+
+/* Checks every argument rule above without touching the GPU.  Returns
+ * FALCON_OK or a negative status.  Pure host code, no HIP call. */
+int falcon_fwd_validate(const falcon_fwd_args *args);
+
+/* Forward pass: validates, then enqueues the kernels on `stream` (a
+ * hipStream_t; NULL = the default stream).  Returns FALCON_OK or a negative
+ * status.  Writes o and, if requested, the device parts of state_out; the
+ * host fields state_out->n_tail and ->fresh are written before returning. */
+int falcon_fwd(const falcon_fwd_args *args, void *stream);
+
+/* Static text for a status code. */
+const char *falcon_status_str(int status);
+
+/* FALCON_ABI_VERSION of the built library. */
+int falcon_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FALCON_H */

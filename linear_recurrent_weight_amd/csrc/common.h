@@ -1,0 +1,75 @@
+// Device helpers shared by the Falcon HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/falcon.h"
+
+namespace falcon {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 is carried as its 16-bit pattern.
+struct bf16_t { uint16_t bits; };
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// round to nearest even; inputs are finite
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return uint16_t(u >> 16);
+}
+
+template <class E> struct elem;
+template <> struct elem<float> {
+    __device__ static float load(const float *p, size_t i) { return p[i]; }
+    __device__ static void store(float *p, size_t i, float v) { p[i] = v; }
+};
+template <> struct elem<bf16_t> {
+    __device__ static float load(const bf16_t *p, size_t i) { return bf16_to_f32(p[i].bits); }
+    __device__ static void store(bf16_t *p, size_t i, float v) { p[i].bits = f32_to_bf16(v); }
+};
+
+template <class E> __device__ __forceinline__ float ld(const E *p, size_t i) { return elem<E>::load(p, i); }
+template <class E> __device__ __forceinline__ void st(E *p, size_t i, float v) { elem<E>::store(p, i, v); }
+
+// Sum over the lanes of a group of `width` consecutive lanes (width a power
+// of two <= 64); every lane of the group receives the total.
+template <int width>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int off = width / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_inclusive_scan(float v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        float u = __shfl_up(v, off, 64);
+        if (lane >= off) v += u;
+    }
+    return v;
+}
+
+// Feature map phi (reading: z / sqrt(mean(z^2) + eps_rms), and 0 when that
+// denominator is 0); `ss` is the sum of squares over d elements.
+__device__ __forceinline__ float phi_scale(float ss, int d, float eps_rms, int phi_kind) {
+    if (phi_kind == FALCON_PHI_IDENTITY) return 1.f;
+    float ms = ss / float(d) + eps_rms;
+    return ms > 0.f ? 1.f / sqrtf(ms) : 0.f;
+}
+
+// eta = beta / den (0 if den == 0), alpha = min(eta * lambda, 1 - eps_gamma)
+__device__ __forceinline__ float step_eta(float beta, float den) { return den != 0.f ? beta / den : 0.f; }
+__device__ __forceinline__ float step_alpha(float eta, float lam, float eps_gamma) {
+    return fminf(eta * lam, 1.f - eps_gamma);
+}
+
+}  // namespace falcon

@@ -1,0 +1,113 @@
+// falcon_fwd: validate, plan, and enqueue the kernels of the chosen path.
+#include "chunk_layout.h"
+#include "kernels.h"
+#include "plan.h"
+
+using namespace falcon;
+
+extern "C" int falcon_fwd(const falcon_fwd_args *args, void *stream) {
+    Plan p;
+    const int rc = build_plan(args, &p, true);
+    if (rc != FALCON_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (args->state_out) {
+        args->state_out->n_tail = p.n_tail_out;
+        args->state_out->fresh = (p.T == 0 && p.fresh) ? 1 : 0;
+    }
+
+    if (p.path == Path::kEmpty) {
+        if (p.S_out) {
+            PassArgs pa{};
+            pa.BH = p.BH;
+            pa.dk = p.dk;
+            pa.dv = p.dv;
+            pa.halo = p.window - 1;
+            pa.n_tail = p.n_tail_in;
+            pa.S_in = p.S_in;
+            pa.xnext_in = p.xnext_in;
+            pa.tailx_in = p.tailx_in;
+            pa.taily_in = p.taily_in;
+            pa.S_out = p.S_out;
+            pa.xnext_out = p.xnext_out;
+            pa.tailx_out = p.tailx_out;
+            pa.taily_out = p.taily_out;
+            launch_passthrough(pa, s);
+        }
+    } else {
+        FeatureArgs fa{};
+        fa.variant = p.variant;
+        fa.phi = p.phi;
+        fa.BH = p.BH;
+        fa.T = p.T;
+        fa.Tpad = p.Tpad;
+        fa.dk = p.dk;
+        fa.dv = p.dv;
+        fa.window = p.window;
+        fa.eps = p.eps;
+        fa.eps_gamma = p.eps_gamma;
+        fa.eps_rms = p.eps_rms;
+        fa.fresh = p.fresh ? 1 : 0;
+        fa.n_tail_in = p.n_tail_in;
+        fa.n_tail_out = p.n_tail_out;
+        fa.q = p.q;
+        fa.k = p.k;
+        fa.v = p.v;
+        fa.beta = p.beta;
+        fa.lambda = p.lambda;
+        fa.xnext_in = p.xnext_in;
+        fa.tailx_in = p.tailx_in;
+        fa.taily_in = p.taily_in;
+        fa.xnext_out = p.xnext_out;
+        fa.tailx_out = p.tailx_out;
+        fa.taily_out = p.taily_out;
+        fa.xn = p.ws_at<void>(p.off_xn);
+        fa.qn = p.ws_at<void>(p.off_qn);
+        fa.eta = p.ws_at<float>(p.off_eta);
+        fa.alpha = p.ws_at<float>(p.off_alpha);
+        const bool io_bf16 = p.dtype == FALCON_BF16;
+        launch_features(fa, io_bf16, !p.feat_f32, s);
+
+        if (p.path == Path::kRecurrent) {
+            RecurrentArgs ra{};
+            ra.variant = p.variant;
+            ra.BH = p.BH;
+            ra.T = p.T;
+            ra.dk = p.dk;
+            ra.dv = p.dv;
+            ra.window = p.window;
+            ra.n_tail_in = p.n_tail_in;
+            ra.xn = fa.xn ? static_cast<const float *>(fa.xn) : nullptr;
+            ra.qn = static_cast<const float *>(fa.qn);
+            ra.eta = fa.eta;
+            ra.alpha = fa.alpha;
+            ra.v = p.v;
+            ra.o = p.o;
+            ra.S_in = p.S_in;
+            ra.tailx_in = p.tailx_in;
+            ra.taily_in = p.taily_in;
+            ra.S_out = p.S_out;
+            launch_recurrent(ra, io_bf16, s);
+        } else if (p.path == Path::kChunkF1) {
+            ChunkF1Args ca{};
+            ca.BH = p.BH;
+            ca.T = p.T;
+            ca.Tpad = p.Tpad;
+            ca.nchunks = p.nchunks;
+            ca.dk = p.dk;
+            ca.dv = p.dv;
+            ca.xn = fa.xn;
+            ca.qn = fa.qn;
+            ca.eta = fa.eta;
+            ca.alpha = fa.alpha;
+            ca.v = p.v;
+            ca.o = p.o;
+            ca.S_in = p.S_in;
+            ca.S_out = p.S_out;
+            ca.ops = p.ws_at<void>(p.off_chunk);
+            ca.chunk_bytes = p.chunk_bytes;
+            launch_chunk_f1(ca, io_bf16, s);
+        }
+    }
+    if (hipGetLastError() != hipSuccess) return FALCON_ERR_HIP;
+    return FALCON_OK;
+}

@@ -1,0 +1,56 @@
+// Launch interfaces of the Falcon kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/falcon.h"
+
+namespace falcon {
+
+struct FeatureArgs {
+    int variant, phi, BH, T, Tpad, dk, dv, window;
+    float eps, eps_gamma, eps_rms;
+    int fresh, n_tail_in, n_tail_out;
+    const void *q, *k, *v;
+    const float *beta, *lambda;
+    const float *xnext_in, *tailx_in, *taily_in;
+    float *xnext_out, *tailx_out, *taily_out;
+    void *xn, *qn;          // [BH, Tpad, dk] features (fp32 or bf16)
+    float *eta, *alpha;     // [BH, Tpad] ([BH, Tpad, dv] for Falcon-2)
+};
+
+struct PassArgs {
+    int BH, dk, dv, halo, n_tail;
+    const float *S_in, *xnext_in, *tailx_in, *taily_in;
+    float *S_out, *xnext_out, *tailx_out, *taily_out;
+};
+
+struct RecurrentArgs {
+    int variant, BH, T, dk, dv, window, n_tail_in;
+    const float *xn, *qn;   // fp32 features [BH, T, dk]
+    const float *eta, *alpha;
+    const void *v;          // [BH, T, dv] in the io dtype
+    void *o;
+    const float *S_in;      // nullptr => 0
+    const float *tailx_in, *taily_in;
+    float *S_out;           // nullptr => not written
+};
+
+struct ChunkF1Args {
+    int BH, T, Tpad, nchunks, dk, dv;
+    const void *xn, *qn;    // features [BH, Tpad, dk] (bf16 or fp32)
+    const float *eta, *alpha;
+    const void *v;          // [BH, T, dv]
+    void *o;
+    const float *S_in;
+    float *S_out;
+    void *ops;              // per-chunk operators
+    size_t chunk_bytes;
+};
+
+void launch_features(const FeatureArgs &a, bool in_bf16, bool feat_bf16, hipStream_t s);
+void launch_passthrough(const PassArgs &a, hipStream_t s);
+void launch_recurrent(const RecurrentArgs &a, bool io_bf16, hipStream_t s);
+void launch_chunk_f1(const ChunkF1Args &a, bool bf16, hipStream_t s);
+
+}  // namespace falcon

@@ -1,0 +1,219 @@
+// Argument validation, path selection and workspace carve-up for falcon_fwd.
+// Pure host code: nothing here calls into HIP, so the whole file can be
+// exercised on a machine without a GPU.
+#include "plan.h"
+
+#include <cmath>
+#include <cstring>
+
+#include "chunk_layout.h"
+
+namespace falcon {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool is_head_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    auto x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+bool finite_nonneg(float x) { return std::isfinite(x) && x >= 0.f; }
+
+}  // namespace
+
+int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
+    if (!a || !p) return FALCON_ERR_INVALID_ARG;
+    *p = Plan{};
+    if (a->abi_version != FALCON_ABI_VERSION) return FALCON_ERR_INVALID_ARG;
+    const int var = a->variant;
+    if (var != FALCON_V1 && var != FALCON_V2 && var != FALCON_V3 && var != FALCON_V1A &&
+        var != FALCON_V3A)
+        return FALCON_ERR_INVALID_ARG;
+    if (a->dtype != FALCON_BF16 && a->dtype != FALCON_F32) return FALCON_ERR_INVALID_ARG;
+    if (a->phi != FALCON_PHI_RMSNORM && a->phi != FALCON_PHI_IDENTITY) return FALCON_ERR_INVALID_ARG;
+    if (a->batch < 1 || a->heads < 1 || a->seqlen < 0 || a->dk < 1 || a->dv < 1)
+        return FALCON_ERR_INVALID_ARG;
+    if (a->window < 1 || a->chunk < 0) return FALCON_ERR_INVALID_ARG;
+    const bool windowed = (var == FALCON_V3 || var == FALCON_V3A);
+    if (!windowed && a->window != 1) return FALCON_ERR_INVALID_ARG;
+    if (!finite_nonneg(a->eps) || !finite_nonneg(a->eps_rms)) return FALCON_ERR_INVALID_ARG;
+    if (!(a->eps_gamma > 0.f && a->eps_gamma < 1.f)) return FALCON_ERR_INVALID_ARG;
+    if (!is_head_dim(a->dk) || !is_head_dim(a->dv)) return FALCON_ERR_UNSUPPORTED;
+    if (a->window > FALCON_MAX_WINDOW) return FALCON_ERR_UNSUPPORTED;
+    const long long bh = static_cast<long long>(a->batch) * a->heads;
+    if (bh > (1LL << 30)) return FALCON_ERR_UNSUPPORTED;
+    // per-head element offsets are kept in 32 bits inside the kernels
+    if (static_cast<long long>(a->seqlen + 64) * (a->dk > a->dv ? a->dk : a->dv) >= (1LL << 31))
+        return FALCON_ERR_UNSUPPORTED;
+
+    p->variant = var;
+    p->dtype = a->dtype;
+    p->phi = a->phi;
+    p->B = a->batch;
+    p->H = a->heads;
+    p->T = a->seqlen;
+    p->dk = a->dk;
+    p->dv = a->dv;
+    p->chunk = a->chunk;
+    p->window = a->window;
+    p->BH = static_cast<int>(bh);
+    p->eps = a->eps;
+    p->eps_gamma = a->eps_gamma;
+    p->eps_rms = a->eps_rms;
+
+    // path selection
+    if (a->chunk == 0) {
+        p->path = Path::kRecurrent;
+    } else if (a->chunk == kChunk) {
+        if (var == FALCON_V1 && chunk_f1_supported(a->dk, a->dv))
+            p->path = Path::kChunkF1;
+        else
+            return FALCON_ERR_UNSUPPORTED;
+    } else {
+        return FALCON_ERR_UNSUPPORTED;
+    }
+    if (a->seqlen == 0) p->path = Path::kEmpty;
+
+
+    // boundary state rules (host fields are always readable)
+    const falcon_state *si = a->state_in;
+    p->fresh = true;
+    p->n_tail_in = 0;
+    if (si) {
+        p->fresh = si->fresh != 0;
+        if (si->n_tail < 0 || si->n_tail > a->window - 1) return FALCON_ERR_INVALID_ARG;
+        if (p->fresh && si->n_tail != 0) return FALCON_ERR_INVALID_ARG;
+        p->n_tail_in = si->n_tail;
+    }
+    {
+        long long pairs = static_cast<long long>(p->n_tail_in) + a->seqlen;
+        p->n_tail_out = static_cast<int>(pairs < a->window - 1 ? pairs : a->window - 1);
+    }
+
+    // workspace carve-up: normalised features and step scalars (padded to
+    // whole chunks on the chunk paths), then the per-chunk operators
+    const int T = a->seqlen;
+    size_t off = 0;
+    if (p->path != Path::kEmpty) {
+        const bool chunked = p->path != Path::kRecurrent;
+        p->nchunks = chunked ? (T + kChunk - 1) / kChunk : 0;
+        p->Tpad = chunked ? p->nchunks * kChunk : T;
+        p->feat_f32 = !chunked || a->dtype == FALCON_F32;
+        const size_t rows = static_cast<size_t>(bh) * p->Tpad;
+        const size_t fsz = p->feat_f32 ? 4 : 2;
+        p->off_xn = off; off = align_up(off + rows * a->dk * fsz);
+        p->off_qn = off; off = align_up(off + rows * a->dk * fsz);
+        const size_t ncol = (var == FALCON_V2) ? a->dv : 1;
+        p->off_eta = off; off = align_up(off + rows * ncol * 4);
+        p->off_alpha = off; off = align_up(off + rows * ncol * 4);
+        if (p->path == Path::kChunkF1) {
+            const size_t nch = static_cast<size_t>(bh) * p->nchunks;
+            p->chunk_bytes = chunk_f1_bytes(a->dk, a->dv, a->dtype == FALCON_F32);
+            p->off_chunk = off;
+            off = align_up(off + nch * p->chunk_bytes);
+        }
+    }
+    p->ws_bytes = off;
+
+    if (!check_pointers) return FALCON_OK;
+
+    // pointers
+    const size_t nk = static_cast<size_t>(bh) * T * a->dk;
+    const size_t nv = static_cast<size_t>(bh) * T * a->dv;
+    const size_t esz = a->dtype == FALCON_BF16 ? 2 : 4;
+    if (T > 0) {
+        if (!a->q || !a->k || !a->v || !a->beta || !a->lambda || !a->o) return FALCON_ERR_INVALID_ARG;
+        if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o) ||
+            !aligned16(a->beta) || !aligned16(a->lambda))
+            return FALCON_ERR_INVALID_ARG;
+        // the output may not alias any input
+        const size_t nb = static_cast<size_t>(bh) * T * (var == FALCON_V2 ? a->dv : 1);
+        const size_t ot = nv * esz;
+        if (overlap(a->o, ot, a->q, nk * esz) || overlap(a->o, ot, a->k, nk * esz) ||
+            overlap(a->o, ot, a->v, nv * esz) || overlap(a->o, ot, a->beta, nb * 4) ||
+            overlap(a->o, ot, a->lambda, static_cast<size_t>(bh) * T * 4))
+            return FALCON_ERR_INVALID_ARG;
+    }
+    const size_t nS = static_cast<size_t>(bh) * a->dk * a->dv * 4;
+    const size_t nX = static_cast<size_t>(bh) * a->dk * 4;
+    const size_t nTx = static_cast<size_t>(bh) * (a->window - 1) * a->dk * 4;
+    const size_t nTy = static_cast<size_t>(bh) * (a->window - 1) * a->dv * 4;
+    if (si) {
+        if (!si->S || !aligned16(si->S)) return FALCON_ERR_INVALID_ARG;
+        if (!p->fresh && (!si->x_next || !aligned16(si->x_next))) return FALCON_ERR_INVALID_ARG;
+        if (si->n_tail > 0 && (!si->tail_x || !si->tail_y)) return FALCON_ERR_INVALID_ARG;
+        p->S_in = si->S;
+        p->xnext_in = p->fresh ? nullptr : si->x_next;
+        p->tailx_in = si->n_tail > 0 ? si->tail_x : nullptr;
+        p->taily_in = si->n_tail > 0 ? si->tail_y : nullptr;
+    }
+    falcon_state *so = a->state_out;
+    if (so) {
+        if (!so->S || !so->x_next || !aligned16(so->S) || !aligned16(so->x_next))
+            return FALCON_ERR_INVALID_ARG;
+        if (a->window > 1 && (!so->tail_x || !so->tail_y)) return FALCON_ERR_INVALID_ARG;
+        p->S_out = so->S;
+        p->xnext_out = so->x_next;
+        p->tailx_out = a->window > 1 ? so->tail_x : nullptr;
+        p->taily_out = a->window > 1 ? so->tail_y : nullptr;
+        if (si) {
+            const void *ins[4] = {p->S_in, p->xnext_in, p->tailx_in, p->taily_in};
+            const size_t ni[4] = {nS, nX, nTx, nTy};
+            const void *outs[4] = {p->S_out, p->xnext_out, p->tailx_out, p->taily_out};
+            const size_t no[4] = {nS, nX, nTx, nTy};
+            for (int i = 0; i < 4; ++i)
+                for (int j = 0; j < 4; ++j)
+                    if (overlap(ins[i], ni[i], outs[j], no[j])) return FALCON_ERR_INVALID_ARG;
+        }
+    }
+    if (p->ws_bytes > 0) {
+        if (!a->workspace || a->workspace_bytes < p->ws_bytes) return FALCON_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(a->workspace) % kAlign) return FALCON_ERR_WORKSPACE;
+    }
+    p->q = a->q;
+    p->k = a->k;
+    p->v = a->v;
+    p->beta = a->beta;
+    p->lambda = a->lambda;
+    p->o = a->o;
+    p->ws = a->workspace;
+    return FALCON_OK;
+}
+
+}  // namespace falcon
+
+extern "C" {
+
+size_t falcon_fwd_workspace_size(const falcon_fwd_args *args) {
+    falcon::Plan p;
+    if (falcon::build_plan(args, &p, false) != FALCON_OK) return 0;
+    return p.ws_bytes;
+}
+
+int falcon_fwd_validate(const falcon_fwd_args *args) {
+    falcon::Plan p;
+    return falcon::build_plan(args, &p, true);
+}
+
+const char *falcon_status_str(int status) {
+    switch (status) {
+        case FALCON_OK: return "ok";
+        case FALCON_ERR_INVALID_ARG: return "invalid argument";
+        case FALCON_ERR_UNSUPPORTED: return "unsupported combination of sizes or options";
+        case FALCON_ERR_WORKSPACE: return "workspace missing or too small";
+        case FALCON_ERR_HIP: return "HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int falcon_abi_version(void) { return FALCON_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Internal host-side plan of one falcon_fwd call: validated sizes, the path
+// chosen, and the carve-up of the caller's workspace.  Pure C++ (no HIP
+// types) so that argument checking can be built and tested without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/falcon.h"
+
+namespace falcon {
+
+enum class Path : int {
+    kEmpty = 0,      // seqlen == 0: only the boundary state is passed through
+    kRecurrent = 1,  // token-recurrent form (every variant)
+    kChunkF1 = 2,    // chunk-parallel Falcon-1
+    kChunkA = 3,     // chunk-parallel Falcon-1A / Falcon-3A (scalar-decay writes)
+    kChunkF2 = 4,    // chunk-parallel Falcon-2
+};
+
+struct Plan {
+    // problem
+    int variant = 0, dtype = 0, phi = 0;
+    int B = 0, H = 0, T = 0, dk = 0, dv = 0, chunk = 0, window = 1;
+    int BH = 0;
+    int nchunks = 0;         // ceil(T / chunk) for chunk paths
+    int Tpad = 0;            // rows of the feature buffers (T, or nchunks * chunk)
+    float eps = 0.f, eps_gamma = 0.f, eps_rms = 0.f;
+    Path path = Path::kEmpty;
+
+    // boundary
+    bool fresh = true;       // input is a fresh sequence
+    int n_tail_in = 0;
+    int n_tail_out = 0;
+    const float *S_in = nullptr, *xnext_in = nullptr, *tailx_in = nullptr, *taily_in = nullptr;
+    float *S_out = nullptr, *xnext_out = nullptr, *tailx_out = nullptr, *taily_out = nullptr;
+
+    // tensors
+    const void *q = nullptr, *k = nullptr, *v = nullptr;
+    const float *beta = nullptr, *lambda = nullptr;
+    void *o = nullptr;
+
+    // workspace carve-up (offsets in bytes from the workspace base)
+    bool feat_f32 = true;    // storage type of the normalised features
+    size_t off_xn = 0, off_qn = 0, off_eta = 0, off_alpha = 0;
+    size_t off_chunk = 0;    // chunk-path operators
+    size_t chunk_bytes = 0;
+    size_t ws_bytes = 0;     // total required
+    void *ws = nullptr;
+
+    template <class T>
+    T *ws_at(size_t off) const { return reinterpret_cast<T *>(static_cast<char *>(ws) + off); }
+};
+
+// Validate `a` and fill `p`.  Never touches the GPU.  Returns a falcon status.
+// With check_pointers == false, only sizes and scalars are checked (used by
+// falcon_fwd_workspace_size, which must not read pointer fields).
+int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers);
+
+}  // namespace falcon

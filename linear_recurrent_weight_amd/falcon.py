@@ -1,0 +1,194 @@
+"""ctypes binding of libfalcon.so.
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+kernels behind ``falcon_fwd``.  PyTorch provides device memory and the
+current stream.  The binding raises if the library is missing; there is no
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import pathlib
+from dataclasses import dataclass
+from typing import Optional
+
+PKG = pathlib.Path(__file__).resolve().parent
+LIB_PATH = PKG / "libfalcon.so"
+
+ABI_VERSION = 1
+MAX_WINDOW = 8
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+VARIANTS = {"F1": 1, "F2": 2, "F3": 3, "F1A": 11, "F3A": 13}
+DTYPES = {"bf16": 0, "f32": 1}
+PHIS = {"rmsnorm": 0, "identity": 1}
+
+
+class FalconStateC(ctypes.Structure):
+    _fields_ = [("S", ctypes.c_void_p), ("x_next", ctypes.c_void_p),
+                ("tail_x", ctypes.c_void_p), ("tail_y", ctypes.c_void_p),
+                ("n_tail", ctypes.c_int), ("fresh", ctypes.c_int)]
+
+
+class FalconFwdArgsC(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int), ("variant", ctypes.c_int), ("dtype", ctypes.c_int),
+                ("phi", ctypes.c_int),
+                ("batch", ctypes.c_int), ("heads", ctypes.c_int), ("seqlen", ctypes.c_int),
+                ("dk", ctypes.c_int), ("dv", ctypes.c_int),
+                ("chunk", ctypes.c_int), ("window", ctypes.c_int),
+                ("eps", ctypes.c_float), ("eps_gamma", ctypes.c_float), ("eps_rms", ctypes.c_float),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("beta", ctypes.c_void_p), ("lambda_", ctypes.c_void_p),
+                ("state_in", ctypes.POINTER(FalconStateC)), ("state_out", ctypes.POINTER(FalconStateC)),
+                ("o", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+EXPORTS = ("falcon_fwd", "falcon_fwd_validate", "falcon_fwd_workspace_size",
+           "falcon_status_str", "falcon_abi_version")
+
+_lib = None
+
+
+def load_library(path: Optional[os.PathLike] = None) -> ctypes.CDLL:
+    """Load libfalcon.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = pathlib.Path(path) if path else LIB_PATH
+    if not p.exists():
+        raise RuntimeError(f"{p} not found: build it with `python -m linear_recurrent_weight_amd.build`")
+    lib = ctypes.CDLL(str(p))
+    lib.falcon_fwd.argtypes = [ctypes.POINTER(FalconFwdArgsC), ctypes.c_void_p]
+    lib.falcon_fwd.restype = ctypes.c_int
+    lib.falcon_fwd_validate.argtypes = [ctypes.POINTER(FalconFwdArgsC)]
+    lib.falcon_fwd_validate.restype = ctypes.c_int
+    lib.falcon_fwd_workspace_size.argtypes = [ctypes.POINTER(FalconFwdArgsC)]
+    lib.falcon_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.falcon_status_str.argtypes = [ctypes.c_int]
+    lib.falcon_status_str.restype = ctypes.c_char_p
+    lib.falcon_abi_version.argtypes = []
+    lib.falcon_abi_version.restype = ctypes.c_int
+    if lib.falcon_abi_version() != ABI_VERSION:
+        raise RuntimeError("libfalcon.so ABI version mismatch")
+    if path is None:
+        _lib = lib
+    return lib
+
+
+class FalconError(RuntimeError):
+    def __init__(self, status: int, lib=None):
+        lib = lib or load_library()
+        super().__init__(f"falcon_fwd failed: {lib.falcon_status_str(status).decode()} ({status})")
+        self.status = status
+
+
+@dataclass
+class FalconState:
+    """Boundary state (torch tensors on the device): S [B,H,dk,dv],
+    x_next [B,H,dk], tail_x [B,H,W-1,dk], tail_y [B,H,W-1,dv], fp32."""
+    S: "object"
+    x_next: "object"
+    tail_x: "object"
+    tail_y: "object"
+    n_tail: int = 0
+    fresh: bool = False
+
+    @staticmethod
+    def empty(batch, heads, dk, dv, window, device):
+        import torch
+        f = dict(dtype=torch.float32, device=device)
+        h = max(window - 1, 0)
+        return FalconState(torch.zeros(batch, heads, dk, dv, **f), torch.zeros(batch, heads, dk, **f),
+                           torch.zeros(batch, heads, h, dk, **f), torch.zeros(batch, heads, h, dv, **f))
+
+    def to_c(self) -> FalconStateC:
+        def ptr(t):
+            return t.data_ptr() if (t is not None and t.numel() > 0) else None
+        return FalconStateC(ptr(self.S), ptr(self.x_next), ptr(self.tail_x), ptr(self.tail_y),
+                            int(self.n_tail), int(bool(self.fresh)))
+
+
+def make_args(*, variant, dtype, batch, heads, seqlen, dk, dv, chunk=64, window=1, eps=1e-6,
+              eps_gamma=1e-3, eps_rms=1e-6, phi="rmsnorm", q=None, k=None, v=None, beta=None,
+              lam=None, o=None, state_in=None, state_out=None, workspace=None,
+              workspace_bytes=0) -> FalconFwdArgsC:
+    """Fill the C argument struct.  Tensor arguments may be torch tensors or
+    raw integer addresses."""
+    def addr(t):
+        if t is None:
+            return None
+        return t if isinstance(t, int) else t.data_ptr()
+    a = FalconFwdArgsC()
+    a.abi_version = ABI_VERSION
+    a.variant = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    a.dtype = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    a.phi = PHIS[phi] if isinstance(phi, str) else int(phi)
+    a.batch, a.heads, a.seqlen, a.dk, a.dv = batch, heads, seqlen, dk, dv
+    a.chunk, a.window = chunk, window
+    a.eps, a.eps_gamma, a.eps_rms = eps, eps_gamma, eps_rms
+    a.q, a.k, a.v, a.beta, a.lambda_, a.o = map(addr, (q, k, v, beta, lam, o))
+    a.state_in = ctypes.pointer(state_in) if state_in is not None else None
+    a.state_out = ctypes.pointer(state_out) if state_out is not None else None
+    a.workspace = addr(workspace)
+    a.workspace_bytes = workspace_bytes
+    return a
+
+
+def fwd(q, k, v, beta, lam, *, variant="F1", chunk=64, window=1, eps=1e-6, eps_gamma=1e-3,
+        eps_rms=1e-6, phi="rmsnorm", state: Optional[FalconState] = None, want_state=True,
+        out=None, workspace=None, stream=None):
+    """Falcon forward pass on the GPU.
+
+    q, k: [B,H,T,dk]; v: [B,H,T,dv] (all bf16 or all fp32, contiguous, on the
+    device); beta: [B,H,T] fp32 ([B,H,T,dv] for F2); lam: [B,H,T] fp32.
+    Returns (o [B,H,T,dv], FalconState or None).
+    """
+    import torch
+    lib = load_library()
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    dtype = {torch.bfloat16: "bf16", torch.float32: "f32"}.get(q.dtype)
+    if dtype is None or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must all be bfloat16 or all float32")
+    for t in (q, k, v, beta, lam):
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    if beta.dtype != torch.float32 or lam.dtype != torch.float32:
+        raise ValueError("beta and lambda must be float32")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    o = out if out is not None else torch.empty(B, H, T, dv, dtype=q.dtype, device=dev)
+    st_in = state.to_c() if state is not None else None
+    st_out_t = FalconState.empty(B, H, dk, dv, window, dev) if want_state else None
+    st_out = st_out_t.to_c() if st_out_t is not None else None
+    args = make_args(variant=variant, dtype=dtype, batch=B, heads=H, seqlen=T, dk=dk, dv=dv,
+                     chunk=chunk, window=window, eps=eps, eps_gamma=eps_gamma, eps_rms=eps_rms,
+                     phi=phi, q=q, k=k, v=v, beta=beta, lam=lam, o=o, state_in=st_in,
+                     state_out=st_out)
+    nbytes = lib.falcon_fwd_workspace_size(ctypes.byref(args))
+    if nbytes:
+        if workspace is None or workspace.numel() < nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        args.workspace = workspace.data_ptr()
+        args.workspace_bytes = workspace.numel()
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.falcon_fwd(ctypes.byref(args), ctypes.c_void_p(stream))
+    if rc != OK:
+        raise FalconError(rc, lib)
+    if st_out_t is not None:
+        st_out_t.n_tail = args.state_out.contents.n_tail
+        st_out_t.fresh = bool(args.state_out.contents.fresh)
+    return o, st_out_t
+
+
+def workspace_size(**kw) -> int:
+    lib = load_library()
+    return int(lib.falcon_fwd_workspace_size(ctypes.byref(make_args(**kw))))
+
+
+def validate(**kw) -> int:
+    lib = load_library()
+    return int(lib.falcon_fwd_validate(ctypes.byref(make_args(**kw))))

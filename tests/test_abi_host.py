@@ -1,0 +1,206 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/falcon.h declares, and rejects malformed arguments with the
+documented status before launching anything.  No GPU needed."""
+from __future__ import annotations
+
+import ctypes
+import pathlib
+import re
+
+import pytest
+
+from linear_recurrent_weight_amd import falcon as fb
+
+ROOT = pathlib.Path(__file__).resolve().parent.parent
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not fb.LIB_PATH.exists():
+        pytest.skip("libfalcon.so not built")
+    return fb.load_library()
+
+
+def header_functions():
+    text = (ROOT / "include" / "falcon.h").read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(falcon_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert header_functions() == sorted(fb.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert lib.falcon_abi_version() == fb.ABI_VERSION
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, -4, 7):
+        assert isinstance(lib.falcon_status_str(st), bytes)
+    assert lib.falcon_status_str(-3) == b"workspace missing or too small"
+
+
+FAKE = 1 << 20  # an aligned, never dereferenced address
+
+
+def args(**kw):
+    base = dict(variant="F1", dtype="bf16", batch=2, heads=3, seqlen=128, dk=64, dv=64, chunk=64,
+                window=1, q=FAKE, k=2 * FAKE, v=3 * FAKE, beta=4 * FAKE, lam=5 * FAKE, o=6 * FAKE)
+    base.update(kw)
+    return fb.make_args(**base)
+
+
+def validate(lib, a):
+    return lib.falcon_fwd_validate(ctypes.byref(a))
+
+
+def wsize(lib, a):
+    return lib.falcon_fwd_workspace_size(ctypes.byref(a))
+
+
+def with_ws(lib, a):
+    n = wsize(lib, a)
+    a.workspace = 1 << 30
+    a.workspace_bytes = n
+    return a
+
+
+def test_valid_arguments(lib):
+    for var, w in [("F1", 1), ("F2", 1), ("F3", 4), ("F1A", 1), ("F3A", 8)]:
+        a = with_ws(lib, args(variant=var, window=w, chunk=0))
+        assert validate(lib, a) == fb.OK, var
+    assert validate(lib, with_ws(lib, args())) == fb.OK
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("abi_version", 99, fb.ERR_INVALID_ARG),
+    ("variant", 4, fb.ERR_INVALID_ARG),
+    ("variant", 12, fb.ERR_INVALID_ARG),
+    ("dtype", 2, fb.ERR_INVALID_ARG),
+    ("phi", 5, fb.ERR_INVALID_ARG),
+    ("batch", 0, fb.ERR_INVALID_ARG),
+    ("heads", -1, fb.ERR_INVALID_ARG),
+    ("seqlen", -5, fb.ERR_INVALID_ARG),
+    ("dk", 48, fb.ERR_UNSUPPORTED),
+    ("dv", 256, fb.ERR_UNSUPPORTED),
+    ("chunk", -1, fb.ERR_INVALID_ARG),
+    ("chunk", 48, fb.ERR_UNSUPPORTED),
+    ("window", 0, fb.ERR_INVALID_ARG),
+    ("window", 2, fb.ERR_INVALID_ARG),
+    ("eps", -1.0, fb.ERR_INVALID_ARG),
+    ("eps", float("nan"), fb.ERR_INVALID_ARG),
+    ("eps_rms", float("inf"), fb.ERR_INVALID_ARG),
+    ("eps_gamma", 0.0, fb.ERR_INVALID_ARG),
+    ("eps_gamma", 1.0, fb.ERR_INVALID_ARG),
+])
+def test_field_rules(lib, field, value, status):
+    a = with_ws(lib, args())
+    setattr(a, field, value)
+    assert validate(lib, a) == status
+    # falcon_fwd reports the same status and launches nothing
+    assert lib.falcon_fwd(ctypes.byref(a), None) == status
+
+
+def test_window_limits(lib):
+    a = with_ws(lib, args(variant="F3A", window=9, chunk=0))
+    assert validate(lib, a) == fb.ERR_UNSUPPORTED
+    a = with_ws(lib, args(variant="F3A", window=8, chunk=0))
+    assert validate(lib, a) == fb.OK
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "beta", "lambda_", "o"])
+def test_null_and_misaligned_tensors(lib, name):
+    a = with_ws(lib, args())
+    setattr(a, name, None)
+    assert validate(lib, a) == fb.ERR_INVALID_ARG
+    a = with_ws(lib, args())
+    setattr(a, name, FAKE * 7 + 2)
+    assert validate(lib, a) == fb.ERR_INVALID_ARG
+
+
+def test_empty_sequence_needs_no_tensors(lib):
+    a = args(seqlen=0, q=None, k=None, v=None, beta=None, lam=None, o=None)
+    assert wsize(lib, a) == 0
+    assert validate(lib, a) == fb.OK
+
+
+def test_output_may_not_alias_inputs(lib):
+    a = with_ws(lib, args(o=FAKE))
+    assert validate(lib, a) == fb.ERR_INVALID_ARG
+
+
+def test_workspace_rules(lib):
+    a = args()
+    n = wsize(lib, a)
+    assert n > 0
+    assert validate(lib, a) == fb.ERR_WORKSPACE          # missing
+    a.workspace = 1 << 30
+    a.workspace_bytes = n - 1
+    assert validate(lib, a) == fb.ERR_WORKSPACE          # too small
+    a.workspace_bytes = n
+    assert validate(lib, a) == fb.OK
+    a.workspace = (1 << 30) + 64
+    assert validate(lib, a) == fb.ERR_WORKSPACE          # not 256-byte aligned
+
+
+def test_workspace_grows_with_problem(lib):
+    small = wsize(lib, args(seqlen=64))
+    big = wsize(lib, args(seqlen=1024))
+    assert 0 < small < big
+    # ragged lengths round up to whole chunks on the chunk path
+    assert wsize(lib, args(seqlen=65)) == wsize(lib, args(seqlen=128))
+    # a malformed request reports 0 bytes
+    assert wsize(lib, args(dk=48)) == 0
+
+
+def test_state_rules(lib):
+    S = fb.FalconStateC(7 * FAKE, 8 * FAKE, 9 * FAKE, 10 * FAKE, 0, 0)
+    a = with_ws(lib, args(state_in=S))
+    assert validate(lib, a) == fb.OK
+    S.x_next = None                                       # continuing needs x_next
+    a = with_ws(lib, args(state_in=S))
+    assert validate(lib, a) == fb.ERR_INVALID_ARG
+    S.fresh = 1                                           # fresh ignores it
+    a = with_ws(lib, args(state_in=S))
+    assert validate(lib, a) == fb.OK
+    S.n_tail = 1                                          # fresh with a tail
+    a = with_ws(lib, args(state_in=S))
+    assert validate(lib, a) == fb.ERR_INVALID_ARG
+    W = fb.FalconStateC(7 * FAKE, 8 * FAKE, 9 * FAKE, 10 * FAKE, 4, 0)
+    a = with_ws(lib, args(variant="F3A", window=4, chunk=0, state_in=W))
+    assert validate(lib, a) == fb.ERR_INVALID_ARG         # n_tail > W - 1
+    W.n_tail = 3
+    a = with_ws(lib, args(variant="F3A", window=4, chunk=0, state_in=W))
+    assert validate(lib, a) == fb.OK
+    W.tail_x = None
+    a = with_ws(lib, args(variant="F3A", window=4, chunk=0, state_in=W))
+    assert validate(lib, a) == fb.ERR_INVALID_ARG
+
+
+def test_state_out_rules(lib):
+    out = fb.FalconStateC(11 * FAKE, 12 * FAKE, None, None, 0, 0)
+    a = with_ws(lib, args(state_out=out))
+    assert validate(lib, a) == fb.OK
+    a = with_ws(lib, args(variant="F3A", window=4, chunk=0, state_out=out))
+    assert validate(lib, a) == fb.ERR_INVALID_ARG         # windowed needs a tail buffer
+    out.x_next = None
+    a = with_ws(lib, args(state_out=out))
+    assert validate(lib, a) == fb.ERR_INVALID_ARG
+    # state_out may not overlap state_in
+    sin = fb.FalconStateC(11 * FAKE, 13 * FAKE, None, None, 0, 0)
+    out = fb.FalconStateC(11 * FAKE, 12 * FAKE, None, None, 0, 0)
+    a = with_ws(lib, args(state_in=sin, state_out=out))
+    assert validate(lib, a) == fb.ERR_INVALID_ARG
+
+
+def test_chunk_path_coverage(lib):
+    """Combinations with a chunk-parallel kernel validate; the others report
+    UNSUPPORTED (and the token-recurrent form takes every variant)."""
+    assert validate(lib, with_ws(lib, args(variant="F1", dk=128, dv=32))) == fb.OK
+    assert validate(lib, with_ws(lib, args(variant="F1", dk=16))) == fb.ERR_UNSUPPORTED
+    for var in ("F1", "F2", "F3", "F1A", "F3A"):
+        w = 3 if var in ("F3", "F3A") else 1
+        assert validate(lib, with_ws(lib, args(variant=var, window=w, chunk=0, dk=16, dv=16))) == fb.OK

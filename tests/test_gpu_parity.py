@@ -1,0 +1,215 @@
+"""GPU parity: the HIP path, called through the C ABI, against the fp64
+oracle on the same seeded inputs.  Bound: max relative error (per head,
+max|gpu - ref| / max|ref|) <= 2e-2 with bf16 inputs and fp32 state, and
+<= 1e-5 in the all-fp32 mode."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from linear_recurrent_weight_amd.inputs import WORKLOADS
+import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+VARIANT_WINDOWS = [("F1", 1), ("F2", 1), ("F3", 3), ("F1A", 1), ("F3A", 3), ("F3", 8), ("F3A", 8)]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from linear_recurrent_weight_amd import falcon as fb
+    fb.load_library()          # raises when the HIP library is missing
+
+
+def check(w, heads=None, chunk=None, tol=None, state=None, oracle_state=None):
+    inp = gu.make(w)
+    dev = gu.to_device(inp, w)
+    heads = gu.sample_heads(w, 6) if heads is None else heads
+    print(f"[parity] {w.name} {w.variant} chunk={w.chunk if chunk is None else chunk} "
+          f"shape=({w.batch},{w.heads},{w.seqlen},{w.dk},{w.dv}) W={w.window} {w.dtype}", flush=True)
+    o, st = gu.run_gpu(w, dev, chunk=chunk, state=state)
+    o_ref, st_ref = gu.oracle_heads(w, inp, heads, state_in=oracle_state)
+    eo, es = gu.compare(w, heads, o, st, o_ref, st_ref)
+    tol = gu.tol_for(w) if tol is None else tol
+    print(f"    err_o={eo:.3e} err_S={es:.3e} tol={tol}", flush=True)
+    assert np.isfinite(eo) and np.isfinite(es)
+    assert eo <= tol and es <= tol, (eo, es)
+    return o, st, inp, dev
+
+
+# -- the named workloads ----------------------------------------------------
+
+def test_c1_recurrent_f32():
+    check(WORKLOADS["c1"])
+
+
+def test_c2_chunk_f1_bf16():
+    check(WORKLOADS["c2"], heads=gu.sample_heads(WORKLOADS["c2"], 8))
+
+
+@pytest.mark.parametrize("name", ["c3", "c4", "c5", "c3clamp", "c5f3"])
+def test_named_workloads_recurrent_form(name):
+    """Every named workload through the token-recurrent HIP form."""
+    check(WORKLOADS[name], chunk=0, heads=gu.sample_heads(WORKLOADS[name], 3))
+
+
+# -- small cases of every variant ------------------------------------------
+
+@pytest.mark.parametrize("variant,window", VARIANT_WINDOWS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_recurrent_variants(variant, window, dtype):
+    w = gu.small(variant, dtype, T=150, dk=64, dv=32, window=window)
+    check(w)
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (128, 16), (128, 128)])
+def test_recurrent_head_dims(dk, dv):
+    check(gu.small("F1", "f32", B=1, H=2, T=70, dk=dk, dv=dv))
+    check(gu.small("F3A", "f32", B=1, H=2, T=70, dk=dk, dv=dv, window=4))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200, 256])
+def test_chunk_f1_lengths(dtype, T):
+    check(gu.small("F1", dtype, B=2, H=3, T=T, dk=64, dv=64, chunk=64))
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 16), (64, 16), (128, 32), (128, 128)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_f1_head_dims(dk, dv, dtype):
+    check(gu.small("F1", dtype, B=1, H=3, T=130, dk=dk, dv=dv, chunk=64))
+
+
+def test_chunk_f1_clamp_binds():
+    """eta*lambda < beta, so beta in (1, 2) with a ridge well above ||x||^2 = 64
+    puts alpha on the clamp 1 - eps_gamma for most tokens."""
+    w = gu.small("F1", "f32", B=1, H=2, T=200, chunk=64, lam_lo=200.0, lam_hi=400.0, eps_gamma=0.3)
+    inp = gu.make(w)
+    inp["beta"] = (1.0 + inp["beta"]).astype(np.float32)
+    dev = gu.to_device(inp, w)
+    o, st = gu.run_gpu(w, dev)
+    o_ref, st_ref, tr = gu.oracle_heads(w, inp, np.arange(2), trace=True)
+    assert (tr.alpha >= 1 - 0.3 - 1e-9).mean() > 0.5
+    eo, es = gu.compare(w, np.arange(2), o, st, o_ref, st_ref)
+    assert eo <= 1e-5 and es <= 1e-5, (eo, es)
+
+
+# -- continuation -------------------------------------------------------------
+
+@pytest.mark.parametrize("variant,window,chunk", [("F1", 1, 0), ("F2", 1, 0), ("F3", 4, 0),
+                                                  ("F1A", 1, 0), ("F3A", 8, 0), ("F1", 1, 64)])
+@pytest.mark.parametrize("split", [0, 3, 64, 100])
+def test_continuation(variant, window, chunk, split):
+    """Two calls carrying (S, x_next, tail) equal one call and the oracle."""
+    import torch
+    w = gu.small(variant, "f32", B=2, H=2, T=160, dk=32, dv=32, chunk=chunk, window=window, seed=11)
+    inp = gu.make(w)
+    dev = gu.to_device(inp, w)
+    o_full, st_full = gu.run_gpu(w, dev)
+    a = {k: v[:, :, :split].contiguous() for k, v in dev.items()}
+    b = {k: v[:, :, split:].contiguous() for k, v in dev.items()}
+    o1, st1 = gu.run_gpu(w.with_(seqlen=split), a)
+    o2, st2 = gu.run_gpu(w.with_(seqlen=160 - split), b, state=st1)
+    o_cat = torch.cat([o1, o2], 2)
+    heads = np.arange(4)
+    o_ref, st_ref = gu.oracle_heads(w, inp, heads)
+    eo, es = gu.compare(w, heads, o_cat, st2, o_ref, st_ref)
+    assert eo <= 1e-5 and es <= 1e-5, (eo, es)
+    assert torch.allclose(o_cat, o_full, rtol=1e-5, atol=1e-6)
+    assert st2.n_tail == st_full.n_tail == min(window - 1, 160)
+    if window > 1:
+        assert torch.allclose(st2.tail_x, st_full.tail_x) and torch.allclose(st2.tail_y, st_full.tail_y)
+    assert torch.allclose(st2.x_next, st_full.x_next)
+
+
+def test_continuation_with_state_from_oracle_layout():
+    """A nonzero incoming state (S, x_next, partial tail) matches the oracle."""
+    import torch
+    from linear_recurrent_weight_amd import falcon as fb
+    w = gu.small("F3A", "f32", B=1, H=2, T=40, dk=16, dv=16, window=5, seed=3)
+    inp = gu.make(w)
+    dev = gu.to_device(inp, w)
+    rng = np.random.default_rng(5)
+    S0 = rng.standard_normal((1, 2, 16, 16)).astype(np.float32)
+    xn = rng.standard_normal((1, 2, 16)).astype(np.float32)
+    tx = np.zeros((1, 2, 4, 16), np.float32)
+    ty = np.zeros((1, 2, 4, 16), np.float32)
+    tx[:, :, 2:] = rng.standard_normal((1, 2, 2, 16))
+    ty[:, :, 2:] = rng.standard_normal((1, 2, 2, 16))
+    cuda = lambda a: torch.from_numpy(a).cuda()
+    st = fb.FalconState(cuda(S0), cuda(xn), cuda(tx), cuda(ty), n_tail=2, fresh=False)
+    import oracle
+    ost = oracle.OracleState(S=S0.reshape(2, 16, 16).astype(np.float64), fresh=False,
+                             x_next=xn.reshape(2, 16).astype(np.float64),
+                             tail_x=tx.reshape(2, 4, 16)[:, 2:].astype(np.float64),
+                             tail_y=ty.reshape(2, 4, 16)[:, 2:].astype(np.float64))
+    o, st_out = gu.run_gpu(w, dev, state=st)
+    o_ref, st_ref = gu.oracle_heads(w, inp, np.arange(2), state_in=ost)
+    eo, es = gu.compare(w, np.arange(2), o, st_out, o_ref, st_ref)
+    assert eo <= 1e-5 and es <= 1e-5, (eo, es)
+    assert st_out.n_tail == 4
+
+
+# -- edge cases ---------------------------------------------------------------
+
+def test_empty_sequence_passes_state_through():
+    import torch
+    from linear_recurrent_weight_amd import falcon as fb
+    w = gu.small("F3A", "f32", B=1, H=2, T=0, dk=16, dv=16, window=3)
+    S0 = torch.randn(1, 2, 16, 16, device="cuda")
+    xn = torch.randn(1, 2, 16, device="cuda")
+    tx = torch.randn(1, 2, 2, 16, device="cuda")
+    ty = torch.randn(1, 2, 2, 16, device="cuda")
+    st = fb.FalconState(S0, xn, tx, ty, n_tail=1, fresh=False)
+    z = torch.zeros(1, 2, 0, 16, device="cuda")
+    o, out = fb.fwd(z, z, z, torch.zeros(1, 2, 0, device="cuda"), torch.zeros(1, 2, 0, device="cuda"),
+                    variant="F3A", chunk=0, window=3, state=st)
+    torch.cuda.synchronize()
+    assert o.shape == (1, 2, 0, 16)
+    assert torch.equal(out.S, S0) and torch.equal(out.x_next, xn)
+    assert out.n_tail == 1 and not out.fresh
+    assert torch.equal(out.tail_x[:, :, 1:], tx[:, :, 1:]) and torch.all(out.tail_x[:, :, :1] == 0)
+    o, out = fb.fwd(z, z, z, torch.zeros(1, 2, 0, device="cuda"), torch.zeros(1, 2, 0, device="cuda"),
+                    variant="F1", chunk=0)
+    assert out.fresh and torch.all(out.S == 0)
+
+
+def test_zero_keys_give_zero_step():
+    """All-zero keys with lambda = eps = 0: the step denominator vanishes, eta
+    = 0, the state stays zero and nothing is NaN."""
+    import torch
+    from linear_recurrent_weight_amd import falcon as fb
+    for chunk in (0, 64):
+        q = torch.randn(1, 1, 70, 64, device="cuda")
+        k = torch.zeros(1, 1, 70, 64, device="cuda")
+        v = torch.randn(1, 1, 70, 64, device="cuda")
+        beta = torch.full((1, 1, 70), 0.5, device="cuda")
+        lam = torch.zeros(1, 1, 70, device="cuda")
+        o, st = fb.fwd(q, k, v, beta, lam, variant="F1", chunk=chunk, eps=0.0)
+        assert torch.all(o == 0) and torch.all(st.S == 0)
+
+
+def test_identity_feature_map():
+    w = gu.small("F1", "f32", B=1, H=2, T=96, dk=32, dv=32, chunk=64)
+    inp = gu.make(w)
+    dev = gu.to_device(inp, w)
+    from linear_recurrent_weight_amd import falcon as fb
+    import oracle
+    for chunk in (0, 64):
+        o, st = fb.fwd(dev["q"], dev["k"], dev["v"], dev["beta"], dev["lam"], variant="F1",
+                       chunk=chunk, phi="identity")
+        o_ref, st_ref = oracle.falcon_forward("F1", inp["q"], inp["k"], inp["v"], inp["beta"],
+                                              inp["lam"], phi_kind=oracle.PHI_IDENTITY)
+        assert gu.max_rel_err(o.double().cpu().numpy()[0], o_ref[0]) <= 1e-5
+
+
+def test_deterministic():
+    import torch
+    w = WORKLOADS["c2"].with_(batch=2)
+    dev = gu.to_device(gu.make(w), w)
+    o1, s1 = gu.run_gpu(w, dev)
+    o2, s2 = gu.run_gpu(w, dev)
+    assert torch.equal(o1, o2) and torch.equal(s1.S, s2.S)
