@@ -158,6 +158,19 @@ int falcon_fwd_validate(const falcon_fwd_args *args);
  * host fields state_out->n_tail and ->fresh are written before returning. */
 int falcon_fwd(const falcon_fwd_args *args, void *stream);
 
+/* Measurement variant of falcon_fwd for benchmarks and profilers: the same
+ * validation and the same kernels on `stream`, and in addition it records
+ * events[0] before the first kernel and events[i] after the i-th kernel, for
+ * i < n_events.  `events` holds hipEvent_t handles owned by the caller (NULL
+ * with n_events == 0 is allowed).  Returns the number of kernels launched
+ * (>= 0) or a negative status. */
+int falcon_fwd_profile(const falcon_fwd_args *args, void *stream, void *const *events, int n_events);
+
+/* Static name of the i-th kernel (0-based) that falcon_fwd launches for these
+ * arguments, or NULL when i is out of range or the arguments are invalid.
+ * Pure host code, no HIP call. */
+const char *falcon_kernel_name(const falcon_fwd_args *args, int i);
+
 /* Static text for a status code. */
 const char *falcon_status_str(int status);
 

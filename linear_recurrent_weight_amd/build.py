@@ -62,6 +62,18 @@ def build(verbose: bool = False) -> pathlib.Path:
     return LIB
 
 
+
+def sources_digest() -> str:
+    """sha256 over the library sources and the public header, to tell whether
+    a stored profile still describes the current kernels."""
+    import hashlib
+    h = hashlib.sha256()
+    for p in sources() + sorted(CSRC.glob("*.h")) + [ROOT / "include" / "falcon.h"]:
+        h.update(p.name.encode())
+        h.update(p.read_bytes())
+    return h.hexdigest()[:16]
+
+
 if __name__ == "__main__":
     path = build(verbose="-v" in sys.argv)
     print(path)

@@ -338,25 +338,27 @@ __global__ __launch_bounds__(256) void chunk_f1_scan(ChunkF1Args a, int nslice) 
 }
 
 template <class E, int DK>
-void launch_dk(const ChunkF1Args &a, hipStream_t s) {
+void launch_dk(const ChunkF1Args &a, hipStream_t s, Marks *m) {
     chunk_f1_prep<E, DK><<<dim3(a.nchunks, a.BH), 256, 0, s>>>(a);
+    m->mark(s);
     const int nslice = a.dv / 16;
     const int groups = (a.BH + 7) / 8;
     chunk_f1_scan<E, DK><<<groups * nslice * 8, 256, 0, s>>>(a, nslice);
+    m->mark(s);
 }
 
 template <class E>
-void launch_e(const ChunkF1Args &a, hipStream_t s) {
-    if (a.dk == 32) launch_dk<E, 32>(a, s);
-    else if (a.dk == 64) launch_dk<E, 64>(a, s);
-    else launch_dk<E, 128>(a, s);
+void launch_e(const ChunkF1Args &a, hipStream_t s, Marks *m) {
+    if (a.dk == 32) launch_dk<E, 32>(a, s, m);
+    else if (a.dk == 64) launch_dk<E, 64>(a, s, m);
+    else launch_dk<E, 128>(a, s, m);
 }
 
 }  // namespace
 
-void launch_chunk_f1(const ChunkF1Args &a, bool bf16, hipStream_t s) {
-    if (bf16) launch_e<bf16_t>(a, s);
-    else launch_e<float>(a, s);
+void launch_chunk_f1(const ChunkF1Args &a, bool bf16, hipStream_t s, Marks *m) {
+    if (bf16) launch_e<bf16_t>(a, s, m);
+    else launch_e<float>(a, s, m);
 }
 
 }  // namespace falcon

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <cstddef>
+#include <cstdlib>
 
 namespace falcon {
 
@@ -21,6 +22,22 @@ constexpr size_t chunk_f1_scal_off(size_t esz) { return 2 * size_t(kChunk) * kCh
 constexpr size_t chunk_f1_bytes(int /*dk*/, int /*dv*/, int dtype_is_f32) {
     const size_t esz = dtype_is_f32 ? 4 : 2;
     return chunk_f1_scal_off(esz) + 4 * size_t(kChunk) * 4;
+}
+
+// Fused bf16 Falcon-1 kernel: d_k = 64, value columns split into slices of
+// 32 or 64 per workgroup.  More slices give more workgroups (and repeat the
+// state-independent chunk work per slice); the slice width is chosen so that
+// a launch has at least ~128 workgroups, unless the sequence is short.
+constexpr bool chunk_f1_fused_supported(bool bf16, int dk, int dv) {
+    return bf16 && dk == 64 && (dv == 32 || dv == 64 || dv == 128);
+}
+inline int chunk_f1_fused_slice(int bh, int dv) {
+    if (dv == 32) return 32;
+    if (const char *e = std::getenv("FALCON_F1_SLICE")) {   // tuning override: 32 or 64
+        const int v = std::atoi(e);
+        if ((v == 32 || v == 64) && dv % v == 0) return v;
+    }
+    return (bh * (dv / 64) >= 128) ? 64 : 32;
 }
 
 }  // namespace falcon

@@ -5,11 +5,19 @@
 
 using namespace falcon;
 
-extern "C" int falcon_fwd(const falcon_fwd_args *args, void *stream) {
+namespace {
+
+const char *const kNamesEmpty[] = {"passthrough"};
+const char *const kNamesRecurrent[] = {"feature", "recurrent"};
+const char *const kNamesChunkF1[] = {"feature", "chunk_f1_prep", "chunk_f1_scan"};
+const char *const kNamesChunkF1Fused[] = {"chunk_f1_fused"};
+
+int run(const falcon_fwd_args *args, void *stream, Marks *m) {
     Plan p;
     const int rc = build_plan(args, &p, true);
     if (rc != FALCON_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    m->mark(s);
     if (args->state_out) {
         args->state_out->n_tail = p.n_tail_out;
         args->state_out->fresh = (p.T == 0 && p.fresh) ? 1 : 0;
@@ -31,8 +39,31 @@ extern "C" int falcon_fwd(const falcon_fwd_args *args, void *stream) {
             pa.xnext_out = p.xnext_out;
             pa.tailx_out = p.tailx_out;
             pa.taily_out = p.taily_out;
-            launch_passthrough(pa, s);
+            launch_passthrough(pa, s, m);
         }
+    } else if (p.path == Path::kChunkF1Fused) {
+        F1FusedArgs fa{};
+        fa.BH = p.BH;
+        fa.T = p.T;
+        fa.nchunks = p.nchunks;
+        fa.dk = p.dk;
+        fa.dv = p.dv;
+        fa.phi = p.phi;
+        fa.fresh = p.fresh ? 1 : 0;
+        fa.eps = p.eps;
+        fa.eps_gamma = p.eps_gamma;
+        fa.eps_rms = p.eps_rms;
+        fa.q = p.q;
+        fa.k = p.k;
+        fa.v = p.v;
+        fa.beta = p.beta;
+        fa.lambda = p.lambda;
+        fa.xnext_in = p.xnext_in;
+        fa.S_in = p.S_in;
+        fa.S_out = p.S_out;
+        fa.xnext_out = p.xnext_out;
+        fa.o = p.o;
+        launch_chunk_f1_fused(fa, p.slice, s, m);
     } else {
         FeatureArgs fa{};
         fa.variant = p.variant;
@@ -65,7 +96,7 @@ extern "C" int falcon_fwd(const falcon_fwd_args *args, void *stream) {
         fa.eta = p.ws_at<float>(p.off_eta);
         fa.alpha = p.ws_at<float>(p.off_alpha);
         const bool io_bf16 = p.dtype == FALCON_BF16;
-        launch_features(fa, io_bf16, !p.feat_f32, s);
+        launch_features(fa, io_bf16, !p.feat_f32, s, m);
 
         if (p.path == Path::kRecurrent) {
             RecurrentArgs ra{};
@@ -86,7 +117,7 @@ extern "C" int falcon_fwd(const falcon_fwd_args *args, void *stream) {
             ra.tailx_in = p.tailx_in;
             ra.taily_in = p.taily_in;
             ra.S_out = p.S_out;
-            launch_recurrent(ra, io_bf16, s);
+            launch_recurrent(ra, io_bf16, s, m);
         } else if (p.path == Path::kChunkF1) {
             ChunkF1Args ca{};
             ca.BH = p.BH;
@@ -105,9 +136,37 @@ extern "C" int falcon_fwd(const falcon_fwd_args *args, void *stream) {
             ca.S_out = p.S_out;
             ca.ops = p.ws_at<void>(p.off_chunk);
             ca.chunk_bytes = p.chunk_bytes;
-            launch_chunk_f1(ca, io_bf16, s);
+            launch_chunk_f1(ca, io_bf16, s, m);
         }
     }
     if (hipGetLastError() != hipSuccess) return FALCON_ERR_HIP;
-    return FALCON_OK;
+    return m->count - 1;
+}
+
+}  // namespace
+
+extern "C" int falcon_fwd(const falcon_fwd_args *args, void *stream) {
+    Marks m;
+    const int rc = run(args, stream, &m);
+    return rc < 0 ? rc : FALCON_OK;
+}
+
+extern "C" int falcon_fwd_profile(const falcon_fwd_args *args, void *stream, void *const *events,
+                                  int n_events) {
+    Marks m;
+    m.ev = events;
+    m.n = n_events < 0 ? 0 : n_events;
+    return run(args, stream, &m);
+}
+
+extern "C" const char *falcon_kernel_name(const falcon_fwd_args *args, int i) {
+    Plan p;
+    if (build_plan(args, &p, false) != FALCON_OK || i < 0) return nullptr;
+    switch (p.path) {
+        case Path::kEmpty: return i < 1 ? kNamesEmpty[i] : nullptr;
+        case Path::kRecurrent: return i < 2 ? kNamesRecurrent[i] : nullptr;
+        case Path::kChunkF1: return i < 3 ? kNamesChunkF1[i] : nullptr;
+        case Path::kChunkF1Fused: return i < 1 ? kNamesChunkF1Fused[i] : nullptr;
+        default: return nullptr;
+    }
 }

@@ -303,7 +303,7 @@ __global__ void passthrough_kernel(PassArgs a) {
 
 }  // namespace
 
-void launch_features(const FeatureArgs &a, bool in_bf16, bool feat_bf16, hipStream_t s) {
+void launch_features(const FeatureArgs &a, bool in_bf16, bool feat_bf16, hipStream_t s, Marks *m) {
     dim3 grid((a.Tpad + kTile - 1) / kTile, a.BH);
     if (in_bf16 && feat_bf16)
         feature_kernel<bf16_t, bf16_t><<<grid, 256, 0, s>>>(a);
@@ -313,13 +313,15 @@ void launch_features(const FeatureArgs &a, bool in_bf16, bool feat_bf16, hipStre
         feature_kernel<float, bf16_t><<<grid, 256, 0, s>>>(a);
     else
         feature_kernel<float, float><<<grid, 256, 0, s>>>(a);
+    m->mark(s);
 }
 
-void launch_passthrough(const PassArgs &a, hipStream_t s) {
+void launch_passthrough(const PassArgs &a, hipStream_t s, Marks *m) {
     size_t n = size_t(a.BH) * a.dk * a.dv;
-    size_t m = size_t(a.BH) * (a.halo > 0 ? a.halo : 1) * (a.dk > a.dv ? a.dk : a.dv);
-    if (m > n) n = m;
+    const size_t nt = size_t(a.BH) * (a.halo > 0 ? a.halo : 1) * (a.dk > a.dv ? a.dk : a.dv);
+    if (nt > n) n = nt;
     passthrough_kernel<<<(n + 255) / 256, 256, 0, s>>>(a);
+    m->mark(s);
 }
 
 }  // namespace falcon

@@ -48,9 +48,32 @@ struct ChunkF1Args {
     size_t chunk_bytes;
 };
 
-void launch_features(const FeatureArgs &a, bool in_bf16, bool feat_bf16, hipStream_t s);
-void launch_passthrough(const PassArgs &a, hipStream_t s);
-void launch_recurrent(const RecurrentArgs &a, bool io_bf16, hipStream_t s);
-void launch_chunk_f1(const ChunkF1Args &a, bool bf16, hipStream_t s);
+// Optional event marks between kernel launches (measurement entry point).
+struct Marks {
+    void *const *ev = nullptr;
+    int n = 0;
+    int count = 0;
+    void mark(hipStream_t s) {
+        if (ev && count < n) (void)hipEventRecord(static_cast<hipEvent_t>(ev[count]), s);
+        ++count;
+    }
+};
+
+struct F1FusedArgs {
+    int BH, T, nchunks, dk, dv, phi, fresh;
+    float eps, eps_gamma, eps_rms;
+    const void *q, *k, *v;  // bf16 [BH, T, d]
+    const float *beta, *lambda;
+    const float *xnext_in;  // nullptr when fresh
+    const float *S_in;
+    float *S_out, *xnext_out;
+    void *o;
+};
+
+void launch_features(const FeatureArgs &a, bool in_bf16, bool feat_bf16, hipStream_t s, Marks *m);
+void launch_passthrough(const PassArgs &a, hipStream_t s, Marks *m);
+void launch_recurrent(const RecurrentArgs &a, bool io_bf16, hipStream_t s, Marks *m);
+void launch_chunk_f1(const ChunkF1Args &a, bool bf16, hipStream_t s, Marks *m);
+void launch_chunk_f1_fused(const F1FusedArgs &a, int ds, hipStream_t s, Marks *m);
 
 }  // namespace falcon

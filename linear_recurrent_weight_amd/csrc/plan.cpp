@@ -73,10 +73,14 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
     if (a->chunk == 0) {
         p->path = Path::kRecurrent;
     } else if (a->chunk == kChunk) {
-        if (var == FALCON_V1 && chunk_f1_supported(a->dk, a->dv))
+        if (var == FALCON_V1 && chunk_f1_fused_supported(a->dtype == FALCON_BF16, a->dk, a->dv)) {
+            p->path = Path::kChunkF1Fused;
+            p->slice = chunk_f1_fused_slice(a->batch * a->heads, a->dv);
+        } else if (var == FALCON_V1 && chunk_f1_supported(a->dk, a->dv)) {
             p->path = Path::kChunkF1;
-        else
+        } else {
             return FALCON_ERR_UNSUPPORTED;
+        }
     } else {
         return FALCON_ERR_UNSUPPORTED;
     }
@@ -102,7 +106,9 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
     // whole chunks on the chunk paths), then the per-chunk operators
     const int T = a->seqlen;
     size_t off = 0;
-    if (p->path != Path::kEmpty) {
+    if (p->path == Path::kChunkF1Fused) {
+        p->nchunks = (T + kChunk - 1) / kChunk;
+    } else if (p->path != Path::kEmpty) {
         const bool chunked = p->path != Path::kRecurrent;
         p->nchunks = chunked ? (T + kChunk - 1) / kChunk : 0;
         p->Tpad = chunked ? p->nchunks * kChunk : T;

@@ -16,6 +16,7 @@ enum class Path : int {
     kChunkF1 = 2,    // chunk-parallel Falcon-1
     kChunkA = 3,     // chunk-parallel Falcon-1A / Falcon-3A (scalar-decay writes)
     kChunkF2 = 4,    // chunk-parallel Falcon-2
+    kChunkF1Fused = 5,  // chunk-parallel Falcon-1, bf16, one fused kernel
 };
 
 struct Plan {
@@ -41,6 +42,7 @@ struct Plan {
     void *o = nullptr;
 
     // workspace carve-up (offsets in bytes from the workspace base)
+    int slice = 0;           // value columns per workgroup of the fused kernel
     bool feat_f32 = true;    // storage type of the normalised features
     size_t off_xn = 0, off_qn = 0, off_eta = 0, off_alpha = 0;
     size_t off_chunk = 0;    // chunk-path operators

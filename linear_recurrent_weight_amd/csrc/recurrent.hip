@@ -198,7 +198,7 @@ void launch_rec_variant(const RecurrentArgs &a, dim3 grid, hipStream_t s) {
 
 }  // namespace
 
-void launch_recurrent(const RecurrentArgs &a, bool io_bf16, hipStream_t s) {
+void launch_recurrent(const RecurrentArgs &a, bool io_bf16, hipStream_t s, Marks *m) {
     const int waves = a.BH * (a.dv / kCpw);
     dim3 grid((waves + 3) / 4);
     const bool two_rows = a.dk > 64;
@@ -209,6 +209,7 @@ void launch_recurrent(const RecurrentArgs &a, bool io_bf16, hipStream_t s) {
         if (two_rows) launch_rec_variant<float, 2>(a, grid, s);
         else launch_rec_variant<float, 1>(a, grid, s);
     }
+    m->mark(s);
 }
 
 }  // namespace falcon

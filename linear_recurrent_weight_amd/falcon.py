@@ -45,7 +45,7 @@ class FalconFwdArgsC(ctypes.Structure):
 
 
 EXPORTS = ("falcon_fwd", "falcon_fwd_validate", "falcon_fwd_workspace_size",
-           "falcon_status_str", "falcon_abi_version")
+           "falcon_fwd_profile", "falcon_kernel_name", "falcon_status_str", "falcon_abi_version")
 
 _lib = None
 
@@ -67,6 +67,11 @@ def load_library(path: Optional[os.PathLike] = None) -> ctypes.CDLL:
     lib.falcon_fwd_workspace_size.restype = ctypes.c_size_t
     lib.falcon_status_str.argtypes = [ctypes.c_int]
     lib.falcon_status_str.restype = ctypes.c_char_p
+    lib.falcon_fwd_profile.argtypes = [ctypes.POINTER(FalconFwdArgsC), ctypes.c_void_p,
+                                       ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+    lib.falcon_fwd_profile.restype = ctypes.c_int
+    lib.falcon_kernel_name.argtypes = [ctypes.POINTER(FalconFwdArgsC), ctypes.c_int]
+    lib.falcon_kernel_name.restype = ctypes.c_char_p
     lib.falcon_abi_version.argtypes = []
     lib.falcon_abi_version.restype = ctypes.c_int
     if lib.falcon_abi_version() != ABI_VERSION:

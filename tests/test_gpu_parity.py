@@ -213,3 +213,39 @@ def test_deterministic():
     o1, s1 = gu.run_gpu(w, dev)
     o2, s2 = gu.run_gpu(w, dev)
     assert torch.equal(o1, o2) and torch.equal(s1.S, s2.S)
+
+
+# -- fused bf16 Falcon-1 kernel (d_k = 64) ------------------------------------
+
+@pytest.mark.parametrize("slice_", ["32", "64"])
+@pytest.mark.parametrize("dv", [32, 64, 128])
+@pytest.mark.parametrize("T", [1, 64, 130, 300])
+def test_chunk_f1_fused_shapes(monkeypatch, slice_, dv, T):
+    monkeypatch.setenv("FALCON_F1_SLICE", slice_)
+    check(gu.small("F1", "bf16", B=2, H=5, T=T, dk=64, dv=dv, chunk=64, seed=T + dv))
+
+
+@pytest.mark.parametrize("slice_", ["32", "64"])
+def test_c2_fused_both_slice_widths(monkeypatch, slice_):
+    monkeypatch.setenv("FALCON_F1_SLICE", slice_)
+    check(WORKLOADS["c2"], heads=gu.sample_heads(WORKLOADS["c2"], 8))
+
+
+@pytest.mark.parametrize("split", [64, 100])
+def test_chunk_f1_fused_continuation(split):
+    """bf16 fused path: two calls carrying the state match the oracle run of
+    the whole sequence."""
+    import torch
+    w = gu.small("F1", "bf16", B=2, H=3, T=300, dk=64, dv=64, chunk=64, seed=13)
+    inp = gu.make(w)
+    dev = gu.to_device(inp, w)
+    a = {k: v[:, :, :split].contiguous() for k, v in dev.items()}
+    b = {k: v[:, :, split:].contiguous() for k, v in dev.items()}
+    o1, st1 = gu.run_gpu(w.with_(seqlen=split), a)
+    o2, st2 = gu.run_gpu(w.with_(seqlen=300 - split), b, state=st1)
+    heads = np.arange(6)
+    o_ref, st_ref = gu.oracle_heads(w, inp, heads)
+    eo, es = gu.compare(w, heads, torch.cat([o1, o2], 2), st2, o_ref, st_ref)
+    assert eo <= gu.TOL_BF16 and es <= gu.TOL_BF16, (eo, es)
+    assert torch.allclose(st2.x_next, torch.from_numpy(st_ref.x_next.reshape(2, 3, 64)).float().cuda(),
+                          rtol=1e-5, atol=1e-5)
