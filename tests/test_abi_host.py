@@ -133,7 +133,7 @@ def test_output_may_not_alias_inputs(lib):
 
 
 def test_workspace_rules(lib):
-    a = args()
+    a = args(dtype="f32")
     n = wsize(lib, a)
     assert n > 0
     assert validate(lib, a) == fb.ERR_WORKSPACE          # missing
@@ -147,11 +147,14 @@ def test_workspace_rules(lib):
 
 
 def test_workspace_grows_with_problem(lib):
-    small = wsize(lib, args(seqlen=64))
-    big = wsize(lib, args(seqlen=1024))
+    small = wsize(lib, args(seqlen=64, dtype="f32"))
+    big = wsize(lib, args(seqlen=1024, dtype="f32"))
     assert 0 < small < big
     # ragged lengths round up to whole chunks on the chunk path
-    assert wsize(lib, args(seqlen=65)) == wsize(lib, args(seqlen=128))
+    assert wsize(lib, args(seqlen=65, dtype="f32")) == wsize(lib, args(seqlen=128, dtype="f32"))
+    # the fused bf16 Falcon-1 kernel (d_k = 64) keeps everything on chip
+    assert wsize(lib, args(seqlen=1024)) == 0
+    assert validate(lib, args(seqlen=1024)) == fb.OK
     # a malformed request reports 0 bytes
     assert wsize(lib, args(dk=48)) == 0
 
