@@ -35,9 +35,17 @@ def algorithmic_bytes(w) -> int:
 
 
 def algorithmic_flops(w) -> int:
-    """Single-solve chunk form, triangle-aware: 2C(dk+dv) + 6 dk dv per token
-    (Falcon-1)."""
-    return w.batch * w.heads * w.seqlen * (2 * w.chunk * (w.dk + w.dv) + 6 * w.dk * w.dv)
+    """Per-token work of the chunk form, triangle-aware: Falcon-1
+    2C(dk+dv) + 6 dk dv (single residual solve); Falcon-2 2C dk + 3C dv +
+    6 dk dv; Falcon-1A / 3A C dk + C dv + 4 dk dv (window terms are lower
+    order)."""
+    C = w.chunk or 64
+    per = {"F1": 2 * C * (w.dk + w.dv) + 6 * w.dk * w.dv,
+           "F2": 2 * C * w.dk + 3 * C * w.dv + 6 * w.dk * w.dv,
+           "F3": 2 * C * (w.dk + w.dv) * w.window + 6 * w.dk * w.dv,
+           "F1A": C * (w.dk + w.dv) + 4 * w.dk * w.dv,
+           "F3A": C * (w.dk + w.dv) + 4 * w.dk * w.dv}[w.variant]
+    return w.batch * w.heads * w.seqlen * per
 
 
 def cpu_baseline(w, inp, min_seconds: float):

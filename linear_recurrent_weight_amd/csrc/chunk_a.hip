@@ -1,0 +1,487 @@
+// Chunk-parallel Falcon-1A / Falcon-3A forward (inner-product writes with a
+// scalar ridge carry; summary §4.3, §4.5, §4.6 "Parallel (Attention) Form of
+// Mini-batch Inner Product Update", §D.1 "Mask Identities and Chunk-Local
+// Evaluation"; Falcon-1A is the window-1 case).
+//
+// Per token s the write is  S_s = gamma_s S_{s-1} + w_s sum_{j in I_s} x_j y_j^T,
+// w_s = eta_s / B_s, I_s the last min(W, #pairs) pairs.  Within a chunk of 64
+// tokens (chunk-local log-prefix b, restarted at 0) this unrolls to
+//     o_t = e^{b_t} S_0^T qh_t + sum_j M_tj (qh_t . x_j) y_j,
+//     S_C = e^{b_C} S_0 + sum_j M_{C,j} x_j y_j^T,
+//     M_tj = sum_{s = max(j,0)}^{min(t, j+W-1)} e^{b_t - b_s} w_s,
+// where j runs over the W-1 halo pairs before the chunk and the chunk's own
+// pairs.  Each column of M obeys the first-order recurrence
+//     M_tj = gamma_t M_{t-1,j} + [max(j,0) <= t <= j+W-1] w_t,
+// so every decay factor is a product of carries in (0, 1] and nothing can
+// overflow however strong the ridge.
+//
+// The sequence of a head is cut into segments of G chunks:
+//   a_segment  (parallel over segments): features (QK-RMSNorm, key shift),
+//              step scalars (window statistic lambda_max for Falcon-3A), and
+//              the segment's aggregate write D_g = sum over its chunks of the
+//              decayed chunk writes (MFMA), with its carry Gamma_g;
+//   a_segscan  (parallel over state entries): S_{g+1} = Gamma_g S_g + D_g;
+//   a_output   (parallel over segments): walks the segment's chunks from its
+//              entry state, with S^T held in MFMA accumulators, and writes o.
+#include "chunk_layout.h"
+#include "kernels.h"
+#include "mma.h"
+
+namespace falcon {
+namespace {
+
+constexpr int C = kChunk;
+constexpr int HMAX = FALCON_MAX_WINDOW - 1;  // halo pairs
+constexpr int KP = 96;                       // pair slots per chunk (64 + halo, padded)
+
+// pair p of a chunk starting at c0 is token tau = c0 - halo + p
+struct PairSrc {
+    const void *k, *v;
+    const float *xnext_in, *tailx_in, *taily_in;
+    int T, dk, dv, halo_state, n_tail_in;   // halo_state = W - 1 of the state layout
+};
+
+// features of the pairs [0, np) of a chunk into an fp32 LDS array xf[p][ldx]
+template <class E>
+__device__ void load_pair_features(float *xf, int ldx, const PairSrc &s, int bh, int c0, int halo, int np,
+                                   float eps_rms, int phi) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int dk = s.dk;
+    const E *k = static_cast<const E *>(s.k) + size_t(bh) * s.T * dk;
+    // one wave per row, lanes over features
+    for (int p = wave; p < np; p += 4) {
+        const int tau = c0 - halo + p;
+        float x[2] = {0.f, 0.f};
+        bool from_k = false;
+        for (int m = 0; m < 2; ++m) {
+            const int e = lane + 64 * m;
+            if (e < dk) {
+                if (tau >= 1 && tau < s.T) {
+                    x[m] = ld(k, size_t(tau - 1) * dk + e);
+                } else if (tau == 0) {
+                    x[m] = s.xnext_in ? s.xnext_in[size_t(bh) * dk + e] : 0.f;
+                } else if (tau < 0 && tau >= -s.n_tail_in) {
+                    x[m] = s.tailx_in[(size_t(bh) * s.halo_state + tau + s.halo_state) * dk + e];
+                }
+            }
+        }
+        from_k = tau >= 1 && tau < s.T;
+        float ss = wave_sum(x[0] * x[0] + x[1] * x[1]);
+        const float sc = from_k ? phi_scale(ss, dk, eps_rms, phi) : 1.f;
+        for (int m = 0; m < 2; ++m) {
+            const int e = lane + 64 * m;
+            if (e < dk) xf[p * ldx + e] = x[m] * sc;
+        }
+    }
+}
+
+// values of the pairs, transposed into yt[j][p] (storage type E); pairs past
+// np (padding) are zero
+template <class E>
+__device__ void load_pair_values_t(E *yt, int ldy, const PairSrc &s, int bh, int c0, int halo, int np) {
+    const int tid = threadIdx.x;
+    const int dv = s.dv;
+    const E *v = static_cast<const E *>(s.v) + size_t(bh) * s.T * dv;
+    for (int idx = tid; idx < KP * dv; idx += 256) {
+        const int p = idx / dv, j = idx % dv;
+        const int tau = c0 - halo + p;
+        float y = 0.f;
+        if (p < np) {
+            if (tau >= 0 && tau < s.T)
+                y = ld(v, size_t(tau) * dv + j);
+            else if (tau < 0 && tau >= -s.n_tail_in)
+                y = s.taily_in[(size_t(bh) * s.halo_state + tau + s.halo_state) * dv + j];
+        }
+        st(yt, size_t(j) * ldy + p, y);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// a_segment
+// ---------------------------------------------------------------------------
+template <class E, int DK, int DV>
+__global__ __launch_bounds__(256) void a_segment(ChunkAArgs a) {
+    constexpr int PD = Pad<E>::v;
+    constexpr int LDX = DK + 1;         // fp32 feature rows
+    constexpr int LDT = KP + PD;        // [.][pair] rows
+    constexpr int NPM = C + HMAX;       // max pairs per chunk
+    __shared__ float XF[NPM * LDX];
+    __shared__ __align__(16) E XT[DK * LDT];     // (diag(coef) X)^T  [d][p]
+    __shared__ __align__(16) E YT[DV * LDT];     // Y^T               [j][p]
+    __shared__ float band[NPM * 8];
+    __shared__ float mu_s[C], ew_s[C], gam_s[C], coef[KP];
+    __shared__ float bC_s;
+
+    const int seg = blockIdx.x, bh = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int T = a.T, dv = a.dv, W = a.window, halo = W - 1;
+    const int np = C + halo;
+    PairSrc src{a.k, a.v, a.xnext_in, a.tailx_in, a.taily_in, T, DK, dv, halo, a.n_tail_in};
+
+    // aggregate write of the segment, transposed: D^T[j][d] in accumulators.
+    // tile (jt, dt) with jt < dv/16, dt < DK/16, spread over the 4 waves
+    constexpr int MAXT = (DV / 16 * DK / 16 + 3) / 4;   // state tiles per wave
+    constexpr int njt = DV / 16, ntiles = njt * (DK / 16);
+    f32x4 acc[MAXT];
+#pragma unroll
+    for (int m = 0; m < MAXT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float bsum = 0.f;
+
+    const int c_begin = seg * a.seg_chunks;
+    const int c_end = min(a.nchunks, c_begin + a.seg_chunks);
+    for (int c = c_begin; c < c_end; ++c) {
+        const int c0 = c * C;
+        load_pair_features<E>(XF, LDX, src, bh, c0, halo, np, a.eps_rms, a.phi);
+        load_pair_values_t<E>(YT, LDT, src, bh, c0, halo, np);
+        __syncthreads();
+        // window statistic / feature energy of the chunk's own tokens
+        if (W > 1) {
+            for (int idx = tid; idx < np * W; idx += 256) {
+                const int r = idx / W, d = idx % W;
+                float s = 0.f;
+                if (r - d >= 0) {
+                    for (int e = 0; e < DK; ++e) s += XF[r * LDX + e] * XF[(r - d) * LDX + e];
+                }
+                band[r * 8 + d] = s;
+            }
+            __syncthreads();
+            if (tid < C) {
+                const int r = tid + halo;
+                float g[8][8];
+#pragma unroll
+                for (int aa = 0; aa < 8; ++aa)
+#pragma unroll
+                    for (int bb = 0; bb < 8; ++bb) {
+                        float v = 0.f;
+                        if (aa < W && bb < W) {
+                            const int lo = aa < bb ? aa : bb, df = aa < bb ? bb - aa : aa - bb;
+                            v = band[(r - lo) * 8 + df];
+                        }
+                        g[aa][bb] = v;
+                    }
+                const long long pairs = (long long)a.n_tail_in + c0 + tid + 1;
+                const int bt = pairs < W ? int(pairs) : W;
+                mu_s[tid] = psd_lambda_max(g, W) / float(bt);
+                ew_s[tid] = 1.f / float(bt);
+            }
+        } else if (tid < C) {
+            float s = 0.f;
+            for (int e = 0; e < DK; ++e) s += XF[(tid + halo) * LDX + e] * XF[(tid + halo) * LDX + e];
+            mu_s[tid] = s;
+            ew_s[tid] = 1.f;
+        }
+        __syncthreads();
+        // step scalars; log-prefix of the chunk
+        if (wave == 0) {
+            const int t = c0 + lane;
+            float eta = 0.f, alpha = 0.f;
+            const bool noop = t >= T || (t == 0 && a.fresh);
+            if (!noop) {
+                const float lam = a.lambda[size_t(bh) * T + t];
+                eta = step_eta(a.beta[size_t(bh) * T + t], mu_s[lane] + lam + a.eps);
+                alpha = step_alpha(eta, lam, a.eps_gamma);
+            }
+            const float lg = log1pf(-alpha);
+            const float ew = eta * ew_s[lane];
+            ew_s[lane] = ew;
+            gam_s[lane] = 1.f - alpha;
+            a.etaw[size_t(bh) * a.Tpad + t] = ew;
+            a.lg[size_t(bh) * a.Tpad + t] = lg;
+            const float b = wave_inclusive_scan(lg);
+            if (lane == 63) bC_s = b;
+        }
+        __syncthreads();
+        // coefficients of the chunk write: coef_p = M_{63, p}
+        if (tid < KP) {
+            const int p = tid, j = p - halo;
+            float m = 0.f;
+            if (p < np) {
+                for (int t = 0; t < C; ++t) {
+                    const bool in = t >= (j > 0 ? j : 0) && t <= j + halo;
+                    m = gam_s[t] * m + (in ? ew_s[t] : 0.f);
+                }
+            }
+            coef[p] = m;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < KP * DK; idx += 256) {
+            const int p = idx / DK, d = idx % DK;
+            st(XT, size_t(d) * LDT + p, p < np ? coef[p] * XF[p * LDX + d] : 0.f);
+        }
+        __syncthreads();
+        // D^T = e^{b_C} D^T + Y^T diag(coef) X
+        const float gC = expf(bC_s);
+        bsum += bC_s;
+#pragma unroll
+        for (int m = 0; m < MAXT; ++m) {
+            const int tile = wave + 4 * m;
+            if (tile < ntiles) {
+                const int jt = tile % njt, dt = tile / njt;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[m][r] *= gC;
+                acc[m] = Mma<E>::run(acc[m], YT + 16 * jt * LDT, LDT, XT + 16 * dt * LDT, LDT, 0, KP);
+            }
+        }
+        // boundary state out from the last chunk of the sequence
+        if (c == a.nchunks - 1 && halo > 0 && a.tailx_out) {
+            const int n_out = a.n_tail_out;
+            for (int idx = tid; idx < halo * DK; idx += 256) {
+                const int sl = idx / DK, e = idx % DK;
+                const int tau = T - halo + sl;
+                const int p = tau - (c0 - halo);
+                a.tailx_out[(size_t(bh) * halo + sl) * DK + e] = sl >= halo - n_out ? XF[p * LDX + e] : 0.f;
+            }
+            for (int idx = tid; idx < halo * dv; idx += 256) {
+                const int sl = idx / dv, e = idx % dv;
+                const int tau = T - halo + sl;
+                const int p = tau - (c0 - halo);
+                a.taily_out[(size_t(bh) * halo + sl) * dv + e] =
+                    sl >= halo - n_out ? ld(YT, size_t(e) * LDT + p) : 0.f;
+            }
+        }
+        __syncthreads();
+    }
+    // segment aggregate (fp32, [j][d]) and carry
+    float *Dg = a.Dseg + (size_t(bh) * a.nseg + seg) * dv * DK;
+#pragma unroll
+    for (int m = 0; m < MAXT; ++m) {
+        const int tile = wave + 4 * m;
+        if (tile < ntiles) {
+            const int jt = tile % njt, dt = tile / njt;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = 16 * jt + 4 * (lane >> 4) + r, d = 16 * dt + (lane & 15);
+                Dg[size_t(j) * DK + d] = acc[m][r];
+            }
+        }
+    }
+    if (tid == 0) a.Gseg[size_t(bh) * a.nseg + seg] = expf(bsum);
+    // x_next = phi(k_{T-1}) from the segment holding the last token
+    if (c_end == a.nchunks && wave == 0 && a.xnext_out) {
+        const E *k = static_cast<const E *>(a.k) + size_t(bh) * T * DK;
+        float x[2] = {0.f, 0.f};
+        for (int m = 0; m < 2; ++m)
+            if (lane + 64 * m < DK) x[m] = ld(k, size_t(T - 1) * DK + lane + 64 * m);
+        const float sc = phi_scale(wave_sum(x[0] * x[0] + x[1] * x[1]), DK, a.eps_rms, a.phi);
+        for (int m = 0; m < 2; ++m)
+            if (lane + 64 * m < DK) a.xnext_out[size_t(bh) * DK + lane + 64 * m] = x[m] * sc;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// a_segscan: entry state of every segment
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void a_segscan(ChunkAArgs a) {
+    const int bh = blockIdx.x;
+    const int e = blockIdx.y * 256 + threadIdx.x;
+    const int dk = a.dk, dv = a.dv;
+    if (e >= dk * dv) return;
+    const int j = e / dk, d = e % dk;
+    float S = a.S_in ? a.S_in[(size_t(bh) * dk + d) * dv + j] : 0.f;
+    const size_t stride = size_t(dk) * dv;
+    const float *Dg = a.Dseg + size_t(bh) * a.nseg * stride + e;
+    float *Se = a.Sseg + size_t(bh) * a.nseg * stride + e;
+    const float *Gg = a.Gseg + size_t(bh) * a.nseg;
+    for (int g = 0; g < a.nseg; ++g) {
+        Se[g * stride] = S;
+        S = Gg[g] * S + Dg[g * stride];
+    }
+    if (a.S_out) a.S_out[(size_t(bh) * dk + d) * dv + j] = S;
+}
+
+// ---------------------------------------------------------------------------
+// a_output
+// ---------------------------------------------------------------------------
+template <class E> struct PBuf;     // bf16: separate scores buffer; fp32: scores in place
+template <> struct PBuf<bf16_t> { static constexpr bool separate = true; };
+template <> struct PBuf<float> { static constexpr bool separate = false; };
+
+template <class E, int DK, int DV>
+__global__ __launch_bounds__(256) void a_output(ChunkAArgs a) {
+    constexpr int PD = Pad<E>::v;
+    constexpr int LDK = DK + PD;        // [.][d] rows
+    constexpr int LDT = KP + PD;        // [.][pair] rows
+    constexpr int LDF = KP + 1;         // fp32 score rows
+    constexpr int NPM = C + HMAX;
+    __shared__ float XF[NPM * (DK + 1)];                 // pair features (fp32)
+    __shared__ __align__(16) E XE[KP * LDK];             // pair features [p][d]
+    __shared__ __align__(16) E XT[DK * LDT];             // (diag(coef) X)^T [d][p]
+    __shared__ __align__(16) E QE[C * LDK];              // query features [t][d]
+    __shared__ __align__(16) E YT[DV * LDT];             // Y^T [j][p]
+    __shared__ __align__(16) E ST[DV * LDK];             // S^T copy [j][d]
+    __shared__ __align__(16) float PF[C * LDF];          // scores, then decayed scores
+    __shared__ __align__(16) E PE[PBuf<E>::separate ? C * LDT : 1];
+    __shared__ float ew_s[C], gam_s[C], g_s[C], coef[KP];
+    __shared__ float bC_s;
+
+    const int seg = blockIdx.x, bh = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int T = a.T, dv = a.dv, W = a.window, halo = W - 1;
+    const int np = C + halo;
+    PairSrc src{a.k, a.v, a.xnext_in, a.tailx_in, a.taily_in, T, DK, dv, halo, a.n_tail_in};
+    const E *q = static_cast<const E *>(a.q) + size_t(bh) * T * DK;
+    E *o = static_cast<E *>(a.o) + size_t(bh) * T * dv;
+
+    // entry state S^T[j][d] of this segment in accumulators, tiles as in a_segment
+    constexpr int MAXT = (DV / 16 * DK / 16 + 3) / 4;
+    constexpr int njt = DV / 16, ntiles = njt * (DK / 16);
+    f32x4 acc[MAXT];
+    const float *Se = a.Sseg + (size_t(bh) * a.nseg + seg) * dv * DK;
+#pragma unroll
+    for (int m = 0; m < MAXT; ++m) {
+        const int tile = wave + 4 * m;
+        if (tile < ntiles) {
+            const int jt = tile % njt, dt = tile / njt;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = 16 * jt + 4 * (lane >> 4) + r, d = 16 * dt + (lane & 15);
+                acc[m][r] = Se[size_t(j) * DK + d];
+                st(ST, size_t(j) * LDK + d, acc[m][r]);
+            }
+        }
+    }
+
+    const int c_begin = seg * a.seg_chunks;
+    const int c_end = min(a.nchunks, c_begin + a.seg_chunks);
+    for (int c = c_begin; c < c_end; ++c) {
+        const int c0 = c * C;
+        load_pair_features<E>(XF, DK + 1, src, bh, c0, halo, np, a.eps_rms, a.phi);
+        load_pair_values_t<E>(YT, LDT, src, bh, c0, halo, np);
+        // query features: one wave per row
+        for (int t = wave; t < C; t += 4) {
+            float y[2] = {0.f, 0.f};
+            for (int m = 0; m < 2; ++m)
+                if (lane + 64 * m < DK && c0 + t < T) y[m] = ld(q, size_t(c0 + t) * DK + lane + 64 * m);
+            const float sc = phi_scale(wave_sum(y[0] * y[0] + y[1] * y[1]), DK, a.eps_rms, a.phi);
+            for (int m = 0; m < 2; ++m)
+                if (lane + 64 * m < DK) st(QE, size_t(t) * LDK + lane + 64 * m, y[m] * sc);
+        }
+        if (wave == 0) {
+            const int t = c0 + lane;
+            const float ew = a.etaw[size_t(bh) * a.Tpad + t];
+            const float lg = a.lg[size_t(bh) * a.Tpad + t];
+            ew_s[lane] = ew;
+            gam_s[lane] = expf(lg);
+            const float b = wave_inclusive_scan(lg);
+            g_s[lane] = expf(b);
+            if (lane == 63) bC_s = b;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < KP * DK; idx += 256) {
+            const int p = idx / DK, d = idx % DK;
+            st(XE, size_t(p) * LDK + d, p < np ? XF[p * (DK + 1) + d] : 0.f);
+        }
+        __syncthreads();
+        // scores Qh X_ext^T (4 token tiles x 6 pair tiles)
+        for (int tile = wave; tile < 4 * (KP / 16); tile += 4) {
+            const int tt = tile % 4, pt = tile / 4;
+            f32x4 s = Mma<E>::run(f32x4{0.f, 0.f, 0.f, 0.f}, QE + 16 * tt * LDK, LDK, XE + 16 * pt * LDK, LDK,
+                                  0, DK);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) PF[(16 * tt + 4 * (lane >> 4) + r) * LDF + 16 * pt + (lane & 15)] = s[r];
+        }
+        __syncthreads();
+        // mask by the column recurrence; coefficients of the chunk write
+        if (tid < KP) {
+            const int p = tid, j = p - halo;
+            float m = 0.f;
+            for (int t = 0; t < C; ++t) {
+                const bool in = p < np && t >= (j > 0 ? j : 0) && t <= j + halo;
+                m = gam_s[t] * m + (in ? ew_s[t] : 0.f);
+                const float pv = PF[t * LDF + p] * m;
+                if constexpr (PBuf<E>::separate)
+                    st(PE, size_t(t) * LDT + p, pv);
+                else
+                    PF[t * LDF + p] = pv;
+            }
+            coef[p] = m;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < KP * DK; idx += 256) {
+            const int p = idx / DK, d = idx % DK;
+            st(XT, size_t(d) * LDT + p, p < np ? coef[p] * XF[p * (DK + 1) + d] : 0.f);
+        }
+        __syncthreads();
+        // outputs: O^T = (S^T Qh^T) diag(Gamma) + Y^T P^T;  tiles (jt, token tile)
+        const E *Pm;
+        int ldp;
+        if constexpr (PBuf<E>::separate) {
+            Pm = PE;
+            ldp = LDT;
+        } else {
+            Pm = reinterpret_cast<const E *>(PF);
+            ldp = LDF;
+        }
+        for (int tile = wave; tile < njt * 4; tile += 4) {
+            const int jt = tile % njt, tt = tile / njt;
+            f32x4 r0 = Mma<E>::run(f32x4{0.f, 0.f, 0.f, 0.f}, ST + 16 * jt * LDK, LDK, QE + 16 * tt * LDK, LDK,
+                                   0, DK);
+            const int t = 16 * tt + (lane & 15);
+            const float gt = g_s[t];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) r0[r] *= gt;
+            r0 = Mma<E>::run(r0, YT + 16 * jt * LDT, LDT, Pm + 16 * tt * ldp, ldp, 0, KP);
+            if (c0 + t < T) {
+                E *dst = o + size_t(c0 + t) * dv + 16 * jt + 4 * (lane >> 4);
+                st4(dst, r0);
+            }
+        }
+        // state: S^T = e^{b_C} S^T + Y^T diag(coef) X
+        const float gC = expf(bC_s);
+#pragma unroll
+        for (int m = 0; m < MAXT; ++m) {
+            const int tile = wave + 4 * m;
+            if (tile < ntiles) {
+                const int jt = tile % njt, dt = tile / njt;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[m][r] *= gC;
+                acc[m] = Mma<E>::run(acc[m], YT + 16 * jt * LDT, LDT, XT + 16 * dt * LDT, LDT, 0, KP);
+            }
+        }
+        __syncthreads();   // every read of ST / YT / XT of this chunk is done
+#pragma unroll
+        for (int m = 0; m < MAXT; ++m) {
+            const int tile = wave + 4 * m;
+            if (tile < ntiles) {
+                const int jt = tile % njt, dt = tile / njt;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    st(ST, size_t(16 * jt + 4 * (lane >> 4) + r) * LDK + 16 * dt + (lane & 15), acc[m][r]);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <class E, int DK, int DV>
+void launch_t(const ChunkAArgs &a, hipStream_t s, Marks *m) {
+    a_segment<E, DK, DV><<<dim3(a.nseg, a.BH), 256, 0, s>>>(a);
+    m->mark(s);
+    a_segscan<<<dim3(a.BH, (a.dk * a.dv + 255) / 256), 256, 0, s>>>(a);
+    m->mark(s);
+    a_output<E, DK, DV><<<dim3(a.nseg, a.BH), 256, 0, s>>>(a);
+    m->mark(s);
+}
+
+template <class E, int DK>
+void launch_dv(const ChunkAArgs &a, hipStream_t s, Marks *m) {
+    if (a.dv == 16) launch_t<E, DK, 16>(a, s, m);
+    else if (a.dv == 32) launch_t<E, DK, 32>(a, s, m);
+    else launch_t<E, DK, 64>(a, s, m);
+}
+
+}  // namespace
+
+void launch_chunk_a(const ChunkAArgs &a, bool bf16, hipStream_t s, Marks *m) {
+    if (bf16) {
+        if (a.dk == 32) launch_dv<bf16_t, 32>(a, s, m);
+        else launch_dv<bf16_t, 64>(a, s, m);
+    } else {
+        if (a.dk == 32) launch_dv<float, 32>(a, s, m);
+        else launch_dv<float, 64>(a, s, m);
+    }
+}
+
+}  // namespace falcon

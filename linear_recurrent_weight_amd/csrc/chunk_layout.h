@@ -40,4 +40,20 @@ inline int chunk_f1_fused_slice(int bh, int dv) {
     return (bh * (dv / 64) >= 128) ? 64 : 32;
 }
 
+// Falcon-1A / Falcon-3A chunk path: d_k in {32, 64}, d_v in {16, 32, 64}.
+constexpr bool chunk_a_supported(int dk, int dv) {
+    return (dk == 32 || dk == 64) && (dv == 16 || dv == 32 || dv == 64);
+}
+// chunks per segment: enough segments for a few workgroups per compute unit
+inline int chunk_a_segment_chunks(long long bh, int nchunks) {
+    if (const char *e = std::getenv("FALCON_A_SEGMENT")) {   // tuning override: 1..32 chunks
+        const int v = std::atoi(e);
+        if (v >= 1 && v <= 32) return v;
+    }
+    long long g = (bh * nchunks + 639) / 640;
+    if (g < 1) g = 1;
+    if (g > 32) g = 32;
+    return int(g);
+}
+
 }  // namespace falcon

@@ -11,6 +11,7 @@ const char *const kNamesEmpty[] = {"passthrough"};
 const char *const kNamesRecurrent[] = {"feature", "recurrent"};
 const char *const kNamesChunkF1[] = {"feature", "chunk_f1_prep", "chunk_f1_scan"};
 const char *const kNamesChunkF1Fused[] = {"chunk_f1_fused"};
+const char *const kNamesChunkA[] = {"a_segment", "a_segscan", "a_output"};
 
 int run(const falcon_fwd_args *args, void *stream, Marks *m) {
     Plan p;
@@ -41,6 +42,45 @@ int run(const falcon_fwd_args *args, void *stream, Marks *m) {
             pa.taily_out = p.taily_out;
             launch_passthrough(pa, s, m);
         }
+    } else if (p.path == Path::kChunkA) {
+        ChunkAArgs ca{};
+        ca.variant = p.variant;
+        ca.phi = p.phi;
+        ca.BH = p.BH;
+        ca.T = p.T;
+        ca.Tpad = p.Tpad;
+        ca.nchunks = p.nchunks;
+        ca.dk = p.dk;
+        ca.dv = p.dv;
+        ca.window = p.window;
+        ca.fresh = p.fresh ? 1 : 0;
+        ca.n_tail_in = p.n_tail_in;
+        ca.n_tail_out = p.n_tail_out;
+        ca.seg_chunks = p.seg_chunks;
+        ca.nseg = p.nseg;
+        ca.eps = p.eps;
+        ca.eps_gamma = p.eps_gamma;
+        ca.eps_rms = p.eps_rms;
+        ca.q = p.q;
+        ca.k = p.k;
+        ca.v = p.v;
+        ca.beta = p.beta;
+        ca.lambda = p.lambda;
+        ca.xnext_in = p.xnext_in;
+        ca.tailx_in = p.tailx_in;
+        ca.taily_in = p.taily_in;
+        ca.S_in = p.S_in;
+        ca.S_out = p.S_out;
+        ca.xnext_out = p.xnext_out;
+        ca.tailx_out = p.tailx_out;
+        ca.taily_out = p.taily_out;
+        ca.o = p.o;
+        ca.etaw = p.ws_at<float>(p.off_eta);
+        ca.lg = p.ws_at<float>(p.off_alpha);
+        ca.Dseg = p.ws_at<float>(p.off_chunk);
+        ca.Gseg = p.ws_at<float>(p.off_seg_g);
+        ca.Sseg = p.ws_at<float>(p.off_seg_s);
+        launch_chunk_a(ca, p.dtype == FALCON_BF16, s, m);
     } else if (p.path == Path::kChunkF1Fused) {
         F1FusedArgs fa{};
         fa.BH = p.BH;
@@ -167,6 +207,7 @@ extern "C" const char *falcon_kernel_name(const falcon_fwd_args *args, int i) {
         case Path::kRecurrent: return i < 2 ? kNamesRecurrent[i] : nullptr;
         case Path::kChunkF1: return i < 3 ? kNamesChunkF1[i] : nullptr;
         case Path::kChunkF1Fused: return i < 1 ? kNamesChunkF1Fused[i] : nullptr;
+        case Path::kChunkA: return i < 3 ? kNamesChunkA[i] : nullptr;
         default: return nullptr;
     }
 }

@@ -17,6 +17,7 @@
 // exact no-op tokens for the chunk kernels.
 #include "common.h"
 #include "kernels.h"
+#include "lambda_max.h"
 
 namespace falcon {
 namespace {
@@ -25,53 +26,6 @@ constexpr int kTile = 64;
 constexpr int kWmax = FALCON_MAX_WINDOW;
 constexpr int kDmax = 128;
 constexpr int kXStride = kDmax + 1;  // odd stride: row-parallel LDS reads hit distinct banks
-
-// Largest eigenvalue of a symmetric 8x8 matrix by cyclic Jacobi rotations.
-__device__ float sym8_lambda_max(float a[8][8]) {
-    for (int sweep = 0; sweep < 10; ++sweep) {
-        float off = 0.f, diag = 0.f;
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            diag += fabsf(a[p][p]);
-#pragma unroll
-            for (int q = p + 1; q < 8; ++q) off += a[p][q] * a[p][q];
-        }
-        if (off <= 1e-14f * diag * diag || off == 0.f) break;
-#pragma unroll
-        for (int p = 0; p < 7; ++p) {
-#pragma unroll
-            for (int q = p + 1; q < 8; ++q) {
-                const float apq = a[p][q];
-                if (fabsf(apq) <= 1e-30f) continue;
-                const float theta = (a[q][q] - a[p][p]) / (2.f * apq);
-                float t;
-                if (fabsf(theta) > 1e18f) {
-                    t = 0.5f / theta;
-                } else {
-                    t = copysignf(1.f, theta) / (fabsf(theta) + sqrtf(theta * theta + 1.f));
-                }
-                const float c = 1.f / sqrtf(t * t + 1.f);
-                const float s = t * c;
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const float akp = a[k][p], akq = a[k][q];
-                    a[k][p] = c * akp - s * akq;
-                    a[k][q] = s * akp + c * akq;
-                }
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const float apk = a[p][k], aqk = a[q][k];
-                    a[p][k] = c * apk - s * aqk;
-                    a[q][k] = s * apk + c * aqk;
-                }
-            }
-        }
-    }
-    float m = a[0][0];
-#pragma unroll
-    for (int p = 1; p < 8; ++p) m = fmaxf(m, a[p][p]);
-    return fmaxf(m, 0.f);
-}
 
 template <class Ein, class Ef>
 __global__ __launch_bounds__(256) void feature_kernel(FeatureArgs a) {
@@ -197,7 +151,7 @@ __global__ __launch_bounds__(256) void feature_kernel(FeatureArgs a) {
             const int t = t0 + i;
             const long long pairs = (long long)a.n_tail_in + t + 1;
             const int bt = pairs < W ? int(pairs) : W;
-            mu_s[i] = sym8_lambda_max(m) / float(bt);
+            mu_s[i] = psd_lambda_max(m, W) / float(bt);
         }
         __syncthreads();
     }

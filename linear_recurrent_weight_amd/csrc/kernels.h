@@ -70,10 +70,26 @@ struct F1FusedArgs {
     void *o;
 };
 
+struct ChunkAArgs {
+    int variant, phi, BH, T, Tpad, nchunks, dk, dv, window, fresh, n_tail_in, n_tail_out;
+    int seg_chunks, nseg;    // chunks per segment, segments per head
+    float eps, eps_gamma, eps_rms;
+    const void *q, *k, *v;
+    const float *beta, *lambda;
+    const float *xnext_in, *tailx_in, *taily_in;
+    const float *S_in;
+    float *S_out, *xnext_out, *tailx_out, *taily_out;
+    void *o;
+    float *etaw, *lg;        // [BH, Tpad] eta_t / B_t and log gamma_t
+    float *Dseg, *Gseg;      // [BH, nseg, dv, dk] segment writes, [BH, nseg] carries
+    float *Sseg;             // [BH, nseg, dv, dk] segment entry states (transposed)
+};
+
 void launch_features(const FeatureArgs &a, bool in_bf16, bool feat_bf16, hipStream_t s, Marks *m);
 void launch_passthrough(const PassArgs &a, hipStream_t s, Marks *m);
 void launch_recurrent(const RecurrentArgs &a, bool io_bf16, hipStream_t s, Marks *m);
 void launch_chunk_f1(const ChunkF1Args &a, bool bf16, hipStream_t s, Marks *m);
 void launch_chunk_f1_fused(const F1FusedArgs &a, int ds, hipStream_t s, Marks *m);
+void launch_chunk_a(const ChunkAArgs &a, bool bf16, hipStream_t s, Marks *m);
 
 }  // namespace falcon

@@ -1,0 +1,57 @@
+// MFMA tile helpers for the chunk kernels (gfx950, wave64).
+#pragma once
+
+#include "common.h"
+#include "lambda_max.h"
+
+namespace falcon {
+
+// One 16x16 output tile: acc += A[16 x K] * B[K x 16].  A is row-major with k
+// contiguous (row stride lda); B is given transposed, Bt[16 x K] with k
+// contiguous (row stride ldb).  Result lane layout: acc[r] holds row
+// 4*(lane/16)+r, column lane%16.  bf16 uses v_mfma_f32_16x16x32_bf16 (k step
+// 32), fp32 uses v_mfma_f32_16x16x4_f32 (k step 4).
+template <class E> struct Mma;
+
+template <> struct Mma<bf16_t> {
+    static constexpr int KS = 32;
+    __device__ static f32x4 run(f32x4 acc, const bf16_t *A, int lda, const bf16_t *Bt, int ldb, int kbeg,
+                                int kend) {
+        const int lane = threadIdx.x & 63;
+        const int row = lane & 15, kq = 8 * (lane >> 4);
+        for (int k0 = kbeg; k0 < kend; k0 += KS) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(A + row * lda + k0 + kq);
+            const bf16x8 b = *reinterpret_cast<const bf16x8 *>(Bt + row * ldb + k0 + kq);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+        }
+        return acc;
+    }
+};
+
+template <> struct Mma<float> {
+    static constexpr int KS = 4;
+    __device__ static f32x4 run(f32x4 acc, const float *A, int lda, const float *Bt, int ldb, int kbeg,
+                                int kend) {
+        const int lane = threadIdx.x & 63;
+        const int row = lane & 15, kq = lane >> 4;
+        for (int k0 = kbeg; k0 < kend; k0 += KS) {
+            const float a = A[row * lda + k0 + kq];
+            const float b = Bt[row * ldb + k0 + kq];
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+        }
+        return acc;
+    }
+};
+
+// LDS row padding (elements) that keeps bf16 rows 16-byte aligned
+template <class E> struct Pad;
+template <> struct Pad<bf16_t> { static constexpr int v = 8; };
+template <> struct Pad<float> { static constexpr int v = 4; };
+
+template <class E>
+__device__ __forceinline__ void st4(E *p, const f32x4 &v) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) st(p, r, v[r]);
+}
+
+}  // namespace falcon

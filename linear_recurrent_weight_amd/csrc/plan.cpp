@@ -78,6 +78,8 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
             p->slice = chunk_f1_fused_slice(a->batch * a->heads, a->dv);
         } else if (var == FALCON_V1 && chunk_f1_supported(a->dk, a->dv)) {
             p->path = Path::kChunkF1;
+        } else if ((var == FALCON_V1A || var == FALCON_V3A) && chunk_a_supported(a->dk, a->dv)) {
+            p->path = Path::kChunkA;
         } else {
             return FALCON_ERR_UNSUPPORTED;
         }
@@ -108,6 +110,18 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
     size_t off = 0;
     if (p->path == Path::kChunkF1Fused) {
         p->nchunks = (T + kChunk - 1) / kChunk;
+    } else if (p->path == Path::kChunkA) {
+        p->nchunks = (T + kChunk - 1) / kChunk;
+        p->Tpad = p->nchunks * kChunk;
+        p->seg_chunks = chunk_a_segment_chunks(bh, p->nchunks);
+        p->nseg = (p->nchunks + p->seg_chunks - 1) / p->seg_chunks;
+        const size_t rows = static_cast<size_t>(bh) * p->Tpad;
+        const size_t st = static_cast<size_t>(bh) * p->nseg * a->dk * a->dv * 4;
+        p->off_eta = off; off = align_up(off + rows * 4);       // eta_t / B_t
+        p->off_alpha = off; off = align_up(off + rows * 4);     // log gamma_t
+        p->off_chunk = off; off = align_up(off + st);           // segment writes
+        p->off_seg_g = off; off = align_up(off + static_cast<size_t>(bh) * p->nseg * 4);
+        p->off_seg_s = off; off = align_up(off + st);           // segment entry states
     } else if (p->path != Path::kEmpty) {
         const bool chunked = p->path != Path::kRecurrent;
         p->nchunks = chunked ? (T + kChunk - 1) / kChunk : 0;

@@ -100,7 +100,8 @@ def test_chunk_f1_clamp_binds():
 # -- continuation -------------------------------------------------------------
 
 @pytest.mark.parametrize("variant,window,chunk", [("F1", 1, 0), ("F2", 1, 0), ("F3", 4, 0),
-                                                  ("F1A", 1, 0), ("F3A", 8, 0), ("F1", 1, 64)])
+                                                  ("F1A", 1, 0), ("F3A", 8, 0), ("F1", 1, 64),
+                                                  ("F1A", 1, 64), ("F3A", 3, 64), ("F3A", 8, 64)])
 @pytest.mark.parametrize("split", [0, 3, 64, 100])
 def test_continuation(variant, window, chunk, split):
     """Two calls carrying (S, x_next, tail) equal one call and the oracle."""
@@ -118,7 +119,8 @@ def test_continuation(variant, window, chunk, split):
     o_ref, st_ref = gu.oracle_heads(w, inp, heads)
     eo, es = gu.compare(w, heads, o_cat, st2, o_ref, st_ref)
     assert eo <= 1e-5 and es <= 1e-5, (eo, es)
-    assert torch.allclose(o_cat, o_full, rtol=1e-5, atol=1e-6)
+    # the split and unsplit GPU runs agree to fp32 rounding (chunk boundaries differ)
+    assert gu.max_rel_err(o_cat.double().cpu().numpy(), o_full.double().cpu().numpy()) <= 1e-5
     assert st2.n_tail == st_full.n_tail == min(window - 1, 160)
     if window > 1:
         assert torch.allclose(st2.tail_x, st_full.tail_x) and torch.allclose(st2.tail_y, st_full.tail_y)
@@ -249,3 +251,45 @@ def test_chunk_f1_fused_continuation(split):
     assert eo <= gu.TOL_BF16 and es <= gu.TOL_BF16, (eo, es)
     assert torch.allclose(st2.x_next, torch.from_numpy(st_ref.x_next.reshape(2, 3, 64)).float().cuda(),
                           rtol=1e-5, atol=1e-5)
+
+
+# -- Falcon-1A / Falcon-3A chunk path -------------------------------------------
+
+@pytest.mark.parametrize("name", ["c3", "c5", "c3clamp"])
+def test_named_workloads_chunk_a(name):
+    check(WORKLOADS[name], heads=gu.sample_heads(WORKLOADS[name], 4))
+
+
+@pytest.mark.parametrize("variant,window", [("F1A", 1), ("F3A", 2), ("F3A", 3), ("F3A", 8)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 5, 64, 130, 700])
+def test_chunk_a_variants(variant, window, dtype, T):
+    check(gu.small(variant, dtype, B=2, H=3, T=T, dk=64, dv=64, chunk=64, window=window, seed=T + window))
+
+
+@pytest.mark.parametrize("seg", ["1", "3", "8"])
+@pytest.mark.parametrize("variant,window", [("F1A", 1), ("F3A", 8)])
+def test_chunk_a_segments(monkeypatch, seg, variant, window):
+    """Segment lengths (chunks per workgroup) do not change the result."""
+    monkeypatch.setenv("FALCON_A_SEGMENT", seg)
+    check(gu.small(variant, "f32", B=1, H=2, T=1000, dk=64, dv=64, chunk=64, window=window, seed=3))
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 16), (32, 64), (64, 32), (64, 16)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_a_head_dims(dk, dv, dtype):
+    check(gu.small("F3A", dtype, B=1, H=3, T=200, dk=dk, dv=dv, chunk=64, window=4))
+
+
+def test_chunk_a_strong_ridge_clamp():
+    """Clamp binding on most tokens (beta in (1, 2), ridge >> ||x||^2): the
+    chunk-local carries stay exact through long products of small gammas."""
+    w = gu.small("F1A", "f32", B=1, H=2, T=300, chunk=64, lam_lo=200.0, lam_hi=400.0, eps_gamma=0.05)
+    inp = gu.make(w)
+    inp["beta"] = (1.0 + inp["beta"]).astype(np.float32)
+    dev = gu.to_device(inp, w)
+    o, st = gu.run_gpu(w, dev)
+    o_ref, st_ref, tr = gu.oracle_heads(w, inp, np.arange(2), trace=True)
+    assert (tr.alpha >= 1 - 0.05 - 1e-9).mean() > 0.5
+    eo, es = gu.compare(w, np.arange(2), o, st, o_ref, st_ref)
+    assert eo <= 1e-5 and es <= 1e-5, (eo, es)
