@@ -34,67 +34,140 @@ constexpr int C = kChunk;
 constexpr int HMAX = FALCON_MAX_WINDOW - 1;  // halo pairs
 constexpr int KP = 96;                       // pair slots per chunk (64 + halo, padded)
 
-// pair p of a chunk starting at c0 is token tau = c0 - halo + p
-struct PairSrc {
-    const void *k, *v;
-    const float *xnext_in, *tailx_in, *taily_in;
-    int T, dk, dv, halo_state, n_tail_in;   // halo_state = W - 1 of the state layout
+// N consecutive elements of a row held as raw words (16- or 8-byte loads)
+template <class E, int N>
+struct RowPart {
+    static constexpr int BYTES = N * int(sizeof(E));
+    static constexpr int W4 = BYTES / 16;
+    static constexpr int W2 = (BYTES % 16) / 8;
+    static_assert(BYTES % 8 == 0, "row parts are whole 8-byte words");
+    uint4 a[W4 > 0 ? W4 : 1];
+    uint2 b[W2 > 0 ? W2 : 1];
+    __device__ void clear() {
+#pragma unroll
+        for (int i = 0; i < (W4 > 0 ? W4 : 1); ++i) a[i] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < (W2 > 0 ? W2 : 1); ++i) b[i] = make_uint2(0, 0);
+    }
+    __device__ void load(const E *p) {
+#pragma unroll
+        for (int i = 0; i < W4; ++i) a[i] = reinterpret_cast<const uint4 *>(p)[i];
+#pragma unroll
+        for (int i = 0; i < W2; ++i) b[i] = reinterpret_cast<const uint2 *>(p + W4 * 16 / int(sizeof(E)))[i];
+    }
+    __device__ uint32_t word(int w) const {   // 32-bit word w of the part
+        if (w < 4 * W4) {
+            const uint4 &u = a[w >> 2];
+            const int c = w & 3;
+            return c == 0 ? u.x : c == 1 ? u.y : c == 2 ? u.z : u.w;
+        }
+        const uint2 &u = b[(w - 4 * W4) >> 1];
+        return ((w - 4 * W4) & 1) ? u.y : u.x;
+    }
+    __device__ float get(int i) const {
+        if constexpr (sizeof(E) == 2) {
+            const uint32_t w = word(i >> 1);
+            return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+        } else {
+            return __uint_as_float(word(i));
+        }
+    }
 };
 
-// features of the pairs [0, np) of a chunk into an fp32 LDS array xf[p][ldx]
-template <class E>
-__device__ void load_pair_features(float *xf, int ldx, const PairSrc &s, int bh, int c0, int halo, int np,
-                                   float eps_rms, int phi) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int dk = s.dk;
-    const E *k = static_cast<const E *>(s.k) + size_t(bh) * s.T * dk;
-    // one wave per row, lanes over features
-    for (int p = wave; p < np; p += 4) {
-        const int tau = c0 - halo + p;
-        float x[2] = {0.f, 0.f};
-        bool from_k = false;
-        for (int m = 0; m < 2; ++m) {
-            const int e = lane + 64 * m;
-            if (e < dk) {
-                if (tau >= 1 && tau < s.T) {
-                    x[m] = ld(k, size_t(tau - 1) * dk + e);
-                } else if (tau == 0) {
-                    x[m] = s.xnext_in ? s.xnext_in[size_t(bh) * dk + e] : 0.f;
-                } else if (tau < 0 && tau >= -s.n_tail_in) {
-                    x[m] = s.tailx_in[(size_t(bh) * s.halo_state + tau + s.halo_state) * dk + e];
-                }
+// Raw rows of one chunk, prefetched into registers: 4 threads per row, pair
+// rows p = row and 64 + row (the halo makes at most 71 pairs), and the
+// chunk's query rows.  tau = c0 - halo + p is the pair's token.
+template <class E, int DK, int DV, bool WITH_Q>
+struct ChunkRows {
+    RowPart<E, DK / 4> kr[2];
+    RowPart<E, DV / 4> vr[2];
+    RowPart<E, DK / 4> qr;
+
+    __device__ void prefetch(const ChunkAArgs &a, int bh, int c0, int halo) {
+        const int row = threadIdx.x >> 2, part = threadIdx.x & 3;
+        const int np = C + halo;
+        const E *k = static_cast<const E *>(a.k) + size_t(bh) * a.T * DK;
+        const E *v = static_cast<const E *>(a.v) + size_t(bh) * a.T * a.dv;
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            const int p = 64 * pass + row;
+            const int tau = c0 - halo + p;
+            if (p < np && tau >= 1 && tau < a.T) kr[pass].load(k + size_t(tau - 1) * DK + part * (DK / 4));
+            else kr[pass].clear();
+            if (p < np && tau >= 0 && tau < a.T) vr[pass].load(v + size_t(tau) * a.dv + part * (DV / 4));
+            else vr[pass].clear();
+        }
+        if constexpr (WITH_Q) {
+            const E *q = static_cast<const E *>(a.q) + size_t(bh) * a.T * DK;
+            const int t = c0 + row;
+            if (t < a.T) qr.load(q + size_t(t) * DK + part * (DK / 4));
+            else qr.clear();
+        }
+    }
+
+    // normalised pair features into xf[p][ldx] (fp32) and values into yt[j][p]
+    __device__ void store_pairs(const ChunkAArgs &a, int bh, int c0, int halo, float *xf, int ldx, E *yt,
+                                int ldy) const {
+        const int row = threadIdx.x >> 2, part = threadIdx.x & 3;
+        const int np = C + halo;
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            const int p = 64 * pass + row;
+            const int tau = c0 - halo + p;
+            float x[DK / 4];
+            bool from_k = p < np && tau >= 1 && tau < a.T;
+#pragma unroll
+            for (int e = 0; e < DK / 4; ++e) x[e] = kr[pass].get(e);
+            if (p < np && tau == 0 && a.xnext_in) {
+#pragma unroll
+                for (int e = 0; e < DK / 4; ++e) x[e] = a.xnext_in[size_t(bh) * DK + part * (DK / 4) + e];
+            } else if (p < np && tau < 0 && tau >= -a.n_tail_in) {
+                const float *src = a.tailx_in + (size_t(bh) * halo + tau + halo) * DK + part * (DK / 4);
+#pragma unroll
+                for (int e = 0; e < DK / 4; ++e) x[e] = src[e];
+            }
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < DK / 4; ++e) ss += x[e] * x[e];
+            ss = group_sum<4>(ss);
+            const float sc = from_k ? phi_scale(ss, DK, a.eps_rms, a.phi) : 1.f;
+            if (p < 64 + HMAX) {
+#pragma unroll
+                for (int e = 0; e < DK / 4; ++e) xf[p * ldx + part * (DK / 4) + e] = x[e] * sc;
+            }
+            float y[DV / 4];
+#pragma unroll
+            for (int e = 0; e < DV / 4; ++e) y[e] = vr[pass].get(e);
+            if (p < np && tau < 0 && tau >= -a.n_tail_in) {
+                const float *src = a.taily_in + (size_t(bh) * halo + tau + halo) * a.dv + part * (DV / 4);
+#pragma unroll
+                for (int e = 0; e < DV / 4; ++e) y[e] = src[e];
+            }
+            if (p < KP) {
+#pragma unroll
+                for (int e = 0; e < DV / 4; ++e) st(yt, size_t(part * (DV / 4) + e) * ldy + p, y[e]);
             }
         }
-        from_k = tau >= 1 && tau < s.T;
-        float ss = wave_sum(x[0] * x[0] + x[1] * x[1]);
-        const float sc = from_k ? phi_scale(ss, dk, eps_rms, phi) : 1.f;
-        for (int m = 0; m < 2; ++m) {
-            const int e = lane + 64 * m;
-            if (e < dk) xf[p * ldx + e] = x[m] * sc;
-        }
+        // padding pair slots [128, KP) never exist (KP <= 128); slots [np, KP)
+        // were written with zeros above (their rows were cleared)
     }
-}
 
-// values of the pairs, transposed into yt[j][p] (storage type E); pairs past
-// np (padding) are zero
-template <class E>
-__device__ void load_pair_values_t(E *yt, int ldy, const PairSrc &s, int bh, int c0, int halo, int np) {
-    const int tid = threadIdx.x;
-    const int dv = s.dv;
-    const E *v = static_cast<const E *>(s.v) + size_t(bh) * s.T * dv;
-    for (int idx = tid; idx < KP * dv; idx += 256) {
-        const int p = idx / dv, j = idx % dv;
-        const int tau = c0 - halo + p;
-        float y = 0.f;
-        if (p < np) {
-            if (tau >= 0 && tau < s.T)
-                y = ld(v, size_t(tau) * dv + j);
-            else if (tau < 0 && tau >= -s.n_tail_in)
-                y = s.taily_in[(size_t(bh) * s.halo_state + tau + s.halo_state) * dv + j];
+    // normalised query features into qe[t][ldq]
+    __device__ void store_queries(const ChunkAArgs &a, E *qe, int ldq) const {
+        const int row = threadIdx.x >> 2, part = threadIdx.x & 3;
+        float y[DK / 4];
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < DK / 4; ++e) {
+            y[e] = qr.get(e);
+            ss += y[e] * y[e];
         }
-        st(yt, size_t(j) * ldy + p, y);
+        ss = group_sum<4>(ss);
+        const float sc = phi_scale(ss, DK, a.eps_rms, a.phi);
+#pragma unroll
+        for (int e = 0; e < DK / 4; ++e) st(qe, size_t(row) * ldq + part * (DK / 4) + e, y[e] * sc);
     }
-}
+};
 
 // ---------------------------------------------------------------------------
 // a_segment
@@ -117,7 +190,7 @@ __global__ __launch_bounds__(256) void a_segment(ChunkAArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int T = a.T, dv = a.dv, W = a.window, halo = W - 1;
     const int np = C + halo;
-    PairSrc src{a.k, a.v, a.xnext_in, a.tailx_in, a.taily_in, T, DK, dv, halo, a.n_tail_in};
+    ChunkRows<E, DK, DV, false> rows;
 
     // aggregate write of the segment, transposed: D^T[j][d] in accumulators.
     // tile (jt, dt) with jt < dv/16, dt < DK/16, spread over the 4 waves
@@ -130,10 +203,16 @@ __global__ __launch_bounds__(256) void a_segment(ChunkAArgs a) {
 
     const int c_begin = seg * a.seg_chunks;
     const int c_end = min(a.nchunks, c_begin + a.seg_chunks);
+    rows.prefetch(a, bh, c_begin * C, halo);
     for (int c = c_begin; c < c_end; ++c) {
         const int c0 = c * C;
-        load_pair_features<E>(XF, LDX, src, bh, c0, halo, np, a.eps_rms, a.phi);
-        load_pair_values_t<E>(YT, LDT, src, bh, c0, halo, np);
+        rows.store_pairs(a, bh, c0, halo, XF, LDX, YT, LDT);
+        float beta_t = 0.f, lam_t = 0.f;
+        if (tid < C && c0 + tid < T) {
+            beta_t = a.beta[size_t(bh) * T + c0 + tid];
+            lam_t = a.lambda[size_t(bh) * T + c0 + tid];
+        }
+        if (c + 1 < c_end) rows.prefetch(a, bh, c0 + C, halo);
         __syncthreads();
         // window statistic / feature energy of the chunk's own tokens
         if (W > 1) {
@@ -178,9 +257,8 @@ __global__ __launch_bounds__(256) void a_segment(ChunkAArgs a) {
             float eta = 0.f, alpha = 0.f;
             const bool noop = t >= T || (t == 0 && a.fresh);
             if (!noop) {
-                const float lam = a.lambda[size_t(bh) * T + t];
-                eta = step_eta(a.beta[size_t(bh) * T + t], mu_s[lane] + lam + a.eps);
-                alpha = step_alpha(eta, lam, a.eps_gamma);
+                eta = step_eta(beta_t, mu_s[lane] + lam_t + a.eps);
+                alpha = step_alpha(eta, lam_t, a.eps_gamma);
             }
             const float lg = log1pf(-alpha);
             const float ew = eta * ew_s[lane];
@@ -320,8 +398,7 @@ __global__ __launch_bounds__(256) void a_output(ChunkAArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int T = a.T, dv = a.dv, W = a.window, halo = W - 1;
     const int np = C + halo;
-    PairSrc src{a.k, a.v, a.xnext_in, a.tailx_in, a.taily_in, T, DK, dv, halo, a.n_tail_in};
-    const E *q = static_cast<const E *>(a.q) + size_t(bh) * T * DK;
+    ChunkRows<E, DK, DV, true> rows;
     E *o = static_cast<E *>(a.o) + size_t(bh) * T * dv;
 
     // entry state S^T[j][d] of this segment in accumulators, tiles as in a_segment
@@ -345,23 +422,18 @@ __global__ __launch_bounds__(256) void a_output(ChunkAArgs a) {
 
     const int c_begin = seg * a.seg_chunks;
     const int c_end = min(a.nchunks, c_begin + a.seg_chunks);
+    rows.prefetch(a, bh, c_begin * C, halo);
     for (int c = c_begin; c < c_end; ++c) {
         const int c0 = c * C;
-        load_pair_features<E>(XF, DK + 1, src, bh, c0, halo, np, a.eps_rms, a.phi);
-        load_pair_values_t<E>(YT, LDT, src, bh, c0, halo, np);
-        // query features: one wave per row
-        for (int t = wave; t < C; t += 4) {
-            float y[2] = {0.f, 0.f};
-            for (int m = 0; m < 2; ++m)
-                if (lane + 64 * m < DK && c0 + t < T) y[m] = ld(q, size_t(c0 + t) * DK + lane + 64 * m);
-            const float sc = phi_scale(wave_sum(y[0] * y[0] + y[1] * y[1]), DK, a.eps_rms, a.phi);
-            for (int m = 0; m < 2; ++m)
-                if (lane + 64 * m < DK) st(QE, size_t(t) * LDK + lane + 64 * m, y[m] * sc);
-        }
+        rows.store_pairs(a, bh, c0, halo, XF, DK + 1, YT, LDT);
+        rows.store_queries(a, QE, LDK);
+        float ew = 0.f, lg = 0.f;
         if (wave == 0) {
-            const int t = c0 + lane;
-            const float ew = a.etaw[size_t(bh) * a.Tpad + t];
-            const float lg = a.lg[size_t(bh) * a.Tpad + t];
+            ew = a.etaw[size_t(bh) * a.Tpad + c0 + lane];
+            lg = a.lg[size_t(bh) * a.Tpad + c0 + lane];
+        }
+        if (c + 1 < c_end) rows.prefetch(a, bh, c0 + C, halo);
+        if (wave == 0) {
             ew_s[lane] = ew;
             gam_s[lane] = expf(lg);
             const float b = wave_inclusive_scan(lg);
