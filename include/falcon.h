@@ -112,8 +112,11 @@ typedef struct falcon_state {
  *   phi          FALCON_PHI_RMSNORM or FALCON_PHI_IDENTITY.
  *   batch, heads >= 1; seqlen >= 0; dk, dv in {16, 32, 64, 128}.
  *   chunk        0 = token-recurrent form (every variant);
- *                64 = chunk-parallel form.  A combination that has no
- *                chunk-parallel kernel returns FALCON_ERR_UNSUPPORTED.
+ *                64 = chunk-parallel form, for Falcon-1 (dk in {32, 64, 128},
+ *                any dv), Falcon-2 (bf16: dk in {64, 128}; fp32: dk = 64;
+ *                any dv) and Falcon-1A / 3A (dk in {32, 64}, dv <= 64).
+ *                A combination that has no chunk-parallel kernel returns
+ *                FALCON_ERR_UNSUPPORTED.
  *   window       W >= 1; must be 1 for V1, V2, V1A; at most FALCON_MAX_WINDOW.
  *   eps >= 0, eps_rms >= 0, 0 < eps_gamma < 1 (defaults 1e-6, 1e-6, 1e-3).
  *   q, k, v      device inputs, 16-byte aligned.

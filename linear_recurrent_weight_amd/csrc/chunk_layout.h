@@ -40,6 +40,12 @@ inline int chunk_f1_fused_slice(int bh, int dv) {
     return (bh * (dv / 64) >= 128) ? 64 : 32;
 }
 
+// Falcon-2 chunk path: one kernel, no workspace.  bf16: d_k in {64, 128};
+// fp32: d_k = 64 (on-chip buffers); any d_v (a multiple of 16).
+constexpr bool chunk_f2_supported(bool bf16, int dk, int dv) {
+    return (bf16 ? (dk == 64 || dk == 128) : dk == 64) && dv % 16 == 0;
+}
+
 // Falcon-1A / Falcon-3A chunk path: d_k in {32, 64}, d_v in {16, 32, 64}.
 constexpr bool chunk_a_supported(int dk, int dv) {
     return (dk == 32 || dk == 64) && (dv == 16 || dv == 32 || dv == 64);

@@ -67,6 +67,14 @@ __device__ __forceinline__ float phi_scale(float ss, int d, float eps_rms, int p
 }
 
 // eta = beta / den (0 if den == 0), alpha = min(eta * lambda, 1 - eps_gamma)
+// Orders LDS traffic between the lanes of one wave (no workgroup barrier):
+// waits for this wave's outstanding LDS operations and keeps the compiler
+// from moving memory accesses across the call.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+}
+
 __device__ __forceinline__ float step_eta(float beta, float den) { return den != 0.f ? beta / den : 0.f; }
 __device__ __forceinline__ float step_alpha(float eta, float lam, float eps_gamma) {
     return fminf(eta * lam, 1.f - eps_gamma);

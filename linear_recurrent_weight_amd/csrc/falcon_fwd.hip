@@ -12,6 +12,7 @@ const char *const kNamesRecurrent[] = {"feature", "recurrent"};
 const char *const kNamesChunkF1[] = {"feature", "chunk_f1_prep", "chunk_f1_scan"};
 const char *const kNamesChunkF1Fused[] = {"chunk_f1_fused"};
 const char *const kNamesChunkA[] = {"a_segment", "a_segscan", "a_output"};
+const char *const kNamesChunkF2[] = {"chunk_f2"};
 
 int run(const falcon_fwd_args *args, void *stream, Marks *m) {
     Plan p;
@@ -81,6 +82,29 @@ int run(const falcon_fwd_args *args, void *stream, Marks *m) {
         ca.Gseg = p.ws_at<float>(p.off_seg_g);
         ca.Sseg = p.ws_at<float>(p.off_seg_s);
         launch_chunk_a(ca, p.dtype == FALCON_BF16, s, m);
+    } else if (p.path == Path::kChunkF2) {
+        ChunkF2Args fa{};
+        fa.BH = p.BH;
+        fa.T = p.T;
+        fa.nchunks = p.nchunks;
+        fa.dk = p.dk;
+        fa.dv = p.dv;
+        fa.phi = p.phi;
+        fa.fresh = p.fresh ? 1 : 0;
+        fa.eps = p.eps;
+        fa.eps_gamma = p.eps_gamma;
+        fa.eps_rms = p.eps_rms;
+        fa.q = p.q;
+        fa.k = p.k;
+        fa.v = p.v;
+        fa.beta = p.beta;
+        fa.lambda = p.lambda;
+        fa.xnext_in = p.xnext_in;
+        fa.S_in = p.S_in;
+        fa.S_out = p.S_out;
+        fa.xnext_out = p.xnext_out;
+        fa.o = p.o;
+        launch_chunk_f2(fa, p.dtype == FALCON_BF16, s, m);
     } else if (p.path == Path::kChunkF1Fused) {
         F1FusedArgs fa{};
         fa.BH = p.BH;
@@ -208,6 +232,7 @@ extern "C" const char *falcon_kernel_name(const falcon_fwd_args *args, int i) {
         case Path::kChunkF1: return i < 3 ? kNamesChunkF1[i] : nullptr;
         case Path::kChunkF1Fused: return i < 1 ? kNamesChunkF1Fused[i] : nullptr;
         case Path::kChunkA: return i < 3 ? kNamesChunkA[i] : nullptr;
+        case Path::kChunkF2: return i < 1 ? kNamesChunkF2[i] : nullptr;
         default: return nullptr;
     }
 }

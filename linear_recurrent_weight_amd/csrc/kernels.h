@@ -85,11 +85,24 @@ struct ChunkAArgs {
     float *Sseg;             // [BH, nseg, dv, dk] segment entry states (transposed)
 };
 
+struct ChunkF2Args {
+    int BH, T, nchunks, dk, dv, phi, fresh;
+    float eps, eps_gamma, eps_rms;
+    const void *q, *k, *v;  // [BH, T, d] in the io dtype
+    const float *beta;      // [BH, T, dv] per-column gains
+    const float *lambda;    // [BH, T]
+    const float *xnext_in;  // nullptr when fresh
+    const float *S_in;
+    float *S_out, *xnext_out;
+    void *o;
+};
+
 void launch_features(const FeatureArgs &a, bool in_bf16, bool feat_bf16, hipStream_t s, Marks *m);
 void launch_passthrough(const PassArgs &a, hipStream_t s, Marks *m);
 void launch_recurrent(const RecurrentArgs &a, bool io_bf16, hipStream_t s, Marks *m);
 void launch_chunk_f1(const ChunkF1Args &a, bool bf16, hipStream_t s, Marks *m);
 void launch_chunk_f1_fused(const F1FusedArgs &a, int ds, hipStream_t s, Marks *m);
 void launch_chunk_a(const ChunkAArgs &a, bool bf16, hipStream_t s, Marks *m);
+void launch_chunk_f2(const ChunkF2Args &a, bool bf16, hipStream_t s, Marks *m);
 
 }  // namespace falcon

@@ -78,6 +78,8 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
             p->slice = chunk_f1_fused_slice(a->batch * a->heads, a->dv);
         } else if (var == FALCON_V1 && chunk_f1_supported(a->dk, a->dv)) {
             p->path = Path::kChunkF1;
+        } else if (var == FALCON_V2 && chunk_f2_supported(a->dtype == FALCON_BF16, a->dk, a->dv)) {
+            p->path = Path::kChunkF2;
         } else if ((var == FALCON_V1A || var == FALCON_V3A) && chunk_a_supported(a->dk, a->dv)) {
             p->path = Path::kChunkA;
         } else {
@@ -108,7 +110,7 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
     // whole chunks on the chunk paths), then the per-chunk operators
     const int T = a->seqlen;
     size_t off = 0;
-    if (p->path == Path::kChunkF1Fused) {
+    if (p->path == Path::kChunkF1Fused || p->path == Path::kChunkF2) {
         p->nchunks = (T + kChunk - 1) / kChunk;
     } else if (p->path == Path::kChunkA) {
         p->nchunks = (T + kChunk - 1) / kChunk;

@@ -207,3 +207,14 @@ def test_chunk_path_coverage(lib):
     for var in ("F1", "F2", "F3", "F1A", "F3A"):
         w = 3 if var in ("F3", "F3A") else 1
         assert validate(lib, with_ws(lib, args(variant=var, window=w, chunk=0, dk=16, dv=16))) == fb.OK
+
+
+def test_chunk_f2_coverage(lib):
+    """Falcon-2 has a chunk-parallel kernel for bf16 d_k in {64, 128} and
+    fp32 d_k = 64; it needs no workspace."""
+    for dt, dk, ok in [("bf16", 64, True), ("bf16", 128, True), ("f32", 64, True),
+                       ("f32", 128, False), ("bf16", 32, False)]:
+        a = args(variant="F2", dtype=dt, dk=dk, dv=128)
+        assert validate(lib, a) == (fb.OK if ok else fb.ERR_UNSUPPORTED), (dt, dk)
+        if ok:
+            assert wsize(lib, a) == 0

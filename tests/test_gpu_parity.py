@@ -293,3 +293,71 @@ def test_chunk_a_strong_ridge_clamp():
     assert (tr.alpha >= 1 - 0.05 - 1e-9).mean() > 0.5
     eo, es = gu.compare(w, np.arange(2), o, st, o_ref, st_ref)
     assert eo <= 1e-5 and es <= 1e-5, (eo, es)
+
+
+# -- Falcon-2 chunk path -------------------------------------------------------
+
+def test_named_workload_c4_chunk_f2():
+    check(WORKLOADS["c4"], heads=gu.sample_heads(WORKLOADS["c4"], 3))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 63, 64, 65, 200])
+def test_chunk_f2_lengths(dtype, T):
+    """Ragged lengths across the 16-token solve blocks and the 64-token chunks."""
+    check(gu.small("F2", dtype, B=2, H=3, T=T, dk=64, dv=64, chunk=64, seed=T))
+
+
+@pytest.mark.parametrize("dk,dv,dtype", [(64, 16, "f32"), (64, 128, "f32"), (64, 32, "bf16"),
+                                         (128, 16, "bf16"), (128, 128, "bf16")])
+def test_chunk_f2_head_dims(dk, dv, dtype):
+    check(gu.small("F2", dtype, B=1, H=3, T=300, dk=dk, dv=dv, chunk=64))
+
+
+def test_chunk_f2_equal_gains_is_falcon1():
+    """With the same gain in every column, Falcon-2 is Falcon-1: the two
+    chunk kernels agree to fp32 rounding."""
+    w1 = gu.small("F1", "f32", B=2, H=2, T=333, dk=64, dv=64, chunk=64, seed=5)
+    inp = gu.make(w1)
+    dev1 = gu.to_device(inp, w1)
+    o1, st1 = gu.run_gpu(w1, dev1)
+    w2 = w1.with_(variant="F2")
+    dev2 = dict(dev1)
+    dev2["beta"] = dev1["beta"][..., None].expand(*dev1["beta"].shape, 64).contiguous()
+    o2, st2 = gu.run_gpu(w2, dev2)
+    assert gu.max_rel_err(o2.double().cpu().numpy(), o1.double().cpu().numpy()) <= 1e-5
+    assert gu.max_rel_err(st2.S.double().cpu().numpy(), st1.S.double().cpu().numpy()) <= 1e-5
+
+
+def test_chunk_f2_strong_ridge_clamp():
+    """Clamp binding on most (token, column) pairs: long products of small
+    per-column carries stay exact inside a chunk."""
+    w = gu.small("F2", "f32", B=1, H=2, T=300, chunk=64, lam_lo=200.0, lam_hi=400.0, eps_gamma=0.05)
+    inp = gu.make(w)
+    inp["beta"] = (1.0 + inp["beta"]).astype(np.float32)
+    dev = gu.to_device(inp, w)
+    o, st = gu.run_gpu(w, dev)
+    o_ref, st_ref, tr = gu.oracle_heads(w, inp, np.arange(2), trace=True)
+    assert (tr.alpha >= 1 - 0.05 - 1e-9).mean() > 0.5
+    eo, es = gu.compare(w, np.arange(2), o, st, o_ref, st_ref)
+    assert eo <= 1e-5 and es <= 1e-5, (eo, es)
+
+
+@pytest.mark.parametrize("split", [0, 3, 64, 100])
+def test_chunk_f2_continuation(split):
+    import torch
+    w = gu.small("F2", "f32", B=2, H=2, T=160, dk=64, dv=32, chunk=64, seed=12)
+    inp = gu.make(w)
+    dev = gu.to_device(inp, w)
+    o_full, st_full = gu.run_gpu(w, dev)
+    a = {k: v[:, :, :split].contiguous() for k, v in dev.items()}
+    b = {k: v[:, :, split:].contiguous() for k, v in dev.items()}
+    o1, st1 = gu.run_gpu(w.with_(seqlen=split), a)
+    o2, st2 = gu.run_gpu(w.with_(seqlen=160 - split), b, state=st1)
+    o_cat = torch.cat([o1, o2], 2)
+    heads = np.arange(4)
+    o_ref, st_ref = gu.oracle_heads(w, inp, heads)
+    eo, es = gu.compare(w, heads, o_cat, st2, o_ref, st_ref)
+    assert eo <= 1e-5 and es <= 1e-5, (eo, es)
+    assert gu.max_rel_err(o_cat.double().cpu().numpy(), o_full.double().cpu().numpy()) <= 1e-5
+    assert torch.allclose(st2.x_next, st_full.x_next)
