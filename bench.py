@@ -71,6 +71,105 @@ def cpu_baseline(w, inp, min_seconds: float):
             "sample": f"whole workload x{reps} ({dt:.1f} s), fp64 NumPy token recurrence, 1 thread"}
 
 
+COPY_KERNEL = "__amd_rocclr_copyBuffer"   # the runtime's device copy (--copy-calibration)
+COPY_BYTES = 256 << 20
+
+
+def _db_rows(db, sql):
+    import sqlite3
+    con = sqlite3.connect(db)
+    try:
+        return list(con.execute(sql))
+    finally:
+        con.close()
+
+
+def rocprof_summary(workload: str, kernels, stats_db: str, fetch_db: str, write_db: str,
+                    command: str) -> str:
+    """Markdown summary of three rocprofv3 runs of this script on one
+    workload: kernel-trace statistics, then FETCH_SIZE and WRITE_SIZE per
+    dispatch (KiB), each scaled by what the same counter reads for the plain
+    device copy of COPY_BYTES that --copy-calibration adds."""
+    from linear_recurrent_weight_amd.build import sources_digest
+    top = _db_rows(stats_db, "select name, total_calls, average, total_duration from top_kernels")
+    lines = [f"# rocprofv3 summary: workload {workload}", "",
+             "Commands (run from the repository root on one MI355X; the .db files stay out of the tree):",
+             "", "```", command.strip(), "```", "",
+             "## Kernel trace (`--kernel-trace --stats`)", "",
+             "| kernel | calls | average (us) |", "|---|---:|---:|"]
+    for name, calls, avg, _ in top:
+        lines.append(f"| `{name[:110]}` | {calls} | {avg:.3f} |")
+
+    def counter(db, cname):
+        rows = _db_rows(db, "select kernel_name, count(*), avg(value) from counters_collection "
+                        f"where counter_name = '{cname}' group by kernel_name")
+        return {k: (n, v) for k, n, v in rows}
+    fetch, write = counter(fetch_db, "FETCH_SIZE"), counter(write_db, "WRITE_SIZE")
+    f_copy = (COPY_BYTES / 1024) / fetch[COPY_KERNEL][1] if COPY_KERNEL in fetch else None
+    w_copy = (COPY_BYTES / 1024) / write[COPY_KERNEL][1] if COPY_KERNEL in write else None
+    lines += ["", "## HBM traffic (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`)", "",
+              f"Calibration: a device copy of {COPY_BYTES >> 20} MiB reads "
+              f"{fetch.get(COPY_KERNEL, (0, float('nan')))[1]:.0f} KiB by FETCH_SIZE and writes "
+              f"{write.get(COPY_KERNEL, (0, float('nan')))[1]:.0f} KiB by WRITE_SIZE: scale factors "
+              f"{f_copy if f_copy is None else round(f_copy, 3)} (fetch) and "
+              f"{w_copy if w_copy is None else round(w_copy, 3)} (write).", "",
+              "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | calibrated bytes / dispatch |",
+              "|---|---:|---:|---:|---:|"]
+    ours = {}
+    for k in sorted(set(fetch) | set(write)):
+        if "falcon::" not in k:
+            continue
+        fk, wk = fetch.get(k, (0, 0.0))[1], write.get(k, (0, 0.0))[1]
+        b = (fk * (f_copy or 1.0) + wk * (w_copy or 1.0)) * 1024
+        ours[k] = b
+        lines.append(f"| `{k[:110]}` | {fetch.get(k, (0,))[0]} | {fk:.0f} | {wk:.0f} | {b:.4g} |")
+    total = sum(ours.values())
+    lines += ["", f"traffic_bytes_per_call: {total:.0f}",
+              f"sources_digest: {sources_digest(kernels)}", ""]
+    return "\n".join(lines)
+
+
+def kernel_names(lib, w):
+    """Names of the kernels one call of workload `w` launches (host-side plan)."""
+    from linear_recurrent_weight_amd import falcon as fb
+    a = fb.make_args(variant=w.variant, dtype=w.dtype, batch=w.batch, heads=w.heads, seqlen=w.seqlen,
+                     dk=w.dk, dv=w.dv, chunk=w.chunk, window=w.window)
+    names = []
+    while True:
+        nm = lib.falcon_kernel_name(ctypes.byref(a), len(names))
+        if nm is None:
+            return names
+        names.append(nm.decode())
+
+
+def profile_path(workload: str, kernels) -> str:
+    """profiles/<kernel source(s)>_<workload>.md"""
+    from linear_recurrent_weight_amd.build import KERNEL_SOURCES
+    stems = []
+    for k in kernels:
+        stem = KERNEL_SOURCES[k].rsplit(".", 1)[0]
+        if stem not in stems:
+            stems.append(stem)
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        "+".join(stems) + f"_{workload}.md")
+
+
+def read_traffic(workload: str, kernels):
+    """Calibrated HBM bytes per call from the committed summary, or None when
+    it is missing or the kernel sources changed since the counters were read."""
+    import re
+    from linear_recurrent_weight_amd.build import sources_digest
+    path = profile_path(workload, kernels)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"^traffic_bytes_per_call: (\d+)$", text, re.M)
+    d = re.search(r"^sources_digest: (\S+)$", text, re.M)
+    if not m or not d or d.group(1) != sources_digest(kernels):
+        return None
+    return int(m.group(1))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -81,7 +180,21 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
+    ap.add_argument("--rocprof-summary", nargs=3, metavar=("STATS_DB", "FETCH_DB", "WRITE_DB"),
+                    help="print a markdown summary of three rocprofv3 runs (no GPU needed)")
+    ap.add_argument("--rocprof-command", default="", help="the commands that made the databases")
     args = ap.parse_args()
+    if args.rocprof_summary:
+        from linear_recurrent_weight_amd import falcon as fb
+        from linear_recurrent_weight_amd.inputs import WORKLOADS
+        names = kernel_names(fb.load_library(), WORKLOADS[args.workload])
+        text = rocprof_summary(args.workload, names, *args.rocprof_summary, args.rocprof_command)
+        path = profile_path(args.workload, names)
+        os.makedirs(os.path.dirname(path), exist_ok=True)
+        with open(path, "w") as f:
+            f.write(text)
+        print(path)
+        return 0
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         return 2
@@ -171,17 +284,7 @@ def main() -> int:
     alg_bytes = algorithmic_bytes(w)
     alg_flops = algorithmic_flops(w)
     achieved_gbs = alg_bytes / (ms * 1e-3) / 1e9
-    traffic = None
-    tpath = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                         f"traffic_{args.workload}.json")
-    if os.path.exists(tpath):
-        try:
-            tj = json.load(open(tpath))
-            from linear_recurrent_weight_amd.build import sources_digest
-            if tj.get("sources_digest") == sources_digest():
-                traffic = tj.get("bytes_per_call")
-        except Exception:
-            traffic = None
+    traffic = read_traffic(args.workload, names)
 
     line = {
         "metric": METRIC,

@@ -63,12 +63,26 @@ def build(verbose: bool = False) -> pathlib.Path:
 
 
 
-def sources_digest() -> str:
-    """sha256 over the library sources and the public header, to tell whether
-    a stored profile still describes the current kernels."""
+# source file of each kernel name that falcon_kernel_name reports
+KERNEL_SOURCES = {"passthrough": "feature.hip", "feature": "feature.hip", "recurrent": "recurrent.hip",
+                  "chunk_f1_prep": "chunk_f1.hip", "chunk_f1_scan": "chunk_f1.hip",
+                  "chunk_f1_fused": "chunk_f1_fused.hip", "chunk_f2": "chunk_f2.hip",
+                  "a_segment": "chunk_a.hip", "a_segscan": "chunk_a.hip", "a_output": "chunk_a.hip"}
+
+
+def sources_digest(kernels=None) -> str:
+    """sha256 over library sources and the public header, to tell whether a
+    stored profile still describes the current kernels.  With `kernels` (names
+    as falcon_kernel_name reports them), only their sources, the shared
+    headers, the planner and the dispatcher count."""
     import hashlib
     h = hashlib.sha256()
-    for p in sources() + sorted(CSRC.glob("*.h")) + [ROOT / "include" / "falcon.h"]:
+    if kernels is None:
+        files = sources()
+    else:
+        files = sorted({CSRC / KERNEL_SOURCES[k] for k in kernels} |
+                       {CSRC / "plan.cpp", CSRC / "falcon_fwd.hip"})
+    for p in files + sorted(CSRC.glob("*.h")) + [ROOT / "include" / "falcon.h"]:
         h.update(p.name.encode())
         h.update(p.read_bytes())
     return h.hexdigest()[:16]
