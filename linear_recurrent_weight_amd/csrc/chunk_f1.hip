@@ -22,6 +22,7 @@
 #include "chunk_layout.h"
 #include "common.h"
 #include "kernels.h"
+#include "tri_inverse.h"
 
 namespace falcon {
 namespace {
@@ -146,49 +147,7 @@ __global__ __launch_bounds__(256) void chunk_f1_prep(ChunkF1Args a) {
     __syncthreads();
 
     // 3. inverse of the unit-lower system I + Lm, by 16x16 blocks
-    //    diagonal blocks: forward substitution, one column per lane
-    if (lane < 16) {
-        const int base = 16 * wave;
-        float tcol[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float s = (r == lane) ? 1.f : 0.f;
-#pragma unroll
-            for (int kk = 0; kk < r; ++kk) s -= Lm[(base + r) * kLs + base + kk] * tcol[kk];
-            tcol[r] = s;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Tm[(base + r) * kLs + base + lane] = tcol[r];
-    }
-    __syncthreads();
-    //    off-diagonal blocks, by distance d = I - J:
-    //    T_IJ = -T_II * sum_{K=J}^{I-1} L_IK T_KJ
-    for (int d = 1; d < 4; ++d) {
-        const int nblk = 4 - d;
-        for (int idx = tid; idx < nblk * 256; idx += 256) {
-            const int blk = idx >> 8, e = idx & 255;
-            const int J = blk, I = blk + d;
-            const int r = e >> 4, cc = e & 15;
-            float s = 0.f;
-            for (int K = J; K < I; ++K)
-#pragma unroll
-                for (int kk = 0; kk < 16; ++kk)
-                    s += Lm[(16 * I + r) * kLs + 16 * K + kk] * Tm[(16 * K + kk) * kLs + 16 * J + cc];
-            Mt[blk * 272 + r * 17 + cc] = s;
-        }
-        __syncthreads();
-        for (int idx = tid; idx < nblk * 256; idx += 256) {
-            const int blk = idx >> 8, e = idx & 255;
-            const int J = blk, I = blk + d;
-            const int r = e >> 4, cc = e & 15;
-            float s = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < 16; ++kk)
-                s += Tm[(16 * I + r) * kLs + 16 * I + kk] * Mt[blk * 272 + kk * 17 + cc];
-            Tm[(16 * I + r) * kLs + 16 * J + cc] = -s;
-        }
-        __syncthreads();
-    }
+    unit_lower_inverse64(Lm, Tm, Mt, kLs);
 
     // 4. Tp = L^{-1} diag(eta) and P, in the storage type
     for (int idx = tid; idx < C * C; idx += 256) {

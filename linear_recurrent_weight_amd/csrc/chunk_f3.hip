@@ -1,0 +1,329 @@
+// Chunk-parallel Falcon-3 forward (window of W pairs, regression writes):
+// summary §4.4 "Mini-batch Update Rule for Regression (Falcon-3)", §C.7, and
+// §H.3 "Mapping Falcon-3 to ParallelFlow" (the window rows stacked into one
+// block-strict-causal system; rows of the same step do not interact).
+//
+// Token t writes the W pairs of its window I_t, each with the residual at the
+// pre-update state and the weight w_t = eta_t / B_t:
+//     u_{t,j} = w_t (y_j - S_{t-1}^T x_j),   S_t = gamma_t S_{t-1} + sum_j x_j u_{t,j}^T.
+// A chunk holds Ct = 64 / W tokens, so its stacked rows r = (t, k) number at
+// most 64; row r carries the pair j = t - W + 1 + k.  With the chunk-local
+// log-prefix b over tokens (restarted at 0) and S_0 the chunk-entry state:
+//     u_r + w_r sum_{r': t' < t} e^{b_{t-1} - b_{t'}} (x_r . x_r') u_r'
+//         = w_r (y_r - e^{b_{t-1}} S_0^T x_r)
+// (unit lower triangular in r; rows of one token are decoupled), and
+//     o_t = e^{b_t} S_0^T qh_t + sum_{r': t' <= t} e^{b_t - b_t'} (qh_t . x_r') u_r',
+//     S_C = e^{b_C} S_0 + sum_r e^{b_C - b_t} x_r u_r^T.
+// Rows whose pair lies before the sequence start (and is not in the incoming
+// tail) have w = 0 and x = 0: they are inert.  The first chunk reads pairs
+// before position 0 from the incoming tail.
+//
+// Kernel f3_prep, one workgroup per chunk, all chunks in parallel: gathers the
+// stacked rows, forms the Gram and the token-by-row scores on MFMA, inverts
+// the unit-lower system in fp32, and stores Tp = L^{-1} diag(w), the scores
+// and the stacked features.
+// Kernel f3_scan, one workgroup per (head, 16 value columns): walks the
+// chunks in order with the fp32 state slice in MFMA accumulators.
+#include "chunk_layout.h"
+#include "kernels.h"
+#include "mma.h"
+#include "tri_inverse.h"
+
+namespace falcon {
+namespace {
+
+constexpr int C = kChunk;
+constexpr int kLs = C + 1;   // fp32 LDS row stride
+
+struct RowMap {
+    int ct, W, halo;
+    // local token of stacked row r (rows past ct * W belong to no token)
+    __device__ int token(int r) const { return r < ct * W ? r / W : -1; }
+    // global pair index of row r of chunk c (may be negative: incoming tail)
+    __device__ int pair(int c, int r) const { return c * ct + r / W - halo + r % W; }
+};
+
+template <class E, int DK>
+__global__ __launch_bounds__(256) void f3_prep(ChunkF3Args a) {
+    constexpr int PD = Pad<E>::v;
+    constexpr int LK = DK + PD;
+    __shared__ __align__(16) E Xs[C * LK];   // stacked write features
+    __shared__ __align__(16) E Qs[C * LK];   // token queries (Ct rows used)
+    __shared__ float Lm[C * kLs];
+    __shared__ float Tm[C * kLs];
+    __shared__ float Pm[C * kLs];
+    __shared__ float Mt[3 * 16 * 17];
+    __shared__ float bt[C], bpt[C];          // per token: b_t, b_{t-1}
+    __shared__ float wr[C];                  // per row: eta_t / B_t (0 when inert)
+    __shared__ int tr[C];                    // per row: local token, -1 for padding
+
+    const int c = blockIdx.x, bh = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const RowMap rm{a.ct, a.window, a.window - 1};
+    const int T = a.T, ct = a.ct, W = a.window, halo = a.window - 1;
+    const size_t frow0 = size_t(bh) * a.Tpad;
+    const E *xn = static_cast<const E *>(a.xn) + frow0 * DK;
+    const E *qn = static_cast<const E *>(a.qn) + frow0 * DK;
+    char *ops = static_cast<char *>(a.ops) + (size_t(bh) * a.nchunks + c) * a.chunk_bytes;
+    E *Tp = reinterpret_cast<E *>(ops + chunk_f1_tp_off());
+    E *Pg = reinterpret_cast<E *>(ops + chunk_f1_p_off(sizeof(E)));
+    E *Xg = reinterpret_cast<E *>(ops + chunk_f3_x_off(sizeof(E)));
+    float *scal = reinterpret_cast<float *>(ops + chunk_f3_scal_off(DK, sizeof(E)));
+
+    // 1. per-token log-prefix (wave 0, lane = local token) and per-row weights
+    if (wave == 0) {
+        const int t = c * ct + lane;   // < Tpad: the feature buffers have a spare tile
+        const float alpha = lane < ct ? a.alpha[frow0 + t] : 0.f;
+        const float b = wave_inclusive_scan(log1pf(-alpha));
+        float bp = __shfl_up(b, 1, 64);
+        if (lane == 0) bp = 0.f;
+        bt[lane] = b;
+        bpt[lane] = bp;
+        const float bC = __shfl(b, ct - 1, 64);
+        scal[2 * C + lane] = expf(b);
+        if (lane == 0) scal[3 * C] = expf(bC);
+    } else if (wave == 1) {
+        const int r = lane, tl = rm.token(r);
+        float w = 0.f;
+        if (tl >= 0) {
+            const int t = c * ct + tl, p = rm.pair(c, r);
+            if (t < T && p >= -a.n_tail_in) {
+                const long long pairs = (long long)a.n_tail_in + t + 1;
+                const int nb = pairs < W ? int(pairs) : W;
+                w = a.eta[frow0 + t] / float(nb);
+            }
+        }
+        wr[r] = w;
+        tr[r] = tl;
+    }
+    // stacked features and token queries
+    for (int idx = tid; idx < C * DK; idx += 256) {
+        const int r = idx / DK, e = idx % DK;
+        const int tl = rm.token(r), p = rm.pair(c, r);
+        float x = 0.f;
+        if (tl >= 0) {
+            if (p >= 0) x = ld(xn, size_t(p) * DK + e);
+            else if (p >= -a.n_tail_in) x = a.tailx_in[(size_t(bh) * halo + halo + p) * DK + e];
+        }
+        st(Xs, size_t(r) * LK + e, x);
+        st(Xg, idx, x);
+        st(Qs, size_t(r) * LK + e, r < ct ? ld(qn, size_t(c * ct + r) * DK + e) : 0.f);
+    }
+    __syncthreads();
+    {
+        const int r = tid & 63, tl = tr[r];
+        if (tid < 64) {
+            scal[0 * C + r] = tl >= 0 ? expf(bpt[tl]) : 0.f;
+            scal[1 * C + r] = tl >= 0 ? expf(bt[ct - 1] - bt[tl]) : 0.f;
+        }
+    }
+
+    // 2. Gram (lower 16x16 tiles) and token-by-row scores (all tiles of the
+    //    token rows) on MFMA, with the decays and the causal masks
+    const int nqt = (ct + 15) / 16;
+    const int njobs = 10 + 4 * nqt;
+    for (int job = wave; job < njobs; job += 4) {
+        const bool isG = job < 10;
+        int I, J;
+        if (isG) {
+            int t = job;
+            I = 0;
+            while (t > I) {
+                t -= I + 1;
+                ++I;
+            }
+            J = t;
+        } else {
+            I = (job - 10) / 4;
+            J = (job - 10) % 4;
+        }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = Mma<E>::run(acc, (isG ? Xs : Qs) + 16 * I * LK, LK, Xs + 16 * J * LK, LK, 0, DK);
+        const int j = 16 * J + (lane & 15), tj = tr[j];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int i = 16 * I + 4 * (lane >> 4) + rr;
+            if (isG) {
+                const int ti = tr[i];
+                const bool live = ti >= 0 && tj >= 0 && tj < ti;
+                Lm[i * kLs + j] = live ? wr[i] * expf(bpt[ti] - bt[tj]) * acc[rr] : 0.f;
+            } else {
+                const bool live = i < ct && tj >= 0 && tj <= i;
+                Pm[i * kLs + j] = live ? expf(bt[i] - bt[tj]) * acc[rr] : 0.f;
+            }
+        }
+    }
+    for (int idx = tid; idx < C * C; idx += 256) {
+        const int i = idx / C, j = idx % C;
+        if ((j >> 4) > (i >> 4)) {
+            Lm[i * kLs + j] = 0.f;
+            Tm[i * kLs + j] = 0.f;
+        }
+        if ((i >> 4) >= nqt) Pm[i * kLs + j] = 0.f;
+    }
+    __syncthreads();
+
+    // 3. inverse of the unit-lower system
+    unit_lower_inverse64(Lm, Tm, Mt, kLs);
+
+    // 4. Tp = L^{-1} diag(w) and the scores, in the storage type
+    for (int idx = tid; idx < C * C; idx += 256) {
+        const int i = idx / C, j = idx % C;
+        st(Tp, idx, j <= i ? Tm[i * kLs + j] * wr[j] : 0.f);
+        st(Pg, idx, Pm[i * kLs + j]);
+    }
+}
+
+template <class E, int DK>
+__global__ __launch_bounds__(256) void f3_scan(ChunkF3Args a, int nslice) {
+    constexpr int PD = Pad<E>::v;
+    constexpr int LS = DK + PD;   // stride of [j][d] buffers
+    constexpr int LT = C + PD;    // stride of [.][row] buffers
+    constexpr int NT = DK >= 64 ? DK / 64 : 1;
+    __shared__ __align__(16) E St[2][16 * LS];  // S^T slice copy
+    __shared__ __align__(16) E R0t[16 * LT];    // residual^T
+    __shared__ __align__(16) E Ut[16 * LT];     // U^T
+    __shared__ __align__(16) E Xht[DK * LT];    // (diag(e^{b_C - b_t}) X)^T
+
+    const int id = blockIdx.x;
+    const int u8 = id & 7, rest = id >> 3;
+    const int s = rest % nslice, g = rest / nslice;
+    const int bh = g * 8 + u8;
+    if (bh >= a.BH) return;
+    const int j0 = 16 * s;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int dv = a.dv, T = a.T, ct = a.ct, halo = a.window - 1;
+    const RowMap rm{a.ct, a.window, a.window - 1};
+    const E *Qall = static_cast<const E *>(a.qn) + size_t(bh) * a.Tpad * DK;
+    const E *V = static_cast<const E *>(a.v) + size_t(bh) * T * dv;
+    E *O = static_cast<E *>(a.o) + size_t(bh) * T * dv;
+    const char *opsb = static_cast<const char *>(a.ops) + size_t(bh) * a.nchunks * a.chunk_bytes;
+
+    const bool owns = 16 * wave * NT < DK;
+    f32x4 S[NT];
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+        const int dbase = 16 * (wave * NT + m);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int d = dbase + 4 * (lane >> 4) + r;
+            S[m][r] = (owns && a.S_in) ? a.S_in[(size_t(bh) * DK + d) * dv + j0 + (lane & 15)] : 0.f;
+        }
+        if (owns) st4(St[0] + (lane & 15) * LS + dbase + 4 * (lane >> 4), S[m]);
+    }
+    int cur = 0;
+    __syncthreads();
+
+    for (int c = 0; c < a.nchunks; ++c) {
+        const char *ops = opsb + size_t(c) * a.chunk_bytes;
+        const E *Tp = reinterpret_cast<const E *>(ops + chunk_f1_tp_off());
+        const E *Pg = reinterpret_cast<const E *>(ops + chunk_f1_p_off(sizeof(E)));
+        const E *X = reinterpret_cast<const E *>(ops + chunk_f3_x_off(sizeof(E)));
+        const float *scal = reinterpret_cast<const float *>(ops + chunk_f3_scal_off(DK, sizeof(E)));
+        const E *Qh = Qall + size_t(c) * ct * DK;   // 64 rows stay inside the padded buffer
+
+        // phase 1: R0 = Y - diag(Gamma_{t-1}) X S_0 for stacked rows 16w..16w+15
+        {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = Mma<E>::run(acc, X + size_t(16 * wave) * DK, DK, St[cur], LS, 0, DK);
+            const int j = lane & 15;
+            f32x4 r0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * wave + 4 * (lane >> 4) + r;
+                const int p = rm.pair(c, i);
+                float y = 0.f;
+                if (rm.token(i) >= 0) {
+                    if (p >= 0) {
+                        if (p < T) y = ld(V, size_t(p) * dv + j0 + j);
+                    } else if (p >= -a.n_tail_in) {
+                        y = a.taily_in[(size_t(bh) * halo + halo + p) * dv + j0 + j];
+                    }
+                }
+                r0[r] = y - scal[i] * acc[r];
+            }
+            st4(R0t + j * LT + 16 * wave + 4 * (lane >> 4), r0);
+        }
+        __syncthreads();
+
+        // phase 2: U = Tp R0; (diag(e^{b_C - b_t}) X)^T
+        {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const int kend = (16 * wave + 16 + Mma<E>::KS - 1) / Mma<E>::KS * Mma<E>::KS;
+            acc = Mma<E>::run(acc, Tp + 16 * wave * C, C, R0t, LT, 0, kend);
+            st4(Ut + (lane & 15) * LT + 16 * wave + 4 * (lane >> 4), acc);
+            for (int idx = tid; idx < C * DK; idx += 256) {
+                const int i = idx / DK, d = idx % DK;
+                st(Xht, d * LT + i, scal[C + i] * ld(X, idx));
+            }
+        }
+        __syncthreads();
+
+        // phase 3a: outputs of the chunk's tokens (rows 16w..16w+15 < Ct)
+        if (16 * wave < ct) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = Mma<E>::run(acc, St[cur], LS, Qh + size_t(16 * wave) * DK, DK, 0, DK);
+            const int i = 16 * wave + (lane & 15);
+            const float gi = scal[2 * C + i];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] *= gi;
+            acc = Mma<E>::run(acc, Ut, LT, Pg + size_t(16 * wave) * C, C, 0, C);
+            const int t = c * ct + i;
+            if (i < ct && t < T) st4(O + size_t(t) * dv + j0 + 4 * (lane >> 4), acc);
+        }
+        // phase 3b: S = Gamma_C S + (diag(e^{b_C - b_t}) X)^T U
+        {
+            const float gC = scal[3 * C];
+            if (owns) {
+#pragma unroll
+                for (int m = 0; m < NT; ++m) {
+                    const int dbase = 16 * (wave * NT + m);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) S[m][r] *= gC;
+                    S[m] = Mma<E>::run(S[m], Xht + dbase * LT, LT, Ut, LT, 0, C);
+                    st4(St[cur ^ 1] + (lane & 15) * LS + dbase + 4 * (lane >> 4), S[m]);
+                }
+            }
+        }
+        cur ^= 1;
+        __syncthreads();
+    }
+
+    if (a.S_out && owns) {
+#pragma unroll
+        for (int m = 0; m < NT; ++m) {
+            const int dbase = 16 * (wave * NT + m);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int d = dbase + 4 * (lane >> 4) + r;
+                a.S_out[(size_t(bh) * DK + d) * dv + j0 + (lane & 15)] = S[m][r];
+            }
+        }
+    }
+}
+
+template <class E, int DK>
+void launch_t(const ChunkF3Args &a, hipStream_t s, Marks *m) {
+    f3_prep<E, DK><<<dim3(a.nchunks, a.BH), 256, 0, s>>>(a);
+    m->mark(s);
+    const int nslice = a.dv / 16;
+    const int blocks = ((a.BH + 7) / 8) * 8 * nslice;
+    f3_scan<E, DK><<<blocks, 256, 0, s>>>(a, nslice);
+    m->mark(s);
+}
+
+}  // namespace
+
+void launch_chunk_f3(const ChunkF3Args &a, bool bf16, hipStream_t s, Marks *m) {
+    if (bf16) {
+        if (a.dk == 32) launch_t<bf16_t, 32>(a, s, m);
+        else if (a.dk == 64) launch_t<bf16_t, 64>(a, s, m);
+        else launch_t<bf16_t, 128>(a, s, m);
+    } else {
+        if (a.dk == 32) launch_t<float, 32>(a, s, m);
+        else if (a.dk == 64) launch_t<float, 64>(a, s, m);
+        else launch_t<float, 128>(a, s, m);
+    }
+}
+
+}  // namespace falcon

@@ -24,6 +24,19 @@ constexpr size_t chunk_f1_bytes(int /*dk*/, int /*dv*/, int dtype_is_f32) {
     return chunk_f1_scal_off(esz) + 4 * size_t(kChunk) * 4;
 }
 
+// Falcon-3 (window W): a chunk holds 64 / W tokens; each token contributes
+// its W window rows, so the stacked system has at most 64 rows.  Per chunk,
+// in the storage type E:  Tp [64][64], P [64][64] (token rows x stacked rows),
+// the stacked write features X [64][dk]; then fp32 [4][64]: per stacked row
+// Gamma_{t-1}, e^{b_C - b_t}; per token Gamma_t; {Gamma_C, 0...}.
+constexpr int chunk_f3_tokens(int window) { return kChunk / window; }
+constexpr bool chunk_f3_supported(int dk, int dv) { return chunk_f1_supported(dk, dv); }
+constexpr size_t chunk_f3_x_off(size_t esz) { return 2 * size_t(kChunk) * kChunk * esz; }
+constexpr size_t chunk_f3_scal_off(int dk, size_t esz) { return chunk_f3_x_off(esz) + size_t(kChunk) * dk * esz; }
+constexpr size_t chunk_f3_bytes(int dk, int dtype_is_f32) {
+    return chunk_f3_scal_off(dk, dtype_is_f32 ? 4 : 2) + 4 * size_t(kChunk) * 4;
+}
+
 // Fused bf16 Falcon-1 kernel: d_k = 64, value columns split into slices of
 // 32 or 64 per workgroup.  More slices give more workgroups (and repeat the
 // state-independent chunk work per slice); the slice width is chosen so that

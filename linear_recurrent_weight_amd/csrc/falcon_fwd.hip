@@ -13,6 +13,7 @@ const char *const kNamesChunkF1[] = {"feature", "chunk_f1_prep", "chunk_f1_scan"
 const char *const kNamesChunkF1Fused[] = {"chunk_f1_fused"};
 const char *const kNamesChunkA[] = {"a_segment", "a_segscan", "a_output"};
 const char *const kNamesChunkF2[] = {"chunk_f2"};
+const char *const kNamesChunkF3[] = {"feature", "f3_prep", "f3_scan"};
 
 int run(const falcon_fwd_args *args, void *stream, Marks *m) {
     Plan p;
@@ -201,6 +202,30 @@ int run(const falcon_fwd_args *args, void *stream, Marks *m) {
             ca.ops = p.ws_at<void>(p.off_chunk);
             ca.chunk_bytes = p.chunk_bytes;
             launch_chunk_f1(ca, io_bf16, s, m);
+        } else if (p.path == Path::kChunkF3) {
+            ChunkF3Args ca{};
+            ca.BH = p.BH;
+            ca.T = p.T;
+            ca.Tpad = p.Tpad;
+            ca.nchunks = p.nchunks;
+            ca.ct = p.ct;
+            ca.window = p.window;
+            ca.dk = p.dk;
+            ca.dv = p.dv;
+            ca.n_tail_in = p.n_tail_in;
+            ca.xn = fa.xn;
+            ca.qn = fa.qn;
+            ca.eta = fa.eta;
+            ca.alpha = fa.alpha;
+            ca.tailx_in = p.tailx_in;
+            ca.taily_in = p.taily_in;
+            ca.v = p.v;
+            ca.o = p.o;
+            ca.S_in = p.S_in;
+            ca.S_out = p.S_out;
+            ca.ops = p.ws_at<void>(p.off_chunk);
+            ca.chunk_bytes = p.chunk_bytes;
+            launch_chunk_f3(ca, io_bf16, s, m);
         }
     }
     if (hipGetLastError() != hipSuccess) return FALCON_ERR_HIP;
@@ -233,6 +258,7 @@ extern "C" const char *falcon_kernel_name(const falcon_fwd_args *args, int i) {
         case Path::kChunkF1Fused: return i < 1 ? kNamesChunkF1Fused[i] : nullptr;
         case Path::kChunkA: return i < 3 ? kNamesChunkA[i] : nullptr;
         case Path::kChunkF2: return i < 1 ? kNamesChunkF2[i] : nullptr;
+        case Path::kChunkF3: return i < 3 ? kNamesChunkF3[i] : nullptr;
         default: return nullptr;
     }
 }

@@ -97,6 +97,19 @@ struct ChunkF2Args {
     void *o;
 };
 
+struct ChunkF3Args {
+    int BH, T, Tpad, nchunks, ct, window, dk, dv, n_tail_in;
+    const void *xn, *qn;    // features [BH, Tpad, dk] (bf16 or fp32)
+    const float *eta, *alpha;
+    const float *tailx_in, *taily_in;   // incoming window pairs (nullptr when none)
+    const void *v;          // [BH, T, dv]
+    void *o;
+    const float *S_in;
+    float *S_out;
+    void *ops;              // per-chunk operators
+    size_t chunk_bytes;
+};
+
 void launch_features(const FeatureArgs &a, bool in_bf16, bool feat_bf16, hipStream_t s, Marks *m);
 void launch_passthrough(const PassArgs &a, hipStream_t s, Marks *m);
 void launch_recurrent(const RecurrentArgs &a, bool io_bf16, hipStream_t s, Marks *m);
@@ -104,5 +117,6 @@ void launch_chunk_f1(const ChunkF1Args &a, bool bf16, hipStream_t s, Marks *m);
 void launch_chunk_f1_fused(const F1FusedArgs &a, int ds, hipStream_t s, Marks *m);
 void launch_chunk_a(const ChunkAArgs &a, bool bf16, hipStream_t s, Marks *m);
 void launch_chunk_f2(const ChunkF2Args &a, bool bf16, hipStream_t s, Marks *m);
+void launch_chunk_f3(const ChunkF3Args &a, bool bf16, hipStream_t s, Marks *m);
 
 }  // namespace falcon

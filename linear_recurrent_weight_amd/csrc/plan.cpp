@@ -80,6 +80,8 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
             p->path = Path::kChunkF1;
         } else if (var == FALCON_V2 && chunk_f2_supported(a->dtype == FALCON_BF16, a->dk, a->dv)) {
             p->path = Path::kChunkF2;
+        } else if (var == FALCON_V3 && chunk_f3_supported(a->dk, a->dv)) {
+            p->path = Path::kChunkF3;
         } else if ((var == FALCON_V1A || var == FALCON_V3A) && chunk_a_supported(a->dk, a->dv)) {
             p->path = Path::kChunkA;
         } else {
@@ -126,8 +128,16 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
         p->off_seg_s = off; off = align_up(off + st);           // segment entry states
     } else if (p->path != Path::kEmpty) {
         const bool chunked = p->path != Path::kRecurrent;
-        p->nchunks = chunked ? (T + kChunk - 1) / kChunk : 0;
-        p->Tpad = chunked ? p->nchunks * kChunk : T;
+        if (p->path == Path::kChunkF3) {
+            // stacked rows: 64 / W tokens per chunk; the feature buffers get
+            // one extra tile so that the last chunk's 64-row reads stay inside
+            p->ct = chunk_f3_tokens(a->window);
+            p->nchunks = (T + p->ct - 1) / p->ct;
+            p->Tpad = (p->nchunks * p->ct + kChunk - 1) / kChunk * kChunk + kChunk;
+        } else {
+            p->nchunks = chunked ? (T + kChunk - 1) / kChunk : 0;
+            p->Tpad = chunked ? p->nchunks * kChunk : T;
+        }
         p->feat_f32 = !chunked || a->dtype == FALCON_F32;
         const size_t rows = static_cast<size_t>(bh) * p->Tpad;
         const size_t fsz = p->feat_f32 ? 4 : 2;
@@ -136,9 +146,10 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
         const size_t ncol = (var == FALCON_V2) ? a->dv : 1;
         p->off_eta = off; off = align_up(off + rows * ncol * 4);
         p->off_alpha = off; off = align_up(off + rows * ncol * 4);
-        if (p->path == Path::kChunkF1) {
+        if (p->path == Path::kChunkF1 || p->path == Path::kChunkF3) {
             const size_t nch = static_cast<size_t>(bh) * p->nchunks;
-            p->chunk_bytes = chunk_f1_bytes(a->dk, a->dv, a->dtype == FALCON_F32);
+            p->chunk_bytes = p->path == Path::kChunkF1 ? chunk_f1_bytes(a->dk, a->dv, a->dtype == FALCON_F32)
+                                                       : chunk_f3_bytes(a->dk, a->dtype == FALCON_F32);
             p->off_chunk = off;
             off = align_up(off + nch * p->chunk_bytes);
         }

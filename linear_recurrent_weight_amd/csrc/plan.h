@@ -17,6 +17,7 @@ enum class Path : int {
     kChunkA = 3,     // chunk-parallel Falcon-1A / Falcon-3A (scalar-decay writes)
     kChunkF2 = 4,    // chunk-parallel Falcon-2
     kChunkF1Fused = 5,  // chunk-parallel Falcon-1, bf16, one fused kernel
+    kChunkF3 = 6,    // chunk-parallel Falcon-3 (stacked window rows)
 };
 
 struct Plan {
@@ -24,7 +25,8 @@ struct Plan {
     int variant = 0, dtype = 0, phi = 0;
     int B = 0, H = 0, T = 0, dk = 0, dv = 0, chunk = 0, window = 1;
     int BH = 0;
-    int nchunks = 0;         // ceil(T / chunk) for chunk paths
+    int nchunks = 0;         // ceil(T / chunk) for chunk paths (T / tokens per chunk for F3)
+    int ct = 0;              // tokens per chunk (Falcon-3 chunk path)
     int Tpad = 0;            // rows of the feature buffers (T, or nchunks * chunk)
     float eps = 0.f, eps_gamma = 0.f, eps_rms = 0.f;
     Path path = Path::kEmpty;

@@ -218,3 +218,14 @@ def test_chunk_f2_coverage(lib):
         assert validate(lib, a) == (fb.OK if ok else fb.ERR_UNSUPPORTED), (dt, dk)
         if ok:
             assert wsize(lib, a) == 0
+
+
+def test_chunk_f3_coverage(lib):
+    """Falcon-3 has a chunk-parallel path (stacked window rows) for every
+    window; it takes workspace for features and per-chunk operators."""
+    for w in (1, 2, 3, 8):
+        a = args(variant="F3", window=w, dk=64, dv=64)
+        n = wsize(lib, a)
+        assert n > 0
+        assert validate(lib, with_ws(lib, a)) == fb.OK
+    assert validate(lib, with_ws(lib, args(variant="F3", window=4, dk=16))) == fb.ERR_UNSUPPORTED

@@ -361,3 +361,69 @@ def test_chunk_f2_continuation(split):
     assert eo <= 1e-5 and es <= 1e-5, (eo, es)
     assert gu.max_rel_err(o_cat.double().cpu().numpy(), o_full.double().cpu().numpy()) <= 1e-5
     assert torch.allclose(st2.x_next, st_full.x_next)
+
+
+# -- Falcon-3 chunk path (stacked window rows) ------------------------------------
+
+def test_named_workload_c5f3_chunk():
+    check(WORKLOADS["c5f3"].with_(chunk=64), heads=gu.sample_heads(WORKLOADS["c5f3"], 4))
+
+
+@pytest.mark.parametrize("window", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 7, 8, 9, 64, 130, 300])
+def test_chunk_f3_windows(window, dtype, T):
+    check(gu.small("F3", dtype, B=2, H=2, T=T, dk=64, dv=32, chunk=64, window=window, seed=T + 10 * window))
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 16), (128, 64), (64, 128)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_f3_head_dims(dk, dv, dtype):
+    check(gu.small("F3", dtype, B=1, H=3, T=200, dk=dk, dv=dv, chunk=64, window=4))
+
+
+def test_chunk_f3_window1_is_falcon1():
+    """At W = 1 the stacked form is the Falcon-1 chunk form."""
+    w1 = gu.small("F1", "f32", B=2, H=2, T=200, dk=64, dv=32, chunk=64, seed=9)
+    inp = gu.make(w1)
+    dev = gu.to_device(inp, w1)
+    o1, st1 = gu.run_gpu(w1, dev)
+    o3, st3 = gu.run_gpu(w1.with_(variant="F3"), dev)
+    assert gu.max_rel_err(o3.double().cpu().numpy(), o1.double().cpu().numpy()) <= 1e-5
+    assert gu.max_rel_err(st3.S.double().cpu().numpy(), st1.S.double().cpu().numpy()) <= 1e-5
+
+
+@pytest.mark.parametrize("window", [3, 8])
+@pytest.mark.parametrize("split", [0, 2, 8, 100])
+def test_chunk_f3_continuation(window, split):
+    """Carrying (S, x_next, the last W-1 pairs) across calls equals one call."""
+    import torch
+    w = gu.small("F3", "f32", B=2, H=2, T=160, dk=32, dv=32, chunk=64, window=window, seed=13)
+    inp = gu.make(w)
+    dev = gu.to_device(inp, w)
+    o_full, st_full = gu.run_gpu(w, dev)
+    a = {k: v[:, :, :split].contiguous() for k, v in dev.items()}
+    b = {k: v[:, :, split:].contiguous() for k, v in dev.items()}
+    o1, st1 = gu.run_gpu(w.with_(seqlen=split), a)
+    o2, st2 = gu.run_gpu(w.with_(seqlen=160 - split), b, state=st1)
+    o_cat = torch.cat([o1, o2], 2)
+    heads = np.arange(4)
+    o_ref, st_ref = gu.oracle_heads(w, inp, heads)
+    eo, es = gu.compare(w, heads, o_cat, st2, o_ref, st_ref)
+    assert eo <= 1e-5 and es <= 1e-5, (eo, es)
+    assert gu.max_rel_err(o_cat.double().cpu().numpy(), o_full.double().cpu().numpy()) <= 1e-5
+    assert st2.n_tail == st_full.n_tail == window - 1
+    assert torch.allclose(st2.tail_x, st_full.tail_x) and torch.allclose(st2.tail_y, st_full.tail_y)
+
+
+def test_chunk_f3_strong_ridge_clamp():
+    w = gu.small("F3", "f32", B=1, H=2, T=300, chunk=64, window=4, lam_lo=200.0, lam_hi=400.0,
+                 eps_gamma=0.05)
+    inp = gu.make(w)
+    inp["beta"] = (1.0 + inp["beta"]).astype(np.float32)
+    dev = gu.to_device(inp, w)
+    o, st = gu.run_gpu(w, dev)
+    o_ref, st_ref, tr = gu.oracle_heads(w, inp, np.arange(2), trace=True)
+    assert (tr.alpha >= 1 - 0.05 - 1e-9).mean() > 0.5
+    eo, es = gu.compare(w, np.arange(2), o, st, o_ref, st_ref)
+    assert eo <= 1e-5 and es <= 1e-5, (eo, es)
