@@ -1,0 +1,539 @@
+// Chunk-parallel Falcon-1 forward for bf16 inputs, d_k = 64, in two kernels
+// (summary Figure 4, §D.1, App. E.2: parallel per-chunk operators, a short
+// sequential carry, parallel output).  With the chunk-local log-prefix b
+// (restarted at 0 in every chunk) and the chunk-entry state S_0:
+//     U   = Tp (Y - diag(e^{b_{i-1}}) X S_0),   Tp = (I + N)^{-1} diag(eta),
+//     N_ij = eta_i e^{b_{i-1}-b_j} x_i.x_j (j < i),
+//     O   = diag(e^{b_i}) Qh S_0 + P U,          P_ij = e^{b_i-b_j} qh_i.x_j (j <= i),
+//     S_C = e^{b_C} S_0 + (diag(e^{b_C-b_i}) X)^T U.
+//
+// f1_ops: one workgroup per chunk, every chunk of every head in parallel.
+//   QK-RMSNorm and the key shift, eta and log gamma, the chunk-local prefix
+//   (and its suffix, so e^{b_C - b_i} is formed from a short sum), Gram and
+//   scores on MFMA, the fp32 inverse of the unit-lower system (diagonal
+//   blocks by substitution, the others on fp32 MFMA), and the operators Tp,
+//   P and (diag(e^{b_C-b_t}) X)^T (bf16) plus the decay rows into the
+//   workspace.
+// f1_walk: one workgroup per (head, slice of DS value columns) walks the
+//   chunks in order.  Chain wave w owns state columns 16w..16w+15 (all d_k
+//   rows in MFMA accumulators) and needs no other chain wave inside a chunk:
+//     XS, Qh S -> R0 -> U = Tp R0 -> O = Gamma Qh S + P U -> S' (MFMA).
+//   Four loader waves stage the next chunk meanwhile: raw q, k, v rows and
+//   the chunk operators prefetched a chunk ahead, QK-RMSNorm, all into the
+//   other LDS buffer.  One workgroup barrier per chunk.
+#include "chunk_layout.h"
+#include "kernels.h"
+#include "mma.h"
+
+namespace falcon {
+namespace {
+
+constexpr int C = kChunk;
+constexpr int kLs = C + 1;    // fp32 LDS row stride
+constexpr int PC = C + 8;     // bf16 stride of [.][token] rows
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
+    return make_uint2(pack2(a, b), pack2(c, d));
+}
+__device__ __forceinline__ void unpack8(const uint4 &u, float *f) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[2 * e] = __uint_as_float(w[e] << 16);
+        f[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ uint4 pack8(const float *f) {
+    return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
+}
+__device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 ld8(const bf16_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+
+// features of one row part: 4 threads per row, EPT elements each
+template <int DK>
+struct RowPart {
+    static constexpr int EPT = DK / 4, NV = EPT / 8;
+    uint4 q[NV], k[NV];
+    __device__ void load(const bf16_t *qg, const bf16_t *kg, int t, int T, int part) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            q[v] = t < T ? *reinterpret_cast<const uint4 *>(qg + size_t(t) * DK + part * EPT + 8 * v)
+                         : make_uint4(0, 0, 0, 0);
+            k[v] = (t >= 1 && t - 1 < T)
+                       ? *reinterpret_cast<const uint4 *>(kg + size_t(t - 1) * DK + part * EPT + 8 * v)
+                       : make_uint4(0, 0, 0, 0);
+        }
+    }
+    // normalised features; returns ||x||^2 of the whole row
+    __device__ float features(float *xv, float *qv, int t, int part, const F1SplitArgs &a, int bh) const {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            unpack8(q[v], qv + 8 * v);
+            unpack8(k[v], xv + 8 * v);
+        }
+        const bool first = (t == 0);   // x_0 comes from the boundary state
+        if (first && a.xnext_in) {
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) xv[e] = a.xnext_in[size_t(bh) * DK + part * EPT + e];
+        }
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            sq += qv[e] * qv[e];
+            sk += xv[e] * xv[e];
+        }
+        sq = group_sum<4>(sq);
+        sk = group_sum<4>(sk);
+        const float scq = phi_scale(sq, DK, a.eps_rms, a.phi);
+        const float sck = first ? 1.f : phi_scale(sk, DK, a.eps_rms, a.phi);
+        float n2 = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            xv[e] *= sck;
+            qv[e] *= scq;
+            n2 += xv[e] * xv[e];
+        }
+        return group_sum<4>(n2);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// f1_ops: per-chunk operators
+// ---------------------------------------------------------------------------
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int DK>
+__global__ __launch_bounds__(256) void f1_ops(F1SplitArgs a) {
+    constexpr int PK = DK + 8;
+    using RP = RowPart<DK>;
+    // LDS: the system N stays; the feature / score staging area is reused
+    // for the inverse once the features are no longer needed
+    __shared__ float Nm[C * kLs];
+    __shared__ __align__(16) unsigned char pool[3 * C * PK * 2 > C * kLs * 4 ? 3 * C * PK * 2 : C * kLs * 4];
+    __shared__ float Mw[4][16 * 17];          // per wave: M blocks of the inverse
+    __shared__ float eta_s[C], lg_s[C], b_s[C], bp_s[C], ew_s[C];
+    bf16_t *XB = reinterpret_cast<bf16_t *>(pool);
+    bf16_t *QB = XB + C * PK;
+    bf16_t *PS = QB + C * PK;                 // stride PC <= PK
+    float *Tm = reinterpret_cast<float *>(pool);
+
+    const int c = blockIdx.x, bh = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int T = a.T;
+    const int row = tid >> 2, part = tid & 3;
+    const int t = c * C + row;
+    const int col = lane & 15, g4 = 4 * (lane >> 4), kq = lane >> 4;
+    const bf16_t *qg = static_cast<const bf16_t *>(a.q) + size_t(bh) * T * DK;
+    const bf16_t *kg = static_cast<const bf16_t *>(a.k) + size_t(bh) * T * DK;
+    char *ops = static_cast<char *>(a.ops) + (size_t(bh) * a.nchunks + c) * kF1SplitChunkBytes;
+    bf16_t *Tp = reinterpret_cast<bf16_t *>(ops);
+    bf16_t *Pg = reinterpret_cast<bf16_t *>(ops + kF1SplitPOff);
+    bf16_t *Xw = reinterpret_cast<bf16_t *>(ops + kF1SplitXwOff);
+    float *scal = reinterpret_cast<float *>(ops + kF1SplitScalOff);
+
+    // 1. features and step scalars (log gamma in base 2)
+    {
+        RP rp;
+        rp.load(qg, kg, t, T, part);
+        float beta = 0.f, lam = 0.f;
+        if (part == 0 && t < T) {
+            beta = a.beta[size_t(bh) * T + t];
+            lam = a.lambda[size_t(bh) * T + t];
+        }
+        float xv[RP::EPT], qv[RP::EPT];
+        const float n2 = rp.features(xv, qv, t, part, a, bh);
+#pragma unroll
+        for (int v = 0; v < RP::NV; ++v) {
+            *reinterpret_cast<uint4 *>(XB + row * PK + part * RP::EPT + 8 * v) = pack8(xv + 8 * v);
+            *reinterpret_cast<uint4 *>(QB + row * PK + part * RP::EPT + 8 * v) = pack8(qv + 8 * v);
+        }
+        if (part == 0) {
+            float eta = 0.f, alpha = 0.f;
+            const bool noop = t >= T || (t == 0 && a.fresh);
+            if (!noop) {
+                eta = step_eta(beta, n2 + lam + a.eps);
+                alpha = step_alpha(eta, lam, a.eps_gamma);
+            }
+            eta_s[row] = eta;
+            lg_s[row] = log1pf(-alpha) * kLog2e;
+        }
+    }
+    __syncthreads();
+
+    // 2. chunk-local prefix (base 2) and its suffix, so that e^{b_C - b_i}
+    //    comes from a short sum (wave 0, lane = token)
+    if (wave == 0) {
+        const float lg = lg_s[lane];
+        const float b = wave_inclusive_scan(lg);
+        float bp = __shfl_up(b, 1, 64);
+        if (lane == 0) bp = 0.f;
+        float sf = lg;   // inclusive suffix
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float y = __shfl_down(sf, o, 64);
+            if (lane + o < 64) sf += y;
+        }
+        float sfx = __shfl_down(sf, 1, 64);
+        if (lane == 63) sfx = 0.f;
+        const float bC = __shfl(b, 63, 64);
+        b_s[lane] = b;
+        bp_s[lane] = bp;
+        const float ew = exp2_(sfx);
+        ew_s[lane] = ew;
+        scal[0 * C + lane] = exp2_(bp);
+        scal[1 * C + lane] = exp2_(b);
+        scal[2 * C + lane] = ew;
+        scal[3 * C + lane] = lane == 0 ? exp2_(bC) : 0.f;
+    }
+    __syncthreads();
+
+    // 3. Gram and score tiles (lower 16x16 tiles) with decays and masks
+    for (int job = wave; job < 20; job += 4) {
+        const bool isG = job < 10;
+        int tt = isG ? job : job - 10, I = 0;
+        while (tt > I) {
+            tt -= I + 1;
+            ++I;
+        }
+        const int J = tt;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < DK; k0 += 32)
+            acc = mfma(ld8((isG ? XB : QB) + (16 * I + col) * PK + k0 + 2 * g4), ld8(XB + (16 * J + col) * PK + k0 + 2 * g4), acc);
+        const int j = 16 * J + col;
+        const float bj = b_s[j];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * I + g4 + r;
+            if (isG) Nm[i * kLs + j] = j < i ? eta_s[i] * exp2_(bp_s[i] - bj) * acc[r] : 0.f;
+            else st(PS, size_t(i) * PC + j, j <= i ? exp2_(b_s[i] - bj) * acc[r] : 0.f);
+        }
+    }
+    for (int idx = tid; idx < C * C; idx += 256) {
+        const int i = idx / C, j = idx % C;
+        if ((j >> 4) > (i >> 4)) st(PS, size_t(i) * PC + j, 0.f);
+    }
+    __syncthreads();
+
+    // 4. scores and the scaled transposed keys to the workspace; diagonal
+    //    blocks of the inverse by forward substitution (wave J: block J,
+    //    lane k < 16: column k), kept in registers until the staging area
+    //    is free
+    {
+        const uint4 *sp = reinterpret_cast<const uint4 *>(PS + row * PC + part * 16);
+        uint4 *dp = reinterpret_cast<uint4 *>(Pg + row * C + part * 16);
+        dp[0] = sp[0];
+        dp[1] = sp[1];
+        // Xw[d][t] for d = row, t = 16 part .. + 15
+        float xw[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int tt = part * 16 + e;
+            xw[e] = ew_s[tt] * bf16_to_f32(XB[tt * PK + row].bits);
+        }
+        uint4 *dx = reinterpret_cast<uint4 *>(Xw + row * C + part * 16);
+        dx[0] = pack8(xw);
+        dx[1] = pack8(xw + 8);
+    }
+    float tcol[16];
+    {
+        const int base = 16 * wave;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float v = (r == col) ? 1.f : 0.f;
+#pragma unroll
+            for (int k = 0; k < r; ++k) v -= Nm[(base + r) * kLs + base + k] * tcol[k];
+            tcol[r] = v;
+        }
+    }
+    __syncthreads();
+    if (lane < 16) {
+        const int base = 16 * wave;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Tm[(base + r) * kLs + base + col] = tcol[r];
+    }
+    __syncthreads();
+
+    // 5. off-diagonal blocks, column block J = wave, rows I = J+1..3 in order:
+    //    T_IJ = -T_II sum_{K=J}^{I-1} N_IK T_KJ  (fp32 MFMA)
+    {
+        const int J = wave;
+        float *mw = Mw[J];
+        for (int I = J + 1; I < 4; ++I) {
+            f32x4 M = {0.f, 0.f, 0.f, 0.f};
+            for (int K = J; K < I; ++K) {
+#pragma unroll
+                for (int k0 = 0; k0 < 16; k0 += 4)
+                    M = mfma_f32(Nm[(16 * I + col) * kLs + 16 * K + k0 + kq], Tm[(16 * K + k0 + kq) * kLs + 16 * J + col], M);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mw[(g4 + r) * 17 + col] = M[r];
+            wave_lds_sync();
+            f32x4 Tij = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k0 = 0; k0 < 16; k0 += 4)
+                Tij = mfma_f32(Tm[(16 * I + col) * kLs + 16 * I + k0 + kq], mw[(k0 + kq) * 17 + col], Tij);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Tm[(16 * I + g4 + r) * kLs + 16 * J + col] = -Tij[r];
+            wave_lds_sync();
+        }
+    }
+    __syncthreads();
+
+    // 6. Tp = L^{-1} diag(eta) to the workspace (row part of 16)
+    {
+        float tv[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int j = part * 16 + e;
+            tv[e] = j <= row ? Tm[row * kLs + j] * eta_s[j] : 0.f;
+        }
+        uint4 *dt = reinterpret_cast<uint4 *>(Tp + row * C + part * 16);
+        dt[0] = pack8(tv);
+        dt[1] = pack8(tv + 8);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// f1_walk: sequential walk over the chunks of one (head, DS-column slice)
+// ---------------------------------------------------------------------------
+template <int DK, int DS>
+__global__ __launch_bounds__((DS / 16 + 4) * 64) void f1_walk(F1SplitArgs a, int nslice) {
+    constexpr int NCW = DS / 16;          // chain waves
+    constexpr int PK = DK + 8;
+    constexpr int PY = DS + 8;            // bf16 stride of value rows
+    constexpr int YE = DS / 4;            // value elements per loader thread
+    constexpr int YV = YE / 8;            // 16-byte vectors of them
+    using RP = RowPart<DK>;
+    static_assert(DK == 64, "loader threads cover 64 rows x 4 parts of 16 features");
+    static_assert(DS == 32 || DS == 64, "slice of 32 or 64 value columns");
+
+    __shared__ __align__(16) bf16_t XB[2][C * PK];     // x rows [t][d]
+    __shared__ __align__(16) bf16_t QB[2][C * PK];     // qh rows [t][d]
+    __shared__ __align__(16) bf16_t XWT[2][DK * PC];   // (e^{b_C-b_t} x_t)^T [d][t]
+    __shared__ __align__(16) bf16_t YB[2][C * PY];     // values [t][j]
+    __shared__ __align__(16) bf16_t TPB[2][C * PC];    // Tp [t][s]
+    __shared__ __align__(16) bf16_t PB[2][C * PC];     // P [t][s]
+    __shared__ float SC[2][4 * C];                     // decay rows
+    __shared__ __align__(16) bf16_t STw[NCW][16 * PK]; // per chain wave: S^T [j][d]
+    __shared__ __align__(16) bf16_t RTw[NCW][16 * PC]; // per chain wave: R0^T [j][t]
+    __shared__ __align__(16) bf16_t UTw[NCW][16 * PC]; // per chain wave: U^T [j][t]
+
+    int bh, s;
+    if (nslice == 1) {
+        bh = blockIdx.x;
+        s = 0;
+    } else {
+        const int id = blockIdx.x, u = id & 7, rest = id >> 3;
+        s = rest % nslice;
+        bh = (rest / nslice) * 8 + u;
+    }
+    if (bh >= a.BH) return;   // the whole workgroup leaves together
+    const int j0 = s * DS;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool chain = wave < NCW;
+    const int T = a.T, DV = a.dv, nch = a.nchunks;
+    const bf16_t *qg = static_cast<const bf16_t *>(a.q) + size_t(bh) * T * DK;
+    const bf16_t *kg = static_cast<const bf16_t *>(a.k) + size_t(bh) * T * DK;
+    const bf16_t *vg = static_cast<const bf16_t *>(a.v) + size_t(bh) * T * DV;
+    bf16_t *og = static_cast<bf16_t *>(a.o) + size_t(bh) * T * DV;
+    const char *opsb = static_cast<const char *>(a.ops) + size_t(bh) * nch * kF1SplitChunkBytes;
+
+    // ---- loaders: rows and operators of the next chunk, prefetched ----
+    const int lt = tid - NCW * 64;        // loader thread index (valid for loaders)
+    const int lrow = lt >> 2, lpart = lt & 3;
+    RP rp;
+    uint4 ry[YV];
+    uint4 rtp0, rtp1, rpp0, rpp1, rxw0, rxw1;   // separate names keep them in registers
+    float rsc = 0.f;
+    auto prefetch = [&](int c) {
+        const int t = c * C + lrow;
+        rp.load(qg, kg, t, T, lpart);
+#pragma unroll
+        for (int v = 0; v < YV; ++v)
+            ry[v] = t < T ? *reinterpret_cast<const uint4 *>(vg + size_t(t) * DV + j0 + lpart * YE + 8 * v)
+                          : make_uint4(0, 0, 0, 0);
+        const char *ops = opsb + size_t(c) * kF1SplitChunkBytes;
+        const uint4 *tp = reinterpret_cast<const uint4 *>(ops);
+        const uint4 *pp = reinterpret_cast<const uint4 *>(ops + kF1SplitPOff);
+        const uint4 *xp = reinterpret_cast<const uint4 *>(ops + kF1SplitXwOff);
+        rtp0 = tp[lt];
+        rtp1 = tp[lt + 256];
+        rpp0 = pp[lt];
+        rpp1 = pp[lt + 256];
+        rxw0 = xp[lt];
+        rxw1 = xp[lt + 256];
+        rsc = reinterpret_cast<const float *>(ops + kF1SplitScalOff)[lt];
+    };
+    auto stage = [&](int c) {   // prefetched rows of chunk c -> LDS buffer c & 1
+        const int b = c & 1;
+        const int t = c * C + lrow;
+        float xv[RP::EPT], qv[RP::EPT];
+        (void)rp.features(xv, qv, t, lpart, a, bh);
+#pragma unroll
+        for (int v = 0; v < RP::NV; ++v) {
+            *reinterpret_cast<uint4 *>(XB[b] + lrow * PK + lpart * RP::EPT + 8 * v) = pack8(xv + 8 * v);
+            *reinterpret_cast<uint4 *>(QB[b] + lrow * PK + lpart * RP::EPT + 8 * v) = pack8(qv + 8 * v);
+        }
+#pragma unroll
+        for (int v = 0; v < YV; ++v)
+            *reinterpret_cast<uint4 *>(YB[b] + lrow * PY + lpart * YE + 8 * v) = ry[v];
+        {
+            // 16-byte piece u of a 64 x 64 tile: row u / 8, columns 8 (u % 8) ..
+            const int r0 = lt >> 3, r1 = (lt + 256) >> 3, c8 = 8 * (lt & 7);
+            *reinterpret_cast<uint4 *>(TPB[b] + r0 * PC + c8) = rtp0;
+            *reinterpret_cast<uint4 *>(TPB[b] + r1 * PC + c8) = rtp1;
+            *reinterpret_cast<uint4 *>(PB[b] + r0 * PC + c8) = rpp0;
+            *reinterpret_cast<uint4 *>(PB[b] + r1 * PC + c8) = rpp1;
+            *reinterpret_cast<uint4 *>(XWT[b] + r0 * PC + c8) = rxw0;
+            *reinterpret_cast<uint4 *>(XWT[b] + r1 * PC + c8) = rxw1;
+        }
+        SC[b][lt] = rsc;
+    };
+
+    // ---- chain state: S[:, j0 + 16w ..] in accumulators (d tiles m) ----
+    f32x4 S[DK / 16];
+    bf16_t *st_w = STw[chain ? wave : 0];
+    bf16_t *rt_w = RTw[chain ? wave : 0];
+    bf16_t *ut_w = UTw[chain ? wave : 0];
+    const int col = lane & 15, g4 = 4 * (lane >> 4), k8 = 8 * (lane >> 4);
+    if (chain) {
+#pragma unroll
+        for (int m = 0; m < DK / 16; ++m) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int d = 16 * m + g4 + r;
+                S[m][r] = a.S_in ? a.S_in[(size_t(bh) * DK + d) * DV + j0 + 16 * wave + col] : 0.f;
+            }
+            *reinterpret_cast<uint2 *>(st_w + col * PK + 16 * m + g4) = pack4(S[m][0], S[m][1], S[m][2], S[m][3]);
+        }
+    } else {
+        prefetch(0);
+        stage(0);
+        if (nch > 1) prefetch(1);
+    }
+    __syncthreads();
+
+    for (int c = 0; c < nch; ++c) {
+        const int b = c & 1;
+        if (chain) {
+            const bf16_t *X = XB[b], *Q = QB[b], *Tp = TPB[b], *P = PB[b];
+            const bf16_t *Y = YB[b] + 16 * wave + col;
+            const float *sc = SC[b];
+            // S^T operand (rows j, k = d), shared by XS and Qh S
+            bf16x8 sb[DK / 32];
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) sb[kk] = ld8(st_w + col * PK + 32 * kk + k8);
+            // XS and (Qh S)^T; R0 = Y - Gamma_{t-1} XS
+            f32x4 qs[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                f32x4 xs = {0.f, 0.f, 0.f, 0.f};
+                qs[m] = xs;
+                const int row = 16 * m + col;
+#pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk) {
+                    xs = mfma(ld8(X + row * PK + 32 * kk + k8), sb[kk], xs);
+                    qs[m] = mfma(sb[kk], ld8(Q + row * PK + 32 * kk + k8), qs[m]);
+                }
+                float r0[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * m + g4 + r;
+                    r0[r] = bf16_to_f32(Y[t * PY].bits) - sc[t] * xs[r];
+                }
+                *reinterpret_cast<uint2 *>(rt_w + col * PC + 16 * m + g4) = pack4(r0[0], r0[1], r0[2], r0[3]);
+            }
+            wave_lds_sync();
+            // U = Tp R0 (lower triangular: token tile m needs s < 16m + 16)
+            {
+                const bf16x8 rb0 = ld8(rt_w + col * PC + k8), rb1 = ld8(rt_w + col * PC + 32 + k8);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int row = 16 * m + col;
+                    f32x4 u = {0.f, 0.f, 0.f, 0.f};
+                    u = mfma(ld8(Tp + row * PC + k8), rb0, u);
+                    if (m >= 2) u = mfma(ld8(Tp + row * PC + 32 + k8), rb1, u);
+                    *reinterpret_cast<uint2 *>(ut_w + col * PC + 16 * m + g4) = pack4(u[0], u[1], u[2], u[3]);
+                }
+            }
+            wave_lds_sync();
+            const bf16x8 ub0 = ld8(ut_w + col * PC + k8), ub1 = ld8(ut_w + col * PC + 32 + k8);
+            // O^T = diag(Gamma_t) (Qh S)^T + U^T P^T, stored as rows t of 4 columns
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int t = 16 * m + col;
+                const float gt = sc[C + t];
+                f32x4 o = qs[m];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[r] *= gt;
+                o = mfma(ub0, ld8(P + t * PC + k8), o);
+                if (m >= 2) o = mfma(ub1, ld8(P + t * PC + 32 + k8), o);
+                const int tg = c * C + t;
+                if (tg < T)
+                    *reinterpret_cast<uint2 *>(og + size_t(tg) * DV + j0 + 16 * wave + g4) = pack4(o[0], o[1], o[2], o[3]);
+            }
+            // S = Gamma_C S + (diag(e^{b_C-b_t}) X)^T U
+            const float gC = sc[3 * C];
+            const bf16_t *XW = XWT[b];
+#pragma unroll
+            for (int m = 0; m < DK / 16; ++m) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) S[m][r] *= gC;
+                S[m] = mfma(ld8(XW + (16 * m + col) * PC + k8), ub0, S[m]);
+                S[m] = mfma(ld8(XW + (16 * m + col) * PC + 32 + k8), ub1, S[m]);
+                *reinterpret_cast<uint2 *>(st_w + col * PK + 16 * m + g4) = pack4(S[m][0], S[m][1], S[m][2], S[m][3]);
+            }
+            wave_lds_sync();
+        } else if (c + 1 < nch) {
+            stage(c + 1);
+            if (c + 2 < nch) prefetch(c + 2);
+        }
+        __syncthreads();
+    }
+
+    // ---- boundary state ----
+    if (chain && a.S_out) {
+#pragma unroll
+        for (int m = 0; m < DK / 16; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                a.S_out[(size_t(bh) * DK + 16 * m + g4 + r) * DV + j0 + 16 * wave + col] = S[m][r];
+    }
+    if (wave == NCW && s == 0 && a.xnext_out && T > 0) {
+        const float xv = bf16_to_f32(kg[size_t(T - 1) * DK + lane].bits);
+        const float sc = phi_scale(wave_sum(xv * xv), DK, a.eps_rms, a.phi);
+        a.xnext_out[size_t(bh) * DK + lane] = xv * sc;
+    }
+}
+
+template <int DS>
+void launch_walk(const F1SplitArgs &a, hipStream_t s, Marks *m) {
+    const int nslice = a.dv / DS;
+    const int blocks = nslice == 1 ? a.BH : ((a.BH + 7) / 8) * 8 * nslice;
+    f1_walk<64, DS><<<blocks, (DS / 16 + 4) * 64, 0, s>>>(a, nslice);
+    m->mark(s);
+}
+
+}  // namespace
+
+void launch_chunk_f1_split(const F1SplitArgs &a, int ds, hipStream_t s, Marks *m) {
+    f1_ops<64><<<dim3(a.nchunks, a.BH), 256, 0, s>>>(a);
+    m->mark(s);
+    if (ds == 64) launch_walk<64>(a, s, m);
+    else launch_walk<32>(a, s, m);
+}
+
+}  // namespace falcon

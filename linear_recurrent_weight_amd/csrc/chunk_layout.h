@@ -59,6 +59,32 @@ constexpr bool chunk_f2_supported(bool bf16, int dk, int dv) {
     return (bf16 ? (dk == 64 || dk == 128) : dk == 64) && dv % 16 == 0;
 }
 
+// Two-kernel bf16 Falcon-1 path (d_k = 64): per chunk, bf16 Tp [64][64],
+// P [64][64] and (diag(e^{b_C - b_t}) X)^T [64 d][64 t], then fp32 [4][64]:
+// Gamma_{i-1}, Gamma_i, e^{b_C - b_i}, {Gamma_C, 0...}.  The walk kernel
+// takes slices of 32 or 64 value columns.
+constexpr size_t kF1SplitPOff = size_t(kChunk) * kChunk * 2;
+constexpr size_t kF1SplitXwOff = 2 * size_t(kChunk) * kChunk * 2;
+constexpr size_t kF1SplitScalOff = 3 * size_t(kChunk) * kChunk * 2;
+constexpr size_t kF1SplitChunkBytes = kF1SplitScalOff + 4 * size_t(kChunk) * 4;
+constexpr bool chunk_f1_split_supported(bool bf16, int dk, int dv) {
+    return bf16 && dk == 64 && (dv == 32 || dv == 64 || dv == 128);
+}
+// which bf16 d_k = 64 Falcon-1 kernel: the two-kernel path unless
+// FALCON_F1_PATH=fused (tuning and test switch)
+inline bool chunk_f1_use_fused() {
+    const char *e = std::getenv("FALCON_F1_PATH");
+    return e && e[0] == 'f';
+}
+inline int chunk_f1_split_slice(int dv) {
+    if (dv == 32) return 32;
+    if (const char *e = std::getenv("FALCON_F1_SLICE")) {   // tuning override: 32 or 64
+        const int v = std::atoi(e);
+        if (v == 32 || v == 64) return v;
+    }
+    return 64;
+}
+
 // Falcon-1A / Falcon-3A chunk path: d_k in {32, 64}, d_v in {16, 32, 64}.
 constexpr bool chunk_a_supported(int dk, int dv) {
     return (dk == 32 || dk == 64) && (dv == 16 || dv == 32 || dv == 64);

@@ -36,25 +36,51 @@ template <> struct elem<bf16_t> {
 template <class E> __device__ __forceinline__ float ld(const E *p, size_t i) { return elem<E>::load(p, i); }
 template <class E> __device__ __forceinline__ void st(E *p, size_t i, float v) { elem<E>::store(p, i, v); }
 
+// Cross-lane moves through DPP (no LDS round trip).  `src` moved by the
+// DPP control `ctrl`; lanes whose source is outside the row, or whose row is
+// masked off, read 0.
+template <int ctrl, int row_mask = 0xf>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, row_mask,
+                                                                 0xf, true));
+}
+// DPP controls (gfx9): quad permutations, row shifts, mirrors, broadcasts
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
 // Sum over the lanes of a group of `width` consecutive lanes (width a power
 // of two <= 64); every lane of the group receives the total.
 template <int width>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int off = width / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    static_assert(width >= 1 && width <= 64 && (width & (width - 1)) == 0, "power of two");
+    if constexpr (width >= 2) v += dpp<kDppQuadXor1>(v);
+    if constexpr (width >= 4) v += dpp<kDppQuadXor2>(v);
+    if constexpr (width >= 8) v += dpp<kDppRowHalfMirror>(v);   // other quad of the half row
+    if constexpr (width >= 16) v += dpp<kDppRowMirror>(v);      // other half of the row
+    if constexpr (width >= 32) v += __shfl_xor(v, 16, 64);
+    if constexpr (width >= 64) v += __shfl_xor(v, 32, 64);
     return v;
 }
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Inclusive prefix sum over the 64 lanes of a wave: scans inside each row of
+// 16 lanes by shifted adds, then carries the row totals forward.
 __device__ __forceinline__ float wave_inclusive_scan(float v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        float u = __shfl_up(v, off, 64);
-        if (lane >= off) v += u;
-    }
+    v += dpp<kDppRowShr1>(v);
+    v += dpp<kDppRowShr2>(v);
+    v += dpp<kDppRowShr4>(v);
+    v += dpp<kDppRowShr8>(v);
+    v += dpp<kDppRowBcast15, 0xa>(v);   // rows 1, 3 += last lane of rows 0, 2
+    v += dpp<kDppRowBcast31, 0xc>(v);   // rows 2, 3 += last lane of row 1
     return v;
 }
 

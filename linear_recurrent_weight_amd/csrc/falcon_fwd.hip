@@ -14,6 +14,7 @@ const char *const kNamesChunkF1Fused[] = {"chunk_f1_fused"};
 const char *const kNamesChunkA[] = {"a_segment", "a_segscan", "a_output"};
 const char *const kNamesChunkF2[] = {"chunk_f2"};
 const char *const kNamesChunkF3[] = {"feature", "f3_prep", "f3_scan"};
+const char *const kNamesChunkF1Split[] = {"f1_ops", "f1_walk"};
 
 int run(const falcon_fwd_args *args, void *stream, Marks *m) {
     Plan p;
@@ -106,6 +107,30 @@ int run(const falcon_fwd_args *args, void *stream, Marks *m) {
         fa.xnext_out = p.xnext_out;
         fa.o = p.o;
         launch_chunk_f2(fa, p.dtype == FALCON_BF16, s, m);
+    } else if (p.path == Path::kChunkF1Split) {
+        F1SplitArgs fa{};
+        fa.BH = p.BH;
+        fa.T = p.T;
+        fa.nchunks = p.nchunks;
+        fa.dk = p.dk;
+        fa.dv = p.dv;
+        fa.phi = p.phi;
+        fa.fresh = p.fresh ? 1 : 0;
+        fa.eps = p.eps;
+        fa.eps_gamma = p.eps_gamma;
+        fa.eps_rms = p.eps_rms;
+        fa.q = p.q;
+        fa.k = p.k;
+        fa.v = p.v;
+        fa.beta = p.beta;
+        fa.lambda = p.lambda;
+        fa.xnext_in = p.xnext_in;
+        fa.S_in = p.S_in;
+        fa.S_out = p.S_out;
+        fa.xnext_out = p.xnext_out;
+        fa.o = p.o;
+        fa.ops = p.ws_at<void>(p.off_chunk);
+        launch_chunk_f1_split(fa, p.slice, s, m);
     } else if (p.path == Path::kChunkF1Fused) {
         F1FusedArgs fa{};
         fa.BH = p.BH;
@@ -259,6 +284,7 @@ extern "C" const char *falcon_kernel_name(const falcon_fwd_args *args, int i) {
         case Path::kChunkA: return i < 3 ? kNamesChunkA[i] : nullptr;
         case Path::kChunkF2: return i < 1 ? kNamesChunkF2[i] : nullptr;
         case Path::kChunkF3: return i < 3 ? kNamesChunkF3[i] : nullptr;
+        case Path::kChunkF1Split: return i < 2 ? kNamesChunkF1Split[i] : nullptr;
         default: return nullptr;
     }
 }

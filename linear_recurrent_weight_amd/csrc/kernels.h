@@ -97,6 +97,18 @@ struct ChunkF2Args {
     void *o;
 };
 
+struct F1SplitArgs {
+    int BH, T, nchunks, dk, dv, phi, fresh;
+    float eps, eps_gamma, eps_rms;
+    const void *q, *k, *v;  // bf16 [BH, T, d]
+    const float *beta, *lambda;
+    const float *xnext_in;  // nullptr when fresh
+    const float *S_in;
+    float *S_out, *xnext_out;
+    void *o;
+    void *ops;              // per-chunk operators (kF1SplitChunkBytes each)
+};
+
 struct ChunkF3Args {
     int BH, T, Tpad, nchunks, ct, window, dk, dv, n_tail_in;
     const void *xn, *qn;    // features [BH, Tpad, dk] (bf16 or fp32)
@@ -118,5 +130,6 @@ void launch_chunk_f1_fused(const F1FusedArgs &a, int ds, hipStream_t s, Marks *m
 void launch_chunk_a(const ChunkAArgs &a, bool bf16, hipStream_t s, Marks *m);
 void launch_chunk_f2(const ChunkF2Args &a, bool bf16, hipStream_t s, Marks *m);
 void launch_chunk_f3(const ChunkF3Args &a, bool bf16, hipStream_t s, Marks *m);
+void launch_chunk_f1_split(const F1SplitArgs &a, int ds, hipStream_t s, Marks *m);
 
 }  // namespace falcon

@@ -73,7 +73,11 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
     if (a->chunk == 0) {
         p->path = Path::kRecurrent;
     } else if (a->chunk == kChunk) {
-        if (var == FALCON_V1 && chunk_f1_fused_supported(a->dtype == FALCON_BF16, a->dk, a->dv)) {
+        if (var == FALCON_V1 && chunk_f1_split_supported(a->dtype == FALCON_BF16, a->dk, a->dv) &&
+            !chunk_f1_use_fused()) {
+            p->path = Path::kChunkF1Split;
+            p->slice = chunk_f1_split_slice(a->dv);
+        } else if (var == FALCON_V1 && chunk_f1_fused_supported(a->dtype == FALCON_BF16, a->dk, a->dv)) {
             p->path = Path::kChunkF1Fused;
             p->slice = chunk_f1_fused_slice(a->batch * a->heads, a->dv);
         } else if (var == FALCON_V1 && chunk_f1_supported(a->dk, a->dv)) {
@@ -114,6 +118,10 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
     size_t off = 0;
     if (p->path == Path::kChunkF1Fused || p->path == Path::kChunkF2) {
         p->nchunks = (T + kChunk - 1) / kChunk;
+    } else if (p->path == Path::kChunkF1Split) {
+        p->nchunks = (T + kChunk - 1) / kChunk;
+        p->off_chunk = off;
+        off = align_up(off + static_cast<size_t>(bh) * p->nchunks * kF1SplitChunkBytes);
     } else if (p->path == Path::kChunkA) {
         p->nchunks = (T + kChunk - 1) / kChunk;
         p->Tpad = p->nchunks * kChunk;

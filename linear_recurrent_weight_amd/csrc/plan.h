@@ -18,6 +18,7 @@ enum class Path : int {
     kChunkF2 = 4,    // chunk-parallel Falcon-2
     kChunkF1Fused = 5,  // chunk-parallel Falcon-1, bf16, one fused kernel
     kChunkF3 = 6,    // chunk-parallel Falcon-3 (stacked window rows)
+    kChunkF1Split = 7,  // chunk-parallel Falcon-1, bf16: per-chunk operators, then the walk
 };
 
 struct Plan {

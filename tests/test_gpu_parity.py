@@ -217,27 +217,36 @@ def test_deterministic():
     assert torch.equal(o1, o2) and torch.equal(s1.S, s2.S)
 
 
-# -- fused bf16 Falcon-1 kernel (d_k = 64) ------------------------------------
+# -- bf16 Falcon-1 kernels for d_k = 64: fused, and operators + walk ------------
 
+F1_PATHS = ["fused", "split"]
+
+
+@pytest.mark.parametrize("path", F1_PATHS)
 @pytest.mark.parametrize("slice_", ["32", "64"])
 @pytest.mark.parametrize("dv", [32, 64, 128])
 @pytest.mark.parametrize("T", [1, 64, 130, 300])
-def test_chunk_f1_fused_shapes(monkeypatch, slice_, dv, T):
+def test_chunk_f1_bf16_shapes(monkeypatch, path, slice_, dv, T):
+    monkeypatch.setenv("FALCON_F1_PATH", path)
     monkeypatch.setenv("FALCON_F1_SLICE", slice_)
     check(gu.small("F1", "bf16", B=2, H=5, T=T, dk=64, dv=dv, chunk=64, seed=T + dv))
 
 
+@pytest.mark.parametrize("path", F1_PATHS)
 @pytest.mark.parametrize("slice_", ["32", "64"])
-def test_c2_fused_both_slice_widths(monkeypatch, slice_):
+def test_c2_both_kernels_both_slice_widths(monkeypatch, path, slice_):
+    monkeypatch.setenv("FALCON_F1_PATH", path)
     monkeypatch.setenv("FALCON_F1_SLICE", slice_)
     check(WORKLOADS["c2"], heads=gu.sample_heads(WORKLOADS["c2"], 8))
 
 
+@pytest.mark.parametrize("path", F1_PATHS)
 @pytest.mark.parametrize("split", [64, 100])
-def test_chunk_f1_fused_continuation(split):
-    """bf16 fused path: two calls carrying the state match the oracle run of
-    the whole sequence."""
+def test_chunk_f1_bf16_continuation(monkeypatch, path, split):
+    """bf16 d_k = 64 paths: two calls carrying the state match the oracle run
+    of the whole sequence."""
     import torch
+    monkeypatch.setenv("FALCON_F1_PATH", path)
     w = gu.small("F1", "bf16", B=2, H=3, T=300, dk=64, dv=64, chunk=64, seed=13)
     inp = gu.make(w)
     dev = gu.to_device(inp, w)
@@ -251,6 +260,20 @@ def test_chunk_f1_fused_continuation(split):
     assert eo <= gu.TOL_BF16 and es <= gu.TOL_BF16, (eo, es)
     assert torch.allclose(st2.x_next, torch.from_numpy(st_ref.x_next.reshape(2, 3, 64)).float().cuda(),
                           rtol=1e-5, atol=1e-5)
+
+
+def test_chunk_f1_bf16_kernels_agree(monkeypatch):
+    """The fused kernel and the operators + walk pair compute the same
+    algebra; on c2-shaped input they agree to bf16 rounding."""
+    w = WORKLOADS["c2"].with_(batch=1, heads=4)
+    inp = gu.make(w)
+    dev = gu.to_device(inp, w)
+    monkeypatch.setenv("FALCON_F1_PATH", "fused")
+    o_f, st_f = gu.run_gpu(w, dev)
+    monkeypatch.setenv("FALCON_F1_PATH", "split")
+    o_s, st_s = gu.run_gpu(w, dev)
+    assert gu.max_rel_err(o_s.double().cpu().numpy(), o_f.double().cpu().numpy()) <= 2e-2
+    assert gu.max_rel_err(st_s.S.double().cpu().numpy(), st_f.S.double().cpu().numpy()) <= 2e-2
 
 
 # -- Falcon-1A / Falcon-3A chunk path -------------------------------------------
