@@ -59,22 +59,30 @@ template <int DK>
 struct RowPart {
     static constexpr int EPT = DK / 4, NV = EPT / 8;
     uint4 q[NV], k[NV];
+    // Loads are unconditional, from rows clamped into [0, T) (T >= 1 here):
+    // a load under a branch would be waited for where the branch joins.
+    // Rows outside the sequence are zeroed when the features are formed.
     __device__ void load(const bf16_t *qg, const bf16_t *kg, int t, int T, int part) {
+        const int tq = t < T ? t : T - 1;
+        const int tk = t < 1 ? 0 : (t - 1 < T ? t - 1 : T - 1);
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            q[v] = t < T ? *reinterpret_cast<const uint4 *>(qg + size_t(t) * DK + part * EPT + 8 * v)
-                         : make_uint4(0, 0, 0, 0);
-            k[v] = (t >= 1 && t - 1 < T)
-                       ? *reinterpret_cast<const uint4 *>(kg + size_t(t - 1) * DK + part * EPT + 8 * v)
-                       : make_uint4(0, 0, 0, 0);
+            q[v] = *reinterpret_cast<const uint4 *>(qg + size_t(tq) * DK + part * EPT + 8 * v);
+            k[v] = *reinterpret_cast<const uint4 *>(kg + size_t(tk) * DK + part * EPT + 8 * v);
         }
     }
     // normalised features; returns ||x||^2 of the whole row
     __device__ float features(float *xv, float *qv, int t, int part, const F1SplitArgs &a, int bh) const {
+        const bool qok = t < a.T, kok = t >= 1 && t - 1 < a.T;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             unpack8(q[v], qv + 8 * v);
             unpack8(k[v], xv + 8 * v);
+        }
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            qv[e] = qok ? qv[e] : 0.f;
+            xv[e] = kok ? xv[e] : 0.f;
         }
         const bool first = (t == 0);   // x_0 comes from the boundary state
         if (first && a.xnext_in) {
@@ -146,11 +154,9 @@ __global__ __launch_bounds__(256) void f1_ops(F1SplitArgs a) {
     {
         RP rp;
         rp.load(qg, kg, t, T, part);
-        float beta = 0.f, lam = 0.f;
-        if (part == 0 && t < T) {
-            beta = a.beta[size_t(bh) * T + t];
-            lam = a.lambda[size_t(bh) * T + t];
-        }
+        const int tc = t < T ? t : T - 1;
+        const float beta = a.beta[size_t(bh) * T + tc];   // unused when t >= T
+        const float lam = a.lambda[size_t(bh) * T + tc];
         float xv[RP::EPT], qv[RP::EPT];
         const float n2 = rp.features(xv, qv, t, part, a, bh);
 #pragma unroll
@@ -198,15 +204,15 @@ __global__ __launch_bounds__(256) void f1_ops(F1SplitArgs a) {
     }
     __syncthreads();
 
-    // 3. Gram and score tiles (lower 16x16 tiles) with decays and masks
-    for (int job = wave; job < 20; job += 4) {
+    // 3. Gram and score tiles (lower 16x16 tiles) with decays and masks;
+    //    wave w takes jobs w, w+4, ..., tiles 0-9 Gram, 10-19 scores, tile
+    //    index -> (I, J) from two packed 2-bit tables
+#pragma unroll
+    for (int m = 0; m < 5; ++m) {
+        const int job = wave + 4 * m;
         const bool isG = job < 10;
-        int tt = isG ? job : job - 10, I = 0;
-        while (tt > I) {
-            tt -= I + 1;
-            ++I;
-        }
-        const int J = tt;
+        const int tt = isG ? job : job - 10;
+        const int I = (0xffa94 >> (2 * tt)) & 3, J = (0xe4910 >> (2 * tt)) & 3;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k0 = 0; k0 < DK; k0 += 32)
@@ -220,10 +226,6 @@ __global__ __launch_bounds__(256) void f1_ops(F1SplitArgs a) {
             else st(PS, size_t(i) * PC + j, j <= i ? exp2_(b_s[i] - bj) * acc[r] : 0.f);
         }
     }
-    for (int idx = tid; idx < C * C; idx += 256) {
-        const int i = idx / C, j = idx % C;
-        if ((j >> 4) > (i >> 4)) st(PS, size_t(i) * PC + j, 0.f);
-    }
     __syncthreads();
 
     // 4. scores and the scaled transposed keys to the workspace; diagonal
@@ -231,10 +233,12 @@ __global__ __launch_bounds__(256) void f1_ops(F1SplitArgs a) {
     //    lane k < 16: column k), kept in registers until the staging area
     //    is free
     {
+        // P row part (columns 16 part ..): zero above the diagonal tiles
         const uint4 *sp = reinterpret_cast<const uint4 *>(PS + row * PC + part * 16);
         uint4 *dp = reinterpret_cast<uint4 *>(Pg + row * C + part * 16);
-        dp[0] = sp[0];
-        dp[1] = sp[1];
+        const bool live = part <= (row >> 4);
+        dp[0] = live ? sp[0] : make_uint4(0, 0, 0, 0);
+        dp[1] = live ? sp[1] : make_uint4(0, 0, 0, 0);
         // Xw[d][t] for d = row, t = 16 part .. + 15
         float xw[16];
 #pragma unroll
@@ -265,28 +269,59 @@ __global__ __launch_bounds__(256) void f1_ops(F1SplitArgs a) {
     }
     __syncthreads();
 
-    // 5. off-diagonal blocks, column block J = wave, rows I = J+1..3 in order:
-    //    T_IJ = -T_II sum_{K=J}^{I-1} N_IK T_KJ  (fp32 MFMA)
+    // 5. off-diagonal blocks by recursive doubling on the 2 x 2 split into
+    //    32-blocks, [[A, 0], [C, D]]^{-1} = [[A^-1, 0], [-D^-1 C A^-1, D^-1]]
+    //    (fp32 MFMA on 16x16 blocks; B(I, J) is block row I, column J):
+    //    level 1: T10 = -T11 N10 T00, T32 = -T33 N32 T22 (waves 0, 1);
+    //    level 2: X = C A^-1 (one block per wave), then -D^-1 X.
     {
-        const int J = wave;
-        float *mw = Mw[J];
-        for (int I = J + 1; I < 4; ++I) {
-            f32x4 M = {0.f, 0.f, 0.f, 0.f};
-            for (int K = J; K < I; ++K) {
+        auto blk = [&](const float *A, const float *B, f32x4 acc) {   // acc += A B (16x16 each)
 #pragma unroll
-                for (int k0 = 0; k0 < 16; k0 += 4)
-                    M = mfma_f32(Nm[(16 * I + col) * kLs + 16 * K + k0 + kq], Tm[(16 * K + k0 + kq) * kLs + 16 * J + col], M);
-            }
+            for (int k0 = 0; k0 < 16; k0 += 4)
+                acc = mfma_f32(A[col * kLs + k0 + kq], B[(k0 + kq) * kLs + col], acc);
+            return acc;
+        };
+        auto at = [&](float *M, int I, int J) { return M + 16 * I * kLs + 16 * J; };
+        float *mw = Mw[wave];
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        if (wave < 2) {
+            const int a0 = 2 * wave;   // blocks (a0 + 1, a0)
+            const f32x4 M = blk(at(Nm, a0 + 1, a0), at(Tm, a0, a0), z);
 #pragma unroll
             for (int r = 0; r < 4; ++r) mw[(g4 + r) * 17 + col] = M[r];
             wave_lds_sync();
-            f32x4 Tij = {0.f, 0.f, 0.f, 0.f};
+            f32x4 Tb = z;
 #pragma unroll
             for (int k0 = 0; k0 < 16; k0 += 4)
-                Tij = mfma_f32(Tm[(16 * I + col) * kLs + 16 * I + k0 + kq], mw[(k0 + kq) * 17 + col], Tij);
+                Tb = mfma_f32(at(Tm, a0 + 1, a0 + 1)[col * kLs + k0 + kq], mw[(k0 + kq) * 17 + col], Tb);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Tm[(16 * I + g4 + r) * kLs + 16 * J + col] = -Tij[r];
-            wave_lds_sync();
+            for (int r = 0; r < 4; ++r) at(Tm, a0 + 1, a0)[(g4 + r) * kLs + col] = -Tb[r];
+        }
+        __syncthreads();
+        // X(I, J) for I in {2, 3}, J in {0, 1}: N_I0 T_0J + N_I1 T_1J (T_01 = 0)
+        {
+            const int I = 2 + (wave >> 1), J = wave & 1;
+            f32x4 X = blk(at(Nm, I, 1), at(Tm, 1, J), z);
+            if (J == 0) X = blk(at(Nm, I, 0), at(Tm, 0, 0), X);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mw[(g4 + r) * 17 + col] = X[r];
+        }
+        __syncthreads();
+        // T(I, J) = -(sum_{K=2}^{I} T_IK X(K, J)) for I in {2, 3}, J in {0, 1}
+        {
+            const int I = 2 + (wave >> 1), J = wave & 1;
+            f32x4 Tb = z;
+#pragma unroll
+            for (int K = 2; K <= 3; ++K) {
+                if (K > I) break;
+                const float *Xk = Mw[2 * (K - 2) + J];
+                const float *Tk = at(Tm, I, K);
+#pragma unroll
+                for (int k0 = 0; k0 < 16; k0 += 4)
+                    Tb = mfma_f32(Tk[col * kLs + k0 + kq], Xk[(k0 + kq) * 17 + col], Tb);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) at(Tm, I, J)[(g4 + r) * kLs + col] = -Tb[r];
         }
     }
     __syncthreads();
@@ -362,9 +397,8 @@ __global__ __launch_bounds__((DS / 16 + 4) * 64) void f1_walk(F1SplitArgs a, int
         const int t = c * C + lrow;
         rp.load(qg, kg, t, T, lpart);
 #pragma unroll
-        for (int v = 0; v < YV; ++v)
-            ry[v] = t < T ? *reinterpret_cast<const uint4 *>(vg + size_t(t) * DV + j0 + lpart * YE + 8 * v)
-                          : make_uint4(0, 0, 0, 0);
+        for (int v = 0; v < YV; ++v)   // clamped row; zeroed at staging when t >= T
+            ry[v] = *reinterpret_cast<const uint4 *>(vg + size_t(t < T ? t : T - 1) * DV + j0 + lpart * YE + 8 * v);
         const char *ops = opsb + size_t(c) * kF1SplitChunkBytes;
         const uint4 *tp = reinterpret_cast<const uint4 *>(ops);
         const uint4 *pp = reinterpret_cast<const uint4 *>(ops + kF1SplitPOff);
@@ -389,7 +423,7 @@ __global__ __launch_bounds__((DS / 16 + 4) * 64) void f1_walk(F1SplitArgs a, int
         }
 #pragma unroll
         for (int v = 0; v < YV; ++v)
-            *reinterpret_cast<uint4 *>(YB[b] + lrow * PY + lpart * YE + 8 * v) = ry[v];
+            *reinterpret_cast<uint4 *>(YB[b] + lrow * PY + lpart * YE + 8 * v) = t < T ? ry[v] : make_uint4(0, 0, 0, 0);
         {
             // 16-byte piece u of a 64 x 64 tile: row u / 8, columns 8 (u % 8) ..
             const int r0 = lt >> 3, r1 = (lt + 256) >> 3, c8 = 8 * (lt & 7);

@@ -82,7 +82,7 @@ inline int chunk_f1_split_slice(int dv) {
         const int v = std::atoi(e);
         if (v == 32 || v == 64) return v;
     }
-    return 64;
+    return 32;   // two chain waves per workgroup, twice the workgroups
 }
 
 // Falcon-1A / Falcon-3A chunk path: d_k in {32, 64}, d_v in {16, 32, 64}.
