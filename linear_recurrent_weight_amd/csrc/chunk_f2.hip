@@ -11,15 +11,24 @@
 //     R0_t = y_t - e^{b_{t-1}} (X S_0)_t,  G = X X^T (shared by the columns),
 //     o_t = e^{b_t} (Qh S_0)_t + sum_{l<=t} e^{b_t-b_l} P0_tl u_l,  P0 = Qh X^T,
 //     S_C = e^{b_C} S_0 + X^T (e^{b_C - b_l} u_l)_l        (all per column).
-// The solve runs in four blocks of 16 tokens.  Contributions of earlier blocks
-// go through MFMA with the writes rescaled to the last token s of the
-// previous block, U~_l = e^{b_s - b_l} u_l, and are multiplied by
-// e^{b_{t-1} - b_s} <= 1 (e^{b_t - b_s} for the output).  Inside a block one
-// lane per column runs the forward substitution, keeping v_l = e^{b_{t-1}-b_l}
-// u_l and multiplying it by gamma_t at every step.  No factor exceeds 1.
 //
-// One workgroup owns one (batch*head, 16 value columns); all slices of a head
-// share an XCD.  The state slice lives in MFMA accumulators.
+// The solve runs in four blocks of 16 tokens; s is the last token before a
+// block and E_t = e^{b_t - b_s} <= 1 the block-local decay.  The writes of
+// earlier blocks are kept rescaled to s, W_l = e^{b_s - b_l} u_l, so their
+// contribution to a block is one MFMA, H = G[block, :] W, times E_{t-1}.
+// Inside the block the decay factorises, e^{b_{t-1} - b_l} = E_{t-1} / E_l,
+// so with w_l = u_l / E_l
+//     u_t = eta_t (R0_t - E_{t-1} (H_t + sum_{l in block, l<t} G_tl w_l)),
+// one multiply per step instead of rescaling every stored write; the block's
+// outputs are then one MFMA, o_t = e^{b_t} (Qh S_0)_t + E_t (P0 [W; w])_t.
+// When a block decays below 2^-100 (1 / E_l could overflow) it takes the
+// exact form instead: v_l = e^{b_{t-1} - b_l} u_l multiplied by gamma_t at
+// every step, outputs inside the step.  Both leave W rescaled to the block end.
+//
+// Lanes of a solve wave: 4 per column (16 columns per wave), each owning the
+// block positions l = q (mod 4); the in-block sums are quad sums (DPP).
+// One workgroup owns one (head, DS value columns); the raw rows of the next
+// chunk are prefetched while a chunk is processed.
 #include "chunk_layout.h"
 #include "kernels.h"
 #include "mma.h"
@@ -28,47 +37,104 @@ namespace falcon {
 namespace {
 
 constexpr int C = kChunk;
-constexpr int DS = 16;   // value columns per workgroup
+constexpr float kLog2e = 1.4426950408889634f;
 
-template <class E, int DK>
+// 16-byte vectors <-> floats for the io type
+template <class E> struct Io;
+template <> struct Io<bf16_t> {
+    static constexpr int per16 = 8;
+    __device__ static void unpack(const uint4 &u, float *f) {
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[2 * e] = __uint_as_float(w[e] << 16);
+            f[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+    }
+    __device__ static uint32_t p2(float a, float b) {
+        return uint32_t(f32_to_bf16(a)) | (uint32_t(f32_to_bf16(b)) << 16);
+    }
+    __device__ static uint4 pack(const float *f) {
+        return make_uint4(p2(f[0], f[1]), p2(f[2], f[3]), p2(f[4], f[5]), p2(f[6], f[7]));
+    }
+    // four consecutive outputs
+    __device__ static void store4(bf16_t *p, const float *f) {
+        *reinterpret_cast<uint2 *>(p) = make_uint2(p2(f[0], f[1]), p2(f[2], f[3]));
+    }
+};
+template <> struct Io<float> {
+    static constexpr int per16 = 4;
+    __device__ static void unpack(const uint4 &u, float *f) {
+        f[0] = __uint_as_float(u.x);
+        f[1] = __uint_as_float(u.y);
+        f[2] = __uint_as_float(u.z);
+        f[3] = __uint_as_float(u.w);
+    }
+    __device__ static uint4 pack(const float *f) {
+        return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                          __float_as_uint(f[3]));
+    }
+    __device__ static void store4(float *p, const float *f) {
+        *reinterpret_cast<float4 *>(p) = make_float4(f[0], f[1], f[2], f[3]);
+    }
+};
+
+__device__ __forceinline__ float quad_sum(float v) {
+    v += dpp<kDppQuadXor1>(v);
+    return v + dpp<kDppQuadXor2>(v);
+}
+// inclusive prefix inside each row of 16 lanes (= one 16-token block)
+__device__ __forceinline__ float row_scan(float v) {
+    v += dpp<kDppRowShr1>(v);
+    v += dpp<kDppRowShr2>(v);
+    v += dpp<kDppRowShr4>(v);
+    return v + dpp<kDppRowShr8>(v);
+}
+template <class E>
+__device__ __forceinline__ int kend_for(int n) {   // n rounded up to the MFMA k step
+    return (n + Mma<E>::KS - 1) / Mma<E>::KS * Mma<E>::KS;
+}
+
+template <class E, int DK, int DS>
 __global__ __launch_bounds__(256) void chunk_f2(ChunkF2Args a, int nslice) {
     constexpr int PD = Pad<E>::v;
-    constexpr int LK = DK + PD;     // [.][d] rows
+    constexpr int LK = DK + PD;     // [t][d] rows
     constexpr int LC = C + PD;      // [.][token] rows
-    constexpr int NT = DK / 64;     // state row tiles per wave (DK = 64 or 128)
-    __shared__ __align__(16) E XB[C * LK];      // x_t rows
-    __shared__ __align__(16) E QB[C * LK];      // qh_t rows
-    __shared__ __align__(16) E XT[DK * LC];     // x^T [d][t]
-    __shared__ __align__(16) E GB[C * LC];      // Gram (strictly lower), MFMA operand
-    __shared__ __align__(16) E PBm[C * LC];     // scores (lower incl. diagonal), MFMA operand
-    __shared__ float GD[4 * 16 * 17];           // diagonal 16x16 blocks of the Gram, fp32
-    __shared__ float PD4[4 * 16 * 17];          // diagonal 16x16 blocks of the scores, fp32
-    __shared__ __align__(16) E ST[DS * LK];     // S^T copy [j][d]
-    __shared__ __align__(16) E UTb[DS * LC];    // U~^T [j][l] (writes rescaled to a block edge)
-    __shared__ __align__(16) E WT[DS * LC];     // (e^{b_C-b_l} u_l)^T [j][l]
-    __shared__ float R0[C * 17];                // residual R0 [t][j]
-    __shared__ float OA[C * 17];                // output accumulator [t][j]
-    __shared__ float H[2][16 * 17];             // cross-block sums for the solve / output
-    // per (token, column) step scalars; decay ratios are formed from short
-    // sums (block-local prefixes, suffixes), never as differences of long
-    // chunk prefixes, so they stay accurate when the carries are small
-    __shared__ float ETA[C * 17];   // eta_t
-    __shared__ float GAM[C * 17];   // gamma_t
-    __shared__ float EB[C * 17];    // e^{b_t}, b restarted at the chunk start
-    __shared__ float EBP[C * 17];   // e^{b_{t-1}}
-    __shared__ float EBL[C * 17];   // e^{b_t - b_s}, s = last token before t's 16-block
-    __shared__ float EBLP[C * 17];  // e^{b_{t-1} - b_s}
-    __shared__ float ESF[C * 17];   // e^{b_C - b_t}
-    __shared__ float nrm[C];
+    constexpr int RS = DS + 1;      // fp32 [t][j] rows
+    constexpr int NCT = DS / 16;    // column tiles (= solve waves)
+    constexpr int EPT = DK / 4;     // features per thread (4 threads per row)
+    constexpr int NV = EPT / Io<E>::per16;
+    constexpr int YE = DS / 4;      // value columns per thread
+    constexpr int NB = YE / 4;      // 16-byte vectors of gains per thread
+    constexpr int NDT = DK / 64;    // state d tiles per wave
+    static_assert(YE * sizeof(E) == 16 || YE * sizeof(E) == 8, "values per thread fit one 16- or 8-byte load");
+
+    __shared__ __align__(16) E XB[C * LK];     // x rows
+    __shared__ __align__(16) E QB[C * LK];     // qh rows
+    __shared__ __align__(16) E XT[DK * LC];    // x^T [d][t]
+    __shared__ __align__(16) E GB[C * LC];     // Gram, strictly lower tiles
+    __shared__ __align__(16) E PB[C * LC];     // scores, lower incl. diagonal
+    __shared__ float GD[4 * 16 * 17];          // diagonal Gram blocks (fp32)
+    __shared__ float PD4[4 * 16 * 17];         // diagonal score blocks (fp32)
+    __shared__ __align__(16) E ST[DS * LK];    // S^T [j][d]
+    __shared__ __align__(16) E WT[DS * LC];    // W^T [j][l]
+    __shared__ float R0[C * RS];               // y, then the residual R0
+    __shared__ float ETA[C * RS];              // eta
+    __shared__ float GAM[C * RS];              // gamma
+    __shared__ float EB[C * RS];               // log2 gamma, then e^{b_t}
+    __shared__ float EBL[C * RS];              // block-local e^{b_t - b_s}
+    __shared__ float OA[C * RS];               // e^{b_t} (Qh S_0)_t
+    __shared__ float Hs[NCT][2][16 * 17];      // per solve wave: cross sums
 
     const int id = blockIdx.x, u8 = id & 7, rest = id >> 3;
     const int s = rest % nslice;
     const int bh = (rest / nslice) * 8 + u8;
-    if (bh >= a.BH) return;
+    if (bh >= a.BH) return;   // the whole workgroup leaves together
     const int j0 = DS * s;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int T = a.T, DV = a.dv;
+    const int col = lane & 15, g4 = 4 * (lane >> 4);
     const E *qg = static_cast<const E *>(a.q) + size_t(bh) * T * DK;
     const E *kg = static_cast<const E *>(a.k) + size_t(bh) * T * DK;
     const E *vg = static_cast<const E *>(a.v) + size_t(bh) * T * DV;
@@ -76,243 +142,308 @@ __global__ __launch_bounds__(256) void chunk_f2(ChunkF2Args a, int nslice) {
     const float *betag = a.beta + size_t(bh) * T * DV;
     const float *lamg = a.lambda + size_t(bh) * T;
 
-    // zero the never-written upper parts of the MFMA operands
+    // ---- raw rows of the next chunk (thread: row, part), prefetched ----
+    const int row = tid >> 2, part = tid & 3;
+    uint4 rq[NV], rk[NV], ry, rb[NB];
+    float rlam;
+    auto prefetch = [&](int c) {   // unconditional loads from rows clamped into [0, T)
+        const int t = c * C + row;
+        const int tq = t < T ? t : T - 1;
+        const int tk = t < 1 ? 0 : (t - 1 < T ? t - 1 : T - 1);
+        const uint4 *q4 = reinterpret_cast<const uint4 *>(qg + size_t(tq) * DK + part * EPT);
+        const uint4 *k4 = reinterpret_cast<const uint4 *>(kg + size_t(tk) * DK + part * EPT);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            rq[v] = q4[v];
+            rk[v] = k4[v];
+        }
+        if constexpr (YE * sizeof(E) == 16) {
+            ry = *reinterpret_cast<const uint4 *>(vg + size_t(tq) * DV + j0 + part * YE);
+        } else {
+            const uint2 h = *reinterpret_cast<const uint2 *>(vg + size_t(tq) * DV + j0 + part * YE);
+            ry = make_uint4(h.x, h.y, 0u, 0u);
+        }
+        const uint4 *b4 = reinterpret_cast<const uint4 *>(betag + size_t(tq) * DV + j0 + part * YE);
+#pragma unroll
+        for (int v = 0; v < NB; ++v) rb[v] = b4[v];
+        rlam = lamg[tq];
+    };
+
+    // the tiles above the diagonal are never written but are read (times
+    // zero) by the bf16 MFMA k steps of 32: they must hold zeros, not NaNs
     for (int idx = tid; idx < C * LC; idx += 256) {
         st(GB, idx, 0.f);
-        st(PBm, idx, 0.f);
+        st(PB, idx, 0.f);
     }
-    // state tiles: wave w owns rows 16 * (w * NT + m), columns j0 .. j0 + 15
-    f32x4 S[NT];
+
+    // ---- state: d tiles {wave, wave + 4, ..} x all column tiles ----
+    f32x4 S[NDT][NCT];
 #pragma unroll
-    for (int m = 0; m < NT; ++m) {
-        const int dbase = 16 * (wave * NT + m);
+    for (int m = 0; m < NDT; ++m)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int d = dbase + 4 * (lane >> 4) + r;
-            S[m][r] = a.S_in ? a.S_in[(size_t(bh) * DK + d) * DV + j0 + (lane & 15)] : 0.f;
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int dbase = 16 * (wave + 4 * m);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int d = dbase + g4 + r;
+                S[m][ct][r] = a.S_in ? a.S_in[(size_t(bh) * DK + d) * DV + j0 + 16 * ct + col] : 0.f;
+            }
+            st4(ST + (16 * ct + col) * LK + dbase + g4, S[m][ct]);
         }
-        st4(ST + (lane & 15) * LK + dbase + 4 * (lane >> 4), S[m]);
-    }
-    __syncthreads();
+    prefetch(0);
 
     for (int c = 0; c < a.nchunks; ++c) {
         const int c0 = c * C;
-        // 1. features: one wave per row, lanes over d
-        for (int t = wave; t < C; t += 4) {
-            const int tt = c0 + t;
-            float xv[2] = {0.f, 0.f}, qv[2] = {0.f, 0.f};
+        // ---- P1: features, values, step scalars; zero W; prefetch ----
+        {
+            const int t = c0 + row;
+            float qv[EPT], xv[EPT];
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const int e = lane + 64 * m;
-                if (e < DK) {
-                    if (tt < T) qv[m] = ld(qg, size_t(tt) * DK + e);
-                    if (tt >= 1 && tt < T) xv[m] = ld(kg, size_t(tt - 1) * DK + e);
-                    else if (tt == 0 && a.xnext_in) xv[m] = a.xnext_in[size_t(bh) * DK + e];
-                }
+            for (int v = 0; v < NV; ++v) {
+                Io<E>::unpack(rq[v], qv + v * Io<E>::per16);
+                Io<E>::unpack(rk[v], xv + v * Io<E>::per16);
             }
-            const bool from_k = tt >= 1 && tt < T;
-            const float sq = phi_scale(wave_sum(qv[0] * qv[0] + qv[1] * qv[1]), DK, a.eps_rms, a.phi);
-            const float sk = from_k ? phi_scale(wave_sum(xv[0] * xv[0] + xv[1] * xv[1]), DK, a.eps_rms, a.phi)
-                                    : 1.f;
+            const bool qok = t < T, kok = t >= 1 && t - 1 < T;
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) {
+                qv[e] = qok ? qv[e] : 0.f;
+                xv[e] = kok ? xv[e] : 0.f;
+            }
+            const bool first = t == 0;   // x_0 comes from the boundary state
+            if (first && a.xnext_in) {
+#pragma unroll
+                for (int e = 0; e < EPT; ++e) xv[e] = a.xnext_in[size_t(bh) * DK + part * EPT + e];
+            }
+            float sq = 0.f, sk = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) {
+                sq += qv[e] * qv[e];
+                sk += xv[e] * xv[e];
+            }
+            const float scq = phi_scale(group_sum<4>(sq), DK, a.eps_rms, a.phi);
+            const float sck = first ? 1.f : phi_scale(group_sum<4>(sk), DK, a.eps_rms, a.phi);
             float n2 = 0.f;
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const int e = lane + 64 * m;
-                xv[m] *= sk;
-                n2 += xv[m] * xv[m];
-                if (e < DK) {
-                    st(XB, size_t(t) * LK + e, xv[m]);
-                    st(QB, size_t(t) * LK + e, qv[m] * sq);
-                    st(XT, size_t(e) * LC + t, xv[m]);
-                }
+            for (int e = 0; e < EPT; ++e) {
+                xv[e] *= sck;
+                qv[e] *= scq;
+                n2 += xv[e] * xv[e];
             }
-            n2 = wave_sum(n2);
-            if (lane == 0) nrm[t] = n2;
-        }
-        // values of this slice; the rescaled writes start at zero (the
-        // cross-block products read the not-yet-written columns too)
-        for (int idx = tid; idx < C * DS; idx += 256) {
-            const int t = idx / DS, j = idx % DS;
-            R0[t * 17 + j] = (c0 + t < T) ? ld(vg, size_t(c0 + t) * DV + j0 + j) : 0.f;
-            st(UTb, size_t(j) * LC + t, 0.f);
+            n2 = group_sum<4>(n2);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                *reinterpret_cast<uint4 *>(XB + row * LK + part * EPT + v * Io<E>::per16) =
+                    Io<E>::pack(xv + v * Io<E>::per16);
+                *reinterpret_cast<uint4 *>(QB + row * LK + part * EPT + v * Io<E>::per16) =
+                    Io<E>::pack(qv + v * Io<E>::per16);
+            }
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) st(XT, size_t(part * EPT + e) * LC + row, xv[e]);
+            float yv[Io<E>::per16], bv[YE];
+            Io<E>::unpack(ry, yv);   // the first YE are this thread's values
+#pragma unroll
+            for (int v = 0; v < NB; ++v) {
+                bv[4 * v] = __uint_as_float(rb[v].x);
+                bv[4 * v + 1] = __uint_as_float(rb[v].y);
+                bv[4 * v + 2] = __uint_as_float(rb[v].z);
+                bv[4 * v + 3] = __uint_as_float(rb[v].w);
+            }
+            const bool noop = t >= T || (t == 0 && a.fresh);
+            const float den = n2 + rlam + a.eps;
+#pragma unroll
+            for (int e = 0; e < YE; ++e) {
+                const int q = row * RS + part * YE + e;
+                float eta = 0.f, alpha = 0.f;
+                if (!noop) {
+                    eta = step_eta(bv[e], den);
+                    alpha = step_alpha(eta, rlam, a.eps_gamma);
+                }
+                R0[q] = qok ? yv[e] : 0.f;
+                ETA[q] = eta;
+                GAM[q] = 1.f - alpha;
+                EB[q] = log1pf(-alpha) * kLog2e;   // log2 gamma
+            }
+            for (int idx = tid; idx < DS * LC; idx += 256) st(WT, idx, 0.f);
+            if (c + 1 < a.nchunks) prefetch(c + 1);
         }
         __syncthreads();
 
-        // 2. per-column steps and log-prefixes (wave w: columns 4w..4w+3,
-        //    lanes = tokens); Gram and score tiles; X S and Qh S
-        {
-            const int t = c0 + lane;
-            const bool noop = t >= T || (t == 0 && a.fresh);
-            const float lam = t < T ? lamg[t] : 0.f;
-            const float den = nrm[lane] + lam + a.eps;
+        // ---- P2a: per-column prefixes; Gram, scores, XS, Qh S on MFMA ----
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int j = 4 * wave + jj;
-                float eta = 0.f, alpha = 0.f;
-                if (!noop) {
-                    eta = step_eta(betag[size_t(t) * DV + j0 + j], den);
-                    alpha = step_alpha(eta, lam, a.eps_gamma);
-                }
-                const float lg = log1pf(-alpha);
-                const float b = wave_inclusive_scan(lg);
-                float bp = __shfl_up(b, 1, 64);
-                if (lane == 0) bp = 0.f;
-                float bl = lg;   // inclusive prefix inside the 16-token block
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) {
-                    const float y = __shfl_up(bl, o, 16);
-                    if ((lane & 15) >= o) bl += y;
-                }
-                float blp = __shfl_up(bl, 1, 16);
-                if ((lane & 15) == 0) blp = 0.f;
-                float sf = lg;   // inclusive suffix to the chunk end
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const float y = __shfl_down(sf, o, 64);
-                    if (lane + o < 64) sf += y;
-                }
-                float sfx = __shfl_down(sf, 1, 64);
-                if (lane == 63) sfx = 0.f;
-                const int q = lane * 17 + j;
-                ETA[q] = eta;
-                GAM[q] = 1.f - alpha;
-                EB[q] = expf(b);
-                EBP[q] = expf(bp);
-                EBL[q] = expf(bl);
-                EBLP[q] = expf(blp);
-                ESF[q] = expf(sfx);
-            }
+        for (int n = 0; n < DS / 4; ++n) {
+            const int j = wave + 4 * n;   // lane = token
+            const float lg = EB[lane * RS + j];
+            EB[lane * RS + j] = __builtin_amdgcn_exp2f(wave_inclusive_scan(lg));
+            EBL[lane * RS + j] = __builtin_amdgcn_exp2f(row_scan(lg));
         }
-        for (int job = wave; job < 20; job += 4) {
+#pragma unroll
+        for (int m = 0; m < 5; ++m) {
+            const int job = wave + 4 * m;   // 0-9 Gram tiles, 10-19 score tiles
             const bool isG = job < 10;
-            int t = isG ? job : job - 10, I = 0;
-            while (t > I) {
-                t -= I + 1;
-                ++I;
-            }
-            const int J = t;
+            const int tt = isG ? job : job - 10;
+            const int I = (0xffa94 >> (2 * tt)) & 3, J = (0xe4910 >> (2 * tt)) & 3;
             const f32x4 g = Mma<E>::run(f32x4{0.f, 0.f, 0.f, 0.f}, (isG ? XB : QB) + 16 * I * LK, LK,
                                         XB + 16 * J * LK, LK, 0, DK);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int i = 16 * I + 4 * (lane >> 4) + r, jn = 16 * J + (lane & 15);
+                const int i = 16 * I + g4 + r, jn = 16 * J + col;
                 const float v = isG ? (jn < i ? g[r] : 0.f) : (jn <= i ? g[r] : 0.f);
-                st(isG ? GB : PBm, size_t(i) * LC + jn, v);
-                if (I == J) (isG ? GD : PD4)[I * 272 + (i - 16 * I) * 17 + (jn - 16 * J)] = v;
+                st(isG ? GB : PB, size_t(i) * LC + jn, v);
+                if (I == J) (isG ? GD : PD4)[I * 272 + (g4 + r) * 17 + col] = v;
             }
         }
-        f32x4 xs = Mma<E>::run(f32x4{0.f, 0.f, 0.f, 0.f}, XB + 16 * wave * LK, LK, ST, LK, 0, DK);
-        f32x4 o1 = Mma<E>::run(f32x4{0.f, 0.f, 0.f, 0.f}, QB + 16 * wave * LK, LK, ST, LK, 0, DK);
+        f32x4 xs[NCT], qs[NCT];   // token rows 16 wave .. + 15
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            xs[ct] = Mma<E>::run(z, XB + 16 * wave * LK, LK, ST + 16 * ct * LK, LK, 0, DK);
+            qs[ct] = Mma<E>::run(z, QB + 16 * wave * LK, LK, ST + 16 * ct * LK, LK, 0, DK);
+        }
         __syncthreads();
 
-        // 3. residuals and the state part of the outputs
-        {
-            const int j = lane & 15;
+        // ---- P2b: residuals and the state part of the outputs ----
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = 16 * wave + 4 * (lane >> 4) + r;
-                R0[t * 17 + j] -= EBP[t * 17 + j] * xs[r];
-                OA[t * 17 + j] = EB[t * 17 + j] * o1[r];
+                const int t = 16 * wave + g4 + r, j = 16 * ct + col;
+                const float ebp = t > 0 ? EB[(t - 1) * RS + j] : 1.f;
+                R0[t * RS + j] -= ebp * xs[ct][r];
+                OA[t * RS + j] = EB[t * RS + j] * qs[ct][r];
             }
-        }
         __syncthreads();
 
-        // 4. blocked per-column solve and outputs (wave 0)
-        if (wave == 0) {
-            const int j = lane & 15;
-            for (int I = 0; I < 4; ++I) {
-                // cross-block sums H = G[I, :16I] U~ and Hp = P0[I, :16I] U~
-                if (I > 0) {
-                    const int kend = (16 * I + Mma<E>::KS - 1) / Mma<E>::KS * Mma<E>::KS;
-                    const f32x4 h = Mma<E>::run(f32x4{0.f, 0.f, 0.f, 0.f}, GB + 16 * I * LC, LC, UTb, LC, 0, kend);
-                    const f32x4 hp = Mma<E>::run(f32x4{0.f, 0.f, 0.f, 0.f}, PBm + 16 * I * LC, LC, UTb, LC, 0, kend);
+        // ---- P3: blocked per-column solve (wave sw: columns 16 sw ..) ----
+        if (wave < NCT) {
+            const int sw = wave, jj = lane >> 2, q = lane & 3, j = 16 * sw + jj;
+            float *H0 = Hs[sw][0], *H1 = Hs[sw][1];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        H[0][(4 * (lane >> 4) + r) * 17 + j] = h[r];
-                        H[1][(4 * (lane >> 4) + r) * 17 + j] = hp[r];
-                    }
-                    wave_lds_sync();
+            for (int I = 0; I < 4; ++I) {
+                if (I > 0) {
+                    const f32x4 h = Mma<E>::run(f32x4{0.f, 0.f, 0.f, 0.f}, GB + 16 * I * LC, LC,
+                                                WT + 16 * sw * LC, LC, 0, kend_for<E>(16 * I));
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) H0[(g4 + r) * 17 + col] = h[r];
                 }
-                // forward substitution inside the block, lane j < 16 = column
-                float v[16];   // v_l = e^{b_t - b_l} u_l for the block's l <= t
-                float ucol[16];
-                if (lane < 16) {
+                const float fblk = EBL[(16 * I + 15) * RS + j];   // e^{b_end - b_s}
+                const bool sep = __all(fblk >= 0x1p-100f);
+                wave_lds_sync();
+                if (sep) {
+                    float w[4] = {0.f, 0.f, 0.f, 0.f};   // w_l = u_l / E_l, l = 4 m + q
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int t = 16 * I + i;
-                        // entering step t: v_l = e^{b_{t-1} - b_l} u_l
-                        float acc = 0.f;
+                        float part_s = 0.f;
 #pragma unroll
-                        for (int l = 0; l < 16; ++l)
-                            if (l < i) acc += GD[I * 272 + i * 17 + l] * v[l];
-                        float cross = 0.f;
-                        if (I > 0) cross = EBLP[t * 17 + j] * H[0][i * 17 + j];
-                        const float u = ETA[t * 17 + j] * (R0[t * 17 + j] - cross - acc);
-                        ucol[i] = u;
-                        // advance to e^{b_t - b_l} u_l and append u_t
-                        const float g = GAM[t * 17 + j];
-#pragma unroll
-                        for (int l = 0; l < 16; ++l)
-                            if (l < i) v[l] *= g;
-                        v[i] = u;
-                        float oin = 0.f;
-#pragma unroll
-                        for (int l = 0; l < 16; ++l)
-                            if (l <= i) oin += PD4[I * 272 + i * 17 + l] * v[l];
-                        float ocross = 0.f;
-                        if (I > 0) ocross = EBL[t * 17 + j] * H[1][i * 17 + j];
-                        OA[t * 17 + j] += oin + ocross;
+                        for (int m = 0; m < 4; ++m)
+                            if (4 * m < i) part_s += (4 * m + q < i ? GD[I * 272 + i * 17 + 4 * m + q] : 0.f) * w[m];
+                        float sum = quad_sum(part_s);
+                        if (I > 0) sum += H0[i * 17 + jj];
+                        const float ep = i > 0 ? EBL[(t - 1) * RS + j] : 1.f;
+                        const float u = ETA[t * RS + j] * (R0[t * RS + j] - ep * sum);
+                        const float wi = u * __builtin_amdgcn_rcpf(EBL[t * RS + j]);
+                        if (q == (i & 3)) w[i >> 2] = wi;
                     }
-                    // U~ for the next block: rescale to its edge s' = 16 I + 15
-                    const float f = EBL[(16 * I + 15) * 17 + j];
-                    for (int l = 0; l < 16 * I; ++l) st(UTb, size_t(j) * LC + l, f * ld(UTb, size_t(j) * LC + l));
 #pragma unroll
-                    for (int l = 0; l < 16; ++l) {
-                        st(UTb, size_t(j) * LC + 16 * I + l, v[l]);
-                        R0[(16 * I + l) * 17 + j] = ucol[l];   // keep u for the state update
+                    for (int m = 0; m < 4; ++m) st(WT, size_t(j) * LC + 16 * I + 4 * m + q, w[m]);
+                    wave_lds_sync();
+                    // outputs of the block: o_t = OA_t + E_t (P0 [W; w])_t, as O^T tiles
+                    {
+                        const f32x4 o = Mma<E>::run(f32x4{0.f, 0.f, 0.f, 0.f}, WT + 16 * sw * LC, LC,
+                                                    PB + 16 * I * LC, LC, 0, kend_for<E>(16 * I + 16));
+                        const int t = 16 * I + col;
+                        float ov[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int jr = 16 * sw + g4 + r;
+                            ov[r] = OA[t * RS + jr] + EBL[t * RS + jr] * o[r];
+                        }
+                        if (c0 + t < T) Io<E>::store4(og + size_t(c0 + t) * DV + j0 + 16 * sw + g4, ov);
                     }
+                    // rescale W to the block end
+                    for (int l = q; l < 16 * I + 16; l += 4) {
+                        const size_t p = size_t(j) * LC + l;
+                        st(WT, p, fblk * ld(WT, p));
+                    }
+                    wave_lds_sync();
+                } else {
+                    if (I > 0) {
+                        const f32x4 h = Mma<E>::run(f32x4{0.f, 0.f, 0.f, 0.f}, PB + 16 * I * LC, LC,
+                                                    WT + 16 * sw * LC, LC, 0, kend_for<E>(16 * I));
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) H1[(g4 + r) * 17 + col] = h[r];
+                        wave_lds_sync();
+                    }
+                    // exact form: v_l = e^{b_{t-1} - b_l} u_l, advanced by gamma_t
+                    float v[4] = {0.f, 0.f, 0.f, 0.f};
+                    float pb = 1.f;   // e^{b_{t-1} - b_s}
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int t = 16 * I + i;
+                        const float gm = GAM[t * RS + j];
+                        float part_s = 0.f;
+#pragma unroll
+                        for (int m = 0; m < 4; ++m)
+                            if (4 * m < i) part_s += (4 * m + q < i ? GD[I * 272 + i * 17 + 4 * m + q] : 0.f) * v[m];
+                        const float acc = quad_sum(part_s);
+                        const float cross = I > 0 ? pb * H0[i * 17 + jj] : 0.f;
+                        const float u = ETA[t * RS + j] * (R0[t * RS + j] - cross - acc);
+#pragma unroll
+                        for (int m = 0; m < 4; ++m)
+                            if (4 * m < i) v[m] = (4 * m + q < i) ? v[m] * gm : v[m];
+                        if (q == (i & 3)) v[i >> 2] = u;
+                        pb *= gm;
+                        float part_o = 0.f;
+#pragma unroll
+                        for (int m = 0; m < 4; ++m)
+                            if (4 * m <= i) part_o += (4 * m + q <= i ? PD4[I * 272 + i * 17 + 4 * m + q] : 0.f) * v[m];
+                        const float oin = quad_sum(part_o);
+                        if (q == 0 && c0 + t < T) {
+                            float o = OA[t * RS + j] + oin;
+                            if (I > 0) o += pb * H1[i * 17 + jj];
+                            st(og, size_t(c0 + t) * DV + j0 + j, o);
+                        }
+                    }
+                    for (int l = q; l < 16 * I; l += 4) {
+                        const size_t p = size_t(j) * LC + l;
+                        st(WT, p, pb * ld(WT, p));
+                    }
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) st(WT, size_t(j) * LC + 16 * I + 4 * m + q, v[m]);
+                    wave_lds_sync();
                 }
-                wave_lds_sync();
             }
         }
         __syncthreads();
 
-        // 5. outputs to HBM; state update S = e^{b_C} S + X^T (e^{b_C-b_l} u_l)
-        for (int idx = tid; idx < C * DS; idx += 256) {
-            const int t = idx / DS, j = idx % DS;
-            if (c0 + t < T) st(og, size_t(c0 + t) * DV + j0 + j, OA[t * 17 + j]);
-            const float w = ESF[t * 17 + j] * R0[t * 17 + j];
-            st(WT, size_t(j) * LC + t, w);
-        }
-        __syncthreads();
-        {
-            const int j = lane & 15;
-            const float gC = EB[63 * 17 + j];
+        // ---- P4: S = e^{b_C} S + X^T W (W = writes rescaled to the chunk end) ----
 #pragma unroll
-            for (int m = 0; m < NT; ++m) {
-                const int dbase = 16 * (wave * NT + m);
+        for (int m = 0; m < NDT; ++m)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) S[m][r] *= gC;
-                S[m] = Mma<E>::run(S[m], XT + dbase * LC, LC, WT, LC, 0, C);
-                st4(ST + j * LK + dbase + 4 * (lane >> 4), S[m]);
+            for (int ct = 0; ct < NCT; ++ct) {
+                const int dbase = 16 * (wave + 4 * m);
+                const float gC = EB[63 * RS + 16 * ct + col];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) S[m][ct][r] *= gC;
+                S[m][ct] = Mma<E>::run(S[m][ct], XT + dbase * LC, LC, WT + 16 * ct * LC, LC, 0, C);
+                st4(ST + (16 * ct + col) * LK + dbase + g4, S[m][ct]);
             }
-        }
         __syncthreads();
     }
 
-    // boundary state
+    // ---- boundary state ----
     if (a.S_out) {
 #pragma unroll
-        for (int m = 0; m < NT; ++m) {
-            const int dbase = 16 * (wave * NT + m);
+        for (int m = 0; m < NDT; ++m)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int d = dbase + 4 * (lane >> 4) + r;
-                a.S_out[(size_t(bh) * DK + d) * DV + j0 + (lane & 15)] = S[m][r];
-            }
-        }
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int d = 16 * (wave + 4 * m) + g4 + r;
+                    a.S_out[(size_t(bh) * DK + d) * DV + j0 + 16 * ct + col] = S[m][ct][r];
+                }
     }
-    if (s == 0 && wave == 0 && a.xnext_out && T > 0) {
+    if (s == 0 && wave == 0 && a.xnext_out) {
         float x[2] = {0.f, 0.f};
         for (int m = 0; m < 2; ++m)
             if (lane + 64 * m < DK) x[m] = ld(kg, size_t(T - 1) * DK + lane + 64 * m);
@@ -322,11 +453,11 @@ __global__ __launch_bounds__(256) void chunk_f2(ChunkF2Args a, int nslice) {
     }
 }
 
-template <class E, int DK>
+template <class E, int DK, int DS>
 void launch_t(const ChunkF2Args &a, hipStream_t s, Marks *m) {
     const int nslice = a.dv / DS;
     const int blocks = ((a.BH + 7) / 8) * 8 * nslice;
-    chunk_f2<E, DK><<<blocks, 256, 0, s>>>(a, nslice);
+    chunk_f2<E, DK, DS><<<blocks, 256, 0, s>>>(a, nslice);
     m->mark(s);
 }
 
@@ -334,10 +465,16 @@ void launch_t(const ChunkF2Args &a, hipStream_t s, Marks *m) {
 
 void launch_chunk_f2(const ChunkF2Args &a, bool bf16, hipStream_t s, Marks *m) {
     if (bf16) {
-        if (a.dk == 64) launch_t<bf16_t, 64>(a, s, m);
-        else launch_t<bf16_t, 128>(a, s, m);
+        // 32 value columns per workgroup when d_v allows it
+        if (a.dv % 32 == 0) {
+            if (a.dk == 64) launch_t<bf16_t, 64, 32>(a, s, m);
+            else launch_t<bf16_t, 128, 32>(a, s, m);
+        } else {
+            if (a.dk == 64) launch_t<bf16_t, 64, 16>(a, s, m);
+            else launch_t<bf16_t, 128, 16>(a, s, m);
+        }
     } else {
-        launch_t<float, 64>(a, s, m);   // the planner admits d_k = 64 only
+        launch_t<float, 64, 16>(a, s, m);   // the planner admits d_k = 64 only
     }
 }
 

@@ -450,3 +450,21 @@ def test_chunk_f3_strong_ridge_clamp():
     assert (tr.alpha >= 1 - 0.05 - 1e-9).mean() > 0.5
     eo, es = gu.compare(w, np.arange(2), o, st, o_ref, st_ref)
     assert eo <= 1e-5 and es <= 1e-5, (eo, es)
+
+
+@pytest.mark.parametrize("eps_gamma,lam_hi,dtype", [(1e-4, 400.0, "f32"), (1e-3, 30.0, "f32"),
+                                                    (1e-4, 400.0, "bf16")])
+def test_chunk_f2_steep_decay_blocks(eps_gamma, lam_hi, dtype):
+    """Blocks whose carry falls below 2^-100 take the exact in-block form;
+    with the clamp binding everywhere (first case) every block does, with a
+    ridge spread (second case) the two forms alternate."""
+    w = gu.small("F2", dtype, B=1, H=2, T=200, dk=64, dv=32, chunk=64, lam_lo=0.0, lam_hi=lam_hi,
+                 eps_gamma=eps_gamma, seed=21)
+    inp = gu.make(w)
+    inp["beta"] = (1.0 + inp["beta"]).astype(np.float32)
+    dev = gu.to_device(inp, w)
+    o, st = gu.run_gpu(w, dev)
+    o_ref, st_ref = gu.oracle_heads(w, inp, np.arange(2))
+    eo, es = gu.compare(w, np.arange(2), o, st, o_ref, st_ref)
+    tol = gu.tol_for(w)
+    assert eo <= tol and es <= tol, (eo, es)
