@@ -101,6 +101,7 @@ __global__ __launch_bounds__(256) void chunk_f2(ChunkF2Args a, int nslice) {
     constexpr int LK = DK + PD;     // [t][d] rows
     constexpr int LC = C + PD;      // [.][token] rows
     constexpr int RS = DS + 1;      // fp32 [t][j] rows
+    constexpr int SVS = C + 1;      // float4 [j][t] rows (odd pitch: no bank conflicts)
     constexpr int NCT = DS / 16;    // column tiles (= solve waves)
     constexpr int EPT = DK / 4;     // features per thread (4 threads per row)
     constexpr int NV = EPT / Io<E>::per16;
@@ -114,15 +115,13 @@ __global__ __launch_bounds__(256) void chunk_f2(ChunkF2Args a, int nslice) {
     __shared__ __align__(16) E XT[DK * LC];    // x^T [d][t]
     __shared__ __align__(16) E GB[C * LC];     // Gram, strictly lower tiles
     __shared__ __align__(16) E PB[C * LC];     // scores, lower incl. diagonal
-    __shared__ float GD[4 * 16 * 17];          // diagonal Gram blocks (fp32)
+    __shared__ float4 GDq[4 * 16 * 4];         // diagonal Gram blocks (fp32): [blk][i][q] = G_{i, 4m+q}, m = 0..3
     __shared__ float PD4[4 * 16 * 17];         // diagonal score blocks (fp32)
     __shared__ __align__(16) E ST[DS * LK];    // S^T [j][d]
     __shared__ __align__(16) E WT[DS * LC];    // W^T [j][l]
-    __shared__ float R0[C * RS];               // y, then the residual R0
-    __shared__ float ETA[C * RS];              // eta
+    __shared__ float4 SV[DS * SVS];            // per (j, t): eta, y then R0, E_{t-1}, E_t
     __shared__ float GAM[C * RS];              // gamma
     __shared__ float EB[C * RS];               // log2 gamma, then e^{b_t}
-    __shared__ float EBL[C * RS];              // block-local e^{b_t - b_s}
     __shared__ float OA[C * RS];               // e^{b_t} (Qh S_0)_t
     __shared__ float Hs[NCT][2][16 * 17];      // per solve wave: cross sums
 
@@ -250,18 +249,17 @@ __global__ __launch_bounds__(256) void chunk_f2(ChunkF2Args a, int nslice) {
             }
             const bool noop = t >= T || (t == 0 && a.fresh);
             const float den = n2 + rlam + a.eps;
+            const float rden = (noop || den == 0.f) ? 0.f : 1.f / den;   // eta = 0 when den == 0
 #pragma unroll
             for (int e = 0; e < YE; ++e) {
                 const int q = row * RS + part * YE + e;
-                float eta = 0.f, alpha = 0.f;
-                if (!noop) {
-                    eta = step_eta(bv[e], den);
-                    alpha = step_alpha(eta, rlam, a.eps_gamma);
-                }
-                R0[q] = qok ? yv[e] : 0.f;
-                ETA[q] = eta;
+                const float eta = bv[e] * rden;
+                const float alpha = step_alpha(eta, rlam, a.eps_gamma);
+                float4 *sv = SV + (part * YE + e) * SVS + row;
+                sv->x = eta;
+                sv->y = qok ? yv[e] : 0.f;
                 GAM[q] = 1.f - alpha;
-                EB[q] = log1pf(-alpha) * kLog2e;   // log2 gamma
+                EB[q] = log2_1m(alpha);   // log2 gamma
             }
             for (int idx = tid; idx < DS * LC; idx += 256) st(WT, idx, 0.f);
             if (c + 1 < a.nchunks) prefetch(c + 1);
@@ -274,7 +272,10 @@ __global__ __launch_bounds__(256) void chunk_f2(ChunkF2Args a, int nslice) {
             const int j = wave + 4 * n;   // lane = token
             const float lg = EB[lane * RS + j];
             EB[lane * RS + j] = __builtin_amdgcn_exp2f(wave_inclusive_scan(lg));
-            EBL[lane * RS + j] = __builtin_amdgcn_exp2f(row_scan(lg));
+            const float el = __builtin_amdgcn_exp2f(row_scan(lg));   // block-local E_t
+            SV[j * SVS + lane].w = el;
+            if ((lane & 15) == 0) SV[j * SVS + lane].z = 1.f;
+            if ((lane & 15) != 15) SV[j * SVS + lane + 1].z = el;
         }
 #pragma unroll
         for (int m = 0; m < 5; ++m) {
@@ -289,7 +290,10 @@ __global__ __launch_bounds__(256) void chunk_f2(ChunkF2Args a, int nslice) {
                 const int i = 16 * I + g4 + r, jn = 16 * J + col;
                 const float v = isG ? (jn < i ? g[r] : 0.f) : (jn <= i ? g[r] : 0.f);
                 st(isG ? GB : PB, size_t(i) * LC + jn, v);
-                if (I == J) (isG ? GD : PD4)[I * 272 + (g4 + r) * 17 + col] = v;
+                if (I == J) {
+                    if (isG) reinterpret_cast<float *>(GDq)[((I * 16 + g4 + r) * 4 + (col & 3)) * 4 + (col >> 2)] = v;
+                    else PD4[I * 272 + (g4 + r) * 17 + col] = v;
+                }
             }
         }
         f32x4 xs[NCT], qs[NCT];   // token rows 16 wave .. + 15
@@ -308,7 +312,7 @@ __global__ __launch_bounds__(256) void chunk_f2(ChunkF2Args a, int nslice) {
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * wave + g4 + r, j = 16 * ct + col;
                 const float ebp = t > 0 ? EB[(t - 1) * RS + j] : 1.f;
-                R0[t * RS + j] -= ebp * xs[ct][r];
+                SV[j * SVS + t].y -= ebp * xs[ct][r];
                 OA[t * RS + j] = EB[t * RS + j] * qs[ct][r];
             }
         __syncthreads();
@@ -325,24 +329,34 @@ __global__ __launch_bounds__(256) void chunk_f2(ChunkF2Args a, int nslice) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) H0[(g4 + r) * 17 + col] = h[r];
                 }
-                const float fblk = EBL[(16 * I + 15) * RS + j];   // e^{b_end - b_s}
+                const float fblk = SV[j * SVS + 16 * I + 15].w;   // e^{b_end - b_s}
                 const bool sep = __all(fblk >= 0x1p-100f);
                 wave_lds_sync();
                 if (sep) {
                     float w[4] = {0.f, 0.f, 0.f, 0.f};   // w_l = u_l / E_l, l = 4 m + q
+                    // operands of step i + 1 are loaded while step i computes
+                    float4 sv_n = SV[j * SVS + 16 * I], gq_n = GDq[(I * 16) * 4 + q];
+                    float h_n = I > 0 ? H0[jj] : 0.f;
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        const int t = 16 * I + i;
+                        const float4 sv = sv_n, gq = gq_n;
+                        const float h = h_n;
+                        if (i < 15) {
+                            sv_n = SV[j * SVS + 16 * I + i + 1];
+                            gq_n = GDq[(I * 16 + i + 1) * 4 + q];
+                            if (I > 0) h_n = H0[(i + 1) * 17 + jj];
+                        }
+                        // w_l = 0 for l >= i (not yet written) and G's diagonal block
+                        // is zero on and above its diagonal: no masks needed
                         float part_s = 0.f;
-#pragma unroll
-                        for (int m = 0; m < 4; ++m)
-                            if (4 * m < i) part_s += (4 * m + q < i ? GD[I * 272 + i * 17 + 4 * m + q] : 0.f) * w[m];
-                        float sum = quad_sum(part_s);
-                        if (I > 0) sum += H0[i * 17 + jj];
-                        const float ep = i > 0 ? EBL[(t - 1) * RS + j] : 1.f;
-                        const float u = ETA[t * RS + j] * (R0[t * RS + j] - ep * sum);
-                        const float wi = u * __builtin_amdgcn_rcpf(EBL[t * RS + j]);
-                        if (q == (i & 3)) w[i >> 2] = wi;
+                        if (i > 0) part_s += gq.x * w[0];
+                        if (i > 4) part_s += gq.y * w[1];
+                        if (i > 8) part_s += gq.z * w[2];
+                        if (i > 12) part_s += gq.w * w[3];
+                        const float sum = quad_sum(part_s) + h;
+                        const float u = sv.x * (sv.y - sv.z * sum);
+                        const float wi = u * __builtin_amdgcn_rcpf(sv.w);
+                        w[i >> 2] = q == (i & 3) ? wi : w[i >> 2];
                     }
 #pragma unroll
                     for (int m = 0; m < 4; ++m) st(WT, size_t(j) * LC + 16 * I + 4 * m + q, w[m]);
@@ -356,7 +370,7 @@ __global__ __launch_bounds__(256) void chunk_f2(ChunkF2Args a, int nslice) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int jr = 16 * sw + g4 + r;
-                            ov[r] = OA[t * RS + jr] + EBL[t * RS + jr] * o[r];
+                            ov[r] = OA[t * RS + jr] + SV[jr * SVS + t].w * o[r];
                         }
                         if (c0 + t < T) Io<E>::store4(og + size_t(c0 + t) * DV + j0 + 16 * sw + g4, ov);
                     }
@@ -381,22 +395,25 @@ __global__ __launch_bounds__(256) void chunk_f2(ChunkF2Args a, int nslice) {
                     for (int i = 0; i < 16; ++i) {
                         const int t = 16 * I + i;
                         const float gm = GAM[t * RS + j];
-                        float part_s = 0.f;
-#pragma unroll
-                        for (int m = 0; m < 4; ++m)
-                            if (4 * m < i) part_s += (4 * m + q < i ? GD[I * 272 + i * 17 + 4 * m + q] : 0.f) * v[m];
+                        const float4 gq = GDq[(I * 16 + i) * 4 + q];
+                        const float4 sv = SV[j * SVS + t];
+                        float part_s = 0.f;   // v_l = 0 for l >= i
+                        if (i > 0) part_s += gq.x * v[0];
+                        if (i > 4) part_s += gq.y * v[1];
+                        if (i > 8) part_s += gq.z * v[2];
+                        if (i > 12) part_s += gq.w * v[3];
                         const float acc = quad_sum(part_s);
                         const float cross = I > 0 ? pb * H0[i * 17 + jj] : 0.f;
-                        const float u = ETA[t * RS + j] * (R0[t * RS + j] - cross - acc);
+                        const float u = sv.x * (sv.y - cross - acc);
 #pragma unroll
                         for (int m = 0; m < 4; ++m)
-                            if (4 * m < i) v[m] = (4 * m + q < i) ? v[m] * gm : v[m];
-                        if (q == (i & 3)) v[i >> 2] = u;
+                            if (4 * m < i) v[m] *= gm;   // zero entries stay zero
+                        v[i >> 2] = q == (i & 3) ? u : v[i >> 2];
                         pb *= gm;
-                        float part_o = 0.f;
+                        float part_o = 0.f;   // P0's diagonal block is zero above its diagonal
 #pragma unroll
                         for (int m = 0; m < 4; ++m)
-                            if (4 * m <= i) part_o += (4 * m + q <= i ? PD4[I * 272 + i * 17 + 4 * m + q] : 0.f) * v[m];
+                            if (4 * m <= i) part_o += PD4[I * 272 + i * 17 + 4 * m + q] * v[m];
                         const float oin = quad_sum(part_o);
                         if (q == 0 && c0 + t < T) {
                             float o = OA[t * RS + j] + oin;

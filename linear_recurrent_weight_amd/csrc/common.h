@@ -101,6 +101,19 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_wave_barrier();
 }
 
+// log2(1 - alpha) for alpha in [0, 1), to about 1e-7 relative: for alpha
+// < 1/4 the series log(1 - a) = -2 atanh(z) = -2 (z + z^3/3 + z^5/5 + ...),
+// z = a / (2 - a) <= 1/7 (five terms); above, the native log2 of 1 - alpha
+// (exact in fp32 there).
+__device__ __forceinline__ float log2_1m(float alpha) {
+    if (alpha < 0.25f) {
+        const float z = alpha * __builtin_amdgcn_rcpf(2.f - alpha), z2 = z * z;
+        const float p = z * (1.f + z2 * (1.f / 3.f + z2 * (1.f / 5.f + z2 * (1.f / 7.f + z2 * (1.f / 9.f)))));
+        return -2.f * 1.4426950408889634f * p;
+    }
+    return __builtin_amdgcn_logf(1.f - alpha);
+}
+
 __device__ __forceinline__ float step_eta(float beta, float den) { return den != 0.f ? beta / den : 0.f; }
 __device__ __forceinline__ float step_alpha(float eta, float lam, float eps_gamma) {
     return fminf(eta * lam, 1.f - eps_gamma);
