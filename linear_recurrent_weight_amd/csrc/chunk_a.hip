@@ -88,26 +88,28 @@ struct ChunkRows {
         const int np = C + halo;
         const E *k = static_cast<const E *>(a.k) + size_t(bh) * a.T * DK;
         const E *v = static_cast<const E *>(a.v) + size_t(bh) * a.T * a.dv;
+        // unconditional loads from rows clamped into [0, T) (a load under a
+        // branch is waited for where the branch joins); rows outside the
+        // sequence are zeroed when the pairs are staged
+        auto clampT = [&](int r) { return r < 0 ? 0 : (r < a.T ? r : a.T - 1); };
+        (void)np;
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
             const int p = 64 * pass + row;
             const int tau = c0 - halo + p;
-            if (p < np && tau >= 1 && tau < a.T) kr[pass].load(k + size_t(tau - 1) * DK + part * (DK / 4));
-            else kr[pass].clear();
-            if (p < np && tau >= 0 && tau < a.T) vr[pass].load(v + size_t(tau) * a.dv + part * (DV / 4));
-            else vr[pass].clear();
+            kr[pass].load(k + size_t(clampT(tau - 1)) * DK + part * (DK / 4));
+            vr[pass].load(v + size_t(clampT(tau)) * a.dv + part * (DV / 4));
         }
         if constexpr (WITH_Q) {
             const E *q = static_cast<const E *>(a.q) + size_t(bh) * a.T * DK;
-            const int t = c0 + row;
-            if (t < a.T) qr.load(q + size_t(t) * DK + part * (DK / 4));
-            else qr.clear();
+            qr.load(q + size_t(clampT(c0 + row)) * DK + part * (DK / 4));
         }
     }
 
-    // normalised pair features into xf[p][ldx] (fp32) and values into yt[j][p]
+    // normalised pair features into xf[p][ldx] (fp32), their squared norms
+    // into nrm[p] and values into yt[j][p]
     __device__ void store_pairs(const ChunkAArgs &a, int bh, int c0, int halo, float *xf, int ldx, E *yt,
-                                int ldy) const {
+                                int ldy, float *nrm) const {
         const int row = threadIdx.x >> 2, part = threadIdx.x & 3;
         const int np = C + halo;
 #pragma unroll
@@ -117,7 +119,7 @@ struct ChunkRows {
             float x[DK / 4];
             bool from_k = p < np && tau >= 1 && tau < a.T;
 #pragma unroll
-            for (int e = 0; e < DK / 4; ++e) x[e] = kr[pass].get(e);
+            for (int e = 0; e < DK / 4; ++e) x[e] = from_k ? kr[pass].get(e) : 0.f;
             if (p < np && tau == 0 && a.xnext_in) {
 #pragma unroll
                 for (int e = 0; e < DK / 4; ++e) x[e] = a.xnext_in[size_t(bh) * DK + part * (DK / 4) + e];
@@ -134,10 +136,12 @@ struct ChunkRows {
             if (p < 64 + HMAX) {
 #pragma unroll
                 for (int e = 0; e < DK / 4; ++e) xf[p * ldx + part * (DK / 4) + e] = x[e] * sc;
+                if (nrm && part == 0) nrm[p] = sc * sc * ss;
             }
+            const bool y_ok = p < np && tau >= 0 && tau < a.T;
             float y[DV / 4];
 #pragma unroll
-            for (int e = 0; e < DV / 4; ++e) y[e] = vr[pass].get(e);
+            for (int e = 0; e < DV / 4; ++e) y[e] = y_ok ? vr[pass].get(e) : 0.f;
             if (p < np && tau < 0 && tau >= -a.n_tail_in) {
                 const float *src = a.taily_in + (size_t(bh) * halo + tau + halo) * a.dv + part * (DV / 4);
 #pragma unroll
@@ -153,13 +157,14 @@ struct ChunkRows {
     }
 
     // normalised query features into qe[t][ldq]
-    __device__ void store_queries(const ChunkAArgs &a, E *qe, int ldq) const {
+    __device__ void store_queries(const ChunkAArgs &a, int c0, E *qe, int ldq) const {
         const int row = threadIdx.x >> 2, part = threadIdx.x & 3;
+        const bool ok = c0 + row < a.T;
         float y[DK / 4];
         float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < DK / 4; ++e) {
-            y[e] = qr.get(e);
+            y[e] = ok ? qr.get(e) : 0.f;
             ss += y[e] * y[e];
         }
         ss = group_sum<4>(ss);
@@ -182,7 +187,7 @@ __global__ __launch_bounds__(256) void a_segment(ChunkAArgs a) {
     __shared__ __align__(16) E XT[DK * LDT];     // (diag(coef) X)^T  [d][p]
     __shared__ __align__(16) E YT[DV * LDT];     // Y^T               [j][p]
     __shared__ float band[NPM * 8];
-    __shared__ float mu_s[C], ew_s[C], gam_s[C], coef[KP];
+    __shared__ float mu_s[C], ew_s[C], gam_s[C], coef[KP], nrm[NPM];
     __shared__ float bC_s;
 
     const int seg = blockIdx.x, bh = blockIdx.y;
@@ -206,12 +211,11 @@ __global__ __launch_bounds__(256) void a_segment(ChunkAArgs a) {
     rows.prefetch(a, bh, c_begin * C, halo);
     for (int c = c_begin; c < c_end; ++c) {
         const int c0 = c * C;
-        rows.store_pairs(a, bh, c0, halo, XF, LDX, YT, LDT);
-        float beta_t = 0.f, lam_t = 0.f;
-        if (tid < C && c0 + tid < T) {
-            beta_t = a.beta[size_t(bh) * T + c0 + tid];
-            lam_t = a.lambda[size_t(bh) * T + c0 + tid];
-        }
+        rows.store_pairs(a, bh, c0, halo, XF, LDX, YT, LDT, nrm);
+        // unconditional (clamped) loads; unused past the sequence end
+        const int tcl = c0 + (tid & 63) < T ? c0 + (tid & 63) : T - 1;
+        const float beta_t = a.beta[size_t(bh) * T + tcl];
+        const float lam_t = a.lambda[size_t(bh) * T + tcl];
         if (c + 1 < c_end) rows.prefetch(a, bh, c0 + C, halo);
         __syncthreads();
         // window statistic / feature energy of the chunk's own tokens
@@ -245,9 +249,7 @@ __global__ __launch_bounds__(256) void a_segment(ChunkAArgs a) {
                 ew_s[tid] = 1.f / float(bt);
             }
         } else if (tid < C) {
-            float s = 0.f;
-            for (int e = 0; e < DK; ++e) s += XF[(tid + halo) * LDX + e] * XF[(tid + halo) * LDX + e];
-            mu_s[tid] = s;
+            mu_s[tid] = nrm[tid + halo];   // ||x_t||^2 from the feature pass
             ew_s[tid] = 1.f;
         }
         __syncthreads();
@@ -272,15 +274,22 @@ __global__ __launch_bounds__(256) void a_segment(ChunkAArgs a) {
         __syncthreads();
         // coefficients of the chunk write: coef_p = M_{63, p}
         if (tid < KP) {
-            const int p = tid, j = p - halo;
+            const int p = tid, j = p - halo, t_lo = j > 0 ? j : 0, t_hi = j + halo;
             float m = 0.f;
-            if (p < np) {
-                for (int t = 0; t < C; ++t) {
-                    const bool in = t >= (j > 0 ? j : 0) && t <= j + halo;
-                    m = gam_s[t] * m + (in ? ew_s[t] : 0.f);
+            for (int t0 = 0; t0 < C; t0 += 8) {
+                float gm[8], ew[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    gm[u] = gam_s[t0 + u];
+                    ew[u] = ew_s[t0 + u];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int t = t0 + u;
+                    m = gm[u] * m + ((t >= t_lo && t <= t_hi) ? ew[u] : 0.f);
                 }
             }
-            coef[p] = m;
+            coef[p] = p < np ? m : 0.f;
         }
         __syncthreads();
         for (int idx = tid; idx < KP * DK; idx += 256) {
@@ -425,8 +434,8 @@ __global__ __launch_bounds__(256) void a_output(ChunkAArgs a) {
     rows.prefetch(a, bh, c_begin * C, halo);
     for (int c = c_begin; c < c_end; ++c) {
         const int c0 = c * C;
-        rows.store_pairs(a, bh, c0, halo, XF, DK + 1, YT, LDT);
-        rows.store_queries(a, QE, LDK);
+        rows.store_pairs(a, bh, c0, halo, XF, DK + 1, YT, LDT, nullptr);
+        rows.store_queries(a, c0, QE, LDK);
         float ew = 0.f, lg = 0.f;
         if (wave == 0) {
             ew = a.etaw[size_t(bh) * a.Tpad + c0 + lane];
@@ -457,16 +466,26 @@ __global__ __launch_bounds__(256) void a_output(ChunkAArgs a) {
         __syncthreads();
         // mask by the column recurrence; coefficients of the chunk write
         if (tid < KP) {
-            const int p = tid, j = p - halo;
+            const int p = tid, j = p - halo, t_lo = j > 0 ? j : 0, t_hi = p < np ? j + halo : -1;
             float m = 0.f;
-            for (int t = 0; t < C; ++t) {
-                const bool in = p < np && t >= (j > 0 ? j : 0) && t <= j + halo;
-                m = gam_s[t] * m + (in ? ew_s[t] : 0.f);
-                const float pv = PF[t * LDF + p] * m;
-                if constexpr (PBuf<E>::separate)
-                    st(PE, size_t(t) * LDT + p, pv);
-                else
-                    PF[t * LDF + p] = pv;
+            for (int t0 = 0; t0 < C; t0 += 8) {
+                float gm[8], ew[8], pf[8];   // operands of 8 steps loaded up front
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    gm[u] = gam_s[t0 + u];
+                    ew[u] = ew_s[t0 + u];
+                    pf[u] = PF[(t0 + u) * LDF + p];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int t = t0 + u;
+                    m = gm[u] * m + ((t >= t_lo && t <= t_hi) ? ew[u] : 0.f);
+                    const float pv = pf[u] * m;
+                    if constexpr (PBuf<E>::separate)
+                        st(PE, size_t(t) * LDT + p, pv);
+                    else
+                        PF[t * LDF + p] = pv;
+                }
             }
             coef[p] = m;
         }
