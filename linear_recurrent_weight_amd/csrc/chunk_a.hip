@@ -74,6 +74,25 @@ struct RowPart {
     }
 };
 
+// N consecutive values (N a multiple of 8 for bf16, of 4 for fp32) to a
+// 16-byte aligned destination with vector stores
+template <class E, int N>
+__device__ __forceinline__ void store_vec(E *dst, const float *v) {
+    if constexpr (sizeof(E) == 2) {
+        static_assert(N % 8 == 0, "bf16 rows in 16-byte pieces");
+        auto p2 = [](float x, float y) { return uint32_t(f32_to_bf16(x)) | (uint32_t(f32_to_bf16(y)) << 16); };
+#pragma unroll
+        for (int i = 0; i < N / 8; ++i)
+            reinterpret_cast<uint4 *>(dst)[i] = make_uint4(p2(v[8 * i], v[8 * i + 1]), p2(v[8 * i + 2], v[8 * i + 3]),
+                                                           p2(v[8 * i + 4], v[8 * i + 5]), p2(v[8 * i + 6], v[8 * i + 7]));
+    } else {
+        static_assert(N % 4 == 0, "fp32 rows in 16-byte pieces");
+#pragma unroll
+        for (int i = 0; i < N / 4; ++i)
+            reinterpret_cast<float4 *>(dst)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+    }
+}
+
 // Raw rows of one chunk, prefetched into registers: 4 threads per row, pair
 // rows p = row and 64 + row (the halo makes at most 71 pairs), and the
 // chunk's query rows.  tau = c0 - halo + p is the pair's token.
@@ -106,10 +125,11 @@ struct ChunkRows {
         }
     }
 
-    // normalised pair features into xf[p][ldx] (fp32), their squared norms
-    // into nrm[p] and values into yt[j][p]
-    __device__ void store_pairs(const ChunkAArgs &a, int bh, int c0, int halo, float *xf, int ldx, E *yt,
-                                int ldy, float *nrm) const {
+    // normalised pair features into xf[p][ldx] (fp32) and / or xe[p][lde]
+    // (storage type, 16-byte vector stores), their squared norms into nrm[p]
+    // and values into yt[j][p]
+    __device__ void store_pairs(const ChunkAArgs &a, int bh, int c0, int halo, float *xf, int ldx, E *xe,
+                                int lde, E *yt, int ldy, float *nrm) const {
         const int row = threadIdx.x >> 2, part = threadIdx.x & 3;
         const int np = C + halo;
 #pragma unroll
@@ -133,11 +153,16 @@ struct ChunkRows {
             for (int e = 0; e < DK / 4; ++e) ss += x[e] * x[e];
             ss = group_sum<4>(ss);
             const float sc = from_k ? phi_scale(ss, DK, a.eps_rms, a.phi) : 1.f;
-            if (p < 64 + HMAX) {
 #pragma unroll
-                for (int e = 0; e < DK / 4; ++e) xf[p * ldx + part * (DK / 4) + e] = x[e] * sc;
+            for (int e = 0; e < DK / 4; ++e) x[e] *= sc;
+            if (p < 64 + HMAX) {
+                if (xf) {
+#pragma unroll
+                    for (int e = 0; e < DK / 4; ++e) xf[p * ldx + part * (DK / 4) + e] = x[e];
+                }
                 if (nrm && part == 0) nrm[p] = sc * sc * ss;
             }
+            if (xe && p < KP) store_vec<E, DK / 4>(xe + size_t(p) * lde + part * (DK / 4), x);
             const bool y_ok = p < np && tau >= 0 && tau < a.T;
             float y[DV / 4];
 #pragma unroll
@@ -156,7 +181,7 @@ struct ChunkRows {
         // were written with zeros above (their rows were cleared)
     }
 
-    // normalised query features into qe[t][ldq]
+    // normalised query features into qe[t][ldq] (16-byte vector stores)
     __device__ void store_queries(const ChunkAArgs &a, int c0, E *qe, int ldq) const {
         const int row = threadIdx.x >> 2, part = threadIdx.x & 3;
         const bool ok = c0 + row < a.T;
@@ -170,7 +195,8 @@ struct ChunkRows {
         ss = group_sum<4>(ss);
         const float sc = phi_scale(ss, DK, a.eps_rms, a.phi);
 #pragma unroll
-        for (int e = 0; e < DK / 4; ++e) st(qe, size_t(row) * ldq + part * (DK / 4) + e, y[e] * sc);
+        for (int e = 0; e < DK / 4; ++e) y[e] *= sc;
+        store_vec<E, DK / 4>(qe + size_t(row) * ldq + part * (DK / 4), y);
     }
 };
 
@@ -211,7 +237,7 @@ __global__ __launch_bounds__(256) void a_segment(ChunkAArgs a) {
     rows.prefetch(a, bh, c_begin * C, halo);
     for (int c = c_begin; c < c_end; ++c) {
         const int c0 = c * C;
-        rows.store_pairs(a, bh, c0, halo, XF, LDX, YT, LDT, nrm);
+        rows.store_pairs(a, bh, c0, halo, XF, LDX, static_cast<E *>(nullptr), 0, YT, LDT, nrm);
         // unconditional (clamped) loads; unused past the sequence end
         const int tcl = c0 + (tid & 63) < T ? c0 + (tid & 63) : T - 1;
         const float beta_t = a.beta[size_t(bh) * T + tcl];
@@ -391,7 +417,6 @@ __global__ __launch_bounds__(256) void a_output(ChunkAArgs a) {
     constexpr int LDT = KP + PD;        // [.][pair] rows
     constexpr int LDF = KP + 1;         // fp32 score rows
     constexpr int NPM = C + HMAX;
-    __shared__ float XF[NPM * (DK + 1)];                 // pair features (fp32)
     __shared__ __align__(16) E XE[KP * LDK];             // pair features [p][d]
     __shared__ __align__(16) E XT[DK * LDT];             // (diag(coef) X)^T [d][p]
     __shared__ __align__(16) E QE[C * LDK];              // query features [t][d]
@@ -399,7 +424,7 @@ __global__ __launch_bounds__(256) void a_output(ChunkAArgs a) {
     __shared__ __align__(16) E ST[DV * LDK];             // S^T copy [j][d]
     __shared__ __align__(16) float PF[C * LDF];          // scores, then decayed scores
     __shared__ __align__(16) E PE[PBuf<E>::separate ? C * LDT : 1];
-    __shared__ float ew_s[C], gam_s[C], g_s[C], coef[KP];
+    __shared__ float ew_s[C], gam_s[C], g_s[C], coef[KP], mend_s[KP];
     __shared__ float bC_s;
 
     const int seg = blockIdx.x, bh = blockIdx.y;
@@ -434,7 +459,7 @@ __global__ __launch_bounds__(256) void a_output(ChunkAArgs a) {
     rows.prefetch(a, bh, c_begin * C, halo);
     for (int c = c_begin; c < c_end; ++c) {
         const int c0 = c * C;
-        rows.store_pairs(a, bh, c0, halo, XF, DK + 1, YT, LDT, nullptr);
+        rows.store_pairs(a, bh, c0, halo, nullptr, 0, XE, LDK, YT, LDT, nullptr);
         rows.store_queries(a, c0, QE, LDK);
         float ew = 0.f, lg = 0.f;
         if (wave == 0) {
@@ -450,11 +475,6 @@ __global__ __launch_bounds__(256) void a_output(ChunkAArgs a) {
             if (lane == 63) bC_s = b;
         }
         __syncthreads();
-        for (int idx = tid; idx < KP * DK; idx += 256) {
-            const int p = idx / DK, d = idx % DK;
-            st(XE, size_t(p) * LDK + d, p < np ? XF[p * (DK + 1) + d] : 0.f);
-        }
-        __syncthreads();
         // scores Qh X_ext^T (4 token tiles x 6 pair tiles)
         for (int tile = wave; tile < 4 * (KP / 16); tile += 4) {
             const int tt = tile % 4, pt = tile / 4;
@@ -465,34 +485,46 @@ __global__ __launch_bounds__(256) void a_output(ChunkAArgs a) {
         }
         __syncthreads();
         // mask by the column recurrence; coefficients of the chunk write
-        if (tid < KP) {
-            const int p = tid, j = p - halo, t_lo = j > 0 ? j : 0, t_hi = p < np ? j + halo : -1;
-            float m = 0.f;
-            for (int t0 = 0; t0 < C; t0 += 8) {
-                float gm[8], ew[8], pf[8];   // operands of 8 steps loaded up front
+        // Each column of the mask in two halves of 32 tokens (thread: column
+        // p, half h): the recurrence from 0 inside the half and the running
+        // product of carries, then the second half adds that product times
+        // the first half's end value (an exact split of the linear recurrence).
+        const int mp = tid % KP, mh = tid / KP;   // threads 0 .. 2 KP - 1
+        float mloc[32], mpr[32];
+        if (tid < 2 * KP) {
+            const int j = mp - halo, t_lo = j > 0 ? j : 0, t_hi = mp < np ? j + halo : -1;
+            float m = 0.f, pr = 1.f;
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    gm[u] = gam_s[t0 + u];
-                    ew[u] = ew_s[t0 + u];
-                    pf[u] = PF[(t0 + u) * LDF + p];
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int t = t0 + u;
-                    m = gm[u] * m + ((t >= t_lo && t <= t_hi) ? ew[u] : 0.f);
-                    const float pv = pf[u] * m;
-                    if constexpr (PBuf<E>::separate)
-                        st(PE, size_t(t) * LDT + p, pv);
-                    else
-                        PF[t * LDF + p] = pv;
-                }
+            for (int u = 0; u < 32; ++u) {
+                const int t = 32 * mh + u;
+                const float gm = gam_s[t];
+                m = gm * m + ((t >= t_lo && t <= t_hi) ? ew_s[t] : 0.f);
+                pr *= gm;
+                mloc[u] = m;
+                mpr[u] = pr;
             }
-            coef[p] = m;
+            if (mh == 0) mend_s[mp] = m;
+        }
+        __syncthreads();
+        if (tid < 2 * KP) {
+            const float m_in = mh == 1 ? mend_s[mp] : 0.f;
+            float m = 0.f;
+#pragma unroll
+            for (int u = 0; u < 32; ++u) {
+                const int t = 32 * mh + u;
+                m = mloc[u] + mpr[u] * m_in;
+                const float pv = PF[t * LDF + mp] * m;
+                if constexpr (PBuf<E>::separate)
+                    st(PE, size_t(t) * LDT + mp, pv);
+                else
+                    PF[t * LDF + mp] = pv;
+            }
+            if (mh == 1) coef[mp] = m;
         }
         __syncthreads();
         for (int idx = tid; idx < KP * DK; idx += 256) {
             const int p = idx / DK, d = idx % DK;
-            st(XT, size_t(d) * LDT + p, p < np ? coef[p] * XF[p * (DK + 1) + d] : 0.f);
+            st(XT, size_t(d) * LDT + p, p < np ? coef[p] * ld(XE, size_t(p) * LDK + d) : 0.f);
         }
         __syncthreads();
         // outputs: O^T = (S^T Qh^T) diag(Gamma) + Y^T P^T;  tiles (jt, token tile)
