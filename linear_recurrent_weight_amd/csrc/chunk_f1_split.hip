@@ -17,7 +17,9 @@
 // f1_walk: one workgroup per (head, slice of DS value columns) walks the
 //   chunks in order.  Chain wave w owns state columns 16w..16w+15 (all d_k
 //   rows in MFMA accumulators) and needs no other chain wave inside a chunk:
-//     XS, Qh S -> R0 -> U = Tp R0 -> O = Gamma Qh S + P U -> S' (MFMA).
+//     XS -> R0 -> U = Tp R0 -> S' = Gamma_C S + (w X)^T U   (MFMA);
+//   output wave w writes the previous chunk's O = Gamma Qh S + P U from the
+//   state and writes that chunk started with.
 //   Four loader waves stage the next chunk meanwhile: raw q, k, v rows and
 //   the chunk operators prefetched a chunk ahead, QK-RMSNorm, all into the
 //   other LDS buffer.  One workgroup barrier per chunk.
@@ -54,10 +56,10 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f3
 }
 __device__ __forceinline__ bf16x8 ld8(const bf16_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 
-// features of one row part: 4 threads per row, EPT elements each
-template <int DK>
+// features of one row part: TPR threads per row, EPT elements each
+template <int DK, int TPR = 4>
 struct RowPart {
-    static constexpr int EPT = DK / 4, NV = EPT / 8;
+    static constexpr int EPT = DK / TPR, NV = EPT / 8;
     uint4 q[NV], k[NV];
     // Loads are unconditional, from rows clamped into [0, T) (T >= 1 here):
     // a load under a branch would be waited for where the branch joins.
@@ -95,8 +97,8 @@ struct RowPart {
             sq += qv[e] * qv[e];
             sk += xv[e] * xv[e];
         }
-        sq = group_sum<4>(sq);
-        sk = group_sum<4>(sk);
+        sq = group_sum<TPR>(sq);
+        sk = group_sum<TPR>(sk);
         const float scq = phi_scale(sq, DK, a.eps_rms, a.phi);
         const float sck = first ? 1.f : phi_scale(sk, DK, a.eps_rms, a.phi);
         float n2 = 0.f;
@@ -106,7 +108,7 @@ struct RowPart {
             qv[e] *= scq;
             n2 += xv[e] * xv[e];
         }
-        return group_sum<4>(n2);
+        return group_sum<TPR>(n2);
     }
 };
 
@@ -343,27 +345,30 @@ __global__ __launch_bounds__(256) void f1_ops(F1SplitArgs a) {
 // ---------------------------------------------------------------------------
 // f1_walk: sequential walk over the chunks of one (head, DS-column slice)
 // ---------------------------------------------------------------------------
-template <int DK, int DS>
-__global__ __launch_bounds__((DS / 16 + 4) * 64) void f1_walk(F1SplitArgs a, int nslice) {
-    constexpr int NCW = DS / 16;          // chain waves
+template <int DK, int DS, int NLW>
+__global__ __launch_bounds__((2 * (DS / 16) + NLW) * 64) void f1_walk(F1SplitArgs a, int nslice) {
+    constexpr int NCW = DS / 16;          // chain waves (= output waves)
+    constexpr int NLT = 64 * NLW;         // loader threads
     constexpr int PK = DK + 8;
-    constexpr int PY = DS + 8;            // bf16 stride of value rows
-    constexpr int YE = DS / 4;            // value elements per loader thread
-    constexpr int YV = YE / 8;            // 16-byte vectors of them
-    using RP = RowPart<DK>;
-    static_assert(DK == 64, "loader threads cover 64 rows x 4 parts of 16 features");
-    static_assert(DS == 32 || DS == 64, "slice of 32 or 64 value columns");
+    constexpr int YP = DS / 8;            // 16-byte pieces of a value row
+    using RP = RowPart<DK, NLW>;          // NLW threads per feature row
+    static_assert(DK == 64 && (NLW == 4 || NLW == 8), "loaders: 64 rows x NLW parts of the features");
+    static_assert(DS == 32, "slice of 32 value columns");
+    static_assert(64 * YP <= NLT && 512 % NLT == 0, "one value piece per thread; whole tiles");
+    constexpr int TPT = 512 / NLT;        // 16-byte tile pieces per loader thread
 
+    // chunk c uses buffers c % 2 (chain operands) and c % 3 (operands the
+    // output waves read one chunk later)
     __shared__ __align__(16) bf16_t XB[2][C * PK];     // x rows [t][d]
-    __shared__ __align__(16) bf16_t QB[2][C * PK];     // qh rows [t][d]
     __shared__ __align__(16) bf16_t XWT[2][DK * PC];   // (e^{b_C-b_t} x_t)^T [d][t]
-    __shared__ __align__(16) bf16_t YB[2][C * PY];     // values [t][j]
+    __shared__ __align__(16) bf16_t YT[2][DS * PC];    // values^T [j][t]
     __shared__ __align__(16) bf16_t TPB[2][C * PC];    // Tp [t][s]
-    __shared__ __align__(16) bf16_t PB[2][C * PC];     // P [t][s]
-    __shared__ float SC[2][4 * C];                     // decay rows
-    __shared__ __align__(16) bf16_t STw[NCW][16 * PK]; // per chain wave: S^T [j][d]
-    __shared__ __align__(16) bf16_t RTw[NCW][16 * PC]; // per chain wave: R0^T [j][t]
-    __shared__ __align__(16) bf16_t UTw[NCW][16 * PC]; // per chain wave: U^T [j][t]
+    __shared__ __align__(16) bf16_t QB[3][C * PK];     // qh rows [t][d]
+    __shared__ __align__(16) bf16_t PB[3][C * PC];     // P [t][s]
+    __shared__ float SC[3][4 * C];                     // decay rows
+    __shared__ __align__(16) bf16_t STw[NCW][3][16 * PK];  // per column tile: S^T [j][d] at chunk start
+    __shared__ __align__(16) bf16_t RTw[NCW][16 * PC];     // per column tile: R0^T [j][t]
+    __shared__ __align__(16) bf16_t UTw[NCW][2][16 * PC];  // per column tile: U^T [j][t]
 
     int bh, s;
     if (nslice == 1) {
@@ -379,6 +384,8 @@ __global__ __launch_bounds__((DS / 16 + 4) * 64) void f1_walk(F1SplitArgs a, int
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool chain = wave < NCW;
+    const bool outw = wave >= NCW && wave < 2 * NCW;
+    const bool loader = wave >= 2 * NCW;
     const int T = a.T, DV = a.dv, nch = a.nchunks;
     const bf16_t *qg = static_cast<const bf16_t *>(a.q) + size_t(bh) * T * DK;
     const bf16_t *kg = static_cast<const bf16_t *>(a.k) + size_t(bh) * T * DK;
@@ -387,107 +394,117 @@ __global__ __launch_bounds__((DS / 16 + 4) * 64) void f1_walk(F1SplitArgs a, int
     const char *opsb = static_cast<const char *>(a.ops) + size_t(bh) * nch * kF1SplitChunkBytes;
 
     // ---- loaders: rows and operators of the next chunk, prefetched ----
-    const int lt = tid - NCW * 64;        // loader thread index (valid for loaders)
-    const int lrow = lt >> 2, lpart = lt & 3;
-    RP rp;
-    uint4 ry[YV];
-    uint4 rtp0, rtp1, rpp0, rpp1, rxw0, rxw1;   // separate names keep them in registers
-    float rsc = 0.f;
-    auto prefetch = [&](int c) {
+    const int lt = tid - 2 * NCW * 64;    // loader thread index (valid for loaders)
+    const int lrow = lt / NLW, lpart = lt % NLW;
+    const int yrow = (lt / YP) % C, ypc = lt % YP;   // value piece of this thread (stored if lt < 64 YP)
+    // two sets of prefetch registers: the rows of a chunk are loaded two
+    // iterations before they are staged (the walk is short per chunk, a
+    // global load round trip is not)
+    struct Regs {
+        RP rp;
+        uint4 ry;
+        uint4 rtp[TPT], rpp[TPT], rxw[TPT];
+        float rsc;
+    };
+    Regs ra, rb;
+    auto prefetch = [&](int c, Regs &R) {
         const int t = c * C + lrow;
-        rp.load(qg, kg, t, T, lpart);
-#pragma unroll
-        for (int v = 0; v < YV; ++v)   // clamped row; zeroed at staging when t >= T
-            ry[v] = *reinterpret_cast<const uint4 *>(vg + size_t(t < T ? t : T - 1) * DV + j0 + lpart * YE + 8 * v);
+        R.rp.load(qg, kg, t, T, lpart);
+        const int ty = c * C + yrow;   // clamped row; zeroed at staging when ty >= T
+        // every loader thread loads (a load under a branch would be waited for
+        // at the join); threads past the value pieces re-read a valid piece
+        R.ry = *reinterpret_cast<const uint4 *>(vg + size_t(ty < T ? ty : T - 1) * DV + j0 + 8 * ypc);
         const char *ops = opsb + size_t(c) * kF1SplitChunkBytes;
         const uint4 *tp = reinterpret_cast<const uint4 *>(ops);
         const uint4 *pp = reinterpret_cast<const uint4 *>(ops + kF1SplitPOff);
         const uint4 *xp = reinterpret_cast<const uint4 *>(ops + kF1SplitXwOff);
-        rtp0 = tp[lt];
-        rtp1 = tp[lt + 256];
-        rpp0 = pp[lt];
-        rpp1 = pp[lt + 256];
-        rxw0 = xp[lt];
-        rxw1 = xp[lt + 256];
-        rsc = reinterpret_cast<const float *>(ops + kF1SplitScalOff)[lt];
+#pragma unroll
+        for (int h = 0; h < TPT; ++h) {
+            R.rtp[h] = tp[lt + NLT * h];
+            R.rpp[h] = pp[lt + NLT * h];
+            R.rxw[h] = xp[lt + NLT * h];
+        }
+        R.rsc = reinterpret_cast<const float *>(ops + kF1SplitScalOff)[lt % (4 * C)];
     };
-    auto stage = [&](int c) {   // prefetched rows of chunk c -> LDS buffer c & 1
-        const int b = c & 1;
+    auto stage = [&](int c, const Regs &R) {   // prefetched rows of chunk c -> LDS buffers
+        const int b2 = c & 1, b3 = c % 3;
         const int t = c * C + lrow;
         float xv[RP::EPT], qv[RP::EPT];
-        (void)rp.features(xv, qv, t, lpart, a, bh);
+        (void)R.rp.features(xv, qv, t, lpart, a, bh);
 #pragma unroll
         for (int v = 0; v < RP::NV; ++v) {
-            *reinterpret_cast<uint4 *>(XB[b] + lrow * PK + lpart * RP::EPT + 8 * v) = pack8(xv + 8 * v);
-            *reinterpret_cast<uint4 *>(QB[b] + lrow * PK + lpart * RP::EPT + 8 * v) = pack8(qv + 8 * v);
+            *reinterpret_cast<uint4 *>(XB[b2] + lrow * PK + lpart * RP::EPT + 8 * v) = pack8(xv + 8 * v);
+            *reinterpret_cast<uint4 *>(QB[b3] + lrow * PK + lpart * RP::EPT + 8 * v) = pack8(qv + 8 * v);
+        }
+        if (lt < 64 * YP) {   // values transposed: 8 columns of row yrow
+            float yv[8];
+            unpack8(R.ry, yv);
+            const bool ok = c * C + yrow < T;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) st(YT[b2], size_t(8 * ypc + e) * PC + yrow, ok ? yv[e] : 0.f);
         }
 #pragma unroll
-        for (int v = 0; v < YV; ++v)
-            *reinterpret_cast<uint4 *>(YB[b] + lrow * PY + lpart * YE + 8 * v) = t < T ? ry[v] : make_uint4(0, 0, 0, 0);
-        {
+        for (int h = 0; h < TPT; ++h) {
             // 16-byte piece u of a 64 x 64 tile: row u / 8, columns 8 (u % 8) ..
-            const int r0 = lt >> 3, r1 = (lt + 256) >> 3, c8 = 8 * (lt & 7);
-            *reinterpret_cast<uint4 *>(TPB[b] + r0 * PC + c8) = rtp0;
-            *reinterpret_cast<uint4 *>(TPB[b] + r1 * PC + c8) = rtp1;
-            *reinterpret_cast<uint4 *>(PB[b] + r0 * PC + c8) = rpp0;
-            *reinterpret_cast<uint4 *>(PB[b] + r1 * PC + c8) = rpp1;
-            *reinterpret_cast<uint4 *>(XWT[b] + r0 * PC + c8) = rxw0;
-            *reinterpret_cast<uint4 *>(XWT[b] + r1 * PC + c8) = rxw1;
+            const int u = lt + NLT * h, r = u >> 3, c8 = 8 * (u & 7);
+            *reinterpret_cast<uint4 *>(TPB[b2] + r * PC + c8) = R.rtp[h];
+            *reinterpret_cast<uint4 *>(PB[b3] + r * PC + c8) = R.rpp[h];
+            *reinterpret_cast<uint4 *>(XWT[b2] + r * PC + c8) = R.rxw[h];
         }
-        SC[b][lt] = rsc;
+        if (lt < 4 * C) SC[b3][lt] = R.rsc;
     };
 
-    // ---- chain state: S[:, j0 + 16w ..] in accumulators (d tiles m) ----
-    f32x4 S[DK / 16];
-    bf16_t *st_w = STw[chain ? wave : 0];
-    bf16_t *rt_w = RTw[chain ? wave : 0];
-    bf16_t *ut_w = UTw[chain ? wave : 0];
     const int col = lane & 15, g4 = 4 * (lane >> 4), k8 = 8 * (lane >> 4);
+    const int ct = chain ? wave : (outw ? wave - NCW : 0);   // column tile of a chain / output wave
+    // ---- chain state: S[:, j0 + 16 ct ..] in accumulators (d tiles m) ----
+    f32x4 S[DK / 16];
     if (chain) {
 #pragma unroll
         for (int m = 0; m < DK / 16; ++m) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int d = 16 * m + g4 + r;
-                S[m][r] = a.S_in ? a.S_in[(size_t(bh) * DK + d) * DV + j0 + 16 * wave + col] : 0.f;
+                S[m][r] = a.S_in ? a.S_in[(size_t(bh) * DK + d) * DV + j0 + 16 * ct + col] : 0.f;
             }
-            *reinterpret_cast<uint2 *>(st_w + col * PK + 16 * m + g4) = pack4(S[m][0], S[m][1], S[m][2], S[m][3]);
+            *reinterpret_cast<uint2 *>(STw[ct][0] + col * PK + 16 * m + g4) = pack4(S[m][0], S[m][1], S[m][2], S[m][3]);
         }
-    } else {
-        prefetch(0);
-        stage(0);
-        if (nch > 1) prefetch(1);
+    } else if (loader) {
+        prefetch(0, ra);
+        stage(0, ra);
+        if (nch > 1) prefetch(1, rb);
+        if (nch > 2) prefetch(2, ra);
     }
     __syncthreads();
 
-    for (int c = 0; c < nch; ++c) {
-        const int b = c & 1;
-        if (chain) {
-            const bf16_t *X = XB[b], *Q = QB[b], *Tp = TPB[b], *P = PB[b];
-            const bf16_t *Y = YB[b] + 16 * wave + col;
-            const float *sc = SC[b];
-            // S^T operand (rows j, k = d), shared by XS and Qh S
-            bf16x8 sb[DK / 32];
+    // iteration c: chain waves advance the state through chunk c, output
+    // waves write the outputs of chunk c - 1, loaders stage chunk c + 1 (its
+    // rows are in the register set (c + 1) % 2) and refill that set with
+    // chunk c + 3
+    auto iteration = [&](int c, Regs &R) {
+        if (chain && c < nch) {
+            const int b2 = c & 1, b3 = c % 3;
+            const bf16_t *X = XB[b2], *Tp = TPB[b2];
+            const bf16_t *Y = YT[b2] + (16 * ct + col) * PC;
+            const float *sc = SC[b3];
+            const bf16_t *st_w = STw[ct][b3];
+            bf16_t *rt_w = RTw[ct];
+            bf16_t *ut_w = UTw[ct][b2];
+            bf16x8 sb[DK / 32];   // S^T operand (rows j, k = d)
 #pragma unroll
             for (int kk = 0; kk < DK / 32; ++kk) sb[kk] = ld8(st_w + col * PK + 32 * kk + k8);
-            // XS and (Qh S)^T; R0 = Y - Gamma_{t-1} XS
-            f32x4 qs[4];
+            // R0 = Y - Gamma_{t-1} XS (token tile m)
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 f32x4 xs = {0.f, 0.f, 0.f, 0.f};
-                qs[m] = xs;
                 const int row = 16 * m + col;
 #pragma unroll
-                for (int kk = 0; kk < DK / 32; ++kk) {
-                    xs = mfma(ld8(X + row * PK + 32 * kk + k8), sb[kk], xs);
-                    qs[m] = mfma(sb[kk], ld8(Q + row * PK + 32 * kk + k8), qs[m]);
-                }
+                for (int kk = 0; kk < DK / 32; ++kk) xs = mfma(ld8(X + row * PK + 32 * kk + k8), sb[kk], xs);
+                const uint2 yy = *reinterpret_cast<const uint2 *>(Y + 16 * m + g4);   // 4 tokens
+                const float y[4] = {__uint_as_float(yy.x << 16), __uint_as_float(yy.x & 0xffff0000u),
+                                    __uint_as_float(yy.y << 16), __uint_as_float(yy.y & 0xffff0000u)};
                 float r0[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * m + g4 + r;
-                    r0[r] = bf16_to_f32(Y[t * PY].bits) - sc[t] * xs[r];
-                }
+                for (int r = 0; r < 4; ++r) r0[r] = y[r] - sc[16 * m + g4 + r] * xs[r];
                 *reinterpret_cast<uint2 *>(rt_w + col * PC + 16 * m + g4) = pack4(r0[0], r0[1], r0[2], r0[3]);
             }
             wave_lds_sync();
@@ -504,38 +521,54 @@ __global__ __launch_bounds__((DS / 16 + 4) * 64) void f1_walk(F1SplitArgs a, int
                 }
             }
             wave_lds_sync();
+            // S = Gamma_C S + (diag(e^{b_C-b_t}) X)^T U  -> S^T copy of chunk c + 1
             const bf16x8 ub0 = ld8(ut_w + col * PC + k8), ub1 = ld8(ut_w + col * PC + 32 + k8);
-            // O^T = diag(Gamma_t) (Qh S)^T + U^T P^T, stored as rows t of 4 columns
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int t = 16 * m + col;
-                const float gt = sc[C + t];
-                f32x4 o = qs[m];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) o[r] *= gt;
-                o = mfma(ub0, ld8(P + t * PC + k8), o);
-                if (m >= 2) o = mfma(ub1, ld8(P + t * PC + 32 + k8), o);
-                const int tg = c * C + t;
-                if (tg < T)
-                    *reinterpret_cast<uint2 *>(og + size_t(tg) * DV + j0 + 16 * wave + g4) = pack4(o[0], o[1], o[2], o[3]);
-            }
-            // S = Gamma_C S + (diag(e^{b_C-b_t}) X)^T U
             const float gC = sc[3 * C];
-            const bf16_t *XW = XWT[b];
+            const bf16_t *XW = XWT[b2];
+            bf16_t *st_n = STw[ct][(c + 1) % 3];
 #pragma unroll
             for (int m = 0; m < DK / 16; ++m) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) S[m][r] *= gC;
                 S[m] = mfma(ld8(XW + (16 * m + col) * PC + k8), ub0, S[m]);
                 S[m] = mfma(ld8(XW + (16 * m + col) * PC + 32 + k8), ub1, S[m]);
-                *reinterpret_cast<uint2 *>(st_w + col * PK + 16 * m + g4) = pack4(S[m][0], S[m][1], S[m][2], S[m][3]);
+                *reinterpret_cast<uint2 *>(st_n + col * PK + 16 * m + g4) = pack4(S[m][0], S[m][1], S[m][2], S[m][3]);
             }
-            wave_lds_sync();
-        } else if (c + 1 < nch) {
-            stage(c + 1);
-            if (c + 2 < nch) prefetch(c + 2);
+        } else if (outw && c >= 1) {
+            // outputs of chunk k = c - 1: O^T = diag(Gamma_t) (Qh S_k)^T + U^T P^T
+            const int k = c - 1, b2 = k & 1, b3 = k % 3;
+            const bf16_t *Q = QB[b3], *P = PB[b3];
+            const float *sc = SC[b3];
+            const bf16_t *st_w = STw[ct][b3];
+            const bf16_t *ut_w = UTw[ct][b2];
+            bf16x8 sb[DK / 32];
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) sb[kk] = ld8(st_w + col * PK + 32 * kk + k8);
+            const bf16x8 ub0 = ld8(ut_w + col * PC + k8), ub1 = ld8(ut_w + col * PC + 32 + k8);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int t = 16 * m + col;
+                f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk) o = mfma(sb[kk], ld8(Q + t * PK + 32 * kk + k8), o);
+                const float gt = sc[C + t];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[r] *= gt;
+                o = mfma(ub0, ld8(P + t * PC + k8), o);
+                if (m >= 2) o = mfma(ub1, ld8(P + t * PC + 32 + k8), o);
+                const int tg = k * C + t;
+                if (tg < T)
+                    *reinterpret_cast<uint2 *>(og + size_t(tg) * DV + j0 + 16 * ct + g4) = pack4(o[0], o[1], o[2], o[3]);
+            }
+        } else if (loader && c + 1 < nch) {
+            stage(c + 1, R);
+            if (c + 3 < nch) prefetch(c + 3, R);
         }
         __syncthreads();
+    };
+    for (int c = 0; c <= nch; c += 2) {   // unrolled by two: register sets by name
+        iteration(c, rb);
+        if (c + 1 <= nch) iteration(c + 1, ra);
     }
 
     // ---- boundary state ----
@@ -544,9 +577,9 @@ __global__ __launch_bounds__((DS / 16 + 4) * 64) void f1_walk(F1SplitArgs a, int
         for (int m = 0; m < DK / 16; ++m)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                a.S_out[(size_t(bh) * DK + 16 * m + g4 + r) * DV + j0 + 16 * wave + col] = S[m][r];
+                a.S_out[(size_t(bh) * DK + 16 * m + g4 + r) * DV + j0 + 16 * ct + col] = S[m][r];
     }
-    if (wave == NCW && s == 0 && a.xnext_out && T > 0) {
+    if (wave == 2 * NCW && s == 0 && a.xnext_out && T > 0) {
         const float xv = bf16_to_f32(kg[size_t(T - 1) * DK + lane].bits);
         const float sc = phi_scale(wave_sum(xv * xv), DK, a.eps_rms, a.phi);
         a.xnext_out[size_t(bh) * DK + lane] = xv * sc;
@@ -555,9 +588,10 @@ __global__ __launch_bounds__((DS / 16 + 4) * 64) void f1_walk(F1SplitArgs a, int
 
 template <int DS>
 void launch_walk(const F1SplitArgs &a, hipStream_t s, Marks *m) {
+    constexpr int NLW = 8;   // loader waves
     const int nslice = a.dv / DS;
     const int blocks = nslice == 1 ? a.BH : ((a.BH + 7) / 8) * 8 * nslice;
-    f1_walk<64, DS><<<blocks, (DS / 16 + 4) * 64, 0, s>>>(a, nslice);
+    f1_walk<64, DS, NLW><<<blocks, (2 * (DS / 16) + NLW) * 64, 0, s>>>(a, nslice);
     m->mark(s);
 }
 
@@ -566,8 +600,8 @@ void launch_walk(const F1SplitArgs &a, hipStream_t s, Marks *m) {
 void launch_chunk_f1_split(const F1SplitArgs &a, int ds, hipStream_t s, Marks *m) {
     f1_ops<64><<<dim3(a.nchunks, a.BH), 256, 0, s>>>(a);
     m->mark(s);
-    if (ds == 64) launch_walk<64>(a, s, m);
-    else launch_walk<32>(a, s, m);
+    (void)ds;   // always 32 value columns per walk workgroup
+    launch_walk<32>(a, s, m);
 }
 
 }  // namespace falcon

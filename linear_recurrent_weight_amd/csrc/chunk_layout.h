@@ -76,14 +76,9 @@ inline bool chunk_f1_use_fused() {
     const char *e = std::getenv("FALCON_F1_PATH");
     return e && e[0] == 'f';
 }
-inline int chunk_f1_split_slice(int dv) {
-    if (dv == 32) return 32;
-    if (const char *e = std::getenv("FALCON_F1_SLICE")) {   // tuning override: 32 or 64
-        const int v = std::atoi(e);
-        if (v == 32 || v == 64) return v;
-    }
-    return 32;   // two chain waves per workgroup, twice the workgroups
-}
+// the walk kernel of the two-kernel path takes 32 value columns per
+// workgroup (its chain, output and loader waves fill the LDS at that width)
+constexpr int chunk_f1_split_slice(int /*dv*/) { return 32; }
 
 // Falcon-1A / Falcon-3A chunk path: d_k in {32, 64}, d_v in {16, 32, 64}.
 constexpr bool chunk_a_supported(int dk, int dv) {
