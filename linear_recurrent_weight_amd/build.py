@@ -69,6 +69,7 @@ KERNEL_SOURCES = {"passthrough": "feature.hip", "feature": "feature.hip", "recur
                   "chunk_f1_fused": "chunk_f1_fused.hip", "chunk_f2": "chunk_f2.hip",
                   "f3_prep": "chunk_f3.hip", "f3_scan": "chunk_f3.hip",
                   "f1_ops": "chunk_f1_split.hip", "f1_walk": "chunk_f1_split.hip",
+                  "f1_xfer": "chunk_f1_xfer.hip", "f1_carry": "chunk_f1_xfer.hip",
                   "a_segment": "chunk_a.hip", "a_segscan": "chunk_a.hip", "a_output": "chunk_a.hip"}
 
 

@@ -70,11 +70,38 @@ constexpr size_t kF1SplitChunkBytes = kF1SplitScalOff + 4 * size_t(kChunk) * 4;
 constexpr bool chunk_f1_split_supported(bool bf16, int dk, int dv) {
     return bf16 && dk == 64 && (dv == 32 || dv == 64 || dv == 128);
 }
-// which bf16 d_k = 64 Falcon-1 kernel: the two-kernel path unless
-// FALCON_F1_PATH=fused (tuning and test switch)
-inline bool chunk_f1_use_fused() {
+// Transfer-operator bf16 Falcon-1 path (d_k = 64): per chunk, bf16
+//   A   [64 d'][64 d] = -(diag(e^{b_C-b_t}) X)^T W        (state transfer, less e^{b_C} I)
+//   G   [64 t][64 d]  = diag(e^{b_t}) Qh - P W             (outputs from the entry state)
+//   B^T [d_v j][64 d] = ((diag(e^{b_C-b_t}) X)^T Ut)^T      (state write)
+//   H   [64 t][d_v j] = P Ut                               (outputs from the chunk's writes)
+// with W = Tp diag(e^{b_{t-1}}) X and Ut = Tp Y; then fp32 e^{b_C} in a
+// 256-byte block.
+constexpr bool chunk_f1_xfer_supported(bool bf16, int dk, int dv) {
+    return bf16 && dk == 64 && (dv == 32 || dv == 64 || dv == 128);
+}
+constexpr size_t kF1XferGOff = 8192;
+constexpr size_t kF1XferBOff = 16384;
+constexpr size_t f1_xfer_h_off(int dv) { return 16384 + size_t(dv) * 128; }
+constexpr size_t f1_xfer_scal_off(int dv) { return 16384 + size_t(dv) * 256; }
+constexpr size_t f1_xfer_bytes(int dv) { return f1_xfer_scal_off(dv) + 256; }
+// value columns per workgroup of the carry kernel: 64 (32 when d_v = 32, or
+// with FALCON_F1_SLICE=32, a tuning override)
+inline int f1_xfer_slice(int dv) {
+    if (dv == 32) return 32;
+    if (const char *e = std::getenv("FALCON_F1_SLICE"))
+        if (std::atoi(e) == 32) return 32;
+    return 64;
+}
+
+// which bf16 d_k = 64 Falcon-1 kernels: the transfer-operator path, unless
+// FALCON_F1_PATH names another ("fused" or "split"; tuning and test switch)
+enum class F1Kind { kXfer, kSplit, kFused };
+inline F1Kind chunk_f1_kind() {
     const char *e = std::getenv("FALCON_F1_PATH");
-    return e && e[0] == 'f';
+    if (e && e[0] == 'f') return F1Kind::kFused;
+    if (e && e[0] == 's') return F1Kind::kSplit;
+    return F1Kind::kXfer;
 }
 // the walk kernel of the two-kernel path takes 32 value columns per
 // workgroup (its chain, output and loader waves fill the LDS at that width)

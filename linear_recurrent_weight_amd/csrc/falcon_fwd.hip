@@ -15,6 +15,7 @@ const char *const kNamesChunkA[] = {"a_segment", "a_segscan", "a_output"};
 const char *const kNamesChunkF2[] = {"chunk_f2"};
 const char *const kNamesChunkF3[] = {"feature", "f3_prep", "f3_scan"};
 const char *const kNamesChunkF1Split[] = {"f1_ops", "f1_walk"};
+const char *const kNamesChunkF1Xfer[] = {"f1_xfer", "f1_carry"};
 
 int run(const falcon_fwd_args *args, void *stream, Marks *m) {
     Plan p;
@@ -107,7 +108,7 @@ int run(const falcon_fwd_args *args, void *stream, Marks *m) {
         fa.xnext_out = p.xnext_out;
         fa.o = p.o;
         launch_chunk_f2(fa, p.dtype == FALCON_BF16, s, m);
-    } else if (p.path == Path::kChunkF1Split) {
+    } else if (p.path == Path::kChunkF1Split || p.path == Path::kChunkF1Xfer) {
         F1SplitArgs fa{};
         fa.BH = p.BH;
         fa.T = p.T;
@@ -130,7 +131,8 @@ int run(const falcon_fwd_args *args, void *stream, Marks *m) {
         fa.xnext_out = p.xnext_out;
         fa.o = p.o;
         fa.ops = p.ws_at<void>(p.off_chunk);
-        launch_chunk_f1_split(fa, p.slice, s, m);
+        if (p.path == Path::kChunkF1Xfer) launch_chunk_f1_xfer(fa, s, m);
+        else launch_chunk_f1_split(fa, p.slice, s, m);
     } else if (p.path == Path::kChunkF1Fused) {
         F1FusedArgs fa{};
         fa.BH = p.BH;
@@ -285,6 +287,7 @@ extern "C" const char *falcon_kernel_name(const falcon_fwd_args *args, int i) {
         case Path::kChunkF2: return i < 1 ? kNamesChunkF2[i] : nullptr;
         case Path::kChunkF3: return i < 3 ? kNamesChunkF3[i] : nullptr;
         case Path::kChunkF1Split: return i < 2 ? kNamesChunkF1Split[i] : nullptr;
+        case Path::kChunkF1Xfer: return i < 2 ? kNamesChunkF1Xfer[i] : nullptr;
         default: return nullptr;
     }
 }

@@ -131,5 +131,7 @@ void launch_chunk_a(const ChunkAArgs &a, bool bf16, hipStream_t s, Marks *m);
 void launch_chunk_f2(const ChunkF2Args &a, bool bf16, hipStream_t s, Marks *m);
 void launch_chunk_f3(const ChunkF3Args &a, bool bf16, hipStream_t s, Marks *m);
 void launch_chunk_f1_split(const F1SplitArgs &a, int ds, hipStream_t s, Marks *m);
+// same arguments; `ops` holds f1_xfer_bytes(dv) per chunk
+void launch_chunk_f1_xfer(const F1SplitArgs &a, hipStream_t s, Marks *m);
 
 }  // namespace falcon

@@ -73,8 +73,13 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
     if (a->chunk == 0) {
         p->path = Path::kRecurrent;
     } else if (a->chunk == kChunk) {
-        if (var == FALCON_V1 && chunk_f1_split_supported(a->dtype == FALCON_BF16, a->dk, a->dv) &&
-            !chunk_f1_use_fused()) {
+        const F1Kind f1 = chunk_f1_kind();
+        if (var == FALCON_V1 && chunk_f1_xfer_supported(a->dtype == FALCON_BF16, a->dk, a->dv) &&
+            f1 == F1Kind::kXfer) {
+            p->path = Path::kChunkF1Xfer;
+            p->slice = f1_xfer_slice(a->dv);
+        } else if (var == FALCON_V1 && chunk_f1_split_supported(a->dtype == FALCON_BF16, a->dk, a->dv) &&
+                   f1 == F1Kind::kSplit) {
             p->path = Path::kChunkF1Split;
             p->slice = chunk_f1_split_slice(a->dv);
         } else if (var == FALCON_V1 && chunk_f1_fused_supported(a->dtype == FALCON_BF16, a->dk, a->dv)) {
@@ -122,6 +127,10 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
         p->nchunks = (T + kChunk - 1) / kChunk;
         p->off_chunk = off;
         off = align_up(off + static_cast<size_t>(bh) * p->nchunks * kF1SplitChunkBytes);
+    } else if (p->path == Path::kChunkF1Xfer) {
+        p->nchunks = (T + kChunk - 1) / kChunk;
+        p->off_chunk = off;
+        off = align_up(off + static_cast<size_t>(bh) * p->nchunks * f1_xfer_bytes(a->dv));
     } else if (p->path == Path::kChunkA) {
         p->nchunks = (T + kChunk - 1) / kChunk;
         p->Tpad = p->nchunks * kChunk;

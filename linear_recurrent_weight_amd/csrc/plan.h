@@ -19,6 +19,7 @@ enum class Path : int {
     kChunkF1Fused = 5,  // chunk-parallel Falcon-1, bf16, one fused kernel
     kChunkF3 = 6,    // chunk-parallel Falcon-3 (stacked window rows)
     kChunkF1Split = 7,  // chunk-parallel Falcon-1, bf16: per-chunk operators, then the walk
+    kChunkF1Xfer = 8,   // chunk-parallel Falcon-1, bf16: per-chunk transfer operators, then the carry
 };
 
 struct Plan {

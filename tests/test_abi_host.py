@@ -210,6 +210,17 @@ def test_chunk_path_coverage(lib):
         assert validate(lib, with_ws(lib, args(variant=var, window=w, chunk=0, dk=16, dv=16))) == fb.OK
 
 
+def test_f1_bf16_workspace_per_path(lib, monkeypatch):
+    """bf16 Falcon-1 at d_k = 64: the transfer-operator path (default) keeps
+    A, G, B^T and H in bf16 plus one 256-byte scalar block per chunk; the
+    operators + walk pair keeps Tp, P, Xw and four decay rows."""
+    for dv in (32, 64, 128):
+        per_chunk = 2 * 64 * 64 * 2 + 2 * 64 * dv * 2 + 256
+        assert wsize(lib, args(seqlen=1000, dv=dv)) == 6 * 16 * per_chunk
+    monkeypatch.setenv("FALCON_F1_PATH", "split")
+    assert wsize(lib, args(seqlen=1000)) == 6 * 16 * (3 * 64 * 64 * 2 + 4 * 64 * 4)
+
+
 def test_fused_f1_needs_no_workspace(lib, monkeypatch):
     monkeypatch.setenv("FALCON_F1_PATH", "fused")
     assert wsize(lib, args(seqlen=1024)) == 0

@@ -219,7 +219,7 @@ def test_deterministic():
 
 # -- bf16 Falcon-1 kernels for d_k = 64: fused, and operators + walk ------------
 
-F1_PATHS = ["fused", "split"]
+F1_PATHS = ["fused", "split", "xfer"]
 
 
 @pytest.mark.parametrize("path", F1_PATHS)
@@ -262,18 +262,31 @@ def test_chunk_f1_bf16_continuation(monkeypatch, path, split):
                           rtol=1e-5, atol=1e-5)
 
 
-def test_chunk_f1_bf16_kernels_agree(monkeypatch):
-    """The fused kernel and the operators + walk pair compute the same
-    algebra; on c2-shaped input they agree to bf16 rounding."""
+@pytest.mark.parametrize("other", ["split", "xfer"])
+def test_chunk_f1_bf16_kernels_agree(monkeypatch, other):
+    """The fused kernel, the operators + walk pair and the transfer-operator
+    pair compute the same algebra; on c2-shaped input they agree to bf16
+    rounding."""
     w = WORKLOADS["c2"].with_(batch=1, heads=4)
     inp = gu.make(w)
     dev = gu.to_device(inp, w)
     monkeypatch.setenv("FALCON_F1_PATH", "fused")
     o_f, st_f = gu.run_gpu(w, dev)
-    monkeypatch.setenv("FALCON_F1_PATH", "split")
+    monkeypatch.setenv("FALCON_F1_PATH", other)
     o_s, st_s = gu.run_gpu(w, dev)
     assert gu.max_rel_err(o_s.double().cpu().numpy(), o_f.double().cpu().numpy()) <= 2e-2
     assert gu.max_rel_err(st_s.S.double().cpu().numpy(), st_f.S.double().cpu().numpy()) <= 2e-2
+
+
+@pytest.mark.parametrize("eps_gamma", [1e-3, 1e-2])
+def test_chunk_f1_bf16_strong_decay(monkeypatch, eps_gamma):
+    """Large ridge weights (eta lambda close to beta): a chunk decays by about
+    2^-100, so some chunks take the separable decays and others form them
+    pairwise."""
+    monkeypatch.setenv("FALCON_F1_PATH", "xfer")
+    w = gu.small("F1", "bf16", B=1, H=3, T=200, dk=64, dv=64, chunk=64, seed=29).with_(
+        lam_lo=500.0, lam_hi=2000.0, eps_gamma=eps_gamma)
+    check(w)
 
 
 # -- Falcon-1A / Falcon-3A chunk path -------------------------------------------
