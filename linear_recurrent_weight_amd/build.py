@@ -19,9 +19,11 @@ LIB = PKG / "libfalcon.so"
 ARCH = os.environ.get("FALCON_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-# packed fp32 instructions are kept out of every code object
+# packed fp32 instructions are kept out of every code object; MFMA results
+# stay in VGPRs (no copies out of accumulation registers)
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "--amdgpu-mfma-vgpr-form",
           f"-I{ROOT / 'include'}", "-Wall", "-Wno-unused-function"]
 
 

@@ -12,11 +12,14 @@
 //     B =  Xw^T Ut [d_k x d_v],   H = P Ut                    [C x d_v],
 // so that  S_C = e^{b_C} S_0 + A S_0 + B  and  O = G S_0 + H.
 //
-// f1_xfer: one workgroup per chunk, all chunks of all heads in parallel:
+// f1_xfer: one chunk per workgroup at a time, all chunks of all heads in
+//   parallel (persistent workgroups; the next chunk's rows load meanwhile):
 //   QK-RMSNorm and the key shift, eta and log2 gamma, the prefix scan, Gram
-//   and scores on MFMA, the fp32 inverse of the unit-lower system, then
-//   Z = Tp [-diag(e^{b_{i-1}}) X | Y] and the four operator products on MFMA;
-//   A, G, B^T and H go to the workspace in bf16 with e^{b_C}.
+//   and scores on MFMA, then Z = (I + N)^{-1} [-diag(eta e^{b_{i-1}}) X |
+//   diag(eta) Y] = [-W | Ut] by forward substitution over 16-row blocks
+//   (diagonal blocks inverted in fp32, the block steps on bf16 MFMA, kept in
+//   registers), and the four operator products on MFMA; A, G, B^T and H go
+//   to the workspace in bf16 with e^{b_C}.
 // f1_carry: one workgroup per (head, slice of value columns) walks the
 //   chunks: per chunk each compute wave owns 16 state columns (fp32 MFMA
 //   accumulators) and issues 8 MFMAs for the carry and 8 for the outputs,
@@ -34,7 +37,6 @@ namespace {
 constexpr int C = kChunk;
 constexpr int DK = 64;
 constexpr int PK = 72;          // bf16 pitch of LDS rows of 64 elements (144 bytes)
-constexpr int kLs = C + 1;      // fp32 pitch of the system
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -51,9 +53,6 @@ __device__ __forceinline__ f32x4 unpk4(const uint2 &u) { return f32x4{lo16(u.x),
 __device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4 &c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 template <class P>
 __device__ __forceinline__ bf16x8 ld8(const P *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -69,63 +68,107 @@ __device__ __forceinline__ void lds_copy4(const void *src, void *dst) {
     __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
 }
 
+// phi's RMS scale 1 / sqrt(mean(z^2) + eps_rms) (0 when that is 0) from the
+// sum of squares over d_k = 64 elements, by the hardware reciprocal square
+// root: the features are rounded to bf16 next
+__device__ __forceinline__ float rms_scale(float ss, float eps_rms, int phi_kind) {
+    if (phi_kind == FALCON_PHI_IDENTITY) return 1.f;
+    const float ms = ss * (1.f / DK) + eps_rms;
+    return ms > 0.f ? __builtin_amdgcn_rsqf(ms) : 0.f;
+}
+
 // per-token scalars of a chunk in LDS
-enum { kEta = 0, kB, kBp, kEw, kRs, kQs, kCs, kGp, kLg, kNsv };
+enum { kEta = 0, kB, kBp, kEw, kRs, kQs, kCs, kLg, kNsv };
 
 // ---------------------------------------------------------------------------
 // f1_xfer: the transfer operators of one chunk
 // ---------------------------------------------------------------------------
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16(const s16x4 &a, const s16x4 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ s16x4 as_s4(const uint2 &u) { return __builtin_bit_cast(s16x4, u); }
+
+constexpr int NBP = 20;         // bf16 pitch of the 16 x 16 solve blocks
+
+// The raw rows of one chunk (16 q and 16 k elements and d_v / 4 values of
+// row `row`, part `part`, and the row's beta and lambda), loaded into
+// registers one chunk ahead.  Loads are unconditional from rows clamped into
+// [0, T): a load under a branch would be waited for where the branch joins.
+template <int DV>
+struct XferRows {
+    uint4 q0, q1, k0, k1, v[DV / 32];
+    float beta, lam;
+    __device__ __forceinline__ void load(const F1SplitArgs &a, int id, int row, int part) {
+        const int c = id / a.BH, bh = id % a.BH, T = a.T, t = c * kChunk + row;
+        const int tq = t < T ? t : T - 1;
+        const int tk = t < 1 ? 0 : (t - 1 < T ? t - 1 : T - 1);
+        const uint4 *qp = reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.q) +
+                                                          (size_t(bh) * T + tq) * DK + 16 * part);
+        const uint4 *kp = reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.k) +
+                                                          (size_t(bh) * T + tk) * DK + 16 * part);
+        const uint4 *vp = reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.v) +
+                                                          (size_t(bh) * T + tq) * DV + (DV / 4) * part);
+        q0 = qp[0];
+        q1 = qp[1];
+        k0 = kp[0];
+        k1 = kp[1];
+#pragma unroll
+        for (int i = 0; i < DV / 32; ++i) v[i] = vp[i];
+        beta = a.beta[size_t(bh) * T + tq];
+        lam = a.lambda[size_t(bh) * T + tq];
+    }
+};
+
 template <int DV>
 __global__ __launch_bounds__(256) void f1_xfer(F1SplitArgs a) {
     constexpr int VPT = DV / 4;               // value elements per thread (row part)
     constexpr int NJ = DV / 16;               // value column tiles
-    constexpr int ZR = DV > DK ? DV : DK;     // rows of one half of Z^T
-    constexpr int RB = 2 * ZR * PK * 2 > C * kLs * 4 ? 2 * ZR * PK * 2 : C * kLs * 4;
+    constexpr int NT = 4 + NJ;                // column tiles of R = [x part | value part]
+    constexpr int U1 = (DK + DV) * PK > C * PK ? (DK + DV) * PK : C * PK;
     __shared__ __align__(16) bf16_t QB[C * PK];     // qh rows [t][d]
     __shared__ __align__(16) bf16_t XT[DK * PK];    // x^T [d][t]
+    __shared__ __align__(16) bf16_t XW[DK * PK];    // (diag(e^{b_C-b_t}) x)^T [d][t]
     __shared__ __align__(16) bf16_t YT[DV * PK];    // values^T [j][t]
     __shared__ __align__(16) bf16_t PB[C * PK];     // P [t][s]
-    __shared__ __align__(16) unsigned char regA[2 * C * PK * 2];   // x rows | inverse scratch | Tp, Tq
-    __shared__ __align__(16) unsigned char regB[RB];               // system and its inverse | Z^T halves
+    __shared__ __align__(16) bf16_t U1B[U1];        // x rows [t][d], then Z^T [n][t]
+    __shared__ __align__(16) bf16_t NB[6][16 * NBP];   // -N below the diagonal blocks
+    __shared__ __align__(16) bf16_t DB[4][16 * NBP];   // inverses of the diagonal blocks of I + N
+    __shared__ float Nd[4][16 * 17];                   // diagonal blocks of N (fp32)
     __shared__ __align__(16) float sv[kNsv][C];
 
-    const int nch = a.nchunks;
-    const int c = blockIdx.x / a.BH, bh = blockIdx.x % a.BH;   // chunk-major: a head stays on one XCD
+    const int nch = a.nchunks, total = nch * a.BH;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, g4 = 4 * (lane >> 4), k8 = 8 * (lane >> 4), kq = lane >> 4;
     const int T = a.T;
     const int row = tid >> 2, part = tid & 3;
-    const int t = c * C + row;
-    const bf16_t *qg = static_cast<const bf16_t *>(a.q) + size_t(bh) * T * DK;
-    const bf16_t *kg = static_cast<const bf16_t *>(a.k) + size_t(bh) * T * DK;
-    const bf16_t *vg = static_cast<const bf16_t *>(a.v) + size_t(bh) * T * DV;
-    char *rec = static_cast<char *>(a.ops) + (size_t(bh) * nch + c) * f1_xfer_bytes(DV);
-
-    bf16_t *XB = reinterpret_cast<bf16_t *>(regA);
-    float *Mw = reinterpret_cast<float *>(regA);      // 4 x 16 x 17 (inverse levels)
-    bf16_t *Tp = reinterpret_cast<bf16_t *>(regA);    // Tp [t][s]
-    bf16_t *Tq = Tp + C * PK;                         // -Tp diag(e^{b_{s-1}}) [t][s]
-    float *Nm = reinterpret_cast<float *>(regB);      // N, inverted in place
-    bf16_t *ZT = reinterpret_cast<bf16_t *>(regB);    // Z^T [n][t] (one half)
-    bf16_t *ZS = ZT + ZR * PK;                        // Z^T diag(e^{b_C - b_t})
+    bf16_t *XB = U1B;
+    bf16_t *ZT = U1B;
     uint16_t *XT16 = reinterpret_cast<uint16_t *>(XT);
     uint16_t *YT16 = reinterpret_cast<uint16_t *>(YT);
 
+    // persistent: chunk ids blockIdx.x, + gridDim.x, ...; the rows of the
+    // next chunk are loaded while this one is worked on
+    XferRows<DV> rows;
+    rows.load(a, blockIdx.x, row, part);
+    for (int id = blockIdx.x; id < total; id += gridDim.x) {
+    const int c = id / a.BH, bh = id % a.BH;   // chunk-major: with 8 | BH a head stays on one XCD
+    const int t = c * C + row;
+    char *rec = static_cast<char *>(a.ops) + (size_t(bh) * nch + c) * f1_xfer_bytes(DV);
+
     // 1. rows: qh, x = phi(k_{t-1}) (x_0 from the boundary), values; eta and
-    //    log2 gamma.  Loads are unconditional from clamped rows; rows past the
-    //    end are zeroed here.
+    //    log2 gamma.  Rows past the end are zeroed here.
     {
-        const int tq = t < T ? t : T - 1;
-        const int tk = t < 1 ? 0 : (t - 1 < T ? t - 1 : T - 1);
-        const uint4 *qp = reinterpret_cast<const uint4 *>(qg + size_t(tq) * DK + 16 * part);
-        const uint4 *kp = reinterpret_cast<const uint4 *>(kg + size_t(tk) * DK + 16 * part);
-        const uint4 *vp = reinterpret_cast<const uint4 *>(vg + size_t(tq) * DV + VPT * part);
-        const uint4 qr0 = qp[0], qr1 = qp[1], kr0 = kp[0], kr1 = kp[1];
+        const uint4 qr0 = rows.q0, qr1 = rows.q1, kr0 = rows.k0, kr1 = rows.k1;
         uint4 vr[VPT / 8];
 #pragma unroll
-        for (int i = 0; i < VPT / 8; ++i) vr[i] = vp[i];
-        const float beta = a.beta[size_t(bh) * T + tq], lam = a.lambda[size_t(bh) * T + tq];
+        for (int i = 0; i < VPT / 8; ++i) vr[i] = rows.v[i];
+        const float beta = rows.beta, lam = rows.lam;
+        {   // the next chunk's rows (the last chunk reloads its own)
+            const int nid = id + int(gridDim.x);
+            rows.load(a, nid < total ? nid : id, row, part);
+        }
         // zero the tiles of P above the diagonal that k-steps of 32 read: (0,1), (2,3)
         if (tid < 64) {
             const int tile = tid >> 5, rr = (tid >> 1) & 15, h = tid & 1;
@@ -137,12 +180,13 @@ __global__ __launch_bounds__(256) void f1_xfer(F1SplitArgs a) {
         float qv[16], xv[16];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            qv[2 * e] = qok ? lo16(qw[e]) : 0.f;
-            qv[2 * e + 1] = qok ? hi16(qw[e]) : 0.f;
-            xv[2 * e] = kok ? lo16(kw[e]) : 0.f;
-            xv[2 * e + 1] = kok ? hi16(kw[e]) : 0.f;
+            qv[2 * e] = lo16(qw[e]);
+            qv[2 * e + 1] = hi16(qw[e]);
+            xv[2 * e] = lo16(kw[e]);
+            xv[2 * e + 1] = hi16(kw[e]);
         }
-        if (first && a.xnext_in) {   // x_0 continues the previous segment (features already formed)
+        const bool carry_x = first && a.xnext_in;
+        if (carry_x) {   // x_0 continues the previous segment (features already formed)
 #pragma unroll
             for (int e = 0; e < 16; ++e) xv[e] = a.xnext_in[size_t(bh) * DK + 16 * part + e];
         }
@@ -154,8 +198,9 @@ __global__ __launch_bounds__(256) void f1_xfer(F1SplitArgs a) {
         }
         sq = group_sum<4>(sq);
         sk = group_sum<4>(sk);
-        const float scq = phi_scale(sq, DK, a.eps_rms, a.phi);
-        const float sck = first ? 1.f : phi_scale(sk, DK, a.eps_rms, a.phi);
+        // rows outside the sequence (clamped loads) get a zero scale
+        const float scq = qok ? rms_scale(sq, a.eps_rms, a.phi) : 0.f;
+        const float sck = carry_x ? 1.f : (kok ? rms_scale(sk, a.eps_rms, a.phi) : 0.f);
         float n2 = 0.f;
         uint32_t xo[8], qo[8];
 #pragma unroll
@@ -190,7 +235,8 @@ __global__ __launch_bounds__(256) void f1_xfer(F1SplitArgs a) {
         if (part == 0) {
             float eta = 0.f, alpha = 0.f;
             if (!(t >= T || (first && a.fresh))) {   // the fresh first step writes nothing
-                eta = step_eta(beta, n2 + lam + a.eps);
+                const float den = n2 + lam + a.eps;
+                eta = den != 0.f ? beta * __builtin_amdgcn_rcpf(den) : 0.f;
                 alpha = step_alpha(eta, lam, a.eps_gamma);
             }
             sv[kEta][row] = eta;
@@ -217,20 +263,13 @@ __global__ __launch_bounds__(256) void f1_xfer(F1SplitArgs a) {
         sv[kRs][lane] = eta * gp;
         sv[kQs][lane] = ex2(b);
         sv[kCs][lane] = sep ? ex2(-b) : 0.f;
-        sv[kGp][lane] = gp;
         if (wave == 0 && lane == 0) *reinterpret_cast<float *>(rec + f1_xfer_scal_off(DV)) = ex2(bC);
     }
     wave_lds_sync();
 
-    // 3. Gram (-> N, fp32) and score (-> P, bf16) tiles below the diagonal;
-    //    wave w takes jobs w, w + 4, ..: 0-9 Gram, 10-19 scores, tile index
-    //    -> (I, J) from two packed 2-bit tables
-#pragma unroll
-    for (int m = 0; m < 5; ++m) {
-        const int job = wave + 4 * m;
-        const bool isG = job < 10;
-        const int tt = isG ? job : job - 10;
-        const int I = (0xffa94 >> (2 * tt)) & 3, J = (0xe4910 >> (2 * tt)) & 3;
+    // decayed Gram (isG: eta_i e^{b_{i-1}-b_j} x_i.x_j) or score (e^{b_i-b_j} qh_i.x_j)
+    // tile (I, J): rows i = 16 I + g4 + r, column j = 16 J + col
+    auto tile = [&](bool isG, int I, int J) {
         const bf16_t *ar = (isG ? XB : QB) + (16 * I + col) * PK + k8;
         const bf16_t *br = XB + (16 * J + col) * PK + k8;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -250,140 +289,104 @@ __global__ __launch_bounds__(256) void f1_xfer(F1SplitArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = acc[r] * ex2(bi[r] - bj) * (isG ? ei[r] : 1.f);
         }
-        if (isG) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Nm[(i0 + r) * kLs + j] = (I != J || j < i0 + r) ? v[r] : 0.f;
-        } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                reinterpret_cast<uint16_t *>(PB)[(i0 + r) * PK + j] = bf((I != J || j <= i0 + r) ? v[r] : 0.f);
-        }
-    }
-    __syncthreads();
+        return v;
+    };
 
-    // 4. (I + N)^{-1} in place: diagonal 16-blocks by forward substitution
-    //    (wave J: block J, lane k < 16: column k); off-diagonal blocks by
-    //    recursive doubling on the 2 x 2 split into 32-blocks,
-    //    [[A, 0], [C, D]]^{-1} = [[A^-1, 0], [-D^-1 C A^-1, D^-1]], on fp32 MFMA.
-    {
+    // 3. wave 0: diagonal Gram blocks, then the inverses of the diagonal
+    //    blocks of I + N by forward substitution (lane = 16 J + column);
+    //    waves 1-3: the Gram blocks below them (-> -N, bf16), the score tiles
+    //    (-> P) and the decayed keys (diag(e^{b_C-b_t}) x)^T.
+    if (wave == 0) {
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            const f32x4 v = tile(true, I, I);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Nd[I][(g4 + r) * 17 + col] = col < g4 + r ? v[r] : 0.f;
+        }
+        wave_lds_sync();
+        const int J = lane >> 4;
+        const float *nd = Nd[J];
         float tcol[16];
-        const int base = 16 * wave;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float v = (r == col) ? 1.f : 0.f;
 #pragma unroll
-            for (int k = 0; k < r; ++k) v -= Nm[(base + r) * kLs + base + k] * tcol[k];
+            for (int k = 0; k < r; ++k) v -= nd[r * 17 + k] * tcol[k];
             tcol[r] = v;
         }
-        __syncthreads();   // every diagonal block has been read
-        if (lane < 16) {
+        uint16_t *db = reinterpret_cast<uint16_t *>(DB[J]);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) Nm[(base + r) * kLs + base + col] = tcol[r];
-        }
-    }
-    __syncthreads();
-    {
-        auto blk = [&](const float *A, const float *B, f32x4 acc) {   // acc += A B (16 x 16 blocks)
+        for (int r = 0; r < 16; ++r) db[r * NBP + col] = bf(tcol[r]);
+    } else {
+        const int w1 = wave - 1;
+        for (int job = w1; job < 16; job += 3) {
+            if (job < 6) {   // Gram blocks (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+                const int I = (0xFE9 >> (2 * job)) & 3, J = (0x910 >> (2 * job)) & 3;
+                const f32x4 v = tile(true, I, J);
+                uint16_t *nb = reinterpret_cast<uint16_t *>(NB[job]);
 #pragma unroll
-            for (int k0 = 0; k0 < 16; k0 += 4) acc = mfma_f32(A[col * kLs + k0 + kq], B[(k0 + kq) * kLs + col], acc);
-            return acc;
-        };
-        auto at = [&](int I, int J) { return Nm + 16 * I * kLs + 16 * J; };
-        float *mw = Mw + wave * 272;
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        if (wave < 2) {   // T_{a+1,a} = -T_{a+1,a+1} N_{a+1,a} T_{a,a}, a = 0, 2
-            const int a0 = 2 * wave;
-            const f32x4 M = blk(at(a0 + 1, a0), at(a0, a0), z);
+                for (int r = 0; r < 4; ++r) nb[(g4 + r) * NBP + col] = bf(-v[r]);
+            } else {         // score tiles on and below the diagonal
+                const int tt = job - 6;
+                const int I = (0xffa94 >> (2 * tt)) & 3, J = (0xe4910 >> (2 * tt)) & 3;
+                const f32x4 v = tile(false, I, J);
+                const int j = 16 * J + col, i0 = 16 * I + g4;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) mw[(g4 + r) * 17 + col] = M[r];
-            wave_lds_sync();
-            f32x4 Tb = z;
-#pragma unroll
-            for (int k0 = 0; k0 < 16; k0 += 4)
-                Tb = mfma_f32(at(a0 + 1, a0 + 1)[col * kLs + k0 + kq], mw[(k0 + kq) * 17 + col], Tb);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) at(a0 + 1, a0)[(g4 + r) * kLs + col] = -Tb[r];
-        }
-        __syncthreads();
-        {   // X(I, J) = N_I0 T_0J + N_I1 T_1J for I in {2, 3}, J in {0, 1}
-            const int I = 2 + (wave >> 1), J = wave & 1;
-            f32x4 X = blk(at(I, 1), at(1, J), z);
-            if (J == 0) X = blk(at(I, 0), at(0, 0), X);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) mw[(g4 + r) * 17 + col] = X[r];
-        }
-        __syncthreads();
-        {   // T(I, J) = -sum_{K=2}^{I} T_IK X(K, J)
-            const int I = 2 + (wave >> 1), J = wave & 1;
-            f32x4 Tb = z;
-#pragma unroll
-            for (int K = 2; K <= 3; ++K) {
-                if (K > I) break;
-                const float *Xk = Mw + (2 * (K - 2) + J) * 272;
-                const float *Tk = at(I, K);
-#pragma unroll
-                for (int k0 = 0; k0 < 16; k0 += 4) Tb = mfma_f32(Tk[col * kLs + k0 + kq], Xk[(k0 + kq) * 17 + col], Tb);
+                for (int r = 0; r < 4; ++r)
+                    reinterpret_cast<uint16_t *>(PB)[(i0 + r) * PK + j] = bf((I != J || j <= i0 + r) ? v[r] : 0.f);
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) at(I, J)[(g4 + r) * kLs + col] = -Tb[r];
+        }
+        for (int p = tid - 64; p < DK * 8; p += 192) {   // 16-byte pieces of XW
+            const int d = p >> 3, t8 = 8 * (p & 7);
+            const uint4 xx = *reinterpret_cast<const uint4 *>(XT + d * PK + t8);
+            const f32x4 e0 = *reinterpret_cast<const f32x4 *>(&sv[kEw][t8]);
+            const f32x4 e1 = *reinterpret_cast<const f32x4 *>(&sv[kEw][t8 + 4]);
+            *reinterpret_cast<uint4 *>(XW + d * PK + t8) =
+                make_uint4(pk2(lo16(xx.x) * e0[0], hi16(xx.x) * e0[1]), pk2(lo16(xx.y) * e0[2], hi16(xx.y) * e0[3]),
+                           pk2(lo16(xx.z) * e1[0], hi16(xx.z) * e1[1]), pk2(lo16(xx.w) * e1[2], hi16(xx.w) * e1[3]));
         }
     }
     __syncthreads();
 
-    // 5. Tp = L^{-1} diag(eta) and Tq = -Tp diag(e^{b_{s-1}}) in bf16 (row part)
-    {
-        uint32_t pw[8], qw[8];
-        const f32x4 *et = reinterpret_cast<const f32x4 *>(&sv[kEta][16 * part]);
-        const f32x4 *gp = reinterpret_cast<const f32x4 *>(&sv[kGp][16 * part]);
+    // 4. Z = (I + N)^{-1} R, R = [-diag(eta e^{b_{t-1}}) X | diag(eta) Y], by
+    //    forward substitution over 16-row blocks, one column tile per pass,
+    //    in registers: the accumulator layout of a 16 x 16 tile (lane
+    //    holds rows 4 (lane / 16) .. + 3 of column lane % 16) is the
+    //    B-operand layout of the 16x16x16 MFMA.  Z^T -> LDS (rows n).
+    //    Z[:, x part] = -W, Z[:, value part] = Ut.
+    for (int n = wave; n < NT; n += 4) {
+        const bool xp = n < 4;
+        const int nr = 16 * n + col;                   // row of Z^T
+        const bf16_t *src = xp ? XT + nr * PK : YT + (nr - DK) * PK;
+        s16x4 zb[4];
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            const f32x4 e4 = et[h], g = gp[h];
-            float tv[4];
+        for (int I = 0; I < 4; ++I) {
+            const f32x4 sc = *reinterpret_cast<const f32x4 *>(&sv[xp ? kRs : kEta][16 * I + g4]);
+            f32x4 acc = unpk4(*reinterpret_cast<const uint2 *>(src + 16 * I + g4)) * (xp ? -sc : sc);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int s = 16 * part + 4 * h + r;
-                tv[r] = s <= row ? Nm[row * kLs + s] * e4[r] : 0.f;
+            for (int J = 0; J < I; ++J) {
+                const int blk = (I * (I - 1)) / 2 + J;   // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+                acc = mfma16(as_s4(*reinterpret_cast<const uint2 *>(NB[blk] + col * NBP + 4 * kq)), zb[J], acc);
             }
-            pw[2 * h] = pk2(tv[0], tv[1]);
-            pw[2 * h + 1] = pk2(tv[2], tv[3]);
-            qw[2 * h] = pk2(-tv[0] * g[0], -tv[1] * g[1]);
-            qw[2 * h + 1] = pk2(-tv[2] * g[2], -tv[3] * g[3]);
+            const f32x4 z0 = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 z = mfma16(as_s4(*reinterpret_cast<const uint2 *>(DB[I] + col * NBP + 4 * kq)), as_s4(pk4(acc)), z0);
+            const uint2 zp = pk4(z);
+            zb[I] = as_s4(zp);
+            put2(ZT + nr * PK + 16 * I + g4, zp);
         }
-        uint4 *dp = reinterpret_cast<uint4 *>(Tp + row * PK + 16 * part);
-        uint4 *dq = reinterpret_cast<uint4 *>(Tq + row * PK + 16 * part);
-        dp[0] = make_uint4(pw[0], pw[1], pw[2], pw[3]);
-        dp[1] = make_uint4(pw[4], pw[5], pw[6], pw[7]);
-        dq[0] = make_uint4(qw[0], qw[1], qw[2], qw[3]);
-        dq[1] = make_uint4(qw[4], qw[5], qw[6], qw[7]);
     }
     __syncthreads();
 
-    // Z = Top R (Top lower triangular: token tile m needs k < 16 m + 16) for the
-    // column tile n of R^T; Z^T and Z^T diag(e^{b_C - b_t}) to LDS
-    auto zhalf = [&](const bf16_t *Top, const bf16_t *Rt, int n) {
-        const bf16x8 b0 = ld8(Rt + (16 * n + col) * PK + k8), b1 = ld8(Rt + (16 * n + col) * PK + 32 + k8);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mfma(ld8(Top + (16 * m + col) * PK + k8), b0, acc);
-            if (m >= 2) acc = mfma(ld8(Top + (16 * m + col) * PK + 32 + k8), b1, acc);
-            const f32x4 ew = *reinterpret_cast<const f32x4 *>(&sv[kEw][16 * m + g4]);
-            put2(ZT + (16 * n + col) * PK + 16 * m + g4, pk4(acc));
-            put2(ZS + (16 * n + col) * PK + 16 * m + g4, pk4(acc * ew));
-        }
-    };
-    // 6a. W half: Z_W = -W = Tq X
-    zhalf(Tq, XT, wave);
-    __syncthreads();
+    // 5. the operators (token-k products on MFMA), bf16 to the workspace
     {
-        const int m = wave;   // d tile (rows of A^T and G^T)
-        const bf16x8 s0 = ld8(ZS + (16 * m + col) * PK + k8), s1 = ld8(ZS + (16 * m + col) * PK + 32 + k8);
+        const int m = wave;
         const bf16x8 z0 = ld8(ZT + (16 * m + col) * PK + k8), z1 = ld8(ZT + (16 * m + col) * PK + 32 + k8);
+        const bf16x8 x0 = ld8(XW + (16 * m + col) * PK + k8), x1 = ld8(XW + (16 * m + col) * PK + 32 + k8);
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {   // A^T [d][d'] = (Z_W^T diag(e^{b_C-b_t})) X
+        for (int n = 0; n < 4; ++n) {   // A^T [d][d'] = Z_W^T diag(e^{b_C-b_t}) X
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mfma(s0, ld8(XT + (16 * n + col) * PK + k8), acc);
-            acc = mfma(s1, ld8(XT + (16 * n + col) * PK + 32 + k8), acc);
+            acc = mfma(z0, ld8(XW + (16 * n + col) * PK + k8), acc);
+            acc = mfma(z1, ld8(XW + (16 * n + col) * PK + 32 + k8), acc);
             put2(rec + ((16 * n + col) * DK + 16 * m + g4) * 2, pk4(acc));
         }
 #pragma unroll
@@ -394,32 +397,28 @@ __global__ __launch_bounds__(256) void f1_xfer(F1SplitArgs a) {
             if (n >= 2) acc = mfma(z1, ld8(PB + tt * PK + 32 + k8), acc);
             put2(rec + kF1XferGOff + (tt * DK + 16 * m + g4) * 2, pk4(acc));
         }
-    }
-    __syncthreads();
-    // 6b. value half: Z_U = Ut = Tp Y
-    for (int n = wave; n < NJ; n += 4) zhalf(Tp, YT, n);
-    __syncthreads();
-    {
-        const int m = wave;   // d' tile of B
-        const bf16x8 x0 = ld8(XT + (16 * m + col) * PK + k8), x1 = ld8(XT + (16 * m + col) * PK + 32 + k8);
 #pragma unroll
-        for (int n = 0; n < NJ; ++n) {   // B [d'][j] = X^T (diag(e^{b_C-b_t}) Ut), stored as B^T [j][d']
+        for (int n = 0; n < NJ; ++n) {   // B [d'][j] = (diag(e^{b_C-b_t}) X)^T Ut, stored as B^T [j][d']
+            const bf16_t *zu = ZT + (DK + 16 * n + col) * PK;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mfma(x0, ld8(ZS + (16 * n + col) * PK + k8), acc);
-            acc = mfma(x1, ld8(ZS + (16 * n + col) * PK + 32 + k8), acc);
+            acc = mfma(x0, ld8(zu + k8), acc);
+            acc = mfma(x1, ld8(zu + 32 + k8), acc);
             put2(rec + kF1XferBOff + ((16 * n + col) * DK + 16 * m + g4) * 2, pk4(acc));
         }
     }
     for (int m = wave; m < NJ; m += 4) {   // H^T [j][t] = Ut^T P^T, stored as H [t][j]
-        const bf16x8 z0 = ld8(ZT + (16 * m + col) * PK + k8), z1 = ld8(ZT + (16 * m + col) * PK + 32 + k8);
+        const bf16_t *zu = ZT + (DK + 16 * m + col) * PK;
+        const bf16x8 u0 = ld8(zu + k8), u1 = ld8(zu + 32 + k8);
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
             const int tt = 16 * n + col;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mfma(z0, ld8(PB + tt * PK + k8), acc);
-            if (n >= 2) acc = mfma(z1, ld8(PB + tt * PK + 32 + k8), acc);
+            acc = mfma(u0, ld8(PB + tt * PK + k8), acc);
+            if (n >= 2) acc = mfma(u1, ld8(PB + tt * PK + 32 + k8), acc);
             put2(rec + f1_xfer_h_off(DV) + (size_t(tt) * DV + 16 * m + g4) * 2, pk4(acc));
         }
+    }
+    __syncthreads();   // the next chunk overwrites the LDS buffers
     }
 }
 
@@ -596,9 +595,26 @@ __global__ __launch_bounds__((DS / 16 + 4) * 64) void f1_carry(F1SplitArgs a, in
     }
 }
 
+// compute units of the current device (read once per device)
+int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 template <int DV>
 void launch_xfer(const F1SplitArgs &a, hipStream_t s, Marks *m) {
-    f1_xfer<DV><<<a.nchunks * a.BH, 256, 0, s>>>(a);
+    // as many workgroups as fit at once (LDS: two per CU, one at d_v = 128),
+    // each walking chunk ids with the grid as stride
+    const int total = a.nchunks * a.BH;
+    const int slots = cu_count() * (DV == 128 ? 1 : 2);
+    f1_xfer<DV><<<total < slots ? total : slots, 256, 0, s>>>(a);
     m->mark(s);
 }
 
