@@ -21,9 +21,10 @@
 //   registers), and the four operator products on MFMA; A, G, B^T and H go
 //   to the workspace in bf16 with e^{b_C}.
 // f1_carry: one workgroup per (head, slice of value columns) walks the
-//   chunks: per chunk each compute wave owns 16 state columns (fp32 MFMA
-//   accumulators) and issues 8 MFMAs for the carry and 8 for the outputs,
-//   all from one bf16 copy of the entry state.  Loader waves copy the
+//   chunks: per chunk each compute wave owns 16 state columns x 32 rows
+//   (fp32 MFMA accumulators) and issues 4 MFMAs for the carry and 4 for the
+//   outputs of 32 tokens, all from one bf16 copy of the entry state
+//   (double-buffered in LDS).  Loader waves copy the
 //   operators of later chunks straight from memory into a ring of LDS slots
 //   (global_load_lds), so no register staging sits between memory and the
 //   matrix cores.  One workgroup barrier per chunk.
@@ -91,68 +92,100 @@ __device__ __forceinline__ s16x4 as_s4(const uint2 &u) { return __builtin_bit_ca
 
 constexpr int NBP = 20;         // bf16 pitch of the 16 x 16 solve blocks
 
-// The raw rows of one chunk (16 q and 16 k elements and d_v / 4 values of
-// row `row`, part `part`, and the row's beta and lambda), loaded into
-// registers one chunk ahead.  Loads are unconditional from rows clamped into
-// [0, T): a load under a branch would be waited for where the branch joins.
+// A B for 16 x 16 fp32 matrices in the accumulator layout (lane l holds rows
+// 4 (l / 16) .. + 3 of column l % 16): `at` holds A^T that way, `b` holds B.
+// Step s of the 16x16x4 MFMA takes k = 4 (l / 16) + s, so both operands
+// are the lane's own accumulator elements.
+__device__ __forceinline__ f32x4 mm16(const f32x4 &at, const f32x4 &b) {
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(at[s], b[s], c, 0, 0, 0);
+    return c;
+}
+constexpr int XW_THREADS = 512; // 8 waves per chunk
+
+// The raw rows of one chunk (8 q and 8 k elements and d_v / 8 values of row
+// `row`, part `part`, and the row's beta and lambda), loaded into registers
+// one chunk ahead.  Loads are unconditional from rows clamped into [0, T): a
+// load under a branch would be waited for where the branch joins.
 template <int DV>
 struct XferRows {
-    uint4 q0, q1, k0, k1, v[DV / 32];
+    static constexpr int VPT = DV / 8;                 // value elements per thread
+    static constexpr int NV = VPT >= 8 ? VPT / 8 : 1;  // 16-byte pieces (8 bytes at d_v = 32)
+    uint4 q, k, v[NV];
     float beta, lam;
     __device__ __forceinline__ void load(const F1SplitArgs &a, int id, int row, int part) {
         const int c = id / a.BH, bh = id % a.BH, T = a.T, t = c * kChunk + row;
         const int tq = t < T ? t : T - 1;
         const int tk = t < 1 ? 0 : (t - 1 < T ? t - 1 : T - 1);
-        const uint4 *qp = reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.q) +
-                                                          (size_t(bh) * T + tq) * DK + 16 * part);
-        const uint4 *kp = reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.k) +
-                                                          (size_t(bh) * T + tk) * DK + 16 * part);
-        const uint4 *vp = reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.v) +
-                                                          (size_t(bh) * T + tq) * DV + (DV / 4) * part);
-        q0 = qp[0];
-        q1 = qp[1];
-        k0 = kp[0];
-        k1 = kp[1];
+        q = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.q) + (size_t(bh) * T + tq) * DK + 8 * part);
+        k = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.k) + (size_t(bh) * T + tk) * DK + 8 * part);
+        const bf16_t *vp = static_cast<const bf16_t *>(a.v) + (size_t(bh) * T + tq) * DV + VPT * part;
+        if constexpr (VPT >= 8) {
 #pragma unroll
-        for (int i = 0; i < DV / 32; ++i) v[i] = vp[i];
+            for (int i = 0; i < NV; ++i) v[i] = reinterpret_cast<const uint4 *>(vp)[i];
+        } else {
+            const uint2 h = *reinterpret_cast<const uint2 *>(vp);
+            v[0] = make_uint4(h.x, h.y, 0u, 0u);
+        }
         beta = a.beta[size_t(bh) * T + tq];
         lam = a.lambda[size_t(bh) * T + tq];
     }
 };
 
 template <int DV>
-__global__ __launch_bounds__(256) void f1_xfer(F1SplitArgs a) {
-    constexpr int VPT = DV / 4;               // value elements per thread (row part)
+__global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1SplitArgs a) {
+    using Rows = XferRows<DV>;
+    constexpr int VPT = Rows::VPT;
+    constexpr int YP = DV + 8;                // bf16 pitch of the value rows
     constexpr int NJ = DV / 16;               // value column tiles
     constexpr int NT = 4 + NJ;                // column tiles of R = [x part | value part]
     constexpr int U1 = (DK + DV) * PK > C * PK ? (DK + DV) * PK : C * PK;
     __shared__ __align__(16) bf16_t QB[C * PK];     // qh rows [t][d]
     __shared__ __align__(16) bf16_t XT[DK * PK];    // x^T [d][t]
     __shared__ __align__(16) bf16_t XW[DK * PK];    // (diag(e^{b_C-b_t}) x)^T [d][t]
-    __shared__ __align__(16) bf16_t YT[DV * PK];    // values^T [j][t]
+    __shared__ __align__(16) bf16_t YB[C * YP];     // value rows [t][j]
     __shared__ __align__(16) bf16_t PB[C * PK];     // P [t][s]
     __shared__ __align__(16) bf16_t U1B[U1];        // x rows [t][d], then Z^T [n][t]
     __shared__ __align__(16) bf16_t NB[6][16 * NBP];   // -N below the diagonal blocks
     __shared__ __align__(16) bf16_t DB[4][16 * NBP];   // inverses of the diagonal blocks of I + N
-    __shared__ float Nd[4][16 * 17];                   // diagonal blocks of N (fp32)
     __shared__ __align__(16) float sv[kNsv][C];
+    __shared__ __align__(16) bf16x8 IDT[2][64];        // column pickers (see below), per lane
 
     const int nch = a.nchunks, total = nch * a.BH;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int col = lane & 15, g4 = 4 * (lane >> 4), k8 = 8 * (lane >> 4), kq = lane >> 4;
     const int T = a.T;
-    const int row = tid >> 2, part = tid & 3;
     bf16_t *XB = U1B;
     bf16_t *ZT = U1B;
-    uint16_t *XT16 = reinterpret_cast<uint16_t *>(XT);
-    uint16_t *YT16 = reinterpret_cast<uint16_t *>(YT);
+    {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int col = lane & 15, k8 = 8 * (lane >> 4);
+    // B operands that pick 16 columns (half h) of a 32-wide A block: the MFMA
+    // then hands back the block transposed into the accumulator layout (lane
+    // holds 4 consecutive rows of one column).  Kept in LDS, not registers.
+    if (tid < 128) {
+        typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+        const int h = tid >> 6;
+        u16x8 u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) u[e] = (k8 + e == 16 * h + col) ? 0x3F80 : 0;   // bf16 1.0
+        IDT[h][lane] = __builtin_bit_cast(bf16x8, u);
+    }
+    }
 
     // persistent: chunk ids blockIdx.x, + gridDim.x, ...; the rows of the
     // next chunk are loaded while this one is worked on
-    XferRows<DV> rows;
-    rows.load(a, blockIdx.x, row, part);
+    Rows rows;
+    rows.load(a, blockIdx.x, threadIdx.x >> 3, threadIdx.x & 7);
     for (int id = blockIdx.x; id < total; id += gridDim.x) {
+    // lane quantities are formed afresh in every pass (an opaque copy of the
+    // thread index), so that the compiler does not keep dozens of derived
+    // addresses live across the loop
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, g4 = 4 * (lane >> 4), k8 = 8 * (lane >> 4), kq = lane >> 4;
+    const int row = tid >> 3, part = tid & 7;
     const int c = id / a.BH, bh = id % a.BH;   // chunk-major: with 8 | BH a head stays on one XCD
     const int t = c * C + row;
     char *rec = static_cast<char *>(a.ops) + (size_t(bh) * nch + c) * f1_xfer_bytes(DV);
@@ -160,10 +193,10 @@ __global__ __launch_bounds__(256) void f1_xfer(F1SplitArgs a) {
     // 1. rows: qh, x = phi(k_{t-1}) (x_0 from the boundary), values; eta and
     //    log2 gamma.  Rows past the end are zeroed here.
     {
-        const uint4 qr0 = rows.q0, qr1 = rows.q1, kr0 = rows.k0, kr1 = rows.k1;
-        uint4 vr[VPT / 8];
+        const uint4 qr = rows.q, kr = rows.k;
+        uint4 vr[Rows::NV];
 #pragma unroll
-        for (int i = 0; i < VPT / 8; ++i) vr[i] = rows.v[i];
+        for (int i = 0; i < Rows::NV; ++i) vr[i] = rows.v[i];
         const float beta = rows.beta, lam = rows.lam;
         {   // the next chunk's rows (the last chunk reloads its own)
             const int nid = id + int(gridDim.x);
@@ -175,11 +208,11 @@ __global__ __launch_bounds__(256) void f1_xfer(F1SplitArgs a) {
             *reinterpret_cast<uint4 *>(PB + (32 * tile + rr) * PK + 32 * tile + 16 + 8 * h) = make_uint4(0, 0, 0, 0);
         }
         const bool qok = t < T, kok = t >= 1 && t <= T, first = t == 0;
-        const uint32_t qw[8] = {qr0.x, qr0.y, qr0.z, qr0.w, qr1.x, qr1.y, qr1.z, qr1.w};
-        const uint32_t kw[8] = {kr0.x, kr0.y, kr0.z, kr0.w, kr1.x, kr1.y, kr1.z, kr1.w};
-        float qv[16], xv[16];
+        const uint32_t qw[4] = {qr.x, qr.y, qr.z, qr.w};
+        const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w};
+        float qv[8], xv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 4; ++e) {
             qv[2 * e] = lo16(qw[e]);
             qv[2 * e + 1] = hi16(qw[e]);
             xv[2 * e] = lo16(kw[e]);
@@ -188,49 +221,37 @@ __global__ __launch_bounds__(256) void f1_xfer(F1SplitArgs a) {
         const bool carry_x = first && a.xnext_in;
         if (carry_x) {   // x_0 continues the previous segment (features already formed)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) xv[e] = a.xnext_in[size_t(bh) * DK + 16 * part + e];
+            for (int e = 0; e < 8; ++e) xv[e] = a.xnext_in[size_t(bh) * DK + 8 * part + e];
         }
         float sq = 0.f, sk = 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
+        for (int e = 0; e < 8; ++e) {
             sq += qv[e] * qv[e];
             sk += xv[e] * xv[e];
         }
-        sq = group_sum<4>(sq);
-        sk = group_sum<4>(sk);
+        sq = group_sum<8>(sq);
+        sk = group_sum<8>(sk);
         // rows outside the sequence (clamped loads) get a zero scale
         const float scq = qok ? rms_scale(sq, a.eps_rms, a.phi) : 0.f;
         const float sck = carry_x ? 1.f : (kok ? rms_scale(sk, a.eps_rms, a.phi) : 0.f);
         float n2 = 0.f;
-        uint32_t xo[8], qo[8];
+        uint32_t xo[4], qo[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 4; ++e) {
             const float x0 = xv[2 * e] * sck, x1 = xv[2 * e + 1] * sck;
             n2 += x0 * x0 + x1 * x1;
             xo[e] = pk2(x0, x1);
             qo[e] = pk2(qv[2 * e] * scq, qv[2 * e + 1] * scq);
         }
-        n2 = group_sum<4>(n2);
-        uint4 *xr = reinterpret_cast<uint4 *>(XB + row * PK + 16 * part);
-        uint4 *qrw = reinterpret_cast<uint4 *>(QB + row * PK + 16 * part);
-        xr[0] = make_uint4(xo[0], xo[1], xo[2], xo[3]);
-        xr[1] = make_uint4(xo[4], xo[5], xo[6], xo[7]);
-        qrw[0] = make_uint4(qo[0], qo[1], qo[2], qo[3]);
-        qrw[1] = make_uint4(qo[4], qo[5], qo[6], qo[7]);
+        n2 = group_sum<8>(n2);
+        *reinterpret_cast<uint4 *>(XB + row * PK + 8 * part) = make_uint4(xo[0], xo[1], xo[2], xo[3]);
+        *reinterpret_cast<uint4 *>(QB + row * PK + 8 * part) = make_uint4(qo[0], qo[1], qo[2], qo[3]);
+        if constexpr (VPT >= 8) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            XT16[(16 * part + 2 * e) * PK + row] = uint16_t(xo[e]);
-            XT16[(16 * part + 2 * e + 1) * PK + row] = uint16_t(xo[e] >> 16);
-        }
-#pragma unroll
-        for (int i = 0; i < VPT / 8; ++i) {
-            const uint32_t vw[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t w = qok ? vw[e] : 0u;
-                YT16[(VPT * part + 8 * i + 2 * e) * PK + row] = uint16_t(w);
-                YT16[(VPT * part + 8 * i + 2 * e + 1) * PK + row] = uint16_t(w >> 16);
-            }
+            for (int i = 0; i < Rows::NV; ++i)
+                *reinterpret_cast<uint4 *>(YB + row * YP + VPT * part + 8 * i) = qok ? vr[i] : make_uint4(0, 0, 0, 0);
+        } else {
+            *reinterpret_cast<uint2 *>(YB + row * YP + VPT * part) = qok ? make_uint2(vr[0].x, vr[0].y) : make_uint2(0, 0);
         }
         if (part == 0) {
             float eta = 0.f, alpha = 0.f;
@@ -256,11 +277,10 @@ __global__ __launch_bounds__(256) void f1_xfer(F1SplitArgs a) {
         const float bC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b), 63));
         sep = bC >= -100.f;
         const float eta = sv[kEta][lane];
-        const float gp = ex2(bp);
         sv[kB][lane] = b;
         sv[kBp][lane] = bp;
         sv[kEw][lane] = ex2(bC - b);
-        sv[kRs][lane] = eta * gp;
+        sv[kRs][lane] = eta * ex2(bp);
         sv[kQs][lane] = ex2(b);
         sv[kCs][lane] = sep ? ex2(-b) : 0.f;
         if (wave == 0 && lane == 0) *reinterpret_cast<float *>(rec + f1_xfer_scal_off(DV)) = ex2(bC);
@@ -291,35 +311,68 @@ __global__ __launch_bounds__(256) void f1_xfer(F1SplitArgs a) {
         }
         return v;
     };
+    // x^T and (diag(e^{b_C-b_t}) x)^T, tile (token block m, feature block n)
+    auto transpose_x = [&](int m, int n) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma(ld8(XB + (16 * m + col) * PK + 32 * (n >> 1) + k8), IDT[n & 1][lane], acc);
+        const f32x4 ew = *reinterpret_cast<const f32x4 *>(&sv[kEw][16 * m + g4]);
+        put2(XT + (16 * n + col) * PK + 16 * m + g4, pk4(acc));
+        put2(XW + (16 * n + col) * PK + 16 * m + g4, pk4(acc * ew));
+    };
 
-    // 3. wave 0: diagonal Gram blocks, then the inverses of the diagonal
-    //    blocks of I + N by forward substitution (lane = 16 J + column);
-    //    waves 1-3: the Gram blocks below them (-> -N, bf16), the score tiles
-    //    (-> P) and the decayed keys (diag(e^{b_C-b_t}) x)^T.
-    if (wave == 0) {
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            const f32x4 v = tile(true, I, I);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Nd[I][(g4 + r) * 17 + col] = col < g4 + r ? v[r] : 0.f;
+    // 3. waves 0-3: diagonal block J = wave of I + N, inverted in fp32 on
+    //    MFMA as (I - L)(I + L^2)(I + L^4)(I + L^8) (L strictly lower 16 x
+    //    16, so L^16 = 0 and the product is the finite Neumann series);
+    //    waves 4-7: the Gram blocks below them (-> -N, bf16) and the score
+    //    tiles (-> P); every wave: two transposes of x.
+    if (wave < 4) {
+        const int J = wave;
+        // the raw Gram block X_J X_J^T is symmetric: one tile gives L (row
+        // i, column j) and L^T (row j, column i) with their own scales
+        f32x4 g = {0.f, 0.f, 0.f, 0.f};
+        {
+            const bf16_t *xr = XB + (16 * J + col) * PK + k8;
+            g = mfma(ld8(xr), ld8(xr), g);
+            g = mfma(ld8(xr + 32), ld8(xr + 32), g);
         }
-        wave_lds_sync();
-        const int J = lane >> 4;
-        const float *nd = Nd[J];
-        float tcol[16];
+        const int jc = 16 * J + col, i0 = 16 * J + g4;
+        f32x4 L, Lt;
+        if (sep) {
+            const f32x4 rs = *reinterpret_cast<const f32x4 *>(&sv[kRs][i0]);
+            const f32x4 cs = *reinterpret_cast<const f32x4 *>(&sv[kCs][i0]);
+            const float rsj = sv[kRs][jc], csj = sv[kCs][jc];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float v = (r == col) ? 1.f : 0.f;
+            for (int r = 0; r < 4; ++r) {
+                L[r] = col < g4 + r ? g[r] * (rs[r] * csj) : 0.f;
+                Lt[r] = g4 + r < col ? g[r] * (rsj * cs[r]) : 0.f;
+            }
+        } else {
+            const f32x4 bp = *reinterpret_cast<const f32x4 *>(&sv[kBp][i0]);
+            const f32x4 bb = *reinterpret_cast<const f32x4 *>(&sv[kB][i0]);
+            const f32x4 et = *reinterpret_cast<const f32x4 *>(&sv[kEta][i0]);
+            const float bpj = sv[kBp][jc], bj = sv[kB][jc], etj = sv[kEta][jc];
 #pragma unroll
-            for (int k = 0; k < r; ++k) v -= nd[r * 17 + k] * tcol[k];
-            tcol[r] = v;
+            for (int r = 0; r < 4; ++r) {
+                L[r] = col < g4 + r ? g[r] * et[r] * ex2(bp[r] - bj) : 0.f;
+                Lt[r] = g4 + r < col ? g[r] * etj * ex2(bpj - bb[r]) : 0.f;
+            }
         }
+        auto plus_i = [&](f32x4 v, float d) {   // v + d I
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] += (g4 + r == col) ? d : 0.f;
+            return v;
+        };
+        const f32x4 L2 = mm16(Lt, L), L2t = mm16(L, Lt);
+        const f32x4 L4 = mm16(L2t, L2), L4t = mm16(L2, L2t);
+        const f32x4 L8 = mm16(L4t, L4);
+        const f32x4 Q1 = mm16(plus_i(L4t, 1.f), plus_i(L8, 1.f));     // (I + L^4)(I + L^8)
+        const f32x4 Q2 = mm16(plus_i(L2t, 1.f), Q1);                   // (I + L^2) Q1
+        const f32x4 Di = mm16(plus_i(-Lt, 1.f), Q2);                   // (I - L) Q2
         uint16_t *db = reinterpret_cast<uint16_t *>(DB[J]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) db[r * NBP + col] = bf(tcol[r]);
+        for (int r = 0; r < 4; ++r) db[(g4 + r) * NBP + col] = bf(Di[r]);
     } else {
-        const int w1 = wave - 1;
-        for (int job = w1; job < 16; job += 3) {
+        for (int job = wave - 4; job < 16; job += 4) {
             if (job < 6) {   // Gram blocks (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
                 const int I = (0xFE9 >> (2 * job)) & 3, J = (0x910 >> (2 * job)) & 3;
                 const f32x4 v = tile(true, I, J);
@@ -336,33 +389,38 @@ __global__ __launch_bounds__(256) void f1_xfer(F1SplitArgs a) {
                     reinterpret_cast<uint16_t *>(PB)[(i0 + r) * PK + j] = bf((I != J || j <= i0 + r) ? v[r] : 0.f);
             }
         }
-        for (int p = tid - 64; p < DK * 8; p += 192) {   // 16-byte pieces of XW
-            const int d = p >> 3, t8 = 8 * (p & 7);
-            const uint4 xx = *reinterpret_cast<const uint4 *>(XT + d * PK + t8);
-            const f32x4 e0 = *reinterpret_cast<const f32x4 *>(&sv[kEw][t8]);
-            const f32x4 e1 = *reinterpret_cast<const f32x4 *>(&sv[kEw][t8 + 4]);
-            *reinterpret_cast<uint4 *>(XW + d * PK + t8) =
-                make_uint4(pk2(lo16(xx.x) * e0[0], hi16(xx.x) * e0[1]), pk2(lo16(xx.y) * e0[2], hi16(xx.y) * e0[3]),
-                           pk2(lo16(xx.z) * e1[0], hi16(xx.z) * e1[1]), pk2(lo16(xx.w) * e1[2], hi16(xx.w) * e1[3]));
-        }
     }
+    transpose_x(wave >> 1, 2 * (wave & 1));
+    transpose_x(wave >> 1, 2 * (wave & 1) + 1);
     __syncthreads();
 
     // 4. Z = (I + N)^{-1} R, R = [-diag(eta e^{b_{t-1}}) X | diag(eta) Y], by
-    //    forward substitution over 16-row blocks, one column tile per pass,
-    //    in registers: the accumulator layout of a 16 x 16 tile (lane
-    //    holds rows 4 (lane / 16) .. + 3 of column lane % 16) is the
-    //    B-operand layout of the 16x16x16 MFMA.  Z^T -> LDS (rows n).
+    //    forward substitution over 16-row blocks, one column tile per wave,
+    //    in registers: the accumulator layout of a 16 x 16 tile (lane holds
+    //    rows 4 (lane / 16) .. + 3 of column lane % 16) is the B-operand
+    //    layout of the 16x16x16 MFMA.  Z^T -> LDS (rows n; this overwrites
+    //    the x rows, which every wave has finished reading).
     //    Z[:, x part] = -W, Z[:, value part] = Ut.
-    for (int n = wave; n < NT; n += 4) {
+    for (int n = wave; n < NT; n += 8) {
         const bool xp = n < 4;
         const int nr = 16 * n + col;                   // row of Z^T
-        const bf16_t *src = xp ? XT + nr * PK : YT + (nr - DK) * PK;
-        s16x4 zb[4];
+        f32x4 r0[4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             const f32x4 sc = *reinterpret_cast<const f32x4 *>(&sv[xp ? kRs : kEta][16 * I + g4]);
-            f32x4 acc = unpk4(*reinterpret_cast<const uint2 *>(src + 16 * I + g4)) * (xp ? -sc : sc);
+            if (xp) {
+                r0[I] = unpk4(*reinterpret_cast<const uint2 *>(XT + nr * PK + 16 * I + g4)) * -sc;
+            } else {   // value rows transposed by an MFMA with a column picker
+                const int jt = n - 4;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                acc = mfma(ld8(YB + (16 * I + col) * YP + 32 * (jt >> 1) + k8), IDT[jt & 1][lane], acc);
+                r0[I] = acc * sc;
+            }
+        }
+        s16x4 zb[4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            f32x4 acc = r0[I];
 #pragma unroll
             for (int J = 0; J < I; ++J) {
                 const int blk = (I * (I - 1)) / 2 + J;   // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
@@ -377,45 +435,51 @@ __global__ __launch_bounds__(256) void f1_xfer(F1SplitArgs a) {
     }
     __syncthreads();
 
-    // 5. the operators (token-k products on MFMA), bf16 to the workspace
+    // 5. the operators (token-k products on MFMA), bf16 to the workspace;
+    //    wave w: row tile m = w % 4 of A^T, G^T and B, column tiles of half w / 4
     {
-        const int m = wave;
+        const int m = wave & 3, hf = wave >> 2;
         const bf16x8 z0 = ld8(ZT + (16 * m + col) * PK + k8), z1 = ld8(ZT + (16 * m + col) * PK + 32 + k8);
         const bf16x8 x0 = ld8(XW + (16 * m + col) * PK + k8), x1 = ld8(XW + (16 * m + col) * PK + 32 + k8);
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {   // A^T [d][d'] = Z_W^T diag(e^{b_C-b_t}) X
+        for (int i = 0; i < 2; ++i) {   // A^T [d][d'] = Z_W^T diag(e^{b_C-b_t}) X
+            const int n = 2 * hf + i;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             acc = mfma(z0, ld8(XW + (16 * n + col) * PK + k8), acc);
             acc = mfma(z1, ld8(XW + (16 * n + col) * PK + 32 + k8), acc);
             put2(rec + ((16 * n + col) * DK + 16 * m + g4) * 2, pk4(acc));
         }
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {   // G^T [d][t] = diag-scaled Qh^T + Z_W^T P^T
-            const int tt = 16 * n + col;
+        for (int i = 0; i < 2; ++i) {   // G^T [d][t] = diag-scaled Qh^T + Z_W^T P^T
+            const int n = 2 * hf + i, tt = 16 * n + col;
             f32x4 acc = unpk4(*reinterpret_cast<const uint2 *>(QB + tt * PK + 16 * m + g4)) * sv[kQs][tt];
             acc = mfma(z0, ld8(PB + tt * PK + k8), acc);
-            if (n >= 2) acc = mfma(z1, ld8(PB + tt * PK + 32 + k8), acc);
+            if (hf) acc = mfma(z1, ld8(PB + tt * PK + 32 + k8), acc);   // token tiles 2, 3 reach k >= 32
             put2(rec + kF1XferGOff + (tt * DK + 16 * m + g4) * 2, pk4(acc));
         }
 #pragma unroll
-        for (int n = 0; n < NJ; ++n) {   // B [d'][j] = (diag(e^{b_C-b_t}) X)^T Ut, stored as B^T [j][d']
+        for (int i = 0; i < NJ / 2; ++i) {   // B [d'][j] = (diag(e^{b_C-b_t}) X)^T Ut, stored as B^T [j][d']
+            const int n = hf + 2 * i;
             const bf16_t *zu = ZT + (DK + 16 * n + col) * PK;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             acc = mfma(x0, ld8(zu + k8), acc);
             acc = mfma(x1, ld8(zu + 32 + k8), acc);
             put2(rec + kF1XferBOff + ((16 * n + col) * DK + 16 * m + g4) * 2, pk4(acc));
         }
-    }
-    for (int m = wave; m < NJ; m += 4) {   // H^T [j][t] = Ut^T P^T, stored as H [t][j]
-        const bf16_t *zu = ZT + (DK + 16 * m + col) * PK;
-        const bf16x8 u0 = ld8(zu + k8), u1 = ld8(zu + 32 + k8);
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const int tt = 16 * n + col;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mfma(u0, ld8(PB + tt * PK + k8), acc);
-            if (n >= 2) acc = mfma(u1, ld8(PB + tt * PK + 32 + k8), acc);
-            put2(rec + f1_xfer_h_off(DV) + (size_t(tt) * DV + 16 * m + g4) * 2, pk4(acc));
+        for (int ij = 0; ij < (NJ + 3) / 4; ++ij) {   // H^T [j][t] = Ut^T P^T, stored as H [t][j]
+            const int mj = m + 4 * ij;
+            if (mj >= NJ) break;
+            const bf16_t *zu = ZT + (DK + 16 * mj + col) * PK;
+            const bf16x8 u0 = ld8(zu + k8), u1 = ld8(zu + 32 + k8);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int n = 2 * hf + i, tt = 16 * n + col;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                acc = mfma(u0, ld8(PB + tt * PK + k8), acc);
+                if (hf) acc = mfma(u1, ld8(PB + tt * PK + 32 + k8), acc);
+                put2(rec + f1_xfer_h_off(DV) + (size_t(tt) * DV + 16 * mj + g4) * 2, pk4(acc));
+            }
         }
     }
     __syncthreads();   // the next chunk overwrites the LDS buffers
@@ -444,19 +508,22 @@ __device__ __forceinline__ void loader_barrier() {
 }
 
 template <int DS>
-__global__ __launch_bounds__((DS / 16 + 4) * 64) void f1_carry(F1SplitArgs a, int nslice) {
-    constexpr int NCW = DS / 16;                 // compute waves, 16 state columns each
+__global__ __launch_bounds__((DS / 8 + 4) * 64) void f1_carry(F1SplitArgs a, int nslice) {
+    constexpr int NCT = DS / 16;                 // column tiles of the slice
+    constexpr int NCW = 2 * NCT;                 // compute waves: column tile x half of the rows
     constexpr int NLW = 4;                       // loader waves
-    constexpr int NB = 4;                        // ring slots (chunks in flight)
     constexpr int kA = 0, kG = 8192, kB = 16384, kH = 16384 + 128 * DS, kS = 16384 + 256 * DS;
     constexpr int SB = kS + 256;                 // slot bytes
+    constexpr int NB = (150 * 1024 - 2 * NCT * 16 * PK * 2) / SB;   // ring slots: as many as fit
+    static_assert(NB >= 3, "ring depth");
     constexpr int NI = kS / 1024;                // 1 KB copies per chunk
     constexpr int IPW = NI / NLW;                // per loader wave (+ one scalar copy)
     constexpr int PPR = DS / 8;                  // 16-byte pieces per H row
+    constexpr int HSH = PPR == 8 ? 1 : (PPR == 4 ? 2 : 3);   // log2 of the H rows per 256 bytes
     static_assert(NI % NLW == 0, "whole copies per loader wave");
-    static_assert(2 * (IPW + 1) < 64, "vmcnt range");
+    static_assert((NB - 2) * (IPW + 1) < 64, "vmcnt range");
     __shared__ __align__(16) unsigned char ring[NB * SB];
-    __shared__ __align__(16) bf16_t STw[NCW][16 * PK];   // per compute wave: S^T [j][d] (bf16)
+    __shared__ __align__(16) bf16_t STw[2][NCT][16 * PK];   // bf16 S^T [j][d] per column tile, by chunk parity
 
     int bh, s;
     if (nslice == 1) {
@@ -478,23 +545,24 @@ __global__ __launch_bounds__((DS / 16 + 4) * 64) void f1_carry(F1SplitArgs a, in
     if (wave >= NCW) {
         // ---- loader waves: chunk cc's operators into slot cc % NB ----
         const int lw = wave - NCW;
-        // source offset of this lane's 16-byte piece in each copy; the LDS
-        // rows are stored with their 16-byte pieces permuted (piece q of row
-        // r at q ^ (r & 7)) so that the column reads of the compute waves
-        // spread over the banks
+        // source offset of this lane's 16-byte piece in each copy.  The LDS
+        // rows are stored with their 16-byte pieces permuted so that the
+        // 16-row column reads of the compute waves hit 16 different bank
+        // groups: rows of 128 bytes put piece q of row r at q ^ ((r / 2) % 8),
+        // rows of 64 bytes at q ^ ((r / 4) % 4), of 32 bytes at q ^ ((r / 8) % 2).
         int goff[IPW];
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
             const int off = 1024 * (lw + NLW * i) + 16 * lane;
             if (off < kB) {
                 const int base = off < kG ? 0 : kG, o = off - base, r = o >> 7, q = (o >> 4) & 7;
-                goff[i] = (base == 0 ? 0 : int(kF1XferGOff)) + r * 128 + 16 * (q ^ (r & 7));
+                goff[i] = (base == 0 ? 0 : int(kF1XferGOff)) + r * 128 + 16 * (q ^ ((r >> 1) & 7));
             } else if (off < kH) {
                 const int o = off - kB, r = o >> 7, q = (o >> 4) & 7;
-                goff[i] = int(kF1XferBOff) + (j0 + r) * 128 + 16 * (q ^ (r & 7));
+                goff[i] = int(kF1XferBOff) + (j0 + r) * 128 + 16 * (q ^ ((r >> 1) & 7));
             } else {
                 const int o = off - kH, r = o / (2 * DS), q = (o % (2 * DS)) >> 4;
-                goff[i] = int(f1_xfer_h_off(DV)) + r * 2 * DV + 2 * j0 + 16 * (q ^ (r & (PPR - 1)));
+                goff[i] = int(f1_xfer_h_off(DV)) + r * 2 * DV + 2 * j0 + 16 * (q ^ ((r >> HSH) & (PPR - 1)));
             }
         }
         const int soff = int(f1_xfer_scal_off(DV));
@@ -502,16 +570,19 @@ __global__ __launch_bounds__((DS / 16 + 4) * 64) void f1_carry(F1SplitArgs a, in
             const char *rec = recs + size_t(cc) * rb;
             unsigned char *slot = ring + (cc % NB) * SB;
 #pragma unroll
-            for (int i = 0; i < IPW; ++i)
-                lds_copy16(rec + goff[i], slot + 1024 * (lw + NLW * i));
+            for (int i = 0; i < IPW; ++i) lds_copy16(rec + goff[i], slot + 1024 * (lw + NLW * i));
             // e^{b_C}: every lane copies the same word (64 copies, one per lane)
             lds_copy4(rec + soff, slot + kS);
         };
         // wait until the chunk followed by `ahead` issued chunks has landed
+        // (ahead <= NB - 2)
         auto wait_chunk = [&](int ahead) {
             if (ahead <= 0) wait_vm<0>();
             else if (ahead == 1) wait_vm<IPW + 1>();
-            else wait_vm<2 * (IPW + 1)>();
+            else if (ahead == 2 || NB < 5) wait_vm<2 * (IPW + 1)>();
+            else if (ahead == 3 || NB < 6) wait_vm<(NB >= 5 ? 3 : 2) * (IPW + 1)>();
+            else if (ahead == 4 || NB < 7) wait_vm<(NB >= 6 ? 4 : 2) * (IPW + 1)>();
+            else wait_vm<(NB >= 7 ? 5 : 2) * (IPW + 1)>();
         };
         const int npro = nch < NB - 1 ? nch : NB - 1;
         for (int cc = 0; cc < npro; ++cc) issue(cc);
@@ -533,65 +604,63 @@ __global__ __launch_bounds__((DS / 16 + 4) * 64) void f1_carry(F1SplitArgs a, in
         return;
     }
 
-    // ---- compute wave ct: state columns j0 + 16 ct .. + 15 ----
-    const int ct = wave;
+    // ---- compute wave: state columns j0 + 16 ct .. + 15, rows 32 mh .. + 31
+    //      (row tiles m = 2 mh, 2 mh + 1), and the outputs of token tiles
+    //      2 mh, 2 mh + 1 for the same columns ----
+    const int ct = wave % NCT, mh = wave / NCT;
     const int col = lane & 15, g4 = 4 * (lane >> 4), k8 = 8 * (lane >> 4), kq = lane >> 4;
-    const int sw = col & 7;
+    const int sw = (col >> 1) & 7;               // piece permutation of rows 16 m + col (128-byte rows)
     // byte offsets inside a slot (row 16 m + col of A and G; pieces 4 kk + kq)
     const int ao0 = col * 128 + 16 * (kq ^ sw), ao1 = col * 128 + 16 * ((4 + kq) ^ sw);
     // B^T row 16 ct + col, d = 16 m + g4 (piece 2 m + g4 / 8, half g4 & 4)
     const int bo = (16 * ct + col) * 128 + ((g4 & 4) << 1);
+    const int bsw = ((16 * ct + col) >> 1) & 7;
     // H row 16 m + col, j = 16 ct + g4 (piece 2 ct + g4 / 8)
-    const int ho = col * (2 * DS) + 16 * ((2 * ct + (g4 >> 3)) ^ (col & (PPR - 1))) + ((g4 & 4) << 1);
-    bf16_t *stw = STw[ct];
+    const int ho = col * (2 * DS) + 16 * ((2 * ct + (g4 >> 3)) ^ ((col >> HSH) & (PPR - 1))) + ((g4 & 4) << 1);
     bf16_t *og = static_cast<bf16_t *>(a.o) + size_t(bh) * T * DV + j0 + 16 * ct + g4;
 
-    f32x4 S[DK / 16];
+    f32x4 S[2];
 #pragma unroll
-    for (int m = 0; m < DK / 16; ++m) {
+    for (int h = 0; h < 2; ++h) {
+        const int m = 2 * mh + h;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            S[m][r] = a.S_in ? a.S_in[(size_t(bh) * DK + 16 * m + g4 + r) * DV + j0 + 16 * ct + col] : 0.f;
-        put2(stw + col * PK + 16 * m + g4, pk4(S[m]));
+            S[h][r] = a.S_in ? a.S_in[(size_t(bh) * DK + 16 * m + g4 + r) * DV + j0 + 16 * ct + col] : 0.f;
+        put2(STw[0][ct] + col * PK + 16 * m + g4, pk4(S[h]));
     }
-    wave_lds_sync();
-    bf16x8 sb0 = ld8(stw + col * PK + k8), sb1 = ld8(stw + col * PK + 32 + k8);
     __syncthreads();
     for (int c = 0; c < nch; ++c) {
         const unsigned char *sl = ring + (c % NB) * SB;
+        const bf16_t *stw = STw[c & 1][ct];
+        const bf16x8 sb0 = ld8(stw + col * PK + k8), sb1 = ld8(stw + col * PK + 32 + k8);
         const float gC = *reinterpret_cast<const float *>(sl + kS);
-        f32x4 O[4];
+        bf16_t *stn = STw[(c + 1) & 1][ct];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            // carry: S' = e^{b_C} S + B + A S
-            const uint2 bq = *reinterpret_cast<const uint2 *>(sl + kB + bo + 16 * ((2 * m + (g4 >> 3)) ^ sw));
+        for (int h = 0; h < 2; ++h) {
+            const int m = 2 * mh + h;
+            // carry: S' = e^{b_C} S + B + A S  (row tile m)
+            const uint2 bq = *reinterpret_cast<const uint2 *>(sl + kB + bo + 16 * ((2 * m + (g4 >> 3)) ^ bsw));
             f32x4 sn = unpk4(bq);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sn[r] += gC * S[m][r];
+            for (int r = 0; r < 4; ++r) sn[r] += gC * S[h][r];
             sn = mfma(ld8(sl + kA + m * 2048 + ao0), sb0, sn);
-            S[m] = mfma(ld8(sl + kA + m * 2048 + ao1), sb1, sn);
+            S[h] = mfma(ld8(sl + kA + m * 2048 + ao1), sb1, sn);
+            put2(stn + col * PK + 16 * m + g4, pk4(S[h]));
             // outputs: O^T = S^T G^T + H^T (token tile m)
             f32x4 o = unpk4(*reinterpret_cast<const uint2 *>(sl + kH + m * 16 * (2 * DS) + ho));
             o = mfma(sb0, ld8(sl + kG + m * 2048 + ao0), o);
-            O[m] = mfma(sb1, ld8(sl + kG + m * 2048 + ao1), o);
-        }
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
+            o = mfma(sb1, ld8(sl + kG + m * 2048 + ao1), o);
             const int tg = c * C + 16 * m + col;
-            if (tg < T) put2(og + size_t(tg) * DV, pk4(O[m]));
-            put2(stw + col * PK + 16 * m + g4, pk4(S[m]));
+            if (tg < T) put2(og + size_t(tg) * DV, pk4(o));
         }
-        wave_lds_sync();
-        sb0 = ld8(stw + col * PK + k8);
-        sb1 = ld8(stw + col * PK + 32 + k8);
         __syncthreads();
     }
     if (a.S_out) {
 #pragma unroll
-        for (int m = 0; m < DK / 16; ++m)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                a.S_out[(size_t(bh) * DK + 16 * m + g4 + r) * DV + j0 + 16 * ct + col] = S[m][r];
+                a.S_out[(size_t(bh) * DK + 16 * (2 * mh + h) + g4 + r) * DV + j0 + 16 * ct + col] = S[h][r];
     }
 }
 
@@ -614,7 +683,7 @@ void launch_xfer(const F1SplitArgs &a, hipStream_t s, Marks *m) {
     // each walking chunk ids with the grid as stride
     const int total = a.nchunks * a.BH;
     const int slots = cu_count() * (DV == 128 ? 1 : 2);
-    f1_xfer<DV><<<total < slots ? total : slots, 256, 0, s>>>(a);
+    f1_xfer<DV><<<total < slots ? total : slots, XW_THREADS, 0, s>>>(a);
     m->mark(s);
 }
 
@@ -622,7 +691,7 @@ template <int DS>
 void launch_carry(const F1SplitArgs &a, hipStream_t s, Marks *m) {
     const int nslice = a.dv / DS;
     const int blocks = nslice == 1 ? a.BH : ((a.BH + 7) / 8) * 8 * nslice;
-    f1_carry<DS><<<blocks, (DS / 16 + 4) * 64, 0, s>>>(a, nslice);
+    f1_carry<DS><<<blocks, (DS / 8 + 4) * 64, 0, s>>>(a, nslice);
     m->mark(s);
 }
 
@@ -634,8 +703,11 @@ void launch_chunk_f1_xfer(const F1SplitArgs &a, hipStream_t s, Marks *m) {
         case 64: launch_xfer<64>(a, s, m); break;
         default: launch_xfer<128>(a, s, m); break;
     }
-    if (f1_xfer_slice(a.dv) == 32) launch_carry<32>(a, s, m);
-    else launch_carry<64>(a, s, m);
+    switch (f1_xfer_slice(a.dv)) {
+        case 16: launch_carry<16>(a, s, m); break;
+        case 32: launch_carry<32>(a, s, m); break;
+        default: launch_carry<64>(a, s, m); break;
+    }
 }
 
 }  // namespace falcon

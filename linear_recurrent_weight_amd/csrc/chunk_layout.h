@@ -85,13 +85,16 @@ constexpr size_t kF1XferBOff = 16384;
 constexpr size_t f1_xfer_h_off(int dv) { return 16384 + size_t(dv) * 128; }
 constexpr size_t f1_xfer_scal_off(int dv) { return 16384 + size_t(dv) * 256; }
 constexpr size_t f1_xfer_bytes(int dv) { return f1_xfer_scal_off(dv) + 256; }
-// value columns per workgroup of the carry kernel: 64 (32 when d_v = 32, or
-// with FALCON_F1_SLICE=32, a tuning override)
+// value columns per workgroup of the carry kernel: 32 (more workgroups share
+// the operator traffic), or 16 or 64 with FALCON_F1_SLICE (a tuning
+// override); never more than d_v
 inline int f1_xfer_slice(int dv) {
-    if (dv == 32) return 32;
-    if (const char *e = std::getenv("FALCON_F1_SLICE"))
-        if (std::atoi(e) == 32) return 32;
-    return 64;
+    int w = 32;
+    if (const char *e = std::getenv("FALCON_F1_SLICE")) {
+        const int v = std::atoi(e);
+        if (v == 16 || v == 32 || v == 64) w = v;
+    }
+    return w < dv ? w : dv;
 }
 
 // which bf16 d_k = 64 Falcon-1 kernels: the transfer-operator path, unless

@@ -223,7 +223,7 @@ F1_PATHS = ["fused", "split", "xfer"]
 
 
 @pytest.mark.parametrize("path", F1_PATHS)
-@pytest.mark.parametrize("slice_", ["32", "64"])
+@pytest.mark.parametrize("slice_", ["16", "32", "64"])
 @pytest.mark.parametrize("dv", [32, 64, 128])
 @pytest.mark.parametrize("T", [1, 64, 130, 300])
 def test_chunk_f1_bf16_shapes(monkeypatch, path, slice_, dv, T):
@@ -233,7 +233,7 @@ def test_chunk_f1_bf16_shapes(monkeypatch, path, slice_, dv, T):
 
 
 @pytest.mark.parametrize("path", F1_PATHS)
-@pytest.mark.parametrize("slice_", ["32", "64"])
+@pytest.mark.parametrize("slice_", ["16", "32", "64"])
 def test_c2_both_kernels_both_slice_widths(monkeypatch, path, slice_):
     monkeypatch.setenv("FALCON_F1_PATH", path)
     monkeypatch.setenv("FALCON_F1_SLICE", slice_)
