@@ -507,10 +507,17 @@ __device__ __forceinline__ void loader_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// row tiles of the state split over compute waves: each column tile has
+// RS waves (RS = 4 while the workgroup stays within 16 waves)
+template <int DS> constexpr int carry_rs() { return DS == 64 ? 2 : 4; }
+template <int DS> constexpr int carry_threads() { return (DS / 16 * carry_rs<DS>() + 4) * 64; }
+
 template <int DS>
-__global__ __launch_bounds__((DS / 8 + 4) * 64) void f1_carry(F1SplitArgs a, int nslice) {
+__global__ __launch_bounds__(carry_threads<DS>()) void f1_carry(F1SplitArgs a, int nslice) {
     constexpr int NCT = DS / 16;                 // column tiles of the slice
-    constexpr int NCW = 2 * NCT;                 // compute waves: column tile x half of the rows
+    constexpr int RS = carry_rs<DS>();           // row groups per column tile
+    constexpr int MT = 4 / RS;                   // row tiles (of 16) per compute wave
+    constexpr int NCW = RS * NCT;                // compute waves
     constexpr int NLW = 4;                       // loader waves
     constexpr int kA = 0, kG = 8192, kB = 16384, kH = 16384 + 128 * DS, kS = 16384 + 256 * DS;
     constexpr int SB = kS + 256;                 // slot bytes
@@ -604,9 +611,9 @@ __global__ __launch_bounds__((DS / 8 + 4) * 64) void f1_carry(F1SplitArgs a, int
         return;
     }
 
-    // ---- compute wave: state columns j0 + 16 ct .. + 15, rows 32 mh .. + 31
-    //      (row tiles m = 2 mh, 2 mh + 1), and the outputs of token tiles
-    //      2 mh, 2 mh + 1 for the same columns ----
+    // ---- compute wave: state columns j0 + 16 ct .. + 15, row tiles
+    //      m = MT mh .. MT mh + MT - 1, and the outputs of the same token
+    //      tiles for those columns ----
     const int ct = wave % NCT, mh = wave / NCT;
     const int col = lane & 15, g4 = 4 * (lane >> 4), k8 = 8 * (lane >> 4), kq = lane >> 4;
     const int sw = (col >> 1) & 7;               // piece permutation of rows 16 m + col (128-byte rows)
@@ -619,10 +626,10 @@ __global__ __launch_bounds__((DS / 8 + 4) * 64) void f1_carry(F1SplitArgs a, int
     const int ho = col * (2 * DS) + 16 * ((2 * ct + (g4 >> 3)) ^ ((col >> HSH) & (PPR - 1))) + ((g4 & 4) << 1);
     bf16_t *og = static_cast<bf16_t *>(a.o) + size_t(bh) * T * DV + j0 + 16 * ct + g4;
 
-    f32x4 S[2];
+    f32x4 S[MT];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int m = 2 * mh + h;
+    for (int h = 0; h < MT; ++h) {
+        const int m = MT * mh + h;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             S[h][r] = a.S_in ? a.S_in[(size_t(bh) * DK + 16 * m + g4 + r) * DV + j0 + 16 * ct + col] : 0.f;
@@ -632,24 +639,36 @@ __global__ __launch_bounds__((DS / 8 + 4) * 64) void f1_carry(F1SplitArgs a, int
     for (int c = 0; c < nch; ++c) {
         const unsigned char *sl = ring + (c % NB) * SB;
         const bf16_t *stw = STw[c & 1][ct];
+        // every LDS read of the step first, so that one latency covers them
         const bf16x8 sb0 = ld8(stw + col * PK + k8), sb1 = ld8(stw + col * PK + 32 + k8);
         const float gC = *reinterpret_cast<const float *>(sl + kS);
+        uint2 bq[MT], hq[MT];
+        bf16x8 a0[MT], a1[MT], q0[MT], q1[MT];
+#pragma unroll
+        for (int h = 0; h < MT; ++h) {
+            const int m = MT * mh + h;
+            bq[h] = *reinterpret_cast<const uint2 *>(sl + kB + bo + 16 * ((2 * m + (g4 >> 3)) ^ bsw));
+            hq[h] = *reinterpret_cast<const uint2 *>(sl + kH + m * 16 * (2 * DS) + ho);
+            a0[h] = ld8(sl + kA + m * 2048 + ao0);
+            a1[h] = ld8(sl + kA + m * 2048 + ao1);
+            q0[h] = ld8(sl + kG + m * 2048 + ao0);
+            q1[h] = ld8(sl + kG + m * 2048 + ao1);
+        }
         bf16_t *stn = STw[(c + 1) & 1][ct];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int m = 2 * mh + h;
-            // carry: S' = e^{b_C} S + B + A S  (row tile m)
-            const uint2 bq = *reinterpret_cast<const uint2 *>(sl + kB + bo + 16 * ((2 * m + (g4 >> 3)) ^ bsw));
-            f32x4 sn = unpk4(bq);
+        for (int h = 0; h < MT; ++h) {
+            const int m = MT * mh + h;
+            // carry: S' = e^{b_C} S + B + A S  (row tile m); the two k halves
+            // accumulate separately (two MFMA chains of one)
+            f32x4 sn = unpk4(bq[h]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) sn[r] += gC * S[h][r];
-            sn = mfma(ld8(sl + kA + m * 2048 + ao0), sb0, sn);
-            S[h] = mfma(ld8(sl + kA + m * 2048 + ao1), sb1, sn);
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            sn = mfma(a0[h], sb0, sn);
+            S[h] = sn + mfma(a1[h], sb1, z);
             put2(stn + col * PK + 16 * m + g4, pk4(S[h]));
             // outputs: O^T = S^T G^T + H^T (token tile m)
-            f32x4 o = unpk4(*reinterpret_cast<const uint2 *>(sl + kH + m * 16 * (2 * DS) + ho));
-            o = mfma(sb0, ld8(sl + kG + m * 2048 + ao0), o);
-            o = mfma(sb1, ld8(sl + kG + m * 2048 + ao1), o);
+            const f32x4 o = mfma(sb0, q0[h], unpk4(hq[h])) + mfma(sb1, q1[h], z);
             const int tg = c * C + 16 * m + col;
             if (tg < T) put2(og + size_t(tg) * DV, pk4(o));
         }
@@ -657,10 +676,10 @@ __global__ __launch_bounds__((DS / 8 + 4) * 64) void f1_carry(F1SplitArgs a, int
     }
     if (a.S_out) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < MT; ++h)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                a.S_out[(size_t(bh) * DK + 16 * (2 * mh + h) + g4 + r) * DV + j0 + 16 * ct + col] = S[h][r];
+                a.S_out[(size_t(bh) * DK + 16 * (MT * mh + h) + g4 + r) * DV + j0 + 16 * ct + col] = S[h][r];
     }
 }
 
@@ -691,7 +710,7 @@ template <int DS>
 void launch_carry(const F1SplitArgs &a, hipStream_t s, Marks *m) {
     const int nslice = a.dv / DS;
     const int blocks = nslice == 1 ? a.BH : ((a.BH + 7) / 8) * 8 * nslice;
-    f1_carry<DS><<<blocks, (DS / 8 + 4) * 64, 0, s>>>(a, nslice);
+    f1_carry<DS><<<blocks, carry_threads<DS>(), 0, s>>>(a, nslice);
     m->mark(s);
 }
 
