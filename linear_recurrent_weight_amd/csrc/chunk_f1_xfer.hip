@@ -140,13 +140,12 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
     constexpr int YP = DV + 8;                // bf16 pitch of the value rows
     constexpr int NJ = DV / 16;               // value column tiles
     constexpr int NT = 4 + NJ;                // column tiles of R = [x part | value part]
-    constexpr int U1 = (DK + DV) * PK > C * PK ? (DK + DV) * PK : C * PK;
     __shared__ __align__(16) bf16_t QB[C * PK];     // qh rows [t][d]
     __shared__ __align__(16) bf16_t XT[DK * PK];    // x^T [d][t]
     __shared__ __align__(16) bf16_t XW[DK * PK];    // (diag(e^{b_C-b_t}) x)^T [d][t]
     __shared__ __align__(16) bf16_t YB[C * YP];     // value rows [t][j]
     __shared__ __align__(16) bf16_t PB[C * PK];     // P [t][s]
-    __shared__ __align__(16) bf16_t U1B[U1];        // x rows [t][d], then Z^T [n][t]
+    __shared__ __align__(16) bf16_t XB[C * PK];     // x rows [t][d]
     __shared__ __align__(16) bf16_t NB[6][16 * NBP];   // -N below the diagonal blocks
     __shared__ __align__(16) bf16_t DB[4][16 * NBP];   // inverses of the diagonal blocks of I + N
     __shared__ __align__(16) float sv[kNsv][C];
@@ -154,8 +153,6 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
 
     const int nch = a.nchunks, total = nch * a.BH;
     const int T = a.T;
-    bf16_t *XB = U1B;
-    bf16_t *ZT = U1B;
     {
     const int tid = threadIdx.x, lane = tid & 63;
     const int col = lane & 15, k8 = 8 * (lane >> 4);
@@ -201,11 +198,6 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
         {   // the next chunk's rows (the last chunk reloads its own)
             const int nid = id + int(gridDim.x);
             rows.load(a, nid < total ? nid : id, row, part);
-        }
-        // zero the tiles of P above the diagonal that k-steps of 32 read: (0,1), (2,3)
-        if (tid < 64) {
-            const int tile = tid >> 5, rr = (tid >> 1) & 15, h = tid & 1;
-            *reinterpret_cast<uint4 *>(PB + (32 * tile + rr) * PK + 32 * tile + 16 + 8 * h) = make_uint4(0, 0, 0, 0);
         }
         const bool qok = t < T, kok = t >= 1 && t <= T, first = t == 0;
         const uint32_t qw[4] = {qr.x, qr.y, qr.z, qr.w};
@@ -398,9 +390,15 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
     //    forward substitution over 16-row blocks, one column tile per wave,
     //    in registers: the accumulator layout of a 16 x 16 tile (lane holds
     //    rows 4 (lane / 16) .. + 3 of column lane % 16) is the B-operand
-    //    layout of the 16x16x16 MFMA.  Z^T -> LDS (rows n; this overwrites
-    //    the x rows, which every wave has finished reading).
-    //    Z[:, x part] = -W, Z[:, value part] = Ut.
+    //    layout of the 16x16x16 MFMA, and read as the A operand it is the
+    //    tile transposed.  Z[:, x part] = -W, Z[:, value part] = Ut.
+    // 5. With its column tile of Z still in registers, the same wave forms
+    //    the operators that tile feeds (token-k products on 16x16x16 MFMA):
+    //      x tile n (d rows):      A^T [d][d'] = Z_W^T diag(e^{b_C-b_t}) X,
+    //                              G^T [d][t]  = diag-scaled Qh^T + Z_W^T P^T;
+    //      value tile (j columns): B [d'][j]   = (diag(e^{b_C-b_t}) X)^T Ut,
+    //                              H^T [j][t]  = Ut^T P^T;
+    //    bf16 to the workspace (A and G row-major, B as B^T [j][d'], H [t][j]).
     for (int n = wave; n < NT; n += 8) {
         const bool xp = n < 4;
         const int nr = 16 * n + col;                   // row of Z^T
@@ -428,57 +426,44 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
             }
             const f32x4 z0 = {0.f, 0.f, 0.f, 0.f};
             const f32x4 z = mfma16(as_s4(*reinterpret_cast<const uint2 *>(DB[I] + col * NBP + 4 * kq)), as_s4(pk4(acc)), z0);
-            const uint2 zp = pk4(z);
-            zb[I] = as_s4(zp);
-            put2(ZT + nr * PK + 16 * I + g4, zp);
+            zb[I] = as_s4(pk4(z));
         }
-    }
-    __syncthreads();
-
-    // 5. the operators (token-k products on MFMA), bf16 to the workspace;
-    //    wave w: row tile m = w % 4 of A^T, G^T and B, column tiles of half w / 4
-    {
-        const int m = wave & 3, hf = wave >> 2;
-        const bf16x8 z0 = ld8(ZT + (16 * m + col) * PK + k8), z1 = ld8(ZT + (16 * m + col) * PK + 32 + k8);
-        const bf16x8 x0 = ld8(XW + (16 * m + col) * PK + k8), x1 = ld8(XW + (16 * m + col) * PK + 32 + k8);
+        // B operand piece of row r (16-token block I, this lane's 4 tokens)
+        auto tok4 = [&](const bf16_t *base, int ld, int r, int I) {
+            return as_s4(*reinterpret_cast<const uint2 *>(base + r * ld + 16 * I + g4));
+        };
+        if (xp) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {   // A^T [d][d'] = Z_W^T diag(e^{b_C-b_t}) X
-            const int n = 2 * hf + i;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mfma(z0, ld8(XW + (16 * n + col) * PK + k8), acc);
-            acc = mfma(z1, ld8(XW + (16 * n + col) * PK + 32 + k8), acc);
-            put2(rec + ((16 * n + col) * DK + 16 * m + g4) * 2, pk4(acc));
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {   // G^T [d][t] = diag-scaled Qh^T + Z_W^T P^T
-            const int n = 2 * hf + i, tt = 16 * n + col;
-            f32x4 acc = unpk4(*reinterpret_cast<const uint2 *>(QB + tt * PK + 16 * m + g4)) * sv[kQs][tt];
-            acc = mfma(z0, ld8(PB + tt * PK + k8), acc);
-            if (hf) acc = mfma(z1, ld8(PB + tt * PK + 32 + k8), acc);   // token tiles 2, 3 reach k >= 32
-            put2(rec + kF1XferGOff + (tt * DK + 16 * m + g4) * 2, pk4(acc));
-        }
-#pragma unroll
-        for (int i = 0; i < NJ / 2; ++i) {   // B [d'][j] = (diag(e^{b_C-b_t}) X)^T Ut, stored as B^T [j][d']
-            const int n = hf + 2 * i;
-            const bf16_t *zu = ZT + (DK + 16 * n + col) * PK;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mfma(x0, ld8(zu + k8), acc);
-            acc = mfma(x1, ld8(zu + 32 + k8), acc);
-            put2(rec + kF1XferBOff + ((16 * n + col) * DK + 16 * m + g4) * 2, pk4(acc));
-        }
-#pragma unroll
-        for (int ij = 0; ij < (NJ + 3) / 4; ++ij) {   // H^T [j][t] = Ut^T P^T, stored as H [t][j]
-            const int mj = m + 4 * ij;
-            if (mj >= NJ) break;
-            const bf16_t *zu = ZT + (DK + 16 * mj + col) * PK;
-            const bf16x8 u0 = ld8(zu + k8), u1 = ld8(zu + 32 + k8);
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int n = 2 * hf + i, tt = 16 * n + col;
+            for (int m = 0; m < 4; ++m) {   // A^T tile (d rows of tile n, d' columns of tile m)
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = mfma(u0, ld8(PB + tt * PK + k8), acc);
-                if (hf) acc = mfma(u1, ld8(PB + tt * PK + 32 + k8), acc);
-                put2(rec + f1_xfer_h_off(DV) + (size_t(tt) * DV + 16 * mj + g4) * 2, pk4(acc));
+#pragma unroll
+                for (int I = 0; I < 4; ++I) acc = mfma16(zb[I], tok4(XW, PK, 16 * m + col, I), acc);
+                put2(rec + ((16 * m + col) * DK + 16 * n + g4) * 2, pk4(acc));
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {   // G^T tile (d rows of tile n, tokens of tile m; P lower)
+                const int tt = 16 * m + col;
+                f32x4 acc = unpk4(*reinterpret_cast<const uint2 *>(QB + tt * PK + 16 * n + g4)) * sv[kQs][tt];
+#pragma unroll
+                for (int I = 0; I <= m; ++I) acc = mfma16(zb[I], tok4(PB, PK, tt, I), acc);
+                put2(rec + kF1XferGOff + (tt * DK + 16 * n + g4) * 2, pk4(acc));
+            }
+        } else {
+            const int jt = n - 4;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {   // B tile (d' rows of tile m, j columns of tile jt)
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int I = 0; I < 4; ++I) acc = mfma16(tok4(XW, PK, 16 * m + col, I), zb[I], acc);
+                put2(rec + kF1XferBOff + ((16 * jt + col) * DK + 16 * m + g4) * 2, pk4(acc));
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {   // H^T tile (j rows of tile jt, tokens of tile m; P lower)
+                const int tt = 16 * m + col;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int I = 0; I <= m; ++I) acc = mfma16(zb[I], tok4(PB, PK, tt, I), acc);
+                put2(rec + f1_xfer_h_off(DV) + (size_t(tt) * DV + 16 * jt + g4) * 2, pk4(acc));
             }
         }
     }
