@@ -141,7 +141,6 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
     constexpr int NJ = DV / 16;               // value column tiles
     constexpr int NT = 4 + NJ;                // column tiles of R = [x part | value part]
     __shared__ __align__(16) bf16_t QB[C * PK];     // qh rows [t][d]
-    __shared__ __align__(16) bf16_t XT[DK * PK];    // x^T [d][t]
     __shared__ __align__(16) bf16_t XW[DK * PK];    // (diag(e^{b_C-b_t}) x)^T [d][t]
     __shared__ __align__(16) bf16_t YB[C * YP];     // value rows [t][j]
     __shared__ __align__(16) bf16_t PB[C * PK];     // P [t][s]
@@ -303,13 +302,17 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
         }
         return v;
     };
-    // x^T and (diag(e^{b_C-b_t}) x)^T, tile (token block m, feature block n)
+    // rows (pitch ld) of a 16 x 32 block, 16 of whose columns (block n of
+    // 16) come back transposed into the accumulator layout: lane holds
+    // rows 16 m + 4 (lane / 16) .. + 3 of column 16 n + lane % 16
+    auto transposed = [&](const bf16_t *rows, int ld, int m, int n) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        return mfma(ld8(rows + (16 * m + col) * ld + 32 * (n >> 1) + k8), IDT[n & 1][lane], z);
+    };
+    // (diag(e^{b_C-b_t}) x)^T, tile (token block m, feature block n)
     auto transpose_x = [&](int m, int n) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mfma(ld8(XB + (16 * m + col) * PK + 32 * (n >> 1) + k8), IDT[n & 1][lane], acc);
         const f32x4 ew = *reinterpret_cast<const f32x4 *>(&sv[kEw][16 * m + g4]);
-        put2(XT + (16 * n + col) * PK + 16 * m + g4, pk4(acc));
-        put2(XW + (16 * n + col) * PK + 16 * m + g4, pk4(acc * ew));
+        put2(XW + (16 * n + col) * PK + 16 * m + g4, pk4(transposed(XB, PK, m, n) * ew));
     };
 
     // 3. waves 0-3: diagonal block J = wave of I + N, inverted in fp32 on
@@ -401,19 +404,11 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
     //    bf16 to the workspace (A and G row-major, B as B^T [j][d'], H [t][j]).
     for (int n = wave; n < NT; n += 8) {
         const bool xp = n < 4;
-        const int nr = 16 * n + col;                   // row of Z^T
-        f32x4 r0[4];
+        f32x4 r0[4];   // R, block by block, from the rows transposed on MFMA
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             const f32x4 sc = *reinterpret_cast<const f32x4 *>(&sv[xp ? kRs : kEta][16 * I + g4]);
-            if (xp) {
-                r0[I] = unpk4(*reinterpret_cast<const uint2 *>(XT + nr * PK + 16 * I + g4)) * -sc;
-            } else {   // value rows transposed by an MFMA with a column picker
-                const int jt = n - 4;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = mfma(ld8(YB + (16 * I + col) * YP + 32 * (jt >> 1) + k8), IDT[jt & 1][lane], acc);
-                r0[I] = acc * sc;
-            }
+            r0[I] = xp ? transposed(XB, PK, I, n) * -sc : transposed(YB, YP, I, n - 4) * sc;
         }
         s16x4 zb[4];
 #pragma unroll
