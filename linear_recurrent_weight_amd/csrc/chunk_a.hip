@@ -33,6 +33,8 @@ namespace {
 constexpr int C = kChunk;
 constexpr int HMAX = FALCON_MAX_WINDOW - 1;  // halo pairs
 constexpr int KP = 96;                       // pair slots per chunk (64 + halo, padded)
+constexpr int kOutThreads = 512;             // a_output: 8 waves (its LDS allows one workgroup per CU)
+constexpr int kSegThreads = 256;             // a_segment: 4 waves (the window solver's registers)
 
 // N consecutive elements of a row held as raw words (16- or 8-byte loads)
 template <class E, int N>
@@ -204,7 +206,7 @@ struct ChunkRows {
 // a_segment
 // ---------------------------------------------------------------------------
 template <class E, int DK, int DV>
-__global__ __launch_bounds__(256) void a_segment(ChunkAArgs a) {
+__global__ __launch_bounds__(kSegThreads) void a_segment(ChunkAArgs a) {
     constexpr int PD = Pad<E>::v;
     constexpr int LDX = DK + 1;         // fp32 feature rows
     constexpr int LDT = KP + PD;        // [.][pair] rows
@@ -224,8 +226,9 @@ __global__ __launch_bounds__(256) void a_segment(ChunkAArgs a) {
     ChunkRows<E, DK, DV, false> rows;
 
     // aggregate write of the segment, transposed: D^T[j][d] in accumulators.
-    // tile (jt, dt) with jt < dv/16, dt < DK/16, spread over the 4 waves
-    constexpr int MAXT = (DV / 16 * DK / 16 + 3) / 4;   // state tiles per wave
+    // tile (jt, dt) with jt < dv/16, dt < DK/16, spread over the waves
+    constexpr int NW = kSegThreads / 64;
+    constexpr int MAXT = (DV / 16 * DK / 16 + NW - 1) / NW;   // state tiles per wave
     constexpr int njt = DV / 16, ntiles = njt * (DK / 16);
     f32x4 acc[MAXT];
 #pragma unroll
@@ -234,19 +237,21 @@ __global__ __launch_bounds__(256) void a_segment(ChunkAArgs a) {
 
     const int c_begin = seg * a.seg_chunks;
     const int c_end = min(a.nchunks, c_begin + a.seg_chunks);
-    rows.prefetch(a, bh, c_begin * C, halo);
+    // the row loads and the feature pass run on waves 0-3 (4 threads per row)
+    const bool rw = wave < 4;
+    if (rw) rows.prefetch(a, bh, c_begin * C, halo);
     for (int c = c_begin; c < c_end; ++c) {
         const int c0 = c * C;
-        rows.store_pairs(a, bh, c0, halo, XF, LDX, static_cast<E *>(nullptr), 0, YT, LDT, nrm);
+        if (rw) rows.store_pairs(a, bh, c0, halo, XF, LDX, static_cast<E *>(nullptr), 0, YT, LDT, nrm);
         // unconditional (clamped) loads; unused past the sequence end
         const int tcl = c0 + (tid & 63) < T ? c0 + (tid & 63) : T - 1;
         const float beta_t = a.beta[size_t(bh) * T + tcl];
         const float lam_t = a.lambda[size_t(bh) * T + tcl];
-        if (c + 1 < c_end) rows.prefetch(a, bh, c0 + C, halo);
+        if (rw && c + 1 < c_end) rows.prefetch(a, bh, c0 + C, halo);
         __syncthreads();
         // window statistic / feature energy of the chunk's own tokens
         if (W > 1) {
-            for (int idx = tid; idx < np * W; idx += 256) {
+            for (int idx = tid; idx < np * W; idx += kSegThreads) {
                 const int r = idx / W, d = idx % W;
                 float s = 0.f;
                 if (r - d >= 0) {
@@ -318,7 +323,7 @@ __global__ __launch_bounds__(256) void a_segment(ChunkAArgs a) {
             coef[p] = p < np ? m : 0.f;
         }
         __syncthreads();
-        for (int idx = tid; idx < KP * DK; idx += 256) {
+        for (int idx = tid; idx < KP * DK; idx += kSegThreads) {
             const int p = idx / DK, d = idx % DK;
             st(XT, size_t(d) * LDT + p, p < np ? coef[p] * XF[p * LDX + d] : 0.f);
         }
@@ -328,7 +333,7 @@ __global__ __launch_bounds__(256) void a_segment(ChunkAArgs a) {
         bsum += bC_s;
 #pragma unroll
         for (int m = 0; m < MAXT; ++m) {
-            const int tile = wave + 4 * m;
+            const int tile = wave + NW * m;
             if (tile < ntiles) {
                 const int jt = tile % njt, dt = tile / njt;
 #pragma unroll
@@ -339,13 +344,13 @@ __global__ __launch_bounds__(256) void a_segment(ChunkAArgs a) {
         // boundary state out from the last chunk of the sequence
         if (c == a.nchunks - 1 && halo > 0 && a.tailx_out) {
             const int n_out = a.n_tail_out;
-            for (int idx = tid; idx < halo * DK; idx += 256) {
+            for (int idx = tid; idx < halo * DK; idx += kSegThreads) {
                 const int sl = idx / DK, e = idx % DK;
                 const int tau = T - halo + sl;
                 const int p = tau - (c0 - halo);
                 a.tailx_out[(size_t(bh) * halo + sl) * DK + e] = sl >= halo - n_out ? XF[p * LDX + e] : 0.f;
             }
-            for (int idx = tid; idx < halo * dv; idx += 256) {
+            for (int idx = tid; idx < halo * dv; idx += kSegThreads) {
                 const int sl = idx / dv, e = idx % dv;
                 const int tau = T - halo + sl;
                 const int p = tau - (c0 - halo);
@@ -359,7 +364,7 @@ __global__ __launch_bounds__(256) void a_segment(ChunkAArgs a) {
     float *Dg = a.Dseg + (size_t(bh) * a.nseg + seg) * dv * DK;
 #pragma unroll
     for (int m = 0; m < MAXT; ++m) {
-        const int tile = wave + 4 * m;
+        const int tile = wave + NW * m;
         if (tile < ntiles) {
             const int jt = tile % njt, dt = tile / njt;
 #pragma unroll
@@ -411,7 +416,7 @@ template <> struct PBuf<bf16_t> { static constexpr bool separate = true; };
 template <> struct PBuf<float> { static constexpr bool separate = false; };
 
 template <class E, int DK, int DV>
-__global__ __launch_bounds__(256) void a_output(ChunkAArgs a) {
+__global__ __launch_bounds__(kOutThreads) void a_output(ChunkAArgs a) {
     constexpr int PD = Pad<E>::v;
     constexpr int LDK = DK + PD;        // [.][d] rows
     constexpr int LDT = KP + PD;        // [.][pair] rows
@@ -435,14 +440,16 @@ __global__ __launch_bounds__(256) void a_output(ChunkAArgs a) {
     ChunkRows<E, DK, DV, true> rows;
     E *o = static_cast<E *>(a.o) + size_t(bh) * T * dv;
 
-    // entry state S^T[j][d] of this segment in accumulators, tiles as in a_segment
-    constexpr int MAXT = (DV / 16 * DK / 16 + 3) / 4;
+    // entry state S^T[j][d] of this segment in accumulators, tiles spread
+    // over the 8 waves
+    constexpr int NW = kOutThreads / 64;
+    constexpr int MAXT = (DV / 16 * DK / 16 + NW - 1) / NW;
     constexpr int njt = DV / 16, ntiles = njt * (DK / 16);
     f32x4 acc[MAXT];
     const float *Se = a.Sseg + (size_t(bh) * a.nseg + seg) * dv * DK;
 #pragma unroll
     for (int m = 0; m < MAXT; ++m) {
-        const int tile = wave + 4 * m;
+        const int tile = wave + NW * m;
         if (tile < ntiles) {
             const int jt = tile % njt, dt = tile / njt;
 #pragma unroll
@@ -456,17 +463,21 @@ __global__ __launch_bounds__(256) void a_output(ChunkAArgs a) {
 
     const int c_begin = seg * a.seg_chunks;
     const int c_end = min(a.nchunks, c_begin + a.seg_chunks);
-    rows.prefetch(a, bh, c_begin * C, halo);
+    // the row loads and the feature pass run on waves 0-3 (4 threads per row)
+    const bool rw = wave < 4;
+    if (rw) rows.prefetch(a, bh, c_begin * C, halo);
     for (int c = c_begin; c < c_end; ++c) {
         const int c0 = c * C;
-        rows.store_pairs(a, bh, c0, halo, nullptr, 0, XE, LDK, YT, LDT, nullptr);
-        rows.store_queries(a, c0, QE, LDK);
+        if (rw) {
+            rows.store_pairs(a, bh, c0, halo, nullptr, 0, XE, LDK, YT, LDT, nullptr);
+            rows.store_queries(a, c0, QE, LDK);
+        }
         float ew = 0.f, lg = 0.f;
         if (wave == 0) {
             ew = a.etaw[size_t(bh) * a.Tpad + c0 + lane];
             lg = a.lg[size_t(bh) * a.Tpad + c0 + lane];
         }
-        if (c + 1 < c_end) rows.prefetch(a, bh, c0 + C, halo);
+        if (rw && c + 1 < c_end) rows.prefetch(a, bh, c0 + C, halo);
         if (wave == 0) {
             ew_s[lane] = ew;
             gam_s[lane] = expf(lg);
@@ -476,7 +487,7 @@ __global__ __launch_bounds__(256) void a_output(ChunkAArgs a) {
         }
         __syncthreads();
         // scores Qh X_ext^T (4 token tiles x 6 pair tiles)
-        for (int tile = wave; tile < 4 * (KP / 16); tile += 4) {
+        for (int tile = wave; tile < 4 * (KP / 16); tile += NW) {
             const int tt = tile % 4, pt = tile / 4;
             f32x4 s = Mma<E>::run(f32x4{0.f, 0.f, 0.f, 0.f}, QE + 16 * tt * LDK, LDK, XE + 16 * pt * LDK, LDK,
                                   0, DK);
@@ -522,7 +533,7 @@ __global__ __launch_bounds__(256) void a_output(ChunkAArgs a) {
             if (mh == 1) coef[mp] = m;
         }
         __syncthreads();
-        for (int idx = tid; idx < KP * DK; idx += 256) {
+        for (int idx = tid; idx < KP * DK; idx += kOutThreads) {
             const int p = idx / DK, d = idx % DK;
             st(XT, size_t(d) * LDT + p, p < np ? coef[p] * ld(XE, size_t(p) * LDK + d) : 0.f);
         }
@@ -537,7 +548,7 @@ __global__ __launch_bounds__(256) void a_output(ChunkAArgs a) {
             Pm = reinterpret_cast<const E *>(PF);
             ldp = LDF;
         }
-        for (int tile = wave; tile < njt * 4; tile += 4) {
+        for (int tile = wave; tile < njt * 4; tile += NW) {
             const int jt = tile % njt, tt = tile / njt;
             f32x4 r0 = Mma<E>::run(f32x4{0.f, 0.f, 0.f, 0.f}, ST + 16 * jt * LDK, LDK, QE + 16 * tt * LDK, LDK,
                                    0, DK);
@@ -555,7 +566,7 @@ __global__ __launch_bounds__(256) void a_output(ChunkAArgs a) {
         const float gC = expf(bC_s);
 #pragma unroll
         for (int m = 0; m < MAXT; ++m) {
-            const int tile = wave + 4 * m;
+            const int tile = wave + NW * m;
             if (tile < ntiles) {
                 const int jt = tile % njt, dt = tile / njt;
 #pragma unroll
@@ -566,7 +577,7 @@ __global__ __launch_bounds__(256) void a_output(ChunkAArgs a) {
         __syncthreads();   // every read of ST / YT / XT of this chunk is done
 #pragma unroll
         for (int m = 0; m < MAXT; ++m) {
-            const int tile = wave + 4 * m;
+            const int tile = wave + NW * m;
             if (tile < ntiles) {
                 const int jt = tile % njt, dt = tile / njt;
 #pragma unroll
@@ -580,11 +591,11 @@ __global__ __launch_bounds__(256) void a_output(ChunkAArgs a) {
 
 template <class E, int DK, int DV>
 void launch_t(const ChunkAArgs &a, hipStream_t s, Marks *m) {
-    a_segment<E, DK, DV><<<dim3(a.nseg, a.BH), 256, 0, s>>>(a);
+    a_segment<E, DK, DV><<<dim3(a.nseg, a.BH), kSegThreads, 0, s>>>(a);
     m->mark(s);
     a_segscan<<<dim3(a.BH, (a.dk * a.dv + 255) / 256), 256, 0, s>>>(a);
     m->mark(s);
-    a_output<E, DK, DV><<<dim3(a.nseg, a.BH), 256, 0, s>>>(a);
+    a_output<E, DK, DV><<<dim3(a.nseg, a.BH), kOutThreads, 0, s>>>(a);
     m->mark(s);
 }
 
