@@ -21,13 +21,15 @@
 //   registers), and the four operator products on MFMA; A, G, B^T and H go
 //   to the workspace in bf16 with e^{b_C}.
 // f1_carry: one workgroup per (head, slice of value columns) walks the
-//   chunks: per chunk each compute wave owns 16 state columns x 32 rows
-//   (fp32 MFMA accumulators) and issues 4 MFMAs for the carry and 4 for the
-//   outputs of 32 tokens, all from one bf16 copy of the entry state
-//   (double-buffered in LDS).  Loader waves copy the
+//   chunks: per chunk each compute wave owns 16 state columns x 16 (or 32)
+//   rows (fp32 MFMA accumulators) and issues the MFMAs of its rows of the
+//   carry and of the outputs of its 16 (or 32) tokens, all from one bf16
+//   copy of the entry state (double-buffered in LDS).  Loader waves copy the
 //   operators of later chunks straight from memory into a ring of LDS slots
 //   (global_load_lds), so no register staging sits between memory and the
-//   matrix cores.  One workgroup barrier per chunk.
+//   matrix cores; the records hold their tiles in operand lane order, so
+//   each operand is one contiguous 16- or 8-byte read per lane.  One
+//   workgroup barrier per chunk.
 #include "chunk_layout.h"
 #include "kernels.h"
 #include "mma.h"
@@ -106,14 +108,17 @@ constexpr int XW_THREADS = 512; // 8 waves per chunk
 
 // The raw rows of one chunk (8 q and 8 k elements and d_v / 8 values of row
 // `row`, part `part`, and the row's beta and lambda), loaded into registers
-// one chunk ahead.  Loads are unconditional from rows clamped into [0, T): a
-// load under a branch would be waited for where the branch joins.
+// one chunk ahead.  Loads are unconditional from rows clamped into [0, T).
+// The one conditional load, the 8 incoming features x_0 of the first token of
+// a continued sequence, comes last: the counted wait for the other rows then
+// does not depend on it.
 template <int DV>
 struct XferRows {
     static constexpr int VPT = DV / 8;                 // value elements per thread
     static constexpr int NV = VPT >= 8 ? VPT / 8 : 1;  // 16-byte pieces (8 bytes at d_v = 32)
     uint4 q, k, v[NV];
     float beta, lam;
+    f32x4 xn[2];                                       // x_0 (row 0 of chunk 0 only)
     __device__ __forceinline__ void load(const F1SplitArgs &a, int id, int row, int part) {
         const int c = id / a.BH, bh = id % a.BH, T = a.T, t = c * kChunk + row;
         const int tq = t < T ? t : T - 1;
@@ -130,6 +135,11 @@ struct XferRows {
         }
         beta = a.beta[size_t(bh) * T + tq];
         lam = a.lambda[size_t(bh) * T + tq];
+        if (t == 0 && a.xnext_in) {
+            const f32x4 *xp = reinterpret_cast<const f32x4 *>(a.xnext_in + size_t(bh) * DK + 8 * part);
+            xn[0] = xp[0];
+            xn[1] = xp[1];
+        }
     }
 };
 
@@ -172,6 +182,10 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
     // next chunk are loaded while this one is worked on
     Rows rows;
     rows.load(a, blockIdx.x, threadIdx.x >> 3, threadIdx.x & 7);
+    // The first chunk's rows are waited for here: the loop is then entered
+    // with no load in flight, and the counted wait inside it for the rows of
+    // the next chunk need not cover that chunk's record stores.
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
     for (int id = blockIdx.x; id < total; id += gridDim.x) {
     // lane quantities are formed afresh in every pass (an opaque copy of the
     // thread index), so that the compiler does not keep dozens of derived
@@ -194,10 +208,6 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
 #pragma unroll
         for (int i = 0; i < Rows::NV; ++i) vr[i] = rows.v[i];
         const float beta = rows.beta, lam = rows.lam;
-        {   // the next chunk's rows (the last chunk reloads its own)
-            const int nid = id + int(gridDim.x);
-            rows.load(a, nid < total ? nid : id, row, part);
-        }
         const bool qok = t < T, kok = t >= 1 && t <= T, first = t == 0;
         const uint32_t qw[4] = {qr.x, qr.y, qr.z, qr.w};
         const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w};
@@ -212,7 +222,10 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
         const bool carry_x = first && a.xnext_in;
         if (carry_x) {   // x_0 continues the previous segment (features already formed)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) xv[e] = a.xnext_in[size_t(bh) * DK + 8 * part + e];
+            for (int e = 0; e < 4; ++e) {
+                xv[e] = rows.xn[0][e];
+                xv[4 + e] = rows.xn[1][e];
+            }
         }
         float sq = 0.f, sk = 0.f;
 #pragma unroll
@@ -254,6 +267,10 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
             sv[kEta][row] = eta;
             sv[kLg][row] = log2_1m(alpha);
         }
+        // the next chunk's rows (the last chunk reloads its own), issued once
+        // this chunk's are consumed, so that they land in the same registers
+        const int nid = id + int(gridDim.x);
+        rows.load(a, nid < total ? nid : id, row, part);
     }
     __syncthreads();
 
@@ -402,7 +419,14 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
     //      value tile (j columns): B [d'][j]   = (diag(e^{b_C-b_t}) X)^T Ut,
     //                              H^T [j][t]  = Ut^T P^T;
     //    bf16 to the workspace (A and G row-major, B as B^T [j][d'], H [t][j]).
-    for (int n = wave; n < NT; n += 8) {
+    // A fixed, unrolled count of tiles per wave: each wave then issues a
+    // known number of stores per chunk, and the wait for the next chunk's
+    // rows (loaded before those stores) leaves the stores in flight.
+    __builtin_assume(wave >= 0 && wave < XW_THREADS / 64);
+#pragma unroll
+    for (int it = 0; it < (NT + 7) / 8; ++it) {
+        const int n = wave + 8 * it;
+        if (NT % 8 != 0 && n >= NT) break;
         const bool xp = n < 4;
         f32x4 r0[4];   // R, block by block, from the rows transposed on MFMA
 #pragma unroll
@@ -427,13 +451,17 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
         auto tok4 = [&](const bf16_t *base, int ld, int r, int I) {
             return as_s4(*reinterpret_cast<const uint2 *>(base + r * ld + 16 * I + g4));
         };
+        // results first, stores after the branch: every wave then issues
+        // the same 8 stores on one path
+        uint2 o1[4], o2[4];
+        const int jt = n - 4;
         if (xp) {
 #pragma unroll
             for (int m = 0; m < 4; ++m) {   // A^T tile (d rows of tile n, d' columns of tile m)
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int I = 0; I < 4; ++I) acc = mfma16(zb[I], tok4(XW, PK, 16 * m + col, I), acc);
-                put2(rec + ((16 * m + col) * DK + 16 * n + g4) * 2, pk4(acc));
+                o1[m] = pk4(acc);
             }
 #pragma unroll
             for (int m = 0; m < 4; ++m) {   // G^T tile (d rows of tile n, tokens of tile m; P lower)
@@ -441,16 +469,15 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
                 f32x4 acc = unpk4(*reinterpret_cast<const uint2 *>(QB + tt * PK + 16 * n + g4)) * sv[kQs][tt];
 #pragma unroll
                 for (int I = 0; I <= m; ++I) acc = mfma16(zb[I], tok4(PB, PK, tt, I), acc);
-                put2(rec + kF1XferGOff + (tt * DK + 16 * n + g4) * 2, pk4(acc));
+                o2[m] = pk4(acc);
             }
         } else {
-            const int jt = n - 4;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {   // B tile (d' rows of tile m, j columns of tile jt)
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int I = 0; I < 4; ++I) acc = mfma16(tok4(XW, PK, 16 * m + col, I), zb[I], acc);
-                put2(rec + kF1XferBOff + ((16 * jt + col) * DK + 16 * m + g4) * 2, pk4(acc));
+                o1[m] = pk4(acc);
             }
 #pragma unroll
             for (int m = 0; m < 4; ++m) {   // H^T tile (j rows of tile jt, tokens of tile m; P lower)
@@ -458,8 +485,22 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int I = 0; I <= m; ++I) acc = mfma16(zb[I], tok4(PB, PK, tt, I), acc);
-                put2(rec + f1_xfer_h_off(DV) + (size_t(tt) * DV + 16 * jt + g4) * 2, pk4(acc));
+                o2[m] = pk4(acc);
             }
+        }
+        // byte offsets in the record, whose tiles are in operand lane order:
+        // this lane's 4 elements of A (row 16 m + col, d = 16 n + g4 ..) and
+        // of G (token 16 m + col) go to lane 16 (2 (n % 2) + kq / 2) + col of
+        // the k half n / 2, bytes 8 (kq % 2) ..; B and H tiles are stored as
+        // the accumulators hold them.  Each store covers 512 contiguous bytes.
+        const int xo = ((n >> 1) * 64 + 16 * (2 * (n & 1) + (kq >> 1)) + col) * 16 + 8 * (kq & 1);
+        const int off1 = xp ? xo : int(kF1XferBOff) + (jt * 256 + lane) * 8;
+        const int off2 = xp ? int(kF1XferGOff) + xo : int(f1_xfer_h_off(DV)) + (jt * 256 + lane) * 8;
+        const int st1 = xp ? 2048 : 512, st2 = st1;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            put2(rec + off1 + m * st1, o1[m]);
+            put2(rec + off2 + m * st2, o2[m]);
         }
     }
     __syncthreads();   // the next chunk overwrites the LDS buffers
@@ -505,8 +546,6 @@ __global__ __launch_bounds__(carry_threads<DS>()) void f1_carry(F1SplitArgs a, i
     static_assert(NB >= 3, "ring depth");
     constexpr int NI = kS / 1024;                // 1 KB copies per chunk
     constexpr int IPW = NI / NLW;                // per loader wave (+ one scalar copy)
-    constexpr int PPR = DS / 8;                  // 16-byte pieces per H row
-    constexpr int HSH = PPR == 8 ? 1 : (PPR == 4 ? 2 : 3);   // log2 of the H rows per 256 bytes
     static_assert(NI % NLW == 0, "whole copies per loader wave");
     static_assert((NB - 2) * (IPW + 1) < 64, "vmcnt range");
     __shared__ __align__(16) unsigned char ring[NB * SB];
@@ -532,25 +571,16 @@ __global__ __launch_bounds__(carry_threads<DS>()) void f1_carry(F1SplitArgs a, i
     if (wave >= NCW) {
         // ---- loader waves: chunk cc's operators into slot cc % NB ----
         const int lw = wave - NCW;
-        // source offset of this lane's 16-byte piece in each copy.  The LDS
-        // rows are stored with their 16-byte pieces permuted so that the
-        // 16-row column reads of the compute waves hit 16 different bank
-        // groups: rows of 128 bytes put piece q of row r at q ^ ((r / 2) % 8),
-        // rows of 64 bytes at q ^ ((r / 4) % 4), of 32 bytes at q ^ ((r / 8) % 2).
+        // source offset of this lane's 16-byte piece in each copy: the slot
+        // is A and G whole, then the slice's value tiles of B^T and of H, each
+        // a contiguous range of the record (its tiles are in lane order)
         int goff[IPW];
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
             const int off = 1024 * (lw + NLW * i) + 16 * lane;
-            if (off < kB) {
-                const int base = off < kG ? 0 : kG, o = off - base, r = o >> 7, q = (o >> 4) & 7;
-                goff[i] = (base == 0 ? 0 : int(kF1XferGOff)) + r * 128 + 16 * (q ^ ((r >> 1) & 7));
-            } else if (off < kH) {
-                const int o = off - kB, r = o >> 7, q = (o >> 4) & 7;
-                goff[i] = int(kF1XferBOff) + (j0 + r) * 128 + 16 * (q ^ ((r >> 1) & 7));
-            } else {
-                const int o = off - kH, r = o / (2 * DS), q = (o % (2 * DS)) >> 4;
-                goff[i] = int(f1_xfer_h_off(DV)) + r * 2 * DV + 2 * j0 + 16 * (q ^ ((r >> HSH) & (PPR - 1)));
-            }
+            goff[i] = off < kB ? off
+                    : off < kH ? int(kF1XferBOff) + 128 * j0 + (off - kB)
+                               : int(f1_xfer_h_off(DV)) + 128 * j0 + (off - kH);
         }
         const int soff = int(f1_xfer_scal_off(DV));
         auto issue = [&](int cc) {
@@ -595,15 +625,11 @@ __global__ __launch_bounds__(carry_threads<DS>()) void f1_carry(F1SplitArgs a, i
     //      m = MT mh .. MT mh + MT - 1, and the outputs of the same token
     //      tiles for those columns ----
     const int ct = wave % NCT, mh = wave / NCT;
-    const int col = lane & 15, g4 = 4 * (lane >> 4), k8 = 8 * (lane >> 4), kq = lane >> 4;
-    const int sw = (col >> 1) & 7;               // piece permutation of rows 16 m + col (128-byte rows)
-    // byte offsets inside a slot (row 16 m + col of A and G; pieces 4 kk + kq)
-    const int ao0 = col * 128 + 16 * (kq ^ sw), ao1 = col * 128 + 16 * ((4 + kq) ^ sw);
-    // B^T row 16 ct + col, d = 16 m + g4 (piece 2 m + g4 / 8, half g4 & 4)
-    const int bo = (16 * ct + col) * 128 + ((g4 & 4) << 1);
-    const int bsw = ((16 * ct + col) >> 1) & 7;
-    // H row 16 m + col, j = 16 ct + g4 (piece 2 ct + g4 / 8)
-    const int ho = col * (2 * DS) + 16 * ((2 * ct + (g4 >> 3)) ^ ((col >> HSH) & (PPR - 1))) + ((g4 & 4) << 1);
+    const int col = lane & 15, g4 = 4 * (lane >> 4), k8 = 8 * (lane >> 4);
+    // byte offsets inside a slot: the operand pieces of this lane (tiles in
+    // lane order), A and G at k half 0 (+ 1024 for half 1), B^T and H tiles
+    // of column tile ct
+    const int ao = 16 * lane, bo = ct * 2048 + 8 * lane;
     bf16_t *og = static_cast<bf16_t *>(a.o) + size_t(bh) * T * DV + j0 + 16 * ct + g4;
 
     f32x4 S[MT];
@@ -627,12 +653,12 @@ __global__ __launch_bounds__(carry_threads<DS>()) void f1_carry(F1SplitArgs a, i
 #pragma unroll
         for (int h = 0; h < MT; ++h) {
             const int m = MT * mh + h;
-            bq[h] = *reinterpret_cast<const uint2 *>(sl + kB + bo + 16 * ((2 * m + (g4 >> 3)) ^ bsw));
-            hq[h] = *reinterpret_cast<const uint2 *>(sl + kH + m * 16 * (2 * DS) + ho);
-            a0[h] = ld8(sl + kA + m * 2048 + ao0);
-            a1[h] = ld8(sl + kA + m * 2048 + ao1);
-            q0[h] = ld8(sl + kG + m * 2048 + ao0);
-            q1[h] = ld8(sl + kG + m * 2048 + ao1);
+            bq[h] = *reinterpret_cast<const uint2 *>(sl + kB + bo + m * 512);
+            hq[h] = *reinterpret_cast<const uint2 *>(sl + kH + bo + m * 512);
+            a0[h] = ld8(sl + kA + m * 2048 + ao);
+            a1[h] = ld8(sl + kA + m * 2048 + 1024 + ao);
+            q0[h] = ld8(sl + kG + m * 2048 + ao);
+            q1[h] = ld8(sl + kG + m * 2048 + 1024 + ao);
         }
         bf16_t *stn = STw[(c + 1) & 1][ct];
 #pragma unroll

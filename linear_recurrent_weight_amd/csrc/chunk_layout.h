@@ -76,7 +76,13 @@ constexpr bool chunk_f1_split_supported(bool bf16, int dk, int dv) {
 //   B^T [d_v j][64 d] = ((diag(e^{b_C-b_t}) X)^T Ut)^T      (state write)
 //   H   [64 t][d_v j] = P Ut                               (outputs from the chunk's writes)
 // with W = Tp diag(e^{b_{t-1}}) X and Ut = Tp Y; then fp32 e^{b_C} in a
-// 256-byte block.
+// 256-byte block.  Each block is stored in the lane order of the MFMA
+// operands that read it, 16 x 16 (or 16 x 32) tiles one after another:
+//   A, G: [row tile m 4][k half h 2][lane l 64] x 16 bytes, lane l holding
+//         row 16 m + l % 16, elements 32 h + 8 (l / 16) .. + 7;
+//   B^T, H: [value tile jt][row tile m 4][lane l 64] x 8 bytes, lane l holding
+//         B rows 16 m + 4 (l / 16) .. + 3 of column 16 jt + l % 16, and H
+//         row 16 m + l % 16, columns 16 jt + 4 (l / 16) .. + 3.
 constexpr bool chunk_f1_xfer_supported(bool bf16, int dk, int dv) {
     return bf16 && dk == 64 && (dv == 32 || dv == 64 || dv == 128);
 }
