@@ -93,16 +93,13 @@ __device__ __forceinline__ f32x4 mfma16(const s16x4 &a, const s16x4 &b, const f3
 __device__ __forceinline__ s16x4 as_s4(const uint2 &u) { return __builtin_bit_cast(s16x4, u); }
 
 constexpr int NBP = 20;         // bf16 pitch of the 16 x 16 solve blocks
+constexpr int LFB = 16 * 16 + 4;   // fp32 stride of the blocks L_J (the four blocks' rows fall in different banks)
 
-// A B for 16 x 16 fp32 matrices in the accumulator layout (lane l holds rows
-// 4 (l / 16) .. + 3 of column l % 16): `at` holds A^T that way, `b` holds B.
-// Step s of the 16x16x4 MFMA takes k = 4 (l / 16) + s, so both operands
-// are the lane's own accumulator elements.
-__device__ __forceinline__ f32x4 mm16(const f32x4 &at, const f32x4 &b) {
-    f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(at[s], b[s], c, 0, 0, 0);
-    return c;
+// the value of lane h of each lane quad, in every lane of the quad (DPP
+// quad_perm [h, h, h, h], CTRL = 0x55 h)
+template <int CTRL>
+__device__ __forceinline__ float quad_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 constexpr int XW_THREADS = 512; // 8 waves per chunk
 
@@ -157,6 +154,7 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
     __shared__ __align__(16) bf16_t XB[C * PK];     // x rows [t][d]
     __shared__ __align__(16) bf16_t NB[6][16 * NBP];   // -N below the diagonal blocks
     __shared__ __align__(16) bf16_t DB[4][16 * NBP];   // inverses of the diagonal blocks of I + N
+    __shared__ __align__(16) float LF[4 * LFB];         // the strictly lower diagonal blocks L_J, fp32 row-major
     __shared__ __align__(16) float sv[kNsv][C];
     __shared__ __align__(16) bf16x8 IDT[2][64];        // column pickers (see below), per lane
 
@@ -295,30 +293,6 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
     }
     wave_lds_sync();
 
-    // decayed Gram (isG: eta_i e^{b_{i-1}-b_j} x_i.x_j) or score (e^{b_i-b_j} qh_i.x_j)
-    // tile (I, J): rows i = 16 I + g4 + r, column j = 16 J + col
-    auto tile = [&](bool isG, int I, int J) {
-        const bf16_t *ar = (isG ? XB : QB) + (16 * I + col) * PK + k8;
-        const bf16_t *br = XB + (16 * J + col) * PK + k8;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mfma(ld8(ar), ld8(br), acc);
-        acc = mfma(ld8(ar + 32), ld8(br + 32), acc);
-        const int j = 16 * J + col, i0 = 16 * I + g4;
-        f32x4 v;
-        if (sep) {
-            const float cj = sv[kCs][j];
-            const f32x4 ri = *reinterpret_cast<const f32x4 *>(&sv[isG ? kRs : kQs][i0]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = acc[r] * (ri[r] * cj);
-        } else {
-            const float bj = sv[kB][j];
-            const f32x4 bi = *reinterpret_cast<const f32x4 *>(&sv[isG ? kBp : kB][i0]);
-            const f32x4 ei = *reinterpret_cast<const f32x4 *>(&sv[kEta][i0]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = acc[r] * ex2(bi[r] - bj) * (isG ? ei[r] : 1.f);
-        }
-        return v;
-    };
     // rows (pitch ld) of a 16 x 32 block, 16 of whose columns (block n of
     // 16) come back transposed into the accumulator layout: lane holds
     // rows 16 m + 4 (lane / 16) .. + 3 of column 16 n + lane % 16
@@ -333,74 +307,96 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
     };
 
     // 3. waves 0-3: diagonal block J = wave of I + N, inverted in fp32 on
-    //    MFMA as (I - L)(I + L^2)(I + L^4)(I + L^8) (L strictly lower 16 x
-    //    16, so L^16 = 0 and the product is the finite Neumann series);
-    //    waves 4-7: the Gram blocks below them (-> -N, bf16) and the score
-    //    tiles (-> P); every wave: two transposes of x.
+    //    the vector ALUs (the matrix cores stay free for the other waves),
+    //    then one score tile each; waves 4-7: the Gram blocks below the
+    //    diagonal (-> -N, bf16) and the other score tiles (-> P); every
+    //    wave: two transposes of x.
+    auto job = [&](int jb) {
+        // job 0-5: Gram block (1,0) (2,0) (2,1) (3,0) (3,1) (3,2) of
+        // eta_i e^{b_{i-1}-b_j} x_i.x_j; job 6-15: score tile on or below the
+        // diagonal, e^{b_i-b_j} qh_i.x_j.  The choices are uniform selects
+        // (no branches), so that unrolled jobs overlap their reads.  The tile
+        // is formed transposed (x rows as the A operand): lane (col, g4)
+        // gets row i = 16 I + col at columns j = 16 J + g4 .. + 3, one
+        // 8-byte write.
+        const int tt = jb - 6;
+        const bool isG = jb < 6;
+        const int I = isG ? (0xFE9 >> (2 * jb)) & 3 : (0xffa94 >> (2 * tt)) & 3;
+        const int J = isG ? (0x910 >> (2 * jb)) & 3 : (0xe4910 >> (2 * tt)) & 3;
+        const bf16_t *ar = (isG ? XB : QB) + (16 * I + col) * PK + k8;
+        const bf16_t *br = XB + (16 * J + col) * PK + k8;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc = mfma(ld8(br), ld8(ar), z);
+        acc = mfma(ld8(br + 32), ld8(ar + 32), acc);
+        const int i = 16 * I + col, j0 = 16 * J + g4;
+        f32x4 v;
+        if (sep) {
+            const float ri = sv[isG ? kRs : kQs][i];
+            const f32x4 cj = *reinterpret_cast<const f32x4 *>(&sv[kCs][j0]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = acc[r] * (ri * cj[r]);
+        } else {
+            const float bi = sv[isG ? kBp : kB][i], ei = isG ? sv[kEta][i] : 1.f;
+            const f32x4 bj = *reinterpret_cast<const f32x4 *>(&sv[kB][j0]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = acc[r] * ex2(bi - bj[r]) * ei;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = isG ? -v[r] : ((I != J || j0 + r <= i) ? v[r] : 0.f);
+        put2(isG ? NB[jb < 6 ? jb : 0] + col * NBP + g4 : PB + i * PK + j0, pk4(v));
+    };
     if (wave < 4) {
         const int J = wave;
-        // the raw Gram block X_J X_J^T is symmetric: one tile gives L (row
-        // i, column j) and L^T (row j, column i) with their own scales
-        f32x4 g = {0.f, 0.f, 0.f, 0.f};
-        {
+        {   // L_J row-major in fp32 (LF): the raw Gram block X_J X_J^T is
+            // symmetric, so the accumulator tile also holds row col of L_J at
+            // columns g4 .. + 3, scaled eta_i e^{b_{i-1}-b_j} (strictly lower)
             const bf16_t *xr = XB + (16 * J + col) * PK + k8;
+            f32x4 g = {0.f, 0.f, 0.f, 0.f};
             g = mfma(ld8(xr), ld8(xr), g);
             g = mfma(ld8(xr + 32), ld8(xr + 32), g);
-        }
-        const int jc = 16 * J + col, i0 = 16 * J + g4;
-        f32x4 L, Lt;
-        if (sep) {
-            const f32x4 rs = *reinterpret_cast<const f32x4 *>(&sv[kRs][i0]);
-            const f32x4 cs = *reinterpret_cast<const f32x4 *>(&sv[kCs][i0]);
-            const float rsj = sv[kRs][jc], csj = sv[kCs][jc];
+            const int i = 16 * J + col, j0 = 16 * J + g4;
+            f32x4 l;
+            if (sep) {
+                const float ri = sv[kRs][i];
+                const f32x4 cj = *reinterpret_cast<const f32x4 *>(&sv[kCs][j0]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                L[r] = col < g4 + r ? g[r] * (rs[r] * csj) : 0.f;
-                Lt[r] = g4 + r < col ? g[r] * (rsj * cs[r]) : 0.f;
+                for (int r = 0; r < 4; ++r) l[r] = g4 + r < col ? g[r] * (ri * cj[r]) : 0.f;
+            } else {
+                const float bpi = sv[kBp][i], ei = sv[kEta][i];
+                const f32x4 bj = *reinterpret_cast<const f32x4 *>(&sv[kB][j0]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) l[r] = g4 + r < col ? g[r] * ei * ex2(bpi - bj[r]) : 0.f;
             }
-        } else {
-            const f32x4 bp = *reinterpret_cast<const f32x4 *>(&sv[kBp][i0]);
-            const f32x4 bb = *reinterpret_cast<const f32x4 *>(&sv[kB][i0]);
-            const f32x4 et = *reinterpret_cast<const f32x4 *>(&sv[kEta][i0]);
-            const float bpj = sv[kBp][jc], bj = sv[kB][jc], etj = sv[kEta][jc];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                L[r] = col < g4 + r ? g[r] * et[r] * ex2(bp[r] - bj) : 0.f;
-                Lt[r] = g4 + r < col ? g[r] * etj * ex2(bpj - bb[r]) : 0.f;
-            }
+            *reinterpret_cast<f32x4 *>(&LF[J * LFB + col * 16 + g4]) = l;
         }
-        auto plus_i = [&](f32x4 v, float d) {   // v + d I
+        wave_lds_sync();
+        // lane (r = lane / 4, h = lane % 4): elements 4 h .. + 3 of row r of
+        // D_J = (I + L_J)^{-1}, from d (I + L_J) = e_r, right-looking over the
+        // columns from the last: once d_k is final (in lane (r, k / 4)) it is
+        // broadcast over the lane quad and d_j -= d_k L_kj for the lane's four
+        // j (L_kj = 0 for j >= k)
+        const int r = lane >> 2, h = lane & 3;
+        const float *lf = LF + J * LFB + 4 * h;
+        f32x4 dq;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] += (g4 + r == col) ? d : 0.f;
-            return v;
-        };
-        const f32x4 L2 = mm16(Lt, L), L2t = mm16(L, Lt);
-        const f32x4 L4 = mm16(L2t, L2), L4t = mm16(L2, L2t);
-        const f32x4 L8 = mm16(L4t, L4);
-        const f32x4 Q1 = mm16(plus_i(L4t, 1.f), plus_i(L8, 1.f));     // (I + L^4)(I + L^8)
-        const f32x4 Q2 = mm16(plus_i(L2t, 1.f), Q1);                   // (I + L^2) Q1
-        const f32x4 Di = mm16(plus_i(-Lt, 1.f), Q2);                   // (I - L) Q2
-        uint16_t *db = reinterpret_cast<uint16_t *>(DB[J]);
+        for (int e = 0; e < 4; ++e) dq[e] = 4 * h + e == r ? 1.f : 0.f;
+        f32x4 lr[3];   // rows of L_J read two steps ahead
+        lr[15 % 3] = *reinterpret_cast<const f32x4 *>(lf + 15 * 16);
+        lr[14 % 3] = *reinterpret_cast<const f32x4 *>(lf + 14 * 16);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) db[(g4 + r) * NBP + col] = bf(Di[r]);
+        for (int k = 15; k > 0; --k) {
+            if (k > 2) lr[(k - 2) % 3] = *reinterpret_cast<const f32x4 *>(lf + (k - 2) * 16);
+            const float x = dq[k & 3];
+            const int hk = k >> 2;
+            const float dk = hk == 0 ? quad_bcast<0x00>(x) : hk == 1 ? quad_bcast<0x55>(x)
+                           : hk == 2 ? quad_bcast<0xAA>(x) : quad_bcast<0xFF>(x);
+            dq -= dk * lr[k % 3];
+        }
+        put2(DB[J] + r * NBP + 4 * h, pk4(dq));
+        job(12 + J);
     } else {
-        for (int job = wave - 4; job < 16; job += 4) {
-            if (job < 6) {   // Gram blocks (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
-                const int I = (0xFE9 >> (2 * job)) & 3, J = (0x910 >> (2 * job)) & 3;
-                const f32x4 v = tile(true, I, J);
-                uint16_t *nb = reinterpret_cast<uint16_t *>(NB[job]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) nb[(g4 + r) * NBP + col] = bf(-v[r]);
-            } else {         // score tiles on and below the diagonal
-                const int tt = job - 6;
-                const int I = (0xffa94 >> (2 * tt)) & 3, J = (0xe4910 >> (2 * tt)) & 3;
-                const f32x4 v = tile(false, I, J);
-                const int j = 16 * J + col, i0 = 16 * I + g4;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    reinterpret_cast<uint16_t *>(PB)[(i0 + r) * PK + j] = bf((I != J || j <= i0 + r) ? v[r] : 0.f);
-            }
-        }
+        for (int u = 0; u < 3; ++u) job(wave - 4 + 4 * u);
     }
     transpose_x(wave >> 1, 2 * (wave & 1));
     transpose_x(wave >> 1, 2 * (wave & 1) + 1);
