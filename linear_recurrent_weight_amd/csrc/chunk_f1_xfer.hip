@@ -81,7 +81,7 @@ __device__ __forceinline__ float rms_scale(float ss, float eps_rms, int phi_kind
 }
 
 // per-token scalars of a chunk in LDS
-enum { kEta = 0, kB, kBp, kEw, kRs, kQs, kCs, kLg, kNsv };
+enum { kEta = 0, kB, kBp, kEw, kRs, kQs, kCs, kLg, kSx, kSq, kNsv };
 
 // ---------------------------------------------------------------------------
 // f1_xfer: the transfer operators of one chunk
@@ -147,11 +147,11 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
     constexpr int YP = DV + 8;                // bf16 pitch of the value rows
     constexpr int NJ = DV / 16;               // value column tiles
     constexpr int NT = 4 + NJ;                // column tiles of R = [x part | value part]
-    __shared__ __align__(16) bf16_t QB[C * PK];     // qh rows [t][d]
+    __shared__ __align__(16) bf16_t QB[C * PK];     // q rows [t][d] (qh = s_q q)
     __shared__ __align__(16) bf16_t XW[DK * PK];    // (diag(e^{b_C-b_t}) x)^T [d][t]
     __shared__ __align__(16) bf16_t YB[C * YP];     // value rows [t][j]
     __shared__ __align__(16) bf16_t PB[C * PK];     // P [t][s]
-    __shared__ __align__(16) bf16_t XB[C * PK];     // x rows [t][d]
+    __shared__ __align__(16) bf16_t XB[C * PK];     // k_{t-1} rows [t][d] (x = s_x k_{t-1})
     __shared__ __align__(16) bf16_t NB[6][16 * NBP];   // -N below the diagonal blocks
     __shared__ __align__(16) bf16_t DB[4][16 * NBP];   // inverses of the diagonal blocks of I + N
     __shared__ __align__(16) float LF[4 * LFB];         // the strictly lower diagonal blocks L_J, fp32 row-major
@@ -198,56 +198,43 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
     const int t = c * C + row;
     char *rec = static_cast<char *>(a.ops) + (size_t(bh) * nch + c) * f1_xfer_bytes(DV);
 
-    // 1. rows: qh, x = phi(k_{t-1}) (x_0 from the boundary), values; eta and
-    //    log2 gamma.  Rows past the end are zeroed here.
+    // 1. rows: q, k_{t-1} (x_0 from the boundary) and the values go to LDS as
+    //    loaded; the RMS scales of phi (s_x for x = phi(k_{t-1}), s_q for qh)
+    //    go to the scalars and are folded into the per-token factors that
+    //    every later product applies anyway.  eta and log2 gamma.  Rows
+    //    outside the sequence get a zero scale.
     {
-        const uint4 qr = rows.q, kr = rows.k;
+        const uint4 qr = rows.q;
+        uint4 xr = rows.k;
         uint4 vr[Rows::NV];
 #pragma unroll
         for (int i = 0; i < Rows::NV; ++i) vr[i] = rows.v[i];
         const float beta = rows.beta, lam = rows.lam;
         const bool qok = t < T, kok = t >= 1 && t <= T, first = t == 0;
         const uint32_t qw[4] = {qr.x, qr.y, qr.z, qr.w};
-        const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w};
-        float qv[8], xv[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            qv[2 * e] = lo16(qw[e]);
-            qv[2 * e + 1] = hi16(qw[e]);
-            xv[2 * e] = lo16(kw[e]);
-            xv[2 * e + 1] = hi16(kw[e]);
-        }
-        const bool carry_x = first && a.xnext_in;
-        if (carry_x) {   // x_0 continues the previous segment (features already formed)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                xv[e] = rows.xn[0][e];
-                xv[4 + e] = rows.xn[1][e];
-            }
-        }
+        const uint32_t kw[4] = {xr.x, xr.y, xr.z, xr.w};
         float sq = 0.f, sk = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            sq += qv[e] * qv[e];
-            sk += xv[e] * xv[e];
+        for (int e = 0; e < 4; ++e) {
+            const bf16x2_t qe = __builtin_bit_cast(bf16x2_t, qw[e]), ke = __builtin_bit_cast(bf16x2_t, kw[e]);
+            sq = __builtin_amdgcn_fdot2_f32_bf16(qe, qe, sq, false);
+            sk = __builtin_amdgcn_fdot2_f32_bf16(ke, ke, sk, false);
+        }
+        const bool carry_x = first && a.xnext_in;
+        if (carry_x) {   // x_0 continues the previous segment (features already formed, scale 1)
+            sk = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sk += rows.xn[0][e] * rows.xn[0][e] + rows.xn[1][e] * rows.xn[1][e];
+            xr = make_uint4(pk2(rows.xn[0][0], rows.xn[0][1]), pk2(rows.xn[0][2], rows.xn[0][3]),
+                            pk2(rows.xn[1][0], rows.xn[1][1]), pk2(rows.xn[1][2], rows.xn[1][3]));
         }
         sq = group_sum<8>(sq);
         sk = group_sum<8>(sk);
-        // rows outside the sequence (clamped loads) get a zero scale
         const float scq = qok ? rms_scale(sq, a.eps_rms, a.phi) : 0.f;
         const float sck = carry_x ? 1.f : (kok ? rms_scale(sk, a.eps_rms, a.phi) : 0.f);
-        float n2 = 0.f;
-        uint32_t xo[4], qo[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float x0 = xv[2 * e] * sck, x1 = xv[2 * e + 1] * sck;
-            n2 += x0 * x0 + x1 * x1;
-            xo[e] = pk2(x0, x1);
-            qo[e] = pk2(qv[2 * e] * scq, qv[2 * e + 1] * scq);
-        }
-        n2 = group_sum<8>(n2);
-        *reinterpret_cast<uint4 *>(XB + row * PK + 8 * part) = make_uint4(xo[0], xo[1], xo[2], xo[3]);
-        *reinterpret_cast<uint4 *>(QB + row * PK + 8 * part) = make_uint4(qo[0], qo[1], qo[2], qo[3]);
+        const float n2 = sck * sck * sk;   // |x_t|^2
+        *reinterpret_cast<uint4 *>(XB + row * PK + 8 * part) = xr;
+        *reinterpret_cast<uint4 *>(QB + row * PK + 8 * part) = qr;
         if constexpr (VPT >= 8) {
 #pragma unroll
             for (int i = 0; i < Rows::NV; ++i)
@@ -264,6 +251,8 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
             }
             sv[kEta][row] = eta;
             sv[kLg][row] = log2_1m(alpha);
+            sv[kSx][row] = sck;
+            sv[kSq][row] = scq;
         }
         // the next chunk's rows (the last chunk reloads its own), issued once
         // this chunk's are consumed, so that they land in the same registers
@@ -282,13 +271,14 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
         const float bp = b - lg;
         const float bC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b), 63));
         sep = bC >= -100.f;
-        const float eta = sv[kEta][lane];
+        const float eta = sv[kEta][lane], sx = sv[kSx][lane], sq = sv[kSq][lane];
         sv[kB][lane] = b;
         sv[kBp][lane] = bp;
-        sv[kEw][lane] = ex2(bC - b);
-        sv[kRs][lane] = eta * ex2(bp);
-        sv[kQs][lane] = ex2(b);
-        sv[kCs][lane] = sep ? ex2(-b) : 0.f;
+        // with the RMS scales of the rows folded in: x = s_x k_{t-1}, qh = s_q q
+        sv[kEw][lane] = ex2(bC - b) * sx;
+        sv[kRs][lane] = eta * ex2(bp) * sx;
+        sv[kQs][lane] = ex2(b) * sq;
+        sv[kCs][lane] = sep ? ex2(-b) * sx : 0.f;
         if (wave == 0 && lane == 0) *reinterpret_cast<float *>(rec + f1_xfer_scal_off(DV)) = ex2(bC);
     }
     wave_lds_sync();
@@ -336,10 +326,11 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = acc[r] * (ri * cj[r]);
         } else {
-            const float bi = sv[isG ? kBp : kB][i], ei = isG ? sv[kEta][i] : 1.f;
+            const float bi = sv[isG ? kBp : kB][i], ei = (isG ? sv[kEta][i] : 1.f) * sv[isG ? kSx : kSq][i];
             const f32x4 bj = *reinterpret_cast<const f32x4 *>(&sv[kB][j0]);
+            const f32x4 sj = *reinterpret_cast<const f32x4 *>(&sv[kSx][j0]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = acc[r] * ex2(bi - bj[r]) * ei;
+            for (int r = 0; r < 4; ++r) v[r] = acc[r] * ex2(bi - bj[r]) * (ei * sj[r]);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = isG ? -v[r] : ((I != J || j0 + r <= i) ? v[r] : 0.f);
@@ -362,10 +353,11 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1Split
 #pragma unroll
                 for (int r = 0; r < 4; ++r) l[r] = g4 + r < col ? g[r] * (ri * cj[r]) : 0.f;
             } else {
-                const float bpi = sv[kBp][i], ei = sv[kEta][i];
+                const float bpi = sv[kBp][i], ei = sv[kEta][i] * sv[kSx][i];
                 const f32x4 bj = *reinterpret_cast<const f32x4 *>(&sv[kB][j0]);
+                const f32x4 sj = *reinterpret_cast<const f32x4 *>(&sv[kSx][j0]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) l[r] = g4 + r < col ? g[r] * ei * ex2(bpi - bj[r]) : 0.f;
+                for (int r = 0; r < 4; ++r) l[r] = g4 + r < col ? g[r] * ex2(bpi - bj[r]) * (ei * sj[r]) : 0.f;
             }
             *reinterpret_cast<f32x4 *>(&LF[J * LFB + col * 16 + g4]) = l;
         }
