@@ -4,6 +4,9 @@
 
 #include <cstddef>
 #include <cstdlib>
+#include <cstring>
+
+#include "../../include/falcon.h"
 
 namespace falcon {
 
@@ -130,6 +133,28 @@ inline int chunk_a_segment_chunks(long long bh, int nchunks) {
     if (g < 1) g = 1;
     if (g > 32) g = 32;
     return int(g);
+}
+
+// The bf16 Falcon-1A path with every token-contracting operand in registers
+// (chunk_a1.hip): d_k = d_v = 64.  FALCON_A_PATH=generic keeps the general
+// 1A/3A kernels (measurement and cross-checks).
+inline bool chunk_a1_supported(bool bf16, int variant, int window, int dk, int dv) {
+    if (const char *e = std::getenv("FALCON_A_PATH"))
+        if (std::strcmp(e, "generic") == 0) return false;
+    return bf16 && variant == FALCON_V1A && window == 1 && dk == 64 && dv == 64;
+}
+// chunks per segment of that path: the fewest that keep all segments of all
+// heads resident at once (two 512-thread workgroups per compute unit, 256
+// units), so that the walks run as one wave of workgroups
+inline int chunk_a1_segment_chunks(long long bh, int nchunks) {
+    if (const char *e = std::getenv("FALCON_A_SEGMENT")) {   // tuning override: 1..64 chunks
+        const int v = std::atoi(e);
+        if (v >= 1 && v <= 64) return v;
+    }
+    constexpr long long kSlots = 512;
+    for (int g = 1; g < nchunks; ++g)
+        if (bh * ((nchunks + g - 1) / g) <= kSlots) return g;
+    return nchunks > 0 ? nchunks : 1;
 }
 
 }  // namespace falcon

@@ -12,6 +12,7 @@ const char *const kNamesRecurrent[] = {"feature", "recurrent"};
 const char *const kNamesChunkF1[] = {"feature", "chunk_f1_prep", "chunk_f1_scan"};
 const char *const kNamesChunkF1Fused[] = {"chunk_f1_fused"};
 const char *const kNamesChunkA[] = {"a_segment", "a_segscan", "a_output"};
+const char *const kNamesChunkA1[] = {"a1_segment", "a1_segscan", "a1_output"};
 const char *const kNamesChunkF2[] = {"chunk_f2"};
 const char *const kNamesChunkF3[] = {"feature", "f3_prep", "f3_scan"};
 const char *const kNamesChunkF1Split[] = {"f1_ops", "f1_walk"};
@@ -46,7 +47,7 @@ int run(const falcon_fwd_args *args, void *stream, Marks *m) {
             pa.taily_out = p.taily_out;
             launch_passthrough(pa, s, m);
         }
-    } else if (p.path == Path::kChunkA) {
+    } else if (p.path == Path::kChunkA || p.path == Path::kChunkA1) {
         ChunkAArgs ca{};
         ca.variant = p.variant;
         ca.phi = p.phi;
@@ -79,12 +80,16 @@ int run(const falcon_fwd_args *args, void *stream, Marks *m) {
         ca.tailx_out = p.tailx_out;
         ca.taily_out = p.taily_out;
         ca.o = p.o;
-        ca.etaw = p.ws_at<float>(p.off_eta);
-        ca.lg = p.ws_at<float>(p.off_alpha);
         ca.Dseg = p.ws_at<float>(p.off_chunk);
         ca.Gseg = p.ws_at<float>(p.off_seg_g);
         ca.Sseg = p.ws_at<float>(p.off_seg_s);
-        launch_chunk_a(ca, p.dtype == FALCON_BF16, s, m);
+        if (p.path == Path::kChunkA1) {
+            launch_chunk_a1(ca, s, m);
+        } else {
+            ca.etaw = p.ws_at<float>(p.off_eta);
+            ca.lg = p.ws_at<float>(p.off_alpha);
+            launch_chunk_a(ca, p.dtype == FALCON_BF16, s, m);
+        }
     } else if (p.path == Path::kChunkF2) {
         ChunkF2Args fa{};
         fa.BH = p.BH;
@@ -284,6 +289,7 @@ extern "C" const char *falcon_kernel_name(const falcon_fwd_args *args, int i) {
         case Path::kChunkF1: return i < 3 ? kNamesChunkF1[i] : nullptr;
         case Path::kChunkF1Fused: return i < 1 ? kNamesChunkF1Fused[i] : nullptr;
         case Path::kChunkA: return i < 3 ? kNamesChunkA[i] : nullptr;
+        case Path::kChunkA1: return i < 3 ? kNamesChunkA1[i] : nullptr;
         case Path::kChunkF2: return i < 1 ? kNamesChunkF2[i] : nullptr;
         case Path::kChunkF3: return i < 3 ? kNamesChunkF3[i] : nullptr;
         case Path::kChunkF1Split: return i < 2 ? kNamesChunkF1Split[i] : nullptr;

@@ -128,6 +128,8 @@ void launch_recurrent(const RecurrentArgs &a, bool io_bf16, hipStream_t s, Marks
 void launch_chunk_f1(const ChunkF1Args &a, bool bf16, hipStream_t s, Marks *m);
 void launch_chunk_f1_fused(const F1FusedArgs &a, int ds, hipStream_t s, Marks *m);
 void launch_chunk_a(const ChunkAArgs &a, bool bf16, hipStream_t s, Marks *m);
+// bf16 Falcon-1A with d_k = d_v = 64 (etaw and lg unused)
+void launch_chunk_a1(const ChunkAArgs &a, hipStream_t s, Marks *m);
 void launch_chunk_f2(const ChunkF2Args &a, bool bf16, hipStream_t s, Marks *m);
 void launch_chunk_f3(const ChunkF3Args &a, bool bf16, hipStream_t s, Marks *m);
 void launch_chunk_f1_split(const F1SplitArgs &a, int ds, hipStream_t s, Marks *m);

@@ -91,6 +91,8 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
             p->path = Path::kChunkF2;
         } else if (var == FALCON_V3 && chunk_f3_supported(a->dk, a->dv)) {
             p->path = Path::kChunkF3;
+        } else if (chunk_a1_supported(a->dtype == FALCON_BF16, var, a->window, a->dk, a->dv)) {
+            p->path = Path::kChunkA1;
         } else if ((var == FALCON_V1A || var == FALCON_V3A) && chunk_a_supported(a->dk, a->dv)) {
             p->path = Path::kChunkA;
         } else {
@@ -131,6 +133,14 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
         p->nchunks = (T + kChunk - 1) / kChunk;
         p->off_chunk = off;
         off = align_up(off + static_cast<size_t>(bh) * p->nchunks * f1_xfer_bytes(a->dv));
+    } else if (p->path == Path::kChunkA1) {
+        p->nchunks = (T + kChunk - 1) / kChunk;
+        p->seg_chunks = chunk_a1_segment_chunks(bh, p->nchunks);
+        p->nseg = (p->nchunks + p->seg_chunks - 1) / p->seg_chunks;
+        const size_t st = static_cast<size_t>(bh) * p->nseg * a->dk * a->dv * 4;
+        p->off_chunk = off; off = align_up(off + st);           // segment writes [d][j]
+        p->off_seg_g = off; off = align_up(off + static_cast<size_t>(bh) * p->nseg * 4);
+        p->off_seg_s = off; off = align_up(off + st);           // segment entry states [d][j]
     } else if (p->path == Path::kChunkA) {
         p->nchunks = (T + kChunk - 1) / kChunk;
         p->Tpad = p->nchunks * kChunk;

@@ -331,6 +331,94 @@ def test_chunk_a_strong_ridge_clamp():
     assert eo <= 1e-5 and es <= 1e-5, (eo, es)
 
 
+# -- bf16 Falcon-1A kernels for d_k = d_v = 64 (register operands) ------------
+
+A_PATHS = ["a1", "generic"]
+
+
+def _a_path(monkeypatch, path):
+    if path == "generic":
+        monkeypatch.setenv("FALCON_A_PATH", "generic")
+    else:
+        monkeypatch.delenv("FALCON_A_PATH", raising=False)
+
+
+@pytest.mark.parametrize("path", A_PATHS)
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 200, 1000])
+def test_chunk_a1_bf16_lengths(monkeypatch, path, T):
+    _a_path(monkeypatch, path)
+    check(gu.small("F1A", "bf16", B=2, H=3, T=T, dk=64, dv=64, chunk=64, seed=T + 7))
+
+
+@pytest.mark.parametrize("seg", ["1", "2", "5", "16", "64"])
+def test_chunk_a1_bf16_segments(monkeypatch, seg):
+    """Chunks per segment do not change the result."""
+    _a_path(monkeypatch, "a1")
+    monkeypatch.setenv("FALCON_A_SEGMENT", seg)
+    check(gu.small("F1A", "bf16", B=1, H=3, T=1300, dk=64, dv=64, chunk=64, seed=17))
+
+
+@pytest.mark.parametrize("split", [0, 3, 64, 100])
+def test_chunk_a1_bf16_continuation(monkeypatch, split):
+    """Two calls carrying (S, x_next) match the oracle run of the whole
+    sequence."""
+    import torch
+    _a_path(monkeypatch, "a1")
+    w = gu.small("F1A", "bf16", B=2, H=3, T=300, dk=64, dv=64, chunk=64, seed=19)
+    inp = gu.make(w)
+    dev = gu.to_device(inp, w)
+    a = {k: v[:, :, :split].contiguous() for k, v in dev.items()}
+    b = {k: v[:, :, split:].contiguous() for k, v in dev.items()}
+    o1, st1 = gu.run_gpu(w.with_(seqlen=split), a)
+    o2, st2 = gu.run_gpu(w.with_(seqlen=300 - split), b, state=st1)
+    heads = np.arange(6)
+    o_ref, st_ref = gu.oracle_heads(w, inp, heads)
+    eo, es = gu.compare(w, heads, torch.cat([o1, o2], 2), st2, o_ref, st_ref)
+    assert eo <= gu.TOL_BF16 and es <= gu.TOL_BF16, (eo, es)
+    assert torch.allclose(st2.x_next, torch.from_numpy(st_ref.x_next.reshape(2, 3, 64)).float().cuda(),
+                          rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("eps_gamma", [1e-3, 5e-2])
+def test_chunk_a1_bf16_strong_decay(monkeypatch, eps_gamma):
+    """Large ridge weights: chunks decay far below 2^-100, so the scores take
+    the pairwise decays instead of the separable ones."""
+    _a_path(monkeypatch, "a1")
+    w = gu.small("F1A", "bf16", B=1, H=3, T=300, dk=64, dv=64, chunk=64, seed=23).with_(
+        lam_lo=500.0, lam_hi=2000.0, eps_gamma=eps_gamma)
+    check(w)
+
+
+def test_chunk_a1_bf16_agrees_with_generic(monkeypatch):
+    """The register-operand kernels and the general 1A/3A kernels compute the
+    same algebra; on c3-shaped input they agree to bf16 rounding."""
+    w = WORKLOADS["c3"].with_(batch=1, heads=3, seqlen=4096)
+    inp = gu.make(w)
+    dev = gu.to_device(inp, w)
+    _a_path(monkeypatch, "generic")
+    o_g, st_g = gu.run_gpu(w, dev)
+    _a_path(monkeypatch, "a1")
+    o_a, st_a = gu.run_gpu(w, dev)
+    assert gu.max_rel_err(o_a.double().cpu().numpy(), o_g.double().cpu().numpy()) <= 2e-2
+    assert gu.max_rel_err(st_a.S.double().cpu().numpy(), st_g.S.double().cpu().numpy()) <= 2e-2
+
+
+def test_chunk_a1_bf16_identity_features(monkeypatch):
+    """phi = identity (no RMS scale): the unnormalised keys go straight into
+    the step and the writes."""
+    _a_path(monkeypatch, "a1")
+    w = gu.small("F1A", "bf16", B=1, H=2, T=150, dk=64, dv=64, chunk=64, seed=5)
+    inp = gu.make(w)
+    dev = gu.to_device(inp, w)
+    from linear_recurrent_weight_amd import falcon as fb
+    import oracle
+    o, st = fb.fwd(dev["q"], dev["k"], dev["v"], dev["beta"], dev["lam"], variant="F1A",
+                   chunk=64, phi="identity")
+    o_ref, st_ref = oracle.falcon_forward("F1A", inp["q"], inp["k"], inp["v"], inp["beta"],
+                                          inp["lam"], phi_kind=oracle.PHI_IDENTITY)
+    assert gu.max_rel_err(o.double().cpu().numpy(), o_ref) <= gu.TOL_BF16
+
+
 # -- Falcon-2 chunk path -------------------------------------------------------
 
 def test_named_workload_c4_chunk_f2():
