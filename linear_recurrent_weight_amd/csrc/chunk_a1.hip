@@ -87,14 +87,24 @@ struct A1Rows {
 // aggregate write of the segment (a1_segment); OUT = true: the outputs, from
 // the segment's entry state (a1_output).
 //
-// Wave w owns the value column tile jt = w % 4 and
-//   - the state tiles (d tile dt, jt) for dt = 2 (w / 4), + 1 (fp32
-//     accumulators, S[d][j] layout);
-//   - (OUT) the output tiles O^T (jt, token tile n) for n in {0, 3} (w < 4)
-//     or {1, 2}: five score tiles per wave either way.
+// Per chunk, after the rows and the step scalars:
+//   - every wave transposes four 16 x 16 blocks on MFMA into LDS: key blocks
+//     scaled by the write coefficients, XT[d][s] = coef_s x_s[d] / s_x, and
+//     value blocks VT[j][s]; each block once per chunk;
+//   - wave w updates the state tiles (d tiles 2 (w / 4), + 1; value tile
+//     w % 4), S[d][j] += XT V by token-contracting 16x16x32 MFMAs from LDS,
+//     and (a1_output) writes them to the bf16 copy S^T[j][d] that the next
+//     chunk's outputs read (double-buffered by chunk parity);
+//   - (a1_output) wave w forms the outputs of token tile n = 0, 0, 1, 1, 3,
+//     3, 2, 2 (w = 0..7) and value tiles 2 (w % 2), + 1: the causal score
+//     tiles P^T (s tile m <= n) once, kept as B operands, then
+//     O^T (jt, n) = diag-scaled S^T Qh^T + V^T P^T.  Waves w and w + 4 share
+//     a SIMD and hold token tiles n and 3 - n: five score tiles per SIMD.
 template <bool OUT>
 __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf16_t *QB, bf16_t *XB, bf16_t *VB,
-                                        bf16_t *STb, float (*sv)[C], bf16x8 (*IDT)[64]) {
+                                        bf16_t *XT, bf16_t *VT, bf16_t *STb, float (*sv)[C],
+                                        bf16x8 (*IDT)[64]) {
+    constexpr int NS = 2;             // state tiles per wave
     const int T = a.T;
     const int c_begin = seg * a.seg_chunks;
     const int c_end = min(a.nchunks, c_begin + a.seg_chunks);
@@ -102,32 +112,38 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, g4 = 4 * (lane >> 4), k8 = 8 * (lane >> 4);
     const int row = tid >> 3, part = tid & 7;
-    const int jt = wave & 3, pr = wave >> 2;
+    const int sj = wave & 3;                 // value tile of the state tiles
+    const int sd0 = 2 * (wave >> 2);         // first d tile of the state tiles
 
-    // rows (pitch ld) 16 m .. + 15 of a tile, columns 16 n .. + 15, in the
-    // accumulator layout: lane holds rows 16 m + g4 .. + 3 of column 16 n + col
+    // rows 16 m .. + 15 of a row-major LDS tile (pitch PK), columns
+    // 16 n .. + 15, in the accumulator layout: lane holds rows 16 m + g4 .. + 3
+    // of column 16 n + col
     auto transposed = [&](const bf16_t *rows, int m, int n) {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         return mfma32(ld8(rows + (16 * m + col) * PK + 32 * (n >> 1) + k8), IDT[n & 1][lane], z);
     };
 
-    f32x4 S[2];   // state tiles (2 pr + h, jt)
-    bf16_t *og = static_cast<bf16_t *>(a.o) + size_t(bh) * T * D + 16 * jt + g4;
-    if constexpr (OUT) {
-        const float *Se = a.Sseg + (size_t(bh) * a.nseg + seg) * D * D;
+    f32x4 S[NS];
+    {
+        if constexpr (OUT) {
+            const float *Se = a.Sseg + (size_t(bh) * a.nseg + seg) * D * D;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int dt = 2 * pr + h;
+            for (int h = 0; h < NS; ++h) {
+                const int dt = sd0 + h;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) S[h][r] = Se[(16 * dt + g4 + r) * D + 16 * jt + col];
-            // bf16 copy S^T [j][d] for the output products (buffer 0 of two)
-            *reinterpret_cast<uint2 *>(STb + (16 * jt + col) * PK + 16 * dt + g4) = pk4(S[h]);
+                for (int r = 0; r < 4; ++r) S[h][r] = Se[(16 * dt + g4 + r) * D + 16 * sj + col];
+                // bf16 copy S^T [j][d] for the output products (buffer 0 of two)
+                *reinterpret_cast<uint2 *>(STb + (16 * sj + col) * PK + 16 * dt + g4) = pk4(S[h]);
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < NS; ++h) S[h] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-    } else {
-        S[0] = S[1] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     float bsum = 0.f;   // log2 of the segment's carry
 
+    // one chunk step; the rows of chunk c + 1 go into `rows` once chunk c's
+    // are consumed
     A1Rows<OUT> rows;
     rows.load(a, c_begin, bh, row, part);
     for (int c = c_begin; c < c_end; ++c) {
@@ -200,94 +216,108 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
             if constexpr (OUT) {
                 const float sq = sv[kSq][lane];
                 sv[kQg][lane] = ex2(b) * sq;                         // e^{b_i} s_q
-                sv[kCs][lane] = sep ? ex2(-b) * eta * sx : 0.f;      // e^{-b_j} eta_j s_x
+                sv[kCs][lane] = (sep ? ex2(-b) : 1.f) * eta * sx;    // (e^{-b_j}) eta_j s_x
                 sv[kB][lane] = b;
             }
         }
         wave_lds_sync();
         bsum += bC;
 
-        // 3. value blocks (m, jt) in the accumulator layout: as the A operand
-        //    the block V^T (jt, m); scaled by the write coefficients, the B
-        //    operand (diag(coef) V) (m, jt)
-        s16x4 vt[4], vw[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const f32x4 vb = transposed(VB, m, jt);
+        // 3. transposes, once per block: wave w takes token block m = w / 2
+        //    and the d / value tiles 2 (w % 2), + 1
+        {
+            const int m = wave >> 1;
             const f32x4 cf = *reinterpret_cast<const f32x4 *>(&sv[kCoef][16 * m + g4]);
-            vw[m] = pk4s(vb * cf);
-            if constexpr (OUT) vt[m] = pk4s(vb);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int n = 2 * (wave & 1) + e;
+                const f32x4 xb = transposed(XB, m, n) * cf;
+                const f32x4 vb = transposed(VB, m, n);
+                *reinterpret_cast<uint2 *>(XT + (16 * n + col) * PK + 16 * m + g4) = pk4(xb);
+                *reinterpret_cast<uint2 *>(VT + (16 * n + col) * PK + 16 * m + g4) = pk4(vb);
+            }
         }
+        __syncthreads();
 
-        // 4. state tiles: S = e^{b_C} S + X^T diag(coef) V, X^T (dt, m) from
-        //    the key rows in the accumulator layout read as the A operand
-        const float gC = ex2(bC);
+        {
+            // 4. state tiles: S = e^{b_C} S + X^T diag(coef) V
+            const float gC = ex2(bC);
+            const bf16_t *vr = VT + (16 * sj + col) * PK + k8;
+            const bf16x8 v0 = ld8(vr), v1 = ld8(vr + 32);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int dt = 2 * pr + h;
-            f32x4 s = S[h] * gC;
+            for (int h = 0; h < NS; ++h) {
+                const bf16_t *xr = XT + (16 * (sd0 + h) + col) * PK + k8;
+                f32x4 s = S[h] * gC;
+                s = mfma32(ld8(xr), v0, s);
+                S[h] = mfma32(ld8(xr + 32), v1, s);
+            }
+            if constexpr (OUT) {
+                // the next chunk's S^T copy goes to the other buffer: its last
+                // reads were before the previous chunk's closing barrier
+                bf16_t *stn = STb + ((c + 1 - c_begin) & 1) * (D * PK);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) s = mfma16(pk4s(transposed(XB, m, dt)), vw[m], s);
-            S[h] = s;
+                for (int h = 0; h < NS; ++h)
+                    *reinterpret_cast<uint2 *>(stn + (16 * sj + col) * PK + 16 * (sd0 + h) + g4) = pk4(S[h]);
+            }
         }
         if constexpr (OUT) {
-            // the next chunk's S^T copy goes to the other buffer: its last
-            // reads were before the previous chunk's closing barrier
-            bf16_t *stn = STb + ((c + 1 - c_begin) & 1) * (D * PK);
+            // 5. outputs O^T (jt, n) = diag-scaled S^T Qh^T + V^T P^T, from the
+            //    entry state's copy
+            const bf16_t *stc = STb + ((c - c_begin) & 1) * (D * PK);
+            bf16_t *og = static_cast<bf16_t *>(a.o) + size_t(bh) * T * D + g4;
+            const int n = wave < 4 ? wave >> 1 : 3 - ((wave - 4) >> 1);
+            const int tq = 16 * n + col;   // this lane's token
+            const bf16_t *qr = QB + tq * PK + k8;
+            const bf16x8 q0 = ld8(qr), q1 = ld8(qr + 32);
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            const float qg = sv[kQg][tq];
+            // separable decays: e^{-b_s} eta_s s_x times e^{b_t} s_q; else
+            // e^{b_t - b_s} times eta_s s_x times s_q
+            const float bq = sep ? 0.f : sv[kB][tq], qf = sep ? qg : sv[kSq][tq];
+            // score tiles P^T (m, n): lane holds x_s . q_t at s = 16 m + g4 + r, t = tq
+            s16x4 pt[4];
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-                *reinterpret_cast<uint2 *>(stn + (16 * jt + col) * PK + 16 * (2 * pr + h) + g4) = pk4(S[h]);
-        }
-        // 5. outputs O^T (jt, n) = diag-scaled S^T Qh^T + V^T P^T, from the
-        //    entry state's copy
-        if constexpr (OUT) {
-#pragma unroll 1
-            for (int u = 0; u < 2; ++u) {
-                const int n = pr == 0 ? (u == 0 ? 0 : 3) : (u == 0 ? 1 : 2);
-                const int tq = 16 * n + col;   // this lane's token
-                const bf16_t *qr = QB + tq * PK + k8;
-                const bf16_t *sr = STb + ((c - c_begin) & 1) * (D * PK) + (16 * jt + col) * PK + k8;
-                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                f32x4 o = mfma32(ld8(sr), ld8(qr), z);
-                o = mfma32(ld8(sr + 32), ld8(qr + 32), o);
-                o *= sv[kQg][tq];
-                const float bq = sv[kB][tq], sqq = sv[kSq][tq];
+            for (int m = 0; m < 4; ++m) {
+                if (m > n) break;
+                const bf16_t *xr = XB + (16 * m + col) * PK + k8;
+                f32x4 p = mfma32(ld8(xr), q0, z);
+                p = mfma32(ld8(xr + 32), q1, p);
+                const f32x4 cs = *reinterpret_cast<const f32x4 *>(&sv[kCs][16 * m + g4]);
+                const f32x4 bs = *reinterpret_cast<const f32x4 *>(&sv[kB][16 * m + g4]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float f = (sep ? 1.f : ex2(bq - bs[r])) * cs[r] * qf;
+                    p[r] = (m < n || g4 + r <= col) ? p[r] * f : 0.f;
+                }
+                pt[m] = pk4s(p);
+            }
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int jt = 2 * (wave & 1) + e;
+                const bf16_t *sr = stc + (16 * jt + col) * PK + k8;
+                f32x4 o = mfma32(ld8(sr), q0, z);
+                o = mfma32(ld8(sr + 32), q1, o);
+                o *= qg;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     if (m > n) break;
-                    // score tile P^T (m, n): lane holds x_s . q_t at s = 16 m + g4 + r, t = tq
-                    const bf16_t *xr = XB + (16 * m + col) * PK + k8;
-                    f32x4 p = mfma32(ld8(xr), ld8(qr), z);
-                    p = mfma32(ld8(xr + 32), ld8(qr + 32), p);
-                    f32x4 f;
-                    if (sep) {
-                        const f32x4 cs = *reinterpret_cast<const f32x4 *>(&sv[kCs][16 * m + g4]);
-                        f = cs * sv[kQg][tq];
-                    } else {
-                        const f32x4 bs = *reinterpret_cast<const f32x4 *>(&sv[kB][16 * m + g4]);
-                        const f32x4 es = *reinterpret_cast<const f32x4 *>(&sv[kEta][16 * m + g4]);
-                        const f32x4 xs = *reinterpret_cast<const f32x4 *>(&sv[kSx][16 * m + g4]);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) f[r] = ex2(bq - bs[r]) * es[r] * xs[r] * sqq;
-                    }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) p[r] = (m < n || g4 + r <= col) ? p[r] * f[r] : 0.f;
-                    o = mfma16(vt[m], pk4s(p), o);
+                    const s16x4 va = __builtin_bit_cast(
+                        s16x4, *reinterpret_cast<const uint2 *>(VT + (16 * jt + col) * PK + 16 * m + g4));
+                    o = mfma16(va, pt[m], o);
                 }
-                if (c0 + tq < T) *reinterpret_cast<uint2 *>(og + size_t(c0 + tq) * D) = pk4(o);
+                if (c0 + tq < T) *reinterpret_cast<uint2 *>(og + size_t(c0 + tq) * D + 16 * jt) = pk4(o);
             }
         }
-
-        __syncthreads();   // the next chunk overwrites the rows and scalars
+        __syncthreads();   // the next chunk overwrites the rows, transposes and scalars
     }
 
     if constexpr (!OUT) {
         // segment aggregate D_g (fp32, [d][j]) and its carry
         float *Dg = a.Dseg + (size_t(bh) * a.nseg + seg) * D * D;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < NS; ++h)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Dg[(16 * (2 * pr + h) + g4 + r) * D + 16 * jt + col] = S[h][r];
+            for (int r = 0; r < 4; ++r) Dg[(16 * (sd0 + h) + g4 + r) * D + 16 * sj + col] = S[h][r];
         if (tid == 0) a.Gseg[size_t(bh) * a.nseg + seg] = ex2(bsum);
         // x for the next segment, phi(k_{T-1}), from the segment holding the last token
         if (c_end == a.nchunks && wave == 0 && a.xnext_out) {
@@ -315,28 +345,33 @@ __device__ __forceinline__ void init_pickers(bf16x8 (*IDT)[64]) {
 __global__ __launch_bounds__(NTH, 4) void a1_segment(ChunkAArgs a) {
     __shared__ __align__(16) bf16_t XB[C * PK];
     __shared__ __align__(16) bf16_t VB[C * PK];
+    __shared__ __align__(16) bf16_t XT[D * PK];
+    __shared__ __align__(16) bf16_t VT[D * PK];
     __shared__ __align__(16) float sv[kNsv][C];
     __shared__ __align__(16) bf16x8 IDT[2][64];
     init_pickers(IDT);
     __syncthreads();
-    a1_walk<false>(a, blockIdx.x, blockIdx.y, nullptr, XB, VB, nullptr, sv, IDT);
+    a1_walk<false>(a, blockIdx.x, blockIdx.y, nullptr, XB, VB, XT, VT, nullptr, sv, IDT);
 }
 
 __global__ __launch_bounds__(NTH, 4) void a1_output(ChunkAArgs a) {
     __shared__ __align__(16) bf16_t QB[C * PK];
     __shared__ __align__(16) bf16_t XB[C * PK];
     __shared__ __align__(16) bf16_t VB[C * PK];
+    __shared__ __align__(16) bf16_t XT[D * PK];
+    __shared__ __align__(16) bf16_t VT[D * PK];
     __shared__ __align__(16) bf16_t STb[2 * D * PK];
     __shared__ __align__(16) float sv[kNsv][C];
     __shared__ __align__(16) bf16x8 IDT[2][64];
     init_pickers(IDT);
     // (the entry state's bf16 copy is written inside the walk; the first
-    // barrier of the walk orders it before its first read)
-    a1_walk<true>(a, blockIdx.x, blockIdx.y, QB, XB, VB, STb, sv, IDT);
+    // barrier of the walk orders it and the pickers before their first reads)
+    a1_walk<true>(a, blockIdx.x, blockIdx.y, QB, XB, VB, XT, VT, STb, sv, IDT);
 }
 
 // entry state of every segment: S_{g+1} = Gamma_g S_g + D_g (one thread per
-// state entry; the segment writes are loaded eight at a time)
+// state entry; the segment writes are loaded 32 at a time, so that one
+// memory latency covers a whole head at the usual segment counts)
 __global__ __launch_bounds__(256) void a1_segscan(ChunkAArgs a) {
     const int bh = blockIdx.x;
     const int e = blockIdx.y * 256 + threadIdx.x;   // d * 64 + j
@@ -347,16 +382,17 @@ __global__ __launch_bounds__(256) void a1_segscan(ChunkAArgs a) {
     float *Se = a.Sseg + size_t(bh) * a.nseg * stride + e;
     const float *Gg = a.Gseg + size_t(bh) * a.nseg;
     const int nseg = a.nseg;
-    for (int g0 = 0; g0 < nseg; g0 += 8) {
-        float dv[8], gv[8];
+    constexpr int NB = 32;
+    for (int g0 = 0; g0 < nseg; g0 += NB) {
+        float dv[NB], gv[NB];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < NB; ++u) {
             const int g = g0 + u < nseg ? g0 + u : nseg - 1;
             dv[u] = Dg[g * stride];
             gv[u] = Gg[g];
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < NB; ++u) {
             if (g0 + u < nseg) {
                 Se[(g0 + u) * stride] = S;
                 S = gv[u] * S + dv[u];
