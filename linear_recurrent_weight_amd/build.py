@@ -73,7 +73,8 @@ KERNEL_SOURCES = {"passthrough": "feature.hip", "feature": "feature.hip", "recur
                   "f1_ops": "chunk_f1_split.hip", "f1_walk": "chunk_f1_split.hip",
                   "f1_xfer": "chunk_f1_xfer.hip", "f1_carry": "chunk_f1_xfer.hip",
                   "a_segment": "chunk_a.hip", "a_segscan": "chunk_a.hip", "a_output": "chunk_a.hip",
-                  "a1_segment": "chunk_a1.hip", "a1_segscan": "chunk_a1.hip", "a1_output": "chunk_a1.hip"}
+                  "a1_segment": "chunk_a1.hip", "a1_segscan": "chunk_a1.hip", "a1_output": "chunk_a1.hip",
+                  "a3_window": "chunk_a1.hip"}
 
 
 def sources_digest(kernels=None) -> str:

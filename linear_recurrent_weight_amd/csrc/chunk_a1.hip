@@ -1,25 +1,43 @@
-// Chunk-parallel Falcon-1A forward for bf16 inputs with d_k = d_v = 64
-// (summary §4.3, §4.6 "Parallel (Attention) Form of Mini-batch Inner Product
-// Update", §D.1 "Mask Identities and Chunk-Local Evaluation").
+// Chunk-parallel Falcon-1A and Falcon-3A forward for bf16 inputs with
+// d_k = d_v = 64 (summary §4.3, §4.5, §4.6 "Parallel (Attention) Form of
+// Mini-batch Inner Product Update", §D.1 "Mask Identities and Chunk-Local
+// Evaluation"; Falcon-1A is the window-1 case).
 //
-// Per token the write is  S_t = gamma_t S_{t-1} + eta_t x_t y_t^T  and the read
+// Per token s the write is  S_s = gamma_s S_{s-1} + w_s sum_{j in I_s} x_j y_j^T,
+// w_s = eta_s / B_s, I_s the last B_s = min(W, #pairs) pairs, and the read is
 // o_t = S_t^T qh_t.  Within a chunk of 64 tokens, with the chunk-local
 // log-prefix b (restarted at 0 in every chunk),
-//     o_i = e^{b_i} S_0^T qh_i + sum_{j <= i} e^{b_i - b_j} eta_j (qh_i . x_j) y_j,
-//     S_C = e^{b_C} S_0 + sum_j e^{b_C - b_j} eta_j x_j y_j^T.
+//     o_t = e^{b_t} S_0^T qh_t + sum_j M_tj (qh_t . x_j) y_j,
+//     S_C = e^{b_C} S_0 + sum_j M_{63,j} x_j y_j^T,
+//     M_tj = sum_{s = max(j,0)}^{min(t, j+W-1)} e^{b_t - b_s} w_s,
+// where j runs over the W - 1 pairs before the chunk (the halo) and the
+// chunk's own pairs.  With c'_j = M_{hi_j, j}, hi_j = min(j + W - 1, 63) (a
+// sum of at most W terms, every factor <= 1):
+//   - past the window, t >= j + W - 1:  M_tj = e^{b_t - b_{hi_j}} c'_j, which
+//     separates into a token factor e^{b_t} and a pair factor e^{-b_{hi_j}} c'_j
+//     while e^{-b} stays in range (chunk decay above 2^-100), and is formed
+//     pairwise otherwise;
+//   - in the band j <= t < j + W - 1 (at most W - 1 pairs per token): the sum
+//     itself, at most W - 1 terms;
+//   - the chunk write coefficient: M_{63,j} = e^{b_63 - b_{hi_j}} c'_j.
+//
 // A head's sequence is cut into segments of G chunks:
+//   a3_window  (Falcon-3A only, one wave per chunk): the window statistic
+//       mu_t = lambda_max(window Gram) / B_t from the banded pair Gram (MFMA)
+//       and the step scalars w_t, log2 gamma_t of every token;
 //   a1_segment (parallel over segments): the segment's aggregate write
-//       D_g = sum over its chunks c of e^{b_end - b_end(c)} dS_c and its carry;
+//       D_g = sum over its chunks c of e^{b_end - b_end(c)} dS_c and its carry,
+//       and the boundary state (x_next, the last W - 1 pairs);
 //   a1_segscan (parallel over state entries): S_{g+1} = Gamma_g S_g + D_g;
 //   a1_output  (parallel over segments): walks the segment's chunks from its
 //       entry state and writes o.
 // Both walking kernels put the raw rows (q, k_{t-1}, v) into LDS as loaded and
-// fold the RMS scales of phi into per-token factors (x = s_x k_{t-1},
-// qh = s_q q).  Every operand that runs over tokens comes from registers: a
-// 16 x 16 block of a row-major LDS tile, multiplied on MFMA by a 0/1 column
-// picker, lands in the accumulator layout (lane holds 4 consecutive rows of
-// one column).  That is the B operand of the 16x16x16 MFMA as it stands, and
-// the block transposed when read as its A operand.
+// fold the RMS scales of phi into per-token and per-pair factors (x = s_x
+// k_{t-1}, qh = s_q q).  Every operand that runs over tokens comes from a
+// transposed copy: a 16 x 16 block of a row-major LDS tile, multiplied on
+// MFMA by a 0/1 column picker, lands in the accumulator layout (lane holds 4
+// consecutive rows of one column), which is written to LDS with one 8-byte
+// store per lane, once per block.
 #include "chunk_layout.h"
 #include "kernels.h"
 #include "mma.h"
@@ -32,6 +50,17 @@ constexpr int D = 64;           // d_k = d_v
 constexpr int PK = 72;          // bf16 pitch of LDS rows of 64 elements (144 bytes)
 constexpr int NTH = 512;        // 8 waves
 
+// pair rows of a chunk: WIN adds a 16-row halo tile in front (pair row of
+// the chunk's first token OFF = 16; the halo pairs sit in rows 16 - (W - 1)
+// .. 15, rows below are zero)
+template <bool WIN>
+struct Geo {
+    static constexpr int OFF = WIN ? 16 : 0;
+    static constexpr int NP = OFF + C;      // pair rows
+    static constexpr int NMT = NP / 16;     // pair tiles
+    static constexpr int PX = NP + 8;       // bf16 pitch of the transposed rows [d or j][pair]
+};
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -42,6 +71,9 @@ __device__ __forceinline__ uint32_t pk2(float lo, float hi) {
 }
 __device__ __forceinline__ uint2 pk4(const f32x4 &v) { return make_uint2(pk2(v[0], v[1]), pk2(v[2], v[3])); }
 __device__ __forceinline__ s16x4 pk4s(const f32x4 &v) { return __builtin_bit_cast(s16x4, pk4(v)); }
+__device__ __forceinline__ uint4 pk8(const f32x4 &a, const f32x4 &b) {
+    return make_uint4(pk2(a[0], a[1]), pk2(a[2], a[3]), pk2(b[0], b[1]), pk2(b[2], b[3]));
+}
 __device__ __forceinline__ f32x4 mfma32(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -50,7 +82,21 @@ __device__ __forceinline__ f32x4 mfma16(const s16x4 &a, const s16x4 &b, const f3
 }
 template <class P>
 __device__ __forceinline__ bf16x8 ld8(const P *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+template <class P>
+__device__ __forceinline__ s16x4 ld4(const P *p) { return __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2 *>(p)); }
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// sum of squares of 8 bf16 values (one 16-byte piece of a row)
+__device__ __forceinline__ float sumsq8(const uint4 &u) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const bf16x2_t h = __builtin_bit_cast(bf16x2_t, w[e]);
+        s = __builtin_amdgcn_fdot2_f32_bf16(h, h, s, false);
+    }
+    return s;
+}
 
 // phi's RMS scale 1 / sqrt(mean(z^2) + eps_rms) (0 when that is 0) from the
 // sum of squares over 64 elements; the features are rounded to bf16 next
@@ -60,52 +106,112 @@ __device__ __forceinline__ float a1_rms_scale(float ss, float eps_rms, int phi_k
     return ms > 0.f ? __builtin_amdgcn_rsqf(ms) : 0.f;
 }
 
-// per-token scalars of a chunk in LDS
-enum { kEta = 0, kLg, kSx, kSq, kCoef, kQg, kCs, kB, kNsv };
+// 8 fp32 features of an incoming boundary row (x_next or a tail pair, phi
+// already applied) -> bf16 piece and its sum of squares
+__device__ __forceinline__ uint4 feat8(const float *src, float &ss) {
+    const f32x4 x0 = reinterpret_cast<const f32x4 *>(src)[0], x1 = reinterpret_cast<const f32x4 *>(src)[1];
+    ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss += x0[e] * x0[e] + x1[e] * x1[e];
+    return pk8(x0, x1);
+}
+
+// A halo pair (position tau < c0, a row of the halo tile) as 8 elements
+// (part `part`) of x and of y, with x's RMS scale: x = phi(k_{tau-1}) of the
+// sequence, the incoming x_next (tau = 0) or an incoming tail pair (tau < 0);
+// pairs that do not exist (before the incoming tail, rows outside the
+// window, the fresh sentinel's x) are zero.  `hk`, `hv` are the raw rows
+// k_{tau-1}, v_tau (loaded clamped).  The 8 lanes of a row take the same
+// branches.
+__device__ __forceinline__ void halo_pair(const ChunkAArgs &a, int bh, int tau, bool in_window, int part,
+                                          const uint4 &hk, const uint4 &hv, uint4 &xr, uint4 &yr, float &sc) {
+    const int H = a.window - 1;
+    const bool exists = in_window && tau >= -a.n_tail_in;
+    float ss = 0.f;
+    bool raw = false;
+    xr = make_uint4(0, 0, 0, 0);
+    yr = make_uint4(0, 0, 0, 0);
+    if (exists && tau >= 1) {
+        xr = hk;
+        ss = sumsq8(hk);
+        raw = true;
+    } else if (exists && tau == 0 && a.xnext_in) {
+        xr = feat8(a.xnext_in + size_t(bh) * D + 8 * part, ss);
+    } else if (exists && tau < 0) {
+        xr = feat8(a.tailx_in + (size_t(bh) * H + H + tau) * D + 8 * part, ss);
+    }
+    if (exists && tau >= 0) {
+        yr = hv;
+    } else if (exists && tau < 0) {
+        float dummy;
+        yr = feat8(a.taily_in + (size_t(bh) * H + H + tau) * D + 8 * part, dummy);
+    }
+    ss = group_sum<8>(ss);
+    const bool xz = !exists || (tau == 0 && !a.xnext_in);
+    sc = xz ? 0.f : (raw ? a1_rms_scale(ss, a.eps_rms, a.phi) : 1.f);
+}
+
+// per-token scalars of a chunk (LDS, [kind][token]) and per-pair scalars
+// ([kind][pair row])
+enum { kW = 0, kLg, kSq, kQg, kB, kNtv };
+enum { pSx = 0, pCoef, pCol, pBh, kNpv };
 
 // The raw rows of one chunk: 8 threads per token row, each with 8 elements of
-// q, of k_{t-1} and of v, and the row's beta and lambda; loaded into registers
-// one chunk ahead, unconditionally from rows clamped into [0, T).
-template <bool WQ>
+// q, of k_{t-1} and of v, and the row's two step inputs (beta and lambda;
+// with a window, w_t and log2 gamma_t from the window pass).  Loaded into
+// registers one chunk ahead, unconditionally from rows clamped into [0, T).
+template <bool WQ, bool WIN>
 struct A1Rows {
     uint4 q, k, v;
-    float beta, lam;
+    float s0, s1;
     __device__ __forceinline__ void load(const ChunkAArgs &a, int c, int bh, int row, int part) {
         const int T = a.T, t = c * C + row;
         const int tq = t < T ? t : T - 1;
         const int tk = t < 1 ? 0 : (t - 1 < T ? t - 1 : T - 1);
         const size_t base = size_t(bh) * T;
+        const bf16_t *kg = static_cast<const bf16_t *>(a.k), *vg = static_cast<const bf16_t *>(a.v);
         if constexpr (WQ) q = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.q) + (base + tq) * D + 8 * part);
-        k = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.k) + (base + tk) * D + 8 * part);
-        v = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.v) + (base + tq) * D + 8 * part);
-        beta = a.beta[base + tq];
-        lam = a.lambda[base + tq];
+        k = *reinterpret_cast<const uint4 *>(kg + (base + tk) * D + 8 * part);
+        v = *reinterpret_cast<const uint4 *>(vg + (base + tq) * D + 8 * part);
+        if constexpr (WIN) {
+            s0 = a.etaw[size_t(bh) * a.Tpad + t];
+            s1 = a.lg[size_t(bh) * a.Tpad + t];
+        } else {
+            s0 = a.beta[base + tq];
+            s1 = a.lambda[base + tq];
+        }
     }
 };
 
 // One walk over the chunks [c_begin, c_end) of head bh.  OUT = false: the
 // aggregate write of the segment (a1_segment); OUT = true: the outputs, from
-// the segment's entry state (a1_output).
+// the segment's entry state (a1_output).  WIN: a window of W > 1 pairs.
 //
 // Per chunk, after the rows and the step scalars:
-//   - every wave transposes four 16 x 16 blocks on MFMA into LDS: key blocks
-//     scaled by the write coefficients, XT[d][s] = coef_s x_s[d] / s_x, and
-//     value blocks VT[j][s]; each block once per chunk;
+//   - the pair coefficients: c'_j, the chunk write coefficient and the score
+//     column factor of every pair (every wave forms the same values);
+//   - every wave transposes NMT 16 x 16 blocks on MFMA into LDS: key blocks
+//     scaled by the write coefficients, XT[d][p], and value blocks VT[j][p];
+//     each block once per chunk;
 //   - wave w updates the state tiles (d tiles 2 (w / 4), + 1; value tile
-//     w % 4), S[d][j] += XT V by token-contracting 16x16x32 MFMAs from LDS,
-//     and (a1_output) writes them to the bf16 copy S^T[j][d] that the next
-//     chunk's outputs read (double-buffered by chunk parity);
+//     w % 4), S[d][j] += XT V by pair-contracting MFMAs from LDS, and
+//     (a1_output) writes them to the bf16 copy S^T[j][d] that the next chunk's
+//     outputs read (double-buffered by chunk parity);
 //   - (a1_output) wave w forms the outputs of token tile n = 0, 0, 1, 1, 3,
-//     3, 2, 2 (w = 0..7) and value tiles 2 (w % 2), + 1: the causal score
-//     tiles P^T (s tile m <= n) once, kept as B operands, then
+//     3, 2, 2 (w = 0..7) and value tiles 2 (w % 2), + 1: the score tiles P^T
+//     of the pair tiles up to the diagonal once, kept as B operands, then
 //     O^T (jt, n) = diag-scaled S^T Qh^T + V^T P^T.  Waves w and w + 4 share
-//     a SIMD and hold token tiles n and 3 - n: five score tiles per SIMD.
-template <bool OUT>
+//     a SIMD and hold token tiles n and 3 - n, which balances the score work.
+template <bool OUT, bool WIN>
 __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf16_t *QB, bf16_t *XB, bf16_t *VB,
-                                        bf16_t *XT, bf16_t *VT, bf16_t *STb, float (*sv)[C],
+                                        bf16_t *XH, bf16_t *VH, float (*hsx)[16], bf16_t *XT, bf16_t *VT,
+                                        bf16_t *STb, float (*tv)[C], float (*pv)[Geo<WIN>::NP], float (*bf)[C],
                                         bf16x8 (*IDT)[64]) {
+    using G = Geo<WIN>;
+    constexpr int OFF = G::OFF, NP = G::NP, NMT = G::NMT, PX = G::PX;
     constexpr int NS = 2;             // state tiles per wave
     const int T = a.T;
+    const int H = WIN ? a.window - 1 : 0;
     const int c_begin = seg * a.seg_chunks;
     const int c_end = min(a.nchunks, c_begin + a.seg_chunks);
     const int tid = threadIdx.x, lane = tid & 63;
@@ -115,71 +221,55 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
     const int sj = wave & 3;                 // value tile of the state tiles
     const int sd0 = 2 * (wave >> 2);         // first d tile of the state tiles
 
-    // rows 16 m .. + 15 of a row-major LDS tile (pitch PK), columns
-    // 16 n .. + 15, in the accumulator layout: lane holds rows 16 m + g4 .. + 3
-    // of column 16 n + col
-    auto transposed = [&](const bf16_t *rows, int m, int n) {
+    // a 16-row tile of row-major LDS rows (pitch PK), columns 16 n .. + 15,
+    // in the accumulator layout: lane holds rows g4 .. + 3 of column 16 n + col
+    auto transposed = [&](const bf16_t *tile, int n) {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        return mfma32(ld8(rows + (16 * m + col) * PK + 32 * (n >> 1) + k8), IDT[n & 1][lane], z);
+        return mfma32(ld8(tile + col * PK + 32 * (n >> 1) + k8), IDT[n & 1][lane], z);
+    };
+
+    // first row of pair tile m: the halo tile (WIN, m = 0) of this chunk's
+    // parity, else the token rows
+    auto ptile = [&](const bf16_t *rows, const bf16_t *halo, int m, int par) {
+        if constexpr (WIN) return m == 0 ? halo + par * (16 * PK) : rows + (m - 1) * (16 * PK);
+        return rows + m * (16 * PK);
     };
 
     f32x4 S[NS];
-    {
-        if constexpr (OUT) {
-            const float *Se = a.Sseg + (size_t(bh) * a.nseg + seg) * D * D;
+    if constexpr (OUT) {
+        const float *Se = a.Sseg + (size_t(bh) * a.nseg + seg) * D * D;
 #pragma unroll
-            for (int h = 0; h < NS; ++h) {
-                const int dt = sd0 + h;
+        for (int h = 0; h < NS; ++h) {
+            const int dt = sd0 + h;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) S[h][r] = Se[(16 * dt + g4 + r) * D + 16 * sj + col];
-                // bf16 copy S^T [j][d] for the output products (buffer 0 of two)
-                *reinterpret_cast<uint2 *>(STb + (16 * sj + col) * PK + 16 * dt + g4) = pk4(S[h]);
-            }
-        } else {
-#pragma unroll
-            for (int h = 0; h < NS; ++h) S[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int r = 0; r < 4; ++r) S[h][r] = Se[(16 * dt + g4 + r) * D + 16 * sj + col];
+            // bf16 copy S^T [j][d] for the output products (buffer 0 of two)
+            *reinterpret_cast<uint2 *>(STb + (16 * sj + col) * PK + 16 * dt + g4) = pk4(S[h]);
         }
+    } else {
+#pragma unroll
+        for (int h = 0; h < NS; ++h) S[h] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     float bsum = 0.f;   // log2 of the segment's carry
 
-    // one chunk step; the rows of chunk c + 1 go into `rows` once chunk c's
-    // are consumed
-    A1Rows<OUT> rows;
+    A1Rows<OUT, WIN> rows;
     rows.load(a, c_begin, bh, row, part);
     for (int c = c_begin; c < c_end; ++c) {
         const int c0 = c * C, t = c0 + row;
-        // 1. rows to LDS as loaded; RMS scales, eta and log2 gamma
+        // 1. rows to LDS as loaded; RMS scales; the step scalars
         {
             uint4 xr = rows.k;
-            float sq = 0.f, sk = 0.f;
-            const uint32_t kw[4] = {xr.x, xr.y, xr.z, xr.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bf16x2_t ke = __builtin_bit_cast(bf16x2_t, kw[e]);
-                sk = __builtin_amdgcn_fdot2_f32_bf16(ke, ke, sk, false);
-            }
-            if constexpr (OUT) {
-                const uint32_t qw[4] = {rows.q.x, rows.q.y, rows.q.z, rows.q.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bf16x2_t qe = __builtin_bit_cast(bf16x2_t, qw[e]);
-                    sq = __builtin_amdgcn_fdot2_f32_bf16(qe, qe, sq, false);
-                }
-            }
+            float sk = sumsq8(xr);
+            float sq = 0.f;
+            if constexpr (OUT) sq = sumsq8(rows.q);
             const bool qok = t < T, kok = t >= 1 && t <= T, first = t == 0;
             const bool carry_x = first && a.xnext_in;
-            if (carry_x) {   // x_0 continues the previous segment (features formed, scale 1)
-                const f32x4 *xp = reinterpret_cast<const f32x4 *>(a.xnext_in + size_t(bh) * D + 8 * part);
-                const f32x4 x0 = xp[0], x1 = xp[1];
-                sk = 0.f;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sk += x0[e] * x0[e] + x1[e] * x1[e];
-                xr = make_uint4(pk2(x0[0], x0[1]), pk2(x0[2], x0[3]), pk2(x1[0], x1[1]), pk2(x1[2], x1[3]));
-            }
+            if (carry_x) xr = feat8(a.xnext_in + size_t(bh) * D + 8 * part, sk);   // x_0: features, scale 1
             sk = group_sum<8>(sk);
             const float sck = carry_x ? 1.f : (kok ? a1_rms_scale(sk, a.eps_rms, a.phi) : 0.f);
+            const uint4 yr = qok ? rows.v : make_uint4(0, 0, 0, 0);
             *reinterpret_cast<uint4 *>(XB + row * PK + 8 * part) = xr;
-            *reinterpret_cast<uint4 *>(VB + row * PK + 8 * part) = qok ? rows.v : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4 *>(VB + row * PK + 8 * part) = yr;
             float scq = 0.f;
             if constexpr (OUT) {
                 sq = group_sum<8>(sq);
@@ -187,69 +277,136 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
                 *reinterpret_cast<uint4 *>(QB + row * PK + 8 * part) = rows.q;
             }
             if (part == 0) {
-                float eta = 0.f, alpha = 0.f;
-                if (!(t >= T || (first && a.fresh))) {   // the fresh first step writes nothing
-                    const float den = sck * sck * sk + rows.lam + a.eps;   // |x_t|^2 + lambda_t + eps
-                    eta = den != 0.f ? rows.beta * __builtin_amdgcn_rcpf(den) : 0.f;
-                    alpha = step_alpha(eta, rows.lam, a.eps_gamma);
+                float w, lg;
+                if constexpr (WIN) {
+                    w = rows.s0;     // eta_t / B_t and log2 gamma_t from the window pass
+                    lg = rows.s1;
+                } else {
+                    float eta = 0.f, alpha = 0.f;
+                    if (!(t >= T || (first && a.fresh))) {   // the fresh first step writes nothing
+                        const float den = sck * sck * sk + rows.s1 + a.eps;   // |x_t|^2 + lambda_t + eps
+                        eta = den != 0.f ? rows.s0 * __builtin_amdgcn_rcpf(den) : 0.f;
+                        alpha = step_alpha(eta, rows.s1, a.eps_gamma);
+                    }
+                    w = eta;
+                    lg = log2_1m(alpha);
                 }
-                sv[kEta][row] = eta;
-                sv[kLg][row] = log2_1m(alpha);
-                sv[kSx][row] = sck;
-                sv[kSq][row] = scq;
+                tv[kW][row] = w;
+                tv[kLg][row] = lg;
+                tv[kSq][row] = scq;
+                pv[pSx][OFF + row] = sck;
+            }
+            if constexpr (WIN) {
+                // the last 16 pair rows are the next chunk's halo tile (rows
+                // outside its window zero), in the other parity's buffer
+                if (row >= C - 16) {
+                    const int h = row - (C - 16), nxt = (c + 1 - c_begin) & 1;
+                    const bool inw = h >= 16 - H;
+                    *reinterpret_cast<uint4 *>(XH + (nxt * 16 + h) * PK + 8 * part) = inw ? xr : make_uint4(0, 0, 0, 0);
+                    *reinterpret_cast<uint4 *>(VH + (nxt * 16 + h) * PK + 8 * part) = inw ? yr : make_uint4(0, 0, 0, 0);
+                    if (part == 0) hsx[nxt][h] = inw ? sck : 0.f;
+                }
+                // the first chunk of the segment reads its halo from memory
+                if (c == c_begin && row < 16) {
+                    const int tau = c0 - 16 + row;
+                    const size_t base = size_t(bh) * T;
+                    const int hkr = tau < 1 ? 0 : tau - 1, hvr = tau < 0 ? 0 : tau;
+                    const uint4 hk = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.k) + (base + hkr) * D + 8 * part);
+                    const uint4 hv = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.v) + (base + hvr) * D + 8 * part);
+                    uint4 hx, hy;
+                    float hs;
+                    halo_pair(a, bh, tau, row >= 16 - H, part, hk, hv, hx, hy, hs);
+                    *reinterpret_cast<uint4 *>(XH + row * PK + 8 * part) = hx;
+                    *reinterpret_cast<uint4 *>(VH + row * PK + 8 * part) = hy;
+                    if (part == 0) hsx[0][row] = hs;
+                }
             }
             if (c + 1 < c_end) rows.load(a, c + 1, bh, row, part);
         }
         __syncthreads();
 
-        // 2. chunk-local prefix b (base 2), lane = token; every wave forms the
-        //    same values (identical LDS writes), so no barrier is needed
+        // 2. chunk-local prefix b (base 2), lane = token, and the pair
+        //    coefficients; every wave forms the same values (identical LDS
+        //    writes), so no barrier is needed
         bool sep;
         float bC;
         {
-            const float lg = sv[kLg][lane];
+            const float lg = tv[kLg][lane];
             const float b = wave_inclusive_scan(lg);
             bC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b), 63));
             sep = bC >= -100.f;
-            const float eta = sv[kEta][lane], sx = sv[kSx][lane];
-            sv[kCoef][lane] = ex2(bC - b) * eta * sx;   // chunk write coefficient of token lane
-            if constexpr (OUT) {
-                const float sq = sv[kSq][lane];
-                sv[kQg][lane] = ex2(b) * sq;                         // e^{b_i} s_q
-                sv[kCs][lane] = (sep ? ex2(-b) : 1.f) * eta * sx;    // (e^{-b_j}) eta_j s_x
-                sv[kB][lane] = b;
+            tv[kB][lane] = b;
+            if constexpr (OUT) tv[kQg][lane] = ex2(b) * tv[kSq][lane];   // e^{b_t} s_q
+            wave_lds_sync();
+            if constexpr (OUT && WIN) {
+                // band of the mask: bf[u][t] = M_{t, t-u} = sum_{s = max(t-u, 0)}^{t}
+                // e^{b_t - b_s} w_s for u < W - 1 (pairs still in the window at t)
+                float mc = 0.f;
+                for (int u = 0; u < H; ++u) {
+                    const int s = lane - u;
+                    if (s >= 0) mc += ex2(b - tv[kB][s]) * tv[kW][s];
+                    bf[u][lane] = mc;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < (NP + 63) / 64; ++u) {
+                const int p = lane + 64 * u;
+                if (p < NP) {
+                    const int j = p - OFF;                     // pair's token (chunk-local)
+                    const int lo = j > 0 ? j : 0, hi = j + H < C - 1 ? j + H : C - 1;
+                    float cp = 0.f, bhi = 0.f;
+                    if (j >= -H && lo <= hi) {
+                        bhi = tv[kB][hi];
+                        for (int s = lo; s <= hi; ++s) cp += ex2(bhi - tv[kB][s]) * tv[kW][s];
+                    }
+                    const float sx = p < OFF ? hsx[(c - c_begin) & 1][p] : pv[pSx][p];
+                    if (p < OFF) pv[pSx][p] = sx;
+                    pv[pCoef][p] = ex2(bC - bhi) * cp * sx;              // M_{63,j} s_x
+                    pv[pCol][p] = (sep ? ex2(-bhi) : 1.f) * cp * sx;     // (e^{-b_hi}) c'_j s_x
+                    pv[pBh][p] = bhi;
+                }
             }
         }
         wave_lds_sync();
         bsum += bC;
 
-        // 3. transposes, once per block: wave w takes token block m = w / 2
-        //    and the d / value tiles 2 (w % 2), + 1
+        // 3. transposes, once per block: waves 0-3 the key blocks (scaled by
+        //    the write coefficients), waves 4-7 the value blocks; NMT blocks
+        //    each (pair tile m, d or value tile n)
         {
-            const int m = wave >> 1;
-            const f32x4 cf = *reinterpret_cast<const f32x4 *>(&sv[kCoef][16 * m + g4]);
+            const int par = (c - c_begin) & 1;
+            if (wave < 4) {
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int n = 2 * (wave & 1) + e;
-                const f32x4 xb = transposed(XB, m, n) * cf;
-                const f32x4 vb = transposed(VB, m, n);
-                *reinterpret_cast<uint2 *>(XT + (16 * n + col) * PK + 16 * m + g4) = pk4(xb);
-                *reinterpret_cast<uint2 *>(VT + (16 * n + col) * PK + 16 * m + g4) = pk4(vb);
+                for (int e = 0; e < NMT; ++e) {
+                    const int b = wave * NMT + e, m = b >> 2, n = b & 3;
+                    const f32x4 cf = *reinterpret_cast<const f32x4 *>(&pv[pCoef][16 * m + g4]);
+                    const f32x4 tb = transposed(ptile(XB, XH, m, par), n) * cf;
+                    *reinterpret_cast<uint2 *>(XT + (16 * n + col) * PX + 16 * m + g4) = pk4(tb);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < NMT; ++e) {
+                    const int b = (wave - 4) * NMT + e, m = b >> 2, n = b & 3;
+                    const f32x4 tb = transposed(ptile(VB, VH, m, par), n);
+                    *reinterpret_cast<uint2 *>(VT + (16 * n + col) * PX + 16 * m + g4) = pk4(tb);
+                }
             }
         }
         __syncthreads();
 
         {
-            // 4. state tiles: S = e^{b_C} S + X^T diag(coef) V
+            // 4. state tiles: S = e^{b_C} S + X^T diag(coef) V over the pairs
             const float gC = ex2(bC);
-            const bf16_t *vr = VT + (16 * sj + col) * PK + k8;
-            const bf16x8 v0 = ld8(vr), v1 = ld8(vr + 32);
+            const bf16_t *vr = VT + (16 * sj + col) * PX;
+            const bf16x8 v0 = ld8(vr + k8), v1 = ld8(vr + 32 + k8);
 #pragma unroll
             for (int h = 0; h < NS; ++h) {
-                const bf16_t *xr = XT + (16 * (sd0 + h) + col) * PK + k8;
+                const bf16_t *xr = XT + (16 * (sd0 + h) + col) * PX;
                 f32x4 s = S[h] * gC;
-                s = mfma32(ld8(xr), v0, s);
-                S[h] = mfma32(ld8(xr + 32), v1, s);
+                s = mfma32(ld8(xr + k8), v0, s);
+                s = mfma32(ld8(xr + 32 + k8), v1, s);
+                if constexpr (WIN) s = mfma16(ld4(xr + 64 + g4), ld4(vr + 64 + g4), s);
+                S[h] = s;
             }
             if constexpr (OUT) {
                 // the next chunk's S^T copy goes to the other buffer: its last
@@ -270,24 +427,34 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
             const bf16_t *qr = QB + tq * PK + k8;
             const bf16x8 q0 = ld8(qr), q1 = ld8(qr + 32);
             const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            const float qg = sv[kQg][tq];
-            // separable decays: e^{-b_s} eta_s s_x times e^{b_t} s_q; else
-            // e^{b_t - b_s} times eta_s s_x times s_q
-            const float bq = sep ? 0.f : sv[kB][tq], qf = sep ? qg : sv[kSq][tq];
-            // score tiles P^T (m, n): lane holds x_s . q_t at s = 16 m + g4 + r, t = tq
-            s16x4 pt[4];
+            const float qg = tv[kQg][tq];
+            const float bq = tv[kB][tq], sqq = tv[kSq][tq];
+            // past the window: separable, (e^{b_t} s_q)(e^{-b_hi} c' s_x), or
+            // e^{b_t - b_hi} s_q (c' s_x)
+            const float qf = sep ? qg : sqq;
+            // score tiles P^T (m, n): lane holds x_p . q_t at pair row
+            // p = 16 m + g4 + r, token t = tq
+            s16x4 pt[NMT];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                if (m > n) break;
-                const bf16_t *xr = XB + (16 * m + col) * PK + k8;
+            for (int m = 0; m < NMT; ++m) {
+                if (m > n + OFF / 16) break;
+                const bf16_t *xr = ptile(XB, XH, m, (c - c_begin) & 1) + col * PK + k8;
                 f32x4 p = mfma32(ld8(xr), q0, z);
                 p = mfma32(ld8(xr + 32), q1, p);
-                const f32x4 cs = *reinterpret_cast<const f32x4 *>(&sv[kCs][16 * m + g4]);
-                const f32x4 bs = *reinterpret_cast<const f32x4 *>(&sv[kB][16 * m + g4]);
+                const f32x4 cl = *reinterpret_cast<const f32x4 *>(&pv[pCol][16 * m + g4]);
+                const f32x4 bh4 = *reinterpret_cast<const f32x4 *>(&pv[pBh][16 * m + g4]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float f = (sep ? 1.f : ex2(bq - bs[r])) * cs[r] * qf;
-                    p[r] = (m < n || g4 + r <= col) ? p[r] * f : 0.f;
+                    const int j = 16 * m + g4 + r - OFF;   // pair's token (chunk-local)
+                    float f;
+                    if (tq >= j + H) {
+                        f = (sep ? 1.f : ex2(bq - bh4[r])) * cl[r] * qf;
+                    } else if (tq < j) {
+                        f = 0.f;
+                    } else {   // band: the pair is still in the window at t
+                        f = bf[tq - j][tq] * pv[pSx][16 * m + g4 + r] * sqq;
+                    }
+                    p[r] *= f;
                 }
                 pt[m] = pk4s(p);
             }
@@ -299,11 +466,9 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
                 o = mfma32(ld8(sr + 32), q1, o);
                 o *= qg;
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    if (m > n) break;
-                    const s16x4 va = __builtin_bit_cast(
-                        s16x4, *reinterpret_cast<const uint2 *>(VT + (16 * jt + col) * PK + 16 * m + g4));
-                    o = mfma16(va, pt[m], o);
+                for (int m = 0; m < NMT; ++m) {
+                    if (m > n + OFF / 16) break;
+                    o = mfma16(ld4(VT + (16 * jt + col) * PX + 16 * m + g4), pt[m], o);
                 }
                 if (c0 + tq < T) *reinterpret_cast<uint2 *>(og + size_t(c0 + tq) * D + 16 * jt) = pk4(o);
             }
@@ -319,12 +484,34 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
 #pragma unroll
             for (int r = 0; r < 4; ++r) Dg[(16 * (sd0 + h) + g4 + r) * D + 16 * sj + col] = S[h][r];
         if (tid == 0) a.Gseg[size_t(bh) * a.nseg + seg] = ex2(bsum);
-        // x for the next segment, phi(k_{T-1}), from the segment holding the last token
-        if (c_end == a.nchunks && wave == 0 && a.xnext_out) {
+        // the boundary state from the segment holding the last token
+        if (c_end == a.nchunks && wave == 0) {
             const bf16_t *kg = static_cast<const bf16_t *>(a.k) + size_t(bh) * T * D;
-            const float xv = bf16_to_f32(kg[size_t(T - 1) * D + lane].bits);
-            const float sc = phi_scale(wave_sum(xv * xv), D, a.eps_rms, a.phi);
-            a.xnext_out[size_t(bh) * D + lane] = xv * sc;
+            const bf16_t *vg = static_cast<const bf16_t *>(a.v) + size_t(bh) * T * D;
+            if (a.xnext_out) {   // x for the next segment: phi(k_{T-1})
+                const float xv = bf16_to_f32(kg[size_t(T - 1) * D + lane].bits);
+                const float sc = phi_scale(wave_sum(xv * xv), D, a.eps_rms, a.phi);
+                a.xnext_out[size_t(bh) * D + lane] = xv * sc;
+            }
+            if (WIN && a.tailx_out) {   // the last W - 1 pairs (features, values), right-aligned
+                for (int sl = 0; sl < H; ++sl) {
+                    const int tau = T - H + sl;
+                    const bool valid = sl >= H - a.n_tail_out;
+                    float x = 0.f, y = 0.f;
+                    if (tau >= 1) {
+                        const float kv = bf16_to_f32(kg[size_t(tau - 1) * D + lane].bits);
+                        x = kv * phi_scale(wave_sum(kv * kv), D, a.eps_rms, a.phi);
+                    } else if (tau == 0) {
+                        x = a.xnext_in ? a.xnext_in[size_t(bh) * D + lane] : 0.f;
+                    } else if (valid) {
+                        x = a.tailx_in[(size_t(bh) * H + H + tau) * D + lane];
+                    }
+                    if (tau >= 0) y = bf16_to_f32(vg[size_t(tau) * D + lane].bits);
+                    else if (valid) y = a.taily_in[(size_t(bh) * H + H + tau) * D + lane];
+                    a.tailx_out[(size_t(bh) * H + sl) * D + lane] = valid ? x : 0.f;
+                    a.taily_out[(size_t(bh) * H + sl) * D + lane] = valid ? y : 0.f;
+                }
+            }
         }
     }
 }
@@ -342,31 +529,118 @@ __device__ __forceinline__ void init_pickers(bf16x8 (*IDT)[64]) {
     }
 }
 
+template <bool WIN>
 __global__ __launch_bounds__(NTH, 4) void a1_segment(ChunkAArgs a) {
+    using G = Geo<WIN>;
     __shared__ __align__(16) bf16_t XB[C * PK];
     __shared__ __align__(16) bf16_t VB[C * PK];
-    __shared__ __align__(16) bf16_t XT[D * PK];
-    __shared__ __align__(16) bf16_t VT[D * PK];
-    __shared__ __align__(16) float sv[kNsv][C];
+    __shared__ __align__(16) bf16_t XH[WIN ? 2 * 16 * PK : 8];   // halo tiles by chunk parity
+    __shared__ __align__(16) bf16_t VH[WIN ? 2 * 16 * PK : 8];
+    __shared__ __align__(16) float hsx[2][16];
+    __shared__ __align__(16) bf16_t XT[D * G::PX];
+    __shared__ __align__(16) bf16_t VT[D * G::PX];
+    __shared__ __align__(16) float tv[kNtv][C];
+    __shared__ __align__(16) float pv[kNpv][G::NP];
     __shared__ __align__(16) bf16x8 IDT[2][64];
     init_pickers(IDT);
     __syncthreads();
-    a1_walk<false>(a, blockIdx.x, blockIdx.y, nullptr, XB, VB, XT, VT, nullptr, sv, IDT);
+    a1_walk<false, WIN>(a, blockIdx.x, blockIdx.y, nullptr, XB, VB, XH, VH, hsx, XT, VT, nullptr, tv, pv, nullptr, IDT);
 }
 
+template <bool WIN>
 __global__ __launch_bounds__(NTH, 4) void a1_output(ChunkAArgs a) {
+    using G = Geo<WIN>;
     __shared__ __align__(16) bf16_t QB[C * PK];
     __shared__ __align__(16) bf16_t XB[C * PK];
     __shared__ __align__(16) bf16_t VB[C * PK];
-    __shared__ __align__(16) bf16_t XT[D * PK];
-    __shared__ __align__(16) bf16_t VT[D * PK];
+    __shared__ __align__(16) bf16_t XH[WIN ? 2 * 16 * PK : 8];   // halo tiles by chunk parity
+    __shared__ __align__(16) bf16_t VH[WIN ? 2 * 16 * PK : 8];
+    __shared__ __align__(16) float hsx[2][16];
+    __shared__ __align__(16) bf16_t XT[D * G::PX];
+    __shared__ __align__(16) bf16_t VT[D * G::PX];
     __shared__ __align__(16) bf16_t STb[2 * D * PK];
-    __shared__ __align__(16) float sv[kNsv][C];
+    __shared__ __align__(16) float tv[kNtv][C];
+    __shared__ __align__(16) float pv[kNpv][G::NP];
+    __shared__ __align__(16) float bf[WIN ? FALCON_MAX_WINDOW - 1 : 1][C];
     __shared__ __align__(16) bf16x8 IDT[2][64];
     init_pickers(IDT);
     // (the entry state's bf16 copy is written inside the walk; the first
     // barrier of the walk orders it and the pickers before their first reads)
-    a1_walk<true>(a, blockIdx.x, blockIdx.y, QB, XB, VB, XT, VT, STb, sv, IDT);
+    a1_walk<true, WIN>(a, blockIdx.x, blockIdx.y, QB, XB, VB, XH, VH, hsx, XT, VT, STb, tv, pv, bf, IDT);
+}
+
+// Falcon-3A window statistic and step scalars of one chunk (one wave): the
+// pair rows of the chunk and its halo, the band of the pair Gram
+// (x_p . x_{p-d}, d < 8) on MFMA, then per token t the window Gram of its
+// B_t pairs, mu_t = lambda_max / B_t, eta_t = beta_t / (mu_t + lambda_t + eps),
+// w_t = eta_t / B_t and log2 gamma_t to the workspace (0 past T and at a
+// fresh first token).
+__global__ __launch_bounds__(64) void a3_window(ChunkAArgs a) {
+    __shared__ __align__(16) bf16_t XR[80 * PK];
+    __shared__ float sx[80];
+    __shared__ float band[80][8];
+    const int c = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
+    const int W = a.window, H = W - 1, T = a.T, c0 = c * C;
+    const int part = lane & 7, col = lane & 15, g4 = 4 * (lane >> 4), k8 = 8 * (lane >> 4);
+    const bf16_t *kg = static_cast<const bf16_t *>(a.k) + size_t(bh) * T * D;
+    // pair rows p = 0..79 at positions tau = c0 - 16 + p, eight rows a pass
+    for (int it = 0; it < 10; ++it) {
+        const int p = 8 * it + (lane >> 3);
+        const int tau = c0 - 16 + p;
+        const int kr = tau < 1 ? 0 : (tau - 1 < T ? tau - 1 : T - 1);
+        const uint4 raw = *reinterpret_cast<const uint4 *>(kg + size_t(kr) * D + 8 * part);
+        uint4 xr, yr;
+        float sc;
+        if (p < 16) {
+            halo_pair(a, bh, tau, p >= 16 - H, part, raw, make_uint4(0, 0, 0, 0), xr, yr, sc);
+        } else {   // the chunk's own pairs (x_0 from the boundary when continuing)
+            float ss = sumsq8(raw);
+            xr = raw;
+            const bool carry_x = tau == 0 && a.xnext_in;
+            if (carry_x) xr = feat8(a.xnext_in + size_t(bh) * D + 8 * part, ss);
+            ss = group_sum<8>(ss);
+            sc = carry_x ? 1.f : ((tau >= 1 && tau < T) ? a1_rms_scale(ss, a.eps_rms, a.phi) : 0.f);
+        }
+        *reinterpret_cast<uint4 *>(XR + p * PK + 8 * part) = xr;
+        if (part == 0) sx[p] = sc;
+    }
+    __syncthreads();
+    // band of the pair Gram: tiles (m, m) for m = 0..4 and (m, m - 1) for m = 1..4
+    for (int tile = 0; tile < 9; ++tile) {
+        const int m = tile < 5 ? tile : tile - 4, mp = tile < 5 ? m : m - 1;
+        const bf16_t *ar = XR + (16 * m + col) * PK + k8, *br = XR + (16 * mp + col) * PK + k8;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        f32x4 g = mfma32(ld8(ar), ld8(br), z);
+        g = mfma32(ld8(ar + 32), ld8(br + 32), g);
+        // lane holds x_p . x_q for p = 16 m + g4 + r, q = 16 mp + col
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int p = 16 * m + g4 + r, q = 16 * mp + col, d = p - q;
+            if (d >= 0 && d < 8) band[p][d] = g[r] * sx[p] * sx[q];
+        }
+    }
+    __syncthreads();
+    const int t = c0 + lane, p = 16 + lane;
+    float w = 0.f, lg = 0.f;
+    if (t < T && !(t == 0 && a.fresh)) {
+        const long long pairs = (long long)a.n_tail_in + t + 1;
+        const int bt = pairs < W ? int(pairs) : W;
+        float g[8][8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int lo = i < j ? i : j, df = i < j ? j - i : i - j;
+                g[i][j] = (i < bt && j < bt) ? band[p - lo][df] : 0.f;
+            }
+        const float mu = psd_lambda_max(g, bt) / float(bt);
+        const float beta = a.beta[size_t(bh) * T + t], lam = a.lambda[size_t(bh) * T + t];
+        const float eta = step_eta(beta, mu + lam + a.eps);
+        w = eta / float(bt);
+        lg = log2_1m(step_alpha(eta, lam, a.eps_gamma));
+    }
+    a.etaw[size_t(bh) * a.Tpad + t] = w;
+    a.lg[size_t(bh) * a.Tpad + t] = lg;
 }
 
 // entry state of every segment: S_{g+1} = Gamma_g S_g + D_g (one thread per
@@ -402,15 +676,26 @@ __global__ __launch_bounds__(256) void a1_segscan(ChunkAArgs a) {
     if (a.S_out) a.S_out[size_t(bh) * D * D + e] = S;
 }
 
-}  // namespace
-
-void launch_chunk_a1(const ChunkAArgs &a, hipStream_t s, Marks *m) {
-    a1_segment<<<dim3(a.nseg, a.BH), NTH, 0, s>>>(a);
+template <bool WIN>
+void launch_walks(const ChunkAArgs &a, hipStream_t s, Marks *m) {
+    a1_segment<WIN><<<dim3(a.nseg, a.BH), NTH, 0, s>>>(a);
     m->mark(s);
     a1_segscan<<<dim3(a.BH, D * D / 256), 256, 0, s>>>(a);
     m->mark(s);
-    a1_output<<<dim3(a.nseg, a.BH), NTH, 0, s>>>(a);
+    a1_output<WIN><<<dim3(a.nseg, a.BH), NTH, 0, s>>>(a);
     m->mark(s);
+}
+
+}  // namespace
+
+void launch_chunk_a1(const ChunkAArgs &a, hipStream_t s, Marks *m) {
+    if (a.window > 1) {
+        a3_window<<<dim3(a.nchunks, a.BH), 64, 0, s>>>(a);
+        m->mark(s);
+        launch_walks<true>(a, s, m);
+    } else {
+        launch_walks<false>(a, s, m);
+    }
 }
 
 }  // namespace falcon

@@ -135,13 +135,15 @@ inline int chunk_a_segment_chunks(long long bh, int nchunks) {
     return int(g);
 }
 
-// The bf16 Falcon-1A path with every token-contracting operand in registers
-// (chunk_a1.hip): d_k = d_v = 64.  FALCON_A_PATH=generic keeps the general
-// 1A/3A kernels (measurement and cross-checks).
+// The bf16 Falcon-1A / Falcon-3A path with every token-contracting operand
+// transposed once per chunk (chunk_a1.hip): d_k = d_v = 64.
+// FALCON_A_PATH=generic keeps the general 1A/3A kernels (measurement and
+// cross-checks).
 inline bool chunk_a1_supported(bool bf16, int variant, int window, int dk, int dv) {
     if (const char *e = std::getenv("FALCON_A_PATH"))
         if (std::strcmp(e, "generic") == 0) return false;
-    return bf16 && variant == FALCON_V1A && window == 1 && dk == 64 && dv == 64;
+    const bool var_ok = (variant == FALCON_V1A && window == 1) || (variant == FALCON_V3A && window >= 1);
+    return bf16 && var_ok && dk == 64 && dv == 64;
 }
 // chunks per segment of that path: the fewest that keep all segments of all
 // heads resident at once (two 512-thread workgroups per compute unit, 256

@@ -13,6 +13,7 @@ const char *const kNamesChunkF1[] = {"feature", "chunk_f1_prep", "chunk_f1_scan"
 const char *const kNamesChunkF1Fused[] = {"chunk_f1_fused"};
 const char *const kNamesChunkA[] = {"a_segment", "a_segscan", "a_output"};
 const char *const kNamesChunkA1[] = {"a1_segment", "a1_segscan", "a1_output"};
+const char *const kNamesChunkA3[] = {"a3_window", "a1_segment", "a1_segscan", "a1_output"};
 const char *const kNamesChunkF2[] = {"chunk_f2"};
 const char *const kNamesChunkF3[] = {"feature", "f3_prep", "f3_scan"};
 const char *const kNamesChunkF1Split[] = {"f1_ops", "f1_walk"};
@@ -84,6 +85,10 @@ int run(const falcon_fwd_args *args, void *stream, Marks *m) {
         ca.Gseg = p.ws_at<float>(p.off_seg_g);
         ca.Sseg = p.ws_at<float>(p.off_seg_s);
         if (p.path == Path::kChunkA1) {
+            if (p.window > 1) {
+                ca.etaw = p.ws_at<float>(p.off_eta);
+                ca.lg = p.ws_at<float>(p.off_alpha);
+            }
             launch_chunk_a1(ca, s, m);
         } else {
             ca.etaw = p.ws_at<float>(p.off_eta);
@@ -289,7 +294,9 @@ extern "C" const char *falcon_kernel_name(const falcon_fwd_args *args, int i) {
         case Path::kChunkF1: return i < 3 ? kNamesChunkF1[i] : nullptr;
         case Path::kChunkF1Fused: return i < 1 ? kNamesChunkF1Fused[i] : nullptr;
         case Path::kChunkA: return i < 3 ? kNamesChunkA[i] : nullptr;
-        case Path::kChunkA1: return i < 3 ? kNamesChunkA1[i] : nullptr;
+        case Path::kChunkA1:
+            if (p.window > 1) return i < 4 ? kNamesChunkA3[i] : nullptr;
+            return i < 3 ? kNamesChunkA1[i] : nullptr;
         case Path::kChunkF2: return i < 1 ? kNamesChunkF2[i] : nullptr;
         case Path::kChunkF3: return i < 3 ? kNamesChunkF3[i] : nullptr;
         case Path::kChunkF1Split: return i < 2 ? kNamesChunkF1Split[i] : nullptr;

@@ -135,9 +135,15 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
         off = align_up(off + static_cast<size_t>(bh) * p->nchunks * f1_xfer_bytes(a->dv));
     } else if (p->path == Path::kChunkA1) {
         p->nchunks = (T + kChunk - 1) / kChunk;
+        p->Tpad = p->nchunks * kChunk;
         p->seg_chunks = chunk_a1_segment_chunks(bh, p->nchunks);
         p->nseg = (p->nchunks + p->seg_chunks - 1) / p->seg_chunks;
         const size_t st = static_cast<size_t>(bh) * p->nseg * a->dk * a->dv * 4;
+        if (a->window > 1) {   // per-token w_t and log2 gamma_t from the window pass
+            const size_t rows = static_cast<size_t>(bh) * p->Tpad;
+            p->off_eta = off; off = align_up(off + rows * 4);
+            p->off_alpha = off; off = align_up(off + rows * 4);
+        }
         p->off_chunk = off; off = align_up(off + st);           // segment writes [d][j]
         p->off_seg_g = off; off = align_up(off + static_cast<size_t>(bh) * p->nseg * 4);
         p->off_seg_s = off; off = align_up(off + st);           // segment entry states [d][j]
