@@ -252,6 +252,24 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
     }
     float bsum = 0.f;   // log2 of the segment's carry
 
+    if constexpr (WIN) {
+        // the first chunk's halo tile from memory (later chunks take theirs
+        // from the previous chunk's rows); ordered by the first barrier
+        if (row < 16) {
+            const int tau = c_begin * C - 16 + row;
+            const size_t base = size_t(bh) * T;
+            const int hkr = tau < 1 ? 0 : tau - 1, hvr = tau < 0 ? 0 : tau;
+            const uint4 hk = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.k) + (base + hkr) * D + 8 * part);
+            const uint4 hv = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.v) + (base + hvr) * D + 8 * part);
+            uint4 hx, hy;
+            float hs;
+            halo_pair(a, bh, tau, row >= 16 - H, part, hk, hv, hx, hy, hs);
+            *reinterpret_cast<uint4 *>(XH + row * PK + 8 * part) = hx;
+            *reinterpret_cast<uint4 *>(VH + row * PK + 8 * part) = hy;
+            if (part == 0) hsx[0][row] = hs;
+        }
+    }
+
     A1Rows<OUT, WIN> rows;
     rows.load(a, c_begin, bh, row, part);
     for (int c = c_begin; c < c_end; ++c) {
@@ -306,20 +324,6 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
                     *reinterpret_cast<uint4 *>(VH + (nxt * 16 + h) * PK + 8 * part) = inw ? yr : make_uint4(0, 0, 0, 0);
                     if (part == 0) hsx[nxt][h] = inw ? sck : 0.f;
                 }
-                // the first chunk of the segment reads its halo from memory
-                if (c == c_begin && row < 16) {
-                    const int tau = c0 - 16 + row;
-                    const size_t base = size_t(bh) * T;
-                    const int hkr = tau < 1 ? 0 : tau - 1, hvr = tau < 0 ? 0 : tau;
-                    const uint4 hk = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.k) + (base + hkr) * D + 8 * part);
-                    const uint4 hv = *reinterpret_cast<const uint4 *>(static_cast<const bf16_t *>(a.v) + (base + hvr) * D + 8 * part);
-                    uint4 hx, hy;
-                    float hs;
-                    halo_pair(a, bh, tau, row >= 16 - H, part, hk, hv, hx, hy, hs);
-                    *reinterpret_cast<uint4 *>(XH + row * PK + 8 * part) = hx;
-                    *reinterpret_cast<uint4 *>(VH + row * PK + 8 * part) = hy;
-                    if (part == 0) hsx[0][row] = hs;
-                }
             }
             if (c + 1 < c_end) rows.load(a, c + 1, bh, row, part);
         }
@@ -343,8 +347,8 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
                 // e^{b_t - b_s} w_s for u < W - 1 (pairs still in the window at t)
                 float mc = 0.f;
                 for (int u = 0; u < H; ++u) {
-                    const int s = lane - u;
-                    if (s >= 0) mc += ex2(b - tv[kB][s]) * tv[kW][s];
+                    const int s = lane - u, sc = s > 0 ? s : 0;
+                    mc += s >= 0 ? ex2(b - tv[kB][sc]) * tv[kW][sc] : 0.f;
                     bf[u][lane] = mc;
                 }
             }
@@ -354,10 +358,13 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
                 if (p < NP) {
                     const int j = p - OFF;                     // pair's token (chunk-local)
                     const int lo = j > 0 ? j : 0, hi = j + H < C - 1 ? j + H : C - 1;
-                    float cp = 0.f, bhi = 0.f;
-                    if (j >= -H && lo <= hi) {
-                        bhi = tv[kB][hi];
-                        for (int s = lo; s <= hi; ++s) cp += ex2(bhi - tv[kB][s]) * tv[kW][s];
+                    // c'_j: at most W terms (none for rows before the window)
+                    const bool live = j >= -H;
+                    const float bhi = live ? tv[kB][hi] : 0.f;
+                    float cp = 0.f;
+                    for (int u = 0; u <= H; ++u) {
+                        const int s = lo + u, sc = s < hi ? s : hi;
+                        cp += (live && s <= hi) ? ex2(bhi - tv[kB][sc]) * tv[kW][sc] : 0.f;
                     }
                     const float sx = p < OFF ? hsx[(c - c_begin) & 1][p] : pv[pSx][p];
                     if (p < OFF) pv[pSx][p] = sx;
@@ -443,16 +450,20 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
                 p = mfma32(ld8(xr + 32), q1, p);
                 const f32x4 cl = *reinterpret_cast<const f32x4 *>(&pv[pCol][16 * m + g4]);
                 const f32x4 bh4 = *reinterpret_cast<const f32x4 *>(&pv[pBh][16 * m + g4]);
+                f32x4 sxb;
+                if constexpr (WIN) sxb = *reinterpret_cast<const f32x4 *>(&pv[pSx][16 * m + g4]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int j = 16 * m + g4 + r - OFF;   // pair's token (chunk-local)
-                    float f;
-                    if (tq >= j + H) {
-                        f = (sep ? 1.f : ex2(bq - bh4[r])) * cl[r] * qf;
-                    } else if (tq < j) {
-                        f = 0.f;
-                    } else {   // band: the pair is still in the window at t
-                        f = bf[tq - j][tq] * pv[pSx][16 * m + g4 + r] * sqq;
+                    // past the window, before the pair (0), or in the band
+                    // (the pair still in the window at t)
+                    float f = (sep ? 1.f : ex2(bq - bh4[r])) * cl[r] * qf;
+                    if constexpr (WIN) {
+                        const int u = tq - j, uc = u < 0 ? 0 : (u < FALCON_MAX_WINDOW - 1 ? u : FALCON_MAX_WINDOW - 2);
+                        const float fb = bf[uc][tq] * sxb[r] * sqq;
+                        f = u >= H ? f : (u < 0 ? 0.f : fb);
+                    } else {
+                        f = tq >= j ? f : 0.f;
                     }
                     p[r] *= f;
                 }
@@ -548,7 +559,7 @@ __global__ __launch_bounds__(NTH, 4) void a1_segment(ChunkAArgs a) {
 }
 
 template <bool WIN>
-__global__ __launch_bounds__(NTH, 4) void a1_output(ChunkAArgs a) {
+__global__ __launch_bounds__(NTH, WIN ? 2 : 4) void a1_output(ChunkAArgs a) {
     using G = Geo<WIN>;
     __shared__ __align__(16) bf16_t QB[C * PK];
     __shared__ __align__(16) bf16_t XB[C * PK];
