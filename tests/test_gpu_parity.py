@@ -358,13 +358,16 @@ def test_chunk_a1_bf16_segments(monkeypatch, seg):
     check(gu.small("F1A", "bf16", B=1, H=3, T=1300, dk=64, dv=64, chunk=64, seed=17))
 
 
+@pytest.mark.parametrize("variant,window", [("F1A", 1), ("F3A", 2), ("F3A", 8)])
 @pytest.mark.parametrize("split", [0, 3, 64, 100])
-def test_chunk_a1_bf16_continuation(monkeypatch, split):
-    """Two calls carrying (S, x_next) match the oracle run of the whole
-    sequence."""
+@pytest.mark.parametrize("seg", ["1", "3"])
+def test_chunk_a1_bf16_continuation(monkeypatch, variant, window, split, seg):
+    """Two calls carrying (S, x_next, the last W - 1 pairs) match the oracle
+    run of the whole sequence; the carried pairs match the oracle's."""
     import torch
     _a_path(monkeypatch, "a1")
-    w = gu.small("F1A", "bf16", B=2, H=3, T=300, dk=64, dv=64, chunk=64, seed=19)
+    monkeypatch.setenv("FALCON_A_SEGMENT", seg)
+    w = gu.small(variant, "bf16", B=2, H=3, T=300, dk=64, dv=64, chunk=64, window=window, seed=19)
     inp = gu.make(w)
     dev = gu.to_device(inp, w)
     a = {k: v[:, :, :split].contiguous() for k, v in dev.items()}
@@ -377,6 +380,28 @@ def test_chunk_a1_bf16_continuation(monkeypatch, split):
     assert eo <= gu.TOL_BF16 and es <= gu.TOL_BF16, (eo, es)
     assert torch.allclose(st2.x_next, torch.from_numpy(st_ref.x_next.reshape(2, 3, 64)).float().cuda(),
                           rtol=1e-5, atol=1e-5)
+    if window > 1:
+        got = gu.gpu_state_to_oracle(st2)
+        assert st2.n_tail == window - 1
+        assert np.allclose(got.tail_x, st_ref.tail_x, rtol=1e-5, atol=1e-5)
+        assert np.allclose(got.tail_y, st_ref.tail_y, rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("seg", ["1", "2", "5", "16"])
+@pytest.mark.parametrize("window", [3, 8])
+def test_chunk_a3_bf16_segments(monkeypatch, seg, window):
+    """Falcon-3A: chunks per segment (the halo carried in LDS or read from
+    memory) do not change the result."""
+    _a_path(monkeypatch, "a1")
+    monkeypatch.setenv("FALCON_A_SEGMENT", seg)
+    check(gu.small("F3A", "bf16", B=1, H=3, T=1100, dk=64, dv=64, chunk=64, window=window, seed=29))
+
+
+@pytest.mark.parametrize("T", [1, 2, 7, 8, 9, 63, 64, 65, 200])
+@pytest.mark.parametrize("window", [2, 8])
+def test_chunk_a3_bf16_lengths(monkeypatch, T, window):
+    _a_path(monkeypatch, "a1")
+    check(gu.small("F3A", "bf16", B=2, H=2, T=T, dk=64, dv=64, chunk=64, window=window, seed=T + 31))
 
 
 @pytest.mark.parametrize("eps_gamma", [1e-3, 5e-2])
