@@ -13,105 +13,66 @@
 namespace falcon {
 
 // Largest eigenvalue of a symmetric positive semi-definite n x n matrix
-// (n <= 8, entries beyond n ignored), fp32.  Lanczos with full
-// re-orthogonalisation reduces G to a symmetric tridiagonal matrix with the
-// same spectrum (whenever the Krylov space closes before n steps, the next
-// vector is the unit vector with the largest component outside the space
-// found so far, and the coupling is 0, so the reduction always covers the
-// whole space).  Newton's method from an upper bound then converges
-// monotonically to the largest root of det(T - x I).  Used for the window
-// statistic mu_t = lambda_max(window covariance) (summary §C.6: the exact
-// top eigenvalue of the small active-window Gram).
+// (n <= 8, entries beyond n ignored), fp32.  The matrix, zero-padded to
+// 8 x 8 (the padding only adds zero eigenvalues) and scaled by its trace,
+// is reduced to a symmetric tridiagonal matrix with the same spectrum by six
+// Householder reflections (A <- H A H, H = I - beta v v^T, applied as the
+// rank-two update A - v w^T - w v^T); Newton's method from an upper bound
+// then converges monotonically to the largest root of det(T - x I).  Used
+// for the window statistic mu_t = lambda_max(window covariance) (summary
+// §C.6: the exact top eigenvalue of the small active-window Gram).
 FALCON_HD inline float psd_lambda_max(const float (&G)[8][8], int n) {
     float tr = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) tr += i < n ? G[i][i] : 0.f;
     if (!(tr > 0.f)) return 0.f;
     const float inv = 1.f / tr;   // work on G / trace: eigenvalues in [0, 1]
-    float Q[8][8];
-    float al[8], be[8];
-    float v[8];
-    const float v0 = 1.f / sqrtf(float(n));
+    float A[8][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = i < n ? v0 : 0.f;
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        al[k] = 0.f;
-        be[k] = 0.f;
-        if (k < n) {
-            if (k > 0) {
-                if (be[k - 1] > 1e-5f) {
+        for (int j = 0; j < 8; ++j) A[i][j] = (i < n && j < n) ? G[i][j] * inv : 0.f;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) v[i] *= 1.f / be[k - 1];
-                } else {
-                    // the Krylov space closed: continue with a fresh direction
-                    be[k - 1] = 0.f;
-                    float best = -1.f;
+    for (int k = 0; k < 6; ++k) {
+        // reflect x = A[k+1..7][k] onto (alpha, 0, ..., 0)
+        float xx = 0.f;
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        if (j < n) {
-                            float u[8];
+        for (int i = k + 1; i < 8; ++i) xx += A[i][k] * A[i][k];
+        const float x0 = A[k + 1][k];
+        const float nx = sqrtf(xx);
+        const float alpha = x0 > 0.f ? -nx : nx;
+        float v[8];
 #pragma unroll
-                            for (int i = 0; i < 8; ++i) u[i] = (i == j) ? 1.f : 0.f;
+        for (int i = k + 1; i < 8; ++i) v[i] = i == k + 1 ? x0 - alpha : A[i][k];
+        const float vv = 2.f * (xx - alpha * x0);   // |v|^2
+        const float beta = vv > 1e-30f ? 2.f / vv : 0.f;
+        float p[8];
 #pragma unroll
-                            for (int q = 0; q < 8; ++q) {
-                                if (q < k) {
-                                    const float h = Q[q][j];
+        for (int i = k + 1; i < 8; ++i) {
+            float s = 0.f;
 #pragma unroll
-                                    for (int i = 0; i < 8; ++i) u[i] -= h * Q[q][i];
-                                }
-                            }
-                            float nn = 0.f;
-#pragma unroll
-                            for (int i = 0; i < 8; ++i) nn += u[i] * u[i];
-                            if (nn > best) {
-                                best = nn;
-#pragma unroll
-                                for (int i = 0; i < 8; ++i) v[i] = u[i];
-                            }
-                        }
-                    }
-                    const float s = 1.f / sqrtf(best);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) v[i] *= s;
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) Q[k][i] = v[i];
-            float w[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float s = 0.f;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) s += (i < n && j < n ? G[i][j] : 0.f) * v[j];
-                w[i] = s * inv;
-            }
-            float a = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) a += v[i] * w[i];
-            al[k] = a;
-            // full re-orthogonalisation against every Lanczos vector, twice
-#pragma unroll
-            for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    if (j <= k) {
-                        float h = 0.f;
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) h += Q[j][i] * w[i];
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) w[i] -= h * Q[j][i];
-                    }
-                }
-            }
-            float b2 = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) b2 += w[i] * w[i];
-            be[k] = sqrtf(b2);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = w[i];
+            for (int j = k + 1; j < 8; ++j) s += A[i][j] * v[j];
+            p[i] = beta * s;
         }
+        float vp = 0.f;
+#pragma unroll
+        for (int i = k + 1; i < 8; ++i) vp += v[i] * p[i];
+        const float K = 0.5f * beta * vp;
+#pragma unroll
+        for (int i = k + 1; i < 8; ++i) p[i] -= K * v[i];   // w
+#pragma unroll
+        for (int i = k + 1; i < 8; ++i)
+#pragma unroll
+            for (int j = k + 1; j < 8; ++j) A[i][j] -= v[i] * p[j] + p[i] * v[j];
+        A[k + 1][k] = beta > 0.f ? alpha : x0;
     }
+    float al[8], be[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        al[i] = A[i][i];
+        be[i] = i < 7 ? A[i + 1][i] : 0.f;
+    }
+    n = 8;
     // Newton from above on det(T_n - x I) (three-term recurrence)
     float x = 0.f;
 #pragma unroll
