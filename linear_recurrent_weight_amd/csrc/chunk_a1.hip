@@ -484,7 +484,13 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
                 if (c0 + tq < T) *reinterpret_cast<uint2 *>(og + size_t(c0 + tq) * D + 16 * jt) = pk4(o);
             }
         }
-        __syncthreads();   // the next chunk overwrites the rows, transposes and scalars
+        // The next chunk overwrites the rows, scalars and halo tiles, and then
+        // the transposes.  The outputs read the rows here, so a1_output
+        // closes the chunk with a barrier.  The segment walk's last reads of
+        // them come before the second barrier, and its state tiles (the last
+        // reads of the transposes) finish before any wave passes the next
+        // chunk's first barrier.
+        if constexpr (OUT) __syncthreads();
     }
 
     if constexpr (!OUT) {
