@@ -439,9 +439,19 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
             // past the window: separable, (e^{b_t} s_q)(e^{-b_hi} c' s_x), or
             // e^{b_t - b_hi} s_q (c' s_x)
             const float qf = sep ? qg : sqq;
-            // score tiles P^T (m, n): lane holds x_p . q_t at pair row
-            // p = 16 m + g4 + r, token t = tq
-            s16x4 pt[NMT];
+            // O^T for value tiles jt0 = 2 (w % 2) and jt0 + 1: the state term
+            // first, then each score tile P^T (m, n) (lane holds x_p . q_t at
+            // pair row p = 16 m + g4 + r, token t = tq) is formed once and fed
+            // to both
+            const int jt0 = 2 * (wave & 1);
+            f32x4 o0, o1;
+            {
+                const bf16_t *sr0 = stc + (16 * jt0 + col) * PK + k8, *sr1 = sr0 + 16 * PK;
+                o0 = mfma32(ld8(sr0), q0, z);
+                o0 = mfma32(ld8(sr0 + 32), q1, o0) * qg;
+                o1 = mfma32(ld8(sr1), q0, z);
+                o1 = mfma32(ld8(sr1 + 32), q1, o1) * qg;
+            }
 #pragma unroll
             for (int m = 0; m < NMT; ++m) {
                 if (m > n + OFF / 16) break;
@@ -467,21 +477,13 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
                     }
                     p[r] *= f;
                 }
-                pt[m] = pk4s(p);
+                const s16x4 pt = pk4s(p);
+                o0 = mfma16(ld4(VT + (16 * jt0 + col) * PX + 16 * m + g4), pt, o0);
+                o1 = mfma16(ld4(VT + (16 * jt0 + 16 + col) * PX + 16 * m + g4), pt, o1);
             }
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int jt = 2 * (wave & 1) + e;
-                const bf16_t *sr = stc + (16 * jt + col) * PK + k8;
-                f32x4 o = mfma32(ld8(sr), q0, z);
-                o = mfma32(ld8(sr + 32), q1, o);
-                o *= qg;
-#pragma unroll
-                for (int m = 0; m < NMT; ++m) {
-                    if (m > n + OFF / 16) break;
-                    o = mfma16(ld4(VT + (16 * jt + col) * PX + 16 * m + g4), pt[m], o);
-                }
-                if (c0 + tq < T) *reinterpret_cast<uint2 *>(og + size_t(c0 + tq) * D + 16 * jt) = pk4(o);
+            if (c0 + tq < T) {
+                *reinterpret_cast<uint2 *>(og + size_t(c0 + tq) * D + 16 * jt0) = pk4(o0);
+                *reinterpret_cast<uint2 *>(og + size_t(c0 + tq) * D + 16 * jt0 + 16) = pk4(o1);
             }
         }
         // The next chunk overwrites the rows, scalars and halo tiles, and then
@@ -565,7 +567,7 @@ __global__ __launch_bounds__(NTH, 4) void a1_segment(ChunkAArgs a) {
 }
 
 template <bool WIN>
-__global__ __launch_bounds__(NTH, WIN ? 2 : 4) void a1_output(ChunkAArgs a) {
+__global__ __launch_bounds__(NTH, 4) void a1_output(ChunkAArgs a) {
     using G = Geo<WIN>;
     __shared__ __align__(16) bf16_t QB[C * PK];
     __shared__ __align__(16) bf16_t XB[C * PK];
