@@ -247,3 +247,57 @@ def test_chunk_f3_coverage(lib):
         assert n > 0
         assert validate(lib, with_ws(lib, a)) == fb.OK
     assert validate(lib, with_ws(lib, args(variant="F3", window=4, dk=16))) == fb.ERR_UNSUPPORTED
+
+
+def _names(lib, a):
+    out = []
+    while True:
+        nm = lib.falcon_kernel_name(ctypes.byref(a), len(out))
+        if nm is None:
+            return out
+        out.append(nm.decode())
+
+
+def _segments(bh, nchunks):
+    """Chunks per segment of the bf16 d = 64 inner-product path: the fewest
+    that keep every segment of every head resident at once (512 workgroups)."""
+    for g in range(1, nchunks):
+        if bh * -(-nchunks // g) <= 512:
+            return g
+    return max(nchunks, 1)
+
+
+@pytest.mark.parametrize("variant,window", [("F1A", 1), ("F3A", 2), ("F3A", 8)])
+def test_inner_product_bf16_d64_path(lib, monkeypatch, variant, window):
+    """bf16 Falcon-1A / 3A at d_k = d_v = 64 take the register-transpose
+    kernels (a window pass first when W > 1); their workspace is the segment
+    writes and entry states (fp32 [d_k][d_v]) and carries, plus w_t and
+    log2 gamma_t per token with a window.  FALCON_A_PATH=generic selects the
+    general kernels."""
+    monkeypatch.delenv("FALCON_A_PATH", raising=False)
+    monkeypatch.delenv("FALCON_A_SEGMENT", raising=False)
+    B, H, T = 2, 12, 16384
+    a = args(variant=variant, window=window, batch=B, heads=H, seqlen=T)
+    names = _names(lib, a)
+    want = (["a3_window"] if window > 1 else []) + ["a1_segment", "a1_segscan", "a1_output"]
+    assert names == want
+    nch = T // 64
+    g = _segments(B * H, nch)
+    nseg = -(-nch // g)
+    align = lambda n: -(-n // 256) * 256
+    st = B * H * nseg * 64 * 64 * 4
+    n = align(st) + align(B * H * nseg * 4) + align(st)
+    if window > 1:
+        n += 2 * align(B * H * nch * 64 * 4)
+    assert wsize(lib, a) == n
+    # (the fake tensor addresses are 1 MiB apart: validate a small shape)
+    assert validate(lib, with_ws(lib, args(variant=variant, window=window))) == fb.OK
+    monkeypatch.setenv("FALCON_A_PATH", "generic")
+    assert _names(lib, a) == ["a_segment", "a_segscan", "a_output"]
+
+
+def test_inner_product_other_shapes_take_the_general_kernels(lib, monkeypatch):
+    monkeypatch.delenv("FALCON_A_PATH", raising=False)
+    for dt, dk, dv in [("f32", 64, 64), ("bf16", 32, 64), ("bf16", 64, 32)]:
+        a = args(variant="F1A", dtype=dt, dk=dk, dv=dv)
+        assert _names(lib, a) == ["a_segment", "a_segscan", "a_output"], (dt, dk, dv)
