@@ -190,18 +190,19 @@ struct A1Rows {
 // Per chunk, after the rows and the step scalars:
 //   - the pair coefficients: c'_j, the chunk write coefficient and the score
 //     column factor of every pair (every wave forms the same values);
-//   - every wave transposes NMT 16 x 16 blocks on MFMA into LDS: key blocks
-//     scaled by the write coefficients, XT[d][p], and value blocks VT[j][p];
-//     each block once per chunk;
+//   - waves 0-3 transpose the key blocks (scaled by the write coefficients),
+//     XT[d][p], and waves 4-7 the value blocks, VT[j][p], NMT each, on MFMA
+//     into LDS; each block once per chunk;
 //   - wave w updates the state tiles (d tiles 2 (w / 4), + 1; value tile
 //     w % 4), S[d][j] += XT V by pair-contracting MFMAs from LDS, and
 //     (a1_output) writes them to the bf16 copy S^T[j][d] that the next chunk's
 //     outputs read (double-buffered by chunk parity);
 //   - (a1_output) wave w forms the outputs of token tile n = 0, 0, 1, 1, 3,
-//     3, 2, 2 (w = 0..7) and value tiles 2 (w % 2), + 1: the score tiles P^T
-//     of the pair tiles up to the diagonal once, kept as B operands, then
-//     O^T (jt, n) = diag-scaled S^T Qh^T + V^T P^T.  Waves w and w + 4 share
-//     a SIMD and hold token tiles n and 3 - n, which balances the score work.
+//     3, 2, 2 (w = 0..7) and value tiles 2 (w % 2), + 1:
+//     O^T (jt, n) = diag-scaled S^T Qh^T + V^T P^T, each score tile P^T of
+//     the pair tiles up to the diagonal formed once and fed as the B operand
+//     to both value tiles.  Waves w and w + 4 share a SIMD and hold token
+//     tiles n and 3 - n, which balances the score work.
 template <bool OUT, bool WIN>
 __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf16_t *QB, bf16_t *XB, bf16_t *VB,
                                         bf16_t *XH, bf16_t *VH, float (*hsx)[16], bf16_t *XT, bf16_t *VT,
