@@ -1,0 +1,65 @@
+"""bench.py: the host-side accounting (CPU) and the JSON line of a short run
+on the GPU."""
+from __future__ import annotations
+
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from linear_recurrent_weight_amd.inputs import WORKLOADS  # noqa: E402
+
+
+def test_algorithmic_bytes():
+    """q, k, v and o once in the io dtype, beta and lambda once in fp32 (beta
+    per column for Falcon-2), the final state once in fp32."""
+    assert bench.algorithmic_bytes(WORKLOADS["c2"]) == 52_690_944
+    assert bench.algorithmic_bytes(WORKLOADS["c3"]) == 204_865_536
+    assert bench.algorithmic_bytes(WORKLOADS["c4"]) == 407_896_064
+    c1 = WORKLOADS["c1"]
+    assert bench.algorithmic_bytes(c1) == 4 * 64 * 16 * 4 + 2 * 64 * 4 + 16 * 16 * 4
+
+
+def test_algorithmic_flops_c2():
+    """Falcon-1 chunk form: 2C(d_k + d_v) + 6 d_k d_v per head-token."""
+    w = WORKLOADS["c2"]
+    assert bench.algorithmic_flops(w) == w.batch * w.heads * w.seqlen * (2 * 64 * 128 + 6 * 64 * 64)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
+
+@pytest.mark.gpu
+def test_bench_line_contract():
+    """A short run prints one JSON line with the keys and the roofline and
+    CPU-baseline objects the measurement contract names."""
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "3", "--warmup", "1",
+                        "--cpu-seconds", "0.5"], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1 and d["vs_baseline"] is None
+    assert d["config"]["workload"].startswith("c2")
+    rf = d["roofline"]
+    assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
+    assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-9
+    cb = d["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0
+    assert d["value"] > 0 and abs(d["value"] - 8 * 12 * 1024 / (d["ms_per_step"] * 1e-3)) < 1e-3 * d["value"]
