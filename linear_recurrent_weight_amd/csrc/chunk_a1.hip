@@ -603,12 +603,23 @@ __global__ __launch_bounds__(64) void a3_window(ChunkAArgs a) {
     const int W = a.window, H = W - 1, T = a.T, c0 = c * C;
     const int part = lane & 7, col = lane & 15, g4 = 4 * (lane >> 4), k8 = 8 * (lane >> 4);
     const bf16_t *kg = static_cast<const bf16_t *>(a.k) + size_t(bh) * T * D;
-    // pair rows p = 0..79 at positions tau = c0 - 16 + p, eight rows a pass
+    // pair rows p = 0..79 at positions tau = c0 - 16 + p, eight rows a pass;
+    // all ten passes' key rows, and this lane's token's beta and lambda, are
+    // requested before any is used
+    uint4 raws[10];
+#pragma unroll
+    for (int it = 0; it < 10; ++it) {
+        const int tau = c0 - 16 + 8 * it + (lane >> 3);
+        const int kr = tau < 1 ? 0 : (tau - 1 < T ? tau - 1 : T - 1);
+        raws[it] = *reinterpret_cast<const uint4 *>(kg + size_t(kr) * D + 8 * part);
+    }
+    const int tl = c0 + lane < T ? c0 + lane : T - 1;
+    const float beta = a.beta[size_t(bh) * T + tl], lam = a.lambda[size_t(bh) * T + tl];
+#pragma unroll
     for (int it = 0; it < 10; ++it) {
         const int p = 8 * it + (lane >> 3);
         const int tau = c0 - 16 + p;
-        const int kr = tau < 1 ? 0 : (tau - 1 < T ? tau - 1 : T - 1);
-        const uint4 raw = *reinterpret_cast<const uint4 *>(kg + size_t(kr) * D + 8 * part);
+        const uint4 raw = raws[it];
         uint4 xr, yr;
         float sc;
         if (p < 16) {
@@ -654,7 +665,6 @@ __global__ __launch_bounds__(64) void a3_window(ChunkAArgs a) {
                 g[i][j] = (i < bt && j < bt) ? band[p - lo][df] : 0.f;
             }
         const float mu = psd_lambda_max(g, bt) / float(bt);
-        const float beta = a.beta[size_t(bh) * T + t], lam = a.lambda[size_t(bh) * T + t];
         const float eta = step_eta(beta, mu + lam + a.eps);
         w = eta / float(bt);
         lg = log2_1m(step_alpha(eta, lam, a.eps_gamma));

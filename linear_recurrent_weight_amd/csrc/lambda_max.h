@@ -17,8 +17,9 @@ namespace falcon {
 // 8 x 8 (the padding only adds zero eigenvalues) and scaled by its trace,
 // is reduced to a symmetric tridiagonal matrix with the same spectrum by six
 // Householder reflections (A <- H A H, H = I - beta v v^T, applied as the
-// rank-two update A - v w^T - w v^T); Newton's method from an upper bound
-// then converges monotonically to the largest root of det(T - x I).  Used
+// rank-two update A - v w^T - w v^T); Laguerre's method from the Gershgorin
+// bound then descends monotonically, with cubic convergence, to the largest
+// root of det(x I - T) (a few iterations where Newton needs about ten).  Used
 // for the window statistic mu_t = lambda_max(window covariance) (summary
 // §C.6: the exact top eigenvalue of the small active-window Gram).
 FALCON_HD inline float psd_lambda_max(const float (&G)[8][8], int n) {
@@ -72,33 +73,37 @@ FALCON_HD inline float psd_lambda_max(const float (&G)[8][8], int n) {
         al[i] = A[i][i];
         be[i] = i < 7 ? A[i + 1][i] : 0.f;
     }
-    n = 8;
-    // Newton from above on det(T_n - x I) (three-term recurrence)
+    // Laguerre's method from above on q(x) = det(x I - T) (degree 8, all
+    // roots real): every iterate stays above the largest root and the
+    // convergence is cubic.  g = q'/q, h = g^2 - q''/q from the three-term
+    // recurrence of det(T_k - x I) and its first two derivatives.
     float x = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        if (i < n) {
-            const float r = al[i] + (i > 0 ? fabsf(be[i - 1]) : 0.f) + (i + 1 < n ? fabsf(be[i]) : 0.f);
-            x = fmaxf(x, r);
-        }
+        const float r = al[i] + (i > 0 ? fabsf(be[i - 1]) : 0.f) + (i < 7 ? fabsf(be[i]) : 0.f);
+        x = fmaxf(x, r);
     }
     x = x * 1.0000001f + 1e-12f;
-    for (int it = 0; it < 80; ++it) {
-        float p0 = 1.f, p1 = al[0] - x, d0 = 0.f, d1 = -1.f;
+    for (int it = 0; it < 32; ++it) {
+        float p0 = 1.f, p1 = al[0] - x, d0 = 0.f, d1 = -1.f, e0 = 0.f, e1 = 0.f;
 #pragma unroll
         for (int i = 1; i < 8; ++i) {
-            if (i < n) {
-                const float b2 = be[i - 1] * be[i - 1];
-                const float p2 = (al[i] - x) * p1 - b2 * p0;
-                const float d2 = (al[i] - x) * d1 - p1 - b2 * d0;
-                p0 = p1;
-                p1 = p2;
-                d0 = d1;
-                d1 = d2;
-            }
+            const float b2 = be[i - 1] * be[i - 1], ai = al[i] - x;
+            const float p2 = ai * p1 - b2 * p0;
+            const float d2 = ai * d1 - p1 - b2 * d0;
+            const float e2 = ai * e1 - 2.f * d1 - b2 * e0;
+            p0 = p1; p1 = p2;
+            d0 = d1; d1 = d2;
+            e0 = e1; e1 = e2;
         }
-        if (d1 == 0.f) break;
-        const float step = p1 / d1;
+        // above every root q > 0 and q'/q > 0; a rounding step onto or past
+        // the largest root ends the iteration there
+        if (!(p1 > 0.f)) break;
+        const float ip = 1.f / p1;
+        const float g = d1 * ip, h = g * g - e1 * ip;
+        if (!(g > 0.f)) break;
+        const float den = g + sqrtf(fmaxf(7.f * (8.f * h - g * g), 0.f));
+        const float step = 8.f / den;
         const float xn = x - step;
         if (!(xn < x)) break;   // monotone from above: stop when no progress
         x = xn;

@@ -1,7 +1,8 @@
 """Host build of the kernels' window statistic (lambda_max of the small
 window Gram, linear_recurrent_weight_amd/csrc/lambda_max.h) checked against
-numpy's symmetric eigen-solver, including windows whose top eigenvector is
-orthogonal to the Lanczos start vector.  CPU only (compiled with g++)."""
+numpy's symmetric eigen-solver: rank-one, repeated and clustered spectra
+(where an iteration from above can step onto or just past the largest root),
+zero rows and duplicates.  CPU only (compiled with g++)."""
 from __future__ import annotations
 
 import ctypes
@@ -42,7 +43,7 @@ def lmax(tmp_path_factory):
 
 
 @pytest.mark.parametrize("kind", ["random", "x_and_minus_x", "duplicates", "zero_rows", "collinear",
-                                  "rms_normalised"])
+                                  "rms_normalised", "clustered", "repeated_top"])
 def test_window_lambda_max_matches_eigvalsh(lmax, kind):
     rng = np.random.default_rng(hash(kind) % 2**32)
     for _ in range(400):
@@ -59,6 +60,14 @@ def test_window_lambda_max_matches_eigvalsh(lmax, kind):
             X[:] = X[0] * rng.choice([-1.0, 1.0, 0.5], size=(n, 1))
         elif kind == "rms_normalised":
             X *= 8.0 / np.linalg.norm(X, axis=1, keepdims=True)
+        elif kind == "clustered":   # near-orthogonal rows of almost equal norm: all eigenvalues close
+            Q, _ = np.linalg.qr(rng.standard_normal((64, n)))
+            X = (Q.T * 8.0) * (1.0 + 1e-4 * rng.standard_normal((n, 1)))
+        elif kind == "repeated_top" and n >= 2:   # the largest eigenvalue twice
+            Q, _ = np.linalg.qr(rng.standard_normal((64, n)))
+            s = rng.uniform(0.1, 1.0, n)
+            s[:2] = 2.0
+            X = (Q * s).T
         G = np.zeros((8, 8), np.float32)
         G[:n, :n] = X @ X.T
         ref = np.linalg.eigvalsh(X @ X.T)[-1]
