@@ -151,6 +151,10 @@ __device__ __forceinline__ void halo_pair(const ChunkAArgs &a, int bh, int tau, 
     sc = xz ? 0.f : (raw ? a1_rms_scale(ss, a.eps_rms, a.phi) : 1.f);
 }
 
+// s_waitcnt immediate (gfx9 encoding) that waits for all vector memory
+// operations: vmcnt 0 (bits 3:0 and 15:14), expcnt 7 and lgkmcnt 15 (no wait)
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // per-token scalars of a chunk (LDS, [kind][token]) and per-pair scalars
 // ([kind][pair row])
 enum { kW = 0, kLg, kSq, kQg, kB, kNtv };
@@ -271,8 +275,21 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
         }
     }
 
+    // the incoming x_0 (features, scale 1) of a continued sequence, loaded
+    // once: a conditional load inside the chunk loop costs every chunk a wait
+    // for all of its outstanding memory operations, the previous chunk's
+    // output stores included
+    uint4 x0r = make_uint4(0, 0, 0, 0);
+    float x0s = 0.f;
+    if (c_begin == 0 && row == 0 && a.xnext_in) x0r = feat8(a.xnext_in + size_t(bh) * D + 8 * part, x0s);
+
     A1Rows<OUT, WIN> rows;
     rows.load(a, c_begin, bh, row, part);
+    // Wait for the first rows here, once.  Otherwise the loop entry merges
+    // this path (loads just issued) with the loop's own (next rows, then this
+    // chunk's output stores), and every chunk would start by waiting for all
+    // memory operations, its predecessor's stores included.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     for (int c = c_begin; c < c_end; ++c) {
         const int c0 = c * C, t = c0 + row;
         // 1. rows to LDS as loaded; RMS scales; the step scalars
@@ -283,7 +300,13 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
             if constexpr (OUT) sq = sumsq8(rows.q);
             const bool qok = t < T, kok = t >= 1 && t <= T, first = t == 0;
             const bool carry_x = first && a.xnext_in;
-            if (carry_x) xr = feat8(a.xnext_in + size_t(bh) * D + 8 * part, sk);   // x_0: features, scale 1
+            // x_0: features, scale 1 (selected per component: a select of
+            // whole vectors is lowered through private memory)
+            xr.x = carry_x ? x0r.x : xr.x;
+            xr.y = carry_x ? x0r.y : xr.y;
+            xr.z = carry_x ? x0r.z : xr.z;
+            xr.w = carry_x ? x0r.w : xr.w;
+            sk = carry_x ? x0s : sk;
             sk = group_sum<8>(sk);
             const float sck = carry_x ? 1.f : (kok ? a1_rms_scale(sk, a.eps_rms, a.phi) : 0.f);
             const uint4 yr = qok ? rows.v : make_uint4(0, 0, 0, 0);
@@ -295,21 +318,22 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
                 scq = qok ? a1_rms_scale(sq, a.eps_rms, a.phi) : 0.f;
                 *reinterpret_cast<uint4 *>(QB + row * PK + 8 * part) = rows.q;
             }
+            // the step scalars on every lane of the row, without branches
+            // (part 0 stores them): a branch here would make the row's inputs
+            // wait for this wave's output stores of the previous chunk too
+            float w, lg;
+            if constexpr (WIN) {
+                w = rows.s0;     // eta_t / B_t and log2 gamma_t from the window pass
+                lg = rows.s1;
+            } else {
+                const bool live = !(t >= T || (first && a.fresh));   // the fresh first step writes nothing
+                const float den = sck * sck * sk + rows.s1 + a.eps;    // |x_t|^2 + lambda_t + eps
+                const float eta = (live && den != 0.f) ? rows.s0 * __builtin_amdgcn_rcpf(den) : 0.f;
+                const float alpha = live ? step_alpha(eta, rows.s1, a.eps_gamma) : 0.f;
+                w = eta;
+                lg = log2_1m(alpha);
+            }
             if (part == 0) {
-                float w, lg;
-                if constexpr (WIN) {
-                    w = rows.s0;     // eta_t / B_t and log2 gamma_t from the window pass
-                    lg = rows.s1;
-                } else {
-                    float eta = 0.f, alpha = 0.f;
-                    if (!(t >= T || (first && a.fresh))) {   // the fresh first step writes nothing
-                        const float den = sck * sck * sk + rows.s1 + a.eps;   // |x_t|^2 + lambda_t + eps
-                        eta = den != 0.f ? rows.s0 * __builtin_amdgcn_rcpf(den) : 0.f;
-                        alpha = step_alpha(eta, rows.s1, a.eps_gamma);
-                    }
-                    w = eta;
-                    lg = log2_1m(alpha);
-                }
                 tv[kW][row] = w;
                 tv[kLg][row] = lg;
                 tv[kSq][row] = scq;
