@@ -104,7 +104,17 @@ def rocprof_summary(workload: str, kernels, stats_db: str, fetch_db: str, write_
         rows = _db_rows(db, "select kernel_name, count(*), avg(value) from counters_collection "
                         f"where counter_name = '{cname}' group by kernel_name")
         return {k: (n, v) for k, n, v in rows}
+    def copy_reading(db, cname):
+        # the largest dispatch of the runtime's copy kernel is the calibration
+        # copy (the inputs' uploads use the same kernel)
+        rows = _db_rows(db, "select count(*), max(value) from counters_collection "
+                        f"where counter_name = '{cname}' and kernel_name = '{COPY_KERNEL}'")
+        return (rows[0][0], rows[0][1]) if rows and rows[0][0] else None
     fetch, write = counter(fetch_db, "FETCH_SIZE"), counter(write_db, "WRITE_SIZE")
+    for table, db, cname in ((fetch, fetch_db, "FETCH_SIZE"), (write, write_db, "WRITE_SIZE")):
+        r = copy_reading(db, cname)
+        if r:
+            table[COPY_KERNEL] = r
     f_copy = (COPY_BYTES / 1024) / fetch[COPY_KERNEL][1] if COPY_KERNEL in fetch else None
     w_copy = (COPY_BYTES / 1024) / write[COPY_KERNEL][1] if COPY_KERNEL in write else None
     lines += ["", "## HBM traffic (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`)", "",
