@@ -92,7 +92,6 @@ __device__ __forceinline__ float phi_scale(float ss, int d, float eps_rms, int p
     return ms > 0.f ? 1.f / sqrtf(ms) : 0.f;
 }
 
-// eta = beta / den (0 if den == 0), alpha = min(eta * lambda, 1 - eps_gamma)
 // Orders LDS traffic between the lanes of one wave (no workgroup barrier):
 // waits for this wave's outstanding LDS operations and keeps the compiler
 // from moving memory accesses across the call.
@@ -114,6 +113,7 @@ __device__ __forceinline__ float log2_1m(float alpha) {
     return __builtin_amdgcn_logf(1.f - alpha);
 }
 
+// eta = beta / den (0 if den == 0), alpha = min(eta * lambda, 1 - eps_gamma)
 __device__ __forceinline__ float step_eta(float beta, float den) { return den != 0.f ? beta / den : 0.f; }
 __device__ __forceinline__ float step_alpha(float eta, float lam, float eps_gamma) {
     return fminf(eta * lam, 1.f - eps_gamma);

@@ -63,3 +63,33 @@ def test_bench_line_contract():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0
     assert d["value"] > 0 and abs(d["value"] - 8 * 12 * 1024 / (d["ms_per_step"] * 1e-3)) < 1e-3 * d["value"]
+
+
+def _fake_db(path, counter, rows, top=()):
+    """A stand-in for a rocprofv3 results database: the two tables and the
+    columns that the summary reads."""
+    import sqlite3
+    con = sqlite3.connect(path)
+    con.execute("create table top_kernels (name text, total_calls int, average real, total_duration real)")
+    con.execute("create table counters_collection (kernel_name text, counter_name text, value real)")
+    con.executemany("insert into top_kernels values (?, ?, ?, ?)", top)
+    con.executemany("insert into counters_collection values (?, ?, ?)", [(k, counter, v) for k, v in rows])
+    con.commit()
+    con.close()
+
+
+def test_rocprof_summary_calibrates_on_the_largest_copy(tmp_path):
+    """The runtime's copy kernel also uploads the inputs: the calibration is
+    the largest of its dispatches (256 MiB read as 131072 KiB by FETCH_SIZE,
+    written as 262144 KiB by WRITE_SIZE gives scale factors 2 and 1)."""
+    k = "void falcon::(anonymous namespace)::a1_output<false>(falcon::ChunkAArgs)"
+    copy = bench.COPY_KERNEL
+    _fake_db(tmp_path / "s.db", "X", [], top=[(k, 3, 50.0, 150.0)])
+    _fake_db(tmp_path / "f.db", "FETCH_SIZE", [(copy, 12.0), (copy, 131072.0), (copy, 40.0), (k, 1000.0), (k, 1000.0)])
+    _fake_db(tmp_path / "w.db", "WRITE_SIZE", [(copy, 8.0), (copy, 262144.0), (k, 500.0)])
+    text = bench.rocprof_summary("c3", ["a1_output"], str(tmp_path / "s.db"), str(tmp_path / "f.db"),
+                                 str(tmp_path / "w.db"), "cmd")
+    assert "scale factors 2.0 (fetch) and 1.0 (write)" in text
+    # per dispatch: 1000 KiB fetched x 2 + 500 KiB written x 1
+    assert "traffic_bytes_per_call: %d" % ((2 * 1000 + 500) * 1024) in text
+    assert "| `%s` | 3 | 50.000 |" % k in text
