@@ -28,7 +28,10 @@
 // Lanes of a solve wave: 4 per column (16 columns per wave), each owning the
 // block positions l = q (mod 4); the in-block sums are quad sums (DPP).
 // One workgroup owns one (head, DS value columns); the raw rows of the next
-// chunk are prefetched while a chunk is processed.
+// chunk are prefetched while a chunk is processed.  It has four waves, or
+// eight for bf16 with d_k = 128 and 32 columns (one workgroup fills a CU's
+// LDS there, and the second four waves share the features, step scalars,
+// Gram, scores, X S and Qh S); the solve runs on the first DS / 16 waves.
 #include "chunk_layout.h"
 #include "kernels.h"
 #include "mma.h"
@@ -95,19 +98,22 @@ __device__ __forceinline__ int kend_for(int n) {   // n rounded up to the MFMA k
     return (n + Mma<E>::KS - 1) / Mma<E>::KS * Mma<E>::KS;
 }
 
-template <class E, int DK, int DS>
-__global__ __launch_bounds__(256) void chunk_f2(ChunkF2Args a, int nslice) {
+template <class E, int DK, int DS, int NW>
+__global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
+    constexpr int NT = 64 * NW;     // threads; NW waves
+    constexpr int TPR = NT / C;     // threads per token row
     constexpr int PD = Pad<E>::v;
     constexpr int LK = DK + PD;     // [t][d] rows
     constexpr int LC = C + PD;      // [.][token] rows
     constexpr int RS = DS + 1;      // fp32 [t][j] rows
     constexpr int SVS = C + 1;      // float4 [j][t] rows (odd pitch: no bank conflicts)
     constexpr int NCT = DS / 16;    // column tiles (= solve waves)
-    constexpr int EPT = DK / 4;     // features per thread (4 threads per row)
+    constexpr int EPT = DK / TPR;   // features per thread
     constexpr int NV = EPT / Io<E>::per16;
-    constexpr int YE = DS / 4;      // value columns per thread
+    constexpr int YE = DS / TPR;    // value columns per thread
     constexpr int NB = YE / 4;      // 16-byte vectors of gains per thread
-    constexpr int NDT = DK / 64;    // state d tiles per wave
+    constexpr int NDT = DK / (16 * NW);   // state d tiles per wave
+    static_assert(NDT >= 1 && NB >= 1, "the thread mapping covers the tiles and gains");
     static_assert(YE * sizeof(E) == 16 || YE * sizeof(E) == 8, "values per thread fit one 16- or 8-byte load");
 
     __shared__ __align__(16) E XB[C * LK];     // x rows
@@ -142,7 +148,7 @@ __global__ __launch_bounds__(256) void chunk_f2(ChunkF2Args a, int nslice) {
     const float *lamg = a.lambda + size_t(bh) * T;
 
     // ---- raw rows of the next chunk (thread: row, part), prefetched ----
-    const int row = tid >> 2, part = tid & 3;
+    const int row = tid / TPR, part = tid % TPR;
     uint4 rq[NV], rk[NV], ry, rb[NB];
     float rlam;
     auto prefetch = [&](int c) {   // unconditional loads from rows clamped into [0, T)
@@ -170,18 +176,18 @@ __global__ __launch_bounds__(256) void chunk_f2(ChunkF2Args a, int nslice) {
 
     // the tiles above the diagonal are never written but are read (times
     // zero) by the bf16 MFMA k steps of 32: they must hold zeros, not NaNs
-    for (int idx = tid; idx < C * LC; idx += 256) {
+    for (int idx = tid; idx < C * LC; idx += NT) {
         st(GB, idx, 0.f);
         st(PB, idx, 0.f);
     }
 
-    // ---- state: d tiles {wave, wave + 4, ..} x all column tiles ----
+    // ---- state: d tiles {wave, wave + NW, ..} x all column tiles ----
     f32x4 S[NDT][NCT];
 #pragma unroll
     for (int m = 0; m < NDT; ++m)
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-            const int dbase = 16 * (wave + 4 * m);
+            const int dbase = 16 * (wave + NW * m);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int d = dbase + g4 + r;
@@ -219,8 +225,8 @@ __global__ __launch_bounds__(256) void chunk_f2(ChunkF2Args a, int nslice) {
                 sq += qv[e] * qv[e];
                 sk += xv[e] * xv[e];
             }
-            const float scq = phi_scale(group_sum<4>(sq), DK, a.eps_rms, a.phi);
-            const float sck = first ? 1.f : phi_scale(group_sum<4>(sk), DK, a.eps_rms, a.phi);
+            const float scq = phi_scale(group_sum<TPR>(sq), DK, a.eps_rms, a.phi);
+            const float sck = first ? 1.f : phi_scale(group_sum<TPR>(sk), DK, a.eps_rms, a.phi);
             float n2 = 0.f;
 #pragma unroll
             for (int e = 0; e < EPT; ++e) {
@@ -228,7 +234,7 @@ __global__ __launch_bounds__(256) void chunk_f2(ChunkF2Args a, int nslice) {
                 qv[e] *= scq;
                 n2 += xv[e] * xv[e];
             }
-            n2 = group_sum<4>(n2);
+            n2 = group_sum<TPR>(n2);
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
                 *reinterpret_cast<uint4 *>(XB + row * LK + part * EPT + v * Io<E>::per16) =
@@ -261,15 +267,15 @@ __global__ __launch_bounds__(256) void chunk_f2(ChunkF2Args a, int nslice) {
                 GAM[q] = 1.f - alpha;
                 EB[q] = log2_1m(alpha);   // log2 gamma
             }
-            for (int idx = tid; idx < DS * LC; idx += 256) st(WT, idx, 0.f);
+            for (int idx = tid; idx < DS * LC; idx += NT) st(WT, idx, 0.f);
             if (c + 1 < a.nchunks) prefetch(c + 1);
         }
         __syncthreads();
 
         // ---- P2a: per-column prefixes; Gram, scores, XS, Qh S on MFMA ----
 #pragma unroll
-        for (int n = 0; n < DS / 4; ++n) {
-            const int j = wave + 4 * n;   // lane = token
+        for (int n = 0; n < DS / NW; ++n) {
+            const int j = wave + NW * n;   // lane = token
             const float lg = EB[lane * RS + j];
             EB[lane * RS + j] = __builtin_amdgcn_exp2f(wave_inclusive_scan(lg));
             const float el = __builtin_amdgcn_exp2f(row_scan(lg));   // block-local E_t
@@ -278,8 +284,9 @@ __global__ __launch_bounds__(256) void chunk_f2(ChunkF2Args a, int nslice) {
             if ((lane & 15) != 15) SV[j * SVS + lane + 1].z = el;
         }
 #pragma unroll
-        for (int m = 0; m < 5; ++m) {
-            const int job = wave + 4 * m;   // 0-9 Gram tiles, 10-19 score tiles
+        for (int m = 0; m < (20 + NW - 1) / NW; ++m) {
+            const int job = wave + NW * m;   // 0-9 Gram tiles, 10-19 score tiles
+            if (job >= 20) break;
             const bool isG = job < 10;
             const int tt = isG ? job : job - 10;
             const int I = (0xffa94 >> (2 * tt)) & 3, J = (0xe4910 >> (2 * tt)) & 3;
@@ -296,12 +303,18 @@ __global__ __launch_bounds__(256) void chunk_f2(ChunkF2Args a, int nslice) {
                 }
             }
         }
-        f32x4 xs[NCT], qs[NCT];   // token rows 16 wave .. + 15
+        // X S and Qh S for token rows 16 tw .. + 15: with eight waves, waves
+        // 0-3 take X S and waves 4-7 Qh S
+        const int tw = wave & 3;
+        const bool doX = NW == 4 || wave < 4, doQ = NW == 4 || wave >= 4;
+        f32x4 xs[NCT], qs[NCT];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            xs[ct] = Mma<E>::run(z, XB + 16 * wave * LK, LK, ST + 16 * ct * LK, LK, 0, DK);
-            qs[ct] = Mma<E>::run(z, QB + 16 * wave * LK, LK, ST + 16 * ct * LK, LK, 0, DK);
+            xs[ct] = z;
+            qs[ct] = z;
+            if (doX) xs[ct] = Mma<E>::run(z, XB + 16 * tw * LK, LK, ST + 16 * ct * LK, LK, 0, DK);
+            if (doQ) qs[ct] = Mma<E>::run(z, QB + 16 * tw * LK, LK, ST + 16 * ct * LK, LK, 0, DK);
         }
         __syncthreads();
 
@@ -310,10 +323,12 @@ __global__ __launch_bounds__(256) void chunk_f2(ChunkF2Args a, int nslice) {
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = 16 * wave + g4 + r, j = 16 * ct + col;
-                const float ebp = t > 0 ? EB[(t - 1) * RS + j] : 1.f;
-                SV[j * SVS + t].y -= ebp * xs[ct][r];
-                OA[t * RS + j] = EB[t * RS + j] * qs[ct][r];
+                const int t = 16 * tw + g4 + r, j = 16 * ct + col;
+                if (doX) {
+                    const float ebp = t > 0 ? EB[(t - 1) * RS + j] : 1.f;
+                    SV[j * SVS + t].y -= ebp * xs[ct][r];
+                }
+                if (doQ) OA[t * RS + j] = EB[t * RS + j] * qs[ct][r];
             }
         __syncthreads();
 
@@ -438,7 +453,7 @@ __global__ __launch_bounds__(256) void chunk_f2(ChunkF2Args a, int nslice) {
         for (int m = 0; m < NDT; ++m)
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                const int dbase = 16 * (wave + 4 * m);
+                const int dbase = 16 * (wave + NW * m);
                 const float gC = EB[63 * RS + 16 * ct + col];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) S[m][ct][r] *= gC;
@@ -456,7 +471,7 @@ __global__ __launch_bounds__(256) void chunk_f2(ChunkF2Args a, int nslice) {
             for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int d = 16 * (wave + 4 * m) + g4 + r;
+                    const int d = 16 * (wave + NW * m) + g4 + r;
                     a.S_out[(size_t(bh) * DK + d) * DV + j0 + 16 * ct + col] = S[m][ct][r];
                 }
     }
@@ -470,11 +485,11 @@ __global__ __launch_bounds__(256) void chunk_f2(ChunkF2Args a, int nslice) {
     }
 }
 
-template <class E, int DK, int DS>
+template <class E, int DK, int DS, int NW = 4>
 void launch_t(const ChunkF2Args &a, hipStream_t s, Marks *m) {
     const int nslice = a.dv / DS;
     const int blocks = ((a.BH + 7) / 8) * 8 * nslice;
-    chunk_f2<E, DK, DS><<<blocks, 256, 0, s>>>(a, nslice);
+    chunk_f2<E, DK, DS, NW><<<blocks, 64 * NW, 0, s>>>(a, nslice);
     m->mark(s);
 }
 
@@ -485,7 +500,7 @@ void launch_chunk_f2(const ChunkF2Args &a, bool bf16, hipStream_t s, Marks *m) {
         // 32 value columns per workgroup when d_v allows it
         if (a.dv % 32 == 0) {
             if (a.dk == 64) launch_t<bf16_t, 64, 32>(a, s, m);
-            else launch_t<bf16_t, 128, 32>(a, s, m);
+            else launch_t<bf16_t, 128, 32, 8>(a, s, m);   // eight waves, 8 threads per row
         } else {
             if (a.dk == 64) launch_t<bf16_t, 64, 16>(a, s, m);
             else launch_t<bf16_t, 128, 16>(a, s, m);

@@ -463,6 +463,32 @@ def test_chunk_f2_head_dims(dk, dv, dtype):
     check(gu.small("F2", dtype, B=1, H=3, T=300, dk=dk, dv=dv, chunk=64))
 
 
+@pytest.mark.parametrize("T", [1, 17, 64, 65, 200])
+@pytest.mark.parametrize("dv", [32, 128])
+def test_chunk_f2_d128_lengths(dv, T):
+    """bf16, d_k = 128, 32-column slices (the eight-wave workgroup): ragged
+    lengths across the solve blocks and the chunks."""
+    check(gu.small("F2", "bf16", B=1, H=3, T=T, dk=128, dv=dv, chunk=64, seed=T + dv))
+
+
+@pytest.mark.parametrize("split", [3, 64, 100])
+def test_chunk_f2_d128_continuation(split):
+    """bf16, d_k = 128 (eight-wave workgroup): two calls carrying (S, x_next)
+    match the oracle over the whole sequence."""
+    import torch
+    w = gu.small("F2", "bf16", B=1, H=2, T=200, dk=128, dv=64, chunk=64, seed=21)
+    inp = gu.make(w)
+    dev = gu.to_device(inp, w)
+    a = {k: v[:, :, :split].contiguous() for k, v in dev.items()}
+    b = {k: v[:, :, split:].contiguous() for k, v in dev.items()}
+    o1, st1 = gu.run_gpu(w.with_(seqlen=split), a)
+    o2, st2 = gu.run_gpu(w.with_(seqlen=200 - split), b, state=st1)
+    heads = np.arange(2)
+    o_ref, st_ref = gu.oracle_heads(w, inp, heads)
+    eo, es = gu.compare(w, heads, torch.cat([o1, o2], 2), st2, o_ref, st_ref)
+    assert eo <= gu.tol_for(w) and es <= gu.tol_for(w), (eo, es)
+
+
 def test_chunk_f2_equal_gains_is_falcon1():
     """With the same gain in every column, Falcon-2 is Falcon-1: the two
     chunk kernels agree to fp32 rounding."""
