@@ -28,11 +28,13 @@ FALCON_HD inline float psd_lambda_max(const float (&G)[8][8], int n) {
     for (int i = 0; i < 8; ++i) tr += i < n ? G[i][i] : 0.f;
     if (!(tr > 0.f)) return 0.f;
     const float inv = 1.f / tr;   // work on G / trace: eigenvalues in [0, 1]
+    // A stays symmetric under the reflections: only its lower triangle
+    // (j <= i) is read, kept and updated, and only G's lower triangle is read
     float A[8][8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) A[i][j] = (i < n && j < n) ? G[i][j] * inv : 0.f;
+        for (int j = 0; j <= i; ++j) A[i][j] = (i < n && j < n) ? G[i][j] * inv : 0.f;
 #pragma unroll
     for (int k = 0; k < 6; ++k) {
         // reflect x = A[k+1..7][k] onto (alpha, 0, ..., 0)
@@ -52,7 +54,7 @@ FALCON_HD inline float psd_lambda_max(const float (&G)[8][8], int n) {
         for (int i = k + 1; i < 8; ++i) {
             float s = 0.f;
 #pragma unroll
-            for (int j = k + 1; j < 8; ++j) s += A[i][j] * v[j];
+            for (int j = k + 1; j < 8; ++j) s += (j <= i ? A[i][j] : A[j][i]) * v[j];
             p[i] = beta * s;
         }
         float vp = 0.f;
@@ -64,7 +66,7 @@ FALCON_HD inline float psd_lambda_max(const float (&G)[8][8], int n) {
 #pragma unroll
         for (int i = k + 1; i < 8; ++i)
 #pragma unroll
-            for (int j = k + 1; j < 8; ++j) A[i][j] -= v[i] * p[j] + p[i] * v[j];
+            for (int j = k + 1; j <= i; ++j) A[i][j] -= v[i] * p[j] + p[i] * v[j];
         A[k + 1][k] = beta > 0.f ? alpha : x0;
     }
     float al[8], be[8];
