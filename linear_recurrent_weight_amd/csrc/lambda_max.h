@@ -12,6 +12,24 @@
 
 namespace falcon {
 
+// Reciprocal and square root: the hardware's approximations (about one ulp)
+// in GPU code, where the exact sequences sit on the dependency chain of every
+// step; the exact operations in the host build that the eigenvalue tests use.
+FALCON_HD inline float lm_rcp(float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_rcpf(x);
+#else
+    return 1.f / x;
+#endif
+}
+FALCON_HD inline float lm_sqrt(float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_sqrtf(x);
+#else
+    return sqrtf(x);
+#endif
+}
+
 // Largest eigenvalue of a symmetric positive semi-definite n x n matrix
 // (n <= 8, entries beyond n ignored), fp32.  The matrix, zero-padded to
 // 8 x 8 (the padding only adds zero eigenvalues) and scaled by its trace,
@@ -27,7 +45,7 @@ FALCON_HD inline float psd_lambda_max(const float (&G)[8][8], int n) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) tr += i < n ? G[i][i] : 0.f;
     if (!(tr > 0.f)) return 0.f;
-    const float inv = 1.f / tr;   // work on G / trace: eigenvalues in [0, 1]
+    const float inv = lm_rcp(tr);   // work on G / trace: eigenvalues in [0, 1]
     // A stays symmetric under the reflections: only its lower triangle
     // (j <= i) is read, kept and updated, and only G's lower triangle is read
     float A[8][8];
@@ -42,13 +60,13 @@ FALCON_HD inline float psd_lambda_max(const float (&G)[8][8], int n) {
 #pragma unroll
         for (int i = k + 1; i < 8; ++i) xx += A[i][k] * A[i][k];
         const float x0 = A[k + 1][k];
-        const float nx = sqrtf(xx);
+        const float nx = lm_sqrt(xx);
         const float alpha = x0 > 0.f ? -nx : nx;
         float v[8];
 #pragma unroll
         for (int i = k + 1; i < 8; ++i) v[i] = i == k + 1 ? x0 - alpha : A[i][k];
         const float vv = 2.f * (xx - alpha * x0);   // |v|^2
-        const float beta = vv > 1e-30f ? 2.f / vv : 0.f;
+        const float beta = vv > 1e-30f ? 2.f * lm_rcp(vv) : 0.f;
         float p[8];
 #pragma unroll
         for (int i = k + 1; i < 8; ++i) {
@@ -101,11 +119,11 @@ FALCON_HD inline float psd_lambda_max(const float (&G)[8][8], int n) {
         // above every root q > 0 and q'/q > 0; a rounding step onto or past
         // the largest root ends the iteration there
         if (!(p1 > 0.f)) break;
-        const float ip = 1.f / p1;
+        const float ip = lm_rcp(p1);
         const float g = d1 * ip, h = g * g - e1 * ip;
         if (!(g > 0.f)) break;
-        const float den = g + sqrtf(fmaxf(7.f * (8.f * h - g * g), 0.f));
-        const float step = 8.f / den;
+        const float den = g + lm_sqrt(fmaxf(7.f * (8.f * h - g * g), 0.f));
+        const float step = 8.f * lm_rcp(den);
         const float xn = x - step;
         if (!(xn < x)) break;   // monotone from above: stop when no progress
         x = xn;
