@@ -349,6 +349,8 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
                 wave_lds_sync();
                 if (sep) {
                     float w[4] = {0.f, 0.f, 0.f, 0.f};   // w_l = u_l / E_l, l = 4 m + q
+                    const float own[4] = {q == 0 ? 1.f : 0.f, q == 1 ? 1.f : 0.f, q == 2 ? 1.f : 0.f,
+                                          q == 3 ? 1.f : 0.f};
                     // operands of step i + 1 are loaded while step i computes
                     float4 sv_n = SV[j * SVS + 16 * I], gq_n = GDq[(I * 16) * 4 + q];
                     float h_n = I > 0 ? H0[jj] : 0.f;
@@ -371,7 +373,10 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
                         const float sum = quad_sum(part_s) + h;
                         const float u = sv.x * (sv.y - sv.z * sum);
                         const float wi = u * __builtin_amdgcn_rcpf(sv.w);
-                        w[i >> 2] = q == (i & 3) ? wi : w[i >> 2];
+                        // the owner lane of position i adds w_i to its entry,
+                        // which is still zero: a multiply-add by a 0/1 lane
+                        // mask keeps the step free of branches
+                        w[i >> 2] = fmaf(own[i & 3], wi, w[i >> 2]);
                     }
 #pragma unroll
                     for (int m = 0; m < 4; ++m) st(WT, size_t(j) * LC + 16 * I + 4 * m + q, w[m]);
