@@ -276,19 +276,17 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
     }
 
     // the incoming x_0 (features, scale 1) of a continued sequence, loaded
-    // once: a conditional load inside the chunk loop costs every chunk a wait
-    // for all of its outstanding memory operations, the previous chunk's
-    // output stores included
+    // once, outside the chunk loop (a conditional load inside it added a wait
+    // for every outstanding memory operation to each chunk)
     uint4 x0r = make_uint4(0, 0, 0, 0);
     float x0s = 0.f;
     if (c_begin == 0 && row == 0 && a.xnext_in) x0r = feat8(a.xnext_in + size_t(bh) * D + 8 * part, x0s);
 
     A1Rows<OUT, WIN> rows;
     rows.load(a, c_begin, bh, row, part);
-    // Wait for the first rows here, once.  Otherwise the loop entry merges
-    // this path (loads just issued) with the loop's own (next rows, then this
-    // chunk's output stores), and every chunk would start by waiting for all
-    // memory operations, its predecessor's stores included.
+    // Wait for the first rows here, once, so that the loop is entered with
+    // no loads pending: the compiler then waits for each row of the next
+    // chunk as it is needed instead of for all of them at the loop head.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     for (int c = c_begin; c < c_end; ++c) {
         const int c0 = c * C, t = c0 + row;
@@ -318,9 +316,8 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
                 scq = qok ? a1_rms_scale(sq, a.eps_rms, a.phi) : 0.f;
                 *reinterpret_cast<uint4 *>(QB + row * PK + 8 * part) = rows.q;
             }
-            // the step scalars on every lane of the row, without branches
-            // (part 0 stores them): a branch here would make the row's inputs
-            // wait for this wave's output stores of the previous chunk too
+            // the step scalars, formed on every lane of the row without
+            // branches; part 0 stores them
             float w, lg;
             if constexpr (WIN) {
                 w = rows.s0;     // eta_t / B_t and log2 gamma_t from the window pass
