@@ -252,9 +252,24 @@ __global__ __launch_bounds__(256) void f3_scan(ChunkF3Args a, int nslice) {
             const int kend = (16 * wave + 16 + Mma<E>::KS - 1) / Mma<E>::KS * Mma<E>::KS;
             acc = Mma<E>::run(acc, Tp + 16 * wave * C, C, R0t, LT, 0, kend);
             st4(Ut + (lane & 15) * LT + 16 * wave + 4 * (lane >> 4), acc);
-            for (int idx = tid; idx < C * DK; idx += 256) {
-                const int i = idx / DK, d = idx % DK;
-                st(Xht, d * LT + i, scal[C + i] * ld(X, idx));
+            // 16 bytes of a row of X per thread and pass, all passes' loads
+            // issued before the first transposed store
+            constexpr int VEC = 16 / int(sizeof(E)), NXV = C * DK / VEC / 256;
+            uint4 xr[NXV];
+#pragma unroll
+            for (int u = 0; u < NXV; ++u) xr[u] = *reinterpret_cast<const uint4 *>(X + (tid + 256 * u) * VEC);
+#pragma unroll
+            for (int u = 0; u < NXV; ++u) {
+                const int idx = (tid + 256 * u) * VEC, i = idx / DK, d = idx % DK;
+                const float sc = scal[C + i];
+                const uint32_t w[4] = {xr[u].x, xr[u].y, xr[u].z, xr[u].w};
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    float f;
+                    if constexpr (sizeof(E) == 2) f = __uint_as_float(e & 1 ? w[e >> 1] & 0xffff0000u : w[e >> 1] << 16);
+                    else f = __uint_as_float(w[e]);
+                    st(Xht, size_t(d + e) * LT + i, sc * f);
+                }
             }
         }
         __syncthreads();
