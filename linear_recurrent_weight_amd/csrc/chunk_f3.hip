@@ -96,18 +96,41 @@ __global__ __launch_bounds__(256) void f3_prep(ChunkF3Args a) {
         wr[r] = w;
         tr[r] = tl;
     }
-    // stacked features and token queries
-    for (int idx = tid; idx < C * DK; idx += 256) {
-        const int r = idx / DK, e = idx % DK;
-        const int tl = rm.token(r), p = rm.pair(c, r);
-        float x = 0.f;
-        if (tl >= 0) {
-            if (p >= 0) x = ld(xn, size_t(p) * DK + e);
-            else if (p >= -a.n_tail_in) x = a.tailx_in[(size_t(bh) * halo + halo + p) * DK + e];
+    // stacked features and token queries, 16 bytes of a row per thread and
+    // pass; all passes' loads (rows clamped into the padded feature buffers)
+    // are issued before the first store
+    {
+        constexpr int VEC = 16 / int(sizeof(E)), NXV = C * DK / VEC / 256;
+        const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+        uint4 xv[NXV], qv[NXV];
+#pragma unroll
+        for (int u = 0; u < NXV; ++u) {
+            const int idx = (tid + 256 * u) * VEC, r = idx / DK, e = idx % DK;
+            const int p = rm.pair(c, r);
+            xv[u] = *reinterpret_cast<const uint4 *>(xn + size_t(p > 0 ? p : 0) * DK + e);
+            qv[u] = *reinterpret_cast<const uint4 *>(qn + size_t(c * ct + r) * DK + e);
         }
-        st(Xs, size_t(r) * LK + e, x);
-        st(Xg, idx, x);
-        st(Qs, size_t(r) * LK + e, r < ct ? ld(qn, size_t(c * ct + r) * DK + e) : 0.f);
+#pragma unroll
+        for (int u = 0; u < NXV; ++u) {
+            const int idx = (tid + 256 * u) * VEC, r = idx / DK, e = idx % DK;
+            const int tl = rm.token(r), p = rm.pair(c, r);
+            uint4 x = (tl >= 0 && p >= 0) ? xv[u] : z4;
+            if (tl >= 0 && p < 0 && p >= -a.n_tail_in) {   // an incoming tail pair (fp32)
+                const float *src = a.tailx_in + (size_t(bh) * halo + halo + p) * DK + e;
+                uint32_t w[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    if constexpr (sizeof(E) == 2)
+                        w[k] = uint32_t(f32_to_bf16(src[2 * k])) | (uint32_t(f32_to_bf16(src[2 * k + 1])) << 16);
+                    else
+                        w[k] = __float_as_uint(src[k]);
+                }
+                x = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+            *reinterpret_cast<uint4 *>(Xs + size_t(r) * LK + e) = x;
+            *reinterpret_cast<uint4 *>(Xg + idx) = x;
+            *reinterpret_cast<uint4 *>(Qs + size_t(r) * LK + e) = r < ct ? qv[u] : z4;
+        }
     }
     __syncthreads();
     {
@@ -166,11 +189,34 @@ __global__ __launch_bounds__(256) void f3_prep(ChunkF3Args a) {
     // 3. inverse of the unit-lower system
     unit_lower_inverse64(Lm, Tm, Mt, kLs);
 
-    // 4. Tp = L^{-1} diag(w) and the scores, in the storage type
-    for (int idx = tid; idx < C * C; idx += 256) {
-        const int i = idx / C, j = idx % C;
-        st(Tp, idx, j <= i ? Tm[i * kLs + j] * wr[j] : 0.f);
-        st(Pg, idx, Pm[i * kLs + j]);
+    // 4. Tp = L^{-1} diag(w) and the scores, in the storage type, 16 bytes
+    //    per thread and store
+    {
+        constexpr int VEC = 16 / int(sizeof(E));
+#pragma unroll
+        for (int u = 0; u < C * C / VEC / 256; ++u) {
+            const int idx = (tid + 256 * u) * VEC, i = idx / C, j0 = idx % C;
+            float tv[VEC], pv[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const int j = j0 + e;
+                tv[e] = j <= i ? Tm[i * kLs + j] * wr[j] : 0.f;
+                pv[e] = Pm[i * kLs + j];
+            }
+            uint32_t wt[4], wp[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if constexpr (sizeof(E) == 2) {
+                    wt[k] = uint32_t(f32_to_bf16(tv[2 * k])) | (uint32_t(f32_to_bf16(tv[2 * k + 1])) << 16);
+                    wp[k] = uint32_t(f32_to_bf16(pv[2 * k])) | (uint32_t(f32_to_bf16(pv[2 * k + 1])) << 16);
+                } else {
+                    wt[k] = __float_as_uint(tv[k]);
+                    wp[k] = __float_as_uint(pv[k]);
+                }
+            }
+            *reinterpret_cast<uint4 *>(Tp + idx) = make_uint4(wt[0], wt[1], wt[2], wt[3]);
+            *reinterpret_cast<uint4 *>(Pg + idx) = make_uint4(wp[0], wp[1], wp[2], wp[3]);
+        }
     }
 }
 
