@@ -260,81 +260,132 @@ __global__ __launch_bounds__(256) void f3_scan(ChunkF3Args a, int nslice) {
     int cur = 0;
     __syncthreads();
 
+    // Each chunk's operands from memory (rows of X, Tp, Qh and Pg as MFMA
+    // fragments, the transposed-copy pieces of X, the scalars and the values
+    // y) are loaded for the next chunk right after their last use in this
+    // one, so their latency overlaps the rest of the chunk.
+    using F = MmaFrag<E>;
+    using FT = typename F::T;
+    constexpr int NKD = DK / F::KS, NKC = C / F::KS;
+    constexpr int VEC = 16 / int(sizeof(E)), NXV = C * DK / VEC / 256;
+    const int kend2 = (16 * wave + 16 + F::KS - 1) / F::KS;   // k steps of Tp's lower rows
+    const bool outw = 16 * wave < ct;                          // wave with output rows
+    auto chunk_ops = [&](int cc) { return opsb + size_t(cc) * a.chunk_bytes; };
+    auto Xof = [&](int cc) { return reinterpret_cast<const E *>(chunk_ops(cc) + chunk_f3_x_off(sizeof(E))); };
+    auto Sof = [&](int cc) { return reinterpret_cast<const float *>(chunk_ops(cc) + chunk_f3_scal_off(DK, sizeof(E))); };
+
+    FT xa[NKD], ta[NKC], qb[NKD], pb[NKC];
+    uint4 xr[NXV];
+    float s1[4], y1[4], s2[NXV], s3 = 0.f, s4;
+    auto load1 = [&](int cc) {   // phase 1: X rows 16 w .., scal[i], y_i
+        const E *X = Xof(cc);
+        const float *scal = Sof(cc);
+#pragma unroll
+        for (int k = 0; k < NKD; ++k) xa[k] = F::load(X + size_t(16 * wave) * DK, DK, k * F::KS);
+        const int j = lane & 15;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * wave + 4 * (lane >> 4) + r;
+            const int p = rm.pair(cc, i);
+            float y = 0.f;
+            if (rm.token(i) >= 0) {
+                if (p >= 0) {
+                    if (p < T) y = ld(V, size_t(p) * dv + j0 + j);
+                } else if (p >= -a.n_tail_in) {
+                    y = a.taily_in[(size_t(bh) * halo + halo + p) * dv + j0 + j];
+                }
+            }
+            y1[r] = y;
+            s1[r] = scal[i];
+        }
+    };
+    auto load2 = [&](int cc) {   // phase 2: Tp rows 16 w .., X pieces and their scales
+        const E *Tp = reinterpret_cast<const E *>(chunk_ops(cc) + chunk_f1_tp_off());
+        const E *X = Xof(cc);
+        const float *scal = Sof(cc);
+#pragma unroll
+        for (int k = 0; k < NKC; ++k)
+            if (k < kend2) ta[k] = F::load(Tp + size_t(16 * wave) * C, C, k * F::KS);
+#pragma unroll
+        for (int u = 0; u < NXV; ++u) {
+            const int idx = (tid + 256 * u) * VEC;
+            xr[u] = *reinterpret_cast<const uint4 *>(X + idx);
+            s2[u] = scal[C + idx / DK];
+        }
+    };
+    auto load3 = [&](int cc) {   // phase 3: Qh and Pg rows 16 w .., the scalars
+        const float *scal = Sof(cc);
+        if (outw) {
+            const E *Pg = reinterpret_cast<const E *>(chunk_ops(cc) + chunk_f1_p_off(sizeof(E)));
+            const E *Qh = Qall + size_t(cc) * ct * DK;   // 64 rows stay inside the padded buffer
+#pragma unroll
+            for (int k = 0; k < NKD; ++k) qb[k] = F::load(Qh + size_t(16 * wave) * DK, DK, k * F::KS);
+#pragma unroll
+            for (int k = 0; k < NKC; ++k) pb[k] = F::load(Pg + size_t(16 * wave) * C, C, k * F::KS);
+            s3 = scal[2 * C + 16 * wave + (lane & 15)];
+        }
+        s4 = scal[3 * C];
+    };
+    load1(0);
+    load2(0);
+    load3(0);
+
     for (int c = 0; c < a.nchunks; ++c) {
-        const char *ops = opsb + size_t(c) * a.chunk_bytes;
-        const E *Tp = reinterpret_cast<const E *>(ops + chunk_f1_tp_off());
-        const E *Pg = reinterpret_cast<const E *>(ops + chunk_f1_p_off(sizeof(E)));
-        const E *X = reinterpret_cast<const E *>(ops + chunk_f3_x_off(sizeof(E)));
-        const float *scal = reinterpret_cast<const float *>(ops + chunk_f3_scal_off(DK, sizeof(E)));
-        const E *Qh = Qall + size_t(c) * ct * DK;   // 64 rows stay inside the padded buffer
+        const int cn = c + 1 < a.nchunks ? c + 1 : c;   // the next chunk (the last reloads itself)
 
         // phase 1: R0 = Y - diag(Gamma_{t-1}) X S_0 for stacked rows 16w..16w+15
         {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = Mma<E>::run(acc, X + size_t(16 * wave) * DK, DK, St[cur], LS, 0, DK);
+#pragma unroll
+            for (int k = 0; k < NKD; ++k) acc = F::mma(xa[k], F::load(St[cur], LS, k * F::KS), acc);
             const int j = lane & 15;
             f32x4 r0;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * wave + 4 * (lane >> 4) + r;
-                const int p = rm.pair(c, i);
-                float y = 0.f;
-                if (rm.token(i) >= 0) {
-                    if (p >= 0) {
-                        if (p < T) y = ld(V, size_t(p) * dv + j0 + j);
-                    } else if (p >= -a.n_tail_in) {
-                        y = a.taily_in[(size_t(bh) * halo + halo + p) * dv + j0 + j];
-                    }
-                }
-                r0[r] = y - scal[i] * acc[r];
-            }
+            for (int r = 0; r < 4; ++r) r0[r] = y1[r] - s1[r] * acc[r];
             st4(R0t + j * LT + 16 * wave + 4 * (lane >> 4), r0);
         }
+        load1(cn);
         __syncthreads();
 
         // phase 2: U = Tp R0; (diag(e^{b_C - b_t}) X)^T
         {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const int kend = (16 * wave + 16 + Mma<E>::KS - 1) / Mma<E>::KS * Mma<E>::KS;
-            acc = Mma<E>::run(acc, Tp + 16 * wave * C, C, R0t, LT, 0, kend);
-            st4(Ut + (lane & 15) * LT + 16 * wave + 4 * (lane >> 4), acc);
-            // 16 bytes of a row of X per thread and pass, all passes' loads
-            // issued before the first transposed store
-            constexpr int VEC = 16 / int(sizeof(E)), NXV = C * DK / VEC / 256;
-            uint4 xr[NXV];
 #pragma unroll
-            for (int u = 0; u < NXV; ++u) xr[u] = *reinterpret_cast<const uint4 *>(X + (tid + 256 * u) * VEC);
+            for (int k = 0; k < NKC; ++k)
+                if (k < kend2) acc = F::mma(ta[k], F::load(R0t, LT, k * F::KS), acc);
+            st4(Ut + (lane & 15) * LT + 16 * wave + 4 * (lane >> 4), acc);
 #pragma unroll
             for (int u = 0; u < NXV; ++u) {
                 const int idx = (tid + 256 * u) * VEC, i = idx / DK, d = idx % DK;
-                const float sc = scal[C + i];
                 const uint32_t w[4] = {xr[u].x, xr[u].y, xr[u].z, xr[u].w};
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
                     float f;
                     if constexpr (sizeof(E) == 2) f = __uint_as_float(e & 1 ? w[e >> 1] & 0xffff0000u : w[e >> 1] << 16);
                     else f = __uint_as_float(w[e]);
-                    st(Xht, size_t(d + e) * LT + i, sc * f);
+                    st(Xht, size_t(d + e) * LT + i, s2[u] * f);
                 }
             }
         }
+        load2(cn);
         __syncthreads();
 
         // phase 3a: outputs of the chunk's tokens (rows 16w..16w+15 < Ct)
-        if (16 * wave < ct) {
+        if (outw) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = Mma<E>::run(acc, St[cur], LS, Qh + size_t(16 * wave) * DK, DK, 0, DK);
-            const int i = 16 * wave + (lane & 15);
-            const float gi = scal[2 * C + i];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] *= gi;
-            acc = Mma<E>::run(acc, Ut, LT, Pg + size_t(16 * wave) * C, C, 0, C);
+            for (int k = 0; k < NKD; ++k) acc = F::mma(F::load(St[cur], LS, k * F::KS), qb[k], acc);
+            const int i = 16 * wave + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] *= s3;
+#pragma unroll
+            for (int k = 0; k < NKC; ++k) acc = F::mma(F::load(Ut, LT, k * F::KS), pb[k], acc);
             const int t = c * ct + i;
             if (i < ct && t < T) st4(O + size_t(t) * dv + j0 + 4 * (lane >> 4), acc);
         }
         // phase 3b: S = Gamma_C S + (diag(e^{b_C - b_t}) X)^T U
         {
-            const float gC = scal[3 * C];
+            const float gC = s4;
             if (owns) {
 #pragma unroll
                 for (int m = 0; m < NT; ++m) {
@@ -346,6 +397,7 @@ __global__ __launch_bounds__(256) void f3_scan(ChunkF3Args a, int nslice) {
                 }
             }
         }
+        load3(cn);
         cur ^= 1;
         __syncthreads();
     }

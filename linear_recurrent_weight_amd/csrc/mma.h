@@ -43,6 +43,35 @@ template <> struct Mma<float> {
     }
 };
 
+// One k step of an MFMA operand held in registers, for operands that are
+// loaded ahead of their use: row lane % 16 of a row-major [16 x K] tile,
+// k = k0 + (the lane's k group).  Same layouts as Mma<E>::run.
+template <class E> struct MmaFrag;
+
+template <> struct MmaFrag<bf16_t> {
+    using T = bf16x8;
+    static constexpr int KS = 32;
+    __device__ static T load(const bf16_t *M, int ld, int k0) {
+        const int lane = threadIdx.x & 63;
+        return *reinterpret_cast<const bf16x8 *>(M + (lane & 15) * ld + k0 + 8 * (lane >> 4));
+    }
+    __device__ static f32x4 mma(const T &a, const T &b, f32x4 acc) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
+};
+
+template <> struct MmaFrag<float> {
+    using T = float;
+    static constexpr int KS = 4;
+    __device__ static T load(const float *M, int ld, int k0) {
+        const int lane = threadIdx.x & 63;
+        return M[(lane & 15) * ld + k0 + (lane >> 4)];
+    }
+    __device__ static f32x4 mma(const T &a, const T &b, f32x4 acc) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+    }
+};
+
 // LDS row padding (elements) that keeps bf16 rows 16-byte aligned
 template <class E> struct Pad;
 template <> struct Pad<bf16_t> { static constexpr int v = 8; };
