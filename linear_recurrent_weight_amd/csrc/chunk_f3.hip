@@ -97,8 +97,8 @@ __global__ __launch_bounds__(256) void f3_prep(ChunkF3Args a) {
         tr[r] = tl;
     }
     // stacked features and token queries, 16 bytes of a row per thread and
-    // pass; all passes' loads (rows clamped into the padded feature buffers)
-    // are issued before the first store
+    // pass; all passes' loads (only of rows that exist) are issued before the
+    // first store
     {
         constexpr int VEC = 16 / int(sizeof(E)), NXV = C * DK / VEC / 256;
         const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
@@ -107,14 +107,16 @@ __global__ __launch_bounds__(256) void f3_prep(ChunkF3Args a) {
         for (int u = 0; u < NXV; ++u) {
             const int idx = (tid + 256 * u) * VEC, r = idx / DK, e = idx % DK;
             const int p = rm.pair(c, r);
-            xv[u] = *reinterpret_cast<const uint4 *>(xn + size_t(p > 0 ? p : 0) * DK + e);
-            qv[u] = *reinterpret_cast<const uint4 *>(qn + size_t(c * ct + r) * DK + e);
+            xv[u] = z4;
+            qv[u] = z4;
+            if (rm.token(r) >= 0 && p >= 0) xv[u] = *reinterpret_cast<const uint4 *>(xn + size_t(p) * DK + e);
+            if (r < ct) qv[u] = *reinterpret_cast<const uint4 *>(qn + size_t(c * ct + r) * DK + e);
         }
 #pragma unroll
         for (int u = 0; u < NXV; ++u) {
             const int idx = (tid + 256 * u) * VEC, r = idx / DK, e = idx % DK;
             const int tl = rm.token(r), p = rm.pair(c, r);
-            uint4 x = (tl >= 0 && p >= 0) ? xv[u] : z4;
+            uint4 x = xv[u];
             if (tl >= 0 && p < 0 && p >= -a.n_tail_in) {   // an incoming tail pair (fp32)
                 const float *src = a.tailx_in + (size_t(bh) * halo + halo + p) * DK + e;
                 uint32_t w[4];
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(256) void f3_prep(ChunkF3Args a) {
             }
             *reinterpret_cast<uint4 *>(Xs + size_t(r) * LK + e) = x;
             *reinterpret_cast<uint4 *>(Xg + idx) = x;
-            *reinterpret_cast<uint4 *>(Qs + size_t(r) * LK + e) = r < ct ? qv[u] : z4;
+            *reinterpret_cast<uint4 *>(Qs + size_t(r) * LK + e) = qv[u];
         }
     }
     __syncthreads();
