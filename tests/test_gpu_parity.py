@@ -65,6 +65,15 @@ def test_recurrent_variants(variant, window, dtype):
     check(w)
 
 
+@pytest.mark.parametrize("T", [1, 7, 8, 9, 15, 16, 17, 33])
+@pytest.mark.parametrize("variant,window", [("F1", 1), ("F2", 1), ("F3A", 3)])
+def test_recurrent_lengths(variant, window, T):
+    """Lengths around the token batches of the recurrent kernel (16 tokens, 8
+    for Falcon-2), with reductions over 16 lanes (d_k = 16) and the whole wave."""
+    check(gu.small(variant, "f32", B=1, H=2, T=T, dk=16, dv=16, window=window, seed=T))
+    check(gu.small(variant, "f32", B=1, H=2, T=T, dk=64, dv=16, window=window, seed=T + 1))
+
+
 @pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (128, 16), (128, 128)])
 def test_recurrent_head_dims(dk, dv):
     check(gu.small("F1", "f32", B=1, H=2, T=70, dk=dk, dv=dv))
