@@ -578,6 +578,25 @@ def test_chunk_f3_window1_is_falcon1():
 
 
 @pytest.mark.parametrize("window", [3, 8])
+@pytest.mark.parametrize("split", [2, 100])
+def test_chunk_f3_bf16_continuation(window, split):
+    """bf16, d_k = 64: the second call's first chunk stacks the incoming tail
+    pairs (fp32, rounded to bf16 as they are staged) with its own rows."""
+    import torch
+    w = gu.small("F3", "bf16", B=1, H=2, T=160, dk=64, dv=32, chunk=64, window=window, seed=17)
+    inp = gu.make(w)
+    dev = gu.to_device(inp, w)
+    a = {k: v[:, :, :split].contiguous() for k, v in dev.items()}
+    b = {k: v[:, :, split:].contiguous() for k, v in dev.items()}
+    o1, st1 = gu.run_gpu(w.with_(seqlen=split), a)
+    o2, st2 = gu.run_gpu(w.with_(seqlen=160 - split), b, state=st1)
+    heads = np.arange(2)
+    o_ref, st_ref = gu.oracle_heads(w, inp, heads)
+    eo, es = gu.compare(w, heads, torch.cat([o1, o2], 2), st2, o_ref, st_ref)
+    assert eo <= gu.tol_for(w) and es <= gu.tol_for(w), (eo, es)
+
+
+@pytest.mark.parametrize("window", [3, 8])
 @pytest.mark.parametrize("split", [0, 2, 8, 100])
 def test_chunk_f3_continuation(window, split):
     """Carrying (S, x_next, the last W-1 pairs) across calls equals one call."""
