@@ -697,6 +697,7 @@ __global__ __launch_bounds__(64) void a3_window(ChunkAArgs a) {
 // entry state of every segment: S_{g+1} = Gamma_g S_g + D_g (one thread per
 // state entry; the segment writes are loaded 32 at a time, so that one
 // memory latency covers a whole head at the usual segment counts)
+template <int NB>   // segment writes loaded per batch
 __global__ __launch_bounds__(256) void a1_segscan(ChunkAArgs a) {
     const int bh = blockIdx.x;
     const int e = blockIdx.y * 256 + threadIdx.x;   // d * 64 + j
@@ -707,7 +708,6 @@ __global__ __launch_bounds__(256) void a1_segscan(ChunkAArgs a) {
     float *Se = a.Sseg + size_t(bh) * a.nseg * stride + e;
     const float *Gg = a.Gseg + size_t(bh) * a.nseg;
     const int nseg = a.nseg;
-    constexpr int NB = 32;
     for (int g0 = 0; g0 < nseg; g0 += NB) {
         float dv[NB], gv[NB];
 #pragma unroll
@@ -731,7 +731,9 @@ template <bool WIN>
 void launch_walks(const ChunkAArgs &a, hipStream_t s, Marks *m) {
     a1_segment<WIN><<<dim3(a.nseg, a.BH), NTH, 0, s>>>(a);
     m->mark(s);
-    a1_segscan<<<dim3(a.BH, D * D / 256), 256, 0, s>>>(a);
+    // one batch of loads covers every segment when there are at most 8
+    if (a.nseg <= 8) a1_segscan<8><<<dim3(a.BH, D * D / 256), 256, 0, s>>>(a);
+    else a1_segscan<32><<<dim3(a.BH, D * D / 256), 256, 0, s>>>(a);
     m->mark(s);
     a1_output<WIN><<<dim3(a.nseg, a.BH), NTH, 0, s>>>(a);
     m->mark(s);
