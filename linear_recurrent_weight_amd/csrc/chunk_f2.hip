@@ -40,7 +40,6 @@ namespace falcon {
 namespace {
 
 constexpr int C = kChunk;
-constexpr float kLog2e = 1.4426950408889634f;
 
 // 16-byte vectors <-> floats for the io type
 template <class E> struct Io;
@@ -130,6 +129,10 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
     __shared__ float EB[C * RS];               // log2 gamma, then e^{b_t}
     __shared__ float OA[C * RS];               // e^{b_t} (Qh S_0)_t
     __shared__ float Hs[NCT][2][16 * 17];      // per solve wave: cross sums
+    // bf16: 0/1 B operands that pick 16 columns (half h) of a 32-wide block,
+    // for the MFMA transposes of x into XT
+    constexpr bool kPick = sizeof(E) == 2;
+    __shared__ __align__(16) bf16x8 IDT[kPick ? 2 : 1][64];
 
     const int id = blockIdx.x, u8 = id & 7, rest = id >> 3;
     const int s = rest % nslice;
@@ -174,6 +177,16 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
         rlam = lamg[tq];
     };
 
+    if constexpr (kPick) {
+        if (tid < 128) {
+            typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+            const int h = tid >> 6, k8 = 8 * (lane >> 4);
+            u16x8 u;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) u[e] = (k8 + e == 16 * h + col) ? 0x3F80 : 0;   // bf16 1.0
+            IDT[h][lane] = __builtin_bit_cast(bf16x8, u);
+        }
+    }
     // the tiles above the diagonal are never written but are read (times
     // zero) by the bf16 MFMA k steps of 32: they must hold zeros, not NaNs
     for (int idx = tid; idx < C * LC; idx += NT) {
@@ -243,7 +256,8 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
                     Io<E>::pack(qv + v * Io<E>::per16);
             }
 #pragma unroll
-            for (int e = 0; e < EPT; ++e) st(XT, size_t(part * EPT + e) * LC + row, xv[e]);
+            for (int e = 0; e < EPT; ++e)
+                if constexpr (!kPick) st(XT, size_t(part * EPT + e) * LC + row, xv[e]);
             float yv[Io<E>::per16], bv[YE];
             Io<E>::unpack(ry, yv);   // the first YE are this thread's values
 #pragma unroll
@@ -301,6 +315,19 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
                     if (isG) reinterpret_cast<float *>(GDq)[((I * 16 + g4 + r) * 4 + (col & 3)) * 4 + (col >> 2)] = v;
                     else PD4[I * 272 + (g4 + r) * 17 + col] = v;
                 }
+            }
+        }
+        // bf16: x^T into XT from the rows, 16 x 16 blocks (token tile m, d tile
+        // n) on MFMA with a column picker; lane holds tokens 16 m + g4 .. + 3
+        // of d = 16 n + col and stores them as 8 bytes (2-byte transposed
+        // stores from the row threads conflict in the LDS banks)
+        if constexpr (kPick) {
+            for (int b = wave; b < 4 * (DK / 16); b += NW) {
+                const int m = b & 3, n = b >> 2, k8 = 8 * (lane >> 4);
+                const bf16x8 av = *reinterpret_cast<const bf16x8 *>(XB + (16 * m + col) * LK + 32 * (n >> 1) + k8);
+                const f32x4 tb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, IDT[n & 1][lane], f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                         0, 0, 0);
+                st4(XT + (16 * n + col) * LC + 16 * m + g4, tb);
             }
         }
         // X S and Qh S for token rows 16 tw .. + 15: with eight waves, waves
