@@ -48,27 +48,86 @@ def algorithmic_flops(w) -> int:
     return w.batch * w.heads * w.seqlen * per
 
 
-def cpu_baseline(w, inp, min_seconds: float):
-    """The fp64 oracle, as it is, on this host: the whole workload, repeated
-    until at least `min_seconds` of CPU time, single-threaded."""
+_SHARED = {}   # inputs of the CPU baseline, inherited by its forked workers
+
+
+def _limit_blas():
     try:
         from threadpoolctl import threadpool_limits
-        ctx = threadpool_limits(limits=1)
+        threadpool_limits(limits=1)
     except Exception:  # pragma: no cover
-        ctx = None
+        pass
+
+
+def _oracle_shard(heads, reps):
+    """Run the oracle `reps` times on a subset of the flattened heads; returns
+    the wall time."""
     import oracle
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.falcon_forward(w.variant, inp["q"], inp["k"], inp["v"], inp["beta"], inp["lam"],
+    w, flat = _SHARED["w"], _SHARED["flat"]
+    part = {n: a[heads][None] for n, a in flat.items()}
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.falcon_forward(w.variant, part["q"], part["k"], part["v"], part["beta"], part["lam"],
                               window=w.window, eps=w.eps, eps_gamma=w.eps_gamma, eps_rms=w.eps_rms)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
-    if ctx is not None:
-        ctx.unregister() if hasattr(ctx, "unregister") else None
-    return {"value": w.tokens * reps / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"whole workload x{reps} ({dt:.1f} s), fp64 NumPy token recurrence, 1 thread"}
+    return time.perf_counter() - t0
+
+
+def _shard_worker(heads, reps, conn):
+    _limit_blas()
+    conn.send(_oracle_shard(heads, reps))
+    conn.close()
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, inp, min_seconds: float):
+    """The fp64 oracle, as it is, on this host's cores: P worker processes
+    (P = the cores this process may run on), each with one BLAS thread, share
+    the (batch, head) pairs of the workload and run them `reps` times; the
+    single-core rate is one worker's share run alone.  Must run before the GPU
+    is initialised (the workers are forked)."""
+    import multiprocessing as mp
+    import numpy as np
+    P = len(os.sched_getaffinity(0))
+    BH = w.batch * w.heads
+    _SHARED["w"] = w
+    _SHARED["flat"] = {n: a.reshape(BH, *a.shape[2:]) for n, a in inp.items()}
+    shards = [s for s in np.array_split(np.arange(BH), min(P, BH)) if len(s)]
+    # single core: the first share, repeated for at least a third of the budget
+    _limit_blas()
+    t1 = _oracle_shard(shards[0], 1)
+    reps1 = max(1, int(np.ceil(min_seconds / 3 / max(t1, 1e-9))))
+    if reps1 > 1:
+        t1 = _oracle_shard(shards[0], reps1) / reps1
+    one_core = len(shards[0]) * w.seqlen / t1
+    # all cores: every share in its own process, repeated for about the budget
+    reps = max(1, int(np.ceil(min_seconds / max(t1, 1e-9))))
+    ctx = mp.get_context("fork")
+    procs = []
+    t0 = time.perf_counter()
+    for sh in shards:
+        r, wr = ctx.Pipe(duplex=False)
+        pr = ctx.Process(target=_shard_worker, args=(sh, reps, wr))
+        pr.start()
+        procs.append((pr, r))
+    for pr, r in procs:
+        r.recv()
+        pr.join()
+    wall = time.perf_counter() - t0
+    return {"value": w.tokens * reps / wall, "unit": "tokens/s", "cores": len(shards), "kind": "oracle",
+            "sample": (f"whole workload x{reps}: {len(shards)} processes over the {BH} heads, "
+                       f"1 BLAS thread each, {wall:.1f} s wall; fp64 NumPy token recurrence"),
+            "single_core_value": one_core,
+            "single_core_sample": f"{len(shards[0])} heads x {w.seqlen} tokens x{reps1}, one process",
+            "cpu_model": cpu_model()}
 
 
 COPY_KERNEL = "__amd_rocclr_copyBuffer"   # the runtime's device copy (--copy-calibration)
@@ -180,6 +239,86 @@ def read_traffic(workload: str, kernels):
     return int(m.group(1))
 
 
+def read_profile_value(workload: str, kernels, key: str):
+    """A `key: value` line of the committed profile summary, or None when it
+    is missing or the kernel sources changed since the counters were read."""
+    import re
+    from linear_recurrent_weight_amd.build import sources_digest
+    path = profile_path(workload, kernels)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"^%s: (\S+)$" % re.escape(key), text, re.M)
+    d = re.search(r"^sources_digest: (\S+)$", text, re.M)
+    if not m or not d or d.group(1) != sources_digest(kernels):
+        return None
+    return float(m.group(1))
+
+
+def mfma_summary(mfma_db: str, stats_db: str, n_cu: int = 256, simd_per_cu: int = 4,
+                 clock_mhz: float = 2400.0) -> str:
+    """Markdown lines for one `--pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA
+    GRBM_GUI_ACTIVE` run: per kernel, the matrix-core busy fraction
+    SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x kernel cycles), with the kernel cycles
+    from the kernel-trace average duration at the peak engine clock (a lower
+    bound on the busy fraction when the clock runs below its peak)."""
+    top = {name: avg for name, _, avg, _ in
+           _db_rows(stats_db, "select name, total_calls, average, total_duration from top_kernels")}
+    rows = _db_rows(mfma_db, "select kernel_name, counter_name, count(*), avg(value) from counters_collection "
+                    "group by kernel_name, counter_name")
+    per = {}
+    for k, c, n, v in rows:
+        per.setdefault(k, {})[c] = (n, v)
+    lines = ["", "## Matrix-core use (`--pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA GRBM_GUI_ACTIVE`)", "",
+             f"busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / ({n_cu} CUs x {simd_per_cu} SIMDs x average duration "
+             f"x {clock_mhz:.0f} MHz)", "",
+             "| kernel | dispatches | SQ_VALU_MFMA_BUSY_CYCLES | SQ_INSTS_MFMA | GRBM_GUI_ACTIVE | avg duration (us) | MFMA busy fraction |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    fracs = {}
+    for k in sorted(per):
+        if "falcon::" not in k:
+            continue
+        busy = per[k].get("SQ_VALU_MFMA_BUSY_CYCLES", (0, float("nan")))
+        insts = per[k].get("SQ_INSTS_MFMA", (0, float("nan")))[1]
+        grbm = per[k].get("GRBM_GUI_ACTIVE", (0, float("nan")))[1]
+        dur = top.get(k)
+        frac = busy[1] / (n_cu * simd_per_cu * dur * clock_mhz) if dur else float("nan")
+        fracs[k] = (frac, dur or 0.0)
+        lines.append(f"| `{k[:110]}` | {busy[0]} | {busy[1]:.4g} | {insts:.4g} | {grbm:.4g} | "
+                     f"{dur if dur else float('nan'):.3f} | {frac:.4f} |")
+    tot = sum(d for _, d in fracs.values())
+    call = sum(f * d for f, d in fracs.values()) / tot if tot else float("nan")
+    lines += ["", f"mfma_busy_frac_per_call: {call:.6f}", ""]
+    return "\n".join(lines)
+
+
+def make_set(w, inp, dev, dt, fb, lib):
+    """One resident set of device buffers and the C arguments of a call on it."""
+    import torch
+    t = {n: torch.from_numpy(inp[n]).to(dev) for n in ("q", "k", "v", "beta", "lam")}
+    for n in ("q", "k", "v"):
+        t[n] = t[n].to(dt).contiguous()
+    t["o"] = torch.empty(w.batch, w.heads, w.seqlen, w.dv, dtype=dt, device=dev)
+    st = fb.FalconState.empty(w.batch, w.heads, w.dk, w.dv, w.window, dev)
+    t["state"] = st
+    t["st_c"] = st.to_c()
+    cargs = fb.make_args(variant=w.variant, dtype=w.dtype, batch=w.batch, heads=w.heads,
+                         seqlen=w.seqlen, dk=w.dk, dv=w.dv, chunk=w.chunk, window=w.window,
+                         eps=w.eps, eps_gamma=w.eps_gamma, eps_rms=w.eps_rms, q=t["q"], k=t["k"],
+                         v=t["v"], beta=t["beta"], lam=t["lam"], o=t["o"], state_out=t["st_c"])
+    nbytes = lib.falcon_fwd_workspace_size(ctypes.byref(cargs))
+    t["ws"] = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    cargs.workspace = t["ws"].data_ptr()
+    cargs.workspace_bytes = t["ws"].numel()
+    t["args"] = cargs
+    t["bytes"] = sum(x.numel() * x.element_size() for n, x in t.items()
+                     if n in ("q", "k", "v", "beta", "lam", "o", "ws"))
+    return t
+
+
+LLC_BYTES = 256 << 20   # MI355X last-level (Infinity) cache
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,15 +329,21 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
-    ap.add_argument("--rocprof-summary", nargs=3, metavar=("STATS_DB", "FETCH_DB", "WRITE_DB"),
-                    help="print a markdown summary of three rocprofv3 runs (no GPU needed)")
+    ap.add_argument("--rocprof-summary", nargs="+", metavar="DB",
+                    help="STATS_DB FETCH_DB WRITE_DB [MFMA_DB]: write the markdown summary of "
+                         "these rocprofv3 runs to profiles/ (no GPU needed)")
     ap.add_argument("--rocprof-command", default="", help="the commands that made the databases")
     args = ap.parse_args()
     if args.rocprof_summary:
         from linear_recurrent_weight_amd import falcon as fb
         from linear_recurrent_weight_amd.inputs import WORKLOADS
+        dbs = args.rocprof_summary
+        if len(dbs) not in (3, 4):
+            ap.error("--rocprof-summary takes 3 or 4 databases")
         names = kernel_names(fb.load_library(), WORKLOADS[args.workload])
-        text = rocprof_summary(args.workload, names, *args.rocprof_summary, args.rocprof_command)
+        text = rocprof_summary(args.workload, names, *dbs[:3], args.rocprof_command)
+        if len(dbs) == 4:
+            text += mfma_summary(dbs[3], dbs[0])
         path = profile_path(args.workload, names)
         os.makedirs(os.path.dirname(path), exist_ok=True)
         with open(path, "w") as f:
@@ -210,36 +355,32 @@ def main() -> int:
         return 2
 
     import numpy as np
-    import torch
 
-    from linear_recurrent_weight_amd import falcon as fb
     from linear_recurrent_weight_amd.inputs import WORKLOADS, make_inputs
 
     w = WORKLOADS[args.workload]
     inp = make_inputs(w)
+    # the oracle's CPU baseline forks workers: it runs before the GPU is touched
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp, args.cpu_seconds)
+
+    import torch
+
+    from linear_recurrent_weight_amd import falcon as fb
+
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    q, k, v = (torch.from_numpy(inp[n]).to(dev).to(dt).contiguous() for n in ("q", "k", "v"))
-    beta = torch.from_numpy(inp["beta"]).to(dev).contiguous()
-    lam = torch.from_numpy(inp["lam"]).to(dev).contiguous()
-    o = torch.empty(w.batch, w.heads, w.seqlen, w.dv, dtype=dt, device=dev)
-    st = fb.FalconState.empty(w.batch, w.heads, w.dk, w.dv, w.window, dev)
-    st_c = st.to_c()
     lib = fb.load_library()
-    cargs = fb.make_args(variant=w.variant, dtype=w.dtype, batch=w.batch, heads=w.heads,
-                         seqlen=w.seqlen, dk=w.dk, dv=w.dv, chunk=w.chunk, window=w.window,
-                         eps=w.eps, eps_gamma=w.eps_gamma, eps_rms=w.eps_rms, q=q, k=k, v=v,
-                         beta=beta, lam=lam, o=o, state_out=st_c)
-    nbytes = lib.falcon_fwd_workspace_size(ctypes.byref(cargs))
-    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
-    cargs.workspace = ws.data_ptr()
-    cargs.workspace_bytes = ws.numel()
+    # enough resident sets that consecutive calls cannot be served from the
+    # last-level cache (more than twice its size together)
+    sets = [make_set(w, inp, dev, dt, fb, lib)]
+    while len(sets) * sets[0]["bytes"] <= 2 * LLC_BYTES:
+        sets.append(make_set(w, inp, dev, dt, fb, lib))
     stream = torch.cuda.current_stream(dev)
     sh = ctypes.c_void_p(stream.cuda_stream)
-    pargs = ctypes.byref(cargs)
+    pargs = [ctypes.byref(t["args"]) for t in sets]
 
-    def step():
-        rc = lib.falcon_fwd(pargs, sh)
+    def step(i):
+        rc = lib.falcon_fwd(pargs[i % len(pargs)], sh)
         if rc != 0:
             raise fb.FalconError(rc, lib)
 
@@ -250,27 +391,32 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
 
-    # timed region: K back-to-back calls, events on the library's stream
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms = e0.elapsed_time(e1) / args.steps
+    def timed(rotate: bool):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(args.steps):
+            step(i if rotate else 0)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps, time.perf_counter() - w0
+
+    # timed region: K back-to-back calls, events on the library's stream;
+    # the headline rotates over the resident sets, the warm figure repeats
+    # one set (its inputs then partly stay in the last-level cache)
+    ms, wall = timed(True)
+    ms_warm, _ = timed(False)
 
     # per-kernel durations inside the call (events between the launches)
     names = []
     while True:
-        nm = lib.falcon_kernel_name(pargs, len(names))
+        nm = lib.falcon_kernel_name(pargs[0], len(names))
         if nm is None:
             break
         names.append(nm.decode())
@@ -283,7 +429,7 @@ def main() -> int:
     torch.cuda.synchronize()
     for r in range(reps):
         arr = (ctypes.c_void_p * (nk + 1))(*[e.cuda_event for e in evs[r]])
-        got = lib.falcon_fwd_profile(pargs, sh, arr, nk + 1)
+        got = lib.falcon_fwd_profile(pargs[r % len(pargs)], sh, arr, nk + 1)
         if got != nk:
             raise RuntimeError(f"falcon_fwd_profile launched {got} kernels, expected {nk}")
     torch.cuda.synchronize()
@@ -295,6 +441,10 @@ def main() -> int:
     alg_flops = algorithmic_flops(w)
     achieved_gbs = alg_bytes / (ms * 1e-3) / 1e9
     traffic = read_traffic(args.workload, names)
+    mfma_busy = read_profile_value(args.workload, names, "mfma_busy_frac_per_call")
+    form = "token-recurrent" if w.chunk == 0 else f"chunk-parallel (C = {w.chunk})"
+    win = f", window {w.window}" if w.window > 1 else ""
+    dominant = max(per_kernel, key=per_kernel.get) if per_kernel else None
 
     line = {
         "metric": METRIC,
@@ -309,21 +459,25 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: Falcon-{w.variant[1:]} chunk-parallel forward",
+        "config": {"workload": f"{w.name}: Falcon-{w.variant[1:]} {form} forward{win}",
                    "variant": w.variant, "batch": w.batch, "heads": w.heads, "seq_len": w.seqlen,
                    "dk": w.dk, "dv": w.dv, "chunk": w.chunk, "window": w.window,
-                   "io_dtype": w.dtype, "state_dtype": "f32", "parallelism": "none (1 GPU)"},
+                   "io_dtype": w.dtype, "state_dtype": "f32", "parallelism": "none (1 GPU)",
+                   "resident_sets": len(sets)},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "falcon_fwd call (" + " + ".join(names) + ")",
+                     "dominant_kernel": dominant,
                      "launch_ms": ms, "algorithmic_bytes": alg_bytes},
         "mfma": {"algorithmic_tflops": alg_flops / (ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
-                 "frac": alg_flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+                 "frac": alg_flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                 "counter_busy_frac": mfma_busy},
         "kernels_ms": per_kernel,
+        "warm_cache_ms_per_step": ms_warm,
         "wall_s_timed": wall,
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
     return 0
 

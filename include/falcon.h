@@ -35,7 +35,16 @@
  *   - Errors are returned as negative status codes (falcon_status_str gives
  *     the text).  On any error except FALCON_ERR_HIP nothing is launched.
  *   - falcon_fwd enqueues work on the given stream and returns without
- *     synchronising, allocating or freeing memory.  It is reentrant.
+ *     synchronising, allocating or freeing memory.  It is reentrant: the
+ *     only process-wide state is a per-device cache of the compute-unit
+ *     count (atomic) and the debug switch below, read once.
+ *   - Debug mode: with the environment variable FALCON_SYNC_CHECK set to a
+ *     value other than "0", every entry point that launches kernels
+ *     synchronises the stream after each launch and checks the HIP error
+ *     state; the first failing kernel is reported on stderr and the call
+ *     returns FALCON_ERR_HIP.  It is read once per process, changes no
+ *     result, must not be used under stream capture, and is the library's
+ *     only environment switch.
  *   - Data preconditions that are documented, not checked on the device:
  *     beta >= 0 and lambda >= 0 (the pages require non-negative steps and
  *     ridge; the NLMS gain is meant to lie in (0, 2)), finite inputs.

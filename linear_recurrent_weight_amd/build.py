@@ -68,9 +68,8 @@ def build(verbose: bool = False) -> pathlib.Path:
 # source file of each kernel name that falcon_kernel_name reports
 KERNEL_SOURCES = {"passthrough": "feature.hip", "feature": "feature.hip", "recurrent": "recurrent.hip",
                   "chunk_f1_prep": "chunk_f1.hip", "chunk_f1_scan": "chunk_f1.hip",
-                  "chunk_f1_fused": "chunk_f1_fused.hip", "chunk_f2": "chunk_f2.hip",
+                  "chunk_f2": "chunk_f2.hip",
                   "f3_prep": "chunk_f3.hip", "f3_scan": "chunk_f3.hip",
-                  "f1_ops": "chunk_f1_split.hip", "f1_walk": "chunk_f1_split.hip",
                   "f1_xfer": "chunk_f1_xfer.hip", "f1_carry": "chunk_f1_xfer.hip",
                   "a_segment": "chunk_a.hip", "a_segscan": "chunk_a.hip", "a_output": "chunk_a.hip",
                   "a1_segment": "chunk_a1.hip", "a1_segscan": "chunk_a1.hip", "a1_output": "chunk_a1.hip",

@@ -116,7 +116,7 @@ struct XferRows {
     uint4 q, k, v[NV];
     float beta, lam;
     f32x4 xn[2];                                       // x_0 (row 0 of chunk 0 only)
-    __device__ __forceinline__ void load(const F1SplitArgs &a, int id, int row, int part) {
+    __device__ __forceinline__ void load(const F1XferArgs &a, int id, int row, int part) {
         const int c = id / a.BH, bh = id % a.BH, T = a.T, t = c * kChunk + row;
         const int tq = t < T ? t : T - 1;
         const int tk = t < 1 ? 0 : (t - 1 < T ? t - 1 : T - 1);
@@ -141,7 +141,7 @@ struct XferRows {
 };
 
 template <int DV>
-__global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1SplitArgs a) {
+__global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1XferArgs a) {
     using Rows = XferRows<DV>;
     constexpr int VPT = Rows::VPT;
     constexpr int YP = DV + 8;                // bf16 pitch of the value rows
@@ -522,7 +522,7 @@ template <int DS> constexpr int carry_rs() { return DS == 64 ? 2 : 4; }
 template <int DS> constexpr int carry_threads() { return (DS / 16 * carry_rs<DS>() + 4) * 64; }
 
 template <int DS>
-__global__ __launch_bounds__(carry_threads<DS>()) void f1_carry(F1SplitArgs a, int nslice) {
+__global__ __launch_bounds__(carry_threads<DS>()) void f1_carry(F1XferArgs a, int nslice) {
     constexpr int NCT = DS / 16;                 // column tiles of the slice
     constexpr int RS = carry_rs<DS>();           // row groups per column tile
     constexpr int MT = 4 / RS;                   // row tiles (of 16) per compute wave
@@ -677,21 +677,8 @@ __global__ __launch_bounds__(carry_threads<DS>()) void f1_carry(F1SplitArgs a, i
     }
 }
 
-// compute units of the current device (read once per device)
-int cu_count() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cached[dev]) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
 template <int DV>
-void launch_xfer(const F1SplitArgs &a, hipStream_t s, Marks *m) {
+void launch_xfer(const F1XferArgs &a, hipStream_t s, Marks *m) {
     // as many workgroups as fit at once (LDS: two per CU, one at d_v = 128),
     // each walking chunk ids with the grid as stride
     const int total = a.nchunks * a.BH;
@@ -701,7 +688,7 @@ void launch_xfer(const F1SplitArgs &a, hipStream_t s, Marks *m) {
 }
 
 template <int DS>
-void launch_carry(const F1SplitArgs &a, hipStream_t s, Marks *m) {
+void launch_carry(const F1XferArgs &a, hipStream_t s, Marks *m) {
     const int nslice = a.dv / DS;
     const int blocks = nslice == 1 ? a.BH : ((a.BH + 7) / 8) * 8 * nslice;
     f1_carry<DS><<<blocks, carry_threads<DS>(), 0, s>>>(a, nslice);
@@ -710,17 +697,14 @@ void launch_carry(const F1SplitArgs &a, hipStream_t s, Marks *m) {
 
 }  // namespace
 
-void launch_chunk_f1_xfer(const F1SplitArgs &a, hipStream_t s, Marks *m) {
+void launch_chunk_f1_xfer(const F1XferArgs &a, int slice, hipStream_t s, Marks *m) {
     switch (a.dv) {
         case 32: launch_xfer<32>(a, s, m); break;
         case 64: launch_xfer<64>(a, s, m); break;
         default: launch_xfer<128>(a, s, m); break;
     }
-    switch (f1_xfer_slice(a.dv)) {
-        case 16: launch_carry<16>(a, s, m); break;
-        case 32: launch_carry<32>(a, s, m); break;
-        default: launch_carry<64>(a, s, m); break;
-    }
+    (void)slice;   // f1_xfer_slice: 32 columns for every d_v this path takes
+    launch_carry<32>(a, s, m);
 }
 
 }  // namespace falcon

@@ -3,8 +3,6 @@
 #pragma once
 
 #include <cstddef>
-#include <cstdlib>
-#include <cstring>
 
 #include "../../include/falcon.h"
 
@@ -40,39 +38,12 @@ constexpr size_t chunk_f3_bytes(int dk, int dtype_is_f32) {
     return chunk_f3_scal_off(dk, dtype_is_f32 ? 4 : 2) + 4 * size_t(kChunk) * 4;
 }
 
-// Fused bf16 Falcon-1 kernel: d_k = 64, value columns split into slices of
-// 32 or 64 per workgroup.  More slices give more workgroups (and repeat the
-// state-independent chunk work per slice); the slice width is chosen so that
-// a launch has at least ~128 workgroups, unless the sequence is short.
-constexpr bool chunk_f1_fused_supported(bool bf16, int dk, int dv) {
-    return bf16 && dk == 64 && (dv == 32 || dv == 64 || dv == 128);
-}
-inline int chunk_f1_fused_slice(int bh, int dv) {
-    if (dv == 32) return 32;
-    if (const char *e = std::getenv("FALCON_F1_SLICE")) {   // tuning override: 32 or 64
-        const int v = std::atoi(e);
-        if ((v == 32 || v == 64) && dv % v == 0) return v;
-    }
-    return (bh * (dv / 64) >= 128) ? 64 : 32;
-}
-
 // Falcon-2 chunk path: one kernel, no workspace.  bf16: d_k in {64, 128};
 // fp32: d_k = 64 (on-chip buffers); any d_v (a multiple of 16).
 constexpr bool chunk_f2_supported(bool bf16, int dk, int dv) {
     return (bf16 ? (dk == 64 || dk == 128) : dk == 64) && dv % 16 == 0;
 }
 
-// Two-kernel bf16 Falcon-1 path (d_k = 64): per chunk, bf16 Tp [64][64],
-// P [64][64] and (diag(e^{b_C - b_t}) X)^T [64 d][64 t], then fp32 [4][64]:
-// Gamma_{i-1}, Gamma_i, e^{b_C - b_i}, {Gamma_C, 0...}.  The walk kernel
-// takes slices of 32 or 64 value columns.
-constexpr size_t kF1SplitPOff = size_t(kChunk) * kChunk * 2;
-constexpr size_t kF1SplitXwOff = 2 * size_t(kChunk) * kChunk * 2;
-constexpr size_t kF1SplitScalOff = 3 * size_t(kChunk) * kChunk * 2;
-constexpr size_t kF1SplitChunkBytes = kF1SplitScalOff + 4 * size_t(kChunk) * 4;
-constexpr bool chunk_f1_split_supported(bool bf16, int dk, int dv) {
-    return bf16 && dk == 64 && (dv == 32 || dv == 64 || dv == 128);
-}
 // Transfer-operator bf16 Falcon-1 path (d_k = 64): per chunk, bf16
 //   A   [64 d'][64 d] = -(diag(e^{b_C-b_t}) X)^T W        (state transfer, less e^{b_C} I)
 //   G   [64 t][64 d]  = diag(e^{b_t}) Qh - P W             (outputs from the entry state)
@@ -94,30 +65,9 @@ constexpr size_t kF1XferBOff = 16384;
 constexpr size_t f1_xfer_h_off(int dv) { return 16384 + size_t(dv) * 128; }
 constexpr size_t f1_xfer_scal_off(int dv) { return 16384 + size_t(dv) * 256; }
 constexpr size_t f1_xfer_bytes(int dv) { return f1_xfer_scal_off(dv) + 256; }
-// value columns per workgroup of the carry kernel: 32 (more workgroups share
-// the operator traffic), or 16 or 64 with FALCON_F1_SLICE (a tuning
-// override); never more than d_v
-inline int f1_xfer_slice(int dv) {
-    int w = 32;
-    if (const char *e = std::getenv("FALCON_F1_SLICE")) {
-        const int v = std::atoi(e);
-        if (v == 16 || v == 32 || v == 64) w = v;
-    }
-    return w < dv ? w : dv;
-}
-
-// which bf16 d_k = 64 Falcon-1 kernels: the transfer-operator path, unless
-// FALCON_F1_PATH names another ("fused" or "split"; tuning and test switch)
-enum class F1Kind { kXfer, kSplit, kFused };
-inline F1Kind chunk_f1_kind() {
-    const char *e = std::getenv("FALCON_F1_PATH");
-    if (e && e[0] == 'f') return F1Kind::kFused;
-    if (e && e[0] == 's') return F1Kind::kSplit;
-    return F1Kind::kXfer;
-}
-// the walk kernel of the two-kernel path takes 32 value columns per
-// workgroup (its chain, output and loader waves fill the LDS at that width)
-constexpr int chunk_f1_split_slice(int /*dv*/) { return 32; }
+// value columns per workgroup of the carry kernel: 32 (two workgroups per
+// head share the operator traffic), never more than d_v
+constexpr int f1_xfer_slice(int dv) { return dv < 32 ? dv : 32; }
 
 // Falcon-1A / Falcon-3A chunk path: d_k in {32, 64}, d_v in {16, 32, 64}.
 constexpr bool chunk_a_supported(int dk, int dv) {
@@ -125,10 +75,6 @@ constexpr bool chunk_a_supported(int dk, int dv) {
 }
 // chunks per segment: enough segments for a few workgroups per compute unit
 inline int chunk_a_segment_chunks(long long bh, int nchunks) {
-    if (const char *e = std::getenv("FALCON_A_SEGMENT")) {   // tuning override: 1..32 chunks
-        const int v = std::atoi(e);
-        if (v >= 1 && v <= 32) return v;
-    }
     long long g = (bh * nchunks + 639) / 640;
     if (g < 1) g = 1;
     if (g > 32) g = 32;
@@ -137,11 +83,7 @@ inline int chunk_a_segment_chunks(long long bh, int nchunks) {
 
 // The bf16 Falcon-1A / Falcon-3A path with every token-contracting operand
 // transposed once per chunk (chunk_a1.hip): d_k = d_v = 64.
-// FALCON_A_PATH=generic keeps the general 1A/3A kernels (measurement and
-// cross-checks).
 inline bool chunk_a1_supported(bool bf16, int variant, int window, int dk, int dv) {
-    if (const char *e = std::getenv("FALCON_A_PATH"))
-        if (std::strcmp(e, "generic") == 0) return false;
     const bool var_ok = (variant == FALCON_V1A && window == 1) || (variant == FALCON_V3A && window >= 1);
     return bf16 && var_ok && dk == 64 && dv == 64;
 }
@@ -149,10 +91,6 @@ inline bool chunk_a1_supported(bool bf16, int variant, int window, int dk, int d
 // heads resident at once (two 512-thread workgroups per compute unit, 256
 // units), so that the walks run as one wave of workgroups
 inline int chunk_a1_segment_chunks(long long bh, int nchunks) {
-    if (const char *e = std::getenv("FALCON_A_SEGMENT")) {   // tuning override: 1..64 chunks
-        const int v = std::atoi(e);
-        if (v >= 1 && v <= 64) return v;
-    }
     constexpr long long kSlots = 512;
     for (int g = 1; g < nchunks; ++g)
         if (bh * ((nchunks + g - 1) / g) <= kSlots) return g;

@@ -1,22 +1,51 @@
 // falcon_fwd: validate, plan, and enqueue the kernels of the chosen path.
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
 #include "chunk_layout.h"
 #include "kernels.h"
 #include "plan.h"
 
 using namespace falcon;
 
+namespace falcon {
+
+int cu_count() {
+    static std::atomic<int> cached[64];   // zero-initialised (static storage)
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);   // every thread stores the same value
+    }
+    return n;
+}
+
+}  // namespace falcon
+
 namespace {
+
+// FALCON_SYNC_CHECK=1 (debug only): synchronise and check the HIP error
+// state after every kernel launch; read once per process
+bool sync_check_enabled() {
+    static const bool on = [] {
+        const char *e = std::getenv("FALCON_SYNC_CHECK");
+        return e && e[0] && std::strcmp(e, "0") != 0;
+    }();
+    return on;
+}
 
 const char *const kNamesEmpty[] = {"passthrough"};
 const char *const kNamesRecurrent[] = {"feature", "recurrent"};
 const char *const kNamesChunkF1[] = {"feature", "chunk_f1_prep", "chunk_f1_scan"};
-const char *const kNamesChunkF1Fused[] = {"chunk_f1_fused"};
 const char *const kNamesChunkA[] = {"a_segment", "a_segscan", "a_output"};
 const char *const kNamesChunkA1[] = {"a1_segment", "a1_segscan", "a1_output"};
 const char *const kNamesChunkA3[] = {"a3_window", "a1_segment", "a1_segscan", "a1_output"};
 const char *const kNamesChunkF2[] = {"chunk_f2"};
 const char *const kNamesChunkF3[] = {"feature", "f3_prep", "f3_scan"};
-const char *const kNamesChunkF1Split[] = {"f1_ops", "f1_walk"};
 const char *const kNamesChunkF1Xfer[] = {"f1_xfer", "f1_carry"};
 
 int run(const falcon_fwd_args *args, void *stream, Marks *m) {
@@ -24,6 +53,7 @@ int run(const falcon_fwd_args *args, void *stream, Marks *m) {
     const int rc = build_plan(args, &p, true);
     if (rc != FALCON_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    m->sync_check = sync_check_enabled();
     m->mark(s);
     if (args->state_out) {
         args->state_out->n_tail = p.n_tail_out;
@@ -118,8 +148,8 @@ int run(const falcon_fwd_args *args, void *stream, Marks *m) {
         fa.xnext_out = p.xnext_out;
         fa.o = p.o;
         launch_chunk_f2(fa, p.dtype == FALCON_BF16, s, m);
-    } else if (p.path == Path::kChunkF1Split || p.path == Path::kChunkF1Xfer) {
-        F1SplitArgs fa{};
+    } else if (p.path == Path::kChunkF1Xfer) {
+        F1XferArgs fa{};
         fa.BH = p.BH;
         fa.T = p.T;
         fa.nchunks = p.nchunks;
@@ -141,31 +171,7 @@ int run(const falcon_fwd_args *args, void *stream, Marks *m) {
         fa.xnext_out = p.xnext_out;
         fa.o = p.o;
         fa.ops = p.ws_at<void>(p.off_chunk);
-        if (p.path == Path::kChunkF1Xfer) launch_chunk_f1_xfer(fa, s, m);
-        else launch_chunk_f1_split(fa, p.slice, s, m);
-    } else if (p.path == Path::kChunkF1Fused) {
-        F1FusedArgs fa{};
-        fa.BH = p.BH;
-        fa.T = p.T;
-        fa.nchunks = p.nchunks;
-        fa.dk = p.dk;
-        fa.dv = p.dv;
-        fa.phi = p.phi;
-        fa.fresh = p.fresh ? 1 : 0;
-        fa.eps = p.eps;
-        fa.eps_gamma = p.eps_gamma;
-        fa.eps_rms = p.eps_rms;
-        fa.q = p.q;
-        fa.k = p.k;
-        fa.v = p.v;
-        fa.beta = p.beta;
-        fa.lambda = p.lambda;
-        fa.xnext_in = p.xnext_in;
-        fa.S_in = p.S_in;
-        fa.S_out = p.S_out;
-        fa.xnext_out = p.xnext_out;
-        fa.o = p.o;
-        launch_chunk_f1_fused(fa, p.slice, s, m);
+        launch_chunk_f1_xfer(fa, p.slice, s, m);
     } else {
         FeatureArgs fa{};
         fa.variant = p.variant;
@@ -265,6 +271,10 @@ int run(const falcon_fwd_args *args, void *stream, Marks *m) {
             launch_chunk_f3(ca, io_bf16, s, m);
         }
     }
+    if (m->failed_at >= 0) {
+        std::fprintf(stderr, "falcon_fwd: FALCON_SYNC_CHECK: kernel %d of the call failed\n", m->failed_at);
+        return FALCON_ERR_HIP;
+    }
     if (hipGetLastError() != hipSuccess) return FALCON_ERR_HIP;
     return m->count - 1;
 }
@@ -292,14 +302,12 @@ extern "C" const char *falcon_kernel_name(const falcon_fwd_args *args, int i) {
         case Path::kEmpty: return i < 1 ? kNamesEmpty[i] : nullptr;
         case Path::kRecurrent: return i < 2 ? kNamesRecurrent[i] : nullptr;
         case Path::kChunkF1: return i < 3 ? kNamesChunkF1[i] : nullptr;
-        case Path::kChunkF1Fused: return i < 1 ? kNamesChunkF1Fused[i] : nullptr;
         case Path::kChunkA: return i < 3 ? kNamesChunkA[i] : nullptr;
         case Path::kChunkA1:
             if (p.window > 1) return i < 4 ? kNamesChunkA3[i] : nullptr;
             return i < 3 ? kNamesChunkA1[i] : nullptr;
         case Path::kChunkF2: return i < 1 ? kNamesChunkF2[i] : nullptr;
         case Path::kChunkF3: return i < 3 ? kNamesChunkF3[i] : nullptr;
-        case Path::kChunkF1Split: return i < 2 ? kNamesChunkF1Split[i] : nullptr;
         case Path::kChunkF1Xfer: return i < 2 ? kNamesChunkF1Xfer[i] : nullptr;
         default: return nullptr;
     }

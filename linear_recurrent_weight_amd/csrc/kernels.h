@@ -48,27 +48,28 @@ struct ChunkF1Args {
     size_t chunk_bytes;
 };
 
-// Optional event marks between kernel launches (measurement entry point).
+// Called after every kernel launch: optional event marks between launches
+// (measurement entry point), and the debug check of FALCON_SYNC_CHECK=1
+// (synchronise the stream and read the HIP error state after each launch).
 struct Marks {
     void *const *ev = nullptr;
     int n = 0;
     int count = 0;
+    bool sync_check = false;
+    int failed_at = -1;      // index of the first launch that failed the debug check
     void mark(hipStream_t s) {
         if (ev && count < n) (void)hipEventRecord(static_cast<hipEvent_t>(ev[count]), s);
+        if (sync_check && count > 0 && failed_at < 0) {
+            const hipError_t e = hipStreamSynchronize(s);
+            const hipError_t l = hipGetLastError();
+            if (e != hipSuccess || l != hipSuccess) failed_at = count - 1;
+        }
         ++count;
     }
 };
 
-struct F1FusedArgs {
-    int BH, T, nchunks, dk, dv, phi, fresh;
-    float eps, eps_gamma, eps_rms;
-    const void *q, *k, *v;  // bf16 [BH, T, d]
-    const float *beta, *lambda;
-    const float *xnext_in;  // nullptr when fresh
-    const float *S_in;
-    float *S_out, *xnext_out;
-    void *o;
-};
+// compute units of the current device (queried once per device, thread-safe)
+int cu_count();
 
 struct ChunkAArgs {
     int variant, phi, BH, T, Tpad, nchunks, dk, dv, window, fresh, n_tail_in, n_tail_out;
@@ -97,7 +98,7 @@ struct ChunkF2Args {
     void *o;
 };
 
-struct F1SplitArgs {
+struct F1XferArgs {
     int BH, T, nchunks, dk, dv, phi, fresh;
     float eps, eps_gamma, eps_rms;
     const void *q, *k, *v;  // bf16 [BH, T, d]
@@ -106,7 +107,7 @@ struct F1SplitArgs {
     const float *S_in;
     float *S_out, *xnext_out;
     void *o;
-    void *ops;              // per-chunk operators (kF1SplitChunkBytes each)
+    void *ops;              // per-chunk transfer operators (f1_xfer_bytes(dv) each)
 };
 
 struct ChunkF3Args {
@@ -126,14 +127,13 @@ void launch_features(const FeatureArgs &a, bool in_bf16, bool feat_bf16, hipStre
 void launch_passthrough(const PassArgs &a, hipStream_t s, Marks *m);
 void launch_recurrent(const RecurrentArgs &a, bool io_bf16, hipStream_t s, Marks *m);
 void launch_chunk_f1(const ChunkF1Args &a, bool bf16, hipStream_t s, Marks *m);
-void launch_chunk_f1_fused(const F1FusedArgs &a, int ds, hipStream_t s, Marks *m);
 void launch_chunk_a(const ChunkAArgs &a, bool bf16, hipStream_t s, Marks *m);
 // bf16 Falcon-1A with d_k = d_v = 64 (etaw and lg unused)
 void launch_chunk_a1(const ChunkAArgs &a, hipStream_t s, Marks *m);
 void launch_chunk_f2(const ChunkF2Args &a, bool bf16, hipStream_t s, Marks *m);
 void launch_chunk_f3(const ChunkF3Args &a, bool bf16, hipStream_t s, Marks *m);
-void launch_chunk_f1_split(const F1SplitArgs &a, int ds, hipStream_t s, Marks *m);
-// same arguments; `ops` holds f1_xfer_bytes(dv) per chunk
-void launch_chunk_f1_xfer(const F1SplitArgs &a, hipStream_t s, Marks *m);
+// bf16 Falcon-1, d_k = 64: transfer operators, then the carry over slices of
+// `slice` value columns
+void launch_chunk_f1_xfer(const F1XferArgs &a, int slice, hipStream_t s, Marks *m);
 
 }  // namespace falcon

@@ -73,18 +73,9 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
     if (a->chunk == 0) {
         p->path = Path::kRecurrent;
     } else if (a->chunk == kChunk) {
-        const F1Kind f1 = chunk_f1_kind();
-        if (var == FALCON_V1 && chunk_f1_xfer_supported(a->dtype == FALCON_BF16, a->dk, a->dv) &&
-            f1 == F1Kind::kXfer) {
+        if (var == FALCON_V1 && chunk_f1_xfer_supported(a->dtype == FALCON_BF16, a->dk, a->dv)) {
             p->path = Path::kChunkF1Xfer;
             p->slice = f1_xfer_slice(a->dv);
-        } else if (var == FALCON_V1 && chunk_f1_split_supported(a->dtype == FALCON_BF16, a->dk, a->dv) &&
-                   f1 == F1Kind::kSplit) {
-            p->path = Path::kChunkF1Split;
-            p->slice = chunk_f1_split_slice(a->dv);
-        } else if (var == FALCON_V1 && chunk_f1_fused_supported(a->dtype == FALCON_BF16, a->dk, a->dv)) {
-            p->path = Path::kChunkF1Fused;
-            p->slice = chunk_f1_fused_slice(a->batch * a->heads, a->dv);
         } else if (var == FALCON_V1 && chunk_f1_supported(a->dk, a->dv)) {
             p->path = Path::kChunkF1;
         } else if (var == FALCON_V2 && chunk_f2_supported(a->dtype == FALCON_BF16, a->dk, a->dv)) {
@@ -123,12 +114,8 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
     // whole chunks on the chunk paths), then the per-chunk operators
     const int T = a->seqlen;
     size_t off = 0;
-    if (p->path == Path::kChunkF1Fused || p->path == Path::kChunkF2) {
+    if (p->path == Path::kChunkF2) {
         p->nchunks = (T + kChunk - 1) / kChunk;
-    } else if (p->path == Path::kChunkF1Split) {
-        p->nchunks = (T + kChunk - 1) / kChunk;
-        p->off_chunk = off;
-        off = align_up(off + static_cast<size_t>(bh) * p->nchunks * kF1SplitChunkBytes);
     } else if (p->path == Path::kChunkF1Xfer) {
         p->nchunks = (T + kChunk - 1) / kChunk;
         p->off_chunk = off;

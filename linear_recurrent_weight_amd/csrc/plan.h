@@ -16,9 +16,7 @@ enum class Path : int {
     kChunkF1 = 2,    // chunk-parallel Falcon-1
     kChunkA = 3,     // chunk-parallel Falcon-1A / Falcon-3A (scalar-decay writes)
     kChunkF2 = 4,    // chunk-parallel Falcon-2
-    kChunkF1Fused = 5,  // chunk-parallel Falcon-1, bf16, one fused kernel
     kChunkF3 = 6,    // chunk-parallel Falcon-3 (stacked window rows)
-    kChunkF1Split = 7,  // chunk-parallel Falcon-1, bf16: per-chunk operators, then the walk
     kChunkF1Xfer = 8,   // chunk-parallel Falcon-1, bf16: per-chunk transfer operators, then the carry
     kChunkA1 = 9,    // chunk-parallel Falcon-1A, bf16, d_k = d_v = 64: register-operand segment kernels
 };
@@ -47,7 +45,7 @@ struct Plan {
     void *o = nullptr;
 
     // workspace carve-up (offsets in bytes from the workspace base)
-    int slice = 0;           // value columns per workgroup of the fused kernel
+    int slice = 0;           // value columns per workgroup of the state carry
     int seg_chunks = 0, nseg = 0;   // segmentation of the Falcon-1A/3A chunk path
     bool feat_f32 = true;    // storage type of the normalised features
     size_t off_xn = 0, off_qn = 0, off_eta = 0, off_alpha = 0;

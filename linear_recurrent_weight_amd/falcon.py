@@ -140,6 +140,66 @@ def make_args(*, variant, dtype, batch, heads, seqlen, dk, dv, chunk=64, window=
     return a
 
 
+def _check_tensor(name, t, shape, dtype, device):
+    """Raise ValueError unless `t` is a contiguous tensor of exactly this
+    shape and dtype on `device`."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def check_fwd_tensors(q, k, v, beta, lam, *, variant, window, state=None, out=None, workspace=None):
+    """Validate every tensor of a forward call against the shapes the C ABI
+    assumes (the library sees only pointers and sizes, so a mismatch here
+    would read or write past a buffer on the GPU).  Returns
+    (B, H, T, dk, dv, torch dtype, device).  Raises ValueError."""
+    import torch
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a 4-d tensor [B,H,T,dk]")
+    dt = q.dtype
+    if dt not in (torch.bfloat16, torch.float32):
+        raise ValueError("q, k, v must all be bfloat16 or all float32")
+    dev = q.device
+    B, H, T, dk = q.shape
+    if not isinstance(v, torch.Tensor) or v.dim() != 4:
+        raise ValueError("v must be a 4-d tensor [B,H,T,dv]")
+    dv = v.shape[-1]
+    var = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    if window < 1 or window > MAX_WINDOW:
+        raise ValueError(f"window must lie in [1, {MAX_WINDOW}]")
+    _check_tensor("q", q, (B, H, T, dk), dt, dev)
+    _check_tensor("k", k, (B, H, T, dk), dt, dev)
+    _check_tensor("v", v, (B, H, T, dv), dt, dev)
+    f32 = torch.float32
+    _check_tensor("beta", beta, (B, H, T, dv) if var == VARIANTS["F2"] else (B, H, T), f32, dev)
+    _check_tensor("lambda", lam, (B, H, T), f32, dev)
+    if out is not None:
+        _check_tensor("out", out, (B, H, T, dv), dt, dev)
+    if state is not None:
+        _check_tensor("state.S", state.S, (B, H, dk, dv), f32, dev)
+        if not state.fresh:
+            _check_tensor("state.x_next", state.x_next, (B, H, dk), f32, dev)
+        if not 0 <= int(state.n_tail) <= window - 1:
+            raise ValueError(f"state.n_tail = {state.n_tail} must lie in [0, window - 1 = {window - 1}]")
+        if state.fresh and state.n_tail:
+            raise ValueError("a fresh state carries no tail pairs")
+        if state.n_tail > 0:
+            _check_tensor("state.tail_x", state.tail_x, (B, H, window - 1, dk), f32, dev)
+            _check_tensor("state.tail_y", state.tail_y, (B, H, window - 1, dv), f32, dev)
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    return B, H, T, dk, dv, dt, dev
+
+
 def fwd(q, k, v, beta, lam, *, variant="F1", chunk=64, window=1, eps=1e-6, eps_gamma=1e-3,
         eps_rms=1e-6, phi="rmsnorm", state: Optional[FalconState] = None, want_state=True,
         out=None, workspace=None, stream=None):
@@ -147,40 +207,39 @@ def fwd(q, k, v, beta, lam, *, variant="F1", chunk=64, window=1, eps=1e-6, eps_g
 
     q, k: [B,H,T,dk]; v: [B,H,T,dv] (all bf16 or all fp32, contiguous, on the
     device); beta: [B,H,T] fp32 ([B,H,T,dv] for F2); lam: [B,H,T] fp32.
-    Returns (o [B,H,T,dv], FalconState or None).
+    `stream` is a torch.cuda.Stream (default: the current stream); the
+    output, the state and any temporary workspace are allocated on it, so the
+    caching allocator never hands them to other streams while the kernels run.
+    Returns (o [B,H,T,dv], FalconState or None).  Raises ValueError on a
+    tensor whose shape, dtype, device or layout does not match.
     """
     import torch
     lib = load_library()
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+    if not (isinstance(q, torch.Tensor) and q.is_cuda):
         raise ValueError("q, k, v must be device tensors")
-    dtype = {torch.bfloat16: "bf16", torch.float32: "f32"}.get(q.dtype)
-    if dtype is None or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must all be bfloat16 or all float32")
-    for t in (q, k, v, beta, lam):
-        if not t.is_contiguous():
-            raise ValueError("inputs must be contiguous")
-    if beta.dtype != torch.float32 or lam.dtype != torch.float32:
-        raise ValueError("beta and lambda must be float32")
-    B, H, T, dk = q.shape
-    dv = v.shape[-1]
-    dev = q.device
-    o = out if out is not None else torch.empty(B, H, T, dv, dtype=q.dtype, device=dev)
-    st_in = state.to_c() if state is not None else None
-    st_out_t = FalconState.empty(B, H, dk, dv, window, dev) if want_state else None
-    st_out = st_out_t.to_c() if st_out_t is not None else None
-    args = make_args(variant=variant, dtype=dtype, batch=B, heads=H, seqlen=T, dk=dk, dv=dv,
-                     chunk=chunk, window=window, eps=eps, eps_gamma=eps_gamma, eps_rms=eps_rms,
-                     phi=phi, q=q, k=k, v=v, beta=beta, lam=lam, o=o, state_in=st_in,
-                     state_out=st_out)
-    nbytes = lib.falcon_fwd_workspace_size(ctypes.byref(args))
-    if nbytes:
-        if workspace is None or workspace.numel() < nbytes:
-            workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-        args.workspace = workspace.data_ptr()
-        args.workspace_bytes = workspace.numel()
+    B, H, T, dk, dv, dt, dev = check_fwd_tensors(q, k, v, beta, lam, variant=variant, window=window,
+                                                  state=state, out=out, workspace=workspace)
+    dtype = "bf16" if dt == torch.bfloat16 else "f32"
     if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = lib.falcon_fwd(ctypes.byref(args), ctypes.c_void_p(stream))
+        stream = torch.cuda.current_stream(dev)
+    elif not isinstance(stream, torch.cuda.Stream):
+        raise ValueError("stream must be a torch.cuda.Stream")
+    with torch.cuda.stream(stream):
+        o = out if out is not None else torch.empty(B, H, T, dv, dtype=dt, device=dev)
+        st_in = state.to_c() if state is not None else None
+        st_out_t = FalconState.empty(B, H, dk, dv, window, dev) if want_state else None
+        st_out = st_out_t.to_c() if st_out_t is not None else None
+        args = make_args(variant=variant, dtype=dtype, batch=B, heads=H, seqlen=T, dk=dk, dv=dv,
+                         chunk=chunk, window=window, eps=eps, eps_gamma=eps_gamma, eps_rms=eps_rms,
+                         phi=phi, q=q, k=k, v=v, beta=beta, lam=lam, o=o, state_in=st_in,
+                         state_out=st_out)
+        nbytes = lib.falcon_fwd_workspace_size(ctypes.byref(args))
+        if nbytes:
+            if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+                workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            args.workspace = workspace.data_ptr()
+            args.workspace_bytes = workspace.numel() * workspace.element_size()
+        rc = lib.falcon_fwd(ctypes.byref(args), ctypes.c_void_p(stream.cuda_stream))
     if rc != OK:
         raise FalconError(rc, lib)
     if st_out_t is not None:

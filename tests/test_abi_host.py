@@ -210,21 +210,24 @@ def test_chunk_path_coverage(lib):
         assert validate(lib, with_ws(lib, args(variant=var, window=w, chunk=0, dk=16, dv=16))) == fb.OK
 
 
-def test_f1_bf16_workspace_per_path(lib, monkeypatch):
-    """bf16 Falcon-1 at d_k = 64: the transfer-operator path (default) keeps
-    A, G, B^T and H in bf16 plus one 256-byte scalar block per chunk; the
-    operators + walk pair keeps Tp, P, Xw and four decay rows."""
+def test_f1_bf16_workspace(lib):
+    """bf16 Falcon-1 at d_k = 64 (transfer operators, then the carry) keeps
+    A, G, B^T and H in bf16 plus one 256-byte scalar block per chunk."""
     for dv in (32, 64, 128):
         per_chunk = 2 * 64 * 64 * 2 + 2 * 64 * dv * 2 + 256
         assert wsize(lib, args(seqlen=1000, dv=dv)) == 6 * 16 * per_chunk
-    monkeypatch.setenv("FALCON_F1_PATH", "split")
-    assert wsize(lib, args(seqlen=1000)) == 6 * 16 * (3 * 64 * 64 * 2 + 4 * 64 * 4)
+    assert _names(lib, args(seqlen=1000)) == ["f1_xfer", "f1_carry"]
 
 
-def test_fused_f1_needs_no_workspace(lib, monkeypatch):
-    monkeypatch.setenv("FALCON_F1_PATH", "fused")
-    assert wsize(lib, args(seqlen=1024)) == 0
-    assert validate(lib, args(seqlen=1024)) == fb.OK
+def test_library_reads_no_tuning_switches():
+    """Path choice, slices and segment lengths follow the arguments alone:
+    the library source reads no environment variable except the debug check
+    FALCON_SYNC_CHECK."""
+    csrc = ROOT / "linear_recurrent_weight_amd" / "csrc"
+    names = set()
+    for f in list(csrc.glob("*.hip")) + list(csrc.glob("*.cpp")) + list(csrc.glob("*.h")):
+        names |= set(re.findall(r'getenv\("([A-Z_]+)"\)', f.read_text()))
+    assert names == {"FALCON_SYNC_CHECK"}
 
 
 def test_chunk_f2_coverage(lib):
@@ -268,14 +271,11 @@ def _segments(bh, nchunks):
 
 
 @pytest.mark.parametrize("variant,window", [("F1A", 1), ("F3A", 2), ("F3A", 8)])
-def test_inner_product_bf16_d64_path(lib, monkeypatch, variant, window):
+def test_inner_product_bf16_d64_path(lib, variant, window):
     """bf16 Falcon-1A / 3A at d_k = d_v = 64 take the register-transpose
     kernels (a window pass first when W > 1); their workspace is the segment
     writes and entry states (fp32 [d_k][d_v]) and carries, plus w_t and
-    log2 gamma_t per token with a window.  FALCON_A_PATH=generic selects the
-    general kernels."""
-    monkeypatch.delenv("FALCON_A_PATH", raising=False)
-    monkeypatch.delenv("FALCON_A_SEGMENT", raising=False)
+    log2 gamma_t per token with a window."""
     B, H, T = 2, 12, 16384
     a = args(variant=variant, window=window, batch=B, heads=H, seqlen=T)
     names = _names(lib, a)
@@ -292,12 +292,9 @@ def test_inner_product_bf16_d64_path(lib, monkeypatch, variant, window):
     assert wsize(lib, a) == n
     # (the fake tensor addresses are 1 MiB apart: validate a small shape)
     assert validate(lib, with_ws(lib, args(variant=variant, window=window))) == fb.OK
-    monkeypatch.setenv("FALCON_A_PATH", "generic")
-    assert _names(lib, a) == ["a_segment", "a_segscan", "a_output"]
 
 
-def test_inner_product_other_shapes_take_the_general_kernels(lib, monkeypatch):
-    monkeypatch.delenv("FALCON_A_PATH", raising=False)
+def test_inner_product_other_shapes_take_the_general_kernels(lib):
     for dt, dk, dv in [("f32", 64, 64), ("bf16", 32, 64), ("bf16", 64, 32)]:
         a = args(variant="F1A", dtype=dt, dk=dk, dv=dv)
         assert _names(lib, a) == ["a_segment", "a_segscan", "a_output"], (dt, dk, dv)

@@ -62,6 +62,7 @@ def test_bench_line_contract():
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-9
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0
+    assert cb["single_core_value"] > 0 and cb["cpu_model"]
     assert d["value"] > 0 and abs(d["value"] - 8 * 12 * 1024 / (d["ms_per_step"] * 1e-3)) < 1e-3 * d["value"]
 
 
@@ -93,3 +94,17 @@ def test_rocprof_summary_calibrates_on_the_largest_copy(tmp_path):
     # per dispatch: 1000 KiB fetched x 2 + 500 KiB written x 1
     assert "traffic_bytes_per_call: %d" % ((2 * 1000 + 500) * 1024) in text
     assert "| `%s` | 3 | 50.000 |" % k in text
+
+
+def test_mfma_summary_busy_fraction(tmp_path):
+    """SQ_VALU_MFMA_BUSY_CYCLES over (CUs x SIMDs x kernel cycles at the peak
+    clock), weighted by kernel time for the call."""
+    a = "void falcon::(anonymous namespace)::ka(falcon::X)"
+    b = "void falcon::(anonymous namespace)::kb(falcon::X)"
+    _fake_db(tmp_path / "s.db", "X", [], top=[(a, 5, 10.0, 50.0), (b, 5, 30.0, 150.0)])
+    import sqlite3
+    _fake_db(tmp_path / "m.db", "SQ_VALU_MFMA_BUSY_CYCLES", [(a, 0.5 * 1024 * 10.0 * 2400), (b, 0.1 * 1024 * 30.0 * 2400)])
+    text = bench.mfma_summary(str(tmp_path / "m.db"), str(tmp_path / "s.db"))
+    assert "| 0.5000 |" in text and "| 0.1000 |" in text
+    frac = float(text.split("mfma_busy_frac_per_call: ")[1].split()[0])
+    assert abs(frac - (0.5 * 10 + 0.1 * 30) / 40) < 1e-6
