@@ -178,6 +178,26 @@ int falcon_fwd(const falcon_fwd_args *args, void *stream);
  * (>= 0) or a negative status. */
 int falcon_fwd_profile(const falcon_fwd_args *args, void *stream, void *const *events, int n_events);
 
+/* Largest workspace falcon_fwd_noalloc can serve: 64 MiB per GPU. */
+#define FALCON_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): falcon_fwd
+ * with the workspace taken from a fixed device array of the library
+ * (FALCON_NOALLOC_SCRATCH_BYTES, one per GPU, held from the library's first
+ * use on that GPU until the process ends) instead of args->workspace, which
+ * is ignored.  The caller still provides every input and output.  Nothing is
+ * allocated or freed: the first call on a device only looks up that device's
+ * array.  Calls whose workspace need (falcon_fwd_workspace_size) exceeds
+ * FALCON_NOALLOC_SCRATCH_BYTES return FALCON_ERR_WORKSPACE without
+ * launching; a failed lookup returns FALCON_ERR_HIP.  Every call on one GPU
+ * uses the same array, which keeps the previous call's contents (no kernel
+ * reads workspace it has not written in the same call): calls that overlap
+ * in time on one GPU, on any streams or host threads, race and must be
+ * ordered by the caller.  Same validation, kernels, results and status codes
+ * as falcon_fwd otherwise. */
+int falcon_fwd_noalloc(const falcon_fwd_args *args, void *stream);
+
 /* Static name of the i-th kernel (0-based) that falcon_fwd launches for these
  * arguments, or NULL when i is out of range or the arguments are invalid.
  * Pure host code, no HIP call. */

@@ -3,6 +3,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "chunk_layout.h"
 #include "kernels.h"
@@ -311,4 +312,58 @@ extern "C" const char *falcon_kernel_name(const falcon_fwd_args *args, int i) {
         case Path::kChunkF1Xfer: return i < 2 ? kNamesChunkF1Xfer[i] : nullptr;
         default: return nullptr;
     }
+}
+
+// ---------------------------------------------------------------------------
+// falcon_fwd_noalloc: falcon_fwd with the workspace taken from a fixed device
+// array of this library instead of the caller's buffer.
+// ---------------------------------------------------------------------------
+namespace {
+
+// One array per device (a __device__ object exists once on every GPU the
+// library runs on and stays allocated until the process ends).  Host code
+// never uses its name as an address: scratch_ptr() looks the address up.
+static __device__ __align__(256) unsigned char scratch[FALCON_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices] = {};
+
+// device address of the current device's copy of `scratch`, looked up once
+// per device with that device current; nullptr on failure
+void *scratch_ptr(int dev) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch[dev] = p;
+    }
+    return g_scratch[dev];
+}
+
+}  // namespace
+
+extern "C" int falcon_fwd_noalloc(const falcon_fwd_args *args, void *stream) {
+    if (!args) return FALCON_ERR_INVALID_ARG;
+    const size_t need = falcon_fwd_workspace_size(args);
+    falcon_fwd_args a = *args;
+    if (need == 0) {
+        // malformed or unsupported arguments, or a path without workspace
+        a.workspace = nullptr;
+        a.workspace_bytes = 0;
+    } else {
+        if (need > FALCON_NOALLOC_SCRATCH_BYTES) return FALCON_ERR_WORKSPACE;
+        int dev = -1;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FALCON_ERR_HIP;
+        void *p = scratch_ptr(dev);
+        if (!p) return FALCON_ERR_HIP;
+        a.workspace = p;
+        a.workspace_bytes = FALCON_NOALLOC_SCRATCH_BYTES;
+    }
+    Marks m;
+    const int rc = run(&a, stream, &m);
+    return rc < 0 ? rc : FALCON_OK;
 }

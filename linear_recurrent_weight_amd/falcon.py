@@ -45,7 +45,9 @@ class FalconFwdArgsC(ctypes.Structure):
 
 
 EXPORTS = ("falcon_fwd", "falcon_fwd_validate", "falcon_fwd_workspace_size",
-           "falcon_fwd_profile", "falcon_kernel_name", "falcon_status_str", "falcon_abi_version")
+           "falcon_fwd_profile", "falcon_fwd_noalloc", "falcon_kernel_name", "falcon_status_str",
+           "falcon_abi_version")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -70,6 +72,8 @@ def load_library(path: Optional[os.PathLike] = None) -> ctypes.CDLL:
     lib.falcon_fwd_profile.argtypes = [ctypes.POINTER(FalconFwdArgsC), ctypes.c_void_p,
                                        ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
     lib.falcon_fwd_profile.restype = ctypes.c_int
+    lib.falcon_fwd_noalloc.argtypes = [ctypes.POINTER(FalconFwdArgsC), ctypes.c_void_p]
+    lib.falcon_fwd_noalloc.restype = ctypes.c_int
     lib.falcon_kernel_name.argtypes = [ctypes.POINTER(FalconFwdArgsC), ctypes.c_int]
     lib.falcon_kernel_name.restype = ctypes.c_char_p
     lib.falcon_abi_version.argtypes = []
