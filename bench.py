@@ -292,8 +292,10 @@ def mfma_summary(mfma_db: str, stats_db: str, n_cu: int = 256, simd_per_cu: int 
     return "\n".join(lines)
 
 
-def make_set(w, inp, dev, dt, fb, lib):
-    """One resident set of device buffers and the C arguments of a call on it."""
+def make_set(w, inp, dev, dt, fb, lib, ws=None):
+    """One resident set of device inputs and outputs and the C arguments of a
+    call on it; the workspace `ws` (scratch, not an input or output) is
+    shared by the sets when given, as a caller reuses one scratch buffer."""
     import torch
     t = {n: torch.from_numpy(inp[n]).to(dev) for n in ("q", "k", "v", "beta", "lam")}
     for n in ("q", "k", "v"):
@@ -307,12 +309,12 @@ def make_set(w, inp, dev, dt, fb, lib):
                          eps=w.eps, eps_gamma=w.eps_gamma, eps_rms=w.eps_rms, q=t["q"], k=t["k"],
                          v=t["v"], beta=t["beta"], lam=t["lam"], o=t["o"], state_out=t["st_c"])
     nbytes = lib.falcon_fwd_workspace_size(ctypes.byref(cargs))
-    t["ws"] = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    t["ws"] = ws if ws is not None else torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
     cargs.workspace = t["ws"].data_ptr()
     cargs.workspace_bytes = t["ws"].numel()
     t["args"] = cargs
     t["bytes"] = sum(x.numel() * x.element_size() for n, x in t.items()
-                     if n in ("q", "k", "v", "beta", "lam", "o", "ws"))
+                     if n in ("q", "k", "v", "beta", "lam", "o"))
     return t
 
 
@@ -370,11 +372,12 @@ def main() -> int:
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     lib = fb.load_library()
-    # enough resident sets that consecutive calls cannot be served from the
-    # last-level cache (more than twice its size together)
+    # enough resident sets of inputs and outputs that consecutive calls cannot
+    # find them in the last-level cache (more than twice its size together);
+    # one workspace serves every set
     sets = [make_set(w, inp, dev, dt, fb, lib)]
     while len(sets) * sets[0]["bytes"] <= 2 * LLC_BYTES:
-        sets.append(make_set(w, inp, dev, dt, fb, lib))
+        sets.append(make_set(w, inp, dev, dt, fb, lib, ws=sets[0]["ws"]))
     stream = torch.cuda.current_stream(dev)
     sh = ctypes.c_void_p(stream.cuda_stream)
     pargs = [ctypes.byref(t["args"]) for t in sets]

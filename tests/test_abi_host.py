@@ -152,10 +152,10 @@ def test_workspace_grows_with_problem(lib):
     assert 0 < small < big
     # ragged lengths round up to whole chunks on the chunk path
     assert wsize(lib, args(seqlen=65, dtype="f32")) == wsize(lib, args(seqlen=128, dtype="f32"))
-    # bf16 Falcon-1 at d_k = 64: the operators + walk pair keeps per-chunk
-    # operators in the workspace; the fused kernel keeps everything on chip
-    assert wsize(lib, args(seqlen=1024)) > 0
-    assert validate(lib, with_ws(lib, args(seqlen=1024))) == fb.OK
+    # bf16 Falcon-1 at d_k = 64, d_v = 32: the transfer-operator pair keeps
+    # per-chunk operators in the workspace (d_v = 64 keeps them on chip)
+    assert wsize(lib, args(seqlen=1024, dv=32)) > 0
+    assert validate(lib, with_ws(lib, args(seqlen=1024, dv=32))) == fb.OK
     # a malformed request reports 0 bytes
     assert wsize(lib, args(dk=48)) == 0
 
@@ -216,7 +216,7 @@ def test_f1_bf16_workspace(lib):
     for dv in (32, 64, 128):
         per_chunk = 2 * 64 * 64 * 2 + 2 * 64 * dv * 2 + 256
         assert wsize(lib, args(seqlen=1000, dv=dv)) == 6 * 16 * per_chunk
-    assert _names(lib, args(seqlen=1000)) == ["f1_xfer", "f1_carry"]
+        assert _names(lib, args(seqlen=1000, dv=dv)) == ["f1_xfer", "f1_carry"]
 
 
 def test_library_reads_no_tuning_switches():
