@@ -26,12 +26,18 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
 def algorithmic_bytes(w) -> int:
     """Unavoidable traffic of one forward call: q, k, v read once, o written
     once (io dtype), beta and lambda read once (fp32), final state written
-    once (fp32)."""
+    once (fp32).  A single-token decode step continues a carried state, so
+    it also reads the incoming state once (S, x_next, the tail pairs) and
+    writes x_next and the tail."""
     esz = 2 if w.dtype == "bf16" else 4
     n = w.batch * w.heads * w.seqlen
     beta_cols = w.dv if w.variant == "F2" else 1
-    return (n * (2 * w.dk + 2 * w.dv) * esz + n * (beta_cols + 1) * 4
-            + w.batch * w.heads * w.dk * w.dv * 4)
+    total = (n * (2 * w.dk + 2 * w.dv) * esz + n * (beta_cols + 1) * 4
+             + w.batch * w.heads * w.dk * w.dv * 4)
+    if w.seqlen == 1:
+        h = w.window - 1
+        total += w.batch * w.heads * 4 * (w.dk * w.dv + 2 * w.dk + 2 * h * (w.dk + w.dv))
+    return total
 
 
 def algorithmic_flops(w) -> int:
@@ -60,15 +66,25 @@ def _limit_blas():
 
 
 def _oracle_shard(heads, reps):
+    import numpy as np
     """Run the oracle `reps` times on a subset of the flattened heads; returns
     the wall time."""
     import oracle
     w, flat = _SHARED["w"], _SHARED["flat"]
     part = {n: a[heads][None] for n, a in flat.items()}
+    state = None
+    if w.seqlen == 1:   # a decode step continues the same carried state as the GPU run
+        from linear_recurrent_weight_amd.inputs import decode_state
+        ds = decode_state(w)
+        BH = w.batch * w.heads
+        pick = lambda a: a.reshape(BH, *a.shape[2:])[heads].astype(np.float64)
+        state = oracle.OracleState(S=pick(ds["S"]), fresh=False, x_next=pick(ds["x_next"]),
+                                   tail_x=pick(ds["tail_x"]), tail_y=pick(ds["tail_y"]))
     t0 = time.perf_counter()
     for _ in range(reps):
         oracle.falcon_forward(w.variant, part["q"], part["k"], part["v"], part["beta"], part["lam"],
-                              window=w.window, eps=w.eps, eps_gamma=w.eps_gamma, eps_rms=w.eps_rms)
+                              window=w.window, eps=w.eps, eps_gamma=w.eps_gamma, eps_rms=w.eps_rms,
+                              state_in=state)
     return time.perf_counter() - t0
 
 
@@ -304,10 +320,19 @@ def make_set(w, inp, dev, dt, fb, lib, ws=None):
     st = fb.FalconState.empty(w.batch, w.heads, w.dk, w.dv, w.window, dev)
     t["state"] = st
     t["st_c"] = st.to_c()
+    st_in = None
+    if w.seqlen == 1:   # a decode step continues a carried state
+        from linear_recurrent_weight_amd.inputs import decode_state
+        ds = decode_state(w)
+        t["state_in"] = fb.FalconState(*(torch.from_numpy(ds[n]).to(dev) for n in
+                                         ("S", "x_next", "tail_x", "tail_y")),
+                                       n_tail=ds["n_tail"], fresh=False)
+        t["st_in_c"] = st_in = t["state_in"].to_c()
     cargs = fb.make_args(variant=w.variant, dtype=w.dtype, batch=w.batch, heads=w.heads,
                          seqlen=w.seqlen, dk=w.dk, dv=w.dv, chunk=w.chunk, window=w.window,
                          eps=w.eps, eps_gamma=w.eps_gamma, eps_rms=w.eps_rms, q=t["q"], k=t["k"],
-                         v=t["v"], beta=t["beta"], lam=t["lam"], o=t["o"], state_out=t["st_c"])
+                         v=t["v"], beta=t["beta"], lam=t["lam"], o=t["o"], state_out=t["st_c"],
+                         state_in=st_in)
     nbytes = lib.falcon_fwd_workspace_size(ctypes.byref(cargs))
     t["ws"] = ws if ws is not None else torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
     cargs.workspace = t["ws"].data_ptr()
@@ -315,6 +340,10 @@ def make_set(w, inp, dev, dt, fb, lib, ws=None):
     t["args"] = cargs
     t["bytes"] = sum(x.numel() * x.element_size() for n, x in t.items()
                      if n in ("q", "k", "v", "beta", "lam", "o"))
+    t["bytes"] += sum(x.numel() * x.element_size() for x in (st.S, st.x_next, st.tail_x, st.tail_y))
+    if "state_in" in t:
+        t["bytes"] += sum(x.numel() * x.element_size() for x in
+                          (t["state_in"].S, t["state_in"].x_next, t["state_in"].tail_x, t["state_in"].tail_y))
     return t
 
 
@@ -445,7 +474,8 @@ def main() -> int:
     achieved_gbs = alg_bytes / (ms * 1e-3) / 1e9
     traffic = read_traffic(args.workload, names)
     mfma_busy = read_profile_value(args.workload, names, "mfma_busy_frac_per_call")
-    form = "token-recurrent" if w.chunk == 0 else f"chunk-parallel (C = {w.chunk})"
+    form = ("single-token decode step" if w.seqlen == 1 else
+            "token-recurrent" if w.chunk == 0 else f"chunk-parallel (C = {w.chunk})")
     win = f", window {w.window}" if w.window > 1 else ""
     dominant = max(per_kernel, key=per_kernel.get) if per_kernel else None
 

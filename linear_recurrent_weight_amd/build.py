@@ -67,6 +67,7 @@ def build(verbose: bool = False) -> pathlib.Path:
 
 # source file of each kernel name that falcon_kernel_name reports
 KERNEL_SOURCES = {"passthrough": "feature.hip", "feature": "feature.hip", "recurrent": "recurrent.hip",
+                  "decode": "decode.hip",
                   "chunk_f1_prep": "chunk_f1.hip", "chunk_f1_scan": "chunk_f1.hip",
                   "chunk_f2": "chunk_f2.hip",
                   "f3_prep": "chunk_f3.hip", "f3_scan": "chunk_f3.hip",

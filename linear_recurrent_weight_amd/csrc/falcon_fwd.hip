@@ -41,6 +41,7 @@ bool sync_check_enabled() {
 
 const char *const kNamesEmpty[] = {"passthrough"};
 const char *const kNamesRecurrent[] = {"feature", "recurrent"};
+const char *const kNamesDecode[] = {"decode"};
 const char *const kNamesChunkF1[] = {"feature", "chunk_f1_prep", "chunk_f1_scan"};
 const char *const kNamesChunkA[] = {"a_segment", "a_segscan", "a_output"};
 const char *const kNamesChunkA1[] = {"a1_segment", "a1_segscan", "a1_output"};
@@ -79,6 +80,35 @@ int run(const falcon_fwd_args *args, void *stream, Marks *m) {
             pa.taily_out = p.taily_out;
             launch_passthrough(pa, s, m);
         }
+    } else if (p.path == Path::kDecode) {
+        DecodeArgs da{};
+        da.variant = p.variant;
+        da.phi = p.phi;
+        da.BH = p.BH;
+        da.dk = p.dk;
+        da.dv = p.dv;
+        da.window = p.window;
+        da.fresh = p.fresh ? 1 : 0;
+        da.n_tail_in = p.n_tail_in;
+        da.n_tail_out = p.n_tail_out;
+        da.eps = p.eps;
+        da.eps_gamma = p.eps_gamma;
+        da.eps_rms = p.eps_rms;
+        da.q = p.q;
+        da.k = p.k;
+        da.v = p.v;
+        da.beta = p.beta;
+        da.lambda = p.lambda;
+        da.xnext_in = p.xnext_in;
+        da.tailx_in = p.tailx_in;
+        da.taily_in = p.taily_in;
+        da.S_in = p.S_in;
+        da.S_out = p.S_out;
+        da.xnext_out = p.xnext_out;
+        da.tailx_out = p.tailx_out;
+        da.taily_out = p.taily_out;
+        da.o = p.o;
+        launch_decode(da, p.dtype == FALCON_BF16, s, m);
     } else if (p.path == Path::kChunkA || p.path == Path::kChunkA1) {
         ChunkAArgs ca{};
         ca.variant = p.variant;
@@ -302,6 +332,7 @@ extern "C" const char *falcon_kernel_name(const falcon_fwd_args *args, int i) {
     switch (p.path) {
         case Path::kEmpty: return i < 1 ? kNamesEmpty[i] : nullptr;
         case Path::kRecurrent: return i < 2 ? kNamesRecurrent[i] : nullptr;
+        case Path::kDecode: return i < 1 ? kNamesDecode[i] : nullptr;
         case Path::kChunkF1: return i < 3 ? kNamesChunkF1[i] : nullptr;
         case Path::kChunkA: return i < 3 ? kNamesChunkA[i] : nullptr;
         case Path::kChunkA1:

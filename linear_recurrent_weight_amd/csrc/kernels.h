@@ -110,6 +110,17 @@ struct F1XferArgs {
     void *ops;              // per-chunk transfer operators (f1_xfer_bytes(dv) each)
 };
 
+// one token (T = 1) of every variant, continuing from the incoming state
+struct DecodeArgs {
+    int variant, phi, BH, dk, dv, window, fresh, n_tail_in, n_tail_out;
+    float eps, eps_gamma, eps_rms;
+    const void *q, *k, *v;      // [BH, 1, d] in the io dtype
+    const float *beta, *lambda; // [BH] ([BH, dv] beta for Falcon-2)
+    const float *xnext_in, *tailx_in, *taily_in, *S_in;
+    float *S_out, *xnext_out, *tailx_out, *taily_out;
+    void *o;
+};
+
 struct ChunkF3Args {
     int BH, T, Tpad, nchunks, ct, window, dk, dv, n_tail_in;
     const void *xn, *qn;    // features [BH, Tpad, dk] (bf16 or fp32)
@@ -126,6 +137,7 @@ struct ChunkF3Args {
 void launch_features(const FeatureArgs &a, bool in_bf16, bool feat_bf16, hipStream_t s, Marks *m);
 void launch_passthrough(const PassArgs &a, hipStream_t s, Marks *m);
 void launch_recurrent(const RecurrentArgs &a, bool io_bf16, hipStream_t s, Marks *m);
+void launch_decode(const DecodeArgs &a, bool io_bf16, hipStream_t s, Marks *m);
 void launch_chunk_f1(const ChunkF1Args &a, bool bf16, hipStream_t s, Marks *m);
 void launch_chunk_a(const ChunkAArgs &a, bool bf16, hipStream_t s, Marks *m);
 // bf16 Falcon-1A with d_k = d_v = 64 (etaw and lg unused)

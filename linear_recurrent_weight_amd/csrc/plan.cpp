@@ -93,6 +93,7 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
         return FALCON_ERR_UNSUPPORTED;
     }
     if (a->seqlen == 0) p->path = Path::kEmpty;
+    if (a->seqlen == 1) p->path = Path::kDecode;   // one token: both forms are one step
 
 
     // boundary state rules (host fields are always readable)
@@ -114,7 +115,9 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
     // whole chunks on the chunk paths), then the per-chunk operators
     const int T = a->seqlen;
     size_t off = 0;
-    if (p->path == Path::kChunkF2) {
+    if (p->path == Path::kDecode) {
+        // no workspace: the step reads the inputs and the state directly
+    } else if (p->path == Path::kChunkF2) {
         p->nchunks = (T + kChunk - 1) / kChunk;
     } else if (p->path == Path::kChunkF1Xfer) {
         p->nchunks = (T + kChunk - 1) / kChunk;

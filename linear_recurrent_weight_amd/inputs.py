@@ -68,6 +68,10 @@ WORKLOADS = {
     # Falcon-3A window 8, bf16, 8 x 12 x 2048 x 64, C = 64
     "c5": Workload("c5", "F3A", 8, 12, 2048, 64, 64, 64, 8, "bf16", "sigmoid", 0, 0,
                    "uniform", 0.0, 0.05, seed=5),
+    # single-token decode step at the c2 shape, continuing from a carried
+    # state (the state is part of the inputs: see decode_state)
+    "c2dec": Workload("c2dec", "F1", 8, 12, 1, 64, 64, 64, 1, "bf16", "sigmoid", 0, 0,
+                      "uniform", 0.0, 0.05, seed=21),
     # parity-only extras
     "c3clamp": Workload("c3clamp", "F1A", 2, 12, 2048, 64, 64, 64, 1, "bf16", "sigmoid",
                         0, 0, "uniform", 0.5, 1.0, seed=31, eps_gamma=0.994),
@@ -107,3 +111,22 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
     if w.dtype == "bf16":
         q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
     return {"q": q, "k": k, "v": v, "beta": beta, "lam": lam}
+
+
+def decode_state(w: Workload, seed: Optional[int] = None) -> dict:
+    """A carried boundary state for a workload that continues a sequence:
+    S [B,H,dk,dv] ~ N(0, 1/dk), x_next [B,H,dk] an RMS-normalised N(0,1)
+    vector (a feature, as the previous call leaves it), and W-1 tail pairs
+    (features and values) when the window is wider than 1.  float32."""
+    rng = np.random.default_rng((w.seed if seed is None else seed) + 1000)
+    B, H = w.batch, w.heads
+    S = (rng.standard_normal((B, H, w.dk, w.dv)) / np.sqrt(w.dk)).astype(np.float32)
+    xn = rng.standard_normal((B, H, w.dk))
+    xn = (xn / np.sqrt(np.mean(xn * xn, axis=-1, keepdims=True))).astype(np.float32)
+    h = max(w.window - 1, 0)
+    tx = rng.standard_normal((B, H, h, w.dk))
+    if h:
+        tx = tx / np.sqrt(np.mean(tx * tx, axis=-1, keepdims=True))
+    ty = rng.standard_normal((B, H, h, w.dv))
+    return {"S": S, "x_next": xn, "tail_x": tx.astype(np.float32), "tail_y": ty.astype(np.float32),
+            "n_tail": h}

@@ -298,3 +298,14 @@ def test_inner_product_other_shapes_take_the_general_kernels(lib):
     for dt, dk, dv in [("f32", 64, 64), ("bf16", 32, 64), ("bf16", 64, 32)]:
         a = args(variant="F1A", dtype=dt, dk=dk, dv=dv)
         assert _names(lib, a) == ["a_segment", "a_segscan", "a_output"], (dt, dk, dv)
+
+
+def test_single_token_takes_the_decode_kernel(lib):
+    """seqlen = 1 runs the one-kernel decode step for every variant and both
+    forms, with no workspace."""
+    for var, W in (("F1", 1), ("F2", 1), ("F3", 5), ("F1A", 1), ("F3A", 8)):
+        for chunk in (0, 64):
+            a = args(variant=var, window=W, seqlen=1, chunk=chunk)
+            assert _names(lib, a) == ["decode"]
+            assert wsize(lib, a) == 0
+            assert validate(lib, a) == fb.OK
