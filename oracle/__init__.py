@@ -3,10 +3,10 @@
 Only the tests, the smoke check and the CPU-baseline leg of the benchmark
 import this package; the HIP library never does.
 """
-from .falcon_oracle import (F1, F2, F3, F1A, F3A, VARIANTS, WINDOW_VARIANTS,
+from .falcon_oracle import (F1, F2, F3, F1A, F2A, F3A, VARIANTS, WINDOW_VARIANTS, PER_COLUMN,
                             PHI_RMSNORM, PHI_IDENTITY, OracleState, OracleTrace,
                             falcon_forward, phi, window_lambda_max)
 
-__all__ = ["F1", "F2", "F3", "F1A", "F3A", "VARIANTS", "WINDOW_VARIANTS",
+__all__ = ["F1", "F2", "F3", "F1A", "F2A", "F3A", "VARIANTS", "WINDOW_VARIANTS", "PER_COLUMN",
            "PHI_RMSNORM", "PHI_IDENTITY", "OracleState", "OracleTrace",
            "falcon_forward", "phi", "window_lambda_max"]

@@ -36,8 +36,10 @@ What is computed, per head (state S has d_k rows and d_v columns):
       F2 : per value column j with its own eta_{t,j}, gamma_{t,j}
       F3 : S_t = gamma S + (eta/B_t) sum_{j in I_t} x_j (y_j - S^T x_j)^T
       F1A: S_t = gamma S + eta x y^T
+      F2A: per value column j, S_t[:, j] = gamma_{t,j} S[:, j] + eta_{t,j} x y_{t,j}
       F3A: S_t = gamma S + (eta/B_t) sum_{j in I_t} x_j y_j^T
-    ([summary §1, §4, §4.3, §4.4, §4.5, App. F], [explainer, Method]);
+    ([summary §1, §4, §4.3, §4.4, §4.5, App. F, "B. Falcon-2A: per-channel
+    inner-product write", Figures 6-8], [explainer, Method]);
   * read-after-write: o_t = S_t^T qh_t ([summary §C.2], [explainer, Method]);
   * boundary state for exact continuation: S_T, the next pair's feature
     phi(k_T) and the last W-1 pairs ([summary §C.7, §4.4], [blog]).
@@ -55,7 +57,15 @@ design notes of the repository):
   R6  Falcon-3A normalises by the same lambda_max of the window covariance as
       Falcon-3;
   R7  the continuation state also carries x_next = phi(k_T), because the
-      next segment's first pair uses the previous key.
+      next segment's first pair uses the previous key;
+  R8  Falcon-2A is the inner-product write of Falcon-1A with the per-column
+      gains of Falcon-2: beta_{t,j} per value column, the same energy
+      ||x_t||^2 and ridge lambda_t for every column (reading R4), so
+      eta_{t,j} = beta_{t,j} / (||x_t||^2 + lambda_t + eps), alpha_{t,j} =
+      min(eta_{t,j} lambda_t, 1 - eps_gamma), and each column decays and is
+      written on its own ([summary §4.3, §4.5 and the bullets on the A family
+      under "C. Falcon-3" and Figures 6-8]: per-column analogue, per-column
+      decay-weighted masks, alpha derived as eta lambda).
 """
 from __future__ import annotations
 
@@ -64,8 +74,9 @@ from typing import List, Optional
 
 import numpy as np
 
-F1, F2, F3, F1A, F3A = 1, 2, 3, 11, 13
-VARIANTS = {"F1": F1, "F2": F2, "F3": F3, "F1A": F1A, "F3A": F3A}
+F1, F2, F3, F1A, F2A, F3A = 1, 2, 3, 11, 12, 13
+VARIANTS = {"F1": F1, "F2": F2, "F3": F3, "F1A": F1A, "F2A": F2A, "F3A": F3A}
+PER_COLUMN = (F2, F2A)
 WINDOW_VARIANTS = (F3, F3A)
 PHI_RMSNORM, PHI_IDENTITY = 0, 1
 
@@ -137,14 +148,14 @@ def falcon_forward(variant, q, k, v, beta, lam, *, window: int = 1,
                    state_in: Optional[OracleState] = None,
                    trace: bool = False):
     """Run the recurrence.  Shapes: q, k [B,H,T,dk]; v [B,H,T,dv];
-    beta [B,H,T] ([B,H,T,dv] for F2); lam [B,H,T].
+    beta [B,H,T] ([B,H,T,dv] for F2 and F2A); lam [B,H,T].
 
     Returns (o [B,H,T,dv], OracleState) or, with trace=True,
     (o, OracleState, OracleTrace).  All arithmetic is float64.
     """
     if isinstance(variant, str):
         variant = VARIANTS[variant]
-    if variant not in (F1, F2, F3, F1A, F3A):
+    if variant not in (F1, F2, F3, F1A, F2A, F3A):
         raise ValueError(f"unknown variant {variant}")
     if window < 1:
         raise ValueError("window must be >= 1")
@@ -163,7 +174,7 @@ def falcon_forward(variant, q, k, v, beta, lam, *, window: int = 1,
     kf = k.reshape(N, T, dk)
     vf = v.reshape(N, T, dv)
     lamf = lam.reshape(N, T)
-    betaf = beta.reshape(N, T, dv) if variant == F2 else beta.reshape(N, T)
+    betaf = beta.reshape(N, T, dv) if variant in PER_COLUMN else beta.reshape(N, T)
 
     qh = phi(qf, eps_rms, phi_kind)
     kh = phi(kf, eps_rms, phi_kind)
@@ -182,7 +193,7 @@ def falcon_forward(variant, q, k, v, beta, lam, *, window: int = 1,
         pairs_y = [np.asarray(state_in.tail_y[:, i], np.float64) for i in range(state_in.n_tail)]
 
     o = np.zeros((N, T, dv))
-    col_shape = (N, T, dv) if variant == F2 else (N, T)
+    col_shape = (N, T, dv) if variant in PER_COLUMN else (N, T)
     tr_mu = np.zeros((N, T))
     tr_eta = np.zeros(col_shape)
     tr_alpha = np.zeros(col_shape)
@@ -220,7 +231,7 @@ def falcon_forward(variant, q, k, v, beta, lam, *, window: int = 1,
 
         # normalised step eta_t and clamped ridge carry gamma_t
         den = mu + lamf[:, t] + eps
-        if variant == F2:
+        if variant in PER_COLUMN:
             num = betaf[:, t, :]
             den_b = np.broadcast_to(den[:, None], num.shape)
             lam_b = lamf[:, t][:, None]
@@ -249,6 +260,8 @@ def falcon_forward(variant, q, k, v, beta, lam, *, window: int = 1,
             S = gamma[:, None, None] * S + (eta / bt)[:, None, None] * g
         elif variant == F1A:
             S = gamma[:, None, None] * S + eta[:, None, None] * np.einsum("nk,nv->nkv", x_t, y_t)
+        elif variant == F2A:
+            S = gamma[:, None, :] * S + np.einsum("nk,nv->nkv", x_t, eta * y_t)
         else:  # F3A
             g = np.einsum("nbk,nbv->nkv", xw, yw)
             S = gamma[:, None, None] * S + (eta / bt)[:, None, None] * g

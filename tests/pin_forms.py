@@ -28,8 +28,8 @@ from __future__ import annotations
 import numpy as np
 from scipy.linalg import solve_triangular
 
-F1, F2, F3, F1A, F3A = 1, 2, 3, 11, 13
-NAMES = {"F1": F1, "F2": F2, "F3": F3, "F1A": F1A, "F3A": F3A}
+F1, F2, F3, F1A, F2A, F3A = 1, 2, 3, 11, 12, 13
+NAMES = {"F1": F1, "F2": F2, "F3": F3, "F1A": F1A, "F2A": F2A, "F3A": F3A}
 
 
 def rms_feature(z, eps_rms, identity=False):
@@ -82,7 +82,7 @@ def step_scalars(variant, seg: Segment, window, eps, eps_gamma):
     T = seg.x.shape[0]
     px = np.concatenate([seg.tail_x, seg.x], 0)
     nt = seg.tail_x.shape[0]
-    per_col = variant == F2
+    per_col = variant in (F2, F2A)
     shape = seg.beta.shape if per_col else (T,)
     eta = np.zeros(shape)
     logg = np.zeros(shape)
@@ -127,6 +127,19 @@ def masked_segment(variant, seg: Segment, window=1, eps=1e-6, eps_gamma=1e-3):
         return O, ST
     if variant == F1:
         return _masked_delta(X, Y, Q, S0, eta, logg)
+    if variant == F2A:
+        # per value column j: decay-weighted mask e^{b_tj - b_sj} eta_sj on
+        # the shared scores q_t . x_s (summary Figures 6-8: per-column masks)
+        O = np.zeros((T, dv))
+        ST = np.zeros((dk, dv))
+        QX = Q @ X.T
+        for j in range(dv):
+            b = np.cumsum(logg[:, j])
+            P = np.tril(np.exp(b[:, None] - b[None, :]) * QX)
+            u = eta[:, j] * Y[:, j]
+            O[:, j] = np.exp(b) * (Q @ S0[:, j]) + P @ u
+            ST[:, j] = np.exp(b[-1]) * S0[:, j] + (np.exp(b[-1] - b)[:, None] * X).T @ u
+        return O, ST
     if variant == F1A:
         b = np.cumsum(logg)
         U = eta[:, None] * Y

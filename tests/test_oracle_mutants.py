@@ -34,6 +34,10 @@ MUTANTS = {
     "l2_instead_of_rms": ("ms = np.mean(z * z, axis=-1, keepdims=True) + eps_rms",
                           "ms = np.sum(z * z, axis=-1, keepdims=True) + eps_rms"),
     "tail_too_long": ("keep = window - 1", "keep = window"),
+    "f2a_first_columns_gain": ('S = gamma[:, None, :] * S + np.einsum("nk,nv->nkv", x_t, eta * y_t)',
+                               'S = gamma[:, None, :] * S + np.einsum("nk,nv->nkv", x_t, eta[:, :1] * y_t)'),
+    "f2a_shared_decay": ('S = gamma[:, None, :] * S + np.einsum("nk,nv->nkv", x_t, eta * y_t)',
+                         'S = gamma[:, None, :1] * S + np.einsum("nk,nv->nkv", x_t, eta * y_t)'),
     "wrong_x_next": ("out_xnext = kh[:, T - 1].copy()", "out_xnext = kh[:, T - 2].copy()"),
 }
 

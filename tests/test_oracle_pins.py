@@ -39,7 +39,7 @@ def _rand(rng, B, H, T, dk, dv, variant="F1", beta=(0.1, 0.9), lam=(0.0, 0.3)):
     q = rng.standard_normal((B, H, T, dk))
     k = rng.standard_normal((B, H, T, dk))
     v = rng.standard_normal((B, H, T, dv))
-    bshape = (B, H, T, dv) if variant == "F2" else (B, H, T)
+    bshape = (B, H, T, dv) if variant in ("F2", "F2A") else (B, H, T)
     b = rng.uniform(*beta, bshape)
     lm = rng.uniform(*lam, (B, H, T))
     return q, k, v, b, lm
@@ -248,7 +248,7 @@ def test_per_step_descent(variant, window):
 
 def test_linearity_in_v():
     rng = np.random.default_rng(2)
-    for variant in ["F1", "F2", "F3", "F1A", "F3A"]:
+    for variant in ["F1", "F2", "F3", "F1A", "F2A", "F3A"]:
         q, k, v, beta, lam = _rand(rng, 1, 2, 7, 3, 4, variant)
         w = 3 if variant in ("F3", "F3A") else 1
         o1, s1 = falcon_forward(variant, q, k, v, beta, lam, window=w)
@@ -259,12 +259,12 @@ def test_linearity_in_v():
 
 def test_columns_and_heads_independent():
     rng = np.random.default_rng(4)
-    for variant in ["F1", "F2", "F3", "F1A", "F3A"]:
+    for variant in ["F1", "F2", "F3", "F1A", "F2A", "F3A"]:
         q, k, v, beta, lam = _rand(rng, 2, 2, 6, 3, 6, variant)
         w = 2 if variant in ("F3", "F3A") else 1
         o, st = falcon_forward(variant, q, k, v, beta, lam, window=w)
         for sl in (slice(0, 2), slice(2, 6)):
-            b = beta[..., sl] if variant == "F2" else beta
+            b = beta[..., sl] if variant in ("F2", "F2A") else beta
             oh, sh = falcon_forward(variant, q, k, v[..., sl], b, lam, window=w)
             np.testing.assert_allclose(oh, o[..., sl], rtol=1e-13, atol=1e-14)
         o1, _ = falcon_forward(variant, q[1:, :1], k[1:, :1], v[1:, :1], beta[1:, :1], lam[1:, :1], window=w)
@@ -291,6 +291,50 @@ def test_f2_equal_gains_is_f1():
     o2, s2 = falcon_forward("F2", q, k, v, b2, lam)
     np.testing.assert_allclose(o2, o1, rtol=1e-13, atol=1e-14)
     np.testing.assert_allclose(s2.S, s1.S, rtol=1e-13, atol=1e-14)
+
+
+def test_f2a_equal_gains_is_f1a():
+    """The same gain in every value column makes Falcon-2A the scalar
+    inner-product write Falcon-1A (summary §4.3, §4.5)."""
+    rng = np.random.default_rng(9)
+    q, k, v, beta, lam = _rand(rng, 2, 1, 11, 4, 5)
+    o1, s1 = falcon_forward("F1A", q, k, v, beta, lam)
+    o2, s2 = falcon_forward("F2A", q, k, v, np.repeat(beta[..., None], 5, -1), lam)
+    np.testing.assert_allclose(o2, o1, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(s2.S, s1.S, rtol=1e-13, atol=1e-14)
+
+
+def test_f2a_column_is_f1a_with_that_columns_gains():
+    """Each value column of Falcon-2A follows its own gain, decay and write:
+    column j equals Falcon-1A run on value column j alone with the gains
+    beta_{:, j} (summary "B. Falcon-2A: per-channel inner-product write")."""
+    rng = np.random.default_rng(10)
+    q, k, v, beta, lam = _rand(rng, 2, 2, 9, 4, 5, "F2A", lam=(0.0, 3.0))
+    o, st = falcon_forward("F2A", q, k, v, beta, lam, eps_gamma=0.05)
+    for j in range(5):
+        oj, sj = falcon_forward("F1A", q, k, v[..., j:j + 1], beta[..., j], lam, eps_gamma=0.05)
+        np.testing.assert_allclose(o[..., j:j + 1], oj, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(st.S.reshape(4, 4, 5)[..., j:j + 1], sj.S, rtol=1e-13, atol=1e-14)
+
+
+def test_f2a_no_ridge_is_additive():
+    """lambda = 0: no decay, purely additive per-column writes,
+    o_{t,j} = sum_{s<=t} eta_{s,j} (qh_t . x_s) v_{s,j} with
+    eta_{s,j} = beta_{s,j} / (||x_s||^2 + eps) (summary §4.5)."""
+    rng = np.random.default_rng(11)
+    T, dk, dv = 8, 3, 4
+    q, k, v, beta, _ = _rand(rng, 1, 1, T, dk, dv, "F2A")
+    lam = np.zeros((1, 1, T))
+    o, _ = falcon_forward("F2A", q, k, v, beta, lam, eps=1e-6)
+    qh = pf.rms_feature(q[0, 0], 1e-6)
+    kh = pf.rms_feature(k[0, 0], 1e-6)
+    x = np.vstack([np.zeros(dk), kh[:-1]])
+    ref = np.zeros((T, dv))
+    for t in range(T):
+        for s in range(1, t + 1):          # s = 0 is the fresh no-op step
+            eta = beta[0, 0, s] / (x[s] @ x[s] + 1e-6)
+            ref[t] += eta * (qh[t] @ x[s]) * v[0, 0, s]
+    np.testing.assert_allclose(o[0, 0], ref, rtol=1e-12, atol=1e-13)
 
 
 @pytest.mark.parametrize("pair", [("F3", "F1"), ("F3A", "F1A")])
@@ -329,7 +373,7 @@ def test_window_lambda_max_three_ways():
 # equivalent forms (independent code in pin_forms.py)
 # --------------------------------------------------------------------------
 
-VARIANT_CASES = [("F1", 1), ("F2", 1), ("F1A", 1), ("F3A", 3), ("F3", 3), ("F3A", 1), ("F3", 2)]
+VARIANT_CASES = [("F1", 1), ("F2", 1), ("F1A", 1), ("F2A", 1), ("F3A", 3), ("F3", 3), ("F3A", 1), ("F3", 2)]
 
 
 @pytest.mark.parametrize("variant,window", VARIANT_CASES)
@@ -375,7 +419,8 @@ def test_renormalized_form_equals_recurrence():
 # continuation
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("variant,window", [("F1", 1), ("F2", 1), ("F3", 4), ("F1A", 1), ("F3A", 4)])
+@pytest.mark.parametrize("variant,window", [("F1", 1), ("F2", 1), ("F3", 4), ("F1A", 1), ("F2A", 1),
+                                            ("F3A", 4)])
 def test_continuation_is_exact(variant, window):
     """Splitting anywhere and carrying (S, x_next, last W-1 pairs) gives the
     single-run outputs and state (summary §C.7, §4.4; blog)."""
