@@ -31,7 +31,7 @@ def algorithmic_bytes(w) -> int:
     writes x_next and the tail."""
     esz = 2 if w.dtype == "bf16" else 4
     n = w.batch * w.heads * w.seqlen
-    beta_cols = w.dv if w.variant == "F2" else 1
+    beta_cols = w.dv if w.variant in ("F2", "F2A") else 1
     total = (n * (2 * w.dk + 2 * w.dv) * esz + n * (beta_cols + 1) * 4
              + w.batch * w.heads * w.dk * w.dv * 4)
     if w.seqlen == 1:
@@ -50,6 +50,7 @@ def algorithmic_flops(w) -> int:
            "F2": 2 * C * w.dk + 3 * C * w.dv + 6 * w.dk * w.dv,
            "F3": 2 * C * (w.dk + w.dv) * w.window + 6 * w.dk * w.dv,
            "F1A": C * (w.dk + w.dv) + 4 * w.dk * w.dv,
+           "F2A": C * (w.dk + w.dv) + 4 * w.dk * w.dv,
            "F3A": C * (w.dk + w.dv) + 4 * w.dk * w.dv}[w.variant]
     return w.batch * w.heads * w.seqlen * per
 

@@ -15,8 +15,9 @@
  *     "Method"; sungsoo.github.io post (clamp and log1p paragraph);
  *   - the writes of Falcon-1 (scalar NLMS), Falcon-2 (per value column),
  *     Falcon-3 (window mini-batch, mu_t = lambda_max of the window
- *     covariance), Falcon-1A / Falcon-3A (inner-product writes):
- *     summary §1, §4, §4.3-§4.5, App. F; explainer "Method";
+ *     covariance), Falcon-1A / Falcon-2A / Falcon-3A (inner-product writes,
+ *     scalar / per value column / window): summary §1, §4, §4.3-§4.5, App. F;
+ *     explainer "Method";
  *   - the feature map phi = QK-RMSNorm (default) or the identity:
  *     summary §5 and §H.3 "The Falcon-3 Recurrence";
  *   - the recurrent and chunk-parallel forms and the chunk-local log-decay:
@@ -31,7 +32,7 @@
  *     memory and are read during the call only.
  *   - Layouts are contiguous row-major with batch, then head, then token,
  *     then feature: q, k [B,H,T,d_k]; v, o [B,H,T,d_v]; beta [B,H,T]
- *     ([B,H,T,d_v] for Falcon-2); lambda [B,H,T]; S [B,H,d_k,d_v].
+ *     ([B,H,T,d_v] for Falcon-2 and -2A); lambda [B,H,T]; S [B,H,d_k,d_v].
  *   - Errors are returned as negative status codes (falcon_status_str gives
  *     the text).  On any error except FALCON_ERR_HIP nothing is launched.
  *   - falcon_fwd enqueues work on the given stream and returns without
@@ -70,12 +71,14 @@ extern "C" {
 #define FALCON_ERR_HIP (-4)         /* a kernel launch failed (hipGetLastError)    */
 
 /* variants: 1/2/3 = scalar, per-column, sliding-window regression;
- * 11/13 = scalar and sliding-window inner-product writes (2A = 12 is not
- * provided) */
+ * 11/12/13 = scalar, per-column, sliding-window inner-product writes
+ * (Falcon-2A: summary "B. Falcon-2A: per-channel inner-product write",
+ * §4.3, §4.5, Figures 6-8) */
 #define FALCON_V1 1
 #define FALCON_V2 2
 #define FALCON_V3 3
 #define FALCON_V1A 11
+#define FALCON_V2A 12
 #define FALCON_V3A 13
 
 /* storage type of q, k, v and o */
@@ -115,7 +118,7 @@ typedef struct falcon_state {
 /*
  * Arguments of one forward call.
  *   abi_version  must equal FALCON_ABI_VERSION.
- *   variant      FALCON_V1, _V2, _V3, _V1A or _V3A.
+ *   variant      FALCON_V1, _V2, _V3, _V1A, _V2A or _V3A.
  *   dtype        FALCON_BF16 or FALCON_F32 (q, k, v, o).  State, beta and
  *                lambda are always fp32; all arithmetic accumulates in fp32.
  *   phi          FALCON_PHI_RMSNORM or FALCON_PHI_IDENTITY.
@@ -126,7 +129,7 @@ typedef struct falcon_state {
  *                any dv) and Falcon-1A / 3A (dk in {32, 64}, dv <= 64).
  *                A combination that has no chunk-parallel kernel returns
  *                FALCON_ERR_UNSUPPORTED.
- *   window       W >= 1; must be 1 for V1, V2, V1A; at most FALCON_MAX_WINDOW.
+ *   window       W >= 1; must be 1 for V1, V2, V1A, V2A; at most FALCON_MAX_WINDOW.
  *   eps >= 0, eps_rms >= 0, 0 < eps_gamma < 1 (defaults 1e-6, 1e-6, 1e-3).
  *   q, k, v      device inputs, 16-byte aligned.
  *   beta, lambda device fp32 inputs, 16-byte aligned.

@@ -69,7 +69,7 @@ def build(verbose: bool = False) -> pathlib.Path:
 KERNEL_SOURCES = {"passthrough": "feature.hip", "feature": "feature.hip", "recurrent": "recurrent.hip",
                   "decode": "decode.hip",
                   "chunk_f1_prep": "chunk_f1.hip", "chunk_f1_scan": "chunk_f1.hip",
-                  "chunk_f2": "chunk_f2.hip",
+                  "chunk_f2": "chunk_f2.hip", "chunk_f2a": "chunk_f2a.hip",
                   "f3_prep": "chunk_f3.hip", "f3_scan": "chunk_f3.hip",
                   "f1_xfer": "chunk_f1_xfer.hip", "f1_carry": "chunk_f1_xfer.hip",
                   "a_segment": "chunk_a.hip", "a_segscan": "chunk_a.hip", "a_output": "chunk_a.hip",

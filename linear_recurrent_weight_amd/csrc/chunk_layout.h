@@ -69,6 +69,10 @@ constexpr size_t f1_xfer_bytes(int dv) { return f1_xfer_scal_off(dv) + 256; }
 // head share the operator traffic), never more than d_v
 constexpr int f1_xfer_slice(int dv) { return dv < 32 ? dv : 32; }
 
+// Falcon-2A chunk path (chunk_f2a.hip): d_k in {32, 64}, any d_v (slices of
+// up to 64 columns), no workspace.
+constexpr bool chunk_f2a_supported(int dk, int dv) { return (dk == 32 || dk == 64) && dv % 16 == 0; }
+
 // Falcon-1A / Falcon-3A chunk path: d_k in {32, 64}, d_v in {16, 32, 64}.
 constexpr bool chunk_a_supported(int dk, int dv) {
     return (dk == 32 || dk == 64) && (dv == 16 || dv == 32 || dv == 64);

@@ -15,7 +15,8 @@
 //         a strict no-op (summary §3.1, §C.3; explainer "Method");
 //   F1 : S = gamma S + eta x (y - S^T x)^T       F2: per value column
 //   F3 : S = gamma S + (eta/B) sum_j x_j (y_j - S^T x_j)^T
-//   F1A: S = gamma S + eta x y^T                  F3A: S = gamma S + (eta/B) sum_j x_j y_j^T
+//   F1A: S = gamma S + eta x y^T                  F2A: per value column
+//   F3A: S = gamma S + (eta/B) sum_j x_j y_j^T
 //   o   = S^T qh (read after write);
 //   out: S, x_next = phi(k_1), the last W-1 pairs.
 //
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     float eta[kCpw], gam[kCpw];
 #pragma unroll
     for (int c = 0; c < kCpw; ++c) {
-        const float beta = VK == FALCON_V2 ? a.beta[size_t(bh) * dv + c0 + c] : a.beta[bh];
+        const float beta = (VK == FALCON_V2 || VK == FALCON_V2A) ? a.beta[size_t(bh) * dv + c0 + c] : a.beta[bh];
         const float e = noop ? 0.f : step_eta(beta, den);
         eta[c] = e;
         gam[c] = 1.f - (noop ? 0.f : step_alpha(e, lam, a.eps_gamma));
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
             for (int r = 0; r < RPL; ++r) S[r][c] = gam[c] * S[r][c] + eta[c] * x[r] * res;
         }
-    } else if constexpr (VK == FALCON_V1A) {
+    } else if constexpr (VK == FALCON_V1A || VK == FALCON_V2A) {
 #pragma unroll
         for (int c = 0; c < kCpw; ++c)
 #pragma unroll
@@ -262,6 +263,7 @@ void launch_dec_variant(const DecodeArgs &a, dim3 grid, hipStream_t s) {
         case FALCON_V2: decode_kernel<E, RPL, FALCON_V2><<<grid, 256, 0, s>>>(a); break;
         case FALCON_V3: decode_kernel<E, RPL, FALCON_V3><<<grid, 256, 0, s>>>(a); break;
         case FALCON_V1A: decode_kernel<E, RPL, FALCON_V1A><<<grid, 256, 0, s>>>(a); break;
+        case FALCON_V2A: decode_kernel<E, RPL, FALCON_V2A><<<grid, 256, 0, s>>>(a); break;
         default: decode_kernel<E, RPL, FALCON_V3A><<<grid, 256, 0, s>>>(a); break;
     }
 }

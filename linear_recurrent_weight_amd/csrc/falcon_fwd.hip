@@ -47,6 +47,7 @@ const char *const kNamesChunkA[] = {"a_segment", "a_segscan", "a_output"};
 const char *const kNamesChunkA1[] = {"a1_segment", "a1_segscan", "a1_output"};
 const char *const kNamesChunkA3[] = {"a3_window", "a1_segment", "a1_segscan", "a1_output"};
 const char *const kNamesChunkF2[] = {"chunk_f2"};
+const char *const kNamesChunkF2A[] = {"chunk_f2a"};
 const char *const kNamesChunkF3[] = {"feature", "f3_prep", "f3_scan"};
 const char *const kNamesChunkF1Xfer[] = {"f1_xfer", "f1_carry"};
 
@@ -156,7 +157,7 @@ int run(const falcon_fwd_args *args, void *stream, Marks *m) {
             ca.lg = p.ws_at<float>(p.off_alpha);
             launch_chunk_a(ca, p.dtype == FALCON_BF16, s, m);
         }
-    } else if (p.path == Path::kChunkF2) {
+    } else if (p.path == Path::kChunkF2 || p.path == Path::kChunkF2A) {
         ChunkF2Args fa{};
         fa.BH = p.BH;
         fa.T = p.T;
@@ -178,7 +179,8 @@ int run(const falcon_fwd_args *args, void *stream, Marks *m) {
         fa.S_out = p.S_out;
         fa.xnext_out = p.xnext_out;
         fa.o = p.o;
-        launch_chunk_f2(fa, p.dtype == FALCON_BF16, s, m);
+        if (p.path == Path::kChunkF2A) launch_chunk_f2a(fa, p.dtype == FALCON_BF16, s, m);
+        else launch_chunk_f2(fa, p.dtype == FALCON_BF16, s, m);
     } else if (p.path == Path::kChunkF1Xfer) {
         F1XferArgs fa{};
         fa.BH = p.BH;
@@ -339,6 +341,7 @@ extern "C" const char *falcon_kernel_name(const falcon_fwd_args *args, int i) {
             if (p.window > 1) return i < 4 ? kNamesChunkA3[i] : nullptr;
             return i < 3 ? kNamesChunkA1[i] : nullptr;
         case Path::kChunkF2: return i < 1 ? kNamesChunkF2[i] : nullptr;
+        case Path::kChunkF2A: return i < 1 ? kNamesChunkF2A[i] : nullptr;
         case Path::kChunkF3: return i < 3 ? kNamesChunkF3[i] : nullptr;
         case Path::kChunkF1Xfer: return i < 2 ? kNamesChunkF1Xfer[i] : nullptr;
         default: return nullptr;

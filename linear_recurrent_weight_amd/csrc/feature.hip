@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void feature_kernel(FeatureArgs a) {
     }
 
     // 3. step scalars
-    const bool per_col = (a.variant == FALCON_V2);
+    const bool per_col = (a.variant == FALCON_V2 || a.variant == FALCON_V2A);
     if (tid < kTile) {
         const int t = t0 + tid;
         float den = 0.f;

@@ -143,6 +143,8 @@ void launch_chunk_a(const ChunkAArgs &a, bool bf16, hipStream_t s, Marks *m);
 // bf16 Falcon-1A with d_k = d_v = 64 (etaw and lg unused)
 void launch_chunk_a1(const ChunkAArgs &a, hipStream_t s, Marks *m);
 void launch_chunk_f2(const ChunkF2Args &a, bool bf16, hipStream_t s, Marks *m);
+// Falcon-2A (same arguments as Falcon-2: per-column beta), d_k in {32, 64}
+void launch_chunk_f2a(const ChunkF2Args &a, bool bf16, hipStream_t s, Marks *m);
 void launch_chunk_f3(const ChunkF3Args &a, bool bf16, hipStream_t s, Marks *m);
 // bf16 Falcon-1, d_k = 64: transfer operators, then the carry over slices of
 // `slice` value columns

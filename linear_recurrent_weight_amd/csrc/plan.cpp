@@ -35,7 +35,7 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
     if (a->abi_version != FALCON_ABI_VERSION) return FALCON_ERR_INVALID_ARG;
     const int var = a->variant;
     if (var != FALCON_V1 && var != FALCON_V2 && var != FALCON_V3 && var != FALCON_V1A &&
-        var != FALCON_V3A)
+        var != FALCON_V2A && var != FALCON_V3A)
         return FALCON_ERR_INVALID_ARG;
     if (a->dtype != FALCON_BF16 && a->dtype != FALCON_F32) return FALCON_ERR_INVALID_ARG;
     if (a->phi != FALCON_PHI_RMSNORM && a->phi != FALCON_PHI_IDENTITY) return FALCON_ERR_INVALID_ARG;
@@ -80,6 +80,8 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
             p->path = Path::kChunkF1;
         } else if (var == FALCON_V2 && chunk_f2_supported(a->dtype == FALCON_BF16, a->dk, a->dv)) {
             p->path = Path::kChunkF2;
+        } else if (var == FALCON_V2A && chunk_f2a_supported(a->dk, a->dv)) {
+            p->path = Path::kChunkF2A;
         } else if (var == FALCON_V3 && chunk_f3_supported(a->dk, a->dv)) {
             p->path = Path::kChunkF3;
         } else if (chunk_a1_supported(a->dtype == FALCON_BF16, var, a->window, a->dk, a->dv)) {
@@ -117,7 +119,7 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
     size_t off = 0;
     if (p->path == Path::kDecode) {
         // no workspace: the step reads the inputs and the state directly
-    } else if (p->path == Path::kChunkF2) {
+    } else if (p->path == Path::kChunkF2 || p->path == Path::kChunkF2A) {
         p->nchunks = (T + kChunk - 1) / kChunk;
     } else if (p->path == Path::kChunkF1Xfer) {
         p->nchunks = (T + kChunk - 1) / kChunk;
@@ -166,7 +168,7 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
         const size_t fsz = p->feat_f32 ? 4 : 2;
         p->off_xn = off; off = align_up(off + rows * a->dk * fsz);
         p->off_qn = off; off = align_up(off + rows * a->dk * fsz);
-        const size_t ncol = (var == FALCON_V2) ? a->dv : 1;
+        const size_t ncol = (var == FALCON_V2 || var == FALCON_V2A) ? a->dv : 1;
         p->off_eta = off; off = align_up(off + rows * ncol * 4);
         p->off_alpha = off; off = align_up(off + rows * ncol * 4);
         if (p->path == Path::kChunkF1 || p->path == Path::kChunkF3) {
@@ -191,7 +193,7 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
             !aligned16(a->beta) || !aligned16(a->lambda))
             return FALCON_ERR_INVALID_ARG;
         // the output may not alias any input
-        const size_t nb = static_cast<size_t>(bh) * T * (var == FALCON_V2 ? a->dv : 1);
+        const size_t nb = static_cast<size_t>(bh) * T * ((var == FALCON_V2 || var == FALCON_V2A) ? a->dv : 1);
         const size_t ot = nv * esz;
         if (overlap(a->o, ot, a->q, nk * esz) || overlap(a->o, ot, a->k, nk * esz) ||
             overlap(a->o, ot, a->v, nv * esz) || overlap(a->o, ot, a->beta, nb * 4) ||

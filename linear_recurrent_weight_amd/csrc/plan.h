@@ -20,6 +20,7 @@ enum class Path : int {
     kChunkF1Xfer = 8,   // chunk-parallel Falcon-1, bf16: per-chunk transfer operators, then the carry
     kChunkA1 = 9,    // chunk-parallel Falcon-1A, bf16, d_k = d_v = 64: register-operand segment kernels
     kDecode = 11,    // seqlen == 1: the single-token step of any variant, one kernel
+    kChunkF2A = 12,  // chunk-parallel Falcon-2A (per-column inner-product write)
 };
 
 struct Plan {

@@ -13,7 +13,7 @@
 //   F1 : S = gamma S + eta x (y - S^T x)^T           (residual at S_{t-1})
 //   F2 : the same per column with eta_j, gamma_j
 //   F3 : S = gamma S + (eta/B_t) sum_{j in I_t} x_j (y_j - S^T x_j)^T
-//   F1A: S = gamma S + eta x y^T
+//   F1A: S = gamma S + eta x y^T                 F2A: per column with eta_j, gamma_j
 //   F3A: S = gamma S + (eta/B_t) sum_{j in I_t} x_j y_j^T
 //   o_t = S_t^T qh_t (read after write)
 // eta/alpha come from the feature pass, so the fresh first step (eta =
@@ -72,8 +72,9 @@ __global__ __launch_bounds__(256) void recurrent_kernel(RecurrentArgs a) {
 
     const E *v = static_cast<const E *>(a.v);
     E *o = static_cast<E *>(a.o);
-    constexpr int NE = VK == FALCON_V2 ? kCpw : 1;   // step scalars per token
-    constexpr int kTb = VK == FALCON_V2 ? 8 : 16;    // tokens whose inputs are loaded together
+    constexpr bool kPerCol = VK == FALCON_V2 || VK == FALCON_V2A;
+    constexpr int NE = kPerCol ? kCpw : 1;           // step scalars per token
+    constexpr int kTb = kPerCol ? 8 : 16;            // tokens whose inputs are loaded together
     for (int t0 = 0; t0 < T; t0 += kTb) {
         // the inputs of tokens t0 .. t0 + kTb - 1 (rows clamped into [0, T))
         float xb[kTb][RPL], qb[kTb][RPL], yb[kTb][kCpw], eb[kTb][NE], ab[kTb][NE];
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(256) void recurrent_kernel(RecurrentArgs a) {
 #pragma unroll
                     for (int r = 0; r < RPL; ++r) S[r][c] = gam[c] * S[r][c] + eta[c] * x[r] * res;
                 }
-            } else if constexpr (VK == FALCON_V1A) {
+            } else if constexpr (VK == FALCON_V1A || VK == FALCON_V2A) {
 #pragma unroll
                 for (int c = 0; c < kCpw; ++c)
 #pragma unroll
@@ -206,6 +207,7 @@ void launch_rec_width(const RecurrentArgs &a, dim3 grid, hipStream_t s) {
         case FALCON_V2: recurrent_kernel<E, RPL, FALCON_V2, RW><<<grid, 256, 0, s>>>(a); break;
         case FALCON_V3: recurrent_kernel<E, RPL, FALCON_V3, RW><<<grid, 256, 0, s>>>(a); break;
         case FALCON_V1A: recurrent_kernel<E, RPL, FALCON_V1A, RW><<<grid, 256, 0, s>>>(a); break;
+        case FALCON_V2A: recurrent_kernel<E, RPL, FALCON_V2A, RW><<<grid, 256, 0, s>>>(a); break;
         default: recurrent_kernel<E, RPL, FALCON_V3A, RW><<<grid, 256, 0, s>>>(a); break;
     }
 }

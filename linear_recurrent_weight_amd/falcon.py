@@ -19,7 +19,8 @@ LIB_PATH = PKG / "libfalcon.so"
 ABI_VERSION = 1
 MAX_WINDOW = 8
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
-VARIANTS = {"F1": 1, "F2": 2, "F3": 3, "F1A": 11, "F3A": 13}
+VARIANTS = {"F1": 1, "F2": 2, "F3": 3, "F1A": 11, "F2A": 12, "F3A": 13}
+PER_COLUMN = (2, 12)
 DTYPES = {"bf16": 0, "f32": 1}
 PHIS = {"rmsnorm": 0, "identity": 1}
 
@@ -183,7 +184,7 @@ def check_fwd_tensors(q, k, v, beta, lam, *, variant, window, state=None, out=No
     _check_tensor("k", k, (B, H, T, dk), dt, dev)
     _check_tensor("v", v, (B, H, T, dv), dt, dev)
     f32 = torch.float32
-    _check_tensor("beta", beta, (B, H, T, dv) if var == VARIANTS["F2"] else (B, H, T), f32, dev)
+    _check_tensor("beta", beta, (B, H, T, dv) if var in PER_COLUMN else (B, H, T), f32, dev)
     _check_tensor("lambda", lam, (B, H, T), f32, dev)
     if out is not None:
         _check_tensor("out", out, (B, H, T, dv), dt, dev)
@@ -210,7 +211,7 @@ def fwd(q, k, v, beta, lam, *, variant="F1", chunk=64, window=1, eps=1e-6, eps_g
     """Falcon forward pass on the GPU.
 
     q, k: [B,H,T,dk]; v: [B,H,T,dv] (all bf16 or all fp32, contiguous, on the
-    device); beta: [B,H,T] fp32 ([B,H,T,dv] for F2); lam: [B,H,T] fp32.
+    device); beta: [B,H,T] fp32 ([B,H,T,dv] for F2 and F2A); lam: [B,H,T] fp32.
     `stream` is a torch.cuda.Stream (default: the current stream); the
     output, the state and any temporary workspace are allocated on it, so the
     caching allocator never hands them to other streams while the kernels run.

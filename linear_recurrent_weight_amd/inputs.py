@@ -24,7 +24,7 @@ import numpy as np
 @dataclass(frozen=True)
 class Workload:
     name: str
-    variant: str          # F1, F2, F3, F1A, F3A
+    variant: str          # F1, F2, F3, F1A, F2A, F3A
     batch: int
     heads: int
     seqlen: int
@@ -98,7 +98,7 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
     q = rng.standard_normal(shp_k, dtype=np.float32)
     k = rng.standard_normal(shp_k, dtype=np.float32)
     v = rng.standard_normal(shp_v, dtype=np.float32)
-    bshape = shp_v if w.variant == "F2" else shp_k[:3]
+    bshape = shp_v if w.variant in ("F2", "F2A") else shp_k[:3]
     if w.beta_kind == "sigmoid":
         z = rng.standard_normal(bshape)
         beta = (1.0 / (1.0 + np.exp(-z))).astype(np.float32)

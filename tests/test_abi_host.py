@@ -78,7 +78,7 @@ def test_valid_arguments(lib):
 @pytest.mark.parametrize("field,value,status", [
     ("abi_version", 99, fb.ERR_INVALID_ARG),
     ("variant", 4, fb.ERR_INVALID_ARG),
-    ("variant", 12, fb.ERR_INVALID_ARG),
+    ("variant", 14, fb.ERR_INVALID_ARG),
     ("dtype", 2, fb.ERR_INVALID_ARG),
     ("phi", 5, fb.ERR_INVALID_ARG),
     ("batch", 0, fb.ERR_INVALID_ARG),
@@ -309,3 +309,17 @@ def test_single_token_takes_the_decode_kernel(lib):
             assert _names(lib, a) == ["decode"]
             assert wsize(lib, a) == 0
             assert validate(lib, a) == fb.OK
+
+
+def test_falcon2a_paths(lib):
+    """Falcon-2A (variant 12): the recurrent form for any head size, the
+    chunk kernel for d_k in {32, 64}, no workspace on the chunk path; it
+    takes no window."""
+    assert validate(lib, with_ws(lib, args(variant="F2A", chunk=0, dk=16, dv=16))) == fb.OK
+    for dk in (32, 64):
+        a = args(variant="F2A", dk=dk, dv=128)
+        assert _names(lib, a) == ["chunk_f2a"]
+        assert wsize(lib, a) == 0
+        assert validate(lib, a) == fb.OK
+    assert validate(lib, with_ws(lib, args(variant="F2A", dk=128))) == fb.ERR_UNSUPPORTED
+    assert validate(lib, args(variant="F2A", window=2)) == fb.ERR_INVALID_ARG

@@ -49,7 +49,7 @@ def check_against_oracle(w, inp, o, st, tol):
 
 
 @pytest.mark.parametrize("variant,window", [("F1", 1), ("F2", 1), ("F3", 3), ("F3", 8), ("F1A", 1),
-                                            ("F3A", 2), ("F3A", 8)])
+                                            ("F2A", 1), ("F3A", 2), ("F3A", 8)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("dk,dv", [(16, 16), (64, 64), (128, 32)])
 def test_decode_chain_equals_one_call(variant, window, dtype, dk, dv):
@@ -65,7 +65,7 @@ def test_decode_chain_equals_one_call(variant, window, dtype, dk, dv):
 
 
 @pytest.mark.parametrize("variant,window,chunk", [("F1", 1, 64), ("F2", 1, 64), ("F3", 4, 64),
-                                                  ("F1A", 1, 64), ("F3A", 8, 64), ("F1", 1, 0)])
+                                                  ("F1A", 1, 64), ("F2A", 1, 64), ("F3A", 8, 64), ("F1", 1, 0)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_decode_after_prefill(variant, window, chunk, dtype):
     """A chunk-parallel (or recurrent) prefill of 130 tokens, then 10
@@ -101,7 +101,7 @@ def test_decode_is_one_kernel():
     import ctypes
     from linear_recurrent_weight_amd import falcon as fb
     lib = fb.load_library()
-    for var, W in (("F1", 1), ("F2", 1), ("F3", 5), ("F1A", 1), ("F3A", 8)):
+    for var, W in (("F1", 1), ("F2", 1), ("F3", 5), ("F1A", 1), ("F2A", 1), ("F3A", 8)):
         for chunk in (0, 64):
             a = fb.make_args(variant=var, dtype="bf16", batch=2, heads=3, seqlen=1, dk=64, dv=64,
                              chunk=chunk, window=W)

@@ -12,7 +12,7 @@ import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
 
-VARIANT_WINDOWS = [("F1", 1), ("F2", 1), ("F3", 3), ("F1A", 1), ("F3A", 3), ("F3", 8), ("F3A", 8)]
+VARIANT_WINDOWS = [("F1", 1), ("F2", 1), ("F3", 3), ("F1A", 1), ("F2A", 1), ("F3A", 3), ("F3", 8), ("F3A", 8)]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -139,7 +139,7 @@ def test_recurrent_variants(variant, window, dtype):
 
 
 @pytest.mark.parametrize("T", [1, 7, 8, 9, 15, 16, 17, 33])
-@pytest.mark.parametrize("variant,window", [("F1", 1), ("F2", 1), ("F3A", 3)])
+@pytest.mark.parametrize("variant,window", [("F1", 1), ("F2", 1), ("F2A", 1), ("F3A", 3)])
 def test_recurrent_lengths(variant, window, T):
     """Lengths around the token batches of the recurrent kernel (16 tokens, 8
     for Falcon-2), with reductions over 16 lanes (d_k = 16) and the whole wave."""
@@ -669,3 +669,70 @@ def test_chunk_f2_steep_decay_blocks(eps_gamma, lam_hi, dtype):
     eo, es = gu.compare(w, np.arange(2), o, st, o_ref, st_ref)
     tol = gu.tol_for(w)
     assert eo <= tol and es <= tol, (eo, es)
+
+
+# -- Falcon-2A chunk path -------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 200, 700])
+def test_chunk_f2a_lengths(dtype, T):
+    check(gu.small("F2A", dtype, B=2, H=3, T=T, dk=64, dv=64, chunk=64, seed=T + 3))
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 16), (32, 64), (64, 32), (64, 128), (64, 16)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_f2a_head_dims(dk, dv, dtype):
+    """Slices of 16, 32 and 64 value columns (d_v = 128: two workgroups per
+    head), d_k of 32 and 64."""
+    w = gu.small("F2A", dtype, B=1, H=3, T=200, dk=dk, dv=dv, chunk=64, seed=dk + dv)
+    check(w, heads=np.arange(3))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_f2a_strong_decay_runs_token_by_token(dtype):
+    """beta in (1, 2) and a ridge far above ||x||^2 put the clamp on most
+    (token, column) pairs: chunks whose decay falls below 2^-64 take the
+    token-by-token form; others the renormalised one."""
+    w = gu.small("F2A", dtype, B=1, H=2, T=300, dk=64, dv=32, chunk=64, lam_lo=0.0, lam_hi=400.0,
+                 eps_gamma=0.01, seed=77)
+    inp = gu.make(w)
+    inp["beta"] = (1.0 + inp["beta"]).astype(np.float32)
+    dev = gu.to_device(inp, w)
+    o, st = gu.run_gpu(w, dev)
+    o_ref, st_ref, tr = gu.oracle_heads(w, inp, np.arange(2), trace=True)
+    assert (tr.alpha >= 1 - 0.01 - 1e-9).mean() > 0.3
+    eo, es = gu.compare(w, np.arange(2), o, st, o_ref, st_ref)
+    tol = gu.tol_for(w)
+    assert eo <= tol and es <= tol, (eo, es)
+
+
+@pytest.mark.parametrize("split", [0, 3, 64, 100])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunk_f2a_continuation(split, dtype):
+    import torch
+    w = gu.small("F2A", dtype, B=2, H=2, T=160, dk=64, dv=32, chunk=64, seed=12)
+    inp = gu.make(w)
+    dev = gu.to_device(inp, w)
+    a = {k: v[:, :, :split].contiguous() for k, v in dev.items()}
+    b = {k: v[:, :, split:].contiguous() for k, v in dev.items()}
+    o1, st1 = gu.run_gpu(w.with_(seqlen=split), a)
+    o2, st2 = gu.run_gpu(w.with_(seqlen=160 - split), b, state=st1)
+    heads = np.arange(4)
+    o_ref, st_ref = gu.oracle_heads(w, inp, heads)
+    eo, es = gu.compare(w, heads, torch.cat([o1, o2], 2), st2, o_ref, st_ref)
+    tol = gu.tol_for(w)
+    assert eo <= tol and es <= tol, (eo, es)
+
+
+def test_chunk_f2a_equal_gains_is_falcon1a():
+    """The same gain in every column: the Falcon-2A chunk kernel and the
+    Falcon-1A chunk kernels agree to fp32 rounding."""
+    w1 = gu.small("F1A", "f32", B=2, H=2, T=333, dk=64, dv=64, chunk=64, seed=5)
+    inp = gu.make(w1)
+    dev1 = gu.to_device(inp, w1)
+    o1, st1 = gu.run_gpu(w1, dev1)
+    dev2 = dict(dev1)
+    dev2["beta"] = dev1["beta"][..., None].expand(*dev1["beta"].shape, 64).contiguous()
+    o2, st2 = gu.run_gpu(w1.with_(variant="F2A"), dev2)
+    assert gu.max_rel_err(o2.double().cpu().numpy(), o1.double().cpu().numpy()) <= 1e-5
+    assert gu.max_rel_err(st2.S.double().cpu().numpy(), st1.S.double().cpu().numpy()) <= 1e-5
