@@ -522,7 +522,7 @@ template <int DS> constexpr int carry_rs() { return DS == 64 ? 2 : 4; }
 template <int DS> constexpr int carry_threads() { return (DS / 16 * carry_rs<DS>() + 4) * 64; }
 
 template <int DS>
-__global__ __launch_bounds__(carry_threads<DS>()) void f1_carry(F1XferArgs a, int nslice) {
+__global__ __launch_bounds__(carry_threads<DS>()) void f1_carry(F1XferArgs a, int nslice, int nbase) {
     constexpr int NCT = DS / 16;                 // column tiles of the slice
     constexpr int RS = carry_rs<DS>();           // row groups per column tile
     constexpr int MT = 4 / RS;                   // row tiles (of 16) per compute wave
@@ -539,12 +539,14 @@ __global__ __launch_bounds__(carry_threads<DS>()) void f1_carry(F1XferArgs a, in
     __shared__ __align__(16) unsigned char ring[NB * SB];
     __shared__ __align__(16) bf16_t STw[2][NCT][16 * PK];   // bf16 S^T [j][d] per column tile, by chunk parity
 
+    // workgroup -> (segment, head, slice); the slices of a head share an XCD
     int bh, s;
+    const int g = blockIdx.x / nbase, id = blockIdx.x % nbase;
     if (nslice == 1) {
-        bh = blockIdx.x;
+        bh = id;
         s = 0;
     } else {
-        const int id = blockIdx.x, u = id & 7, rest = id >> 3;
+        const int u = id & 7, rest = id >> 3;
         s = rest % nslice;
         bh = (rest / nslice) * 8 + u;
     }
@@ -552,9 +554,15 @@ __global__ __launch_bounds__(carry_threads<DS>()) void f1_carry(F1XferArgs a, in
     const int j0 = s * DS;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int T = a.T, DV = a.dv, nch = a.nchunks;
+    const int T = a.T, DV = a.dv;
+    // this workgroup's chunks: [c_lo, c_lo + nch) of segment g
+    const int c_lo = g * a.seg_chunks;
+    const int nch = (a.nchunks - c_lo) < a.seg_chunks ? a.nchunks - c_lo : a.seg_chunks;
+    const bool last_seg = g == a.nseg - 1;
     const size_t rb = f1_xfer_bytes(DV);
-    const char *recs = static_cast<const char *>(a.ops) + size_t(bh) * nch * rb;
+    const char *recs = static_cast<const char *>(a.ops) + (size_t(bh) * a.nchunks + c_lo) * rb;
+    // entry state: the incoming state, or the segment's from the scan
+    const float *S0 = g == 0 ? a.S_in : a.Sseg + (size_t(bh) * a.nseg + g) * DK * DV;
 
     if (wave >= NCW) {
         // ---- loader waves: chunk cc's operators into slot cc % NB ----
@@ -600,7 +608,7 @@ __global__ __launch_bounds__(carry_threads<DS>()) void f1_carry(F1XferArgs a, in
             wait_chunk(last - (c + 1));   // chunk c + 1 complete before the barrier
             loader_barrier();
         }
-        if (lw == 0 && s == 0 && a.xnext_out) {   // x for the next segment: phi(k_{T-1})
+        if (lw == 0 && s == 0 && last_seg && a.xnext_out) {   // x for the next call: phi(k_{T-1})
             const bf16_t *kg = static_cast<const bf16_t *>(a.k) + size_t(bh) * T * DK;
             const float xv = bf16_to_f32(kg[size_t(T - 1) * DK + lane].bits);
             const float sc = phi_scale(wave_sum(xv * xv), DK, a.eps_rms, a.phi);
@@ -626,7 +634,7 @@ __global__ __launch_bounds__(carry_threads<DS>()) void f1_carry(F1XferArgs a, in
         const int m = MT * mh + h;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            S[h][r] = a.S_in ? a.S_in[(size_t(bh) * DK + 16 * m + g4 + r) * DV + j0 + 16 * ct + col] : 0.f;
+            S[h][r] = S0 ? S0[(size_t(g == 0 ? bh : 0) * DK + 16 * m + g4 + r) * DV + j0 + 16 * ct + col] : 0.f;
         put2(STw[0][ct] + col * PK + 16 * m + g4, pk4(S[h]));
     }
     __syncthreads();
@@ -663,17 +671,195 @@ __global__ __launch_bounds__(carry_threads<DS>()) void f1_carry(F1XferArgs a, in
             put2(stn + col * PK + 16 * m + g4, pk4(S[h]));
             // outputs: O^T = S^T G^T + H^T (token tile m)
             const f32x4 o = mfma(sb0, q0[h], unpk4(hq[h])) + mfma(sb1, q1[h], z);
-            const int tg = c * C + 16 * m + col;
+            const int tg = (c_lo + c) * C + 16 * m + col;
             if (tg < T) put2(og + size_t(tg) * DV, pk4(o));
         }
         __syncthreads();
     }
-    if (a.S_out) {
+    if (a.S_out && last_seg) {
 #pragma unroll
         for (int h = 0; h < MT; ++h)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 a.S_out[(size_t(bh) * DK + 16 * (MT * mh + h) + g4 + r) * DV + j0 + 16 * ct + col] = S[h][r];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Segments: the chunk maps S -> Gamma_c S + A_c S + B_c of a head compose
+// associatively (summary §H.1 "Affine Chunk Map", §H.2), so the walk over a
+// long sequence splits into segments of G chunks that run in parallel:
+//   f1_segmap: each segment's composed map, kept as gamma I + A~ (the
+//     identity part as an exact fp32 scalar) and the offset beta;
+//   f1_segscan: per head, the segments' entry states in order,
+//     S_{g+1} = gamma_g S_g + A~_g S_g + beta_g;
+//   f1_carry: every segment walks its chunks from its entry state.
+// ---------------------------------------------------------------------------
+constexpr int SM_THREADS = 256;
+
+// workgroup barrier after this wave's LDS writes have completed, without
+// the release fence of __syncthreads (which would also wait for the global
+// loads of the next step, issued ahead on purpose)
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4));   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// the parts of a chunk's record one segment-map wave uses: its row tile m of
+// A_c as MFMA A operands (both k halves), its rows of B_c per value tile and
+// the chunk's scalar Gamma_c = e^{b_C}
+template <int DV>
+struct MapRec {
+    bf16x8 a0, a1;
+    uint2 b[DV / 16];
+    float gc;
+    __device__ __forceinline__ void load(const char *rec, int m, int lane) {
+        a0 = ld8(rec + m * 2048 + 16 * lane);
+        a1 = ld8(rec + m * 2048 + 1024 + 16 * lane);
+#pragma unroll
+        for (int n = 0; n < DV / 16; ++n)
+            b[n] = *reinterpret_cast<const uint2 *>(rec + kF1XferBOff + n * 2048 + 8 * lane + m * 512);
+        gc = *reinterpret_cast<const float *>(rec + f1_xfer_scal_off(DV));
+    }
+};
+
+// composed map of segment g of head bh: wave m owns row tile m (16 rows of
+// d) of [A~ | beta] (d_k x (d_k + d_v)) in fp32 accumulators; a bf16 copy of
+// its transpose in LDS is the B operand of A_c [A~ | beta].  The term
+// gamma A_c takes A_c's entries in accumulator order from an MFMA with the
+// identity (exact: one product by 1 per output).
+template <int DV>
+__global__ __launch_bounds__(SM_THREADS) void f1_segmap(F1XferArgs a) {
+    constexpr int NCOL = (DK + DV) / 16;        // column tiles of [A~ | beta]
+    __shared__ __align__(16) bf16_t XT[2][DK + DV][PK];   // bf16 [A~ | beta]^T [col][d]
+    const int nsm = a.nseg - 1;                 // the last segment's map is never used
+    const int bh = blockIdx.x / nsm, g = blockIdx.x % nsm;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int m = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, g4 = 4 * (lane >> 4), k8 = 8 * (lane >> 4);
+    const int nc = a.seg_chunks;                // every segment but the last is whole
+    const size_t rb = f1_xfer_bytes(DV);
+    const char *recs = static_cast<const char *>(a.ops) + (size_t(bh) * a.nchunks + size_t(g) * nc) * rb;
+
+    // identity B operands: column 16 (n % 2) + col of a k half, rows k8 .. + 7
+    bf16x8 id[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) id[p][e] = __bf16(16 * p + col == k8 + e ? 1.f : 0.f);
+
+    f32x4 X[NCOL];
+#pragma unroll
+    for (int n = 0; n < NCOL; ++n) {
+        X[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        put2(&XT[0][16 * n + col][16 * m + g4], make_uint2(0u, 0u));
+    }
+    float gam = 1.f;
+    MapRec<DV> cur;
+    cur.load(recs, m, lane);
+    lds_barrier();
+    for (int c = 0; c < nc; ++c) {
+        MapRec<DV> nxt;   // the next chunk's record loads during this step
+        nxt.load(recs + size_t(c + 1 < nc ? c + 1 : c) * rb, m, lane);
+        const bf16_t *xt = &XT[c & 1][0][0];
+        bf16_t *xn = &XT[(c + 1) & 1][0][0];
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int n = 0; n < NCOL; ++n) {
+            // A~' = Gamma_c A~ + gamma A_c + A_c A~;  beta' = Gamma_c beta + A_c beta + B_c
+            f32x4 acc = X[n] * cur.gc;
+            if (n < DK / 16) acc += gam * mfma(n < 2 ? cur.a0 : cur.a1, id[n & 1], z);
+            else acc += unpk4(cur.b[n - DK / 16]);
+            acc = mfma(cur.a0, ld8(xt + (16 * n + col) * PK + k8), acc);
+            acc = mfma(cur.a1, ld8(xt + (16 * n + col) * PK + 32 + k8), acc);
+            X[n] = acc;
+            put2(xn + (16 * n + col) * PK + 16 * m + g4, pk4(acc));
+        }
+        gam *= cur.gc;
+        cur = nxt;
+        lds_barrier();
+    }
+    float *M = a.Mseg + (size_t(bh) * a.nseg + g) * DK * (DK + DV);
+#pragma unroll
+    for (int n = 0; n < NCOL; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) M[size_t(16 * m + g4 + r) * (DK + DV) + 16 * n + col] = X[n][r];
+    if (tid == 0) a.Gseg[size_t(bh) * a.nseg + g] = gam;
+}
+
+// the parts of a segment map one scan wave uses: rows 16 m + col of A~ as
+// MFMA A operands (rounded to bf16), its rows of beta and gamma
+template <int DV>
+struct ScanMap {
+    float4 a[4];
+    f32x4 b[DV / 16];
+    float gam;
+    __device__ __forceinline__ void load(const float *M, const float *G, int m, int col, int g4, int k8) {
+        const float *arow = M + size_t(16 * m + col) * (DK + DV);
+        a[0] = *reinterpret_cast<const float4 *>(arow + k8);
+        a[1] = *reinterpret_cast<const float4 *>(arow + k8 + 4);
+        a[2] = *reinterpret_cast<const float4 *>(arow + 32 + k8);
+        a[3] = *reinterpret_cast<const float4 *>(arow + 32 + k8 + 4);
+#pragma unroll
+        for (int n = 0; n < DV / 16; ++n)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) b[n][r] = M[size_t(16 * m + g4 + r) * (DK + DV) + DK + 16 * n + col];
+        gam = *G;
+    }
+};
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const float4 &lo, const float4 &hi) {
+    const uint4 u = make_uint4(pk2(lo.x, lo.y), pk2(lo.z, lo.w), pk2(hi.x, hi.y), pk2(hi.z, hi.w));
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+// entry states of the segments of head bh, in order: S_{g+1} = gamma_g S_g +
+// A~_g S_g + beta_g; wave m owns row tile m of S (all value columns)
+template <int DV>
+__global__ __launch_bounds__(SM_THREADS) void f1_segscan(F1XferArgs a) {
+    constexpr int NJ = DV / 16;
+    __shared__ __align__(16) bf16_t ST[2][DV][PK];   // bf16 S^T [j][d]
+    const int bh = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int m = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, g4 = 4 * (lane >> 4), k8 = 8 * (lane >> 4);
+    const size_t msz = size_t(DK) * (DK + DV);
+    const float *Mh = a.Mseg + size_t(bh) * a.nseg * msz;
+    const float *Gh = a.Gseg + size_t(bh) * a.nseg;
+    f32x4 S[NJ];
+#pragma unroll
+    for (int n = 0; n < NJ; ++n) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            S[n][r] = a.S_in ? a.S_in[(size_t(bh) * DK + 16 * m + g4 + r) * DV + 16 * n + col] : 0.f;
+        put2(&ST[0][16 * n + col][16 * m + g4], pk4(S[n]));
+    }
+    const int ns = a.nseg - 1;                  // maps to apply
+    ScanMap<DV> cur;
+    cur.load(Mh, Gh, m, col, g4, k8);
+    lds_barrier();
+    for (int g = 0; g < ns; ++g) {
+        ScanMap<DV> nxt;   // the next map loads during this step
+        const int gn = g + 1 < ns ? g + 1 : g;
+        nxt.load(Mh + gn * msz, Gh + gn, m, col, g4, k8);
+        const bf16x8 a0 = to_bf16x8(cur.a[0], cur.a[1]), a1 = to_bf16x8(cur.a[2], cur.a[3]);
+        const bf16_t *st = &ST[g & 1][0][0];
+        bf16_t *sn = &ST[(g + 1) & 1][0][0];
+        float *Sout = a.Sseg + (size_t(bh) * a.nseg + g + 1) * DK * DV;
+#pragma unroll
+        for (int n = 0; n < NJ; ++n) {
+            f32x4 acc = S[n] * cur.gam + cur.b[n];
+            acc = mfma(a0, ld8(st + (16 * n + col) * PK + k8), acc);
+            acc = mfma(a1, ld8(st + (16 * n + col) * PK + 32 + k8), acc);
+            S[n] = acc;
+            put2(sn + (16 * n + col) * PK + 16 * m + g4, pk4(acc));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Sout[size_t(16 * m + g4 + r) * DV + 16 * n + col] = acc[r];
+        }
+        cur = nxt;
+        lds_barrier();
     }
 }
 
@@ -690,8 +876,16 @@ void launch_xfer(const F1XferArgs &a, hipStream_t s, Marks *m) {
 template <int DS>
 void launch_carry(const F1XferArgs &a, hipStream_t s, Marks *m) {
     const int nslice = a.dv / DS;
-    const int blocks = nslice == 1 ? a.BH : ((a.BH + 7) / 8) * 8 * nslice;
-    f1_carry<DS><<<blocks, carry_threads<DS>(), 0, s>>>(a, nslice);
+    const int nbase = nslice == 1 ? a.BH : ((a.BH + 7) / 8) * 8 * nslice;
+    f1_carry<DS><<<nbase * a.nseg, carry_threads<DS>(), 0, s>>>(a, nslice, nbase);
+    m->mark(s);
+}
+
+template <int DV>
+void launch_segments(const F1XferArgs &a, hipStream_t s, Marks *m) {
+    f1_segmap<DV><<<a.BH * (a.nseg - 1), SM_THREADS, 0, s>>>(a);
+    m->mark(s);
+    f1_segscan<DV><<<a.BH, SM_THREADS, 0, s>>>(a);
     m->mark(s);
 }
 
@@ -702,6 +896,13 @@ void launch_chunk_f1_xfer(const F1XferArgs &a, int slice, hipStream_t s, Marks *
         case 32: launch_xfer<32>(a, s, m); break;
         case 64: launch_xfer<64>(a, s, m); break;
         default: launch_xfer<128>(a, s, m); break;
+    }
+    if (a.nseg > 1) {
+        switch (a.dv) {
+            case 32: launch_segments<32>(a, s, m); break;
+            case 64: launch_segments<64>(a, s, m); break;
+            default: launch_segments<128>(a, s, m); break;
+        }
     }
     (void)slice;   // f1_xfer_slice: 32 columns for every d_v this path takes
     launch_carry<32>(a, s, m);

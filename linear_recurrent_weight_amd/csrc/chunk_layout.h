@@ -68,6 +68,21 @@ constexpr size_t f1_xfer_bytes(int dv) { return f1_xfer_scal_off(dv) + 256; }
 // value columns per workgroup of the carry kernel: 32 (two workgroups per
 // head share the operator traffic), never more than d_v
 constexpr int f1_xfer_slice(int dv) { return dv < 32 ? dv : 32; }
+// Chunks per segment of the carry.  The walk over a head's chunks is the
+// sequential part; when few walks run (few heads) over many chunks, it
+// splits into segments whose composed maps are scanned first.  Segments are
+// sized so that the carry's workgroups (one per compute unit, 256 of them
+// on the chip) run in about one pass, and hold at least 16 chunks so that
+// the map and scan stay short.  A walk of fewer than 48 chunks, or one
+// whose heads alone fill the chip, is not split (returns nchunks).
+constexpr int f1_xfer_segment_chunks(long long bh, int dv, int nchunks) {
+    const long long nslice = dv / f1_xfer_slice(dv);
+    const long long nbase = nslice == 1 ? bh : (bh + 7) / 8 * 8 * nslice;
+    const long long nseg = nbase > 0 ? 256 / nbase : 0;
+    if (nchunks < 48 || nseg < 2) return nchunks;
+    const long long g = (nchunks + nseg - 1) / nseg;
+    return static_cast<int>(g < 16 ? 16 : g);
+}
 
 // Falcon-2A chunk path (chunk_f2a.hip): d_k in {32, 64}, any d_v (slices of
 // up to 64 columns), no workspace.

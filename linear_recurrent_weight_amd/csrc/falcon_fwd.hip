@@ -50,6 +50,7 @@ const char *const kNamesChunkF2[] = {"chunk_f2"};
 const char *const kNamesChunkF2A[] = {"chunk_f2a"};
 const char *const kNamesChunkF3[] = {"feature", "f3_prep", "f3_scan"};
 const char *const kNamesChunkF1Xfer[] = {"f1_xfer", "f1_carry"};
+const char *const kNamesChunkF1XferSeg[] = {"f1_xfer", "f1_segmap", "f1_segscan", "f1_carry"};
 
 int run(const falcon_fwd_args *args, void *stream, Marks *m) {
     Plan p;
@@ -204,6 +205,13 @@ int run(const falcon_fwd_args *args, void *stream, Marks *m) {
         fa.xnext_out = p.xnext_out;
         fa.o = p.o;
         fa.ops = p.ws_at<void>(p.off_chunk);
+        fa.seg_chunks = p.seg_chunks;
+        fa.nseg = p.nseg;
+        if (p.nseg > 1) {
+            fa.Mseg = p.ws_at<float>(p.off_seg_m);
+            fa.Gseg = p.ws_at<float>(p.off_seg_g);
+            fa.Sseg = p.ws_at<float>(p.off_seg_s);
+        }
         launch_chunk_f1_xfer(fa, p.slice, s, m);
     } else {
         FeatureArgs fa{};
@@ -343,7 +351,9 @@ extern "C" const char *falcon_kernel_name(const falcon_fwd_args *args, int i) {
         case Path::kChunkF2: return i < 1 ? kNamesChunkF2[i] : nullptr;
         case Path::kChunkF2A: return i < 1 ? kNamesChunkF2A[i] : nullptr;
         case Path::kChunkF3: return i < 3 ? kNamesChunkF3[i] : nullptr;
-        case Path::kChunkF1Xfer: return i < 2 ? kNamesChunkF1Xfer[i] : nullptr;
+        case Path::kChunkF1Xfer:
+            if (p.nseg > 1) return i < 4 ? kNamesChunkF1XferSeg[i] : nullptr;
+            return i < 2 ? kNamesChunkF1Xfer[i] : nullptr;
         default: return nullptr;
     }
 }

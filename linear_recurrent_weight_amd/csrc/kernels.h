@@ -108,6 +108,12 @@ struct F1XferArgs {
     float *S_out, *xnext_out;
     void *o;
     void *ops;              // per-chunk transfer operators (f1_xfer_bytes(dv) each)
+    // segments of seg_chunks chunks whose maps are composed and scanned
+    // (nseg == 1: one walk over all chunks)
+    int seg_chunks, nseg;
+    float *Mseg;            // [BH][nseg][d_k][d_k + d_v] composed maps (A~ | beta), fp32
+    float *Gseg;            // [BH][nseg] scalar part gamma of the composed maps
+    float *Sseg;            // [BH][nseg][d_k][d_v] entry states of the segments
 };
 
 // one token (T = 1) of every variant, continuing from the incoming state

@@ -123,8 +123,16 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
         p->nchunks = (T + kChunk - 1) / kChunk;
     } else if (p->path == Path::kChunkF1Xfer) {
         p->nchunks = (T + kChunk - 1) / kChunk;
+        p->seg_chunks = f1_xfer_segment_chunks(bh, a->dv, p->nchunks);
+        p->nseg = (p->nchunks + p->seg_chunks - 1) / p->seg_chunks;
         p->off_chunk = off;
         off = align_up(off + static_cast<size_t>(bh) * p->nchunks * f1_xfer_bytes(a->dv));
+        if (p->nseg > 1) {   // composed maps [A~ | beta], their gamma, entry states
+            const size_t ns = static_cast<size_t>(bh) * p->nseg;
+            p->off_seg_m = off; off = align_up(off + ns * a->dk * (a->dk + a->dv) * 4);
+            p->off_seg_g = off; off = align_up(off + ns * 4);
+            p->off_seg_s = off; off = align_up(off + ns * a->dk * a->dv * 4);
+        }
     } else if (p->path == Path::kChunkA1) {
         p->nchunks = (T + kChunk - 1) / kChunk;
         p->Tpad = p->nchunks * kChunk;

@@ -48,11 +48,11 @@ struct Plan {
 
     // workspace carve-up (offsets in bytes from the workspace base)
     int slice = 0;           // value columns per workgroup of the state carry
-    int seg_chunks = 0, nseg = 0;   // segmentation of the Falcon-1A/3A chunk path
+    int seg_chunks = 0, nseg = 0;   // segmentation of the Falcon-1A/3A and bf16 Falcon-1 chunk paths
     bool feat_f32 = true;    // storage type of the normalised features
     size_t off_xn = 0, off_qn = 0, off_eta = 0, off_alpha = 0;
     size_t off_chunk = 0;    // chunk-path operators
-    size_t off_seg_g = 0, off_seg_s = 0;
+    size_t off_seg_g = 0, off_seg_s = 0, off_seg_m = 0;
     size_t chunk_bytes = 0;
     size_t ws_bytes = 0;     // total required
     void *ws = nullptr;

@@ -75,6 +75,10 @@ WORKLOADS = {
     # parity-only extras
     "c3clamp": Workload("c3clamp", "F1A", 2, 12, 2048, 64, 64, 64, 1, "bf16", "sigmoid",
                         0, 0, "uniform", 0.5, 1.0, seed=31, eps_gamma=0.994),
+    # Falcon-1 over the long sequences of c3 (2 x 12 x 16384 x 64, C = 64) with
+    # c2's step distributions: few heads, a 256-chunk walk per head
+    "c3f1": Workload("c3f1", "F1", 2, 12, 16384, 64, 64, 64, 1, "bf16", "sigmoid", 0, 0,
+                     "uniform", 0.0, 0.05, seed=33),
     "c5f3": Workload("c5f3", "F3", 8, 12, 512, 64, 64, 64, 8, "bf16", "sigmoid", 0, 0,
                      "uniform", 0.0, 0.05, seed=51),
 }

@@ -219,6 +219,43 @@ def test_f1_bf16_workspace(lib):
         assert _names(lib, args(seqlen=1000, dv=dv)) == ["f1_xfer", "f1_carry"]
 
 
+def _f1_segments(bh, dv, nchunks):
+    """Chunks per segment of the bf16 Falcon-1 carry: one segment for walks
+    under 48 chunks or when the carry's workgroups (32 value columns each,
+    heads rounded up to 8 when a head has several) alone reach 128;
+    otherwise about 256 / workgroups segments of at least 16 chunks."""
+    nslice = dv // min(dv, 32)
+    nbase = bh if nslice == 1 else -(-bh // 8) * 8 * nslice
+    nseg = 256 // nbase
+    if nchunks < 48 or nseg < 2:
+        return nchunks
+    return max(16, -(-nchunks // nseg))
+
+
+@pytest.mark.parametrize("B,H,T,dv", [(2, 12, 16384, 64), (1, 3, 5000, 32), (1, 1, 3072, 128),
+                                      (8, 12, 1024, 64), (8, 12, 16384, 64), (2, 6, 3000, 64)])
+def test_f1_bf16_long_walks_split_into_segments(lib, B, H, T, dv):
+    """Long walks over few heads compose each segment's chunk maps and scan
+    them before the carry; the workspace adds the composed maps [A~ | beta]
+    (fp32 d_k x (d_k + d_v)), their scalars and the segments' entry states."""
+    a = args(batch=B, heads=H, seqlen=T, dv=dv)
+    bh, nch = B * H, -(-T // 64)
+    g = _f1_segments(bh, dv, nch)
+    nseg = -(-nch // g)
+    align = lambda n: -(-n // 256) * 256
+    per_chunk = 2 * 64 * 64 * 2 + 2 * 64 * dv * 2 + 256
+    n = align(bh * nch * per_chunk)
+    if nseg > 1:
+        n += align(bh * nseg * 64 * (64 + dv) * 4) + align(bh * nseg * 4) + align(bh * nseg * 64 * dv * 4)
+        assert _names(lib, a) == ["f1_xfer", "f1_segmap", "f1_segscan", "f1_carry"]
+    else:
+        assert _names(lib, a) == ["f1_xfer", "f1_carry"]
+    assert wsize(lib, a) == n
+    # the long-sequence workload with few heads is split
+    if (B, H, T) == (2, 12, 16384):
+        assert nseg == 5 and g == 52
+
+
 def test_library_reads_no_tuning_switches():
     """Path choice, slices and segment lengths follow the arguments alone:
     the library source reads no environment variable except the debug check
@@ -323,3 +360,20 @@ def test_falcon2a_paths(lib):
         assert validate(lib, a) == fb.OK
     assert validate(lib, with_ws(lib, args(variant="F2A", dk=128))) == fb.ERR_UNSUPPORTED
     assert validate(lib, args(variant="F2A", window=2)) == fb.ERR_INVALID_ARG
+
+
+def test_every_kernel_name_maps_to_its_source(lib):
+    """The names falcon_kernel_name reports, over every path, are the keys
+    profiles and the bench use to find each kernel's source file, and every
+    name appears in that source."""
+    from linear_recurrent_weight_amd.build import CSRC, KERNEL_SOURCES
+    cases = [args(), args(seqlen=16384, heads=12), args(seqlen=1), args(seqlen=0), args(chunk=0),
+             args(dtype="f32"), args(variant="F2"), args(variant="F2A"), args(variant="F3", window=4),
+             args(variant="F1A"), args(variant="F3A", window=3), args(variant="F1A", dv=32)]
+    seen = set()
+    for a in cases:
+        seen |= set(_names(lib, a))
+    assert {"f1_segmap", "f1_segscan", "decode", "chunk_f2a"} <= seen
+    for nm in seen:
+        assert nm in KERNEL_SOURCES, nm
+        assert nm in (CSRC / KERNEL_SOURCES[nm]).read_text(), nm

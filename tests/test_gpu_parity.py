@@ -345,6 +345,54 @@ def test_chunk_f1_bf16_strong_decay(eps_gamma):
     check(w)
 
 
+# Long walks over few heads split into segments: the segments' composed
+# chunk maps are scanned, then every segment walks its chunks.  Shapes with
+# whole and partial last segments and ragged last chunks, every d_v.
+F1_SEGMENT_SHAPES = [(1, 3, 5000, 32), (1, 1, 3072, 128), (2, 6, 3100, 64), (1, 2, 7000, 64)]
+
+
+@pytest.mark.parametrize("B,H,T,dv", F1_SEGMENT_SHAPES)
+def test_chunk_f1_bf16_segments(B, H, T, dv):
+    w = gu.small("F1", "bf16", B=B, H=H, T=T, dk=64, dv=dv, chunk=64, seed=T + dv)
+    check(w, heads=np.arange(B * H))
+
+
+def test_named_workload_c3f1_segments():
+    """Falcon-1 over 16384 tokens and 24 heads: five segments of 52 chunks."""
+    check_named("c3f1")
+
+
+@pytest.mark.parametrize("split", [4000, 4160])
+def test_chunk_f1_bf16_segments_continuation(split):
+    """Two segmented calls carrying the state match one oracle run (the split
+    falls inside a chunk, then on a chunk boundary)."""
+    import torch
+    B, H, T = 1, 3, 9000
+    w = gu.small("F1", "bf16", B=B, H=H, T=T, dk=64, dv=64, chunk=64, seed=77)
+    inp = gu.make(w)
+    dev = gu.to_device(inp, w)
+    a = {k: v[:, :, :split].contiguous() for k, v in dev.items()}
+    b = {k: v[:, :, split:].contiguous() for k, v in dev.items()}
+    o1, st1 = gu.run_gpu(w.with_(seqlen=split), a)
+    o2, st2 = gu.run_gpu(w.with_(seqlen=T - split), b, state=st1)
+    heads = np.arange(B * H)
+    o_ref, st_ref = gu.oracle_heads(w, inp, heads)
+    eo, es = gu.compare(w, heads, torch.cat([o1, o2], 2), st2, o_ref, st_ref)
+    print(f"    err_o={eo:.3e} err_S={es:.3e}", flush=True)
+    assert eo <= gu.TOL_BF16 and es <= gu.TOL_BF16, (eo, es)
+    got = gu.gpu_state_to_oracle(st2)
+    assert np.allclose(got.x_next, st_ref.x_next, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("lam", [(0.0, 0.05), (500.0, 2000.0)])
+def test_chunk_f1_bf16_segments_decay(lam):
+    """Segment maps whose scalar part underflows (strong ridge: each chunk
+    decays by about 2^-100) and ones that keep most of the state."""
+    w = gu.small("F1", "bf16", B=1, H=2, T=4096, dk=64, dv=64, chunk=64, seed=91).with_(
+        lam_lo=lam[0], lam_hi=lam[1])
+    check(w, heads=np.arange(2))
+
+
 # -- Falcon-1A / Falcon-3A chunk path -------------------------------------------
 
 @pytest.mark.parametrize("name", ["c3", "c5", "c3clamp"])
