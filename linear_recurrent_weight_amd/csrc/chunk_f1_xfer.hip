@@ -561,7 +561,8 @@ __global__ __launch_bounds__(carry_threads<DS>()) void f1_carry(F1XferArgs a, in
     const bool last_seg = g == a.nseg - 1;
     const size_t rb = f1_xfer_bytes(DV);
     const char *recs = static_cast<const char *>(a.ops) + (size_t(bh) * a.nchunks + c_lo) * rb;
-    // entry state: the incoming state, or the segment's from the scan
+    // entry state: the incoming state (row-major), or the segment's from the
+    // scan (accumulator tiles [row tile][value tile][lane])
     const float *S0 = g == 0 ? a.S_in : a.Sseg + (size_t(bh) * a.nseg + g) * DK * DV;
 
     if (wave >= NCW) {
@@ -632,9 +633,13 @@ __global__ __launch_bounds__(carry_threads<DS>()) void f1_carry(F1XferArgs a, in
 #pragma unroll
     for (int h = 0; h < MT; ++h) {
         const int m = MT * mh + h;
+        if (g > 0) {
+            S[h] = reinterpret_cast<const f32x4 *>(S0)[(m * (DV / 16) + j0 / 16 + ct) * 64 + lane];
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            S[h][r] = S0 ? S0[(size_t(g == 0 ? bh : 0) * DK + 16 * m + g4 + r) * DV + j0 + 16 * ct + col] : 0.f;
+            for (int r = 0; r < 4; ++r)
+                S[h][r] = S0 ? S0[(size_t(bh) * DK + 16 * m + g4 + r) * DV + j0 + 16 * ct + col] : 0.f;
+        }
         put2(STw[0][ct] + col * PK + 16 * m + g4, pk4(S[h]));
     }
     __syncthreads();
@@ -696,6 +701,7 @@ __global__ __launch_bounds__(carry_threads<DS>()) void f1_carry(F1XferArgs a, in
 //   f1_carry: every segment walks its chunks from its entry state.
 // ---------------------------------------------------------------------------
 constexpr int SM_THREADS = 256;
+constexpr int NPF = 3;          // operator buffers in flight per wave (2 steps ahead)
 
 // workgroup barrier after this wave's LDS writes have completed, without
 // the release fence of __syncthreads (which would also wait for the global
@@ -757,12 +763,7 @@ __global__ __launch_bounds__(SM_THREADS) void f1_segmap(F1XferArgs a) {
         put2(&XT[0][16 * n + col][16 * m + g4], make_uint2(0u, 0u));
     }
     float gam = 1.f;
-    MapRec<DV> cur;
-    cur.load(recs, m, lane);
-    lds_barrier();
-    for (int c = 0; c < nc; ++c) {
-        MapRec<DV> nxt;   // the next chunk's record loads during this step
-        nxt.load(recs + size_t(c + 1 < nc ? c + 1 : c) * rb, m, lane);
+    auto step = [&](int c, const MapRec<DV> &cur) {
         const bf16_t *xt = &XT[c & 1][0][0];
         bf16_t *xn = &XT[(c + 1) & 1][0][0];
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -778,42 +779,60 @@ __global__ __launch_bounds__(SM_THREADS) void f1_segmap(F1XferArgs a) {
             put2(xn + (16 * n + col) * PK + 16 * m + g4, pk4(acc));
         }
         gam *= cur.gc;
-        cur = nxt;
         lds_barrier();
+    };
+    // NPF record buffers in turn: chunk c + NPF - 1 loads during step c (a
+    // clamped index re-reads the last record at the end)
+    MapRec<DV> buf[NPF];
+#pragma unroll
+    for (int u = 0; u + 1 < NPF; ++u) buf[u].load(recs + size_t(u < nc ? u : nc - 1) * rb, m, lane);
+    lds_barrier();
+    for (int c = 0; c < nc; c += NPF) {
+#pragma unroll
+        for (int u = 0; u < NPF; ++u) {
+            if (c + u >= nc) break;
+            const int cl = c + u + NPF - 1 < nc ? c + u + NPF - 1 : nc - 1;
+            buf[(u + NPF - 1) % NPF].load(recs + size_t(cl) * rb, m, lane);
+            asm volatile("" ::: "memory");   // issue the loads before the step
+            step(c + u, buf[u]);
+        }
     }
-    float *M = a.Mseg + (size_t(bh) * a.nseg + g) * DK * (DK + DV);
+    // the composed map in the scan's operand order: A~ in bf16 as MFMA A
+    // operands (row 16 m + col, k half h, elements 8 (lane / 16) ..), from
+    // the transpose the last step left in LDS; beta as fp32 accumulator tiles
+    char *M = reinterpret_cast<char *>(a.Mseg) + (size_t(bh) * a.nseg + g) * f1_segmap_bytes(DV);
+    const bf16_t *xt = &XT[nc & 1][0][0];
 #pragma unroll
-    for (int n = 0; n < NCOL; ++n)
+    for (int h = 0; h < 2; ++h) {
+        uint32_t w[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) M[size_t(16 * m + g4 + r) * (DK + DV) + 16 * n + col] = X[n][r];
+        for (int e = 0; e < 4; ++e)
+            w[e] = uint32_t(xt[(32 * h + k8 + 2 * e) * PK + 16 * m + col].bits) |
+                   uint32_t(xt[(32 * h + k8 + 2 * e + 1) * PK + 16 * m + col].bits) << 16;
+        *reinterpret_cast<uint4 *>(M + m * 2048 + h * 1024 + 16 * lane) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+#pragma unroll
+    for (int n = 0; n < DV / 16; ++n)
+        *reinterpret_cast<f32x4 *>(M + kF1SegBetaOff + ((m * (DV / 16) + n) * 64 + lane) * 16) = X[DK / 16 + n];
     if (tid == 0) a.Gseg[size_t(bh) * a.nseg + g] = gam;
 }
 
-// the parts of a segment map one scan wave uses: rows 16 m + col of A~ as
-// MFMA A operands (rounded to bf16), its rows of beta and gamma
+// the parts of a segment map one scan wave uses: rows 16 m + l % 16 of A~
+// as MFMA A operands, its accumulator tiles of beta, and gamma
 template <int DV>
 struct ScanMap {
-    float4 a[4];
+    bf16x8 a0, a1;
     f32x4 b[DV / 16];
     float gam;
-    __device__ __forceinline__ void load(const float *M, const float *G, int m, int col, int g4, int k8) {
-        const float *arow = M + size_t(16 * m + col) * (DK + DV);
-        a[0] = *reinterpret_cast<const float4 *>(arow + k8);
-        a[1] = *reinterpret_cast<const float4 *>(arow + k8 + 4);
-        a[2] = *reinterpret_cast<const float4 *>(arow + 32 + k8);
-        a[3] = *reinterpret_cast<const float4 *>(arow + 32 + k8 + 4);
+    __device__ __forceinline__ void load(const char *M, const float *G, int m, int lane) {
+        a0 = ld8(M + m * 2048 + 16 * lane);
+        a1 = ld8(M + m * 2048 + 1024 + 16 * lane);
 #pragma unroll
         for (int n = 0; n < DV / 16; ++n)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) b[n][r] = M[size_t(16 * m + g4 + r) * (DK + DV) + DK + 16 * n + col];
+            b[n] = *reinterpret_cast<const f32x4 *>(M + kF1SegBetaOff + ((m * (DV / 16) + n) * 64 + lane) * 16);
         gam = *G;
     }
 };
-
-__device__ __forceinline__ bf16x8 to_bf16x8(const float4 &lo, const float4 &hi) {
-    const uint4 u = make_uint4(pk2(lo.x, lo.y), pk2(lo.z, lo.w), pk2(hi.x, hi.y), pk2(hi.z, hi.w));
-    return __builtin_bit_cast(bf16x8, u);
-}
 
 // entry states of the segments of head bh, in order: S_{g+1} = gamma_g S_g +
 // A~_g S_g + beta_g; wave m owns row tile m of S (all value columns)
@@ -825,8 +844,8 @@ __global__ __launch_bounds__(SM_THREADS) void f1_segscan(F1XferArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int m = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, g4 = 4 * (lane >> 4), k8 = 8 * (lane >> 4);
-    const size_t msz = size_t(DK) * (DK + DV);
-    const float *Mh = a.Mseg + size_t(bh) * a.nseg * msz;
+    const size_t msz = f1_segmap_bytes(DV);
+    const char *Mh = reinterpret_cast<const char *>(a.Mseg) + size_t(bh) * a.nseg * msz;
     const float *Gh = a.Gseg + size_t(bh) * a.nseg;
     f32x4 S[NJ];
 #pragma unroll
@@ -837,29 +856,39 @@ __global__ __launch_bounds__(SM_THREADS) void f1_segscan(F1XferArgs a) {
         put2(&ST[0][16 * n + col][16 * m + g4], pk4(S[n]));
     }
     const int ns = a.nseg - 1;                  // maps to apply
-    ScanMap<DV> cur;
-    cur.load(Mh, Gh, m, col, g4, k8);
-    lds_barrier();
-    for (int g = 0; g < ns; ++g) {
-        ScanMap<DV> nxt;   // the next map loads during this step
-        const int gn = g + 1 < ns ? g + 1 : g;
-        nxt.load(Mh + gn * msz, Gh + gn, m, col, g4, k8);
-        const bf16x8 a0 = to_bf16x8(cur.a[0], cur.a[1]), a1 = to_bf16x8(cur.a[2], cur.a[3]);
+    auto step = [&](int g, const ScanMap<DV> &cur) {
         const bf16_t *st = &ST[g & 1][0][0];
         bf16_t *sn = &ST[(g + 1) & 1][0][0];
-        float *Sout = a.Sseg + (size_t(bh) * a.nseg + g + 1) * DK * DV;
+        // entry state of segment g + 1 as accumulator tiles [row tile][value tile][lane]
+        f32x4 *Sout = reinterpret_cast<f32x4 *>(a.Sseg + (size_t(bh) * a.nseg + g + 1) * DK * DV);
 #pragma unroll
         for (int n = 0; n < NJ; ++n) {
             f32x4 acc = S[n] * cur.gam + cur.b[n];
-            acc = mfma(a0, ld8(st + (16 * n + col) * PK + k8), acc);
-            acc = mfma(a1, ld8(st + (16 * n + col) * PK + 32 + k8), acc);
+            acc = mfma(cur.a0, ld8(st + (16 * n + col) * PK + k8), acc);
+            acc = mfma(cur.a1, ld8(st + (16 * n + col) * PK + 32 + k8), acc);
             S[n] = acc;
             put2(sn + (16 * n + col) * PK + 16 * m + g4, pk4(acc));
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Sout[size_t(16 * m + g4 + r) * DV + 16 * n + col] = acc[r];
+            Sout[(m * NJ + n) * 64 + lane] = acc;
         }
-        cur = nxt;
         lds_barrier();
+    };
+    // NPF map buffers in turn: map g + NPF - 1 loads during step g
+    ScanMap<DV> buf[NPF];
+#pragma unroll
+    for (int u = 0; u + 1 < NPF; ++u) {
+        const int gl = u < ns ? u : ns - 1;
+        buf[u].load(Mh + gl * msz, Gh + gl, m, lane);
+    }
+    lds_barrier();
+    for (int g = 0; g < ns; g += NPF) {
+#pragma unroll
+        for (int u = 0; u < NPF; ++u) {
+            if (g + u >= ns) break;
+            const int gl = g + u + NPF - 1 < ns ? g + u + NPF - 1 : ns - 1;
+            buf[(u + NPF - 1) % NPF].load(Mh + gl * msz, Gh + gl, m, lane);
+            asm volatile("" ::: "memory");   // issue the loads before the step
+            step(g + u, buf[u]);
+        }
     }
 }
 

@@ -68,18 +68,33 @@ constexpr size_t f1_xfer_bytes(int dv) { return f1_xfer_scal_off(dv) + 256; }
 // value columns per workgroup of the carry kernel: 32 (two workgroups per
 // head share the operator traffic), never more than d_v
 constexpr int f1_xfer_slice(int dv) { return dv < 32 ? dv : 32; }
+// Composed map of a segment, S -> gamma S + A~ S + beta (gamma apart):
+//   A~   [64 d][64 d'] bf16 in MFMA A-operand lane order, [row tile m 4][k half
+//        h 2][lane l 64] x 16 bytes (row 16 m + l % 16, d' = 32 h + 8 (l / 16) ..);
+//   beta [64 d][d_v j] fp32 in accumulator order, [row tile m 4][value tile
+//        d_v / 16][lane l 64] x 16 bytes (rows 16 m + 4 (l / 16) .. + 3 of
+//        column 16 jt + l % 16).
+constexpr size_t kF1SegBetaOff = 8192;
+constexpr size_t f1_segmap_bytes(int dv) { return kF1SegBetaOff + size_t(dv) * 256; }
+// workgroups of the carry for bh heads walking in slices of ds columns
+// (heads rounded up to 8 when a head has several slices)
+constexpr long long f1_carry_groups(long long bh, int dv, int ds) {
+    return dv / ds == 1 ? bh : (bh + 7) / 8 * 8 * (dv / ds);
+}
 // Chunks per segment of the carry.  The walk over a head's chunks is the
 // sequential part; when few walks run (few heads) over many chunks, it
-// splits into segments whose composed maps are scanned first.  Segments are
-// sized so that the carry's workgroups (one per compute unit, 256 of them
-// on the chip) run in about one pass, and hold at least 16 chunks so that
-// the map and scan stay short.  A walk of fewer than 48 chunks, or one
-// whose heads alone fill the chip, is not split (returns nchunks).
+// splits into segments whose composed maps are scanned first.  A carry
+// workgroup (one per compute unit) moves its operators at about a fixed
+// rate, so the carry's time follows its chunk steps per compute unit, and
+// the segment maps stream every record once more whatever their length.
+// Segments are sized for about two passes of carry workgroups (512), and
+// hold at least 16 chunks.  A walk of fewer than 48 chunks, or one whose
+// heads alone exceed one pass (256 workgroups), is not split (returns
+// nchunks).
 constexpr int f1_xfer_segment_chunks(long long bh, int dv, int nchunks) {
-    const long long nslice = dv / f1_xfer_slice(dv);
-    const long long nbase = nslice == 1 ? bh : (bh + 7) / 8 * 8 * nslice;
-    const long long nseg = nbase > 0 ? 256 / nbase : 0;
-    if (nchunks < 48 || nseg < 2) return nchunks;
+    const long long groups = f1_carry_groups(bh, dv, f1_xfer_slice(dv));
+    if (nchunks < 48 || groups > 256) return nchunks;
+    const long long nseg = 512 / groups;
     const long long g = (nchunks + nseg - 1) / nseg;
     return static_cast<int>(g < 16 ? 16 : g);
 }

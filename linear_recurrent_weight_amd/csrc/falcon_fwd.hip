@@ -208,7 +208,7 @@ int run(const falcon_fwd_args *args, void *stream, Marks *m) {
         fa.seg_chunks = p.seg_chunks;
         fa.nseg = p.nseg;
         if (p.nseg > 1) {
-            fa.Mseg = p.ws_at<float>(p.off_seg_m);
+            fa.Mseg = p.ws_at<void>(p.off_seg_m);
             fa.Gseg = p.ws_at<float>(p.off_seg_g);
             fa.Sseg = p.ws_at<float>(p.off_seg_s);
         }

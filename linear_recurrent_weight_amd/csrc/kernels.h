@@ -111,9 +111,10 @@ struct F1XferArgs {
     // segments of seg_chunks chunks whose maps are composed and scanned
     // (nseg == 1: one walk over all chunks)
     int seg_chunks, nseg;
-    float *Mseg;            // [BH][nseg][d_k][d_k + d_v] composed maps (A~ | beta), fp32
+    void *Mseg;             // [BH][nseg] composed maps (f1_segmap_bytes(d_v) each)
     float *Gseg;            // [BH][nseg] scalar part gamma of the composed maps
-    float *Sseg;            // [BH][nseg][d_k][d_v] entry states of the segments
+    float *Sseg;            // [BH][nseg] entry states of the segments, d_k x d_v fp32
+                            // in accumulator tiles [row tile][value tile][lane][4]
 };
 
 // one token (T = 1) of every variant, continuing from the incoming state

@@ -129,7 +129,7 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
         off = align_up(off + static_cast<size_t>(bh) * p->nchunks * f1_xfer_bytes(a->dv));
         if (p->nseg > 1) {   // composed maps [A~ | beta], their gamma, entry states
             const size_t ns = static_cast<size_t>(bh) * p->nseg;
-            p->off_seg_m = off; off = align_up(off + ns * a->dk * (a->dk + a->dv) * 4);
+            p->off_seg_m = off; off = align_up(off + ns * f1_segmap_bytes(a->dv));
             p->off_seg_g = off; off = align_up(off + ns * 4);
             p->off_seg_s = off; off = align_up(off + ns * a->dk * a->dv * 4);
         }

@@ -222,14 +222,13 @@ def test_f1_bf16_workspace(lib):
 def _f1_segments(bh, dv, nchunks):
     """Chunks per segment of the bf16 Falcon-1 carry: one segment for walks
     under 48 chunks or when the carry's workgroups (32 value columns each,
-    heads rounded up to 8 when a head has several) alone reach 128;
-    otherwise about 256 / workgroups segments of at least 16 chunks."""
+    heads rounded up to 8 when a head has several) exceed 256; otherwise
+    about 512 / workgroups segments of at least 16 chunks."""
     nslice = dv // min(dv, 32)
-    nbase = bh if nslice == 1 else -(-bh // 8) * 8 * nslice
-    nseg = 256 // nbase
-    if nchunks < 48 or nseg < 2:
+    groups = bh if nslice == 1 else -(-bh // 8) * 8 * nslice
+    if nchunks < 48 or groups > 256:
         return nchunks
-    return max(16, -(-nchunks // nseg))
+    return max(16, -(-nchunks // (512 // groups)))
 
 
 @pytest.mark.parametrize("B,H,T,dv", [(2, 12, 16384, 64), (1, 3, 5000, 32), (1, 1, 3072, 128),
@@ -237,7 +236,8 @@ def _f1_segments(bh, dv, nchunks):
 def test_f1_bf16_long_walks_split_into_segments(lib, B, H, T, dv):
     """Long walks over few heads compose each segment's chunk maps and scan
     them before the carry; the workspace adds the composed maps [A~ | beta]
-    (fp32 d_k x (d_k + d_v)), their scalars and the segments' entry states."""
+    (A~ in bf16, beta in fp32), their scalars and the segments' fp32 entry
+    states."""
     a = args(batch=B, heads=H, seqlen=T, dv=dv)
     bh, nch = B * H, -(-T // 64)
     g = _f1_segments(bh, dv, nch)
@@ -246,14 +246,14 @@ def test_f1_bf16_long_walks_split_into_segments(lib, B, H, T, dv):
     per_chunk = 2 * 64 * 64 * 2 + 2 * 64 * dv * 2 + 256
     n = align(bh * nch * per_chunk)
     if nseg > 1:
-        n += align(bh * nseg * 64 * (64 + dv) * 4) + align(bh * nseg * 4) + align(bh * nseg * 64 * dv * 4)
+        n += align(bh * nseg * (64 * 64 * 2 + 64 * dv * 4)) + align(bh * nseg * 4) + align(bh * nseg * 64 * dv * 4)
         assert _names(lib, a) == ["f1_xfer", "f1_segmap", "f1_segscan", "f1_carry"]
     else:
         assert _names(lib, a) == ["f1_xfer", "f1_carry"]
     assert wsize(lib, a) == n
     # the long-sequence workload with few heads is split
     if (B, H, T) == (2, 12, 16384):
-        assert nseg == 5 and g == 52
+        assert nseg == 10 and g == 26
 
 
 def test_library_reads_no_tuning_switches():
