@@ -42,11 +42,30 @@ MUTANTS = {
 }
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_pins_catch_planted_mistake(name, tmp_path):
-    src = (ROOT / "oracle" / "falcon_oracle.py").read_text()
-    old, new = MUTANTS[name]
-    assert old in src, f"mutation site for {name} no longer exists"
+# planted mistakes in the backward oracle, caught by its own pins
+MUTANTS_BWD = {
+    "bwd_dx_state_term_dropped": (
+        'dx[t] += eta[:, None] * (np.einsum("nkv,nv->nk", G, r) - np.einsum("nkv,nv->nk", Sp, w))',
+        'dx[t] += eta[:, None] * np.einsum("nkv,nv->nk", G, r)'),
+    "bwd_clamp_not_gated": ("deta = deta + np.where(unclamped[t], dalpha * lamf[:, t], 0.0)",
+                            "deta = deta + dalpha * lamf[:, t]"),
+    "bwd_decay_adjoint_at_post_state": ('dgamma = np.einsum("nkv,nkv->n", G, Sp)',
+                                        'dgamma = np.einsum("nkv,nkv->n", G, S_post[t])'),
+    "bwd_rank_one_adjoint_dropped": (
+        'G = gamma[:, None, None] * G - eta[:, None, None] * np.einsum("nk,nv->nkv", x_t, w)',
+        "G = gamma[:, None, None] * G"),
+    "bwd_energy_term_dropped": ("dx[t] += 2.0 * dden[:, None] * x_t", "dx[t] += 0.0 * x_t"),
+    "bwd_rms_vjp_sign": ("s * g - (s ** 3 / d) * zg * z", "s * g + (s ** 3 / d) * zg * z"),
+    "bwd_read_at_pre_state": ('dqh[:, t] = np.einsum("nkv,nv->nk", S_post[t], dof[:, t])',
+                              'dqh[:, t] = np.einsum("nkv,nv->nk", S_prev[t], dof[:, t])'),
+    "bwd_key_gradient_shifted": ("dkf[:, t - 1] = phi_vjp(kf[:, t - 1], dx[t], eps_rms, phi_kind)",
+                                 "dkf[:, t - 1] = phi_vjp(kf[:, t - 1], dx[t - 1], eps_rms, phi_kind)"),
+}
+
+
+def _run_pins_on_mutant(tmp_path, target, old, new, pins):
+    src = (ROOT / "oracle" / target).read_text()
+    assert old in src, "mutation site no longer exists"
     shutil.copytree(ROOT / "oracle", tmp_path / "oracle")
     shutil.copytree(ROOT / "tests", tmp_path / "tests",
                     ignore=shutil.ignore_patterns("__pycache__", "test_oracle_mutants.py", "test_gpu*"))
@@ -54,8 +73,20 @@ def test_pins_catch_planted_mistake(name, tmp_path):
     pkg.mkdir()
     shutil.copy(ROOT / "linear_recurrent_weight_amd" / "inputs.py", pkg / "inputs.py")
     (pkg / "__init__.py").write_text("")
-    (tmp_path / "oracle" / "falcon_oracle.py").write_text(src.replace(old, new, 1))
-    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        "tests/test_oracle_pins.py"], cwd=tmp_path, capture_output=True, text=True,
-                       timeout=300)
+    (tmp_path / "oracle" / target).write_text(src.replace(old, new, 1))
+    return subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                           f"tests/{pins}"], cwd=tmp_path, capture_output=True, text=True, timeout=300)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    r = _run_pins_on_mutant(tmp_path, "falcon_oracle.py", old, new, "test_oracle_pins.py")
+    assert r.returncode != 0, f"planted mistake {name} went unnoticed:\n{r.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS_BWD))
+def test_backward_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTANTS_BWD[name]
+    r = _run_pins_on_mutant(tmp_path, "falcon_backward.py", old, new, "test_oracle_backward_pins.py")
     assert r.returncode != 0, f"planted mistake {name} went unnoticed:\n{r.stdout[-2000:]}"
