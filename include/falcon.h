@@ -201,6 +201,83 @@ int falcon_fwd_profile(const falcon_fwd_args *args, void *stream, void *const *e
  * as falcon_fwd otherwise. */
 int falcon_fwd_noalloc(const falcon_fwd_args *args, void *stream);
 
+/*
+ * Backward pass of Falcon-1 (summary §D.2 "Backward Pass", §E.3 "Chunk-
+ * Parallel Backward Pass", §G.3 "Forward and Backward Algorithms"): the
+ * gradients of a scalar loss through one falcon_fwd call of variant
+ * FALCON_V1 (window 1), given the gradients that reach its outputs.
+ *   - o_t = S_t^T phi(q_t) and S_t = gamma_t S_{t-1} + eta_t x_t r_t^T,
+ *     r_t = v_t - S_{t-1}^T x_t, are reversed token by token from the end:
+ *     with G_t = dL/dS_t and w_t = G_t^T x_t, G_{t-1} = gamma_t G_t -
+ *     eta_t x_t w_t^T; dgamma_t = <G_t, S_{t-1}>, deta_t = w_t . r_t,
+ *     dv_t = eta_t w_t, dx_t = eta_t (G_t r_t - S_{t-1} w_t).
+ *   - The decay gradient reaches eta_t and lambda_t only where the clamp
+ *     alpha_t = min(eta_t lambda_t, 1 - eps_gamma) does not bind
+ *     (eta_t lambda_t < 1 - eps_gamma, evaluated in fp32 as in the forward).
+ *   - eta_t = beta_t / d_t, d_t = ||x_t||^2 + lambda_t + eps; where d_t = 0
+ *     the step is 0 and its gradients are 0 (no 0/0).
+ *   - The no-op first step of a fresh sequence is a boundary constant:
+ *     d_beta and d_lambda of that token are 0.
+ *   - x_t = phi(k_{t-1}) and phi(q_t) are differentiated through phi
+ *     (QK-RMSNorm: dz = s g - (s^3 / d_k)(z . g) z, s = (mean(z^2) +
+ *     eps_rms)^(-1/2); 0 where mean(z^2) + eps_rms = 0; identity: dz = g).
+ *     k_{T-1} feeds only the next segment's first pair: d_k of token T-1 is
+ *     phi's product with d_x_next_out (0 when NULL).
+ * The forward is recomputed from the inputs (nothing from falcon_fwd is
+ * reused): every pre-step state is kept in the workspace, which therefore
+ * grows as B*H*(T+1)*d_k*d_v*4 bytes.
+ *
+ *   abi_version  FALCON_ABI_VERSION.  variant: FALCON_V1 only (other
+ *                variants return FALCON_ERR_UNSUPPORTED).
+ *   dtype, phi, batch, heads, seqlen (>= 0), dk, dv (in {16, 32, 64, 128}),
+ *   eps, eps_gamma, eps_rms: as in falcon_fwd_args.
+ *   q, k, v, beta, lambda: the forward's inputs (device, 16-byte aligned).
+ *   state_in     the forward's input state, or NULL (fresh, S_0 = 0);
+ *                n_tail must be 0.
+ *   d_o          [B,H,T,d_v] in dtype: dL/do.
+ *   d_S_out      [B,H,d_k,d_v] fp32: dL/dS_T, or NULL (0).
+ *   d_x_next_out [B,H,d_k] fp32: dL/d(state_out->x_next), or NULL (0).
+ *   d_q, d_k, d_v  [B,H,T,d_k / d_v] in dtype, written.
+ *   d_beta, d_lambda  [B,H,T] fp32, written.
+ *   d_S_in       [B,H,d_k,d_v] fp32: dL/dS_0, written unless NULL.
+ *   d_x_next_in  [B,H,d_k] fp32: dL/d(state_in->x_next), written unless NULL
+ *                (0 for a fresh sequence).
+ *   No output may overlap an input or another output.
+ *   workspace    at least falcon_bwd_workspace_size(args) bytes, 256-byte
+ *                aligned.
+ * Same conventions as falcon_fwd otherwise (errors, streams, no allocation,
+ * reentrancy, bitwise-identical results for identical inputs).
+ */
+typedef struct falcon_bwd_args {
+    int abi_version;
+    int variant;
+    int dtype;
+    int phi;
+    int batch, heads, seqlen, dk, dv;
+    float eps, eps_gamma, eps_rms;
+    const void *q, *k, *v;
+    const float *beta, *lambda;
+    const falcon_state *state_in;
+    const void *d_o;
+    const float *d_S_out, *d_x_next_out;
+    void *d_q, *d_k, *d_v;
+    float *d_beta, *d_lambda;
+    float *d_S_in, *d_x_next_in;
+    void *workspace;
+    size_t workspace_bytes;
+} falcon_bwd_args;
+
+/* Bytes of workspace falcon_bwd needs (pointer fields are not read); 0 for
+ * an invalid or unsupported argument set.  Pure host code. */
+size_t falcon_bwd_workspace_size(const falcon_bwd_args *args);
+
+/* Checks every rule above without touching the GPU.  Pure host code. */
+int falcon_bwd_validate(const falcon_bwd_args *args);
+
+/* Backward pass: validates, then enqueues its kernels on `stream` (NULL =
+ * the default stream).  Returns FALCON_OK or a negative status. */
+int falcon_bwd(const falcon_bwd_args *args, void *stream);
+
 /* Static name of the i-th kernel (0-based) that falcon_fwd launches for these
  * arguments, or NULL when i is out of range or the arguments are invalid.
  * Pure host code, no HIP call. */

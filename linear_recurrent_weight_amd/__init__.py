@@ -1,9 +1,10 @@
-"""MI355X-native Falcon fast-weight forward pass (HIP kernels behind a C ABI).
+"""MI355X-native Falcon fast-weight forward pass and Falcon-1 backward pass
+(HIP kernels behind a C ABI).
 
 Importing the package does not load the native library; ``falcon_fwd`` and
 friends load ``libfalcon.so`` on first use and raise if it is missing.
 """
-__all__ = ["fwd", "FalconState", "load_library"]
+__all__ = ["fwd", "bwd", "FalconState", "load_library"]
 
 
 def __getattr__(name):

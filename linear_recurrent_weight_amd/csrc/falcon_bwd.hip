@@ -1,0 +1,503 @@
+// Falcon-1 backward pass, token-recurrent (summary §D.2 "Backward Pass",
+// §E.3 "Chunk-Parallel Backward Pass", §G.3 "Forward and Backward
+// Algorithms"), in fp32, and the falcon_bwd entry point.
+//
+// The reverse recursion of the state adjoint G_t = dL/dS_t,
+//   G_t += qh_t do_t^T;   w_t = G_t^T x_t;   G_{t-1} = gamma_t G_t - eta_t x_t w_t^T,
+// acts on every value column on its own once eta_t and gamma_t are known
+// (they are shared by the columns), so the kernels keep the forward's
+// layout: one wavefront per (head, group of 4 value columns), lane l holding
+// rows l (and l + 64) of those columns.  The gradients that sum over the
+// columns (dgamma_t = <G_t, S_{t-1}>, deta_t = w_t . r_t, dx_t = eta_t (G_t
+// r_t - S_{t-1} w_t), dqh_t = S_t do_t) leave each wavefront as per-group
+// partial sums and are added up per token afterwards, in a fixed order.
+//   feature     (the forward's feature pass) x_t, qh_t, eta_t, alpha_t;
+//   bwd_states  the forward recurrence again, keeping every pre-step state;
+//   bwd_sweep   the reverse sweep: dv_t, the partial sums, and dS_0;
+//   bwd_reduce  per token: the sums over groups, the decay and step chain
+//               (clamp-gated, zero steps masked, the fresh first step a
+//               boundary constant), phi's vector-Jacobian products for q_t
+//               and k_{t-1}, and the carried feature's gradient.
+#include <cstdio>
+
+#include "common.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace falcon {
+namespace {
+
+constexpr int kCpw = 4;   // value columns per wavefront
+constexpr int kTb = 4;    // tokens whose inputs are loaded together
+
+// rows of the state S_t of (head bh, column group g), one float4 (the 4
+// columns) per row
+__device__ __forceinline__ float4 *state_at(const BwdArgs &a, int bh, int t, int g) {
+    const int groups = a.dv / kCpw;
+    return reinterpret_cast<float4 *>(a.states) + ((size_t(bh) * (a.T + 1) + t) * groups + g) * a.dk;
+}
+
+template <int RPL>
+__device__ __forceinline__ float4 ld_row(const float4 *p, int lane, int r, int dk) {
+    const int i = lane + 64 * r;
+    return i < dk ? p[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+__device__ __forceinline__ float col(const float4 &v, int c) {
+    return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
+}
+
+// ---------------------------------------------------------------------------
+// bwd_states: S_0 .. S_T of 4 value columns (the forward recurrence)
+// ---------------------------------------------------------------------------
+template <class E, int RPL, int RW>
+__global__ __launch_bounds__(256) void bwd_states(BwdArgs a) {
+    auto rsum = [](float v) { return group_sum<RW>(v); };
+    const int lane = threadIdx.x & 63;
+    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int groups = a.dv / kCpw;
+    if (gw >= a.BH * groups) return;
+    const int bh = gw / groups, g = gw % groups, c0 = g * kCpw;
+    const int dk = a.dk, dv = a.dv, T = a.T;
+    const E *v = static_cast<const E *>(a.v);
+
+    float S[RPL][kCpw];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+        const int i = lane + 64 * r;
+#pragma unroll
+        for (int c = 0; c < kCpw; ++c)
+            S[r][c] = (a.S_in && i < dk) ? a.S_in[(size_t(bh) * dk + i) * dv + c0 + c] : 0.f;
+    }
+    auto put = [&](int t) {
+        float4 *p = state_at(a, bh, t, g);
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+            const int i = lane + 64 * r;
+            if (i < dk) p[i] = make_float4(S[r][0], S[r][1], S[r][2], S[r][3]);
+        }
+    };
+    for (int t0 = 0; t0 < T; t0 += kTb) {
+        float xb[kTb][RPL], yb[kTb][kCpw], eb[kTb], gb[kTb];
+#pragma unroll
+        for (int u = 0; u < kTb; ++u) {
+            const size_t row = size_t(bh) * T + (t0 + u < T ? t0 + u : T - 1);
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) {
+                const int i = lane + 64 * r;
+                xb[u][r] = i < dk ? a.xn[row * dk + i] : 0.f;
+            }
+#pragma unroll
+            for (int c = 0; c < kCpw; ++c) yb[u][c] = ld(v, row * dv + c0 + c);
+            eb[u] = a.eta[row];
+            gb[u] = 1.f - a.alpha[row];
+        }
+#pragma unroll
+        for (int u = 0; u < kTb; ++u) {
+            if (t0 + u >= T) break;
+            put(t0 + u);   // S_{t-1}, the state this step starts from
+            float pred[kCpw];
+#pragma unroll
+            for (int c = 0; c < kCpw; ++c) {
+                float s = 0.f;
+#pragma unroll
+                for (int r = 0; r < RPL; ++r) s += S[r][c] * xb[u][r];
+                pred[c] = rsum(s);
+            }
+#pragma unroll
+            for (int c = 0; c < kCpw; ++c) {
+                const float res = yb[u][c] - pred[c];
+#pragma unroll
+                for (int r = 0; r < RPL; ++r) S[r][c] = gb[u] * S[r][c] + eb[u] * xb[u][r] * res;
+            }
+        }
+    }
+    put(T);
+}
+
+// ---------------------------------------------------------------------------
+// bwd_sweep: the reverse sweep over the tokens of 4 value columns
+// ---------------------------------------------------------------------------
+template <class E, int RPL, int RW>
+__global__ __launch_bounds__(256) void bwd_sweep(BwdArgs a) {
+    auto rsum = [](float v) { return group_sum<RW>(v); };
+    const int lane = threadIdx.x & 63;
+    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int groups = a.dv / kCpw;
+    if (gw >= a.BH * groups) return;
+    const int bh = gw / groups, g = gw % groups, c0 = g * kCpw;
+    const int dk = a.dk, dv = a.dv, T = a.T;
+    const int PF = bwd_part_floats(dk);
+    const E *v = static_cast<const E *>(a.v);
+    const E *dO = static_cast<const E *>(a.d_o);
+    E *dV = static_cast<E *>(a.d_v);
+
+    float G[RPL][kCpw];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+        const int i = lane + 64 * r;
+#pragma unroll
+        for (int c = 0; c < kCpw; ++c)
+            G[r][c] = (a.d_S_out && i < dk) ? a.d_S_out[(size_t(bh) * dk + i) * dv + c0 + c] : 0.f;
+    }
+
+    for (int tb = T - 1; tb >= 0; tb -= kTb) {
+        // inputs of tokens tb, tb - 1, .. (rows clamped at 0)
+        float xb[kTb][RPL], qb[kTb][RPL], yb[kTb][kCpw], ob[kTb][kCpw], eb[kTb], gb[kTb];
+        float4 sp[kTb][RPL], sn[kTb][RPL];
+#pragma unroll
+        for (int u = 0; u < kTb; ++u) {
+            const int t = tb - u >= 0 ? tb - u : 0;
+            const size_t row = size_t(bh) * T + t;
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) {
+                const int i = lane + 64 * r;
+                xb[u][r] = i < dk ? a.xn[row * dk + i] : 0.f;
+                qb[u][r] = i < dk ? a.qn[row * dk + i] : 0.f;
+                sp[u][r] = ld_row<RPL>(state_at(a, bh, t, g), lane, r, dk);
+                sn[u][r] = ld_row<RPL>(state_at(a, bh, t + 1, g), lane, r, dk);
+            }
+#pragma unroll
+            for (int c = 0; c < kCpw; ++c) {
+                yb[u][c] = ld(v, row * dv + c0 + c);
+                ob[u][c] = ld(dO, row * dv + c0 + c);
+            }
+            eb[u] = a.eta[row];
+            gb[u] = 1.f - a.alpha[row];
+        }
+#pragma unroll
+        for (int u = 0; u < kTb; ++u) {
+            const int t = tb - u;
+            if (t < 0) break;
+            const size_t row = size_t(bh) * T + t;
+            const float eta = eb[u], gam = gb[u];
+            // read after write: G_t += qh_t do_t^T, dqh_t = S_t do_t
+            float dq[RPL];
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) {
+                dq[r] = 0.f;
+#pragma unroll
+                for (int c = 0; c < kCpw; ++c) {
+                    G[r][c] += qb[u][r] * ob[u][c];
+                    dq[r] += col(sn[u][r], c) * ob[u][c];
+                }
+            }
+            // w = G^T x, r = y - S_{t-1}^T x, dgamma = <G, S_{t-1}>
+            float w[kCpw], res[kCpw], gs = 0.f;
+#pragma unroll
+            for (int c = 0; c < kCpw; ++c) {
+                float sw = 0.f, sx = 0.f;
+#pragma unroll
+                for (int r = 0; r < RPL; ++r) {
+                    sw += G[r][c] * xb[u][r];
+                    sx += col(sp[u][r], c) * xb[u][r];
+                    gs += G[r][c] * col(sp[u][r], c);
+                }
+                w[c] = rsum(sw);
+                res[c] = yb[u][c] - rsum(sx);
+            }
+            const float dgam = rsum(gs);
+            float deta = 0.f;
+#pragma unroll
+            for (int c = 0; c < kCpw; ++c) deta += w[c] * res[c];
+            // dv_t = eta w (this group's columns, lanes 0..3)
+            if (lane < kCpw) {
+                const float wl = lane == 0 ? w[0] : lane == 1 ? w[1] : lane == 2 ? w[2] : w[3];
+                st(dV, row * dv + c0 + lane, eta * wl);
+            }
+            // dx_t = eta (G r - S_{t-1} w), then G_{t-1} = gamma G - eta x w^T
+            float dx[RPL];
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) {
+                float s = 0.f;
+#pragma unroll
+                for (int c = 0; c < kCpw; ++c) s += G[r][c] * res[c] - col(sp[u][r], c) * w[c];
+                dx[r] = eta * s;
+#pragma unroll
+                for (int c = 0; c < kCpw; ++c) G[r][c] = gam * G[r][c] - eta * xb[u][r] * w[c];
+            }
+            float *P = a.part + (row * groups + g) * PF;
+            if (lane == 0) {
+                P[0] = dgam;
+                P[1] = deta;
+            }
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) {
+                const int i = lane + 64 * r;
+                if (i < dk) {
+                    P[4 + i] = dx[r];
+                    P[4 + dk + i] = dq[r];
+                }
+            }
+        }
+    }
+    if (a.d_S_in) {
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+            const int i = lane + 64 * r;
+            if (i < dk)
+#pragma unroll
+                for (int c = 0; c < kCpw; ++c) a.d_S_in[(size_t(bh) * dk + i) * dv + c0 + c] = G[r][c];
+        }
+    }
+    // an empty segment passes the carried feature's gradient through
+    if (T == 0 && g == 0 && a.d_x_next_in) {
+        for (int i = lane; i < dk; i += 64)
+            a.d_x_next_in[size_t(bh) * dk + i] = (!a.fresh && a.d_x_next_out) ? a.d_x_next_out[size_t(bh) * dk + i] : 0.f;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_reduce: one wavefront per (head, token)
+// ---------------------------------------------------------------------------
+// phi's vector-Jacobian product: dz = s g - (s^3 / d)(z . g) z (RMSNorm), g
+// (identity); z and g hold rows lane + 64 r, zero past d
+template <int RPL, int RW>
+__device__ __forceinline__ void phi_vjp(const float (&z)[RPL], const float (&gv)[RPL], float (&out)[RPL], int d,
+                                        float eps_rms, int phi_kind) {
+    if (phi_kind == FALCON_PHI_IDENTITY) {
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) out[r] = gv[r];
+        return;
+    }
+    float ss = 0.f, zg = 0.f;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+        ss += z[r] * z[r];
+        zg += z[r] * gv[r];
+    }
+    ss = group_sum<RW>(ss);
+    zg = group_sum<RW>(zg);
+    const float ms = ss / float(d) + eps_rms;
+    const float s = ms > 0.f ? 1.f / sqrtf(ms) : 0.f;
+    const float k3 = s * s * s / float(d) * zg;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) out[r] = s * gv[r] - k3 * z[r];
+}
+
+template <class E, int RPL, int RW>
+__global__ __launch_bounds__(256) void bwd_reduce(BwdArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int id = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int T = a.T, dk = a.dk;
+    if (id >= a.BH * T) return;
+    const int bh = id / T, t = id % T;
+    const int groups = a.dv / kCpw, PF = bwd_part_floats(dk);
+    const size_t row = size_t(bh) * T + t;
+    const float *P = a.part + row * groups * PF;
+    const E *q = static_cast<const E *>(a.q);
+    const E *k = static_cast<const E *>(a.k);
+
+    // sums over the column groups, in group order
+    float dx[RPL], dqh[RPL], x[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+        const int i = lane + 64 * r;
+        float sx = 0.f, sq = 0.f;
+        if (i < dk)
+            for (int gi = 0; gi < groups; ++gi) {
+                sx += P[gi * PF + 4 + i];
+                sq += P[gi * PF + 4 + dk + i];
+            }
+        dx[r] = sx;
+        dqh[r] = sq;
+        x[r] = i < dk ? a.xn[row * dk + i] : 0.f;
+    }
+    float dgam = 0.f, deta = 0.f;
+    for (int gi = 0; gi < groups; ++gi) {
+        dgam += P[gi * PF + 0];
+        deta += P[gi * PF + 1];
+    }
+
+    // gamma = 1 - alpha, alpha = min(eta lambda, 1 - eps_gamma);
+    // eta = beta / den, den = ||x||^2 + lambda + eps
+    const bool noop = a.fresh && t == 0;
+    float xx = 0.f;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) xx += x[r] * x[r];
+    xx = group_sum<RW>(xx);
+    const float lam = a.lambda[row], eta = a.eta[row], alpha = a.alpha[row];
+    const float den = xx + lam + a.eps;
+    float dbeta = 0.f, dlam = 0.f;
+    if (!noop) {
+        const float dalpha = -dgam;
+        if (alpha < 1.f - a.eps_gamma) {   // the clamp does not bind
+            deta += dalpha * lam;
+            dlam = dalpha * eta;
+        }
+        if (den != 0.f) {
+            dbeta = deta / den;
+            const float dden = -deta * eta / den;
+            dlam += dden;
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) dx[r] += 2.f * dden * x[r];
+        }
+    }
+    if (lane == 0) {
+        a.d_beta[row] = dbeta;
+        a.d_lambda[row] = dlam;
+    }
+
+    // dq_t through phi
+    float z[RPL], out[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+        const int i = lane + 64 * r;
+        z[r] = i < dk ? ld(q, row * dk + i) : 0.f;
+    }
+    phi_vjp<RPL, RW>(z, dqh, out, dk, a.eps_rms, a.phi);
+    E *dQ = static_cast<E *>(a.d_q);
+    E *dK = static_cast<E *>(a.d_k);
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+        const int i = lane + 64 * r;
+        if (i < dk) st(dQ, row * dk + i, out[r]);
+    }
+    // x_t = phi(k_{t-1}): dk_{t-1}; for t = 0 the carried feature's gradient
+    if (t > 0) {
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+            const int i = lane + 64 * r;
+            z[r] = i < dk ? ld(k, (row - 1) * dk + i) : 0.f;
+        }
+        phi_vjp<RPL, RW>(z, dx, out, dk, a.eps_rms, a.phi);
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+            const int i = lane + 64 * r;
+            if (i < dk) st(dK, (row - 1) * dk + i, out[r]);
+        }
+    } else if (a.d_x_next_in) {
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+            const int i = lane + 64 * r;
+            if (i < dk) a.d_x_next_in[size_t(bh) * dk + i] = a.fresh ? 0.f : dx[r];
+        }
+    }
+    // k_{T-1} feeds only the next segment's first pair
+    if (t == T - 1) {
+        float gx[RPL];
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+            const int i = lane + 64 * r;
+            z[r] = i < dk ? ld(k, row * dk + i) : 0.f;
+            gx[r] = (a.d_x_next_out && i < dk) ? a.d_x_next_out[size_t(bh) * dk + i] : 0.f;
+        }
+        phi_vjp<RPL, RW>(z, gx, out, dk, a.eps_rms, a.phi);
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+            const int i = lane + 64 * r;
+            if (i < dk) st(dK, row * dk + i, out[r]);
+        }
+    }
+}
+
+template <class E, int RPL, int RW>
+void launch_shape(const BwdArgs &a, hipStream_t s, Marks *m) {
+    const int waves = a.BH * (a.dv / kCpw);
+    const int blocks = (waves + 3) / 4;
+    bwd_states<E, RPL, RW><<<blocks, 256, 0, s>>>(a);
+    m->mark(s);
+    bwd_sweep<E, RPL, RW><<<blocks, 256, 0, s>>>(a);
+    m->mark(s);
+    if (a.T > 0) {
+        const long long rw = static_cast<long long>(a.BH) * a.T;
+        bwd_reduce<E, RPL, RW><<<static_cast<unsigned>((rw + 3) / 4), 256, 0, s>>>(a);
+        m->mark(s);
+    }
+}
+
+template <class E>
+void launch_io(const BwdArgs &a, hipStream_t s, Marks *m) {
+    switch (a.dk) {
+        case 16: launch_shape<E, 1, 16>(a, s, m); break;
+        case 32: launch_shape<E, 1, 32>(a, s, m); break;
+        case 64: launch_shape<E, 1, 64>(a, s, m); break;
+        default: launch_shape<E, 2, 64>(a, s, m); break;
+    }
+}
+
+}  // namespace
+
+void launch_bwd(const BwdArgs &a, bool io_bf16, hipStream_t s, Marks *m) {
+    if (io_bf16) launch_io<bf16_t>(a, s, m);
+    else launch_io<float>(a, s, m);
+}
+
+}  // namespace falcon
+
+extern "C" int falcon_bwd(const falcon_bwd_args *args, void *stream) {
+    using namespace falcon;
+    BwdPlan p;
+    const int rc = build_bwd_plan(args, &p, true);
+    if (rc != FALCON_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Marks m;
+    m.sync_check = sync_check_enabled();
+    m.mark(s);
+    const bool bf16 = p.dtype == FALCON_BF16;
+    if (p.T > 0) {
+        FeatureArgs fa{};
+        fa.variant = FALCON_V1;
+        fa.phi = p.phi;
+        fa.BH = p.BH;
+        fa.T = p.T;
+        fa.Tpad = p.T;
+        fa.dk = p.dk;
+        fa.dv = p.dv;
+        fa.window = 1;
+        fa.eps = p.eps;
+        fa.eps_gamma = p.eps_gamma;
+        fa.eps_rms = p.eps_rms;
+        fa.fresh = p.fresh ? 1 : 0;
+        fa.q = args->q;
+        fa.k = args->k;
+        fa.v = args->v;
+        fa.beta = args->beta;
+        fa.lambda = args->lambda;
+        fa.xnext_in = p.xnext_in;
+        fa.xn = p.ws_at<float>(p.off_xn);
+        fa.qn = p.ws_at<float>(p.off_qn);
+        fa.eta = p.ws_at<float>(p.off_eta);
+        fa.alpha = p.ws_at<float>(p.off_alpha);
+        launch_features(fa, bf16, false, s, &m);
+    }
+    BwdArgs ba{};
+    ba.phi = p.phi;
+    ba.BH = p.BH;
+    ba.T = p.T;
+    ba.dk = p.dk;
+    ba.dv = p.dv;
+    ba.fresh = p.fresh ? 1 : 0;
+    ba.eps = p.eps;
+    ba.eps_gamma = p.eps_gamma;
+    ba.eps_rms = p.eps_rms;
+    ba.q = args->q;
+    ba.k = args->k;
+    ba.v = args->v;
+    ba.d_o = args->d_o;
+    ba.beta = args->beta;
+    ba.lambda = args->lambda;
+    ba.S_in = p.S_in;
+    ba.d_S_out = args->d_S_out;
+    ba.d_x_next_out = args->d_x_next_out;
+    ba.xn = p.ws_at<float>(p.off_xn);
+    ba.qn = p.ws_at<float>(p.off_qn);
+    ba.eta = p.ws_at<float>(p.off_eta);
+    ba.alpha = p.ws_at<float>(p.off_alpha);
+    ba.states = p.ws_at<float>(p.off_states);
+    ba.part = p.ws_at<float>(p.off_part);
+    ba.d_q = args->d_q;
+    ba.d_k = args->d_k;
+    ba.d_v = args->d_v;
+    ba.d_beta = args->d_beta;
+    ba.d_lambda = args->d_lambda;
+    ba.d_S_in = args->d_S_in;
+    ba.d_x_next_in = args->d_x_next_in;
+    launch_bwd(ba, bf16, s, &m);
+    if (m.failed_at >= 0) {
+        std::fprintf(stderr, "falcon_bwd: FALCON_SYNC_CHECK: kernel %d of the call failed\n", m.failed_at);
+        return FALCON_ERR_HIP;
+    }
+    if (hipGetLastError() != hipSuccess) return FALCON_ERR_HIP;
+    return FALCON_OK;
+}

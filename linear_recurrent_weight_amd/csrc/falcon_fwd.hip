@@ -27,7 +27,7 @@ int cu_count() {
 
 }  // namespace falcon
 
-namespace {
+namespace falcon {
 
 // FALCON_SYNC_CHECK=1 (debug only): synchronise and check the HIP error
 // state after every kernel launch; read once per process
@@ -38,6 +38,10 @@ bool sync_check_enabled() {
     }();
     return on;
 }
+
+}  // namespace falcon
+
+namespace {
 
 const char *const kNamesEmpty[] = {"passthrough"};
 const char *const kNamesRecurrent[] = {"feature", "recurrent"};

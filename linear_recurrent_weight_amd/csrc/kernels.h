@@ -71,6 +71,24 @@ struct Marks {
 // compute units of the current device (queried once per device, thread-safe)
 int cu_count();
 
+// the FALCON_SYNC_CHECK debug switch (read once per process)
+bool sync_check_enabled();
+
+// Falcon-1 backward (token-recurrent): fp32 features and step scalars from
+// the feature pass, the states S_0 .. S_T [BH][T+1][d_v/4][d_k][4], and the
+// partial sums of the reverse sweep [BH][T][d_v/4][bwd_part_floats(d_k)]
+struct BwdArgs {
+    int phi, BH, T, dk, dv, fresh;
+    float eps, eps_gamma, eps_rms;
+    const void *q, *k, *v, *d_o;          // io dtype
+    const float *beta, *lambda;
+    const float *S_in, *d_S_out, *d_x_next_out;
+    const float *xn, *qn, *eta, *alpha;   // [BH, T, d_k], [BH, T]
+    float *states, *part;
+    void *d_q, *d_k, *d_v;                // io dtype
+    float *d_beta, *d_lambda, *d_S_in, *d_x_next_in;
+};
+
 struct ChunkAArgs {
     int variant, phi, BH, T, Tpad, nchunks, dk, dv, window, fresh, n_tail_in, n_tail_out;
     int seg_chunks, nseg;    // chunks per segment, segments per head
@@ -156,5 +174,7 @@ void launch_chunk_f3(const ChunkF3Args &a, bool bf16, hipStream_t s, Marks *m);
 // bf16 Falcon-1, d_k = 64: transfer operators, then the carry over slices of
 // `slice` value columns
 void launch_chunk_f1_xfer(const F1XferArgs &a, int slice, hipStream_t s, Marks *m);
+// Falcon-1 backward after the feature pass: states, reverse sweep, reduction
+void launch_bwd(const BwdArgs &a, bool io_bf16, hipStream_t s, Marks *m);
 
 }  // namespace falcon

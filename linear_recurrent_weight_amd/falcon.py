@@ -1,7 +1,8 @@
 """ctypes binding of libfalcon.so.
 
 Argument marshalling only: every step of the forward pass runs in the HIP
-kernels behind ``falcon_fwd``.  PyTorch provides device memory and the
+kernels behind ``falcon_fwd``, every step of the Falcon-1 backward pass in
+those behind ``falcon_bwd``.  PyTorch provides device memory and the
 current stream.  The binding raises if the library is missing; there is no
 fallback.
 """
@@ -45,9 +46,25 @@ class FalconFwdArgsC(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
+class FalconBwdArgsC(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int), ("variant", ctypes.c_int), ("dtype", ctypes.c_int),
+                ("phi", ctypes.c_int),
+                ("batch", ctypes.c_int), ("heads", ctypes.c_int), ("seqlen", ctypes.c_int),
+                ("dk", ctypes.c_int), ("dv", ctypes.c_int),
+                ("eps", ctypes.c_float), ("eps_gamma", ctypes.c_float), ("eps_rms", ctypes.c_float),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("beta", ctypes.c_void_p), ("lambda_", ctypes.c_void_p),
+                ("state_in", ctypes.POINTER(FalconStateC)),
+                ("d_o", ctypes.c_void_p), ("d_S_out", ctypes.c_void_p), ("d_x_next_out", ctypes.c_void_p),
+                ("d_q", ctypes.c_void_p), ("d_k", ctypes.c_void_p), ("d_v", ctypes.c_void_p),
+                ("d_beta", ctypes.c_void_p), ("d_lambda", ctypes.c_void_p),
+                ("d_S_in", ctypes.c_void_p), ("d_x_next_in", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
 EXPORTS = ("falcon_fwd", "falcon_fwd_validate", "falcon_fwd_workspace_size",
            "falcon_fwd_profile", "falcon_fwd_noalloc", "falcon_kernel_name", "falcon_status_str",
-           "falcon_abi_version")
+           "falcon_abi_version", "falcon_bwd", "falcon_bwd_validate", "falcon_bwd_workspace_size")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
@@ -77,6 +94,12 @@ def load_library(path: Optional[os.PathLike] = None) -> ctypes.CDLL:
     lib.falcon_fwd_noalloc.restype = ctypes.c_int
     lib.falcon_kernel_name.argtypes = [ctypes.POINTER(FalconFwdArgsC), ctypes.c_int]
     lib.falcon_kernel_name.restype = ctypes.c_char_p
+    lib.falcon_bwd.argtypes = [ctypes.POINTER(FalconBwdArgsC), ctypes.c_void_p]
+    lib.falcon_bwd.restype = ctypes.c_int
+    lib.falcon_bwd_validate.argtypes = [ctypes.POINTER(FalconBwdArgsC)]
+    lib.falcon_bwd_validate.restype = ctypes.c_int
+    lib.falcon_bwd_workspace_size.argtypes = [ctypes.POINTER(FalconBwdArgsC)]
+    lib.falcon_bwd_workspace_size.restype = ctypes.c_size_t
     lib.falcon_abi_version.argtypes = []
     lib.falcon_abi_version.restype = ctypes.c_int
     if lib.falcon_abi_version() != ABI_VERSION:
@@ -89,7 +112,7 @@ def load_library(path: Optional[os.PathLike] = None) -> ctypes.CDLL:
 class FalconError(RuntimeError):
     def __init__(self, status: int, lib=None):
         lib = lib or load_library()
-        super().__init__(f"falcon_fwd failed: {lib.falcon_status_str(status).decode()} ({status})")
+        super().__init__(f"falcon call failed: {lib.falcon_status_str(status).decode()} ({status})")
         self.status = status
 
 
@@ -261,3 +284,84 @@ def workspace_size(**kw) -> int:
 def validate(**kw) -> int:
     lib = load_library()
     return int(lib.falcon_fwd_validate(ctypes.byref(make_args(**kw))))
+
+
+def make_bwd_args(*, dtype, batch, heads, seqlen, dk, dv, variant="F1", eps=1e-6, eps_gamma=1e-3,
+                  eps_rms=1e-6, phi="rmsnorm", q=None, k=None, v=None, beta=None, lam=None,
+                  state_in=None, d_o=None, d_S_out=None, d_x_next_out=None, d_q=None, d_k=None,
+                  d_v=None, d_beta=None, d_lam=None, d_S_in=None, d_x_next_in=None, workspace=None,
+                  workspace_bytes=0) -> FalconBwdArgsC:
+    """Fill the backward's C argument struct (tensors or raw addresses)."""
+    def addr(t):
+        if t is None:
+            return None
+        return t if isinstance(t, int) else t.data_ptr()
+    a = FalconBwdArgsC()
+    a.abi_version = ABI_VERSION
+    a.variant = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    a.dtype = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    a.phi = PHIS[phi] if isinstance(phi, str) else int(phi)
+    a.batch, a.heads, a.seqlen, a.dk, a.dv = batch, heads, seqlen, dk, dv
+    a.eps, a.eps_gamma, a.eps_rms = eps, eps_gamma, eps_rms
+    a.q, a.k, a.v, a.beta, a.lambda_ = map(addr, (q, k, v, beta, lam))
+    a.state_in = ctypes.pointer(state_in) if state_in is not None else None
+    a.d_o, a.d_S_out, a.d_x_next_out = map(addr, (d_o, d_S_out, d_x_next_out))
+    a.d_q, a.d_k, a.d_v, a.d_beta, a.d_lambda = map(addr, (d_q, d_k, d_v, d_beta, d_lam))
+    a.d_S_in, a.d_x_next_in = addr(d_S_in), addr(d_x_next_in)
+    a.workspace = addr(workspace)
+    a.workspace_bytes = workspace_bytes
+    return a
+
+
+def bwd(q, k, v, beta, lam, d_o, *, d_S_out=None, d_x_next_out=None, eps=1e-6, eps_gamma=1e-3,
+        eps_rms=1e-6, phi="rmsnorm", state: Optional[FalconState] = None, workspace=None, stream=None):
+    """Falcon-1 backward pass on the GPU: the gradients of a loss through
+    ``fwd(..., variant="F1")`` on the same inputs and state, given d_o
+    [B,H,T,dv] (the inputs' dtype) and optionally d_S_out [B,H,dk,dv] and
+    d_x_next_out [B,H,dk] (fp32).  Returns a dict with dq, dk, dv (inputs'
+    dtype), dbeta, dlam [B,H,T], dS_in [B,H,dk,dv] and dx_next_in [B,H,dk]
+    (fp32).  Raises ValueError on a tensor that does not match."""
+    import torch
+    lib = load_library()
+    if not (isinstance(q, torch.Tensor) and q.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    if state is not None and int(state.n_tail) != 0:
+        raise ValueError("the Falcon-1 backward takes no tail pairs")
+    B, H, T, dk, dv, dt, dev = check_fwd_tensors(q, k, v, beta, lam, variant="F1", window=1,
+                                                  state=state, workspace=workspace)
+    f32 = torch.float32
+    _check_tensor("d_o", d_o, (B, H, T, dv), dt, dev)
+    if d_S_out is not None:
+        _check_tensor("d_S_out", d_S_out, (B, H, dk, dv), f32, dev)
+    if d_x_next_out is not None:
+        _check_tensor("d_x_next_out", d_x_next_out, (B, H, dk), f32, dev)
+    dtype = "bf16" if dt == torch.bfloat16 else "f32"
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    elif not isinstance(stream, torch.cuda.Stream):
+        raise ValueError("stream must be a torch.cuda.Stream")
+    with torch.cuda.stream(stream):
+        g = dict(dq=torch.empty(B, H, T, dk, dtype=dt, device=dev),
+                 dk=torch.empty(B, H, T, dk, dtype=dt, device=dev),
+                 dv=torch.empty(B, H, T, dv, dtype=dt, device=dev),
+                 dbeta=torch.empty(B, H, T, dtype=f32, device=dev),
+                 dlam=torch.empty(B, H, T, dtype=f32, device=dev),
+                 dS_in=torch.empty(B, H, dk, dv, dtype=f32, device=dev),
+                 dx_next_in=torch.empty(B, H, dk, dtype=f32, device=dev))
+        st_in = state.to_c() if state is not None else None
+        args = make_bwd_args(dtype=dtype, batch=B, heads=H, seqlen=T, dk=dk, dv=dv, eps=eps,
+                             eps_gamma=eps_gamma, eps_rms=eps_rms, phi=phi, q=q, k=k, v=v, beta=beta,
+                             lam=lam, state_in=st_in, d_o=d_o, d_S_out=d_S_out,
+                             d_x_next_out=d_x_next_out, d_q=g["dq"], d_k=g["dk"], d_v=g["dv"],
+                             d_beta=g["dbeta"], d_lam=g["dlam"], d_S_in=g["dS_in"],
+                             d_x_next_in=g["dx_next_in"])
+        nbytes = lib.falcon_bwd_workspace_size(ctypes.byref(args))
+        if nbytes:
+            if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+                workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            args.workspace = workspace.data_ptr()
+            args.workspace_bytes = workspace.numel() * workspace.element_size()
+        rc = lib.falcon_bwd(ctypes.byref(args), ctypes.c_void_p(stream.cuda_stream))
+    if rc != OK:
+        raise FalconError(rc, lib)
+    return g

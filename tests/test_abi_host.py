@@ -377,3 +377,59 @@ def test_every_kernel_name_maps_to_its_source(lib):
     for nm in seen:
         assert nm in KERNEL_SOURCES, nm
         assert nm in (CSRC / KERNEL_SOURCES[nm]).read_text(), nm
+
+
+# -- falcon_bwd (Falcon-1 backward) ---------------------------------------------
+
+def bargs(**kw):
+    base = dict(dtype="bf16", batch=2, heads=3, seqlen=100, dk=64, dv=64, q=FAKE, k=2 * FAKE,
+                v=3 * FAKE, beta=4 * FAKE, lam=5 * FAKE, d_o=6 * FAKE, d_q=7 * FAKE, d_k=8 * FAKE,
+                d_v=9 * FAKE, d_beta=10 * FAKE, d_lam=11 * FAKE)
+    base.update(kw)
+    return fb.make_bwd_args(**base)
+
+
+def bwd_wsize(lib, a):
+    return lib.falcon_bwd_workspace_size(ctypes.byref(a))
+
+
+def bwd_validate(lib, a):
+    return lib.falcon_bwd_validate(ctypes.byref(a))
+
+
+def test_bwd_workspace_layout(lib):
+    """fp32 features and step scalars, the states S_0 .. S_T of every head,
+    and the sweep's partial sums (4 + 2 d_k floats per token and group of 4
+    value columns), each 256-byte aligned."""
+    align = lambda n: -(-n // 256) * 256
+    for B, H, T, dk, dv in [(2, 3, 100, 64, 64), (1, 1, 7, 16, 128), (3, 2, 0, 128, 16)]:
+        bh = B * H
+        want = (2 * align(bh * T * dk * 4) + 2 * align(bh * T * 4) + align(bh * (T + 1) * dk * dv * 4)
+                + align(bh * T * (dv // 4) * (4 + 2 * dk) * 4))
+        assert bwd_wsize(lib, bargs(batch=B, heads=H, seqlen=T, dk=dk, dv=dv)) == want
+
+
+def test_bwd_rules(lib):
+    a = bargs()
+    n = bwd_wsize(lib, a)
+    ok = bargs(workspace=1 << 40, workspace_bytes=n)
+    assert bwd_validate(lib, ok) == fb.OK
+    assert bwd_validate(lib, bargs()) == fb.ERR_WORKSPACE
+    for var in ("F2", "F3", "F1A", "F2A", "F3A"):
+        assert bwd_validate(lib, bargs(variant=var, workspace=1 << 40, workspace_bytes=n)) == fb.ERR_UNSUPPORTED
+    assert bwd_validate(lib, bargs(variant=14)) == fb.ERR_INVALID_ARG
+    assert bwd_validate(lib, bargs(dk=48)) == fb.ERR_UNSUPPORTED
+    assert bwd_validate(lib, bargs(eps_gamma=1.0)) == fb.ERR_INVALID_ARG
+    assert bwd_validate(lib, bargs(d_o=None, workspace=1 << 40, workspace_bytes=n)) == fb.ERR_INVALID_ARG
+    assert bwd_validate(lib, bargs(d_q=FAKE + 8, workspace=1 << 40, workspace_bytes=n)) == fb.ERR_INVALID_ARG
+    # an output on top of an input
+    assert bwd_validate(lib, bargs(d_v=3 * FAKE, workspace=1 << 40, workspace_bytes=n)) == fb.ERR_INVALID_ARG
+    # two outputs on top of each other
+    assert bwd_validate(lib, bargs(d_k=7 * FAKE, workspace=1 << 40, workspace_bytes=n)) == fb.ERR_INVALID_ARG
+    # tail pairs belong to window variants
+    st = fb.FalconStateC(12 * FAKE, 13 * FAKE, 14 * FAKE, 15 * FAKE, 1, 0)
+    assert bwd_validate(lib, bargs(state_in=st, workspace=1 << 40, workspace_bytes=n)) == fb.ERR_INVALID_ARG
+    st = fb.FalconStateC(12 * FAKE, 13 * FAKE, None, None, 0, 0)
+    assert bwd_validate(lib, bargs(state_in=st, workspace=1 << 40, workspace_bytes=n)) == fb.OK
+    st = fb.FalconStateC(12 * FAKE, None, None, None, 0, 0)      # continued without x_next
+    assert bwd_validate(lib, bargs(state_in=st, workspace=1 << 40, workspace_bytes=n)) == fb.ERR_INVALID_ARG
