@@ -7,7 +7,8 @@ workload is Falcon-1, batch 8, 12 heads, T = 1024, d_k = d_v = 64, C = 64,
 bf16 inputs and fp32 state.  Inputs are resident in HBM before timing.
 
 Prints one JSON line (see the keys below).  `--gpus N` with N > 1 exits:
-this build runs on one GPU only.
+this build runs on one GPU only.  `--backward` times the Falcon-1 backward
+pass (falcon_bwd) on the workload instead, with its own metric.
 """
 from __future__ import annotations
 
@@ -38,6 +39,21 @@ def algorithmic_bytes(w) -> int:
         h = w.window - 1
         total += w.batch * w.heads * 4 * (w.dk * w.dv + 2 * w.dk + 2 * h * (w.dk + w.dv))
     return total
+
+
+METRIC_BWD = "Falcon-1 backward tokens/s (B*H*T) + % of HBM roofline"
+
+
+def algorithmic_bytes_bwd(w) -> int:
+    """Unavoidable traffic of one backward call: q, k, v and d_o read once
+    and d_q, d_k, d_v written once (io dtype); beta and lambda read and
+    d_beta, d_lambda written once (fp32); per head the initial state and
+    the final state's gradient read and the initial state's gradient written
+    (fp32).  The forward's intermediates are recomputed, not counted."""
+    esz = 2 if w.dtype == "bf16" else 4
+    n = w.batch * w.heads * w.seqlen
+    return (n * (2 * w.dk + 2 * w.dv + 2 * w.dk + w.dv) * esz + n * 4 * 4
+            + w.batch * w.heads * w.dk * w.dv * 4 * 3)
 
 
 def algorithmic_flops(w) -> int:
@@ -215,14 +231,20 @@ def rocprof_summary(workload: str, kernels, stats_db: str, fetch_db: str, write_
     return "\n".join(lines)
 
 
-def kernel_names(lib, w):
-    """Names of the kernels one call of workload `w` launches (host-side plan)."""
+def kernel_names(lib, w, backward=False):
+    """Names of the kernels one call of workload `w` launches (host-side plan),
+    of falcon_bwd with `backward`."""
     from linear_recurrent_weight_amd import falcon as fb
-    a = fb.make_args(variant=w.variant, dtype=w.dtype, batch=w.batch, heads=w.heads, seqlen=w.seqlen,
-                     dk=w.dk, dv=w.dv, chunk=w.chunk, window=w.window)
+    if backward:
+        a = fb.make_bwd_args(dtype=w.dtype, batch=w.batch, heads=w.heads, seqlen=w.seqlen, dk=w.dk, dv=w.dv)
+        fn = lib.falcon_bwd_kernel_name
+    else:
+        a = fb.make_args(variant=w.variant, dtype=w.dtype, batch=w.batch, heads=w.heads, seqlen=w.seqlen,
+                         dk=w.dk, dv=w.dv, chunk=w.chunk, window=w.window)
+        fn = lib.falcon_kernel_name
     names = []
     while True:
-        nm = lib.falcon_kernel_name(ctypes.byref(a), len(names))
+        nm = fn(ctypes.byref(a), len(names))
         if nm is None:
             return names
         names.append(nm.decode())
@@ -365,18 +387,21 @@ def main() -> int:
                     help="STATS_DB FETCH_DB WRITE_DB [MFMA_DB]: write the markdown summary of "
                          "these rocprofv3 runs to profiles/ (no GPU needed)")
     ap.add_argument("--rocprof-command", default="", help="the commands that made the databases")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the Falcon-1 backward pass (falcon_bwd) on the workload")
     args = ap.parse_args()
+    prof_name = args.workload + ("_bwd" if args.backward else "")
     if args.rocprof_summary:
         from linear_recurrent_weight_amd import falcon as fb
         from linear_recurrent_weight_amd.inputs import WORKLOADS
         dbs = args.rocprof_summary
         if len(dbs) not in (3, 4):
             ap.error("--rocprof-summary takes 3 or 4 databases")
-        names = kernel_names(fb.load_library(), WORKLOADS[args.workload])
-        text = rocprof_summary(args.workload, names, *dbs[:3], args.rocprof_command)
+        names = kernel_names(fb.load_library(), WORKLOADS[args.workload], args.backward)
+        text = rocprof_summary(prof_name, names, *dbs[:3], args.rocprof_command)
         if len(dbs) == 4:
             text += mfma_summary(dbs[3], dbs[0])
-        path = profile_path(args.workload, names)
+        path = profile_path(prof_name, names)
         os.makedirs(os.path.dirname(path), exist_ok=True)
         with open(path, "w") as f:
             f.write(text)
@@ -392,6 +417,8 @@ def main() -> int:
 
     w = WORKLOADS[args.workload]
     inp = make_inputs(w)
+    if args.backward:
+        return bwd_main(args, w, inp, prof_name)
     # the oracle's CPU baseline forks workers: it runs before the GPU is touched
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp, args.cpu_seconds)
 
@@ -515,6 +542,137 @@ def main() -> int:
     print(json.dumps(line), flush=True)
     return 0
 
+
+
+def bwd_cpu_baseline(w, inp, min_seconds: float):
+    """The fp64 backward oracle, as it is, on one core over a bounded sample
+    of heads (whole sequences), scaled to head-tokens per second."""
+    import numpy as np
+    from oracle.falcon_backward import falcon1_backward
+    _limit_blas()
+    BH = w.batch * w.heads
+    rng = np.random.default_rng(0)
+    flat = {n: a.reshape(BH, *a.shape[2:]) for n, a in inp.items()}
+    done, heads, t0 = 0, 0, time.perf_counter()
+    while time.perf_counter() - t0 < min_seconds and heads < BH:
+        part = {n: a[heads:heads + 1][None] for n, a in flat.items()}
+        d_o = rng.standard_normal((1, 1, w.seqlen, w.dv))
+        falcon1_backward(part["q"], part["k"], part["v"], part["beta"], part["lam"], d_o,
+                         eps=w.eps, eps_gamma=w.eps_gamma, eps_rms=w.eps_rms)
+        done += w.seqlen
+        heads += 1
+    wall = time.perf_counter() - t0
+    return {"value": done / wall, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{heads} of {BH} heads x {w.seqlen} tokens, one process, {wall:.1f} s; "
+                      "fp64 NumPy reverse token recurrence", "cpu_model": cpu_model()}
+
+
+def bwd_main(args, w, inp, prof_name) -> int:
+    """Time falcon_bwd (Falcon-1 backward) on workload w: K calls over
+    resident input sets, events on the library's stream, per-kernel times
+    from falcon_bwd_profile."""
+    import numpy as np
+    if w.variant != "F1" or w.window != 1:
+        print(json.dumps({"error": "the backward pass covers Falcon-1 only"}))
+        return 2
+    cpu = None if args.no_cpu_baseline else bwd_cpu_baseline(w, inp, args.cpu_seconds)
+    import torch
+    from linear_recurrent_weight_amd import falcon as fb
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    lib = fb.load_library()
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    ws = None
+
+    def make_bwd_set():
+        nonlocal ws
+        t = {n: torch.from_numpy(inp[n]).to(dev) for n in ("q", "k", "v", "beta", "lam")}
+        for n in ("q", "k", "v"):
+            t[n] = t[n].to(dt).contiguous()
+        B, H, T, dk, dv = w.batch, w.heads, w.seqlen, w.dk, w.dv
+        t["d_o"] = torch.randn(B, H, T, dv, generator=gen).to(dev).to(dt)
+        t["d_S_out"] = torch.randn(B, H, dk, dv, generator=gen).to(dev)
+        for n, shape, d in (("d_q", (B, H, T, dk), dt), ("d_k", (B, H, T, dk), dt), ("d_v", (B, H, T, dv), dt),
+                            ("d_beta", (B, H, T), torch.float32), ("d_lam", (B, H, T), torch.float32),
+                            ("d_S_in", (B, H, dk, dv), torch.float32)):
+            t[n] = torch.empty(*shape, dtype=d, device=dev)
+        a = fb.make_bwd_args(dtype=w.dtype, batch=B, heads=H, seqlen=T, dk=dk, dv=dv, eps=w.eps,
+                             eps_gamma=w.eps_gamma, eps_rms=w.eps_rms, q=t["q"], k=t["k"], v=t["v"],
+                             beta=t["beta"], lam=t["lam"], d_o=t["d_o"], d_S_out=t["d_S_out"],
+                             d_q=t["d_q"], d_k=t["d_k"], d_v=t["d_v"], d_beta=t["d_beta"],
+                             d_lam=t["d_lam"], d_S_in=t["d_S_in"])
+        nbytes = lib.falcon_bwd_workspace_size(ctypes.byref(a))
+        if ws is None:
+            ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        a.workspace = ws.data_ptr()
+        a.workspace_bytes = ws.numel()
+        t["args"] = a
+        t["bytes"] = sum(x.numel() * x.element_size() for n, x in t.items() if n != "args")
+        return t
+
+    sets = [make_bwd_set()]
+    while len(sets) * sets[0]["bytes"] <= 2 * LLC_BYTES:
+        sets.append(make_bwd_set())
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    pargs = [ctypes.byref(t["args"]) for t in sets]
+
+    def step(i):
+        rc = lib.falcon_bwd(pargs[i % len(pargs)], sh)
+        if rc != 0:
+            raise fb.FalconError(rc, lib)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    wall = time.perf_counter() - w0
+
+    names = kernel_names(lib, w, backward=True)
+    nk = len(names)
+    reps = max(5, min(args.steps, 50))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(reps)]
+    for row in evs:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for r in range(reps):
+        arr = (ctypes.c_void_p * (nk + 1))(*[e.cuda_event for e in evs[r]])
+        got = lib.falcon_bwd_profile(pargs[r % len(pargs)], sh, arr, nk + 1)
+        if got != nk:
+            raise RuntimeError(f"falcon_bwd_profile launched {got} kernels, expected {nk}")
+    torch.cuda.synchronize()
+    per_kernel = {n: float(np.mean([evs[r][i].elapsed_time(evs[r][i + 1]) for r in range(reps)]))
+                  for i, n in enumerate(names)}
+    alg = algorithmic_bytes_bwd(w)
+    gbs = alg / (ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC_BWD, "value": w.tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{w.name}: Falcon-1 backward (token-recurrent)", "variant": w.variant,
+                   "batch": w.batch, "heads": w.heads, "seq_len": w.seqlen, "dk": w.dk, "dv": w.dv,
+                   "io_dtype": w.dtype, "state_dtype": "f32", "parallelism": "none (1 GPU)",
+                   "resident_sets": len(sets)},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": read_traffic(prof_name, names),
+                     "kernel": "falcon_bwd call (" + " + ".join(names) + ")",
+                     "dominant_kernel": max(per_kernel, key=per_kernel.get), "launch_ms": ms,
+                     "algorithmic_bytes": alg},
+        "kernels_ms": per_kernel, "wall_s_timed": wall,
+    }
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+    return 0
 
 if __name__ == "__main__":
     sys.exit(main())

@@ -278,6 +278,15 @@ int falcon_bwd_validate(const falcon_bwd_args *args);
  * the default stream).  Returns FALCON_OK or a negative status. */
 int falcon_bwd(const falcon_bwd_args *args, void *stream);
 
+/* Measurement variant of falcon_bwd, with the event convention of
+ * falcon_fwd_profile: events[0] before the first kernel, events[i] after the
+ * i-th.  Returns the number of kernels launched or a negative status. */
+int falcon_bwd_profile(const falcon_bwd_args *args, void *stream, void *const *events, int n_events);
+
+/* Static name of the i-th kernel falcon_bwd launches for these arguments, or
+ * NULL (i out of range, invalid arguments).  Pure host code. */
+const char *falcon_bwd_kernel_name(const falcon_bwd_args *args, int i);
+
 /* Static name of the i-th kernel (0-based) that falcon_fwd launches for these
  * arguments, or NULL when i is out of range or the arguments are invalid.
  * Pure host code, no HIP call. */

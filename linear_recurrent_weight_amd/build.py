@@ -73,6 +73,7 @@ KERNEL_SOURCES = {"passthrough": "feature.hip", "feature": "feature.hip", "recur
                   "f3_prep": "chunk_f3.hip", "f3_scan": "chunk_f3.hip",
                   "f1_xfer": "chunk_f1_xfer.hip", "f1_carry": "chunk_f1_xfer.hip",
                   "f1_segmap": "chunk_f1_xfer.hip", "f1_segscan": "chunk_f1_xfer.hip",
+                  "bwd_states": "falcon_bwd.hip", "bwd_sweep": "falcon_bwd.hip", "bwd_reduce": "falcon_bwd.hip",
                   "a_segment": "chunk_a.hip", "a_segscan": "chunk_a.hip", "a_output": "chunk_a.hip",
                   "a1_segment": "chunk_a1.hip", "a1_segscan": "chunk_a1.hip", "a1_output": "chunk_a1.hip",
                   "a3_window": "chunk_a1.hip"}

@@ -425,13 +425,18 @@ void launch_bwd(const BwdArgs &a, bool io_bf16, hipStream_t s, Marks *m) {
 
 }  // namespace falcon
 
-extern "C" int falcon_bwd(const falcon_bwd_args *args, void *stream) {
+namespace {
+
+const char *const kNamesBwd[] = {"feature", "bwd_states", "bwd_sweep", "bwd_reduce"};
+const char *const kNamesBwdEmpty[] = {"bwd_states", "bwd_sweep"};
+
+// returns the number of kernels launched, or a negative status
+int run_bwd(const falcon_bwd_args *args, void *stream, falcon::Marks &m) {
     using namespace falcon;
     BwdPlan p;
     const int rc = build_bwd_plan(args, &p, true);
     if (rc != FALCON_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    Marks m;
     m.sync_check = sync_check_enabled();
     m.mark(s);
     const bool bf16 = p.dtype == FALCON_BF16;
@@ -499,5 +504,28 @@ extern "C" int falcon_bwd(const falcon_bwd_args *args, void *stream) {
         return FALCON_ERR_HIP;
     }
     if (hipGetLastError() != hipSuccess) return FALCON_ERR_HIP;
-    return FALCON_OK;
+    return m.count - 1;
+}
+
+}  // namespace
+
+extern "C" int falcon_bwd(const falcon_bwd_args *args, void *stream) {
+    falcon::Marks m;
+    const int rc = run_bwd(args, stream, m);
+    return rc < 0 ? rc : FALCON_OK;
+}
+
+extern "C" int falcon_bwd_profile(const falcon_bwd_args *args, void *stream, void *const *events,
+                                  int n_events) {
+    falcon::Marks m;
+    m.ev = events;
+    m.n = n_events < 0 ? 0 : n_events;
+    return run_bwd(args, stream, m);
+}
+
+extern "C" const char *falcon_bwd_kernel_name(const falcon_bwd_args *args, int i) {
+    falcon::BwdPlan p;
+    if (falcon::build_bwd_plan(args, &p, false) != FALCON_OK || i < 0) return nullptr;
+    if (p.T == 0) return i < 2 ? kNamesBwdEmpty[i] : nullptr;
+    return i < 4 ? kNamesBwd[i] : nullptr;
 }

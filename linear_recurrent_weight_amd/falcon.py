@@ -64,7 +64,8 @@ class FalconBwdArgsC(ctypes.Structure):
 
 EXPORTS = ("falcon_fwd", "falcon_fwd_validate", "falcon_fwd_workspace_size",
            "falcon_fwd_profile", "falcon_fwd_noalloc", "falcon_kernel_name", "falcon_status_str",
-           "falcon_abi_version", "falcon_bwd", "falcon_bwd_validate", "falcon_bwd_workspace_size")
+           "falcon_abi_version", "falcon_bwd", "falcon_bwd_validate", "falcon_bwd_workspace_size",
+           "falcon_bwd_profile", "falcon_bwd_kernel_name")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
@@ -100,6 +101,11 @@ def load_library(path: Optional[os.PathLike] = None) -> ctypes.CDLL:
     lib.falcon_bwd_validate.restype = ctypes.c_int
     lib.falcon_bwd_workspace_size.argtypes = [ctypes.POINTER(FalconBwdArgsC)]
     lib.falcon_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.falcon_bwd_profile.argtypes = [ctypes.POINTER(FalconBwdArgsC), ctypes.c_void_p,
+                                       ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+    lib.falcon_bwd_profile.restype = ctypes.c_int
+    lib.falcon_bwd_kernel_name.argtypes = [ctypes.POINTER(FalconBwdArgsC), ctypes.c_int]
+    lib.falcon_bwd_kernel_name.restype = ctypes.c_char_p
     lib.falcon_abi_version.argtypes = []
     lib.falcon_abi_version.restype = ctypes.c_int
     if lib.falcon_abi_version() != ABI_VERSION:

@@ -433,3 +433,18 @@ def test_bwd_rules(lib):
     assert bwd_validate(lib, bargs(state_in=st, workspace=1 << 40, workspace_bytes=n)) == fb.OK
     st = fb.FalconStateC(12 * FAKE, None, None, None, 0, 0)      # continued without x_next
     assert bwd_validate(lib, bargs(state_in=st, workspace=1 << 40, workspace_bytes=n)) == fb.ERR_INVALID_ARG
+
+
+def test_bwd_kernel_names(lib):
+    from linear_recurrent_weight_amd.build import CSRC, KERNEL_SOURCES
+
+    def names(a):
+        out = []
+        while (nm := lib.falcon_bwd_kernel_name(ctypes.byref(a), len(out))) is not None:
+            out.append(nm.decode())
+        return out
+    assert names(bargs()) == ["feature", "bwd_states", "bwd_sweep", "bwd_reduce"]
+    assert names(bargs(seqlen=0)) == ["bwd_states", "bwd_sweep"]
+    assert names(bargs(variant="F2")) == []
+    for nm in names(bargs()):
+        assert nm in (CSRC / KERNEL_SOURCES[nm]).read_text()

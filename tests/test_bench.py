@@ -26,6 +26,14 @@ def test_algorithmic_bytes():
     assert bench.algorithmic_bytes(c1) == 4 * 64 * 16 * 4 + 2 * 64 * 4 + 16 * 16 * 4
 
 
+def test_algorithmic_bytes_backward_c2():
+    """q, k, v, d_o read and d_q, d_k, d_v written in bf16 (7 x 64 x 2 bytes
+    per head-token), four fp32 scalars per head-token, and three fp32 states
+    per head."""
+    n = 8 * 12 * 1024
+    assert bench.algorithmic_bytes_bwd(WORKLOADS["c2"]) == n * (7 * 64 * 2 + 16) + 96 * 64 * 64 * 4 * 3
+
+
 def test_algorithmic_flops_c2():
     """Falcon-1 chunk form: 2C(d_k + d_v) + 6 d_k d_v per head-token."""
     w = WORKLOADS["c2"]
