@@ -14,8 +14,9 @@
 // elementwise.  The rewrite needs 1/Gamma in range: a chunk in which some
 // column decays below 2^-64 is run token by token instead (exact, slower).
 //
-// One workgroup (4 waves) per (batch*head, slice of up to 64 value columns)
-// walks its chunks in order; the fp32 state slice stays in LDS.
+// One workgroup (4 waves) per (batch*head, slice of up to 32 value columns)
+// walks its chunks in order; the fp32 state slice stays in LDS, and the next
+// chunk's rows load into registers while a chunk is processed.
 #include "chunk_layout.h"
 #include "kernels.h"
 #include "mma.h"
@@ -37,11 +38,46 @@ struct F2aShared {
     E Lb[C][C + PE];        // lower(Qh X^T)
     E ST[DS][DK + PE];      // bf16/fp32 copy of S^T [j][d]
     float Sf[DK][DS];       // the state slice, fp32
-    float Yf[C][DS];        // raw values of the chunk
-    float Bf[C][DS];        // beta, then the log-prefix b (base 2)
+    float Yf[C][DS + 1];    // raw values of the chunk (odd pitch: a token per lane reads distinct banks)
+    float Bf[C][DS + 1];    // beta, then the log-prefix b (base 2)
     float n2[C], lam[C], ok[C];
-    int fast;
+    int fastw[NT / 64];
 };
+
+// 8-byte pieces <-> floats for the io type
+template <class E> struct Io8;
+template <> struct Io8<bf16_t> {
+    static constexpr int n = 4;   // elements per 8 bytes
+    __device__ static void unpack(const uint2 &u, float *f) {
+        f[0] = __uint_as_float(u.x << 16);
+        f[1] = __uint_as_float(u.x & 0xffff0000u);
+        f[2] = __uint_as_float(u.y << 16);
+        f[3] = __uint_as_float(u.y & 0xffff0000u);
+    }
+};
+template <> struct Io8<float> {
+    static constexpr int n = 2;
+    __device__ static void unpack(const uint2 &u, float *f) {
+        f[0] = __uint_as_float(u.x);
+        f[1] = __uint_as_float(u.y);
+    }
+};
+
+// n consecutive row elements (n a multiple of 4) from floats, as 8-byte
+// (bf16) or 16-byte (fp32) stores
+template <class E, int n>
+__device__ __forceinline__ void put_row(E *dst, const float *v) {
+#pragma unroll
+    for (int i = 0; i < n; i += 4) {
+        if constexpr (sizeof(E) == 2) {
+            const uint32_t lo = uint32_t(f32_to_bf16(v[i])) | (uint32_t(f32_to_bf16(v[i + 1])) << 16);
+            const uint32_t hi = uint32_t(f32_to_bf16(v[i + 2])) | (uint32_t(f32_to_bf16(v[i + 3])) << 16);
+            *reinterpret_cast<uint2 *>(dst + i) = make_uint2(lo, hi);
+        } else {
+            *reinterpret_cast<float4 *>(dst + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+        }
+    }
+}
 
 template <class E, int DK, int DS>
 __global__ __launch_bounds__(NT) void chunk_f2a_kernel(ChunkF2Args a, int nslice) {
@@ -63,23 +99,56 @@ __global__ __launch_bounds__(NT) void chunk_f2a_kernel(ChunkF2Args a, int nslice
     }
 
     // rows: thread (row = tid / 4, part = tid % 4) holds DK / 4 features and
-    // DS / 4 values of one token
+    // DS / 4 values and gains of one token, loaded as 8-byte pieces one chunk
+    // ahead (unconditional loads from rows clamped into [0, T))
     const int row = tid >> 2, part = tid & 3;
     constexpr int EK = DK / 4, EV = DS / 4;
+    constexpr int NQ = EK / Io8<E>::n, NVv = EV / Io8<E>::n;
+    static_assert(NQ >= 1 && NVv >= 1 && EV % 4 == 0, "whole 8-byte pieces per thread");
+    uint2 rq[NQ], rk[NQ], rv[NVv];
+    float4 rb[EV / 4];
+    float rlam;
+    auto prefetch = [&](int c) {
+        const int t = c * C + row;
+        const int tq = t < T ? t : T - 1;
+        const int tk = t < 1 ? 0 : (t - 1 < T ? t - 1 : T - 1);
+        const uint2 *q2 = reinterpret_cast<const uint2 *>(qg + size_t(tq) * DK + part * EK);
+        const uint2 *k2 = reinterpret_cast<const uint2 *>(kg + size_t(tk) * DK + part * EK);
+        const uint2 *v2 = reinterpret_cast<const uint2 *>(vg + size_t(tq) * DV + j0 + part * EV);
+        const float4 *b4 = reinterpret_cast<const float4 *>(a.beta + (size_t(bh) * T + tq) * DV + j0 + part * EV);
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            rq[i] = q2[i];
+            rk[i] = k2[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NVv; ++i) rv[i] = v2[i];
+#pragma unroll
+        for (int i = 0; i < EV / 4; ++i) rb[i] = b4[i];
+        rlam = a.lambda[size_t(bh) * T + tq];
+    };
+    prefetch(0);
+
     for (int c = 0; c < a.nchunks; ++c) {
         __syncthreads();   // the previous chunk's readers are done
         {
             const int t = c * C + row;
             const bool qok = t < T;
-            const int tq = qok ? t : T - 1;
-            float q[EK], x[EK];
+            float q[EK], x[EK], y[EV];
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                Io8<E>::unpack(rq[i], q + i * Io8<E>::n);
+                Io8<E>::unpack(rk[i], x + i * Io8<E>::n);
+            }
+#pragma unroll
+            for (int i = 0; i < NVv; ++i) Io8<E>::unpack(rv[i], y + i * Io8<E>::n);
+            if (t == 0) {   // x_0: the carried feature of a continued sequence, 0 when fresh
+#pragma unroll
+                for (int e = 0; e < EK; ++e) x[e] = a.xnext_in ? a.xnext_in[size_t(bh) * DK + part * EK + e] : 0.f;
+            }
             float sq = 0.f, sx = 0.f;
 #pragma unroll
             for (int e = 0; e < EK; ++e) {
-                const int d = part * EK + e;
-                q[e] = ld(qg, size_t(tq) * DK + d);
-                if (t == 0) x[e] = a.xnext_in ? a.xnext_in[size_t(bh) * DK + d] : 0.f;
-                else x[e] = ld(kg, size_t(t - 1 < T ? t - 1 : T - 1) * DK + d);
                 sq += q[e] * q[e];
                 sx += x[e] * x[e];
             }
@@ -93,46 +162,52 @@ __global__ __launch_bounds__(NT) void chunk_f2a_kernel(ChunkF2Args a, int nslice
             float n2 = 0.f;
 #pragma unroll
             for (int e = 0; e < EK; ++e) {
-                const int d = part * EK + e;
-                const float xs = x[e] * scx;
-                n2 += xs * xs;
-                st(&sh.Qh[row][0], d, q[e] * scq);
-                st(&sh.Xr[row][0], d, xs);
-                st(&sh.XT[d][0], row, xs);
+                q[e] *= scq;
+                x[e] *= scx;
+                n2 += x[e] * x[e];
+                st(&sh.XT[part * EK + e][0], row, x[e]);
             }
+            put_row<E, EK>(&sh.Qh[row][part * EK], q);
+            put_row<E, EK>(&sh.Xr[row][part * EK], x);
             n2 += dpp<kDppQuadXor1>(n2);
             n2 += dpp<kDppQuadXor2>(n2);
 #pragma unroll
             for (int e = 0; e < EV; ++e) {
                 const int j = part * EV + e;
-                sh.Yf[row][j] = qok ? ld(vg, size_t(tq) * DV + j0 + j) : 0.f;
-                sh.Bf[row][j] = a.beta[(size_t(bh) * T + tq) * DV + j0 + j];
+                sh.Yf[row][j] = qok ? y[e] : 0.f;
+                sh.Bf[row][j] = rb[e >> 2][e & 3];
             }
             if (part == 0) {
                 sh.n2[row] = n2;
-                sh.lam[row] = a.lambda[size_t(bh) * T + tq];
+                sh.lam[row] = rlam;
                 sh.ok[row] = (qok && !(t == 0 && a.fresh)) ? 1.f : 0.f;   // the fresh first step writes nothing
             }
+            if (c + 1 < a.nchunks) prefetch(c + 1);
         }
         __syncthreads();
 
-        // per-column steps and log-prefix (thread j walks the chunk's tokens)
-        if (tid < DS) {
-            const int j = tid;
-            float b = 0.f;
-            for (int t = 0; t < C; ++t) {
-                const float den = sh.n2[t] + sh.lam[t] + a.eps;
-                const float eta = sh.ok[t] != 0.f ? step_eta(sh.Bf[t][j], den) : 0.f;
-                b += log2_1m(step_alpha(eta, sh.lam[t], a.eps_gamma));
-                sh.Bf[t][j] = b;
-                st(&sh.YT[j][0], t, eta * sh.Yf[t][j] * exp2f(-b));
+        // per-column steps and log-prefix: wave w takes columns w, w + 4, ..,
+        // lane = token; the prefix is a wave scan
+        {
+            const float den = sh.n2[lane] + sh.lam[lane] + a.eps;
+            const bool live = sh.ok[lane] != 0.f;
+            const float lam = sh.lam[lane];
+            bool in_range = true;
+            for (int j = wave; j < DS; j += NT / 64) {
+                const float eta = live ? step_eta(sh.Bf[lane][j], den) : 0.f;
+                const float b = wave_inclusive_scan(log2_1m(step_alpha(eta, lam, a.eps_gamma)));
+                sh.Bf[lane][j] = b;
+                st(&sh.YT[j][0], lane, eta * sh.Yf[lane][j] * exp2f(-b));
+                in_range = in_range && __shfl(b, 63, 64) >= kMinLog2Decay;
             }
-            const bool in_range = __ballot(j < DS && b >= kMinLog2Decay) == __ballot(j < DS);
-            if (tid == 0) sh.fast = in_range ? 1 : 0;
+            if (lane == 0) sh.fastw[wave] = in_range ? 1 : 0;
         }
         __syncthreads();
+        bool fast = true;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) fast = fast && sh.fastw[w] != 0;
 
-        if (sh.fast) {
+        if (fast) {
             // L = lower(Qh X^T), 16 x 16 tiles
             for (int tile = wave; tile < 16; tile += 4) {
                 const int m = tile >> 2, n = tile & 3;
@@ -228,11 +303,14 @@ __global__ __launch_bounds__(NT) void chunk_f2a_kernel(ChunkF2Args a, int nslice
 
 template <class E, int DK>
 void launch_f2a_dk(const ChunkF2Args &a, hipStream_t s) {
-    const int ds = a.dv < 64 ? a.dv : 64, nslice = a.dv / ds;
+    // slices of 32 value columns (two workgroups per CU by LDS), or of 16
+    // when 32-column slices would leave compute units idle; every slice forms
+    // the head's shared features and scores again (its rows come from L2)
+    const int ds = (a.dv < 32 || static_cast<long long>(a.BH) * (a.dv / 32) < 256) ? 16 : 32;
+    const int nslice = a.dv / ds;
     const dim3 grid(a.BH * nslice);
     if (ds == 16) chunk_f2a_kernel<E, DK, 16><<<grid, NT, 0, s>>>(a, nslice);
-    else if (ds == 32) chunk_f2a_kernel<E, DK, 32><<<grid, NT, 0, s>>>(a, nslice);
-    else chunk_f2a_kernel<E, DK, 64><<<grid, NT, 0, s>>>(a, nslice);
+    else chunk_f2a_kernel<E, DK, 32><<<grid, NT, 0, s>>>(a, nslice);
 }
 
 }  // namespace

@@ -79,6 +79,10 @@ WORKLOADS = {
     # c2's step distributions: few heads, a 256-chunk walk per head
     "c3f1": Workload("c3f1", "F1", 2, 12, 16384, 64, 64, 64, 1, "bf16", "sigmoid", 0, 0,
                      "uniform", 0.0, 0.05, seed=33),
+    # Falcon-2A (per-column gains, inner-product write) at the c2 shape; its
+    # chunk kernel takes d_k <= 64, so c4's d = 128 shape runs it token by token
+    "c2f2a": Workload("c2f2a", "F2A", 8, 12, 1024, 64, 64, 64, 1, "bf16", "sigmoid", 0, 0,
+                      "uniform", 0.0, 0.05, seed=22),
     "c5f3": Workload("c5f3", "F3", 8, 12, 512, 64, 64, 64, 8, "bf16", "sigmoid", 0, 0,
                      "uniform", 0.0, 0.05, seed=51),
 }

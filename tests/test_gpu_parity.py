@@ -772,6 +772,11 @@ def test_chunk_f2a_continuation(split, dtype):
     assert eo <= tol and es <= tol, (eo, es)
 
 
+def test_named_workload_c2f2a_chunk():
+    """Falcon-2A at the c2 shape over all 96 heads."""
+    check_named("c2f2a")
+
+
 def test_chunk_f2a_equal_gains_is_falcon1a():
     """The same gain in every column: the Falcon-2A chunk kernel and the
     Falcon-1A chunk kernels agree to fp32 rounding."""
