@@ -12,7 +12,8 @@
 // r_t - S_{t-1} w_t), dqh_t = S_t do_t) leave each wavefront as per-group
 // partial sums and are added up per token afterwards, in a fixed order.
 //   feature     (the forward's feature pass) x_t, qh_t, eta_t, alpha_t;
-//   bwd_states  the forward recurrence again, keeping every pre-step state;
+//   bwd_states  the forward recurrence again, keeping the state before every
+//               4th token and each token's residual r_t;
 //   bwd_sweep   the reverse sweep: dv_t, the partial sums, and dS_0;
 //   bwd_reduce  per token: the sums over groups, the decay and step chain
 //               (clamp-gated, zero steps masked, the fresh first step a
@@ -27,14 +28,15 @@
 namespace falcon {
 namespace {
 
-constexpr int kCpw = 4;   // value columns per wavefront
-constexpr int kTb = 4;    // tokens whose inputs are loaded together
+constexpr int kCpw = 4;               // value columns per wavefront
+constexpr int kTb = kBwdCheckpoint;   // tokens whose inputs are loaded together (a checkpoint block)
 
-// rows of the state S_t of (head bh, column group g), one float4 (the 4
-// columns) per row
-__device__ __forceinline__ float4 *state_at(const BwdArgs &a, int bh, int t, int g) {
+// rows of the checkpointed state before token kTb * k of (head bh, column
+// group g), one float4 (the 4 columns) per row
+__device__ __forceinline__ float4 *state_at(const BwdArgs &a, int bh, int k, int g) {
     const int groups = a.dv / kCpw;
-    return reinterpret_cast<float4 *>(a.states) + ((size_t(bh) * (a.T + 1) + t) * groups + g) * a.dk;
+    const size_t nck = size_t(bwd_checkpoints(a.T));
+    return reinterpret_cast<float4 *>(a.states) + ((size_t(bh) * nck + k) * groups + g) * a.dk;
 }
 
 template <int RPL>
@@ -48,8 +50,32 @@ __device__ __forceinline__ float col(const float4 &v, int c) {
 }
 
 // ---------------------------------------------------------------------------
-// bwd_states: S_0 .. S_T of 4 value columns (the forward recurrence)
+// bwd_states: S_0 .. S_T and r_t of 4 value columns (the forward recurrence)
 // ---------------------------------------------------------------------------
+// the inputs of kTb consecutive tokens (rows clamped into [0, T)); two sets
+// alternate so that one block's loads are in flight while the previous
+// block computes
+template <class E, int RPL>
+struct FwdBlock {
+    float x[kTb][RPL], y[kTb][kCpw], eta[kTb], gam[kTb];
+    __device__ __forceinline__ void load(const BwdArgs &a, const E *v, int bh, int t0, int lane, int c0) {
+        const int T = a.T, dk = a.dk, dv = a.dv;
+#pragma unroll
+        for (int u = 0; u < kTb; ++u) {
+            const size_t row = size_t(bh) * T + (t0 + u < T ? t0 + u : T - 1);
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) {
+                const int i = lane + 64 * r;
+                x[u][r] = i < dk ? a.xn[row * dk + i] : 0.f;
+            }
+#pragma unroll
+            for (int c = 0; c < kCpw; ++c) y[u][c] = ld(v, row * dv + c0 + c);
+            eta[u] = a.eta[row];
+            gam[u] = 1.f - a.alpha[row];
+        }
+    }
+};
+
 template <class E, int RPL, int RW>
 __global__ __launch_bounds__(256) void bwd_states(BwdArgs a) {
     auto rsum = [](float v) { return group_sum<RW>(v); };
@@ -69,55 +95,87 @@ __global__ __launch_bounds__(256) void bwd_states(BwdArgs a) {
         for (int c = 0; c < kCpw; ++c)
             S[r][c] = (a.S_in && i < dk) ? a.S_in[(size_t(bh) * dk + i) * dv + c0 + c] : 0.f;
     }
-    auto put = [&](int t) {
-        float4 *p = state_at(a, bh, t, g);
+    auto put = [&](int k) {   // the state before token kTb * k
+        float4 *p = state_at(a, bh, k, g);
 #pragma unroll
         for (int r = 0; r < RPL; ++r) {
             const int i = lane + 64 * r;
             if (i < dk) p[i] = make_float4(S[r][0], S[r][1], S[r][2], S[r][3]);
         }
     };
-    for (int t0 = 0; t0 < T; t0 += kTb) {
-        float xb[kTb][RPL], yb[kTb][kCpw], eb[kTb], gb[kTb];
+    auto step = [&](const FwdBlock<E, RPL> &b, int t0) {
+        put(t0 / kTb);
 #pragma unroll
         for (int u = 0; u < kTb; ++u) {
-            const size_t row = size_t(bh) * T + (t0 + u < T ? t0 + u : T - 1);
-#pragma unroll
-            for (int r = 0; r < RPL; ++r) {
-                const int i = lane + 64 * r;
-                xb[u][r] = i < dk ? a.xn[row * dk + i] : 0.f;
-            }
-#pragma unroll
-            for (int c = 0; c < kCpw; ++c) yb[u][c] = ld(v, row * dv + c0 + c);
-            eb[u] = a.eta[row];
-            gb[u] = 1.f - a.alpha[row];
-        }
-#pragma unroll
-        for (int u = 0; u < kTb; ++u) {
-            if (t0 + u >= T) break;
-            put(t0 + u);   // S_{t-1}, the state this step starts from
-            float pred[kCpw];
+            const int t = t0 + u;
+            if (t >= T) break;
+            float res[kCpw];
 #pragma unroll
             for (int c = 0; c < kCpw; ++c) {
                 float s = 0.f;
 #pragma unroll
-                for (int r = 0; r < RPL; ++r) s += S[r][c] * xb[u][r];
-                pred[c] = rsum(s);
+                for (int r = 0; r < RPL; ++r) s += S[r][c] * b.x[u][r];
+                res[c] = b.y[u][c] - rsum(s);
             }
+            if (lane == 0)
+                *reinterpret_cast<float4 *>(a.res + (size_t(bh) * T + t) * dv + c0) = make_float4(res[0], res[1], res[2], res[3]);
 #pragma unroll
-            for (int c = 0; c < kCpw; ++c) {
-                const float res = yb[u][c] - pred[c];
+            for (int c = 0; c < kCpw; ++c)
 #pragma unroll
-                for (int r = 0; r < RPL; ++r) S[r][c] = gb[u] * S[r][c] + eb[u] * xb[u][r] * res;
-            }
+                for (int r = 0; r < RPL; ++r) S[r][c] = b.gam[u] * S[r][c] + b.eta[u] * b.x[u][r] * res[c];
         }
+    };
+    FwdBlock<E, RPL> b0, b1;
+    if (T > 0) b0.load(a, v, bh, 0, lane, c0);
+    for (int t0 = 0; t0 < T; t0 += 2 * kTb) {
+        if (t0 + kTb < T) b1.load(a, v, bh, t0 + kTb, lane, c0);
+        asm volatile("" ::: "memory");   // the next block's loads issue before this block's steps
+        step(b0, t0);
+        if (t0 + kTb >= T) break;
+        if (t0 + 2 * kTb < T) b0.load(a, v, bh, t0 + 2 * kTb, lane, c0);
+        asm volatile("" ::: "memory");
+        step(b1, t0 + kTb);
     }
-    put(T);
 }
 
 // ---------------------------------------------------------------------------
 // bwd_sweep: the reverse sweep over the tokens of 4 value columns
 // ---------------------------------------------------------------------------
+// the inputs of the tokens kTb k .. kTb k + kTb - 1 of checkpoint block k
+// (rows clamped into [0, T)): features, step scalars, r_t, do_t, and the
+// checkpointed state before the block; the states inside the block are
+// rebuilt from it, S_t = gamma_t S_{t-1} + eta_t x_t r_t^T
+template <class E, int RPL>
+struct RevBlock {
+    float x[kTb][RPL], q[kTb][RPL], res[kTb][kCpw], o[kTb][kCpw], eta[kTb], gam[kTb];
+    float4 ck[RPL];
+    __device__ __forceinline__ void load(const BwdArgs &a, const E *dO, int bh, int g, int k, int lane, int c0) {
+        const int T = a.T, dk = a.dk, dv = a.dv;
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) ck[r] = ld_row<RPL>(state_at(a, bh, k, g), lane, r, dk);
+#pragma unroll
+        for (int u = 0; u < kTb; ++u) {
+            const int t = kTb * k + u < T ? kTb * k + u : T - 1;
+            const size_t row = size_t(bh) * T + t;
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) {
+                const int i = lane + 64 * r;
+                x[u][r] = i < dk ? a.xn[row * dk + i] : 0.f;
+                q[u][r] = i < dk ? a.qn[row * dk + i] : 0.f;
+            }
+            const float4 rr = *reinterpret_cast<const float4 *>(a.res + row * dv + c0);
+            res[u][0] = rr.x;
+            res[u][1] = rr.y;
+            res[u][2] = rr.z;
+            res[u][3] = rr.w;
+#pragma unroll
+            for (int c = 0; c < kCpw; ++c) o[u][c] = ld(dO, row * dv + c0 + c);
+            eta[u] = a.eta[row];
+            gam[u] = 1.f - a.alpha[row];
+        }
+    }
+};
+
 template <class E, int RPL, int RW>
 __global__ __launch_bounds__(256) void bwd_sweep(BwdArgs a) {
     auto rsum = [](float v) { return group_sum<RW>(v); };
@@ -128,7 +186,6 @@ __global__ __launch_bounds__(256) void bwd_sweep(BwdArgs a) {
     const int bh = gw / groups, g = gw % groups, c0 = g * kCpw;
     const int dk = a.dk, dv = a.dv, T = a.T;
     const int PF = bwd_part_floats(dk);
-    const E *v = static_cast<const E *>(a.v);
     const E *dO = static_cast<const E *>(a.d_o);
     E *dV = static_cast<E *>(a.d_v);
 
@@ -140,37 +197,26 @@ __global__ __launch_bounds__(256) void bwd_sweep(BwdArgs a) {
         for (int c = 0; c < kCpw; ++c)
             G[r][c] = (a.d_S_out && i < dk) ? a.d_S_out[(size_t(bh) * dk + i) * dv + c0 + c] : 0.f;
     }
-
-    for (int tb = T - 1; tb >= 0; tb -= kTb) {
-        // inputs of tokens tb, tb - 1, .. (rows clamped at 0)
-        float xb[kTb][RPL], qb[kTb][RPL], yb[kTb][kCpw], ob[kTb][kCpw], eb[kTb], gb[kTb];
-        float4 sp[kTb][RPL], sn[kTb][RPL];
+    auto step = [&](const RevBlock<E, RPL> &b, int k) {
+        // the block's states: sb[u] = S before token kTb k + u, sb[kTb] after its last token
+        float4 sb[kTb + 1][RPL];
 #pragma unroll
-        for (int u = 0; u < kTb; ++u) {
-            const int t = tb - u >= 0 ? tb - u : 0;
-            const size_t row = size_t(bh) * T + t;
+        for (int r = 0; r < RPL; ++r) sb[0][r] = b.ck[r];
+#pragma unroll
+        for (int u = 0; u < kTb; ++u)
 #pragma unroll
             for (int r = 0; r < RPL; ++r) {
-                const int i = lane + 64 * r;
-                xb[u][r] = i < dk ? a.xn[row * dk + i] : 0.f;
-                qb[u][r] = i < dk ? a.qn[row * dk + i] : 0.f;
-                sp[u][r] = ld_row<RPL>(state_at(a, bh, t, g), lane, r, dk);
-                sn[u][r] = ld_row<RPL>(state_at(a, bh, t + 1, g), lane, r, dk);
+                const float ex = b.eta[u] * b.x[u][r], gm = b.gam[u];
+                sb[u + 1][r] = make_float4(gm * sb[u][r].x + ex * b.res[u][0], gm * sb[u][r].y + ex * b.res[u][1],
+                                           gm * sb[u][r].z + ex * b.res[u][2], gm * sb[u][r].w + ex * b.res[u][3]);
             }
 #pragma unroll
-            for (int c = 0; c < kCpw; ++c) {
-                yb[u][c] = ld(v, row * dv + c0 + c);
-                ob[u][c] = ld(dO, row * dv + c0 + c);
-            }
-            eb[u] = a.eta[row];
-            gb[u] = 1.f - a.alpha[row];
-        }
-#pragma unroll
-        for (int u = 0; u < kTb; ++u) {
-            const int t = tb - u;
-            if (t < 0) break;
+        for (int u = kTb - 1; u >= 0; --u) {
+            const int t = kTb * k + u;
+            if (t >= T) continue;
             const size_t row = size_t(bh) * T + t;
-            const float eta = eb[u], gam = gb[u];
+            const float eta = b.eta[u], gam = b.gam[u];
+            const float4 *sp = sb[u], *sn = sb[u + 1];   // S_{t-1}, S_t
             // read after write: G_t += qh_t do_t^T, dqh_t = S_t do_t
             float dq[RPL];
 #pragma unroll
@@ -178,28 +224,26 @@ __global__ __launch_bounds__(256) void bwd_sweep(BwdArgs a) {
                 dq[r] = 0.f;
 #pragma unroll
                 for (int c = 0; c < kCpw; ++c) {
-                    G[r][c] += qb[u][r] * ob[u][c];
-                    dq[r] += col(sn[u][r], c) * ob[u][c];
+                    G[r][c] += b.q[u][r] * b.o[u][c];
+                    dq[r] += col(sn[r], c) * b.o[u][c];
                 }
             }
-            // w = G^T x, r = y - S_{t-1}^T x, dgamma = <G, S_{t-1}>
-            float w[kCpw], res[kCpw], gs = 0.f;
+            // w = G^T x, dgamma = <G, S_{t-1}>
+            float w[kCpw], gs = 0.f;
 #pragma unroll
             for (int c = 0; c < kCpw; ++c) {
-                float sw = 0.f, sx = 0.f;
+                float sw = 0.f;
 #pragma unroll
                 for (int r = 0; r < RPL; ++r) {
-                    sw += G[r][c] * xb[u][r];
-                    sx += col(sp[u][r], c) * xb[u][r];
-                    gs += G[r][c] * col(sp[u][r], c);
+                    sw += G[r][c] * b.x[u][r];
+                    gs += G[r][c] * col(sp[r], c);
                 }
                 w[c] = rsum(sw);
-                res[c] = yb[u][c] - rsum(sx);
             }
             const float dgam = rsum(gs);
             float deta = 0.f;
 #pragma unroll
-            for (int c = 0; c < kCpw; ++c) deta += w[c] * res[c];
+            for (int c = 0; c < kCpw; ++c) deta += w[c] * b.res[u][c];
             // dv_t = eta w (this group's columns, lanes 0..3)
             if (lane < kCpw) {
                 const float wl = lane == 0 ? w[0] : lane == 1 ? w[1] : lane == 2 ? w[2] : w[3];
@@ -211,10 +255,10 @@ __global__ __launch_bounds__(256) void bwd_sweep(BwdArgs a) {
             for (int r = 0; r < RPL; ++r) {
                 float s = 0.f;
 #pragma unroll
-                for (int c = 0; c < kCpw; ++c) s += G[r][c] * res[c] - col(sp[u][r], c) * w[c];
+                for (int c = 0; c < kCpw; ++c) s += G[r][c] * b.res[u][c] - col(sp[r], c) * w[c];
                 dx[r] = eta * s;
 #pragma unroll
-                for (int c = 0; c < kCpw; ++c) G[r][c] = gam * G[r][c] - eta * xb[u][r] * w[c];
+                for (int c = 0; c < kCpw; ++c) G[r][c] = gam * G[r][c] - eta * b.x[u][r] * w[c];
             }
             float *P = a.part + (row * groups + g) * PF;
             if (lane == 0) {
@@ -230,6 +274,20 @@ __global__ __launch_bounds__(256) void bwd_sweep(BwdArgs a) {
                 }
             }
         }
+    };
+    // checkpoint blocks from the last; two input sets alternate so that the
+    // next block's loads are in flight while a block computes
+    RevBlock<E, RPL> b0, b1;
+    const int nck = int(bwd_checkpoints(T));
+    if (nck > 0) b0.load(a, dO, bh, g, nck - 1, lane, c0);
+    for (int k = nck - 1; k >= 0; k -= 2) {
+        if (k - 1 >= 0) b1.load(a, dO, bh, g, k - 1, lane, c0);
+        asm volatile("" ::: "memory");   // the next block's loads issue before this block's steps
+        step(b0, k);
+        if (k - 1 < 0) break;
+        if (k - 2 >= 0) b0.load(a, dO, bh, g, k - 2, lane, c0);
+        asm volatile("" ::: "memory");
+        step(b1, k - 1);
     }
     if (a.d_S_in) {
 #pragma unroll
@@ -490,6 +548,7 @@ int run_bwd(const falcon_bwd_args *args, void *stream, falcon::Marks &m) {
     ba.eta = p.ws_at<float>(p.off_eta);
     ba.alpha = p.ws_at<float>(p.off_alpha);
     ba.states = p.ws_at<float>(p.off_states);
+    ba.res = p.ws_at<float>(p.off_res);
     ba.part = p.ws_at<float>(p.off_part);
     ba.d_q = args->d_q;
     ba.d_k = args->d_k;

@@ -75,8 +75,9 @@ int cu_count();
 bool sync_check_enabled();
 
 // Falcon-1 backward (token-recurrent): fp32 features and step scalars from
-// the feature pass, the states S_0 .. S_T [BH][T+1][d_v/4][d_k][4], and the
-// partial sums of the reverse sweep [BH][T][d_v/4][bwd_part_floats(d_k)]
+// the feature pass, the states before tokens 0, 4, 8, ..
+// [BH][ceil(T/4)][d_v/4][d_k][4], the residuals, and the partial sums of the
+// reverse sweep [BH][T][d_v/4][bwd_part_floats(d_k)]
 struct BwdArgs {
     int phi, BH, T, dk, dv, fresh;
     float eps, eps_gamma, eps_rms;
@@ -84,7 +85,7 @@ struct BwdArgs {
     const float *beta, *lambda;
     const float *S_in, *d_S_out, *d_x_next_out;
     const float *xn, *qn, *eta, *alpha;   // [BH, T, d_k], [BH, T]
-    float *states, *part;
+    float *states, *res, *part;             // res: r_t = y_t - S_{t-1}^T x_t [BH][T][d_v]
     void *d_q, *d_k, *d_v;                // io dtype
     float *d_beta, *d_lambda, *d_S_in, *d_x_next_in;
 };

@@ -67,14 +67,14 @@ struct Plan {
 int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers);
 
 // Plan of one falcon_bwd call: sizes, the state in, and the workspace
-// carve-up (features and step scalars, every pre-step state, per-group
-// partial sums of the reverse sweep).
+// carve-up (features and step scalars, checkpointed states, the residuals,
+// per-group partial sums of the reverse sweep).
 struct BwdPlan {
     int dtype = 0, phi = 0, BH = 0, T = 0, dk = 0, dv = 0;
     float eps = 0.f, eps_gamma = 0.f, eps_rms = 0.f;
     bool fresh = true;
     const float *S_in = nullptr, *xnext_in = nullptr;
-    size_t off_xn = 0, off_qn = 0, off_eta = 0, off_alpha = 0, off_states = 0, off_part = 0;
+    size_t off_xn = 0, off_qn = 0, off_eta = 0, off_alpha = 0, off_states = 0, off_res = 0, off_part = 0;
     size_t ws_bytes = 0;
     void *ws = nullptr;
     template <class T>
@@ -84,6 +84,10 @@ struct BwdPlan {
 // floats per (head, token, group of 4 value columns) record of the reverse
 // sweep's partial sums: dgamma, deta, two pad words, dx [d_k], dqh [d_k]
 constexpr int bwd_part_floats(int dk) { return 4 + 2 * dk; }
+// the state pass keeps the state before every kBwdCheckpoint-th token; the
+// sweep rebuilds the states in between from the stored residuals
+constexpr int kBwdCheckpoint = 4;
+constexpr long long bwd_checkpoints(long long T) { return (T + kBwdCheckpoint - 1) / kBwdCheckpoint; }
 
 int build_bwd_plan(const falcon_bwd_args *a, BwdPlan *p, bool check_pointers);
 

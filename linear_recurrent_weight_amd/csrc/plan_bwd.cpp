@@ -60,15 +60,17 @@ int build_bwd_plan(const falcon_bwd_args *a, BwdPlan *p, bool check_pointers) {
     p->eps_gamma = a->eps_gamma;
     p->eps_rms = a->eps_rms;
 
-    // workspace: fp32 features and step scalars, the states S_0 .. S_T, and
-    // the partial sums of the reverse sweep
+    // workspace: fp32 features and step scalars, the states before every
+    // kBwdCheckpoint-th token, the residuals r_t, and the partial sums of the
+    // reverse sweep
     const size_t T = static_cast<size_t>(a->seqlen), ub = static_cast<size_t>(bh);
     size_t off = 0;
     p->off_xn = off; off = align_up(off + ub * T * a->dk * 4);
     p->off_qn = off; off = align_up(off + ub * T * a->dk * 4);
     p->off_eta = off; off = align_up(off + ub * T * 4);
     p->off_alpha = off; off = align_up(off + ub * T * 4);
-    p->off_states = off; off = align_up(off + ub * (T + 1) * a->dk * a->dv * 4);
+    p->off_states = off; off = align_up(off + ub * bwd_checkpoints(a->seqlen) * a->dk * a->dv * 4);
+    p->off_res = off; off = align_up(off + ub * T * a->dv * 4);   // residuals r_t
     p->off_part = off; off = align_up(off + ub * T * (a->dv / 4) * bwd_part_floats(a->dk) * 4);
     p->ws_bytes = off;
 
