@@ -9,13 +9,14 @@
 // layout: one wavefront per (head, group of 4 value columns), lane l holding
 // rows l (and l + 64) of those columns.  The gradients that sum over the
 // columns (dgamma_t = <G_t, S_{t-1}>, deta_t = w_t . r_t, dx_t = eta_t (G_t
-// r_t - S_{t-1} w_t), dqh_t = S_t do_t) leave each wavefront as per-group
-// partial sums and are added up per token afterwards, in a fixed order.
+// r_t - S_{t-1} w_t), dqh_t = S_t do_t) are added up over the four waves of a
+// workgroup in LDS, leave it as partial sums per 16 columns, and are added
+// up per token afterwards; every sum runs in a fixed order.
 //   feature     (the forward's feature pass) x_t, qh_t, eta_t, alpha_t;
 //   bwd_states  the forward recurrence again, keeping the state before every
 //               4th token and each token's residual r_t;
 //   bwd_sweep   the reverse sweep: dv_t, the partial sums, and dS_0;
-//   bwd_reduce  per token: the sums over groups, the decay and step chain
+//   bwd_reduce  per token: the sums of the records, the decay and step chain
 //               (clamp-gated, zero steps masked, the fresh first step a
 //               boundary constant), phi's vector-Jacobian products for q_t
 //               and k_{t-1}, and the carried feature's gradient.
@@ -179,13 +180,17 @@ struct RevBlock {
 template <class E, int RPL, int RW>
 __global__ __launch_bounds__(256) void bwd_sweep(BwdArgs a) {
     auto rsum = [](float v) { return group_sum<RW>(v); };
-    const int lane = threadIdx.x & 63;
-    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int groups = a.dv / kCpw;
-    if (gw >= a.BH * groups) return;
+    constexpr int PFM = bwd_part_floats(64 * RPL);   // record size at the largest d_k of this shape
+    // the four waves' partial sums of a block of tokens, by block parity
+    __shared__ float red[2][4][kTb][PFM];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int gw = blockIdx.x * 4 + wave;
+    const int groups = a.dv / kCpw;   // a multiple of 4: the grid's waves fill it exactly,
+                                      // and the four waves of a workgroup share one head
     const int bh = gw / groups, g = gw % groups, c0 = g * kCpw;
     const int dk = a.dk, dv = a.dv, T = a.T;
     const int PF = bwd_part_floats(dk);
+    const int ngp = groups / 4, gp = g / 4;   // records per token; this workgroup's record
     const E *dO = static_cast<const E *>(a.d_o);
     E *dV = static_cast<E *>(a.d_v);
 
@@ -260,7 +265,7 @@ __global__ __launch_bounds__(256) void bwd_sweep(BwdArgs a) {
 #pragma unroll
                 for (int c = 0; c < kCpw; ++c) G[r][c] = gam * G[r][c] - eta * b.x[u][r] * w[c];
             }
-            float *P = a.part + (row * groups + g) * PF;
+            float *P = red[k & 1][wave][u];
             if (lane == 0) {
                 P[0] = dgam;
                 P[1] = deta;
@@ -273,6 +278,17 @@ __global__ __launch_bounds__(256) void bwd_sweep(BwdArgs a) {
                     P[4 + dk + i] = dq[r];
                 }
             }
+        }
+        // the four waves' sums of the block, in wave order, to this
+        // workgroup's record; the other parity's buffer is rewritten only
+        // after the next block's barrier, which every wave passes after
+        // finishing these sums
+        __syncthreads();
+        for (int idx = tid; idx < kTb * PF; idx += 256) {
+            const int u = idx / PF, e = idx % PF, t = kTb * k + u;
+            if (t >= T) continue;
+            const float v = ((red[k & 1][0][u][e] + red[k & 1][1][u][e]) + red[k & 1][2][u][e]) + red[k & 1][3][u][e];
+            a.part[((size_t(bh) * T + t) * ngp + gp) * PF + e] = v;
         }
     };
     // checkpoint blocks from the last; two input sets alternate so that the
@@ -340,20 +356,20 @@ __global__ __launch_bounds__(256) void bwd_reduce(BwdArgs a) {
     const int T = a.T, dk = a.dk;
     if (id >= a.BH * T) return;
     const int bh = id / T, t = id % T;
-    const int groups = a.dv / kCpw, PF = bwd_part_floats(dk);
+    const int ngp = a.dv / (4 * kCpw), PF = bwd_part_floats(dk);   // records per token
     const size_t row = size_t(bh) * T + t;
-    const float *P = a.part + row * groups * PF;
+    const float *P = a.part + row * ngp * PF;
     const E *q = static_cast<const E *>(a.q);
     const E *k = static_cast<const E *>(a.k);
 
-    // sums over the column groups, in group order
+    // sums over the records, in order
     float dx[RPL], dqh[RPL], x[RPL];
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
         const int i = lane + 64 * r;
         float sx = 0.f, sq = 0.f;
         if (i < dk)
-            for (int gi = 0; gi < groups; ++gi) {
+            for (int gi = 0; gi < ngp; ++gi) {
                 sx += P[gi * PF + 4 + i];
                 sq += P[gi * PF + 4 + dk + i];
             }
@@ -362,7 +378,7 @@ __global__ __launch_bounds__(256) void bwd_reduce(BwdArgs a) {
         x[r] = i < dk ? a.xn[row * dk + i] : 0.f;
     }
     float dgam = 0.f, deta = 0.f;
-    for (int gi = 0; gi < groups; ++gi) {
+    for (int gi = 0; gi < ngp; ++gi) {
         dgam += P[gi * PF + 0];
         deta += P[gi * PF + 1];
     }

@@ -77,7 +77,7 @@ bool sync_check_enabled();
 // Falcon-1 backward (token-recurrent): fp32 features and step scalars from
 // the feature pass, the states before tokens 0, 4, 8, ..
 // [BH][ceil(T/4)][d_v/4][d_k][4], the residuals, and the partial sums of the
-// reverse sweep [BH][T][d_v/4][bwd_part_floats(d_k)]
+// reverse sweep [BH][T][d_v/16][bwd_part_floats(d_k)]
 struct BwdArgs {
     int phi, BH, T, dk, dv, fresh;
     float eps, eps_gamma, eps_rms;

@@ -81,7 +81,7 @@ struct BwdPlan {
     T *ws_at(size_t off) const { return reinterpret_cast<T *>(static_cast<char *>(ws) + off); }
 };
 
-// floats per (head, token, group of 4 value columns) record of the reverse
+// floats per (head, token, group of 16 value columns) record of the reverse
 // sweep's partial sums: dgamma, deta, two pad words, dx [d_k], dqh [d_k]
 constexpr int bwd_part_floats(int dk) { return 4 + 2 * dk; }
 // the state pass keeps the state before every kBwdCheckpoint-th token; the

@@ -71,7 +71,7 @@ int build_bwd_plan(const falcon_bwd_args *a, BwdPlan *p, bool check_pointers) {
     p->off_alpha = off; off = align_up(off + ub * T * 4);
     p->off_states = off; off = align_up(off + ub * bwd_checkpoints(a->seqlen) * a->dk * a->dv * 4);
     p->off_res = off; off = align_up(off + ub * T * a->dv * 4);   // residuals r_t
-    p->off_part = off; off = align_up(off + ub * T * (a->dv / 4) * bwd_part_floats(a->dk) * 4);
+    p->off_part = off; off = align_up(off + ub * T * (a->dv / 16) * bwd_part_floats(a->dk) * 4);
     p->ws_bytes = off;
 
     if (!check_pointers) return FALCON_OK;

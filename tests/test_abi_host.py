@@ -400,13 +400,13 @@ def bwd_validate(lib, a):
 def test_bwd_workspace_layout(lib):
     """fp32 features and step scalars, the state before every 4th token of
     every head, the residuals r_t (d_v per token), and the sweep's partial
-    sums (4 + 2 d_k floats per token and group of 4 value columns), each
+    sums (4 + 2 d_k floats per token and group of 16 value columns), each
     256-byte aligned."""
     align = lambda n: -(-n // 256) * 256
     for B, H, T, dk, dv in [(2, 3, 100, 64, 64), (1, 1, 7, 16, 128), (3, 2, 0, 128, 16)]:
         bh = B * H
         want = (2 * align(bh * T * dk * 4) + 2 * align(bh * T * 4) + align(bh * -(-T // 4) * dk * dv * 4)
-                + align(bh * T * dv * 4) + align(bh * T * (dv // 4) * (4 + 2 * dk) * 4))
+                + align(bh * T * dv * 4) + align(bh * T * (dv // 16) * (4 + 2 * dk) * 4))
         assert bwd_wsize(lib, bargs(batch=B, heads=H, seqlen=T, dk=dk, dv=dv)) == want
 
 
