@@ -622,6 +622,13 @@ def bwd_main(args, w, inp, prof_name) -> int:
         if rc != 0:
             raise fb.FalconError(rc, lib)
 
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
