@@ -371,6 +371,7 @@ def make_set(w, inp, dev, dt, fb, lib, ws=None):
 
 
 LLC_BYTES = 256 << 20   # MI355X last-level (Infinity) cache
+MAX_SETS = 256          # at most this many resident input sets (a tiny workload stays in the cache)
 
 
 def main() -> int:
@@ -433,7 +434,7 @@ def main() -> int:
     # find them in the last-level cache (more than twice its size together);
     # one workspace serves every set
     sets = [make_set(w, inp, dev, dt, fb, lib)]
-    while len(sets) * sets[0]["bytes"] <= 2 * LLC_BYTES:
+    while len(sets) * sets[0]["bytes"] <= 2 * LLC_BYTES and len(sets) < MAX_SETS:
         sets.append(make_set(w, inp, dev, dt, fb, lib, ws=sets[0]["ws"]))
     stream = torch.cuda.current_stream(dev)
     sh = ctypes.c_void_p(stream.cuda_stream)
@@ -611,7 +612,7 @@ def bwd_main(args, w, inp, prof_name) -> int:
         return t
 
     sets = [make_bwd_set()]
-    while len(sets) * sets[0]["bytes"] <= 2 * LLC_BYTES:
+    while len(sets) * sets[0]["bytes"] <= 2 * LLC_BYTES and len(sets) < MAX_SETS:
         sets.append(make_bwd_set())
     stream = torch.cuda.current_stream(dev)
     sh = ctypes.c_void_p(stream.cuda_stream)
