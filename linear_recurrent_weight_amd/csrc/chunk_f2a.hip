@@ -83,7 +83,12 @@ template <class E, int DK, int DS>
 __global__ __launch_bounds__(NT) void chunk_f2a_kernel(ChunkF2Args a, int nslice) {
     using Sh = F2aShared<E, DK, DS>;
     __shared__ __align__(16) Sh sh;
-    const int bh = blockIdx.x / nslice, j0 = (blockIdx.x % nslice) * DS;
+    // workgroup -> (head, slice): the slices of a head share an XCD (block
+    // ids 8 apart), so they read the head's rows through one L2
+    const int id = blockIdx.x, u8 = id & 7, rest = id >> 3;
+    const int sl = rest % nslice, bh = (rest / nslice) * 8 + u8;
+    if (bh >= a.BH) return;   // the whole workgroup leaves together
+    const int j0 = sl * DS;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int T = a.T, DV = a.dv;
     const E *qg = static_cast<const E *>(a.q) + size_t(bh) * T * DK;
@@ -294,7 +299,7 @@ __global__ __launch_bounds__(NT) void chunk_f2a_kernel(ChunkF2Args a, int nslice
             const int d = i / DS, j = i % DS;
             a.S_out[(size_t(bh) * DK + d) * DV + j0 + j] = sh.Sf[d][j];
         }
-    if (blockIdx.x % nslice == 0 && wave == 0 && a.xnext_out) {   // phi(k_{T-1})
+    if (sl == 0 && wave == 0 && a.xnext_out) {   // phi(k_{T-1})
         const float xv = lane < DK ? ld(kg, size_t(T - 1) * DK + lane) : 0.f;
         const float sc = phi_scale(wave_sum(xv * xv), DK, a.eps_rms, a.phi);
         if (lane < DK) a.xnext_out[size_t(bh) * DK + lane] = xv * sc;
@@ -308,7 +313,7 @@ void launch_f2a_dk(const ChunkF2Args &a, hipStream_t s) {
     // the head's shared features and scores again (its rows come from L2)
     const int ds = (a.dv < 32 || static_cast<long long>(a.BH) * (a.dv / 32) < 256) ? 16 : 32;
     const int nslice = a.dv / ds;
-    const dim3 grid(a.BH * nslice);
+    const dim3 grid(((a.BH + 7) / 8) * 8 * nslice);
     if (ds == 16) chunk_f2a_kernel<E, DK, 16><<<grid, NT, 0, s>>>(a, nslice);
     else chunk_f2a_kernel<E, DK, 32><<<grid, NT, 0, s>>>(a, nslice);
 }
