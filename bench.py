@@ -7,7 +7,7 @@ workload is Falcon-1, batch 8, 12 heads, T = 1024, d_k = d_v = 64, C = 64,
 bf16 inputs and fp32 state.  Inputs are resident in HBM before timing.
 
 Prints one JSON line (see the keys below).  `--gpus N` with N > 1 exits:
-this build runs on one GPU only.  `--backward` times the Falcon-1 backward
+this library runs on one GPU only.  `--backward` times the Falcon-1 backward
 pass (falcon_bwd) on the workload instead, with its own metric.
 """
 from __future__ import annotations
@@ -409,7 +409,7 @@ def main() -> int:
         print(path)
         return 0
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this library runs on one GPU only; --gpus must be 1"}))
         return 2
 
     import numpy as np
