@@ -74,6 +74,8 @@ KERNEL_SOURCES = {"passthrough": "feature.hip", "feature": "feature.hip", "recur
                   "f1_xfer": "chunk_f1_xfer.hip", "f1_carry": "chunk_f1_xfer.hip",
                   "f1_segmap": "chunk_f1_xfer.hip", "f1_segscan": "chunk_f1_xfer.hip",
                   "bwd_states": "falcon_bwd.hip", "bwd_sweep": "falcon_bwd.hip", "bwd_reduce": "falcon_bwd.hip",
+                  "bwd_ops": "bwd_chunk.hip", "bwd_carry_fwd": "bwd_chunk.hip", "bwd_carry_rev": "bwd_chunk.hip",
+                  "bwd_grads": "bwd_chunk.hip",
                   "a_segment": "chunk_a.hip", "a_segscan": "chunk_a.hip", "a_output": "chunk_a.hip",
                   "a1_segment": "chunk_a1.hip", "a1_segscan": "chunk_a1.hip", "a1_output": "chunk_a1.hip",
                   "a3_window": "chunk_a1.hip"}

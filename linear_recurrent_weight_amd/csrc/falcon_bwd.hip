@@ -502,6 +502,7 @@ void launch_bwd(const BwdArgs &a, bool io_bf16, hipStream_t s, Marks *m) {
 namespace {
 
 const char *const kNamesBwd[] = {"feature", "bwd_states", "bwd_sweep", "bwd_reduce"};
+const char *const kNamesBwdChunk[] = {"bwd_ops", "bwd_carry_fwd", "bwd_carry_rev", "bwd_grads"};
 const char *const kNamesBwdEmpty[] = {"bwd_states", "bwd_sweep"};
 
 // returns the number of kernels launched, or a negative status
@@ -514,7 +515,7 @@ int run_bwd(const falcon_bwd_args *args, void *stream, falcon::Marks &m) {
     m.sync_check = sync_check_enabled();
     m.mark(s);
     const bool bf16 = p.dtype == FALCON_BF16;
-    if (p.T > 0) {
+    if (p.T > 0 && !p.chunked) {
         FeatureArgs fa{};
         fa.variant = FALCON_V1;
         fa.phi = p.phi;
@@ -573,7 +574,17 @@ int run_bwd(const falcon_bwd_args *args, void *stream, falcon::Marks &m) {
     ba.d_lambda = args->d_lambda;
     ba.d_S_in = args->d_S_in;
     ba.d_x_next_in = args->d_x_next_in;
-    launch_bwd(ba, bf16, s, &m);
+    if (p.chunked) {
+        ba.nchunks = p.nchunks;
+        ba.xnext_in = p.xnext_in;
+        ba.ops = p.ws_at<float>(p.off_ops);
+        ba.cst = p.ws_at<float>(p.off_cst);
+        ba.hg = p.ws_at<float>(p.off_hg);
+        ba.phip = p.ws_at<float>(p.off_phip);
+        launch_bwd_chunk(ba, bf16, s, &m);
+    } else {
+        launch_bwd(ba, bf16, s, &m);
+    }
     if (m.failed_at >= 0) {
         std::fprintf(stderr, "falcon_bwd: FALCON_SYNC_CHECK: kernel %d of the call failed\n", m.failed_at);
         return FALCON_ERR_HIP;
@@ -602,5 +613,6 @@ extern "C" const char *falcon_bwd_kernel_name(const falcon_bwd_args *args, int i
     falcon::BwdPlan p;
     if (falcon::build_bwd_plan(args, &p, false) != FALCON_OK || i < 0) return nullptr;
     if (p.T == 0) return i < 2 ? kNamesBwdEmpty[i] : nullptr;
+    if (p.chunked) return i < 4 ? kNamesBwdChunk[i] : nullptr;
     return i < 4 ? kNamesBwd[i] : nullptr;
 }

@@ -88,6 +88,13 @@ struct BwdArgs {
     float *states, *res, *part;             // res: r_t = y_t - S_{t-1}^T x_t [BH][T][d_v]
     void *d_q, *d_k, *d_v;                // io dtype
     float *d_beta, *d_lambda, *d_S_in, *d_x_next_in;
+    // chunk-parallel form
+    int nchunks;
+    const float *xnext_in;                // carried feature (nullptr when fresh)
+    float *ops;                           // [BH][nchunks] records: A [d_k][d_k], B, G^T dO [d_k][d_v]
+    float *cst;                           // [BH][nchunks + 1][d_k][d_v] chunk entry states, then S_T
+    float *hg;                            // [BH][nchunks][d_k][d_v] dL/dS at each chunk's end
+    float *phip;                          // [BH][nchunks][d_v / 16] <H, S_end> per 16 value columns
 };
 
 struct ChunkAArgs {
@@ -177,5 +184,6 @@ void launch_chunk_f3(const ChunkF3Args &a, bool bf16, hipStream_t s, Marks *m);
 void launch_chunk_f1_xfer(const F1XferArgs &a, int slice, hipStream_t s, Marks *m);
 // Falcon-1 backward after the feature pass: states, reverse sweep, reduction
 void launch_bwd(const BwdArgs &a, bool io_bf16, hipStream_t s, Marks *m);
+void launch_bwd_chunk(const BwdArgs &a, bool io_bf16, hipStream_t s, Marks *m);
 
 }  // namespace falcon

@@ -74,12 +74,21 @@ struct BwdPlan {
     float eps = 0.f, eps_gamma = 0.f, eps_rms = 0.f;
     bool fresh = true;
     const float *S_in = nullptr, *xnext_in = nullptr;
+    // chunk-parallel form (T > 0, d_k and d_v at most 64): 64-token chunks
+    bool chunked = false;
+    int nchunks = 0;
+    size_t off_ops = 0, off_cst = 0, off_hg = 0, off_phip = 0;
+    // token-recurrent form (the other shapes)
     size_t off_xn = 0, off_qn = 0, off_eta = 0, off_alpha = 0, off_states = 0, off_res = 0, off_part = 0;
     size_t ws_bytes = 0;
     void *ws = nullptr;
     template <class T>
     T *ws_at(size_t off) const { return reinterpret_cast<T *>(static_cast<char *>(ws) + off); }
 };
+
+// tokens per chunk of the chunk-parallel backward
+constexpr int kBwdChunk = 64;
+constexpr bool bwd_chunked(long long T, int dk, int dv) { return T > 0 && dk <= 64 && dv <= 64; }
 
 // floats per (head, token, group of 16 value columns) record of the reverse
 // sweep's partial sums: dgamma, deta, two pad words, dx [d_k], dqh [d_k]

@@ -60,18 +60,32 @@ int build_bwd_plan(const falcon_bwd_args *a, BwdPlan *p, bool check_pointers) {
     p->eps_gamma = a->eps_gamma;
     p->eps_rms = a->eps_rms;
 
-    // workspace: fp32 features and step scalars, the states before every
-    // kBwdCheckpoint-th token, the residuals r_t, and the partial sums of the
-    // reverse sweep
     const size_t T = static_cast<size_t>(a->seqlen), ub = static_cast<size_t>(bh);
+    const size_t dk = static_cast<size_t>(a->dk), dv = static_cast<size_t>(a->dv);
     size_t off = 0;
-    p->off_xn = off; off = align_up(off + ub * T * a->dk * 4);
-    p->off_qn = off; off = align_up(off + ub * T * a->dk * 4);
-    p->off_eta = off; off = align_up(off + ub * T * 4);
-    p->off_alpha = off; off = align_up(off + ub * T * 4);
-    p->off_states = off; off = align_up(off + ub * bwd_checkpoints(a->seqlen) * a->dk * a->dv * 4);
-    p->off_res = off; off = align_up(off + ub * T * a->dv * 4);   // residuals r_t
-    p->off_part = off; off = align_up(off + ub * T * (a->dv / 16) * bwd_part_floats(a->dk) * 4);
+    p->chunked = bwd_chunked(a->seqlen, a->dk, a->dv);
+    if (p->chunked) {
+        // workspace: per chunk the records A [d_k][d_k], B and G^T dO
+        // [d_k][d_v]; the entry state of every chunk and S_T; the state
+        // gradient at every chunk's end; <H, S_end> per 16 value columns
+        const size_t nck = (T + kBwdChunk - 1) / kBwdChunk;
+        p->nchunks = static_cast<int>(nck);
+        p->off_ops = off; off = align_up(off + ub * nck * (dk * dk + 2 * dk * dv) * 4);
+        p->off_cst = off; off = align_up(off + ub * (nck + 1) * dk * dv * 4);
+        p->off_hg = off; off = align_up(off + ub * nck * dk * dv * 4);
+        p->off_phip = off; off = align_up(off + ub * nck * (dv / 16) * 4);
+    } else {
+        // workspace: fp32 features and step scalars, the states before every
+        // kBwdCheckpoint-th token, the residuals r_t, and the partial sums of
+        // the reverse sweep
+        p->off_xn = off; off = align_up(off + ub * T * dk * 4);
+        p->off_qn = off; off = align_up(off + ub * T * dk * 4);
+        p->off_eta = off; off = align_up(off + ub * T * 4);
+        p->off_alpha = off; off = align_up(off + ub * T * 4);
+        p->off_states = off; off = align_up(off + ub * bwd_checkpoints(a->seqlen) * dk * dv * 4);
+        p->off_res = off; off = align_up(off + ub * T * dv * 4);   // residuals r_t
+        p->off_part = off; off = align_up(off + ub * T * (dv / 16) * bwd_part_floats(a->dk) * 4);
+    }
     p->ws_bytes = off;
 
     if (!check_pointers) return FALCON_OK;

@@ -398,12 +398,21 @@ def bwd_validate(lib, a):
 
 
 def test_bwd_workspace_layout(lib):
-    """fp32 features and step scalars, the state before every 4th token of
-    every head, the residuals r_t (d_v per token), and the sweep's partial
-    sums (4 + 2 d_k floats per token and group of 16 value columns), each
-    256-byte aligned."""
+    """Chunk-parallel form (T > 0, d_k and d_v at most 64): per 64-token
+    chunk an fp32 record of A [d_k][d_k], B and G^T dO [d_k][d_v]; the entry
+    state of every chunk plus S_T; the state gradient at every chunk's end;
+    one float per chunk and 16 value columns.  Token-recurrent form (the other
+    shapes): fp32 features and step scalars, the state before every 4th token
+    of every head, the residuals r_t (d_v per token), and the sweep's partial
+    sums (4 + 2 d_k floats per token and group of 16 value columns).  Each
+    piece 256-byte aligned."""
     align = lambda n: -(-n // 256) * 256
-    for B, H, T, dk, dv in [(2, 3, 100, 64, 64), (1, 1, 7, 16, 128), (3, 2, 0, 128, 16)]:
+    for B, H, T, dk, dv in [(2, 3, 100, 64, 64), (1, 1, 7, 16, 32), (4, 3, 1024, 32, 64), (2, 1, 64, 64, 16)]:
+        bh, nck = B * H, -(-T // 64)
+        want = (align(bh * nck * (dk * dk + 2 * dk * dv) * 4) + align(bh * (nck + 1) * dk * dv * 4)
+                + align(bh * nck * dk * dv * 4) + align(bh * nck * (dv // 16) * 4))
+        assert bwd_wsize(lib, bargs(batch=B, heads=H, seqlen=T, dk=dk, dv=dv)) == want
+    for B, H, T, dk, dv in [(1, 1, 7, 16, 128), (3, 2, 0, 128, 16), (2, 2, 0, 64, 64), (1, 2, 90, 128, 128)]:
         bh = B * H
         want = (2 * align(bh * T * dk * 4) + 2 * align(bh * T * 4) + align(bh * -(-T // 4) * dk * dv * 4)
                 + align(bh * T * dv * 4) + align(bh * T * (dv // 16) * (4 + 2 * dk) * 4))
@@ -444,8 +453,10 @@ def test_bwd_kernel_names(lib):
         while (nm := lib.falcon_bwd_kernel_name(ctypes.byref(a), len(out))) is not None:
             out.append(nm.decode())
         return out
-    assert names(bargs()) == ["feature", "bwd_states", "bwd_sweep", "bwd_reduce"]
+    assert names(bargs()) == ["bwd_ops", "bwd_carry_fwd", "bwd_carry_rev", "bwd_grads"]
+    assert names(bargs(dk=128)) == ["feature", "bwd_states", "bwd_sweep", "bwd_reduce"]
+    assert names(bargs(dv=128)) == ["feature", "bwd_states", "bwd_sweep", "bwd_reduce"]
     assert names(bargs(seqlen=0)) == ["bwd_states", "bwd_sweep"]
     assert names(bargs(variant="F2")) == []
-    for nm in names(bargs()):
+    for nm in names(bargs()) + names(bargs(dk=128)):
         assert nm in (CSRC / KERNEL_SOURCES[nm]).read_text()

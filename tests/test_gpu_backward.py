@@ -115,6 +115,13 @@ def test_bwd_lengths(dtype, T):
     check(T, 2, 3, T, 64, 64, dtype)
 
 
+@pytest.mark.parametrize("T", [63, 64, 65, 128, 129, 300, 640])
+def test_bwd_chunk_boundaries(T):
+    """Lengths at and around the 64-token chunks of the chunk-parallel form
+    (one chunk, a full last chunk, a one-token tail, ten chunks)."""
+    check(100 + T, 1, 3, T, 64, 64, "f32", continued=True)
+
+
 @pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 32), (128, 16), (16, 128), (128, 128)])
 def test_bwd_head_dims(dk, dv):
     check(dk + dv, 1, 3, 40, dk, dv, "f32", continued=True)
