@@ -22,6 +22,7 @@ import time
 METRIC = "Falcon chunk-parallel fwd tokens/s (B*H*T) + % of bf16 MFMA / HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+F32_PEAK_TFLOPS = 157.3        # MI355X dense fp32 MFMA, vendor figure
 
 
 def algorithmic_bytes(w) -> int:
@@ -54,6 +55,17 @@ def algorithmic_bytes_bwd(w) -> int:
     n = w.batch * w.heads * w.seqlen
     return (n * (2 * w.dk + 2 * w.dv + 2 * w.dk + w.dv) * esz + n * 4 * 4
             + w.batch * w.heads * w.dk * w.dv * 4 * 3)
+
+
+def algorithmic_flops_bwd(w) -> int:
+    """Matrix products of the chunk-parallel backward per head and 64-token
+    chunk (C = 64, K = d_k, V = d_v; triangular products counted at half):
+    the transfer records 3C^2 K + 3C^2 V + 2C K^2 + 6C K V, the two state
+    carries 4 K^2 V, the token gradients 6C^2 K + 8C^2 V + 10 C K V; all in
+    fp32."""
+    C, K, V = 64, w.dk, w.dv
+    per_chunk = 9 * C * C * K + 11 * C * C * V + 2 * C * K * K + 16 * C * K * V + 4 * K * K * V
+    return w.batch * w.heads * (-(-w.seqlen // C)) * per_chunk
 
 
 def algorithmic_flops(w) -> int:
@@ -662,19 +674,30 @@ def bwd_main(args, w, inp, prof_name) -> int:
                   for i, n in enumerate(names)}
     alg = algorithmic_bytes_bwd(w)
     gbs = alg / (ms * 1e-3) / 1e9
+    chunked = names[0] == "bwd_ops"
+    flops = algorithmic_flops_bwd(w)
+    tfs = flops / (ms * 1e-3) / 1e12
+    if chunked:   # fp32 products: the fp32 matrix-core peak binds before HBM
+        roof = {"bound": "mfma", "achieved": tfs, "peak": F32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": tfs / F32_PEAK_TFLOPS, "algorithmic_flops": flops,
+                "hbm": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}}
+    else:
+        roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": gbs / HBM_PEAK_GBS}
+    roof.update({"traffic": read_traffic(prof_name, names),
+                 "kernel": "falcon_bwd call (" + " + ".join(names) + ")",
+                 "dominant_kernel": max(per_kernel, key=per_kernel.get), "launch_ms": ms,
+                 "algorithmic_bytes": alg})
+    form = "chunk-parallel (C = 64)" if chunked else "token-recurrent"
     line = {
         "metric": METRIC_BWD, "value": w.tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": f"{w.name}: Falcon-1 backward (token-recurrent)", "variant": w.variant,
+        "config": {"workload": f"{w.name}: Falcon-1 backward, {form}", "variant": w.variant,
                    "batch": w.batch, "heads": w.heads, "seq_len": w.seqlen, "dk": w.dk, "dv": w.dv,
                    "io_dtype": w.dtype, "state_dtype": "f32", "parallelism": "none (1 GPU)",
                    "resident_sets": len(sets)},
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": read_traffic(prof_name, names),
-                     "kernel": "falcon_bwd call (" + " + ".join(names) + ")",
-                     "dominant_kernel": max(per_kernel, key=per_kernel.get), "launch_ms": ms,
-                     "algorithmic_bytes": alg},
+        "roofline": roof,
         "kernels_ms": per_kernel, "wall_s_timed": wall,
     }
     if cpu is not None:

@@ -32,6 +32,8 @@ def test_algorithmic_bytes_backward_c2():
     per head."""
     n = 8 * 12 * 1024
     assert bench.algorithmic_bytes_bwd(WORKLOADS["c2"]) == n * (7 * 64 * 2 + 16) + 96 * 64 * 64 * 4 * 3
+    # 42 64^3-sized product terms per head and 64-token chunk at d_k = d_v = 64
+    assert bench.algorithmic_flops_bwd(WORKLOADS["c2"]) == 96 * 16 * 42 * 64 ** 3
 
 
 def test_algorithmic_flops_c2():
