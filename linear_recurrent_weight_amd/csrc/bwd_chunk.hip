@@ -46,7 +46,6 @@
 #include "common.h"
 #include "kernels.h"
 #include "plan.h"
-#include "tri_inverse.h"
 
 namespace falcon {
 namespace {
@@ -54,7 +53,6 @@ namespace {
 constexpr int kC = 64;            // tokens per chunk
 constexpr int kLd = 68;           // LDS row stride (floats)
 constexpr int kMat = kC * kLd;    // floats of one 64-row LDS matrix
-constexpr int kInvScratch = 3 * 16 * 17;
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -79,6 +77,24 @@ __device__ __forceinline__ f32x4 mma16(f32x4 acc, const f32x4 &a, const f32x4 &b
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
     return acc;
 }
+// the tile at rows row0.., columns col0.. of an LDS matrix in accumulator
+// layout (lane holds rows row0 + 4 g + r, column col0 + l16)
+__device__ __forceinline__ f32x4 get_tile(const float *M, int row0, int col0) {
+    const int lane = threadIdx.x & 63;
+    const float *p = M + (row0 + 4 * (lane >> 4)) * kLd + col0 + (lane & 15);
+    return f32x4{p[0], p[kLd], p[2 * kLd], p[3 * kLd]};
+}
+// an accumulator tile stored transposed: element (row0 + 4 g + r, col0 + l16)
+// at M[col0 + l16][row0 + 4 g + r] (one 16-byte write per lane)
+__device__ __forceinline__ void put_tile_t(float *M, int row0, int col0, const f32x4 &v) {
+    const int lane = threadIdx.x & 63;
+    *reinterpret_cast<f32x4 *>(M + (col0 + (lane & 15)) * kLd + row0 + 4 * (lane >> 4)) = v;
+}
+// arr[row0 + 4 g + r], r = 0..3: per-token values of this lane's accumulator rows
+__device__ __forceinline__ f32x4 rows4(const float *arr, int row0) {
+    const int lane = threadIdx.x & 63;
+    return *reinterpret_cast<const f32x4 *>(arr + row0 + 4 * (lane >> 4));
+}
 // an accumulator tile stored as rows row0.. / columns col0.. of an LDS matrix
 __device__ __forceinline__ void put_tile(float *M, int row0, int col0, const f32x4 &v) {
     const int lane = threadIdx.x & 63;
@@ -99,7 +115,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // per-token scalars of one chunk
-struct Tok {
+struct __attribute__((aligned(16))) Tok {
     float eta[kC], alpha[kC], lam[kC], den[kC];
     float bl[kC], bm[kC];       // b_t and b_{t-1}
     float sq[kC], sk[kC];       // phi's scale of q_t and of k_{t-1}
@@ -135,14 +151,8 @@ __device__ __forceinline__ void load_row(const E *p, bool valid, float (&z)[n]) 
     }
 }
 
-// Features and step scalars of chunk c of head bh into LDS: Qh rows
-// phi(q_t), X rows x_t = phi(k_{t-1}) (x of the sequence's first token: the
-// carried feature, or 0 for a fresh sequence), rows past T zero, and the
-// per-token eta, alpha (0 past T and for the fresh first step), lambda, the
-// denominator, b_t, b_{t-1} and phi's scales.  All 256 threads; ends with a
-// barrier.
 template <class E, int DK>
-__device__ void chunk_features(const BwdArgs &a, int bh, int t0, float *X, float *Q, Tok &tk) {
+__device__ void rows_features(const BwdArgs &a, int bh, int t0, float *X, float *Q, Tok &tk) {
     constexpr int HALF = DK / 2;
     const int tid = threadIdx.x;
     const int mq = tid >> 7, t = (tid >> 1) & 63, h = tid & 1;   // matrix (0: q, 1: k), row, half
@@ -183,8 +193,13 @@ __device__ void chunk_features(const BwdArgs &a, int bh, int t0, float *X, float
             tk.xx[t] = xs;
         }
     }
-    __syncthreads();
-    if (tid < 64) {   // lane = token
+}
+
+// eta, alpha, lambda, the denominator and the log-decay prefix (wave 0, lane =
+// token), after the rows
+__device__ void step_scalars(const BwdArgs &a, int bh, int t0, Tok &tk) {
+    const int tid = threadIdx.x, T = a.T;
+    if (tid < 64) {
         const int tt = tid, gtt = t0 + tid;
         const bool in = gtt < T;
         const size_t row = size_t(bh) * T + (in ? gtt : 0);
@@ -206,6 +221,102 @@ __device__ void chunk_features(const BwdArgs &a, int bh, int t0, float *X, float
         tk.bl[tt] = b;
         tk.bm[tt] = bp;
     }
+}
+
+// Features and step scalars of chunk c of head bh into LDS: Qh rows
+// phi(q_t), X rows x_t = phi(k_{t-1}) (x of the sequence's first token: the
+// carried feature, or 0 for a fresh sequence), rows past T zero, and the
+// per-token eta, alpha (0 past T and for the fresh first step), lambda, the
+// denominator, b_t, b_{t-1} and phi's scales.  The rows take the first 256
+// threads (two per row); called by all threads of the workgroup, ends with a
+// barrier.
+template <class E, int DK>
+__device__ void chunk_features(const BwdArgs &a, int bh, int t0, float *X, float *Q, Tok &tk) {
+    if (threadIdx.x < 256) rows_features<E, DK>(a, bh, t0, X, Q, tk);
+    __syncthreads();
+    step_scalars(a, bh, t0, tk);
+    __syncthreads();
+}
+
+__device__ void inverse_diagonal(const float *Nm, float *Tm, float *Tt) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, l16 = lane & 15;
+    float *scr = w < 3 ? Tm + 16 * (w + 1) : Tm + 16 * kLd + 32;
+    const float *Lw = Nm + 16 * w * kLd + 16 * w;   // diagonal block w of N (strictly lower part read)
+    auto sync = [] {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4));   // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+    };
+    // L as operands: A rows from Lw (k contiguous), B k-major; entries on or
+    // above the diagonal are zero by construction of N
+    f32x4 z1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = 4 * g + r;
+        z1[r] = (i == l16 ? 1.f : 0.f) - (l16 < i ? Lw[i * kLd + l16] : 0.f);
+    }
+    f32x4 la = frag_kc(Lw, 0, 0), lb = frag_km(Lw, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {   // zero the diagonal and above (not part of L)
+        const int i = l16, k = 4 * g + r;
+        if (k >= i) la[r] = 0.f;
+        if (i >= k) lb[r] = 0.f;
+    }
+    f32x4 p = mma16(zero4(), la, lb);   // L^2
+    put_tile(scr, 0, 0, p);
+    sync();
+    f32x4 z = z1 + mma16(zero4(), frag_kc(scr, 0, 0), z1);   // (I + L^2)(I - L)
+    f32x4 p4 = mma16(zero4(), frag_kc(scr, 0, 0), p);         // L^4
+    sync();
+    put_tile(scr, 0, 0, p4);
+    sync();
+    z = z + mma16(zero4(), frag_kc(scr, 0, 0), z);            // (I + L^4) ...
+    f32x4 p8 = mma16(zero4(), frag_kc(scr, 0, 0), p4);        // L^8
+    sync();
+    put_tile(scr, 0, 0, p8);
+    sync();
+    z = z + mma16(zero4(), frag_kc(scr, 0, 0), z);            // (I + L^8) ...
+    put_tile(Tm, 16 * w, 16 * w, z);
+    if (Tt) put_tile_t(Tt, 16 * w, 16 * w, z);
+}
+
+// column block w of T below the diagonal, from the diagonal blocks in Tm
+__device__ void inverse_columns(const float *Nm, float *Tm, float *Tt) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, l16 = lane & 15;
+    (void)g;
+    (void)l16;
+    const f32x4 z = get_tile(Tm, 16 * w, 16 * w);
+    f32x4 col[4];
+#pragma unroll
+    for (int K = 0; K < 4; ++K) col[K] = K == w ? z : zero4();
+#pragma unroll
+    for (int I = 1; I < 4; ++I) {
+        if (I <= w) continue;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int K = 0; K < 4; ++K)
+            if (K >= w && K < I) acc = mma16(acc, frag_kc(Nm, 16 * I, 16 * K), col[K]);
+        f32x4 t = mma16(zero4(), frag_kc(Tm, 16 * I, 16 * I), acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[r] = -t[r];
+        col[I] = t;
+        put_tile(Tm, 16 * I, 16 * w, t);
+        if (Tt) put_tile_t(Tt, 16 * I, 16 * w, t);
+    }
+}
+
+// T = (I + N)^{-1} for N strictly lower (64 x 64 in LDS), into the lower
+// tiles of Tm (and transposed into Tt when given); all 256 threads, N complete before the call, ends with a
+// barrier.  Wave w inverts diagonal block w as (I - L)(I + L^2)(I + L^4)(I +
+// L^8) (L = N_ww, exact because L^16 = 0), with upper tile (0,1), (0,2),
+// (0,3) or (1,2) of Tm (never read as part of T) as its scratch; then column
+// block w by substitution, T_IJ = -T_II sum_{K=J}^{I-1} N_IK T_KJ.
+__device__ void unit_lower_inverse_mfma(const float *Nm, float *Tm, float *Tt = nullptr) {
+    const int w = threadIdx.x >> 6;
+    if (w < 4) inverse_diagonal(Nm, Tm, Tt);
+    __syncthreads();
+    if (w < 3) inverse_columns(Nm, Tm, Tt);
     __syncthreads();
 }
 
@@ -217,13 +328,14 @@ __device__ __forceinline__ void lower_tile(int idx, int &m, int &n) {
 
 // The Grams of a chunk: L = D1 o (X X^T) (into Lm when given) and N =
 // diag(eta) L (into Nm), lower tiles; the raw lower tiles of Qh X^T stay in
-// qk (this wave's tiles w, w + 4, w + 8).  The caller puts a barrier after.
+// qk (this wave's tiles w and w + 8 of eight waves).  The caller puts a
+// barrier after.
 template <int NK>
-__device__ void chunk_grams(const float *X, const float *Q, const Tok &tk, float *Lm, float *Nm, f32x4 (&qk)[3]) {
+__device__ void chunk_grams(const float *X, const float *Q, const Tok &tk, float *Lm, float *Nm, f32x4 (&qk)[2]) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, l16 = lane & 15;
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-        const int idx = w + 4 * q;
+    for (int q = 0; q < 2; ++q) {
+        const int idx = w + 8 * q;
         qk[q] = zero4();
         if (idx >= 10) continue;
         int m, n;
@@ -248,12 +360,13 @@ __device__ void chunk_grams(const float *X, const float *Q, const Tok &tk, float
     }
 }
 
-// M = D0 o (Qh X^T) from the raw tiles of chunk_grams, into Mm (lower tiles)
-__device__ void chunk_put_m(const Tok &tk, const f32x4 (&qk)[3], float *Mm) {
+// M = D0 o (Qh X^T) from the raw tiles of chunk_grams, stored transposed
+// into Mm (Mm[j][t] = M_tj; the lower tiles of M)
+__device__ void chunk_put_m(const Tok &tk, const f32x4 (&qk)[2], float *Mm) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, l16 = lane & 15;
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-        const int idx = w + 4 * q;
+    for (int q = 0; q < 2; ++q) {
+        const int idx = w + 8 * q;
         if (idx >= 10) continue;
         int m, n;
         lower_tile(idx, m, n);
@@ -263,7 +376,7 @@ __device__ void chunk_put_m(const Tok &tk, const f32x4 (&qk)[3], float *Mm) {
             const int t = 16 * m + 4 * g + r, j = 16 * n + l16;
             v[r] = j <= t ? ex2(tk.bl[t] - tk.bl[j]) * qk[q][r] : 0.f;
         }
-        put_tile(Mm, 16 * m, 16 * n, v);
+        put_tile_t(Mm, 16 * m, 16 * n, v);
     }
 }
 
@@ -285,98 +398,105 @@ __device__ __forceinline__ f32x4 load_tile(const E *p, int stride, int row0, int
 // bwd_ops: per chunk, the forward's transfer A, B and the reverse term G^T dO
 // ---------------------------------------------------------------------------
 template <class E, int NK, int NV>
-__global__ __launch_bounds__(256) void bwd_ops(BwdArgs a) {
+__global__ __launch_bounds__(512, 4) void bwd_ops(BwdArgs a) {
     constexpr int DK = 16 * NK, DV = 16 * NV;
-    __shared__ __attribute__((aligned(16))) float lds[4 * kMat + kInvScratch];
+    __shared__ __attribute__((aligned(16))) float lds[4 * kMat];
     __shared__ Tok tk;
-    float *X = lds, *Q = lds + kMat, *Nm = lds + 2 * kMat, *Tm = lds + 3 * kMat, *scr = lds + 4 * kMat;
+    float *X = lds, *Q = lds + kMat, *Nm = lds + 2 * kMat, *Tm = lds + 3 * kMat;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, l16 = lane & 15;
     const int nck = a.nchunks;
     const int bh = blockIdx.x / nck, c = blockIdx.x % nck, t0 = c * kC;
     const int T = a.T;
+    // waves 0-3: A (key tile w) and B (value tile w); waves 4-7: G^T dO (value tile w - 4)
+    const int n = w & 3;
+    const bool val = n < NV;
+    // this wave's value tile of V (waves 0-3) or dO (waves 4-7), requested first
+    f32x4 vt[4];
+    {
+        const E *src = static_cast<const E *>(w < 4 ? a.v : a.d_o) + (size_t(bh) * T + t0) * DV;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) vt[s] = val ? load_tile(src, DV, 16 * s, 16 * n, T - t0) : zero4();
+    }
 
     chunk_features<E, DK>(a, bh, t0, X, Q, tk);
-    f32x4 qk[3];
+    f32x4 qk[2];
     chunk_grams<NK>(X, Q, tk, nullptr, Nm, qk);
     __syncthreads();
-    unit_lower_inverse64(Nm, Tm, scr, kLd);   // ends with a barrier; Nm is free afterwards
-    chunk_put_m(tk, qk, Nm);                  // Nm now holds M
+    unit_lower_inverse_mfma(Nm, Tm);          // ends with a barrier; Nm is free afterwards
+    chunk_put_m(tk, qk, Nm);                  // Nm now holds M^T
     __syncthreads();
 
     float *rec = a.ops + (size_t(bh) * nck + c) * size_t(DK * DK + 2 * DK * DV);
     float *Aop = rec, *Bop = rec + DK * DK, *Bb = Bop + DK * DV;
     const float bC = tk.bl[kC - 1];
-    if (w < NK) {
-        // Y = T diag(eta_t 2^{b_{t-1}}) X, column tile w; then A = 2^{b_63} I - X^T diag(2^{b_63-b_t}) Y
-        f32x4 xb[4], y[4];
+    if (w < 4) {
+        if (val) {
+            // Z = T diag(eta) V; B = X^T diag(2^{b_63-b_t}) Z
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            xb[s] = frag_km(X, 16 * w, 16 * s);
+            for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * s + 4 * g + r;
-                xb[s][r] *= tk.eta[t] * ex2(tk.bm[t]);
+                for (int r = 0; r < 4; ++r) vt[s][r] *= tk.eta[16 * s + 4 * g + r];
+            f32x4 z[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int s = 0; s <= m; ++s) acc = mma16(acc, frag_kc(Tm, 16 * m, 16 * s), vt[s]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] *= ex2(bC - tk.bl[16 * m + 4 * g + r]);
+                z[m] = acc;
+            }
+#pragma unroll
+            for (int mm = 0; mm < NK; ++mm) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc = mma16(acc, frag_km(X, 16 * mm, 16 * s), z[s]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Bop[(16 * mm + 4 * g + r) * DV + 16 * n + l16] = acc[r];
             }
         }
+        if (w < NK) {
+            // Y = T diag(eta_t 2^{b_{t-1}}) X, column tile w; A = 2^{b_63} I - X^T diag(2^{b_63-b_t}) Y
+            f32x4 xb[4], y[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            f32x4 acc = zero4();
+            for (int s = 0; s < 4; ++s) {
+                xb[s] = frag_km(X, 16 * w, 16 * s);
 #pragma unroll
-            for (int s = 0; s <= m; ++s) acc = mma16(acc, frag_kc(Tm, 16 * m, 16 * s), xb[s]);
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * s + 4 * g + r;
+                    xb[s][r] *= tk.eta[t] * ex2(tk.bm[t]);
+                }
+            }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] *= ex2(bC - tk.bl[16 * m + 4 * g + r]);
-            y[m] = acc;
-        }
-        const float gC = ex2(bC);
+            for (int m = 0; m < 4; ++m) {
+                f32x4 acc = zero4();
 #pragma unroll
-        for (int mm = 0; mm < NK; ++mm) {
-            f32x4 acc = zero4();
+                for (int s = 0; s <= m; ++s) acc = mma16(acc, frag_kc(Tm, 16 * m, 16 * s), xb[s]);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) acc = mma16(acc, frag_km(X, 16 * mm, 16 * s), y[s]);
+                for (int r = 0; r < 4; ++r) acc[r] *= ex2(bC - tk.bl[16 * m + 4 * g + r]);
+                y[m] = acc;
+            }
+            const float gC = ex2(bC);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i1 = 16 * mm + 4 * g + r, i2 = 16 * w + l16;
-                Aop[i1 * DK + i2] = (i1 == i2 ? gC : 0.f) - acc[r];
+            for (int mm = 0; mm < NK; ++mm) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc = mma16(acc, frag_km(X, 16 * mm, 16 * s), y[s]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i1 = 16 * mm + 4 * g + r, i2 = 16 * w + l16;
+                    Aop[i1 * DK + i2] = (i1 == i2 ? gC : 0.f) - acc[r];
+                }
             }
         }
-    }
-    if (w < NV) {
-        const E *v = static_cast<const E *>(a.v) + size_t(bh) * T * DV;
-        const E *dO = static_cast<const E *>(a.d_o) + size_t(bh) * T * DV;
-        // Z = T diag(eta) V; B = X^T diag(2^{b_63-b_t}) Z
-        f32x4 zb[4], dov[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            zb[s] = load_tile(v + size_t(t0) * DV, DV, 16 * s, 16 * w, T - t0);
-            dov[s] = load_tile(dO + size_t(t0) * DV, DV, 16 * s, 16 * w, T - t0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) zb[s][r] *= tk.eta[16 * s + 4 * g + r];
-        }
-        f32x4 z[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int s = 0; s <= m; ++s) acc = mma16(acc, frag_kc(Tm, 16 * m, 16 * s), zb[s]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] *= ex2(bC - tk.bl[16 * m + 4 * g + r]);
-            z[m] = acc;
-        }
-#pragma unroll
-        for (int mm = 0; mm < NK; ++mm) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int s = 0; s < 4; ++s) acc = mma16(acc, frag_km(X, 16 * mm, 16 * s), z[s]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Bop[(16 * mm + 4 * g + r) * DV + 16 * w + l16] = acc[r];
-        }
+    } else if (val) {
         // W_do = T^T M^T dO; G^T dO = Qh^T diag(2^{b_t}) dO - X^T diag(eta_t 2^{b_{t-1}}) W_do
         f32x4 pd[4], wd[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int s = m; s < 4; ++s) acc = mma16(acc, frag_km(Nm, 16 * m, 16 * s), dov[s]);
+            for (int s = m; s < 4; ++s) acc = mma16(acc, frag_kc(Nm, 16 * m, 16 * s), vt[s]);
             pd[m] = acc;
         }
 #pragma unroll
@@ -388,7 +508,7 @@ __global__ __launch_bounds__(256) void bwd_ops(BwdArgs a) {
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * m + 4 * g + r;
                 acc[r] *= tk.eta[t] * ex2(tk.bm[t]);
-                dov[m][r] *= ex2(tk.bl[t]);
+                vt[m][r] *= ex2(tk.bl[t]);
             }
             wd[m] = acc;
         }
@@ -397,11 +517,11 @@ __global__ __launch_bounds__(256) void bwd_ops(BwdArgs a) {
             f32x4 acc = zero4(), neg = zero4();
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                acc = mma16(acc, frag_km(Q, 16 * mm, 16 * s), dov[s]);
+                acc = mma16(acc, frag_km(Q, 16 * mm, 16 * s), vt[s]);
                 neg = mma16(neg, frag_km(X, 16 * mm, 16 * s), wd[s]);
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Bb[(16 * mm + 4 * g + r) * DV + 16 * w + l16] = acc[r] - neg[r];
+            for (int r = 0; r < 4; ++r) Bb[(16 * mm + 4 * g + r) * DV + 16 * n + l16] = acc[r] - neg[r];
         }
     }
 }
@@ -412,47 +532,67 @@ __global__ __launch_bounds__(256) void bwd_ops(BwdArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kXs = 20;   // row stride of the exchanged column tile
 
+// (head, 16-column tile) of a carry workgroup.  Workgroup ids go round-robin
+// over the 8 XCDs; the tiles of one head take ids 8 apart, so they run on one
+// XCD and read each chunk's record through one L2.  The grid is padded to a
+// multiple of 8 heads (workgroups past the last head return at once).
+__device__ __forceinline__ void carry_tile(int NV, int &bh, int &n) {
+    const int id = blockIdx.x, rest = id >> 3;
+    n = rest % NV;
+    bh = (rest / NV) * 8 + (id & 7);
+}
+constexpr int kRing = 4;  // chunk records requested ahead of their step
+
 template <int NK>
 __global__ __launch_bounds__(64 * NK) void bwd_carry_fwd(BwdArgs a) {
     constexpr int DK = 16 * NK;
     __shared__ float Sx[2][DK * kXs];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, l16 = lane & 15;
     const int DV = a.dv, NV = DV / 16, nck = a.nchunks;
-    const int bh = blockIdx.x / NV, n = blockIdx.x % NV;
+    int bh, n;
+    carry_tile(NV, bh, n);
+    if (bh >= a.BH) return;
     const size_t rec = size_t(DK) * DK + 2 * size_t(DK) * DV;
     const int row0 = 16 * w + 4 * g, col = 16 * n + l16;
     f32x4 S;
 #pragma unroll
     for (int r = 0; r < 4; ++r) S[r] = a.S_in ? a.S_in[(size_t(bh) * DK + row0 + r) * DV + col] : 0.f;
     float *cst = a.cst + size_t(bh) * (nck + 1) * DK * DV;
-    auto load_ops = [&](int c, f32x4 (&fa)[NK], f32x4 &fbias) {
+    // ring slot u holds chunk c = u (mod kRing): A rows 16 w + l16 as A
+    // operands, and B rows row0 + r
+    f32x4 fa[kRing][NK], fb[kRing];
+    auto load = [&](int c, f32x4 (&ra)[NK], f32x4 &rb) {
         const float *A = a.ops + (size_t(bh) * nck + c) * rec, *B = A + DK * DK;
 #pragma unroll
         for (int s = 0; s < NK; ++s)
-            fa[s] = *reinterpret_cast<const f32x4 *>(A + (16 * w + l16) * DK + 16 * s + 4 * g);
+            ra[s] = *reinterpret_cast<const f32x4 *>(A + (16 * w + l16) * DK + 16 * s + 4 * g);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) fbias[r] = B[(row0 + r) * DV + col];
+        for (int r = 0; r < 4; ++r) rb[r] = B[(row0 + r) * DV + col];
     };
-    f32x4 fa[NK], fb, na[NK], nb;
-    load_ops(0, fa, fb);
-    for (int c = 0; c < nck; ++c) {
-        if (c + 1 < nck) load_ops(c + 1, na, nb);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            cst[(size_t(c) * DK + row0 + r) * DV + col] = S[r];
-            Sx[c & 1][(row0 + r) * kXs + l16] = S[r];
+    for (int u = 0; u < kRing; ++u)
+        if (u < nck) load(u, fa[u], fb[u]);
+    for (int c0 = 0; c0 < nck; c0 += kRing) {
+#pragma unroll
+        for (int u = 0; u < kRing; ++u) {
+            const int c = c0 + u;
+            if (c >= nck) break;
+            float *sx = Sx[u & 1];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                cst[(size_t(c) * DK + row0 + r) * DV + col] = S[r];
+                sx[(row0 + r) * kXs + l16] = S[r];
+            }
+            lds_barrier();
+            f32x4 acc = fb[u];
+#pragma unroll
+            for (int s = 0; s < NK; ++s) {
+                const float *p = sx + (16 * s + 4 * g) * kXs + l16;
+                acc = mma16(acc, fa[u][s], f32x4{p[0], p[kXs], p[2 * kXs], p[3 * kXs]});
+            }
+            S = acc;
+            if (c + kRing < nck) load(c + kRing, fa[u], fb[u]);
         }
-        lds_barrier();
-        f32x4 acc = fb;
-#pragma unroll
-        for (int s = 0; s < NK; ++s) {
-            const float *p = &Sx[c & 1][(16 * s + 4 * g) * kXs + l16];
-            acc = mma16(acc, fa[s], f32x4{p[0], p[kXs], p[2 * kXs], p[3 * kXs]});
-        }
-        S = acc;
-#pragma unroll
-        for (int s = 0; s < NK; ++s) fa[s] = na[s];
-        fb = nb;
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) cst[(size_t(nck) * DK + row0 + r) * DV + col] = S[r];
@@ -465,7 +605,9 @@ __global__ __launch_bounds__(64 * NK) void bwd_carry_rev(BwdArgs a) {
     __shared__ float red[2][NK];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, l16 = lane & 15;
     const int DV = a.dv, NV = DV / 16, nck = a.nchunks;
-    const int bh = blockIdx.x / NV, n = blockIdx.x % NV;
+    int bh, n;
+    carry_tile(NV, bh, n);
+    if (bh >= a.BH) return;
     const size_t rec = size_t(DK) * DK + 2 * size_t(DK) * DV;
     const int row0 = 16 * w + 4 * g, col = 16 * n + l16;
     f32x4 H;
@@ -473,49 +615,55 @@ __global__ __launch_bounds__(64 * NK) void bwd_carry_rev(BwdArgs a) {
     for (int r = 0; r < 4; ++r) H[r] = a.d_S_out ? a.d_S_out[(size_t(bh) * DK + row0 + r) * DV + col] : 0.f;
     const float *cst = a.cst + size_t(bh) * (nck + 1) * DK * DV;
     float *hg = a.hg + size_t(bh) * nck * DK * DV;
-    // A^T as A operand: element (i, k) = A[k][i]; and the bias G^T dO
-    auto load_ops = [&](int c, f32x4 (&fa)[NK], f32x4 &fbias, f32x4 &snext) {
+    // ring slot u holds the u-th chunk from the end (mod kRing): A^T as A
+    // operands (element (i, k) = A[k][i]), the rows of G^T dO, and the rows
+    // of the state after the chunk
+    f32x4 fa[kRing][NK], fb[kRing], sn[kRing];
+    auto load = [&](int c, f32x4 (&ra)[NK], f32x4 &rb, f32x4 &rs) {
         const float *A = a.ops + (size_t(bh) * nck + c) * rec, *Bb = A + DK * DK + DK * DV;
 #pragma unroll
         for (int s = 0; s < NK; ++s)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) fa[s][r] = A[(16 * s + 4 * g + r) * DK + 16 * w + l16];
+            for (int r = 0; r < 4; ++r) ra[s][r] = A[(16 * s + 4 * g + r) * DK + 16 * w + l16];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            fbias[r] = Bb[(row0 + r) * DV + col];
-            snext[r] = cst[(size_t(c + 1) * DK + row0 + r) * DV + col];
+            rb[r] = Bb[(row0 + r) * DV + col];
+            rs[r] = cst[(size_t(c + 1) * DK + row0 + r) * DV + col];
         }
     };
-    f32x4 fa[NK], fb, sn, na[NK], nb, nsn;
-    load_ops(nck - 1, fa, fb, sn);
-    for (int c = nck - 1; c >= 0; --c) {
-        if (c > 0) load_ops(c - 1, na, nb, nsn);
-        float ph = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            hg[(size_t(c) * DK + row0 + r) * DV + col] = H[r];
-            Hx[c & 1][(row0 + r) * kXs + l16] = H[r];
-            ph += H[r] * sn[r];
-        }
-        ph = wave_sum(ph);
-        if (lane == 0) red[c & 1][w] = ph;
-        lds_barrier();
-        if (w == 0 && lane == 0) {
-            float tot = 0.f;
-            for (int q = 0; q < NK; ++q) tot += red[c & 1][q];
-            a.phip[(size_t(bh) * nck + c) * NV + n] = tot;
-        }
-        f32x4 acc = fb;
+    for (int u = 0; u < kRing; ++u)
+        if (u < nck) load(nck - 1 - u, fa[u], fb[u], sn[u]);
+    for (int e0 = 0; e0 < nck; e0 += kRing) {
 #pragma unroll
-        for (int s = 0; s < NK; ++s) {
-            const float *p = &Hx[c & 1][(16 * s + 4 * g) * kXs + l16];
-            acc = mma16(acc, fa[s], f32x4{p[0], p[kXs], p[2 * kXs], p[3 * kXs]});
-        }
-        H = acc;
+        for (int u = 0; u < kRing; ++u) {
+            const int e = e0 + u, c = nck - 1 - e;
+            if (e >= nck) break;
+            float *hx = Hx[u & 1];
+            float ph = 0.f;
 #pragma unroll
-        for (int s = 0; s < NK; ++s) fa[s] = na[s];
-        fb = nb;
-        sn = nsn;
+            for (int r = 0; r < 4; ++r) {
+                hg[(size_t(c) * DK + row0 + r) * DV + col] = H[r];
+                hx[(row0 + r) * kXs + l16] = H[r];
+                ph += H[r] * sn[u][r];
+            }
+            ph = wave_sum(ph);
+            if (lane == 0) red[u & 1][w] = ph;
+            lds_barrier();
+            if (w == 0 && lane == 0) {
+                float tot = 0.f;
+                for (int q = 0; q < NK; ++q) tot += red[u & 1][q];
+                a.phip[(size_t(bh) * nck + c) * NV + n] = tot;
+            }
+            f32x4 acc = fb[u];
+#pragma unroll
+            for (int s = 0; s < NK; ++s) {
+                const float *p = hx + (16 * s + 4 * g) * kXs + l16;
+                acc = mma16(acc, fa[u][s], f32x4{p[0], p[kXs], p[2 * kXs], p[3 * kXs]});
+            }
+            H = acc;
+            if (e + kRing < nck) load(c - kRing, fa[u], fb[u], sn[u]);
+        }
     }
     if (a.d_S_in)
 #pragma unroll
@@ -526,215 +674,284 @@ __global__ __launch_bounds__(64 * NK) void bwd_carry_rev(BwdArgs a) {
 // bwd_grads: per chunk, every token gradient
 // ---------------------------------------------------------------------------
 template <class E, int NK, int NV>
-__global__ __launch_bounds__(256) void bwd_grads(BwdArgs a) {
+__global__ __launch_bounds__(512) void bwd_grads(BwdArgs a) {
     constexpr int DK = 16 * NK, DV = 16 * NV;
-    __shared__ __attribute__((aligned(16))) float lds[6 * kMat + kInvScratch];
+    __shared__ __attribute__((aligned(16))) float lds[6 * kMat];
     __shared__ Tok tk;
-    __shared__ float red[4][4][kC];   // per-wave partial sums: deta, w.v, qh.dqh, x.dx
+    __shared__ float red[4][4][kC];   // partial sums per 16 columns: deta, w.v, qh.dqh, x.dx
     float *X = lds, *Q = lds + kMat, *SL = lds + 2 * kMat, *SN = lds + 3 * kMat, *ST = lds + 4 * kMat,
-          *SD = lds + 5 * kMat, *scr = lds + 6 * kMat;
+          *SD = lds + 5 * kMat;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
     const int nck = a.nchunks;
     const int bh = blockIdx.x / nck, c = blockIdx.x % nck, t0 = c * kC;
     const int T = a.T, nin = T - t0;   // rows of this chunk inside the sequence (> 0)
-
-    chunk_features<E, DK>(a, bh, t0, X, Q, tk);
-    f32x4 qk[3];
-    chunk_grams<NK>(X, Q, tk, SL, SN, qk);
-    __syncthreads();
-    unit_lower_inverse64(SN, ST, scr, kLd);
-    chunk_put_m(tk, qk, SN);   // SN: M
-    __syncthreads();
-
-    const float bC = tk.bl[kC - 1];
     const float *S0 = a.cst + (size_t(bh) * (nck + 1) + c) * DK * DV;
     const float *Hc = a.hg + (size_t(bh) * nck + c) * DK * DV;
     const size_t rowbase = size_t(bh) * T + t0;
+    // Waves w and w + 4 share a SIMD.  Value tile n = w & 3: waves 0-3 the
+    // forward solve (U, R), waves 4-7 the backward one (P, W).  Key tile
+    // n: waves 0-3 dqh, waves 4-7 dx.
+    const int n = w & 3;
+    const bool lo = w < 4, val = n < NV, key = n < NK;
 
-    // ---- value tile w: U, R, W; deta and w.v partial sums; dv
-    f32x4 u[4], rr[4], wv[4], dov[4];
-    if (w < NV) {
+    // operands from memory, requested before the chunk's features
+    f32x4 vv[4], dov[4], sb[NK], s0t[NV], ht[NV];
+    {
         const E *v = static_cast<const E *>(a.v) + rowbase * DV;
         const E *dO = static_cast<const E *>(a.d_o) + rowbase * DV;
-        f32x4 s0b[NK], hb[NK], vv[4], rhs[4];
-#pragma unroll
-        for (int s = 0; s < NK; ++s) {
-            s0b[s] = load_tile(S0, DV, 16 * s, 16 * w, DK);
-            hb[s] = load_tile(Hc, DV, 16 * s, 16 * w, DK);
-        }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            vv[s] = load_tile(v, DV, 16 * s, 16 * w, nin);
-            dov[s] = load_tile(dO, DV, 16 * s, 16 * w, nin);
+            vv[s] = val ? load_tile(v, DV, 16 * s, 16 * n, nin) : zero4();
+            dov[s] = (val && !lo) ? load_tile(dO, DV, 16 * s, 16 * n, nin) : zero4();
         }
-        // RHS0 = V - diag(2^{b_{t-1}}) X S_0, Y = diag(eta) RHS0
-        f32x4 y[4];
+        // S_0 (waves 0-3) or H (waves 4-7) as B operands over the key index
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            f32x4 xs = zero4();
+        for (int s = 0; s < NK; ++s) sb[s] = val ? load_tile(lo ? S0 : Hc, DV, 16 * s, 16 * n, DK) : zero4();
+        // S_0^T and H^T blocks: lane (g, i) holds row 16 n + i, columns 16 s + 4 g ..
 #pragma unroll
-            for (int s = 0; s < NK; ++s) xs = mma16(xs, frag_kc(X, 16 * m, 16 * s), s0b[s]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * m + 4 * g + r;
-                rhs[m][r] = vv[m][r] - ex2(tk.bm[t]) * xs[r];
-                y[m][r] = tk.eta[t] * rhs[m][r];
-            }
+        for (int s = 0; s < NV; ++s) {
+            s0t[s] = key ? *reinterpret_cast<const f32x4 *>(S0 + (16 * n + l16) * DV + 16 * s + 4 * g) : zero4();
+            ht[s] = (key && !lo) ? *reinterpret_cast<const f32x4 *>(Hc + (16 * n + l16) * DV + 16 * s + 4 * g)
+                                 : zero4();
         }
-        // U = T Y, R = RHS0 - L U
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int s = 0; s <= m; ++s) acc = mma16(acc, frag_kc(ST, 16 * m, 16 * s), y[s]);
-            u[m] = acc;
-        }
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int s = 0; s <= m; ++s) acc = mma16(acc, frag_kc(SL, 16 * m, 16 * s), u[s]);
-            rr[m] = rhs[m] - acc;
-        }
-        // P = M^T dO + diag(2^{b_63-b_t}) X H, W = T^T P
-        f32x4 p[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            f32x4 acc = zero4(), xh = zero4();
-#pragma unroll
-            for (int s = m; s < 4; ++s) acc = mma16(acc, frag_km(SN, 16 * m, 16 * s), dov[s]);
-#pragma unroll
-            for (int s = 0; s < NK; ++s) xh = mma16(xh, frag_kc(X, 16 * m, 16 * s), hb[s]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] += ex2(bC - tk.bl[16 * m + 4 * g + r]) * xh[r];
-            p[m] = acc;
-        }
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int s = m; s < 4; ++s) acc = mma16(acc, frag_km(ST, 16 * m, 16 * s), p[s]);
-            wv[m] = acc;
-        }
-        // deta_t and w_t . v_t over this tile's columns; dv_t = eta_t w_t
-        E *dV = static_cast<E *>(a.d_v) + rowbase * DV;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * m + 4 * g + r;
-                const float de = group_sum<16>(wv[m][r] * rr[m][r]);
-                const float wvv = group_sum<16>(wv[m][r] * vv[m][r]);
-                if (l16 == 0) {
-                    red[0][w][t] = de;
-                    red[1][w][t] = wvv;
-                }
-                if (t < nin) st(dV, size_t(t) * DV + 16 * w + l16, tk.eta[t] * wv[m][r]);
-            }
     }
-    __syncthreads();   // L, M and T are no longer read
-    if (w < NV) {
+
+    chunk_features<E, DK>(a, bh, t0, X, Q, tk);
+    f32x4 qk[2];
+    chunk_grams<NK>(X, Q, tk, SL, SN, qk);
+    __syncthreads();
+    unit_lower_inverse_mfma(SN, ST, SD);   // SD: T^T until dO is stored there
+    chunk_put_m(tk, qk, SN);               // SN: M^T
+    __syncthreads();
+
+    const float bC = tk.bl[kC - 1];
+    // ---- value tile n: waves 0-3 U = T diag(eta) RHS0, R = RHS0 - L U with
+    // RHS0 = V - diag(2^{b_{t-1}}) X S_0; waves 4-7 P = M^T dO + diag(2^{b_63-b_t}) X H,
+    // W = T^T P, dv = eta W, w.v
+    f32x4 sol[4];
+    f32x4 rr[4];
+    if (val) {
+        if (lo) {
+            f32x4 rhs[4], y[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                f32x4 xs = zero4();
+#pragma unroll
+                for (int s = 0; s < NK; ++s) xs = mma16(xs, frag_kc(X, 16 * m, 16 * s), sb[s]);
+                const f32x4 bm = rows4(tk.bm, 16 * m), et = rows4(tk.eta, 16 * m);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    rhs[m][r] = vv[m][r] - ex2(bm[r]) * xs[r];
+                    y[m][r] = et[r] * rhs[m][r];
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int s = 0; s <= m; ++s) acc = mma16(acc, frag_kc(ST, 16 * m, 16 * s), y[s]);
+                sol[m] = acc;
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int s = 0; s <= m; ++s) acc = mma16(acc, frag_kc(SL, 16 * m, 16 * s), sol[s]);
+                rr[m] = rhs[m] - acc;
+            }
+        } else {
+            f32x4 p[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                f32x4 acc = zero4(), xh = zero4();
+#pragma unroll
+                for (int s = m; s < 4; ++s) acc = mma16(acc, frag_kc(SN, 16 * m, 16 * s), dov[s]);
+#pragma unroll
+                for (int s = 0; s < NK; ++s) xh = mma16(xh, frag_kc(X, 16 * m, 16 * s), sb[s]);
+                const f32x4 bl = rows4(tk.bl, 16 * m);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] += ex2(bC - bl[r]) * xh[r];
+                p[m] = acc;
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int s = m; s < 4; ++s) acc = mma16(acc, frag_kc(SD, 16 * m, 16 * s), p[s]);
+                sol[m] = acc;
+            }
+            E *dV = static_cast<E *>(a.d_v) + rowbase * DV;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const f32x4 et = rows4(tk.eta, 16 * m);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * m + 4 * g + r;
+                    const float wvv = group_sum<16>(sol[m][r] * vv[m][r]);
+                    if (l16 == 0) red[1][n][t] = wvv;
+                    if (t < nin) st(dV, size_t(t) * DV + 16 * n + l16, et[r] * sol[m][r]);
+                }
+            }
+        }
+    }
+    __syncthreads();   // L, M^T, T and T^T are no longer read
+    float *SU = SL, *SR = SN, *SW = ST, *SO = SD;
+    if (val) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            put_tile(SL, 16 * m, 16 * w, u[m]);
-            put_tile(SN, 16 * m, 16 * w, rr[m]);
-            put_tile(ST, 16 * m, 16 * w, wv[m]);
-            put_tile(SD, 16 * m, 16 * w, dov[m]);
+            if (lo) {
+                put_tile(SU, 16 * m, 16 * n, sol[m]);
+                put_tile(SR, 16 * m, 16 * n, rr[m]);
+            } else {
+                put_tile(SW, 16 * m, 16 * n, sol[m]);
+                put_tile(SO, 16 * m, 16 * n, dov[m]);
+            }
         }
     }
     __syncthreads();
-    float *SU = SL, *SR = SN, *SW = ST, *SO = SD;
-
-    // ---- products over the value index: column tile w of dO U^T, W U^T
-    // (lower tiles), R dO^T, R W^T (upper tiles); and for key tile w: dO S_0^T,
-    // R H^T, W S_0^T
-    f32x4 m1[4], wu[4], m3[4], rw[4];
+    // deta_t = w_t . r_t over value tile n (waves 4-7: W in registers, R from LDS)
+    if (val && !lo) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        m1[m] = zero4();
-        wu[m] = zero4();
-        m3[m] = zero4();
-        rw[m] = zero4();
-        if (m >= w) {
+        for (int m = 0; m < 4; ++m) {
+            const f32x4 rv = get_tile(SR, 16 * m, 16 * n);
 #pragma unroll
-            for (int s = 0; s < NV; ++s) {
-                const f32x4 fu = frag_kc(SU, 16 * w, 16 * s);
-                m1[m] = mma16(m1[m], frag_kc(SO, 16 * m, 16 * s), fu);
-                wu[m] = mma16(wu[m], frag_kc(SW, 16 * m, 16 * s), fu);
-            }
-        }
-        if (m <= w) {
-#pragma unroll
-            for (int s = 0; s < NV; ++s) {
-                const f32x4 fr = frag_kc(SR, 16 * m, 16 * s);
-                m3[m] = mma16(m3[m], fr, frag_kc(SO, 16 * w, 16 * s));
-                rw[m] = mma16(rw[m], fr, frag_kc(SW, 16 * w, 16 * s));
+            for (int r = 0; r < 4; ++r) {
+                const float de = group_sum<16>(sol[m][r] * rv[r]);
+                if (l16 == 0) red[0][n][16 * m + 4 * g + r] = de;
             }
         }
     }
-    f32x4 ds[4], rh[4], ws[4];
-    if (w < NK) {
-        f32x4 s0t[NV], ht[NV];   // S_0^T, H^T blocks: lane (g, i) holds row 16 w + i, columns 16 s + 4 g ..
+
+    // ---- products over the value index, column tile n of C x C:
+    //   waves 0-3: dO U^T and W U^T on lower tiles (m >= n), R W^T on tile (n, n);
+    //   waves 4-7: R dO^T on upper tiles (m <= n), R W^T on tiles m < n.
+    // Key tile n: waves 0-3 dO S_0^T; waves 4-7 R H^T and W S_0^T.
+    // The shared operand blocks are read once per value block s.
+    f32x4 fa[4], fb[4], kx[4], ky = zero4();
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        fa[m] = zero4();
+        fb[m] = zero4();
+        kx[m] = zero4();
+    }
+    if (lo) {
 #pragma unroll
         for (int s = 0; s < NV; ++s) {
-            s0t[s] = *reinterpret_cast<const f32x4 *>(S0 + (16 * w + l16) * DV + 16 * s + 4 * g);
-            ht[s] = *reinterpret_cast<const f32x4 *>(Hc + (16 * w + l16) * DV + 16 * s + 4 * g);
+            const f32x4 bu = frag_kc(SU, 16 * n, 16 * s), bw = frag_kc(SW, 16 * n, 16 * s);
+            ky = mma16(ky, frag_kc(SR, 16 * n, 16 * s), bw);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const f32x4 ado = frag_kc(SO, 16 * m, 16 * s);
+                if (key) kx[m] = mma16(kx[m], ado, s0t[s]);
+                if (m >= n) {
+                    fa[m] = mma16(fa[m], ado, bu);
+                    fb[m] = mma16(fb[m], frag_kc(SW, 16 * m, 16 * s), bu);
+                }
+            }
+        }
+    } else {
+        f32x4 rh[4], ws[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            rh[m] = zero4();
+            ws[m] = zero4();
+        }
+#pragma unroll
+        for (int s = 0; s < NV; ++s) {
+            const f32x4 bo = frag_kc(SO, 16 * n, 16 * s), bw = frag_kc(SW, 16 * n, 16 * s);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const f32x4 ar = frag_kc(SR, 16 * m, 16 * s);
+                if (key) {
+                    rh[m] = mma16(rh[m], ar, ht[s]);
+                    ws[m] = mma16(ws[m], frag_kc(SW, 16 * m, 16 * s), s0t[s]);
+                }
+                if (m <= n) fa[m] = mma16(fa[m], ar, bo);
+                if (m < n) fb[m] = mma16(fb[m], ar, bw);
+            }
         }
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            ds[m] = zero4();
-            rh[m] = zero4();
-            ws[m] = zero4();
+            const f32x4 bl = rows4(tk.bl, 16 * m), bm = rows4(tk.bm, 16 * m);
 #pragma unroll
-            for (int s = 0; s < NV; ++s) {
-                ds[m] = mma16(ds[m], frag_kc(SO, 16 * m, 16 * s), s0t[s]);
-                rh[m] = mma16(rh[m], frag_kc(SR, 16 * m, 16 * s), ht[s]);
-                ws[m] = mma16(ws[m], frag_kc(SW, 16 * m, 16 * s), s0t[s]);
-            }
+            for (int r = 0; r < 4; ++r) kx[m][r] = ex2(bC - bl[r]) * rh[m][r] - ex2(bm[r]) * ws[m][r];
         }
     }
     __syncthreads();   // U, R, W, dO are no longer read
-    // the masked C x C factors, column tile w:
-    //   SL: D0 o (dO U^T);  SN: -(D1^T o (R W^T)) diag(eta) - D1 o (W U^T);  ST: D0^T o (R dO^T)
+    // the masked C x C factors, column tile n:
+    //   F1 (SL) = D0 o (dO U^T), lower tiles (waves 0-3);
+    //   F2 (SN) = -(D1^T o (R W^T)) diag(eta) - D1 o (W U^T): tiles m >= n by waves 0-3, m < n by waves 4-7;
+    //   F3 (ST) = D0^T o (R dO^T), upper tiles (waves 4-7)
     float *F1 = SL, *F2 = SN, *F3 = ST;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        f32x4 v1, v2, v3;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * m + 4 * g + r, uu = 16 * w + l16;
-            v1[r] = uu <= t ? ex2(tk.bl[t] - tk.bl[uu]) * m1[m][r] : 0.f;
-            v2[r] = uu < t ? -ex2(tk.bm[t] - tk.bl[uu]) * wu[m][r]
-                  : uu > t ? -ex2(tk.bm[uu] - tk.bl[t]) * tk.eta[uu] * rw[m][r] : 0.f;
-            v3[r] = uu >= t ? ex2(tk.bl[uu] - tk.bl[t]) * m3[m][r] : 0.f;
-        }
-        put_tile(F1, 16 * m, 16 * w, v1);
-        put_tile(F2, 16 * m, 16 * w, v2);
-        put_tile(F3, 16 * m, 16 * w, v3);
-    }
-    __syncthreads();
-
-    // ---- key tile w: dqh and dx / eta
-    f32x4 dq[4], dx[4];
-    if (w < NK) {
+    {
+        const int uu = 16 * n + l16;
+        const float bl_u = tk.bl[uu], bm_u = tk.bm[uu], eta_u = tk.eta[uu];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int s = 0; s <= m; ++s) acc = mma16(acc, frag_kc(F1, 16 * m, 16 * s), frag_km(X, 16 * w, 16 * s));
-            f32x4 bcc = zero4();
-#pragma unroll
-            for (int s = m; s < 4; ++s) bcc = mma16(bcc, frag_kc(F3, 16 * m, 16 * s), frag_km(Q, 16 * w, 16 * s));
-#pragma unroll
-            for (int s = 0; s < 4; ++s) bcc = mma16(bcc, frag_kc(F2, 16 * m, 16 * s), frag_km(X, 16 * w, 16 * s));
+            const f32x4 bl = rows4(tk.bl, 16 * m), bm = rows4(tk.bm, 16 * m);
+            f32x4 v1, v2, v3;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * m + 4 * g + r;
-                dq[m][r] = ex2(tk.bl[t]) * ds[m][r] + acc[r];
-                dx[m][r] = ex2(bC - tk.bl[t]) * rh[m][r] - ex2(tk.bm[t]) * ws[m][r] + bcc[r];
-                const float qd = group_sum<16>(Q[t * kLd + 16 * w + l16] * dq[m][r]);
-                if (l16 == 0) red[2][w][t] = qd;
+                if (lo) {
+                    v1[r] = uu <= t ? ex2(bl[r] - bl_u) * fa[m][r] : 0.f;
+                    v2[r] = uu < t ? -ex2(bm[r] - bl_u) * fb[m][r]
+                          : uu > t ? -ex2(bm_u - bl[r]) * eta_u * ky[r] : 0.f;
+                } else {
+                    v3[r] = uu >= t ? ex2(bl_u - bl[r]) * fa[m][r] : 0.f;
+                    v2[r] = -ex2(bm_u - bl[r]) * eta_u * fb[m][r];
+                }
             }
+            if (lo) {
+                if (m >= n) {
+                    put_tile(F1, 16 * m, 16 * n, v1);
+                    put_tile(F2, 16 * m, 16 * n, v2);
+                }
+            } else {
+                if (m <= n) put_tile(F3, 16 * m, 16 * n, v3);
+                if (m < n) put_tile(F2, 16 * m, 16 * n, v2);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- key tile n: waves 0-3 dqh = diag(2^{b_t}) dO S_0^T + F1 X;
+    // waves 4-7 dx / eta = (R H^T, W S_0^T terms) + F3 Qh + F2 X
+    f32x4 kd[4];
+    if (key) {
+        f32x4 acc[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[m] = zero4();
+        if (lo) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const f32x4 bx = frag_km(X, 16 * n, 16 * s);
+#pragma unroll
+                for (int m = s; m < 4; ++m) acc[m] = mma16(acc[m], frag_kc(F1, 16 * m, 16 * s), bx);
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const f32x4 bl = rows4(tk.bl, 16 * m);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * m + 4 * g + r;
+                    kd[m][r] = ex2(bl[r]) * kx[m][r] + acc[m][r];
+                    const float qd = group_sum<16>(Q[t * kLd + 16 * n + l16] * kd[m][r]);
+                    if (l16 == 0) red[2][n][t] = qd;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const f32x4 bx = frag_km(X, 16 * n, 16 * s), bq = frag_km(Q, 16 * n, 16 * s);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    acc[m] = mma16(acc[m], frag_kc(F2, 16 * m, 16 * s), bx);
+                    if (m <= s) acc[m] = mma16(acc[m], frag_kc(F3, 16 * m, 16 * s), bq);
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) kd[m] = kx[m] + acc[m];
         }
     }
     __syncthreads();
@@ -780,45 +997,52 @@ __global__ __launch_bounds__(256) void bwd_grads(BwdArgs a) {
     }
     __syncthreads();
 
-    // ---- dq_t through phi; dx_t = eta_t (...) + 2 dden_t x_t
-    if (w < NK) {
-        E *dQ = static_cast<E *>(a.d_q) + rowbase * DK;
-        const float invd = 1.f / float(DK);
-        const bool rms = a.phi == FALCON_PHI_RMSNORM;
+    // ---- waves 0-3: dq_t through phi.  Waves 4-7: dx_t = eta_t (...) + 2 dden_t x_t
+    const float invd = 1.f / float(DK);
+    const bool rms = a.phi == FALCON_PHI_RMSNORM;
+    if (key) {
+        if (lo) {
+            E *dQ = static_cast<E *>(a.d_q) + rowbase * DK;
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
+            for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * m + 4 * g + r, i = 16 * w + l16;
-                const float qh = Q[t * kLd + i], xh = X[t * kLd + i];
-                if (t < nin) {
-                    const float val = rms ? tk.sq[t] * (dq[m][r] - invd * tk.qdq[t] * qh) : dq[m][r];
-                    st(dQ, size_t(t) * DK + i, val);
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * m + 4 * g + r, i = 16 * n + l16;
+                    if (t < nin) {
+                        const float val_ = rms ? tk.sq[t] * (kd[m][r] - invd * tk.qdq[t] * Q[t * kLd + i]) : kd[m][r];
+                        st(dQ, size_t(t) * DK + i, val_);
+                    }
                 }
-                dx[m][r] = tk.eta[t] * dx[m][r] + 2.f * tk.dden[t] * xh;
-                const float xd = group_sum<16>(xh * dx[m][r]);
-                if (l16 == 0) red[3][w][t] = xd;
-            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * m + 4 * g + r, i = 16 * n + l16;
+                    const float xh = X[t * kLd + i];
+                    kd[m][r] = tk.eta[t] * kd[m][r] + 2.f * tk.dden[t] * xh;
+                    const float xd = group_sum<16>(xh * kd[m][r]);
+                    if (l16 == 0) red[3][n][t] = xd;
+                }
+        }
     }
     __syncthreads();
     // x_t = phi(k_{t-1}): d_k of token t - 1; the first token's x is the carried feature
-    if (w < NK) {
+    if (key && !lo) {
         E *dK = static_cast<E *>(a.d_k) + size_t(bh) * T * DK;
-        const float invd = 1.f / float(DK);
-        const bool rms = a.phi == FALCON_PHI_RMSNORM;
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = 16 * m + 4 * g + r, gt = t0 + t, i = 16 * w + l16;
+                const int t = 16 * m + 4 * g + r, gt = t0 + t, i = 16 * n + l16;
                 if (t >= nin) continue;
                 float xd = 0.f;
                 for (int q = 0; q < NK; ++q) xd += red[3][q][t];
                 if (gt >= 1) {
-                    const float val = rms ? tk.sk[t] * (dx[m][r] - invd * xd * X[t * kLd + i]) : dx[m][r];
-                    st(dK, size_t(gt - 1) * DK + i, val);
+                    const float val_ = rms ? tk.sk[t] * (kd[m][r] - invd * xd * X[t * kLd + i]) : kd[m][r];
+                    st(dK, size_t(gt - 1) * DK + i, val_);
                 } else if (a.d_x_next_in) {
-                    a.d_x_next_in[size_t(bh) * DK + i] = a.fresh ? 0.f : dx[m][r];
+                    a.d_x_next_in[size_t(bh) * DK + i] = a.fresh ? 0.f : kd[m][r];
                 }
             }
     }
@@ -831,22 +1055,22 @@ __global__ __launch_bounds__(256) void bwd_grads(BwdArgs a) {
         const float s = phi_scale(wave_sum(z * z), DK, a.eps_rms, a.phi);
         const float xh = s * z;
         const float xg = wave_sum(xh * gx);
-        const float val = a.phi == FALCON_PHI_RMSNORM ? s * (gx - xg * xh / float(DK)) : gx;
-        if (lane < DK) st(dK, size_t(T - 1) * DK + lane, val);
+        const float val_ = rms ? s * (gx - xg * xh * invd) : gx;
+        if (lane < DK) st(dK, size_t(T - 1) * DK + lane, val_);
     }
 }
 
 template <class E, int NK, int NV>
 void launch_nv(const BwdArgs &a, hipStream_t s, Marks *m) {
     const unsigned chunks = static_cast<unsigned>(a.BH) * static_cast<unsigned>(a.nchunks);
-    const unsigned tiles = static_cast<unsigned>(a.BH) * NV;
-    bwd_ops<E, NK, NV><<<chunks, 256, 0, s>>>(a);
+    const unsigned tiles = static_cast<unsigned>((a.BH + 7) / 8) * 8 * NV;
+    bwd_ops<E, NK, NV><<<chunks, 512, 0, s>>>(a);
     m->mark(s);
     bwd_carry_fwd<NK><<<tiles, 64 * NK, 0, s>>>(a);
     m->mark(s);
     bwd_carry_rev<NK><<<tiles, 64 * NK, 0, s>>>(a);
     m->mark(s);
-    bwd_grads<E, NK, NV><<<chunks, 256, 0, s>>>(a);
+    bwd_grads<E, NK, NV><<<chunks, 512, 0, s>>>(a);
     m->mark(s);
 }
 
