@@ -224,8 +224,15 @@ int falcon_fwd_noalloc(const falcon_fwd_args *args, void *stream);
  *     k_{T-1} feeds only the next segment's first pair: d_k of token T-1 is
  *     phi's product with d_x_next_out (0 when NULL).
  * The forward is recomputed from the inputs (nothing from falcon_fwd is
- * reused): every pre-step state is kept in the workspace, which therefore
- * grows as B*H*(T+1)*d_k*d_v*4 bytes.
+ * reused).  For T > 0 and d_k, d_v <= 64 the pass is chunk-parallel in
+ * 64-token chunks (summary §E.3, §H.1): one chunk of the forward is affine in
+ * its entry state, S_end = A S_0 + B, O = G S_0 + ..., so the state gradient
+ * crosses a chunk backwards as H <- A^T H + G^T dO, and each chunk's token
+ * gradients follow from its entry state and H at its end; the workspace holds
+ * per chunk the fp32 records A, B, G^T dO and the chunk's entry state and H
+ * (about B*H*ceil(T/64)*(d_k*d_k + 4*d_k*d_v)*4 bytes).  Other shapes run the
+ * token-recurrent reverse, keeping the state before every 4th token.  All
+ * products are fp32.
  *
  *   abi_version  FALCON_ABI_VERSION.  variant: FALCON_V1 only (other
  *                variants return FALCON_ERR_UNSUPPORTED).
