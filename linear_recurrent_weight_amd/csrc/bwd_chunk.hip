@@ -197,13 +197,12 @@ __device__ void rows_features(const BwdArgs &a, int bh, int t0, float *X, float 
 
 // eta, alpha, lambda, the denominator and the log-decay prefix (wave 0, lane =
 // token), after the rows
-__device__ void step_scalars(const BwdArgs &a, int bh, int t0, Tok &tk) {
+__device__ void step_scalars(const BwdArgs &a, int t0, Tok &tk, const float2 &beta_lam) {
     const int tid = threadIdx.x, T = a.T;
     if (tid < 64) {
         const int tt = tid, gtt = t0 + tid;
         const bool in = gtt < T;
-        const size_t row = size_t(bh) * T + (in ? gtt : 0);
-        const float beta = in ? a.beta[row] : 0.f, lam = in ? a.lambda[row] : 0.f;
+        const float beta = beta_lam.x, lam = beta_lam.y;
         const float den = tk.xx[tt] + lam + a.eps;
         float eta = step_eta(beta, den), alpha = step_alpha(eta, lam, a.eps_gamma);
         if (!in || (a.fresh && gtt == 0)) {
@@ -223,6 +222,18 @@ __device__ void step_scalars(const BwdArgs &a, int bh, int t0, Tok &tk) {
     }
 }
 
+// beta_t and lambda_t of token t0 + lane (wave 0 only; 0 past T), requested
+// at kernel entry so that their latency overlaps the rows'
+__device__ __forceinline__ float2 load_beta_lam(const BwdArgs &a, int bh, int t0) {
+    float2 v = make_float2(0.f, 0.f);
+    const int gt = t0 + (threadIdx.x & 63);
+    if (threadIdx.x < 64 && gt < a.T) {
+        const size_t row = size_t(bh) * a.T + gt;
+        v = make_float2(a.beta[row], a.lambda[row]);
+    }
+    return v;
+}
+
 // Features and step scalars of chunk c of head bh into LDS: Qh rows
 // phi(q_t), X rows x_t = phi(k_{t-1}) (x of the sequence's first token: the
 // carried feature, or 0 for a fresh sequence), rows past T zero, and the
@@ -231,10 +242,11 @@ __device__ void step_scalars(const BwdArgs &a, int bh, int t0, Tok &tk) {
 // threads (two per row); called by all threads of the workgroup, ends with a
 // barrier.
 template <class E, int DK>
-__device__ void chunk_features(const BwdArgs &a, int bh, int t0, float *X, float *Q, Tok &tk) {
+__device__ void chunk_features(const BwdArgs &a, int bh, int t0, float *X, float *Q, Tok &tk,
+                               const float2 &beta_lam) {
     if (threadIdx.x < 256) rows_features<E, DK>(a, bh, t0, X, Q, tk);
     __syncthreads();
-    step_scalars(a, bh, t0, tk);
+    step_scalars(a, t0, tk, beta_lam);
     __syncthreads();
 }
 
@@ -409,6 +421,7 @@ __global__ __launch_bounds__(512, 4) void bwd_ops(BwdArgs a) {
     const int T = a.T;
     // waves 0-3: A (key tile w) and B (value tile w); waves 4-7: G^T dO (value tile w - 4)
     const int n = w & 3;
+    const float2 beta_lam = load_beta_lam(a, bh, t0);
     const bool val = n < NV;
     // this wave's value tile of V (waves 0-3) or dO (waves 4-7), requested first
     f32x4 vt[4];
@@ -418,7 +431,7 @@ __global__ __launch_bounds__(512, 4) void bwd_ops(BwdArgs a) {
         for (int s = 0; s < 4; ++s) vt[s] = val ? load_tile(src, DV, 16 * s, 16 * n, T - t0) : zero4();
     }
 
-    chunk_features<E, DK>(a, bh, t0, X, Q, tk);
+    chunk_features<E, DK>(a, bh, t0, X, Q, tk, beta_lam);
     f32x4 qk[2];
     chunk_grams<NK>(X, Q, tk, nullptr, Nm, qk);
     __syncthreads();
@@ -695,6 +708,7 @@ __global__ __launch_bounds__(512) void bwd_grads(BwdArgs a) {
     const bool lo = w < 4, val = n < NV, key = n < NK;
 
     // operands from memory, requested before the chunk's features
+    const float2 beta_lam = load_beta_lam(a, bh, t0);
     f32x4 vv[4], dov[4], sb[NK], s0t[NV], ht[NV];
     {
         const E *v = static_cast<const E *>(a.v) + rowbase * DV;
@@ -716,7 +730,7 @@ __global__ __launch_bounds__(512) void bwd_grads(BwdArgs a) {
         }
     }
 
-    chunk_features<E, DK>(a, bh, t0, X, Q, tk);
+    chunk_features<E, DK>(a, bh, t0, X, Q, tk, beta_lam);
     f32x4 qk[2];
     chunk_grams<NK>(X, Q, tk, SL, SN, qk);
     __syncthreads();

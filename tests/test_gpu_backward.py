@@ -218,3 +218,28 @@ def test_bwd_deterministic():
     for n in g1:
         assert np.array_equal(g1[n], g2[n]), n
     del torch
+
+
+def test_bwd_c2_full_shape_sampled_heads():
+    """The c2 workload shape (8 x 12 heads, T = 1024, d_k = d_v = 64, bf16) in
+    the launch configuration the bench times: all 96 heads in one call, fresh
+    state, no outgoing x_next gradient.  Eight heads spread over the batch are
+    compared with the fp64 oracle (heads are independent), to the bf16 bounds
+    above."""
+    from linear_recurrent_weight_amd.inputs import WORKLOADS, make_inputs, round_to_bf16
+    w = WORKLOADS["c2"]
+    B, H, T, dk, dv = w.batch, w.heads, w.seqlen, w.dk, w.dv
+    raw = make_inputs(w)
+    f = lambda a: round_to_bf16(np.asarray(a, np.float32)).astype(np.float64)
+    inp = dict(q=f(raw["q"]), k=f(raw["k"]), v=f(raw["v"]),
+               beta=np.asarray(raw["beta"], np.float64), lam=np.asarray(raw["lam"], np.float64))
+    rng = np.random.default_rng(2024)
+    up = dict(d_o=f(rng.standard_normal((B, H, T, dv))),
+              d_S_out=rng.standard_normal((B, H, dk, dv)).astype(np.float32).astype(np.float64))
+    print(f"[bwd] c2 full shape ({B},{H},{T},{dk},{dv}) bf16", flush=True)
+    got = run_gpu(inp, up, None, "bf16")
+    heads = np.unique(np.linspace(0, B * H - 1, 8).round().astype(int))
+    sel = lambda a: np.asarray(a).reshape(B * H, *np.asarray(a).shape[2:])[heads][None]
+    ref = run_oracle({n: sel(v) for n, v in inp.items()}, {n: sel(v) for n, v in up.items()}, None,
+                     eps=w.eps, eps_gamma=w.eps_gamma, eps_rms=w.eps_rms)
+    compare({n: sel(v) for n, v in got.items()}, ref, "bf16", "c2 sampled heads")
