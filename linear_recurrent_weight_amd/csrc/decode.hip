@@ -47,6 +47,27 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const E *kg = static_cast<const E *>(a.k) + size_t(bh) * dk;
     const E *vg = static_cast<const E *>(a.v) + size_t(bh) * dv;
 
+    // Every input is requested here, before any arithmetic, so that the
+    // step waits for one memory round trip: the state columns, the step's
+    // beta (per column for the per-column variants) and lambda, then the
+    // pair, the query and the next pair's feature.
+    float S[RPL][kCpw];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+        const int i = lane + 64 * r;
+#pragma unroll
+        for (int c = 0; c < kCpw; ++c)
+            S[r][c] = (a.S_in && i < dk) ? a.S_in[(size_t(bh) * dk + i) * dv + c0 + c] : 0.f;
+    }
+    float beta_c[kCpw];
+#pragma unroll
+    for (int c = 0; c < kCpw; ++c)
+        beta_c[c] = (VK == FALCON_V2 || VK == FALCON_V2A) ? a.beta[size_t(bh) * dv + c0 + c] : a.beta[bh];
+    const float lam = a.lambda[bh];
+    float y[kCpw];
+#pragma unroll
+    for (int c = 0; c < kCpw; ++c) y[c] = ld(vg, c0 + c);
+
     // this token's pair (x, y), query and the next pair's feature
     float x[RPL], q[RPL], kn[RPL];
 #pragma unroll
@@ -56,9 +77,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         q[r] = i < dk ? ld(qg, i) : 0.f;
         kn[r] = i < dk ? ld(kg, i) : 0.f;
     }
-    float y[kCpw];
-#pragma unroll
-    for (int c = 0; c < kCpw; ++c) y[c] = ld(vg, c0 + c);
     {
         float sq = 0.f, sk = 0.f;
 #pragma unroll
@@ -73,15 +91,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             q[r] *= scq;
             kn[r] *= sck;
         }
-    }
-
-    float S[RPL][kCpw];
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-        const int i = lane + 64 * r;
-#pragma unroll
-        for (int c = 0; c < kCpw; ++c)
-            S[r][c] = (a.S_in && i < dk) ? a.S_in[(size_t(bh) * dk + i) * dv + c0 + c] : 0.f;
     }
 
     // the window: the carried pairs (slot s holds the pair W-1-s before this
@@ -137,14 +146,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         for (int r = 0; r < RPL; ++r) n2 += x[r] * x[r];
         mu = wave_sum(n2);
     }
-    const float lam = a.lambda[bh];
     const float den = mu + lam + a.eps;
     const bool noop = a.fresh != 0;              // the fresh first step writes nothing
     float eta[kCpw], gam[kCpw];
 #pragma unroll
     for (int c = 0; c < kCpw; ++c) {
-        const float beta = (VK == FALCON_V2 || VK == FALCON_V2A) ? a.beta[size_t(bh) * dv + c0 + c] : a.beta[bh];
-        const float e = noop ? 0.f : step_eta(beta, den);
+        const float e = noop ? 0.f : step_eta(beta_c[c], den);
         eta[c] = e;
         gam[c] = 1.f - (noop ? 0.f : step_alpha(e, lam, a.eps_gamma));
     }
