@@ -199,8 +199,8 @@ struct A1Rows {
 //     into LDS; each block once per chunk;
 //   - wave w updates the state tiles (d tiles 2 (w / 4), + 1; value tile
 //     w % 4), S[d][j] += XT V by pair-contracting MFMAs from LDS, and
-//     (a1_output) writes them to the bf16 copy S^T[j][d] that the next chunk's
-//     outputs read (double-buffered by chunk parity);
+//     (a1_output) the next chunk writes them to the bf16 copy S^T[j][d] that
+//     its outputs read (after this chunk's closing barrier);
 //   - (a1_output) wave w forms the outputs of token tile n = 0, 0, 1, 1, 3,
 //     3, 2, 2 (w = 0..7) and value tiles 2 (w % 2), + 1:
 //     O^T (jt, n) = diag-scaled S^T Qh^T + V^T P^T, each score tile P^T of
@@ -248,8 +248,6 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
             const int dt = sd0 + h;
 #pragma unroll
             for (int r = 0; r < 4; ++r) S[h][r] = Se[(16 * dt + g4 + r) * D + 16 * sj + col];
-            // bf16 copy S^T [j][d] for the output products (buffer 0 of two)
-            *reinterpret_cast<uint2 *>(STb + (16 * sj + col) * PK + 16 * dt + g4) = pk4(S[h]);
         }
     } else {
 #pragma unroll
@@ -277,10 +275,16 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
 
     // the incoming x_0 (features, scale 1) of a continued sequence, loaded
     // once, outside the chunk loop (a conditional load inside it added a wait
-    // for every outstanding memory operation to each chunk)
-    uint4 x0r = make_uint4(0, 0, 0, 0);
-    float x0s = 0.f;
-    if (c_begin == 0 && row == 0 && a.xnext_in) x0r = feat8(a.xnext_in + size_t(bh) * D + 8 * part, x0s);
+    // for every outstanding memory operation to each chunk), and kept in LDS
+    // (registers would hold it through every chunk)
+    __shared__ __align__(16) uint4 x0r[8];
+    __shared__ float x0s;
+    if (c_begin == 0 && row == 0 && a.xnext_in) {
+        float ss;
+        x0r[part] = feat8(a.xnext_in + size_t(bh) * D + 8 * part, ss);
+        ss = group_sum<8>(ss);   // over the row's 8 lanes, all active here
+        if (part == 0) x0s = ss;
+    }
 
     A1Rows<OUT, WIN> rows;
     rows.load(a, c_begin, bh, row, part);
@@ -290,6 +294,14 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     for (int c = c_begin; c < c_end; ++c) {
         const int c0 = c * C, t = c0 + row;
+        if constexpr (OUT) {
+            // bf16 copy S^T [j][d] of the chunk's entry state for the output
+            // products; the previous chunk's last reads of the copy came
+            // before its closing barrier
+#pragma unroll
+            for (int h = 0; h < NS; ++h)
+                *reinterpret_cast<uint2 *>(STb + (16 * sj + col) * PK + 16 * (sd0 + h) + g4) = pk4(S[h]);
+        }
         // 1. rows to LDS as loaded; RMS scales; the step scalars
         {
             uint4 xr = rows.k;
@@ -298,14 +310,11 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
             if constexpr (OUT) sq = sumsq8(rows.q);
             const bool qok = t < T, kok = t >= 1 && t <= T, first = t == 0;
             const bool carry_x = first && a.xnext_in;
-            // x_0: features, scale 1 (selected per component: a select of
-            // whole vectors is lowered through private memory)
-            xr.x = carry_x ? x0r.x : xr.x;
-            xr.y = carry_x ? x0r.y : xr.y;
-            xr.z = carry_x ? x0r.z : xr.z;
-            xr.w = carry_x ? x0r.w : xr.w;
-            sk = carry_x ? x0s : sk;
             sk = group_sum<8>(sk);
+            if (carry_x) {   // x_0: features, scale 1 (row 0 of the first chunk, its 8 lanes together)
+                xr = x0r[part];
+                sk = x0s;
+            }
             const float sck = carry_x ? 1.f : (kok ? a1_rms_scale(sk, a.eps_rms, a.phi) : 0.f);
             const uint4 yr = qok ? rows.v : make_uint4(0, 0, 0, 0);
             *reinterpret_cast<uint4 *>(XB + row * PK + 8 * part) = xr;
@@ -437,19 +446,17 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
                 if constexpr (WIN) s = mfma16(ld4(xr + 64 + g4), ld4(vr + 64 + g4), s);
                 S[h] = s;
             }
-            if constexpr (OUT) {
-                // the next chunk's S^T copy goes to the other buffer: its last
-                // reads were before the previous chunk's closing barrier
-                bf16_t *stn = STb + ((c + 1 - c_begin) & 1) * (D * PK);
-#pragma unroll
-                for (int h = 0; h < NS; ++h)
-                    *reinterpret_cast<uint2 *>(stn + (16 * sj + col) * PK + 16 * (sd0 + h) + g4) = pk4(S[h]);
-            }
         }
         if constexpr (OUT) {
             // 5. outputs O^T (jt, n) = diag-scaled S^T Qh^T + V^T P^T, from the
             //    entry state's copy
-            const bf16_t *stc = STb + ((c - c_begin) & 1) * (D * PK);
+            const bf16_t *stc = STb;
+            // lane quantities formed afresh from an opaque copy of the lane
+            // index: hoisted out of the chunk loop, the band's per-element
+            // indexes and masks would hold registers through every chunk
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const int col = ln & 15, g4 = 4 * (ln >> 4), k8 = 8 * (ln >> 4);
             bf16_t *og = static_cast<bf16_t *>(a.o) + size_t(bh) * T * D + g4;
             const int n = wave < 4 ? wave >> 1 : 3 - ((wave - 4) >> 1);
             const int tq = 16 * n + col;   // this lane's token
@@ -599,7 +606,7 @@ __global__ __launch_bounds__(NTH, 4) void a1_output(ChunkAArgs a) {
     __shared__ __align__(16) float hsx[2][16];
     __shared__ __align__(16) bf16_t XT[D * G::PX];
     __shared__ __align__(16) bf16_t VT[D * G::PX];
-    __shared__ __align__(16) bf16_t STb[2 * D * PK];
+    __shared__ __align__(16) bf16_t STb[D * PK];
     __shared__ __align__(16) float tv[kNtv][C];
     __shared__ __align__(16) float pv[kNpv][G::NP];
     __shared__ __align__(16) float bf[WIN ? FALCON_MAX_WINDOW - 1 : 1][C];
