@@ -28,7 +28,9 @@
 //   a1_segment (parallel over segments): the segment's aggregate write
 //       D_g = sum over its chunks c of e^{b_end - b_end(c)} dS_c and its carry,
 //       and the boundary state (x_next, the last W - 1 pairs);
-//   a1_segscan (parallel over state entries): S_{g+1} = Gamma_g S_g + D_g;
+//   a1_segscan (parallel over state entries, more than kFoldSegs segments):
+//       S_{g+1} = Gamma_g S_g + D_g (with fewer, every output walk folds its
+//       own entry state from the aggregates);
 //   a1_output  (parallel over segments): walks the segment's chunks from its
 //       entry state and writes o.
 // Both walking kernels put the raw rows (q, k_{t-1}, v) into LDS as loaded and
@@ -151,6 +153,8 @@ __device__ __forceinline__ void halo_pair(const ChunkAArgs &a, int bh, int tau, 
     sc = xz ? 0.f : (raw ? a1_rms_scale(ss, a.eps_rms, a.phi) : 1.f);
 }
 
+constexpr int kFoldSegs = chunk_a1_fold_segments;
+
 // s_waitcnt immediate (gfx9 encoding) that waits for all vector memory
 // operations: vmcnt 0 (bits 3:0 and 15:14), expcnt 7 and lgkmcnt 15 (no wait)
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -242,12 +246,50 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
 
     f32x4 S[NS];
     if constexpr (OUT) {
-        const float *Se = a.Sseg + (size_t(bh) * a.nseg + seg) * D * D;
+        if (a.nseg <= kFoldSegs) {
+            // entry state folded here from the incoming state and the
+            // earlier segments' aggregates, S_{g+1} = Gamma_g S_g + D_g (all
+            // loads first)
+            constexpr int NBF = 4;   // aggregates loaded per batch
+            const size_t e0 = size_t(16 * sd0 + g4) * D + 16 * sj + col;
+            float Sv[NS][4];
 #pragma unroll
-        for (int h = 0; h < NS; ++h) {
-            const int dt = sd0 + h;
+            for (int h = 0; h < NS; ++h)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) S[h][r] = Se[(16 * dt + g4 + r) * D + 16 * sj + col];
+                for (int r = 0; r < 4; ++r)
+                    Sv[h][r] = a.S_in ? a.S_in[size_t(bh) * D * D + e0 + size_t(16 * h + r) * D] : 0.f;
+            for (int g0 = 0; g0 < seg; g0 += NBF) {
+                float Dv[NBF][NS][4], Gv[NBF];
+#pragma unroll
+                for (int u = 0; u < NBF; ++u) {
+                    const int gc = g0 + u < seg ? g0 + u : g0;   // loads stay inside the segments present
+                    const float *Dg = a.Dseg + (size_t(bh) * a.nseg + gc) * D * D + e0;
+#pragma unroll
+                    for (int h = 0; h < NS; ++h)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) Dv[u][h][r] = Dg[size_t(16 * h + r) * D];
+                    Gv[u] = a.Gseg[size_t(bh) * a.nseg + gc];
+                }
+#pragma unroll
+                for (int u = 0; u < NBF; ++u)
+#pragma unroll
+                    for (int h = 0; h < NS; ++h)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            Sv[h][r] = g0 + u < seg ? Gv[u] * Sv[h][r] + Dv[u][h][r] : Sv[h][r];
+            }
+#pragma unroll
+            for (int h = 0; h < NS; ++h)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) S[h][r] = Sv[h][r];
+        } else {
+            const float *Se = a.Sseg + (size_t(bh) * a.nseg + seg) * D * D;
+#pragma unroll
+            for (int h = 0; h < NS; ++h) {
+                const int dt = sd0 + h;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) S[h][r] = Se[(16 * dt + g4 + r) * D + 16 * sj + col];
+            }
         }
     } else {
 #pragma unroll
@@ -293,6 +335,13 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
     // chunk as it is needed instead of for all of them at the loop head.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     for (int c = c_begin; c < c_end; ++c) {
+        // lane quantities formed afresh in every chunk from an opaque copy of
+        // the thread index (hoisted, their derived addresses would hold
+        // registers through the loop)
+        int tid_o = tid;
+        asm volatile("" : "+v"(tid_o));
+        const int lane = tid_o & 63, col = lane & 15, g4 = 4 * (lane >> 4), k8 = 8 * (lane >> 4);
+        const int row = tid_o >> 3, part = tid_o & 7;
         const int c0 = c * C, t = c0 + row;
         if constexpr (OUT) {
             // bf16 copy S^T [j][d] of the chunk's entry state for the output
@@ -451,12 +500,6 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
             // 5. outputs O^T (jt, n) = diag-scaled S^T Qh^T + V^T P^T, from the
             //    entry state's copy
             const bf16_t *stc = STb;
-            // lane quantities formed afresh from an opaque copy of the lane
-            // index: hoisted out of the chunk loop, the band's per-element
-            // indexes and masks would hold registers through every chunk
-            int ln = lane;
-            asm volatile("" : "+v"(ln));
-            const int col = ln & 15, g4 = 4 * (ln >> 4), k8 = 8 * (ln >> 4);
             bf16_t *og = static_cast<bf16_t *>(a.o) + size_t(bh) * T * D + g4;
             const int n = wave < 4 ? wave >> 1 : 3 - ((wave - 4) >> 1);
             const int tq = 16 * n + col;   // this lane's token
@@ -524,6 +567,17 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
         if constexpr (OUT) __syncthreads();
     }
 
+    if constexpr (OUT) {
+        // with the entry states folded in the walks, the final state comes
+        // from the last segment's walk
+        if (a.nseg <= kFoldSegs && c_end == a.nchunks && a.S_out) {
+#pragma unroll
+            for (int h = 0; h < NS; ++h)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    a.S_out[size_t(bh) * D * D + size_t(16 * (sd0 + h) + g4 + r) * D + 16 * sj + col] = S[h][r];
+        }
+    }
     if constexpr (!OUT) {
         // segment aggregate D_g (fp32, [d][j]) and its carry
         float *Dg = a.Dseg + (size_t(bh) * a.nseg + seg) * D * D;
@@ -624,7 +678,10 @@ __global__ __launch_bounds__(NTH, 4) void a1_output(ChunkAArgs a) {
 // w_t = eta_t / B_t and log2 gamma_t to the workspace (0 past T and at a
 // fresh first token).
 __global__ __launch_bounds__(64) void a3_window(ChunkAArgs a) {
-    __shared__ __align__(16) bf16_t XR[80 * PK];
+    // pair rows without padding, the 16-byte pieces of row p at positions
+    // piece ^ (p % 8) (conflict-free operand reads); 13 KB, so that every
+    // chunk of the workload finds a slot at once (twelve per CU)
+    __shared__ __align__(16) bf16_t XR[80 * D];
     __shared__ float sx[80];
     __shared__ float band[80][8];
     const int c = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
@@ -660,17 +717,20 @@ __global__ __launch_bounds__(64) void a3_window(ChunkAArgs a) {
             ss = group_sum<8>(ss);
             sc = carry_x ? 1.f : ((tau >= 1 && tau < T) ? a1_rms_scale(ss, a.eps_rms, a.phi) : 0.f);
         }
-        *reinterpret_cast<uint4 *>(XR + p * PK + 8 * part) = xr;
+        *reinterpret_cast<uint4 *>(XR + p * D + 8 * (part ^ (p & 7))) = xr;
         if (part == 0) sx[p] = sc;
     }
     __syncthreads();
     // band of the pair Gram: tiles (m, m) for m = 0..4 and (m, m - 1) for m = 1..4
     for (int tile = 0; tile < 9; ++tile) {
         const int m = tile < 5 ? tile : tile - 4, mp = tile < 5 ? m : m - 1;
-        const bf16_t *ar = XR + (16 * m + col) * PK + k8, *br = XR + (16 * mp + col) * PK + k8;
+        // row r's elements 8 k .. + 7 (piece k), for this lane's k8 and the
+        // two k halves
+        auto piece = [&](int r, int k) { return ld8(XR + r * D + 8 * (k ^ (r & 7))); };
+        const int ra = 16 * m + col, rb = 16 * mp + col, kq = k8 >> 3;
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        f32x4 g = mfma32(ld8(ar), ld8(br), z);
-        g = mfma32(ld8(ar + 32), ld8(br + 32), g);
+        f32x4 g = mfma32(piece(ra, kq), piece(rb, kq), z);
+        g = mfma32(piece(ra, kq + 4), piece(rb, kq + 4), g);
         // lane holds x_p . x_q for p = 16 m + g4 + r, q = 16 mp + col
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -738,10 +798,10 @@ template <bool WIN>
 void launch_walks(const ChunkAArgs &a, hipStream_t s, Marks *m) {
     a1_segment<WIN><<<dim3(a.nseg, a.BH), NTH, 0, s>>>(a);
     m->mark(s);
-    // one batch of loads covers every segment when there are at most 8
-    if (a.nseg <= 8) a1_segscan<8><<<dim3(a.BH, D * D / 256), 256, 0, s>>>(a);
-    else a1_segscan<32><<<dim3(a.BH, D * D / 256), 256, 0, s>>>(a);
-    m->mark(s);
+    if (a.nseg > kFoldSegs) {
+        a1_segscan<32><<<dim3(a.BH, D * D / 256), 256, 0, s>>>(a);
+        m->mark(s);
+    }
     a1_output<WIN><<<dim3(a.nseg, a.BH), NTH, 0, s>>>(a);
     m->mark(s);
 }

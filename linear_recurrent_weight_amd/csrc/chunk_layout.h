@@ -121,6 +121,10 @@ inline bool chunk_a1_supported(bool bf16, int variant, int window, int dk, int d
     const bool var_ok = (variant == FALCON_V1A && window == 1) || (variant == FALCON_V3A && window >= 1);
     return bf16 && var_ok && dk == 64 && dv == 64;
 }
+// Up to this many segments per head, each output walk of that path folds its
+// own entry state from the segment aggregates (no scan launch); more segments
+// take the scan.
+constexpr int chunk_a1_fold_segments = 8;
 // chunks per segment of that path: the fewest that keep all segments of all
 // heads resident at once (two 512-thread workgroups per compute unit, 256
 // units), so that the walks run as one wave of workgroups

@@ -50,6 +50,8 @@ const char *const kNamesChunkF1[] = {"feature", "chunk_f1_prep", "chunk_f1_scan"
 const char *const kNamesChunkA[] = {"a_segment", "a_segscan", "a_output"};
 const char *const kNamesChunkA1[] = {"a1_segment", "a1_segscan", "a1_output"};
 const char *const kNamesChunkA3[] = {"a3_window", "a1_segment", "a1_segscan", "a1_output"};
+const char *const kNamesChunkA1Fold[] = {"a1_segment", "a1_output"};
+const char *const kNamesChunkA3Fold[] = {"a3_window", "a1_segment", "a1_output"};
 const char *const kNamesChunkF2[] = {"chunk_f2"};
 const char *const kNamesChunkF2A[] = {"chunk_f2a"};
 const char *const kNamesChunkF3[] = {"feature", "f3_prep", "f3_scan"};
@@ -350,6 +352,10 @@ extern "C" const char *falcon_kernel_name(const falcon_fwd_args *args, int i) {
         case Path::kChunkF1: return i < 3 ? kNamesChunkF1[i] : nullptr;
         case Path::kChunkA: return i < 3 ? kNamesChunkA[i] : nullptr;
         case Path::kChunkA1:
+            if (p.nseg <= chunk_a1_fold_segments) {
+                if (p.window > 1) return i < 3 ? kNamesChunkA3Fold[i] : nullptr;
+                return i < 2 ? kNamesChunkA1Fold[i] : nullptr;
+            }
             if (p.window > 1) return i < 4 ? kNamesChunkA3[i] : nullptr;
             return i < 3 ? kNamesChunkA1[i] : nullptr;
         case Path::kChunkF2: return i < 1 ? kNamesChunkF2[i] : nullptr;

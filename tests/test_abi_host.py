@@ -308,19 +308,22 @@ def _segments(bh, nchunks):
 
 
 @pytest.mark.parametrize("variant,window", [("F1A", 1), ("F3A", 2), ("F3A", 8)])
-def test_inner_product_bf16_d64_path(lib, variant, window):
+@pytest.mark.parametrize("B,H,T", [(2, 12, 16384), (8, 12, 2048)])
+def test_inner_product_bf16_d64_path(lib, variant, window, B, H, T):
     """bf16 Falcon-1A / 3A at d_k = d_v = 64 take the register-transpose
     kernels (a window pass first when W > 1); their workspace is the segment
     writes and entry states (fp32 [d_k][d_v]) and carries, plus w_t and
-    log2 gamma_t per token with a window."""
-    B, H, T = 2, 12, 16384
+    log2 gamma_t per token with a window.  With at most 8 segments per head
+    the output walks fold their entry states themselves (no scan launch)."""
     a = args(variant=variant, window=window, batch=B, heads=H, seqlen=T)
     names = _names(lib, a)
-    want = (["a3_window"] if window > 1 else []) + ["a1_segment", "a1_segscan", "a1_output"]
-    assert names == want
     nch = T // 64
     g = _segments(B * H, nch)
     nseg = -(-nch // g)
+    scan = ["a1_segscan"] if nseg > 8 else []
+    want = (["a3_window"] if window > 1 else []) + ["a1_segment"] + scan + ["a1_output"]
+    assert names == want
+    assert (nseg > 8) == ((B, H, T) == (2, 12, 16384))
     align = lambda n: -(-n // 256) * 256
     st = B * H * nseg * 64 * 64 * 4
     n = align(st) + align(B * H * nseg * 4) + align(st)
