@@ -70,7 +70,7 @@ KERNEL_SOURCES = {"passthrough": "feature.hip", "feature": "feature.hip", "recur
                   "decode": "decode.hip",
                   "chunk_f1_prep": "chunk_f1.hip", "chunk_f1_scan": "chunk_f1.hip",
                   "chunk_f2": "chunk_f2.hip", "chunk_f2a": "chunk_f2a.hip",
-                  "f3_prep": "chunk_f3.hip", "f3_scan": "chunk_f3.hip",
+                  "f3_prep": "chunk_f3.hip", "f3_scan": "chunk_f3.hip", "f3_xfer": "chunk_f3_xfer.hip",
                   "f1_xfer": "chunk_f1_xfer.hip", "f1_carry": "chunk_f1_xfer.hip",
                   "f1_segmap": "chunk_f1_xfer.hip", "f1_segscan": "chunk_f1_xfer.hip",
                   "bwd_states": "falcon_bwd.hip", "bwd_sweep": "falcon_bwd.hip", "bwd_reduce": "falcon_bwd.hip",

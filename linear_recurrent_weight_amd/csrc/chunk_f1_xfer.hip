@@ -926,6 +926,11 @@ void launch_chunk_f1_xfer(const F1XferArgs &a, int slice, hipStream_t s, Marks *
         case 64: launch_xfer<64>(a, s, m); break;
         default: launch_xfer<128>(a, s, m); break;
     }
+    (void)slice;   // f1_xfer_slice: 32 columns for every d_v this path takes
+    launch_f1_walk(a, s, m);
+}
+
+void launch_f1_walk(const F1XferArgs &a, hipStream_t s, Marks *m) {
     if (a.nseg > 1) {
         switch (a.dv) {
             case 32: launch_segments<32>(a, s, m); break;
@@ -933,7 +938,6 @@ void launch_chunk_f1_xfer(const F1XferArgs &a, int slice, hipStream_t s, Marks *
             default: launch_segments<128>(a, s, m); break;
         }
     }
-    (void)slice;   // f1_xfer_slice: 32 columns for every d_v this path takes
     launch_carry<32>(a, s, m);
 }
 

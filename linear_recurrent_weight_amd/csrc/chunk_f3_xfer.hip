@@ -1,0 +1,428 @@
+// Chunk-parallel Falcon-3 forward for bf16 inputs, d_k = d_v = 64 and a
+// window W of 2, 4 or 8 pairs (summary §4.4 "Mini-batch Update Rule for
+// Regression (Falcon-3)", §C.7, §H.3 "Mapping Falcon-3 to ParallelFlow"),
+// through the same per-chunk transfer operators as the bf16 Falcon-1 path.
+//
+// Token t writes the W pairs of its window, each with the residual at the
+// state before t and the weight w_t = eta_t / B_t.  Stacking the W rows of
+// every token (row r = (token tau, slot k), pair tau - W + 1 + k) turns a
+// chunk into a unit-lower system whose rows of one token do not interact:
+// with the chunk-local log-prefix b (base 2, restarted at 0 per chunk),
+//     u_r + w_r sum_{r': tau' < tau} 2^{b_{tau-1} - b_tau'} (x_r . x_r') u_r'
+//         = w_r (y_r - 2^{b_{tau-1}} S_0^T x_r),
+// so that, as for Falcon-1, u = Ut - W S_0 with [-W | Ut] = Z = (I + N)^{-1} R,
+// R = [-diag(w 2^{b_{tau-1}}) X | diag(w) Y], and the chunk folds into
+//     A = sum_r 2^{b_C - b_tau} x_r Z_W,r,   B = sum_r 2^{b_C - b_tau} x_r Z_U,r,
+//     [G | H]_t = [2^{b_t} qh_t | 0] + sum_{r: tau <= t} 2^{b_t - b_tau} (qh_t . x_r) Z_r
+// (S_C = 2^{b_C} S_0 + A S_0 + B, o_t = G_t S_0 + H_t).
+//
+// A chunk of 64 tokens has 64 W stacked rows.  It is worked in W sub-chunks
+// of 64 / W tokens (64 rows each, as in Falcon-1).  The rows of earlier
+// sub-chunks enter a sub-chunk only through
+//     K = sum_{r earlier} 2^{b_e - b_tau} x_r Z_r        [d_k x (d_k + d_v)],
+// b_e the log-prefix at the end of the previous sub-chunk (every factor at
+// most 1): the residuals lose w_r 2^{b_{tau-1} - b_e} (X K)_r, the outputs
+// gain 2^{b_t - b_e} qh_t^T K, and K advances by 2^{b_e' - b_e} and the
+// sub-chunk's own rows.  After the last sub-chunk K = [A | B].  The
+// sub-chunk's system is solved as in the Falcon-1 kernel: diagonal 16-row
+// blocks of I + N inverted in fp32, forward substitution over the blocks on
+// MFMA, one column tile of Z per wave, in registers; K stays in the waves'
+// accumulators (fp32) with a bf16 copy in LDS for the products that read it.
+//
+// One workgroup per (chunk, head), chunk-major; the records go to the
+// workspace in the Falcon-1 layout, and f1_carry walks them.
+#include "chunk_layout.h"
+#include "kernels.h"
+#include "mma.h"
+
+namespace falcon {
+namespace {
+
+constexpr int C = kChunk;       // tokens of a chunk; stacked rows of a sub-chunk
+constexpr int D = 64;           // d_k = d_v
+constexpr int PK = 72;          // bf16 pitch of LDS rows of 64 elements
+constexpr int NBP = 20;         // bf16 pitch of the 16 x 16 solve blocks
+constexpr int LFB = 16 * 16 + 4;
+constexpr int NTH = 512;        // 8 waves
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t pk2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+__device__ __forceinline__ uint2 pk4(const f32x4 &v) { return make_uint2(pk2(v[0], v[1]), pk2(v[2], v[3])); }
+__device__ __forceinline__ float lo16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ f32x4 unpk4(const uint2 &u) { return f32x4{lo16(u.x), hi16(u.x), lo16(u.y), hi16(u.y)}; }
+__device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(const s16x4 &a, const s16x4 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ s16x4 as_s4(const uint2 &u) { return __builtin_bit_cast(s16x4, u); }
+template <class P>
+__device__ __forceinline__ bf16x8 ld8(const P *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ void put2(void *p, const uint2 &v) { *reinterpret_cast<uint2 *>(p) = v; }
+template <int CTRL>
+__device__ __forceinline__ float quad_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// 8 fp32 values -> 8 bf16 (16 bytes)
+__device__ __forceinline__ uint4 pk8(const float *f) {
+    return make_uint4(pk2(f[0], f[1]), pk2(f[2], f[3]), pk2(f[4], f[5]), pk2(f[6], f[7]));
+}
+
+// per stacked row of a sub-chunk: w_r, w_r 2^{b_{tau-1}}, w_r 2^{b_{tau-1} - b_e}
+// (residual cross term and Gram row factor), 2^{b_e - b_tau} (separable
+// column factor), 2^{b_e' - b_tau} (weight of the row in K), and b_{tau-1} -
+// b_e, b_tau - b_e for the pairwise form
+enum { rW = 0, rXf, rRs, rCs, rEw, rBp, rBt, kNr };
+// per token slot of a sub-chunk: 2^{b_t - b_e}, 2^{b_t}, b_t - b_e
+enum { tQs = 0, tGd, tB, kNt };
+
+// The raw data of one sub-chunk: for stacked row tid / 8 its pair's 8
+// features (part tid % 8) and 8 values; for token slot tid / 8 its query
+// piece.  Loaded unconditionally from clamped rows; pairs before position 0
+// come from the incoming tail when the rows are stored.
+struct F3Rows {
+    uint4 x, y, q;
+    __device__ __forceinline__ void load(const ChunkF3Args &a, int bh, int c, int s, int W, int CT, int TR,
+                                         int row, int part) {
+        const int tau = row / W, k = row % W;
+        const int t = c * C + s * CT + tau, p = t - (W - 1) + k;
+        const bf16_t *xn = static_cast<const bf16_t *>(a.xn) + size_t(bh) * a.Tpad * D;
+        const bf16_t *qn = static_cast<const bf16_t *>(a.qn) + size_t(bh) * a.Tpad * D;
+        const bf16_t *v = static_cast<const bf16_t *>(a.v) + size_t(bh) * a.T * D;
+        const int pc = p < 0 ? 0 : p;                      // p <= t < Tpad
+        const int py = p < 0 ? 0 : (p < a.T ? p : a.T - 1);
+        x = *reinterpret_cast<const uint4 *>(xn + size_t(pc) * D + 8 * part);
+        y = *reinterpret_cast<const uint4 *>(v + size_t(py) * D + 8 * part);
+        const int tq = c * C + s * CT + (row < TR ? row : 0);
+        q = *reinterpret_cast<const uint4 *>(qn + size_t(tq) * D + 8 * part);
+    }
+};
+
+template <int W>
+__global__ __launch_bounds__(NTH, 4) void f3_xfer(ChunkF3Args a) {
+    static_assert(W == 2 || W == 4 || W == 8, "windows whose token blocks tile 16 rows");
+    constexpr int CT = C / W;                      // tokens of a sub-chunk
+    constexpr int NTT = CT >= 16 ? CT / 16 : 1;    // token tiles of a sub-chunk
+    constexpr int TR = 16 * NTT;                   // token slots (rows of QB, PB)
+    constexpr size_t RB = f1_xfer_bytes(D);
+    __shared__ __align__(16) bf16_t XB[C * PK];     // stacked pair features [r][d]
+    __shared__ __align__(16) bf16_t YB[C * PK];     // stacked pair values [r][j]
+    __shared__ __align__(16) bf16_t XW[D * PK];     // (diag(2^{b_e' - b_tau}) X)^T [d][r]
+    __shared__ __align__(16) bf16_t QB[TR * PK];    // queries of the sub-chunk's tokens [t][d]
+    __shared__ __align__(16) bf16_t PB[TR * PK];    // scores [t][r]
+    __shared__ __align__(16) bf16_t KT[2 * D * PK]; // K^T [j'][d], bf16
+    __shared__ __align__(16) bf16_t NB[6][16 * NBP];   // -N below the diagonal blocks
+    __shared__ __align__(16) bf16_t DB[4][16 * NBP];   // inverses of the diagonal blocks of I + N
+    __shared__ __align__(16) float LF[4 * LFB];         // the diagonal blocks L_J, fp32 row-major
+    __shared__ __align__(16) float rs[kNr][C];
+    __shared__ __align__(16) float ts[kNt][TR];
+    __shared__ float cb[C], cw[C];                      // chunk tokens: b_t, w_t
+    __shared__ __align__(16) bf16x8 IDT[2][64];         // column pickers
+
+    const int c = blockIdx.x / a.BH, bh = blockIdx.x % a.BH;   // chunk-major: a head's chunks on one XCD
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, g4 = 4 * (lane >> 4), k8 = 8 * (lane >> 4), kq = lane >> 4;
+    const int row = tid >> 3, part = tid & 7;
+    const int T = a.T, H = W - 1;
+    char *rec = static_cast<char *>(a.ops) + (size_t(bh) * a.nchunks + c) * RB;
+
+    if (tid < 128) {
+        typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+        const int h = tid >> 6;
+        u16x8 u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) u[e] = (k8 + e == 16 * h + col) ? 0x3F80 : 0;   // bf16 1.0
+        IDT[h][lane] = __builtin_bit_cast(bf16x8, u);
+    }
+    // the chunk's step scalars (wave 0, lane = token): b_t (base 2, restarted
+    // at 0) and w_t = eta_t / B_t, B_t the pairs in the window of t
+    if (wave == 0) {
+        const int t = c * C + lane;   // < Tpad (padding tokens have eta = alpha = 0)
+        const size_t ft = size_t(bh) * a.Tpad + t;
+        const float b = wave_inclusive_scan(log2_1m(a.alpha[ft]));
+        const long long pairs = (long long)a.n_tail_in + t + 1;
+        const int nb = pairs < W ? int(pairs) : W;
+        cb[lane] = b;
+        cw[lane] = t < T ? a.eta[ft] / float(nb) : 0.f;
+        if (lane == 63) *reinterpret_cast<float *>(rec + f1_xfer_scal_off(D)) = ex2(b);
+    }
+
+    F3Rows rows;
+    rows.load(a, bh, c, 0, W, CT, TR, row, part);
+    f32x4 K[4];   // K tiles (rows d = 16 m + g4 .., columns j' = 16 wave + col), fp32
+#pragma unroll
+    for (int m = 0; m < 4; ++m) K[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // rows (pitch PK) of a 16 x 32 block, 16 of whose columns (block n of 16)
+    // come back transposed into the accumulator layout
+    auto transposed = [&](const bf16_t *src, int m, int n) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        return mfma(ld8(src + (16 * m + col) * PK + 32 * (n >> 1) + k8), IDT[n & 1][lane], z);
+    };
+    auto tok4 = [&](const bf16_t *base, int r, int I) {
+        return as_s4(*reinterpret_cast<const uint2 *>(base + r * PK + 16 * I + g4));
+    };
+
+    for (int s = 0; s < W; ++s) {
+        // 1. the sub-chunk's rows to LDS (pairs before position 0 from the
+        //    incoming tail, pairs that do not exist zero), then the next
+        //    sub-chunk's loads
+        {
+            const int tau = row / W, k = row % W;
+            const int t = c * C + s * CT + tau, p = t - H + k;
+            uint4 xr = rows.x, yr = rows.y;
+            if (p < 0) {
+                xr = make_uint4(0, 0, 0, 0);
+                yr = xr;
+                if (p >= -a.n_tail_in) {
+                    const float *tx = a.tailx_in + (size_t(bh) * H + H + p) * D + 8 * part;
+                    const float *ty = a.taily_in + (size_t(bh) * H + H + p) * D + 8 * part;
+                    xr = pk8(tx);
+                    yr = pk8(ty);
+                }
+            } else if (p >= T) {
+                yr = make_uint4(0, 0, 0, 0);
+            }
+            *reinterpret_cast<uint4 *>(XB + row * PK + 8 * part) = xr;
+            *reinterpret_cast<uint4 *>(YB + row * PK + 8 * part) = yr;
+            if (row < TR)
+                *reinterpret_cast<uint4 *>(QB + row * PK + 8 * part) = row < CT ? rows.q : make_uint4(0, 0, 0, 0);
+            if (s + 1 < W) rows.load(a, bh, c, s + 1, W, CT, TR, row, part);
+        }
+        __syncthreads();
+
+        // 2. row and token scalars (every wave forms the same values)
+        const float b_e = s > 0 ? cb[s * CT - 1] : 0.f;
+        const float b_e2 = cb[s * CT + CT - 1];
+        const bool sep = b_e2 >= b_e - 100.f;
+        {
+            const int tc = s * CT + lane / W;
+            const float w = cw[tc], bt = cb[tc], bp = tc > 0 ? cb[tc - 1] : 0.f;
+            rs[rW][lane] = w;
+            rs[rXf][lane] = w * ex2(bp);
+            rs[rRs][lane] = w * ex2(bp - b_e);
+            rs[rCs][lane] = sep ? ex2(b_e - bt) : 0.f;
+            rs[rEw][lane] = ex2(b_e2 - bt);
+            rs[rBp][lane] = bp - b_e;
+            rs[rBt][lane] = bt - b_e;
+            if (lane < TR) {
+                const bool live = lane < CT;
+                const float btk = live ? cb[s * CT + lane] : b_e2;
+                ts[tQs][lane] = live ? ex2(btk - b_e) : 0.f;
+                ts[tGd][lane] = live ? ex2(btk) : 0.f;
+                ts[tB][lane] = btk - b_e;
+            }
+        }
+        wave_lds_sync();
+
+        // 3. Gram blocks, scores, diagonal inverses, transposes of x
+        //    Gram N_ij = w_i 2^{b_{tau_i - 1} - b_tau_j} x_i . x_j for tau_j < tau_i
+        //    (rows of different 16-row blocks always belong to different
+        //    tokens); scores P_tj = 2^{b_t - b_tau_j} qh_t . x_j for tau_j <= t
+        auto gram_scale = [&](int i, int j) {   // factor of entry (i, j)
+            return sep ? rs[rRs][i] * rs[rCs][j] : rs[rW][i] * ex2(rs[rBp][i] - rs[rBt][j]);
+        };
+        auto score_scale = [&](int t, int j) {
+            return sep ? ts[tQs][t] * rs[rCs][j] : ex2(ts[tB][t] - rs[rBt][j]);
+        };
+        // job 0-5: Gram block (1,0) (2,0) (2,1) (3,0) (3,1) (3,2); job 6 ..:
+        // score tile (token tile, row block J); the tile is formed
+        // transposed (rows of x as the A operand): lane (col, g4) gets
+        // row i = 16 I + col at columns j = 16 J + g4 .. + 3
+        auto job = [&](int jb) {
+            const bool isG = jb < 6;
+            const int tt = isG ? 0 : (jb - 6) >> 2;
+            const int I = isG ? (0xFE9 >> (2 * jb)) & 3 : tt;
+            const int J = isG ? (0x910 >> (2 * jb)) & 3 : (jb - 6) & 3;
+            const bf16_t *ar = (isG ? XB : QB) + (16 * I + col) * PK + k8;
+            const bf16_t *br = XB + (16 * J + col) * PK + k8;
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            f32x4 acc = mfma(ld8(br), ld8(ar), z);
+            acc = mfma(ld8(br + 32), ld8(ar + 32), acc);
+            const int i = 16 * I + col, j0 = 16 * J + g4;
+            f32x4 v;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = j0 + r;
+                if (isG) {
+                    v[r] = -acc[r] * gram_scale(i, j);
+                } else {
+                    const bool live = i < CT && (j / W) <= i;   // token of row j up to slot i
+                    v[r] = live ? acc[r] * score_scale(i, j) : 0.f;
+                }
+            }
+            put2(isG ? NB[jb] + col * NBP + g4 : PB + i * PK + j0, pk4(v));
+        };
+        constexpr int NJ = 6 + 4 * NTT;   // jobs: 6 Gram blocks, the score tiles
+        if (wave < 4) {
+            const int J = wave;
+            {   // L_J row-major in fp32: the block X_J X_J^T is symmetric, so
+                // the accumulator tile also holds row col of L_J at columns
+                // g4 .. + 3; entries of a later token than the column's
+                const bf16_t *xr = XB + (16 * J + col) * PK + k8;
+                f32x4 g = {0.f, 0.f, 0.f, 0.f};
+                g = mfma(ld8(xr), ld8(xr), g);
+                g = mfma(ld8(xr + 32), ld8(xr + 32), g);
+                const int i = 16 * J + col, j0 = 16 * J + g4;
+                f32x4 l;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) l[r] = (j0 + r) / W < i / W ? g[r] * gram_scale(i, j0 + r) : 0.f;
+                *reinterpret_cast<f32x4 *>(&LF[J * LFB + col * 16 + g4]) = l;
+            }
+            wave_lds_sync();
+            // lane (r = lane / 4, h = lane % 4): elements 4 h .. + 3 of row r of
+            // D_J = (I + L_J)^{-1}, from d (I + L_J) = e_r, right-looking over
+            // the columns from the last
+            const int r = lane >> 2, h = lane & 3;
+            const float *lf = LF + J * LFB + 4 * h;
+            f32x4 dq;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dq[e] = 4 * h + e == r ? 1.f : 0.f;
+#pragma unroll
+            for (int k = 15; k > 0; --k) {
+                const float x = dq[k & 3];
+                const int hk = k >> 2;
+                const float dk = hk == 0 ? quad_bcast<0x00>(x) : hk == 1 ? quad_bcast<0x55>(x)
+                               : hk == 2 ? quad_bcast<0xAA>(x) : quad_bcast<0xFF>(x);
+                dq -= dk * *reinterpret_cast<const f32x4 *>(lf + k * 16);
+            }
+            put2(DB[J] + r * NBP + 4 * h, pk4(dq));
+        }
+        // waves 0-3 take the score tiles, waves 4-7 the Gram blocks
+        if (wave < 4) {
+            for (int jb = 6 + wave; jb < NJ; jb += 4) job(jb);
+        } else {
+            for (int jb = wave - 4; jb < 6; jb += 4) job(jb);
+        }
+        {   // (diag(2^{b_e' - b_tau}) x)^T, tile (row block m, d block n): two per wave
+            const int m = wave >> 1;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int n = 2 * (wave & 1) + u;
+                const f32x4 ew = *reinterpret_cast<const f32x4 *>(&rs[rEw][16 * m + g4]);
+                put2(XW + (16 * n + col) * PK + 16 * m + g4, pk4(transposed(XB, m, n) * ew));
+            }
+        }
+        __syncthreads();
+
+        // 4. Z = (I + N)^{-1} R, column tile n = wave of R = [x part | value
+        //    part], R = [-diag(w 2^{b_{tau-1}}) X | diag(w) Y] - diag(w
+        //    2^{b_{tau-1} - b_e}) X K, by forward substitution over 16-row
+        //    blocks in registers
+        const int n = wave;
+        const bool xp = n < 4;
+        f32x4 r0[4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            const f32x4 sc = *reinterpret_cast<const f32x4 *>(&rs[xp ? rXf : rW][16 * I + g4]);
+            r0[I] = xp ? transposed(XB, I, n) * -sc : transposed(YB, I, n - 4) * sc;
+            if (s > 0) {   // cross term: (X K)[r][j'] with K^T rows j' = 16 n + col
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                const bf16_t *xr = XB + (16 * I + col) * PK + k8, *kr = KT + (16 * n + col) * PK + k8;
+                f32x4 cr = mfma(ld8(xr), ld8(kr), z);
+                cr = mfma(ld8(xr + 32), ld8(kr + 32), cr);
+                const f32x4 rr = *reinterpret_cast<const f32x4 *>(&rs[rRs][16 * I + g4]);
+                r0[I] -= rr * cr;
+            }
+        }
+        s16x4 zb[4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            f32x4 acc = r0[I];
+#pragma unroll
+            for (int J = 0; J < I; ++J) {
+                const int blk = (I * (I - 1)) / 2 + J;
+                acc = mfma16(as_s4(*reinterpret_cast<const uint2 *>(NB[blk] + col * NBP + 4 * kq)), zb[J], acc);
+            }
+            const f32x4 z0 = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 zz = mfma16(as_s4(*reinterpret_cast<const uint2 *>(DB[I] + col * NBP + 4 * kq)),
+                                    as_s4(pk4(acc)), z0);
+            zb[I] = as_s4(pk4(zz));
+        }
+
+        // 5. outputs of the sub-chunk's tokens: tile (rows j' of tile n,
+        //    token slots of tile tt) = 2^{b_t - b_e} K^T qh_t + Z^T P^T (+ 2^{b_t}
+        //    qh_t for the x part), to the record's G or H tiles
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) {
+            const int ts_ = 16 * tt + col;   // this lane's token slot
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (s > 0) {
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                const bf16_t *kr = KT + (16 * n + col) * PK + k8, *qr = QB + ts_ * PK + k8;
+                acc = mfma(ld8(kr), ld8(qr), z);
+                acc = mfma(ld8(kr + 32), ld8(qr + 32), acc);
+                acc *= ts[tQs][ts_];
+            }
+            if (xp) acc += unpk4(*reinterpret_cast<const uint2 *>(QB + ts_ * PK + 16 * n + g4)) * ts[tGd][ts_];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) acc = mfma16(zb[I], tok4(PB, ts_, I), acc);
+            if (ts_ < CT) {
+                const int tr = s * CT + ts_;       // token within the chunk
+                const int m = tr >> 4, cl = tr & 15;
+                if (xp) {
+                    const int xo = ((n >> 1) * 64 + 16 * (2 * (n & 1) + (kq >> 1)) + cl) * 16 + 8 * (kq & 1);
+                    put2(rec + kF1XferGOff + xo + m * 2048, pk4(acc));
+                } else {
+                    put2(rec + f1_xfer_h_off(D) + ((n - 4) * 256 + 16 * kq + cl) * 8 + m * 512, pk4(acc));
+                }
+            }
+        }
+        // K <- 2^{b_e' - b_e} K + X^T diag(2^{b_e' - b_tau}) Z (tiles of
+        // column tile n)
+        {
+            const float gk = ex2(b_e2 - b_e);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                f32x4 acc = K[m] * gk;
+#pragma unroll
+                for (int I = 0; I < 4; ++I) acc = mfma16(tok4(XW, 16 * m + col, I), zb[I], acc);
+                K[m] = acc;
+            }
+        }
+        __syncthreads();   // every read of this sub-chunk's buffers and of K^T is done
+#pragma unroll
+        for (int m = 0; m < 4; ++m) put2(KT + (16 * n + col) * PK + 16 * m + g4, pk4(K[m]));
+    }
+
+    // B (value tiles, as the accumulators hold them) and A (from K^T: row d,
+    // elements d' .. + 7) in the record's operand lane order
+    if (wave >= 4) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) put2(rec + kF1XferBOff + ((wave - 4) * 256 + lane) * 8 + m * 512, pk4(K[m]));
+    }
+    __syncthreads();
+    {
+        const int m = tid >> 7, h = (tid >> 6) & 1;
+        const int d = 16 * m + col, d1 = 32 * h + 8 * kq;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = reinterpret_cast<const uint16_t *>(KT)[(d1 + 2 * e) * PK + d];
+            const uint32_t hi = reinterpret_cast<const uint16_t *>(KT)[(d1 + 2 * e + 1) * PK + d];
+            w[e] = lo | (hi << 16);
+        }
+        *reinterpret_cast<uint4 *>(rec + m * 2048 + h * 1024 + 16 * lane) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+}  // namespace
+
+void launch_chunk_f3_xfer(const ChunkF3Args &a, hipStream_t s, Marks *m) {
+    const int blocks = a.nchunks * a.BH;
+    if (a.window == 2) f3_xfer<2><<<blocks, NTH, 0, s>>>(a);
+    else if (a.window == 4) f3_xfer<4><<<blocks, NTH, 0, s>>>(a);
+    else f3_xfer<8><<<blocks, NTH, 0, s>>>(a);
+    m->mark(s);
+}
+
+}  // namespace falcon

@@ -38,6 +38,13 @@ constexpr size_t chunk_f3_bytes(int dk, int dtype_is_f32) {
     return chunk_f3_scal_off(dk, dtype_is_f32 ? 4 : 2) + 4 * size_t(kChunk) * 4;
 }
 
+// bf16 Falcon-3 at d_k = d_v = 64 with a window of 2, 4 or 8 pairs: per
+// 64-token chunk the Falcon-1 transfer operators (chunk_f3_xfer.hip, W
+// sub-chunks of 64 stacked rows), walked by the Falcon-1 carry.
+constexpr bool chunk_f3_xfer_supported(bool bf16, int dk, int dv, int window) {
+    return bf16 && dk == 64 && dv == 64 && (window == 2 || window == 4 || window == 8);
+}
+
 // Falcon-2 chunk path: one kernel, no workspace.  bf16: d_k in {64, 128};
 // fp32: d_k = 64 (on-chip buffers); any d_v (a multiple of 16).
 constexpr bool chunk_f2_supported(bool bf16, int dk, int dv) {

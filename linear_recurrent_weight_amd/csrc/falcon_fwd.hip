@@ -55,6 +55,8 @@ const char *const kNamesChunkA3Fold[] = {"a3_window", "a1_segment", "a1_output"}
 const char *const kNamesChunkF2[] = {"chunk_f2"};
 const char *const kNamesChunkF2A[] = {"chunk_f2a"};
 const char *const kNamesChunkF3[] = {"feature", "f3_prep", "f3_scan"};
+const char *const kNamesChunkF3X[] = {"feature", "f3_xfer", "f1_carry"};
+const char *const kNamesChunkF3XSeg[] = {"feature", "f3_xfer", "f1_segmap", "f1_segscan", "f1_carry"};
 const char *const kNamesChunkF1Xfer[] = {"f1_xfer", "f1_carry"};
 const char *const kNamesChunkF1XferSeg[] = {"f1_xfer", "f1_segmap", "f1_segscan", "f1_carry"};
 
@@ -315,7 +317,32 @@ int run(const falcon_fwd_args *args, void *stream, Marks *m) {
             ca.S_out = p.S_out;
             ca.ops = p.ws_at<void>(p.off_chunk);
             ca.chunk_bytes = p.chunk_bytes;
-            launch_chunk_f3(ca, io_bf16, s, m);
+            if (p.f3x) {
+                launch_chunk_f3_xfer(ca, s, m);
+                F1XferArgs wa{};   // the walk reads the records only (x_next comes from the feature pass)
+                wa.BH = p.BH;
+                wa.T = p.T;
+                wa.nchunks = p.nchunks;
+                wa.dk = p.dk;
+                wa.dv = p.dv;
+                wa.phi = p.phi;
+                wa.eps_rms = p.eps_rms;
+                wa.k = p.k;
+                wa.S_in = p.S_in;
+                wa.S_out = p.S_out;
+                wa.o = p.o;
+                wa.ops = ca.ops;
+                wa.seg_chunks = p.seg_chunks;
+                wa.nseg = p.nseg;
+                if (p.nseg > 1) {
+                    wa.Mseg = p.ws_at<void>(p.off_seg_m);
+                    wa.Gseg = p.ws_at<float>(p.off_seg_g);
+                    wa.Sseg = p.ws_at<float>(p.off_seg_s);
+                }
+                launch_f1_walk(wa, s, m);
+            } else {
+                launch_chunk_f3(ca, io_bf16, s, m);
+            }
         }
     }
     if (m->failed_at >= 0) {
@@ -360,7 +387,10 @@ extern "C" const char *falcon_kernel_name(const falcon_fwd_args *args, int i) {
             return i < 3 ? kNamesChunkA1[i] : nullptr;
         case Path::kChunkF2: return i < 1 ? kNamesChunkF2[i] : nullptr;
         case Path::kChunkF2A: return i < 1 ? kNamesChunkF2A[i] : nullptr;
-        case Path::kChunkF3: return i < 3 ? kNamesChunkF3[i] : nullptr;
+        case Path::kChunkF3:
+            if (p.f3x && p.nseg > 1) return i < 5 ? kNamesChunkF3XSeg[i] : nullptr;
+            if (p.f3x) return i < 3 ? kNamesChunkF3X[i] : nullptr;
+            return i < 3 ? kNamesChunkF3[i] : nullptr;
         case Path::kChunkF1Xfer:
             if (p.nseg > 1) return i < 4 ? kNamesChunkF1XferSeg[i] : nullptr;
             return i < 2 ? kNamesChunkF1Xfer[i] : nullptr;

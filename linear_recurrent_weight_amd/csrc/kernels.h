@@ -182,6 +182,13 @@ void launch_chunk_f3(const ChunkF3Args &a, bool bf16, hipStream_t s, Marks *m);
 // bf16 Falcon-1, d_k = 64: transfer operators, then the carry over slices of
 // `slice` value columns
 void launch_chunk_f1_xfer(const F1XferArgs &a, int slice, hipStream_t s, Marks *m);
+// the carry over records already in the workspace (segment maps and scan
+// first when a.nseg > 1)
+void launch_f1_walk(const F1XferArgs &a, hipStream_t s, Marks *m);
+// bf16 Falcon-3, d_k = d_v = 64, W in {2, 4, 8}: per 64-token chunk the
+// Falcon-1 transfer operators (a.nchunks counts 64-token chunks, a.ops holds
+// f1_xfer_bytes(64) per chunk); the walk is launch_f1_walk
+void launch_chunk_f3_xfer(const ChunkF3Args &a, hipStream_t s, Marks *m);
 // Falcon-1 backward after the feature pass: states, reverse sweep, reduction
 void launch_bwd(const BwdArgs &a, bool io_bf16, hipStream_t s, Marks *m);
 void launch_bwd_chunk(const BwdArgs &a, bool io_bf16, hipStream_t s, Marks *m);

@@ -164,7 +164,8 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
         if (p->path == Path::kChunkF3) {
             // stacked rows: 64 / W tokens per chunk; the feature buffers get
             // one extra tile so that the last chunk's 64-row reads stay inside
-            p->ct = chunk_f3_tokens(a->window);
+            p->f3x = chunk_f3_xfer_supported(a->dtype == FALCON_BF16, a->dk, a->dv, a->window);
+            p->ct = p->f3x ? kChunk : chunk_f3_tokens(a->window);
             p->nchunks = (T + p->ct - 1) / p->ct;
             p->Tpad = (p->nchunks * p->ct + kChunk - 1) / kChunk * kChunk + kChunk;
         } else {
@@ -182,9 +183,20 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
         if (p->path == Path::kChunkF1 || p->path == Path::kChunkF3) {
             const size_t nch = static_cast<size_t>(bh) * p->nchunks;
             p->chunk_bytes = p->path == Path::kChunkF1 ? chunk_f1_bytes(a->dk, a->dv, a->dtype == FALCON_F32)
+                           : p->f3x                    ? f1_xfer_bytes(a->dv)
                                                        : chunk_f3_bytes(a->dk, a->dtype == FALCON_F32);
             p->off_chunk = off;
             off = align_up(off + nch * p->chunk_bytes);
+        }
+        if (p->f3x) {   // the Falcon-1 walk over the records, split as for Falcon-1
+            p->seg_chunks = f1_xfer_segment_chunks(bh, a->dv, p->nchunks);
+            p->nseg = (p->nchunks + p->seg_chunks - 1) / p->seg_chunks;
+            if (p->nseg > 1) {
+                const size_t ns = static_cast<size_t>(bh) * p->nseg;
+                p->off_seg_m = off; off = align_up(off + ns * f1_segmap_bytes(a->dv));
+                p->off_seg_g = off; off = align_up(off + ns * 4);
+                p->off_seg_s = off; off = align_up(off + ns * a->dk * a->dv * 4);
+            }
         }
     }
     p->ws_bytes = off;

@@ -30,6 +30,7 @@ struct Plan {
     int BH = 0;
     int nchunks = 0;         // ceil(T / chunk) for chunk paths (T / tokens per chunk for F3)
     int ct = 0;              // tokens per chunk (Falcon-3 chunk path)
+    bool f3x = false;        // Falcon-3 through 64-token transfer operators and the Falcon-1 carry
     int Tpad = 0;            // rows of the feature buffers (T, or nchunks * chunk)
     float eps = 0.f, eps_gamma = 0.f, eps_rms = 0.f;
     Path path = Path::kEmpty;

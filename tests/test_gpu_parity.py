@@ -688,6 +688,75 @@ def test_chunk_f3_continuation(window, split):
     assert torch.allclose(st2.tail_x, st_full.tail_x) and torch.allclose(st2.tail_y, st_full.tail_y)
 
 
+# -- Falcon-3 through 64-token transfer operators (bf16, d_k = d_v = 64, W in
+#    {2, 4, 8}): W sub-chunks of 64 stacked rows, then the Falcon-1 carry ----
+
+def _f3x(**kw):
+    base = dict(B=2, H=3, dk=64, dv=64, chunk=64)
+    base.update(kw)
+    return gu.small("F3", "bf16", **base)
+
+
+def test_chunk_f3_xfer_takes_the_transfer_path():
+    import ctypes
+    from linear_recurrent_weight_amd import falcon as fb
+    lib = fb.load_library()
+    a = fb.make_args(variant="F3", dtype="bf16", batch=2, heads=3, seqlen=300, dk=64, dv=64, chunk=64, window=8)
+    names = []
+    while (nm := lib.falcon_kernel_name(ctypes.byref(a), len(names))) is not None:
+        names.append(nm.decode())
+    assert names == ["feature", "f3_xfer", "f1_carry"]
+
+
+@pytest.mark.parametrize("window", [2, 4, 8])
+@pytest.mark.parametrize("T", [7, 8, 9, 64, 65, 130, 300])
+def test_chunk_f3_xfer_lengths(window, T):
+    """Chunks of 64 tokens in W sub-chunks, ragged last chunk, sub-chunks
+    past the end of the sequence.  (Below 7 tokens a head's whole output is
+    one or two rows whose size can rest on a single dot product: the
+    per-head relative error then measures that dot product's bf16 rounding,
+    about 1e-3 absolute as everywhere else, against a reference of a few
+    1e-3; the shortest lengths are the same as the other Falcon-3 tests'.)"""
+    check(_f3x(T=T, window=window, seed=T + 7 * window), heads=np.arange(6))
+
+
+@pytest.mark.parametrize("window", [4, 8])
+@pytest.mark.parametrize("split", [1, 5, 64, 100])
+def test_chunk_f3_xfer_continuation(window, split):
+    """The second call's first sub-chunk stacks the incoming tail pairs
+    (fp32, rounded to bf16 as staged) with its own rows; the carried state
+    enters through the Falcon-1 walk."""
+    import torch
+    w = _f3x(B=1, H=2, T=200, window=window, seed=23)
+    inp = gu.make(w)
+    dev = gu.to_device(inp, w)
+    a = {k: v[:, :, :split].contiguous() for k, v in dev.items()}
+    b = {k: v[:, :, split:].contiguous() for k, v in dev.items()}
+    o1, st1 = gu.run_gpu(w.with_(seqlen=split), a)
+    o2, st2 = gu.run_gpu(w.with_(seqlen=200 - split), b, state=st1)
+    heads = np.arange(2)
+    o_ref, st_ref = gu.oracle_heads(w, inp, heads)
+    eo, es = gu.compare(w, heads, torch.cat([o1, o2], 2), st2, o_ref, st_ref)
+    print(f"    split={split} W={window} err_o={eo:.3e} err_S={es:.3e}", flush=True)
+    assert eo <= gu.tol_for(w) and es <= gu.tol_for(w), (eo, es)
+
+
+@pytest.mark.parametrize("window", [4, 8])
+def test_chunk_f3_xfer_strong_decay(window):
+    """Steps near the clamp with a tiny eps_gamma: sub-chunks decay below
+    2^-100, which takes the pairwise (non-separable) decay form."""
+    w = _f3x(B=1, H=2, T=300, window=window, seed=29, lam_lo=5e3, lam_hi=1e4, eps_gamma=1e-6)
+    inp = gu.make(w)
+    inp["beta"] = (1.0 + inp["beta"]).astype(np.float32)
+    dev = gu.to_device(inp, w)
+    o, st = gu.run_gpu(w, dev)
+    o_ref, st_ref, tr = gu.oracle_heads(w, inp, np.arange(2), trace=True)
+    lg = np.log2(1.0 - tr.alpha)
+    assert (lg < -12.5).mean() > 0.5   # sub-chunks of 8 or 16 such tokens span more than 2^-100
+    eo, es = gu.compare(w, np.arange(2), o, st, o_ref, st_ref)
+    assert eo <= gu.tol_for(w) and es <= gu.tol_for(w), (eo, es)
+
+
 def test_chunk_f3_strong_ridge_clamp():
     w = gu.small("F3", "f32", B=1, H=2, T=300, chunk=64, window=4, lam_lo=200.0, lam_hi=400.0,
                  eps_gamma=0.05)
