@@ -808,10 +808,14 @@ void launch_walks(const ChunkAArgs &a, hipStream_t s, Marks *m) {
 
 }  // namespace
 
+void launch_a3_window(const ChunkAArgs &a, hipStream_t s, Marks *m) {
+    a3_window<<<dim3(a.nchunks, a.BH), 64, 0, s>>>(a);
+    m->mark(s);
+}
+
 void launch_chunk_a1(const ChunkAArgs &a, hipStream_t s, Marks *m) {
     if (a.window > 1) {
-        a3_window<<<dim3(a.nchunks, a.BH), 64, 0, s>>>(a);
-        m->mark(s);
+        launch_a3_window(a, s, m);
         launch_walks<true>(a, s, m);
     } else {
         launch_walks<false>(a, s, m);

@@ -29,8 +29,13 @@
 // MFMA, one column tile of Z per wave, in registers; K stays in the waves'
 // accumulators (fp32) with a bf16 copy in LDS for the products that read it.
 //
+// The rows are the raw q, k_{p-1} and v of the sequence: the RMS scales of
+// phi (s_x of a pair, s_q of a query) are formed as the rows are staged and
+// folded into the per-row and per-token factors that every product applies
+// anyway.  w_t = eta_t / B_t and log2 gamma_t come from the window pass.
 // One workgroup per (chunk, head), chunk-major; the records go to the
-// workspace in the Falcon-1 layout, and f1_carry walks them.
+// workspace in the Falcon-1 layout, and f1_carry walks them.  The workgroup
+// holding the last token writes the boundary state's x_next and window pairs.
 #include "chunk_layout.h"
 #include "kernels.h"
 #include "mma.h"
@@ -76,38 +81,60 @@ __device__ __forceinline__ uint4 pk8(const float *f) {
     return make_uint4(pk2(f[0], f[1]), pk2(f[2], f[3]), pk2(f[4], f[5]), pk2(f[6], f[7]));
 }
 
-// per stacked row of a sub-chunk: w_r, w_r 2^{b_{tau-1}}, w_r 2^{b_{tau-1} - b_e}
-// (residual cross term and Gram row factor), 2^{b_e - b_tau} (separable
-// column factor), 2^{b_e' - b_tau} (weight of the row in K), and b_{tau-1} -
-// b_e, b_tau - b_e for the pairwise form
-enum { rW = 0, rXf, rRs, rCs, rEw, rBp, rBt, kNr };
-// per token slot of a sub-chunk: 2^{b_t - b_e}, 2^{b_t}, b_t - b_e
-enum { tQs = 0, tGd, tB, kNt };
+// per stacked row of a sub-chunk: w_r (the values' factor); with the row's
+// RMS scale s_x folded in, w_r 2^{b_{tau-1}} s_x, w_r 2^{b_{tau-1} - b_e} s_x
+// (residual cross term and Gram row factor), 2^{b_e - b_tau} s_x (separable
+// column factor), 2^{b_e' - b_tau} s_x (weight of the row in K); then
+// b_{tau-1} - b_e, b_tau - b_e for the pairwise form, and s_x itself
+enum { rW = 0, rXf, rRs, rCs, rEw, rBp, rBt, rSx, kNr };
+// per token slot of a sub-chunk: 2^{b_t - b_e} s_q, 2^{b_t} s_q, b_t - b_e, s_q
+enum { tQs = 0, tGd, tB, tSq, kNt };
 
-// The raw data of one sub-chunk: for stacked row tid / 8 its pair's 8
-// features (part tid % 8) and 8 values; for token slot tid / 8 its query
-// piece.  Loaded unconditionally from clamped rows; pairs before position 0
-// come from the incoming tail when the rows are stored.
+// phi's RMS scale 1 / sqrt(mean(z^2) + eps_rms) (0 when that is 0) from the
+// sum of squares over 64 elements
+__device__ __forceinline__ float rms_scale(float ss, float eps_rms, int phi_kind) {
+    if (phi_kind == FALCON_PHI_IDENTITY) return 1.f;
+    const float ms = ss * (1.f / D) + eps_rms;
+    return ms > 0.f ? __builtin_amdgcn_rsqf(ms) : 0.f;
+}
+// sum of squares of 8 bf16 values
+__device__ __forceinline__ float sumsq8(const uint4 &u) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const bf16x2_t h = __builtin_bit_cast(bf16x2_t, w[e]);
+        s = __builtin_amdgcn_fdot2_f32_bf16(h, h, s, false);
+    }
+    return s;
+}
+
+// The raw data of one sub-chunk: for stacked row tid / 8 (pair p) 8
+// elements (part tid % 8) of k_{p-1} and of v_p; for token slot tid / 8 its
+// query piece.  Loaded unconditionally from rows clamped into [0, T); pairs
+// at or before position 0 (the incoming x_0 and tail) are replaced when the
+// rows are stored.
 struct F3Rows {
     uint4 x, y, q;
-    __device__ __forceinline__ void load(const ChunkF3Args &a, int bh, int c, int s, int W, int CT, int TR,
+    __device__ __forceinline__ void load(const F3XferArgs &a, int bh, int c, int s, int W, int CT, int TR,
                                          int row, int part) {
+        const int T = a.T;
         const int tau = row / W, k = row % W;
         const int t = c * C + s * CT + tau, p = t - (W - 1) + k;
-        const bf16_t *xn = static_cast<const bf16_t *>(a.xn) + size_t(bh) * a.Tpad * D;
-        const bf16_t *qn = static_cast<const bf16_t *>(a.qn) + size_t(bh) * a.Tpad * D;
-        const bf16_t *v = static_cast<const bf16_t *>(a.v) + size_t(bh) * a.T * D;
-        const int pc = p < 0 ? 0 : p;                      // p <= t < Tpad
-        const int py = p < 0 ? 0 : (p < a.T ? p : a.T - 1);
-        x = *reinterpret_cast<const uint4 *>(xn + size_t(pc) * D + 8 * part);
-        y = *reinterpret_cast<const uint4 *>(v + size_t(py) * D + 8 * part);
+        const bf16_t *kg = static_cast<const bf16_t *>(a.k) + size_t(bh) * T * D;
+        const bf16_t *qg = static_cast<const bf16_t *>(a.q) + size_t(bh) * T * D;
+        const bf16_t *vg = static_cast<const bf16_t *>(a.v) + size_t(bh) * T * D;
+        const int pk = p < 1 ? 0 : (p - 1 < T ? p - 1 : T - 1);
+        const int py = p < 0 ? 0 : (p < T ? p : T - 1);
+        x = *reinterpret_cast<const uint4 *>(kg + size_t(pk) * D + 8 * part);
+        y = *reinterpret_cast<const uint4 *>(vg + size_t(py) * D + 8 * part);
         const int tq = c * C + s * CT + (row < TR ? row : 0);
-        q = *reinterpret_cast<const uint4 *>(qn + size_t(tq) * D + 8 * part);
+        q = *reinterpret_cast<const uint4 *>(qg + size_t(tq < T ? tq : T - 1) * D + 8 * part);
     }
 };
 
 template <int W>
-__global__ __launch_bounds__(NTH, 4) void f3_xfer(ChunkF3Args a) {
+__global__ __launch_bounds__(NTH, 4) void f3_xfer(F3XferArgs a) {
     static_assert(W == 2 || W == 4 || W == 8, "windows whose token blocks tile 16 rows");
     constexpr int CT = C / W;                      // tokens of a sub-chunk
     constexpr int NTT = CT >= 16 ? CT / 16 : 1;    // token tiles of a sub-chunk
@@ -124,6 +151,7 @@ __global__ __launch_bounds__(NTH, 4) void f3_xfer(ChunkF3Args a) {
     __shared__ __align__(16) float LF[4 * LFB];         // the diagonal blocks L_J, fp32 row-major
     __shared__ __align__(16) float rs[kNr][C];
     __shared__ __align__(16) float ts[kNt][TR];
+    __shared__ float rsx[C], tsq[TR];                   // RMS scales of the staged rows
     __shared__ float cb[C], cw[C];                      // chunk tokens: b_t, w_t
     __shared__ __align__(16) bf16x8 IDT[2][64];         // column pickers
 
@@ -144,15 +172,12 @@ __global__ __launch_bounds__(NTH, 4) void f3_xfer(ChunkF3Args a) {
         IDT[h][lane] = __builtin_bit_cast(bf16x8, u);
     }
     // the chunk's step scalars (wave 0, lane = token): b_t (base 2, restarted
-    // at 0) and w_t = eta_t / B_t, B_t the pairs in the window of t
+    // at 0) and w_t (padding tokens have w = 0 and log2 gamma = 0)
     if (wave == 0) {
-        const int t = c * C + lane;   // < Tpad (padding tokens have eta = alpha = 0)
-        const size_t ft = size_t(bh) * a.Tpad + t;
-        const float b = wave_inclusive_scan(log2_1m(a.alpha[ft]));
-        const long long pairs = (long long)a.n_tail_in + t + 1;
-        const int nb = pairs < W ? int(pairs) : W;
+        const size_t ft = size_t(bh) * a.Tpad + c * C + lane;
+        const float b = wave_inclusive_scan(a.lg[ft]);
         cb[lane] = b;
-        cw[lane] = t < T ? a.eta[ft] / float(nb) : 0.f;
+        cw[lane] = a.w[ft];
         if (lane == 63) *reinterpret_cast<float *>(rec + f1_xfer_scal_off(D)) = ex2(b);
     }
 
@@ -180,22 +205,36 @@ __global__ __launch_bounds__(NTH, 4) void f3_xfer(ChunkF3Args a) {
             const int tau = row / W, k = row % W;
             const int t = c * C + s * CT + tau, p = t - H + k;
             uint4 xr = rows.x, yr = rows.y;
-            if (p < 0) {
+            float ss = sumsq8(xr);
+            bool feat = false;   // a boundary pair: features already (scale 1)
+            if (p <= 0) {
                 xr = make_uint4(0, 0, 0, 0);
-                yr = xr;
-                if (p >= -a.n_tail_in) {
-                    const float *tx = a.tailx_in + (size_t(bh) * H + H + p) * D + 8 * part;
-                    const float *ty = a.taily_in + (size_t(bh) * H + H + p) * D + 8 * part;
-                    xr = pk8(tx);
-                    yr = pk8(ty);
+                if (p < 0) yr = xr;
+                ss = 0.f;
+                const float *src = nullptr;
+                if (p == 0 && a.xnext_in) src = a.xnext_in + size_t(bh) * D + 8 * part;
+                if (p < 0 && p >= -a.n_tail_in) {
+                    src = a.tailx_in + (size_t(bh) * H + H + p) * D + 8 * part;
+                    yr = pk8(a.taily_in + (size_t(bh) * H + H + p) * D + 8 * part);
+                }
+                if (src) {
+                    xr = pk8(src);
+                    feat = true;
                 }
             } else if (p >= T) {
                 yr = make_uint4(0, 0, 0, 0);
             }
+            ss = group_sum<8>(ss);
+            const float sx = feat ? 1.f : (p >= 1 && p <= T ? rms_scale(ss, a.eps_rms, a.phi) : 0.f);
             *reinterpret_cast<uint4 *>(XB + row * PK + 8 * part) = xr;
             *reinterpret_cast<uint4 *>(YB + row * PK + 8 * part) = yr;
-            if (row < TR)
-                *reinterpret_cast<uint4 *>(QB + row * PK + 8 * part) = row < CT ? rows.q : make_uint4(0, 0, 0, 0);
+            if (part == 0) rsx[row] = sx;
+            if (row < TR) {
+                const bool live = row < CT && c * C + s * CT + row < T;
+                float sq = group_sum<8>(sumsq8(rows.q));
+                *reinterpret_cast<uint4 *>(QB + row * PK + 8 * part) = live ? rows.q : make_uint4(0, 0, 0, 0);
+                if (part == 0) tsq[row] = live ? rms_scale(sq, a.eps_rms, a.phi) : 0.f;
+            }
             if (s + 1 < W) rows.load(a, bh, c, s + 1, W, CT, TR, row, part);
         }
         __syncthreads();
@@ -206,20 +245,22 @@ __global__ __launch_bounds__(NTH, 4) void f3_xfer(ChunkF3Args a) {
         const bool sep = b_e2 >= b_e - 100.f;
         {
             const int tc = s * CT + lane / W;
-            const float w = cw[tc], bt = cb[tc], bp = tc > 0 ? cb[tc - 1] : 0.f;
+            const float w = cw[tc], bt = cb[tc], bp = tc > 0 ? cb[tc - 1] : 0.f, sx = rsx[lane];
             rs[rW][lane] = w;
-            rs[rXf][lane] = w * ex2(bp);
-            rs[rRs][lane] = w * ex2(bp - b_e);
-            rs[rCs][lane] = sep ? ex2(b_e - bt) : 0.f;
-            rs[rEw][lane] = ex2(b_e2 - bt);
+            rs[rXf][lane] = w * ex2(bp) * sx;
+            rs[rRs][lane] = w * ex2(bp - b_e) * sx;
+            rs[rCs][lane] = sep ? ex2(b_e - bt) * sx : 0.f;
+            rs[rEw][lane] = ex2(b_e2 - bt) * sx;
             rs[rBp][lane] = bp - b_e;
             rs[rBt][lane] = bt - b_e;
+            rs[rSx][lane] = sx;
             if (lane < TR) {
                 const bool live = lane < CT;
-                const float btk = live ? cb[s * CT + lane] : b_e2;
-                ts[tQs][lane] = live ? ex2(btk - b_e) : 0.f;
-                ts[tGd][lane] = live ? ex2(btk) : 0.f;
+                const float btk = live ? cb[s * CT + lane] : b_e2, sq = tsq[lane];
+                ts[tQs][lane] = live ? ex2(btk - b_e) * sq : 0.f;
+                ts[tGd][lane] = live ? ex2(btk) * sq : 0.f;
                 ts[tB][lane] = btk - b_e;
+                ts[tSq][lane] = sq;
             }
         }
         wave_lds_sync();
@@ -228,11 +269,12 @@ __global__ __launch_bounds__(NTH, 4) void f3_xfer(ChunkF3Args a) {
         //    Gram N_ij = w_i 2^{b_{tau_i - 1} - b_tau_j} x_i . x_j for tau_j < tau_i
         //    (rows of different 16-row blocks always belong to different
         //    tokens); scores P_tj = 2^{b_t - b_tau_j} qh_t . x_j for tau_j <= t
-        auto gram_scale = [&](int i, int j) {   // factor of entry (i, j)
-            return sep ? rs[rRs][i] * rs[rCs][j] : rs[rW][i] * ex2(rs[rBp][i] - rs[rBt][j]);
+        auto gram_scale = [&](int i, int j) {   // factor of entry (i, j), the RMS scales included
+            return sep ? rs[rRs][i] * rs[rCs][j]
+                       : rs[rW][i] * rs[rSx][i] * ex2(rs[rBp][i] - rs[rBt][j]) * rs[rSx][j];
         };
         auto score_scale = [&](int t, int j) {
-            return sep ? ts[tQs][t] * rs[rCs][j] : ex2(ts[tB][t] - rs[rBt][j]);
+            return sep ? ts[tQs][t] * rs[rCs][j] : ex2(ts[tB][t] - rs[rBt][j]) * ts[tSq][t] * rs[rSx][j];
         };
         // job 0-5: Gram block (1,0) (2,0) (2,1) (3,0) (3,1) (3,2); job 6 ..:
         // score tile (token tile, row block J); the tile is formed
@@ -413,11 +455,43 @@ __global__ __launch_bounds__(NTH, 4) void f3_xfer(ChunkF3Args a) {
         }
         *reinterpret_cast<uint4 *>(rec + m * 2048 + h * 1024 + 16 * lane) = make_uint4(w[0], w[1], w[2], w[3]);
     }
+
+    // the boundary state's x_next = phi(k_{T-1}) and last W - 1 pairs
+    // (features, values; right-aligned, the valid ones last), from the
+    // workgroup holding the last token
+    if (c == (T - 1) / C && wave == 0) {
+        const bf16_t *kg = static_cast<const bf16_t *>(a.k) + size_t(bh) * T * D;
+        const bf16_t *vg = static_cast<const bf16_t *>(a.v) + size_t(bh) * T * D;
+        if (a.xnext_out) {
+            const float xv = bf16_to_f32(kg[size_t(T - 1) * D + lane].bits);
+            const float sc = phi_scale(wave_sum(xv * xv), D, a.eps_rms, a.phi);
+            a.xnext_out[size_t(bh) * D + lane] = xv * sc;
+        }
+        if (a.tailx_out) {
+            for (int sl = 0; sl < H; ++sl) {
+                const int tau = T - H + sl;
+                const bool valid = sl >= H - a.n_tail_out;
+                float x = 0.f, y = 0.f;
+                if (tau >= 1) {
+                    const float kv = bf16_to_f32(kg[size_t(tau - 1) * D + lane].bits);
+                    x = kv * phi_scale(wave_sum(kv * kv), D, a.eps_rms, a.phi);
+                } else if (tau == 0) {
+                    x = a.xnext_in ? a.xnext_in[size_t(bh) * D + lane] : 0.f;
+                } else if (valid) {
+                    x = a.tailx_in[(size_t(bh) * H + H + tau) * D + lane];
+                }
+                if (tau >= 0) y = bf16_to_f32(vg[size_t(tau) * D + lane].bits);
+                else if (valid) y = a.taily_in[(size_t(bh) * H + H + tau) * D + lane];
+                a.tailx_out[(size_t(bh) * H + sl) * D + lane] = valid ? x : 0.f;
+                a.taily_out[(size_t(bh) * H + sl) * D + lane] = valid ? y : 0.f;
+            }
+        }
+    }
 }
 
 }  // namespace
 
-void launch_chunk_f3_xfer(const ChunkF3Args &a, hipStream_t s, Marks *m) {
+void launch_chunk_f3_xfer(const F3XferArgs &a, hipStream_t s, Marks *m) {
     const int blocks = a.nchunks * a.BH;
     if (a.window == 2) f3_xfer<2><<<blocks, NTH, 0, s>>>(a);
     else if (a.window == 4) f3_xfer<4><<<blocks, NTH, 0, s>>>(a);

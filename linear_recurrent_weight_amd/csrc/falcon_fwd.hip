@@ -55,8 +55,8 @@ const char *const kNamesChunkA3Fold[] = {"a3_window", "a1_segment", "a1_output"}
 const char *const kNamesChunkF2[] = {"chunk_f2"};
 const char *const kNamesChunkF2A[] = {"chunk_f2a"};
 const char *const kNamesChunkF3[] = {"feature", "f3_prep", "f3_scan"};
-const char *const kNamesChunkF3X[] = {"feature", "f3_xfer", "f1_carry"};
-const char *const kNamesChunkF3XSeg[] = {"feature", "f3_xfer", "f1_segmap", "f1_segscan", "f1_carry"};
+const char *const kNamesChunkF3X[] = {"a3_window", "f3_xfer", "f1_carry"};
+const char *const kNamesChunkF3XSeg[] = {"a3_window", "f3_xfer", "f1_segmap", "f1_segscan", "f1_carry"};
 const char *const kNamesChunkF1Xfer[] = {"f1_xfer", "f1_carry"};
 const char *const kNamesChunkF1XferSeg[] = {"f1_xfer", "f1_segmap", "f1_segscan", "f1_carry"};
 
@@ -190,6 +190,77 @@ int run(const falcon_fwd_args *args, void *stream, Marks *m) {
         fa.o = p.o;
         if (p.path == Path::kChunkF2A) launch_chunk_f2a(fa, p.dtype == FALCON_BF16, s, m);
         else launch_chunk_f2(fa, p.dtype == FALCON_BF16, s, m);
+    } else if (p.path == Path::kChunkF3X) {
+        // the window pass (w_t, log2 gamma_t), the 64-token operators, the walk
+        ChunkAArgs wa{};
+        wa.variant = p.variant;
+        wa.phi = p.phi;
+        wa.BH = p.BH;
+        wa.T = p.T;
+        wa.Tpad = p.Tpad;
+        wa.nchunks = p.nchunks;
+        wa.dk = p.dk;
+        wa.dv = p.dv;
+        wa.window = p.window;
+        wa.fresh = p.fresh ? 1 : 0;
+        wa.n_tail_in = p.n_tail_in;
+        wa.n_tail_out = p.n_tail_out;
+        wa.eps = p.eps;
+        wa.eps_gamma = p.eps_gamma;
+        wa.eps_rms = p.eps_rms;
+        wa.k = p.k;
+        wa.beta = p.beta;
+        wa.lambda = p.lambda;
+        wa.xnext_in = p.xnext_in;
+        wa.tailx_in = p.tailx_in;
+        wa.taily_in = p.taily_in;
+        wa.etaw = p.ws_at<float>(p.off_eta);
+        wa.lg = p.ws_at<float>(p.off_alpha);
+        launch_a3_window(wa, s, m);
+        F3XferArgs xa{};
+        xa.BH = p.BH;
+        xa.T = p.T;
+        xa.Tpad = p.Tpad;
+        xa.nchunks = p.nchunks;
+        xa.window = p.window;
+        xa.phi = p.phi;
+        xa.n_tail_in = p.n_tail_in;
+        xa.n_tail_out = p.n_tail_out;
+        xa.eps_rms = p.eps_rms;
+        xa.q = p.q;
+        xa.k = p.k;
+        xa.v = p.v;
+        xa.w = wa.etaw;
+        xa.lg = wa.lg;
+        xa.xnext_in = p.xnext_in;
+        xa.tailx_in = p.tailx_in;
+        xa.taily_in = p.taily_in;
+        xa.xnext_out = p.xnext_out;
+        xa.tailx_out = p.tailx_out;
+        xa.taily_out = p.taily_out;
+        xa.ops = p.ws_at<void>(p.off_chunk);
+        launch_chunk_f3_xfer(xa, s, m);
+        F1XferArgs fa{};   // the walk reads the records (x_next is written above)
+        fa.BH = p.BH;
+        fa.T = p.T;
+        fa.nchunks = p.nchunks;
+        fa.dk = p.dk;
+        fa.dv = p.dv;
+        fa.phi = p.phi;
+        fa.eps_rms = p.eps_rms;
+        fa.k = p.k;
+        fa.S_in = p.S_in;
+        fa.S_out = p.S_out;
+        fa.o = p.o;
+        fa.ops = xa.ops;
+        fa.seg_chunks = p.seg_chunks;
+        fa.nseg = p.nseg;
+        if (p.nseg > 1) {
+            fa.Mseg = p.ws_at<void>(p.off_seg_m);
+            fa.Gseg = p.ws_at<float>(p.off_seg_g);
+            fa.Sseg = p.ws_at<float>(p.off_seg_s);
+        }
+        launch_f1_walk(fa, s, m);
     } else if (p.path == Path::kChunkF1Xfer) {
         F1XferArgs fa{};
         fa.BH = p.BH;
@@ -317,32 +388,7 @@ int run(const falcon_fwd_args *args, void *stream, Marks *m) {
             ca.S_out = p.S_out;
             ca.ops = p.ws_at<void>(p.off_chunk);
             ca.chunk_bytes = p.chunk_bytes;
-            if (p.f3x) {
-                launch_chunk_f3_xfer(ca, s, m);
-                F1XferArgs wa{};   // the walk reads the records only (x_next comes from the feature pass)
-                wa.BH = p.BH;
-                wa.T = p.T;
-                wa.nchunks = p.nchunks;
-                wa.dk = p.dk;
-                wa.dv = p.dv;
-                wa.phi = p.phi;
-                wa.eps_rms = p.eps_rms;
-                wa.k = p.k;
-                wa.S_in = p.S_in;
-                wa.S_out = p.S_out;
-                wa.o = p.o;
-                wa.ops = ca.ops;
-                wa.seg_chunks = p.seg_chunks;
-                wa.nseg = p.nseg;
-                if (p.nseg > 1) {
-                    wa.Mseg = p.ws_at<void>(p.off_seg_m);
-                    wa.Gseg = p.ws_at<float>(p.off_seg_g);
-                    wa.Sseg = p.ws_at<float>(p.off_seg_s);
-                }
-                launch_f1_walk(wa, s, m);
-            } else {
-                launch_chunk_f3(ca, io_bf16, s, m);
-            }
+            launch_chunk_f3(ca, io_bf16, s, m);
         }
     }
     if (m->failed_at >= 0) {
@@ -387,10 +433,10 @@ extern "C" const char *falcon_kernel_name(const falcon_fwd_args *args, int i) {
             return i < 3 ? kNamesChunkA1[i] : nullptr;
         case Path::kChunkF2: return i < 1 ? kNamesChunkF2[i] : nullptr;
         case Path::kChunkF2A: return i < 1 ? kNamesChunkF2A[i] : nullptr;
-        case Path::kChunkF3:
-            if (p.f3x && p.nseg > 1) return i < 5 ? kNamesChunkF3XSeg[i] : nullptr;
-            if (p.f3x) return i < 3 ? kNamesChunkF3X[i] : nullptr;
-            return i < 3 ? kNamesChunkF3[i] : nullptr;
+        case Path::kChunkF3: return i < 3 ? kNamesChunkF3[i] : nullptr;
+        case Path::kChunkF3X:
+            if (p.nseg > 1) return i < 5 ? kNamesChunkF3XSeg[i] : nullptr;
+            return i < 3 ? kNamesChunkF3X[i] : nullptr;
         case Path::kChunkF1Xfer:
             if (p.nseg > 1) return i < 4 ? kNamesChunkF1XferSeg[i] : nullptr;
             return i < 2 ? kNamesChunkF1Xfer[i] : nullptr;

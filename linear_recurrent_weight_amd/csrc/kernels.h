@@ -186,9 +186,21 @@ void launch_chunk_f1_xfer(const F1XferArgs &a, int slice, hipStream_t s, Marks *
 // first when a.nseg > 1)
 void launch_f1_walk(const F1XferArgs &a, hipStream_t s, Marks *m);
 // bf16 Falcon-3, d_k = d_v = 64, W in {2, 4, 8}: per 64-token chunk the
-// Falcon-1 transfer operators (a.nchunks counts 64-token chunks, a.ops holds
-// f1_xfer_bytes(64) per chunk); the walk is launch_f1_walk
-void launch_chunk_f3_xfer(const ChunkF3Args &a, hipStream_t s, Marks *m);
+// Falcon-1 transfer operators (f1_xfer_bytes(64) each), from the raw rows
+// and the window pass's step scalars; the walk is launch_f1_walk
+struct F3XferArgs {
+    int BH, T, Tpad, nchunks, window, phi, n_tail_in, n_tail_out;
+    float eps_rms;
+    const void *q, *k, *v;          // bf16 [BH, T, 64]
+    const float *w, *lg;            // [BH, Tpad] eta_t / B_t and log2 gamma_t
+    const float *xnext_in, *tailx_in, *taily_in;
+    float *xnext_out, *tailx_out, *taily_out;
+    void *ops;                      // [BH][nchunks] Falcon-1 records
+};
+void launch_chunk_f3_xfer(const F3XferArgs &a, hipStream_t s, Marks *m);
+// the window pass of the bf16 d = 64 inner-product path: per token w_t =
+// eta_t / B_t and log2 gamma_t into a.etaw and a.lg
+void launch_a3_window(const ChunkAArgs &a, hipStream_t s, Marks *m);
 // Falcon-1 backward after the feature pass: states, reverse sweep, reduction
 void launch_bwd(const BwdArgs &a, bool io_bf16, hipStream_t s, Marks *m);
 void launch_bwd_chunk(const BwdArgs &a, bool io_bf16, hipStream_t s, Marks *m);

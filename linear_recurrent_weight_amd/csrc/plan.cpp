@@ -82,6 +82,8 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
             p->path = Path::kChunkF2;
         } else if (var == FALCON_V2A && chunk_f2a_supported(a->dk, a->dv)) {
             p->path = Path::kChunkF2A;
+        } else if (var == FALCON_V3 && chunk_f3_xfer_supported(a->dtype == FALCON_BF16, a->dk, a->dv, a->window)) {
+            p->path = Path::kChunkF3X;
         } else if (var == FALCON_V3 && chunk_f3_supported(a->dk, a->dv)) {
             p->path = Path::kChunkF3;
         } else if (chunk_a1_supported(a->dtype == FALCON_BF16, var, a->window, a->dk, a->dv)) {
@@ -147,6 +149,25 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
         p->off_chunk = off; off = align_up(off + st);           // segment writes [d][j]
         p->off_seg_g = off; off = align_up(off + static_cast<size_t>(bh) * p->nseg * 4);
         p->off_seg_s = off; off = align_up(off + st);           // segment entry states [d][j]
+    } else if (p->path == Path::kChunkF3X) {
+        // per-token w_t and log2 gamma_t from the window pass, then the
+        // Falcon-1 records of every 64-token chunk and the Falcon-1 walk
+        // (split into segments as for Falcon-1)
+        p->nchunks = (T + kChunk - 1) / kChunk;
+        p->Tpad = p->nchunks * kChunk;
+        const size_t rows = static_cast<size_t>(bh) * p->Tpad;
+        p->off_eta = off; off = align_up(off + rows * 4);
+        p->off_alpha = off; off = align_up(off + rows * 4);
+        p->chunk_bytes = f1_xfer_bytes(a->dv);
+        p->off_chunk = off; off = align_up(off + static_cast<size_t>(bh) * p->nchunks * p->chunk_bytes);
+        p->seg_chunks = f1_xfer_segment_chunks(bh, a->dv, p->nchunks);
+        p->nseg = (p->nchunks + p->seg_chunks - 1) / p->seg_chunks;
+        if (p->nseg > 1) {
+            const size_t ns = static_cast<size_t>(bh) * p->nseg;
+            p->off_seg_m = off; off = align_up(off + ns * f1_segmap_bytes(a->dv));
+            p->off_seg_g = off; off = align_up(off + ns * 4);
+            p->off_seg_s = off; off = align_up(off + ns * a->dk * a->dv * 4);
+        }
     } else if (p->path == Path::kChunkA) {
         p->nchunks = (T + kChunk - 1) / kChunk;
         p->Tpad = p->nchunks * kChunk;
@@ -164,8 +185,7 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
         if (p->path == Path::kChunkF3) {
             // stacked rows: 64 / W tokens per chunk; the feature buffers get
             // one extra tile so that the last chunk's 64-row reads stay inside
-            p->f3x = chunk_f3_xfer_supported(a->dtype == FALCON_BF16, a->dk, a->dv, a->window);
-            p->ct = p->f3x ? kChunk : chunk_f3_tokens(a->window);
+            p->ct = chunk_f3_tokens(a->window);
             p->nchunks = (T + p->ct - 1) / p->ct;
             p->Tpad = (p->nchunks * p->ct + kChunk - 1) / kChunk * kChunk + kChunk;
         } else {
@@ -183,20 +203,9 @@ int build_plan(const falcon_fwd_args *a, Plan *p, bool check_pointers) {
         if (p->path == Path::kChunkF1 || p->path == Path::kChunkF3) {
             const size_t nch = static_cast<size_t>(bh) * p->nchunks;
             p->chunk_bytes = p->path == Path::kChunkF1 ? chunk_f1_bytes(a->dk, a->dv, a->dtype == FALCON_F32)
-                           : p->f3x                    ? f1_xfer_bytes(a->dv)
                                                        : chunk_f3_bytes(a->dk, a->dtype == FALCON_F32);
             p->off_chunk = off;
             off = align_up(off + nch * p->chunk_bytes);
-        }
-        if (p->f3x) {   // the Falcon-1 walk over the records, split as for Falcon-1
-            p->seg_chunks = f1_xfer_segment_chunks(bh, a->dv, p->nchunks);
-            p->nseg = (p->nchunks + p->seg_chunks - 1) / p->seg_chunks;
-            if (p->nseg > 1) {
-                const size_t ns = static_cast<size_t>(bh) * p->nseg;
-                p->off_seg_m = off; off = align_up(off + ns * f1_segmap_bytes(a->dv));
-                p->off_seg_g = off; off = align_up(off + ns * 4);
-                p->off_seg_s = off; off = align_up(off + ns * a->dk * a->dv * 4);
-            }
         }
     }
     p->ws_bytes = off;

@@ -21,6 +21,7 @@ enum class Path : int {
     kChunkA1 = 9,    // chunk-parallel Falcon-1A, bf16, d_k = d_v = 64: register-operand segment kernels
     kDecode = 11,    // seqlen == 1: the single-token step of any variant, one kernel
     kChunkF2A = 12,  // chunk-parallel Falcon-2A (per-column inner-product write)
+    kChunkF3X = 13,  // Falcon-3, bf16, d = 64, W in {2, 4, 8}: window pass, 64-token transfer operators, Falcon-1 walk
 };
 
 struct Plan {
@@ -30,7 +31,6 @@ struct Plan {
     int BH = 0;
     int nchunks = 0;         // ceil(T / chunk) for chunk paths (T / tokens per chunk for F3)
     int ct = 0;              // tokens per chunk (Falcon-3 chunk path)
-    bool f3x = false;        // Falcon-3 through 64-token transfer operators and the Falcon-1 carry
     int Tpad = 0;            // rows of the feature buffers (T, or nchunks * chunk)
     float eps = 0.f, eps_gamma = 0.f, eps_rms = 0.f;
     Path path = Path::kEmpty;

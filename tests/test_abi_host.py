@@ -61,6 +61,10 @@ def wsize(lib, a):
     return lib.falcon_fwd_workspace_size(ctypes.byref(a))
 
 
+def _align(n):
+    return -(-n // 256) * 256
+
+
 def with_ws(lib, a):
     n = wsize(lib, a)
     a.workspace = 1 << 30
@@ -254,6 +258,29 @@ def test_f1_bf16_long_walks_split_into_segments(lib, B, H, T, dv):
     # the long-sequence workload with few heads is split
     if (B, H, T) == (2, 12, 16384):
         assert nseg == 10 and g == 26
+
+
+@pytest.mark.parametrize("window", [2, 4, 8])
+@pytest.mark.parametrize("B,H,T", [(8, 12, 512), (2, 3, 300), (1, 2, 16384)])
+def test_f3_bf16_d64_transfer_path(lib, window, B, H, T):
+    """bf16 Falcon-3 at d_k = d_v = 64 with W in {2, 4, 8}: the window pass,
+    Falcon-1 records for every 64-token chunk and the Falcon-1 walk (split
+    into segments by the Falcon-1 rule); the workspace is w_t and log2 gamma_t
+    per token, the records, and the segment maps when split."""
+    a = args(variant="F3", window=window, batch=B, heads=H, seqlen=T)
+    bh, nch = B * H, -(-T // 64)
+    g = _f1_segments(bh, 64, nch)
+    nseg = -(-nch // g)
+    n = 2 * _align(bh * nch * 64 * 4) + _align(bh * nch * (2 * 64 * 64 * 2 + 2 * 64 * 64 * 2 + 256))
+    if nseg > 1:
+        n += _align(bh * nseg * (64 * 64 * 2 + 64 * 64 * 4)) + _align(bh * nseg * 4) + _align(bh * nseg * 64 * 64 * 4)
+        assert _names(lib, a) == ["a3_window", "f3_xfer", "f1_segmap", "f1_segscan", "f1_carry"]
+    else:
+        assert _names(lib, a) == ["a3_window", "f3_xfer", "f1_carry"]
+    assert wsize(lib, a) == n
+    # other windows, head sizes or fp32 keep the stacked-row kernels
+    assert _names(lib, args(variant="F3", window=3, batch=B, heads=H, seqlen=T)) == ["feature", "f3_prep", "f3_scan"]
+    assert _names(lib, args(variant="F3", window=window, dv=32, batch=B, heads=H, seqlen=T))[1] == "f3_prep"
 
 
 def test_library_reads_no_tuning_switches():

@@ -705,7 +705,7 @@ def test_chunk_f3_xfer_takes_the_transfer_path():
     names = []
     while (nm := lib.falcon_kernel_name(ctypes.byref(a), len(names))) is not None:
         names.append(nm.decode())
-    assert names == ["feature", "f3_xfer", "f1_carry"]
+    assert names == ["a3_window", "f3_xfer", "f1_carry"]
 
 
 @pytest.mark.parametrize("window", [2, 4, 8])
