@@ -81,6 +81,24 @@ template <> struct Io<float> {
     }
 };
 
+// the value of lane h of each lane quad, in every lane of the quad (DPP
+// quad_perm [h, h, h, h], CTRL = 0x55 h)
+template <int CTRL>
+__device__ __forceinline__ float quad_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// four consecutive elements of an LDS row (8- or 16-byte aligned) as fp32
+__device__ __forceinline__ f32x4 ld4e(const bf16_t *p) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(p);
+    return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                 __uint_as_float(u.y & 0xffff0000u)};
+}
+__device__ __forceinline__ f32x4 ld4e(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ void st4e(bf16_t *p, const f32x4 &v) {
+    *reinterpret_cast<uint2 *>(p) = make_uint2(Io<bf16_t>::p2(v[0], v[1]), Io<bf16_t>::p2(v[2], v[3]));
+}
+__device__ __forceinline__ void st4e(float *p, const f32x4 &v) { *reinterpret_cast<f32x4 *>(p) = v; }
+
 __device__ __forceinline__ float quad_sum(float v) {
     v += dpp<kDppQuadXor1>(v);
     return v + dpp<kDppQuadXor2>(v);
@@ -121,6 +139,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
     __shared__ __align__(16) E GB[C * LC];     // Gram, strictly lower tiles
     __shared__ __align__(16) E PB[C * LC];     // scores, lower incl. diagonal
     __shared__ float4 GDq[4 * 16 * 4];         // diagonal Gram blocks (fp32): [blk][i][q] = G_{i, 4m+q}, m = 0..3
+    __shared__ float4 GDu[4 * 16 * 4];         // their strictly upper parts, same layout (G_{i, 4m+q} for 4m+q > i)
     __shared__ float PD4[4 * 16 * 17];         // diagonal score blocks (fp32)
     __shared__ __align__(16) E ST[DS * LK];    // S^T [j][d]
     __shared__ __align__(16) E WT[DS * LC];    // W^T [j][l]
@@ -312,7 +331,11 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
                 const float v = isG ? (jn < i ? g[r] : 0.f) : (jn <= i ? g[r] : 0.f);
                 st(isG ? GB : PB, size_t(i) * LC + jn, v);
                 if (I == J) {
-                    if (isG) reinterpret_cast<float *>(GDq)[((I * 16 + g4 + r) * 4 + (col & 3)) * 4 + (col >> 2)] = v;
+                    if (isG) {
+                        const int e = ((I * 16 + g4 + r) * 4 + (col & 3)) * 4 + (col >> 2);
+                        reinterpret_cast<float *>(GDq)[e] = v;
+                        reinterpret_cast<float *>(GDu)[e] = jn > i ? g[r] : 0.f;   // the block is symmetric
+                    }
                     else PD4[I * 272 + (g4 + r) * 17 + col] = v;
                 }
             }
@@ -378,32 +401,41 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
                     float w[4] = {0.f, 0.f, 0.f, 0.f};   // w_l = u_l / E_l, l = 4 m + q
                     const float own[4] = {q == 0 ? 1.f : 0.f, q == 1 ? 1.f : 0.f, q == 2 ? 1.f : 0.f,
                                           q == 3 ? 1.f : 0.f};
-                    // operands of step i + 1 are loaded while step i computes
-                    float4 sv_n = SV[j * SVS + 16 * I], gq_n = GDq[(I * 16) * 4 + q];
+                    // Running in-block sums: acc[m] of lane q holds
+                    // sum_{l < t} G_tl w_l for its position t = 4 m + q over the
+                    // writes known so far; once w_i is known, every later
+                    // position adds G_ti w_i (G_ti = G_it, row i of the upper
+                    // part).  With a_i = eta_i (y_i - E_{i-1} h_i) / E_i and
+                    // c_i = eta_i E_{i-1} / E_i (neither depends on the writes)
+                    //     w_i = a_i - c_i acc_i,
+                    // so a step's dependent chain is the broadcast of acc_i from
+                    // its owner lane and two multiply-adds.  Operands of step
+                    // i + 1 are loaded while step i computes.
+                    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+                    float4 sv_n = SV[j * SVS + 16 * I], gu_n = GDu[(I * 16) * 4 + q];
                     float h_n = I > 0 ? H0[jj] : 0.f;
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        const float4 sv = sv_n, gq = gq_n;
+                        const float4 sv = sv_n, gu = gu_n;
                         const float h = h_n;
                         if (i < 15) {
                             sv_n = SV[j * SVS + 16 * I + i + 1];
-                            gq_n = GDq[(I * 16 + i + 1) * 4 + q];
+                            gu_n = GDu[(I * 16 + i + 1) * 4 + q];
                             if (I > 0) h_n = H0[(i + 1) * 17 + jj];
                         }
-                        // w_l = 0 for l >= i (not yet written) and G's diagonal block
-                        // is zero on and above its diagonal: no masks needed
-                        float part_s = 0.f;
-                        if (i > 0) part_s += gq.x * w[0];
-                        if (i > 4) part_s += gq.y * w[1];
-                        if (i > 8) part_s += gq.z * w[2];
-                        if (i > 12) part_s += gq.w * w[3];
-                        const float sum = quad_sum(part_s) + h;
-                        const float u = sv.x * (sv.y - sv.z * sum);
-                        const float wi = u * __builtin_amdgcn_rcpf(sv.w);
-                        // the owner lane of position i adds w_i to its entry,
-                        // which is still zero: a multiply-add by a 0/1 lane
-                        // mask keeps the step free of branches
+                        const float re = __builtin_amdgcn_rcpf(sv.w);
+                        const float ai = sv.x * (sv.y - sv.z * h) * re, ci = sv.x * sv.z * re;
+                        const float x = acc[i >> 2];
+                        const float s_i = (i & 3) == 0 ? quad_bcast<0x00>(x) : (i & 3) == 1 ? quad_bcast<0x55>(x)
+                                        : (i & 3) == 2 ? quad_bcast<0xAA>(x) : quad_bcast<0xFF>(x);
+                        const float wi = fmaf(-ci, s_i, ai);
+                        // the owner lane of position i keeps w_i (its entry is
+                        // still zero: a multiply-add by a 0/1 lane mask)
                         w[i >> 2] = fmaf(own[i & 3], wi, w[i >> 2]);
+                        acc[0] = fmaf(gu.x, wi, acc[0]);
+                        acc[1] = fmaf(gu.y, wi, acc[1]);
+                        acc[2] = fmaf(gu.z, wi, acc[2]);
+                        acc[3] = fmaf(gu.w, wi, acc[3]);
                     }
 #pragma unroll
                     for (int m = 0; m < 4; ++m) st(WT, size_t(j) * LC + 16 * I + 4 * m + q, w[m]);
@@ -421,10 +453,18 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
                         }
                         if (c0 + t < T) Io<E>::store4(og + size_t(c0 + t) * DV + j0 + 16 * sw + g4, ov);
                     }
-                    // rescale W to the block end
-                    for (int l = q; l < 16 * I + 16; l += 4) {
-                        const size_t p = size_t(j) * LC + l;
-                        st(WT, p, fblk * ld(WT, p));
+                    // rescale W to the block end: the quad of column j takes the
+                    // row's 4-element pieces, lane q pieces q, q + 4, .. (every
+                    // load before the first store)
+                    {
+                        E *wrow = WT + size_t(j) * LC;
+                        f32x4 pc[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            if (u <= I) pc[u] = ld4e(wrow + 4 * (q + 4 * u));
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            if (u <= I) st4e(wrow + 4 * (q + 4 * u), pc[u] * fblk);
                     }
                     wave_lds_sync();
                 } else {
