@@ -91,6 +91,18 @@ __device__ __forceinline__ f32x4 mfma16(const s16x4 &a, const s16x4 &b, const f3
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ s16x4 as_s4(const uint2 &u) { return __builtin_bit_cast(s16x4, u); }
+// two 4-token operand pieces side by side: one 8-token piece of a 32-token
+// contraction
+__device__ __forceinline__ bf16x8 cat8(const s16x4 &lo, const s16x4 &hi) {
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// position of token t (t % 4 == 0, and the next 3) in pair order: inside
+// each 32 tokens, the 4-token groups of the two 16-token blocks alternate
+// (t, t + 16, t + 4, t + 20, ...), so that 8 consecutive positions are the
+// tokens one lane of a 32-deep MFMA operand takes
+__device__ __forceinline__ int pair_slot(int t) {
+    return (t & ~31) | (((t & 15) >> 2) << 3) | (((t >> 4) & 1) << 2);
+}
 
 constexpr int NBP = 20;         // bf16 pitch of the 16 x 16 solve blocks
 constexpr int LFB = 16 * 16 + 4;   // fp32 stride of the blocks L_J (the four blocks' rows fall in different banks)
@@ -148,9 +160,9 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1XferA
     constexpr int NJ = DV / 16;               // value column tiles
     constexpr int NT = 4 + NJ;                // column tiles of R = [x part | value part]
     __shared__ __align__(16) bf16_t QB[C * PK];     // q rows [t][d] (qh = s_q q)
-    __shared__ __align__(16) bf16_t XW[DK * PK];    // (diag(e^{b_C-b_t}) x)^T [d][t]
+    __shared__ __align__(16) bf16_t XW[DK * PK];    // (diag(e^{b_C-b_t}) x)^T [d][t], t in pair order
     __shared__ __align__(16) bf16_t YB[C * YP];     // value rows [t][j]
-    __shared__ __align__(16) bf16_t PB[C * PK];     // P [t][s]
+    __shared__ __align__(16) bf16_t PB[C * PK];     // P [t][s], s in pair order
     __shared__ __align__(16) bf16_t XB[C * PK];     // k_{t-1} rows [t][d] (x = s_x k_{t-1})
     __shared__ __align__(16) bf16_t NB[6][16 * NBP];   // -N below the diagonal blocks
     __shared__ __align__(16) bf16_t DB[4][16 * NBP];   // inverses of the diagonal blocks of I + N
@@ -174,6 +186,9 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1XferA
         for (int e = 0; e < 8; ++e) u[e] = (k8 + e == 16 * h + col) ? 0x3F80 : 0;   // bf16 1.0
         IDT[h][lane] = __builtin_bit_cast(bf16x8, u);
     }
+    // the score tiles above the diagonal that the paired products read,
+    // (0, 1) and (2, 3), stay zero (no chunk writes them)
+    for (int e = tid; e < C * PK / 8; e += XW_THREADS) reinterpret_cast<uint4 *>(PB)[e] = make_uint4(0, 0, 0, 0);
     }
 
     // persistent: chunk ids blockIdx.x, + gridDim.x, ...; the rows of the
@@ -293,7 +308,7 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1XferA
     // (diag(e^{b_C-b_t}) x)^T, tile (token block m, feature block n)
     auto transpose_x = [&](int m, int n) {
         const f32x4 ew = *reinterpret_cast<const f32x4 *>(&sv[kEw][16 * m + g4]);
-        put2(XW + (16 * n + col) * PK + 16 * m + g4, pk4(transposed(XB, PK, m, n) * ew));
+        put2(XW + (16 * n + col) * PK + pair_slot(16 * m + g4), pk4(transposed(XB, PK, m, n) * ew));
     };
 
     // 3. waves 0-3: diagonal block J = wave of I + N, inverted in fp32 on
@@ -334,7 +349,7 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1XferA
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = isG ? -v[r] : ((I != J || j0 + r <= i) ? v[r] : 0.f);
-        put2(isG ? NB[jb < 6 ? jb : 0] + col * NBP + g4 : PB + i * PK + j0, pk4(v));
+        put2(isG ? NB[jb < 6 ? jb : 0] + col * NBP + g4 : PB + i * PK + pair_slot(j0), pk4(v));
     };
     if (wave < 4) {
         const int J = wave;
@@ -435,10 +450,13 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1XferA
             const f32x4 z = mfma16(as_s4(*reinterpret_cast<const uint2 *>(DB[I] + col * NBP + 4 * kq)), as_s4(pk4(acc)), z0);
             zb[I] = as_s4(pk4(z));
         }
-        // B operand piece of row r (16-token block I, this lane's 4 tokens)
-        auto tok4 = [&](const bf16_t *base, int ld, int r, int I) {
-            return as_s4(*reinterpret_cast<const uint2 *>(base + r * ld + 16 * I + g4));
-        };
+        // The products contract over tokens 32 at a time: lane (col, q) of
+        // the 16x16x32 MFMA takes the 8 tokens 32 p + 4 q .. + 3 (block 2 p)
+        // and 32 p + 16 + 4 q .. + 3 (block 2 p + 1), so its Z operand is its
+        // two register pieces side by side, and XW and P hold their token
+        // index in that order (pair_slot), one 16-byte read per operand.
+        const bf16x8 zp[2] = {cat8(zb[0], zb[1]), cat8(zb[2], zb[3])};
+        auto tok8 = [&](const bf16_t *base, int r, int p) { return ld8(base + r * PK + 32 * p + k8); };
         // results first, stores after the branch: every wave then issues
         // the same 8 stores on one path
         uint2 o1[4], o2[4];
@@ -448,7 +466,7 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1XferA
             for (int m = 0; m < 4; ++m) {   // A^T tile (d rows of tile n, d' columns of tile m)
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int I = 0; I < 4; ++I) acc = mfma16(zb[I], tok4(XW, PK, 16 * m + col, I), acc);
+                for (int p = 0; p < 2; ++p) acc = mfma(zp[p], tok8(XW, 16 * m + col, p), acc);
                 o1[m] = pk4(acc);
             }
 #pragma unroll
@@ -456,7 +474,7 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1XferA
                 const int tt = 16 * m + col;
                 f32x4 acc = unpk4(*reinterpret_cast<const uint2 *>(QB + tt * PK + 16 * n + g4)) * sv[kQs][tt];
 #pragma unroll
-                for (int I = 0; I <= m; ++I) acc = mfma16(zb[I], tok4(PB, PK, tt, I), acc);
+                for (int p = 0; p <= m / 2; ++p) acc = mfma(zp[p], tok8(PB, tt, p), acc);
                 o2[m] = pk4(acc);
             }
         } else {
@@ -464,7 +482,7 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1XferA
             for (int m = 0; m < 4; ++m) {   // B tile (d' rows of tile m, j columns of tile jt)
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int I = 0; I < 4; ++I) acc = mfma16(tok4(XW, PK, 16 * m + col, I), zb[I], acc);
+                for (int p = 0; p < 2; ++p) acc = mfma(tok8(XW, 16 * m + col, p), zp[p], acc);
                 o1[m] = pk4(acc);
             }
 #pragma unroll
@@ -472,7 +490,7 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1XferA
                 const int tt = 16 * m + col;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int I = 0; I <= m; ++I) acc = mfma16(zb[I], tok4(PB, PK, tt, I), acc);
+                for (int p = 0; p <= m / 2; ++p) acc = mfma(zp[p], tok8(PB, tt, p), acc);
                 o2[m] = pk4(acc);
             }
         }
