@@ -91,18 +91,6 @@ __device__ __forceinline__ f32x4 mfma16(const s16x4 &a, const s16x4 &b, const f3
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ s16x4 as_s4(const uint2 &u) { return __builtin_bit_cast(s16x4, u); }
-// two 4-token operand pieces side by side: one 8-token piece of a 32-token
-// contraction
-__device__ __forceinline__ bf16x8 cat8(const s16x4 &lo, const s16x4 &hi) {
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-// position of token t (t % 4 == 0, and the next 3) in pair order: inside
-// each 32 tokens, the 4-token groups of the two 16-token blocks alternate
-// (t, t + 16, t + 4, t + 20, ...), so that 8 consecutive positions are the
-// tokens one lane of a 32-deep MFMA operand takes
-__device__ __forceinline__ int pair_slot(int t) {
-    return (t & ~31) | (((t & 15) >> 2) << 3) | (((t >> 4) & 1) << 2);
-}
 
 constexpr int NBP = 20;         // bf16 pitch of the 16 x 16 solve blocks
 constexpr int LFB = 16 * 16 + 4;   // fp32 stride of the blocks L_J (the four blocks' rows fall in different banks)

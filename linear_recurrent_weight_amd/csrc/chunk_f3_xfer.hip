@@ -193,9 +193,11 @@ __global__ __launch_bounds__(NTH, 4) void f3_xfer(F3XferArgs a) {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         return mfma(ld8(src + (16 * m + col) * PK + 32 * (n >> 1) + k8), IDT[n & 1][lane], z);
     };
-    auto tok4 = [&](const bf16_t *base, int r, int I) {
-        return as_s4(*reinterpret_cast<const uint2 *>(base + r * PK + 16 * I + g4));
-    };
+    // the products below contract over the 64 stacked rows 32 at a time:
+    // lane (col, q) of the 16x16x32 MFMA takes rows 32 p + 4 q .. + 3 and
+    // 32 p + 16 + 4 q .. + 3, i.e. its two register pieces of Z side by side,
+    // and XW and the scores hold their row index in that order (pair_slot)
+    auto tok8 = [&](const bf16_t *base, int r, int p) { return ld8(base + r * PK + 32 * p + k8); };
 
     for (int s = 0; s < W; ++s) {
         // 1. the sub-chunk's rows to LDS (pairs before position 0 from the
@@ -302,7 +304,7 @@ __global__ __launch_bounds__(NTH, 4) void f3_xfer(F3XferArgs a) {
                     v[r] = live ? acc[r] * score_scale(i, j) : 0.f;
                 }
             }
-            put2(isG ? NB[jb] + col * NBP + g4 : PB + i * PK + j0, pk4(v));
+            put2(isG ? NB[jb] + col * NBP + g4 : PB + i * PK + pair_slot(j0), pk4(v));
         };
         constexpr int NJ = 6 + 4 * NTT;   // jobs: 6 Gram blocks, the score tiles
         if (wave < 4) {
@@ -351,7 +353,7 @@ __global__ __launch_bounds__(NTH, 4) void f3_xfer(F3XferArgs a) {
             for (int u = 0; u < 2; ++u) {
                 const int n = 2 * (wave & 1) + u;
                 const f32x4 ew = *reinterpret_cast<const f32x4 *>(&rs[rEw][16 * m + g4]);
-                put2(XW + (16 * n + col) * PK + 16 * m + g4, pk4(transposed(XB, m, n) * ew));
+                put2(XW + (16 * n + col) * PK + pair_slot(16 * m + g4), pk4(transposed(XB, m, n) * ew));
             }
         }
         __syncthreads();
@@ -390,6 +392,7 @@ __global__ __launch_bounds__(NTH, 4) void f3_xfer(F3XferArgs a) {
                                     as_s4(pk4(acc)), z0);
             zb[I] = as_s4(pk4(zz));
         }
+        const bf16x8 zp[2] = {cat8(zb[0], zb[1]), cat8(zb[2], zb[3])};
 
         // 5. outputs of the sub-chunk's tokens: tile (rows j' of tile n,
         //    token slots of tile tt) = 2^{b_t - b_e} K^T qh_t + Z^T P^T (+ 2^{b_t}
@@ -407,7 +410,7 @@ __global__ __launch_bounds__(NTH, 4) void f3_xfer(F3XferArgs a) {
             }
             if (xp) acc += unpk4(*reinterpret_cast<const uint2 *>(QB + ts_ * PK + 16 * n + g4)) * ts[tGd][ts_];
 #pragma unroll
-            for (int I = 0; I < 4; ++I) acc = mfma16(zb[I], tok4(PB, ts_, I), acc);
+            for (int p = 0; p < 2; ++p) acc = mfma(zp[p], tok8(PB, ts_, p), acc);
             if (ts_ < CT) {
                 const int tr = s * CT + ts_;       // token within the chunk
                 const int m = tr >> 4, cl = tr & 15;
@@ -427,7 +430,7 @@ __global__ __launch_bounds__(NTH, 4) void f3_xfer(F3XferArgs a) {
             for (int m = 0; m < 4; ++m) {
                 f32x4 acc = K[m] * gk;
 #pragma unroll
-                for (int I = 0; I < 4; ++I) acc = mfma16(tok4(XW, 16 * m + col, I), zb[I], acc);
+                for (int p = 0; p < 2; ++p) acc = mfma(tok8(XW, 16 * m + col, p), zp[p], acc);
                 K[m] = acc;
             }
         }

@@ -72,6 +72,22 @@ template <> struct MmaFrag<float> {
     }
 };
 
+// 32-deep contractions from 16-deep register pieces.  A 16x16 accumulator
+// tile read back as a 16x16x16 operand gives lane (col, q) the 4 k values
+// 4 q .. + 3 of its 16-block.  Two such pieces of consecutive 16-blocks side
+// by side (cat8) are the lane's 8 k values of a 16x16x32 operand whose k
+// index runs in pair order: within each 32, the 4-groups of the two 16-blocks
+// alternate (k, k + 16, k + 4, k + 20, ...).  The other operand is stored
+// with its k index in that same order (pair_slot of the first k of each
+// aligned 4-group), so one 16-byte read gives its lane piece.
+typedef short bf16x4_bits __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8 cat8(const bf16x4_bits &lo, const bf16x4_bits &hi) {
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+__device__ __forceinline__ int pair_slot(int k) {
+    return (k & ~31) | (((k & 15) >> 2) << 3) | (((k >> 4) & 1) << 2);
+}
+
 // LDS row padding (elements) that keeps bf16 rows 16-byte aligned
 template <class E> struct Pad;
 template <> struct Pad<bf16_t> { static constexpr int v = 8; };
