@@ -492,7 +492,10 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
                 f32x4 s = S[h] * gC;
                 s = mfma32(ld8(xr + k8), v0, s);
                 s = mfma32(ld8(xr + 32 + k8), v1, s);
-                if constexpr (WIN) s = mfma16(ld4(xr + 64 + g4), ld4(vr + 64 + g4), s);
+                // the halo pairs' 16-deep product in an accumulator of its
+                // own, added on the vector ALU: an accumulator handed from a
+                // 16x16x32 MFMA straight to a 16x16x16 one is not safe
+                if constexpr (WIN) s += mfma16(ld4(xr + 64 + g4), ld4(vr + 64 + g4), f32x4{0.f, 0.f, 0.f, 0.f});
                 S[h] = s;
             }
         }
@@ -679,11 +682,13 @@ __global__ __launch_bounds__(NTH, 4) void a1_output(ChunkAArgs a) {
 // fresh first token).
 __global__ __launch_bounds__(64) void a3_window(ChunkAArgs a) {
     // pair rows without padding, the 16-byte pieces of row p at positions
-    // piece ^ (p % 8) (conflict-free operand reads); 13 KB, so that every
-    // chunk of the workload finds a slot at once (twelve per CU)
+    // piece ^ (p % 8) (conflict-free operand reads); the band rows padded to
+    // 9 floats, so that the 64 lanes (consecutive rows p) of each gather
+    // below fall in 64 different banks.  13.1 KB, so that every chunk of the
+    // workload finds a slot at once (twelve per CU)
     __shared__ __align__(16) bf16_t XR[80 * D];
     __shared__ float sx[80];
-    __shared__ float band[80][8];
+    __shared__ float band[80][9];
     const int c = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
     const int W = a.window, H = W - 1, T = a.T, c0 = c * C;
     const int part = lane & 7, col = lane & 15, g4 = 4 * (lane >> 4), k8 = 8 * (lane >> 4);

@@ -404,7 +404,8 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1XferA
     //    layout of the 16x16x16 MFMA, and read as the A operand it is the
     //    tile transposed.  Z[:, x part] = -W, Z[:, value part] = Ut.
     // 5. With its column tile of Z still in registers, the same wave forms
-    //    the operators that tile feeds (token-k products on 16x16x16 MFMA):
+    //    the operators that tile feeds (token-k products on 16x16x32 MFMA,
+    //    32 tokens per step in pair order):
     //      x tile n (d rows):      A^T [d][d'] = Z_W^T diag(e^{b_C-b_t}) X,
     //                              G^T [d][t]  = diag-scaled Qh^T + Z_W^T P^T;
     //      value tile (j columns): B [d'][j]   = (diag(e^{b_C-b_t}) X)^T Ut,
@@ -425,18 +426,25 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1XferA
             const f32x4 sc = *reinterpret_cast<const f32x4 *>(&sv[xp ? kRs : kEta][16 * I + g4]);
             r0[I] = xp ? transposed(XB, PK, I, n) * -sc : transposed(YB, YP, I, n - 4) * sc;
         }
+        // blocks (1,0) (2,0) (2,1) (3,0) (3,1) (3,2) of -N: the pieces of
+        // (I, 0) and (I, 1) side by side meet Z's blocks 0 and 1 in one
+        // 32-deep MFMA (pair order), which block 3 issues before Z block 2;
+        // block 3's 16-deep term has an accumulator of its own (an
+        // accumulator handed from a 16x16x32 MFMA straight to a 16x16x16
+        // one is not safe)
+        auto nbp = [&](int blk) { return as_s4(*reinterpret_cast<const uint2 *>(NB[blk] + col * NBP + 4 * kq)); };
         s16x4 zb[4];
+        bf16x8 zp01;
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             f32x4 acc = r0[I];
-#pragma unroll
-            for (int J = 0; J < I; ++J) {
-                const int blk = (I * (I - 1)) / 2 + J;   // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
-                acc = mfma16(as_s4(*reinterpret_cast<const uint2 *>(NB[blk] + col * NBP + 4 * kq)), zb[J], acc);
-            }
+            if (I == 1) acc = mfma16(nbp(0), zb[0], acc);
+            if (I >= 2) acc = mfma(cat8(nbp(I == 2 ? 1 : 3), nbp(I == 2 ? 2 : 4)), zp01, acc);
             const f32x4 z0 = {0.f, 0.f, 0.f, 0.f};
+            if (I == 3) acc += mfma16(nbp(5), zb[2], z0);
             const f32x4 z = mfma16(as_s4(*reinterpret_cast<const uint2 *>(DB[I] + col * NBP + 4 * kq)), as_s4(pk4(acc)), z0);
             zb[I] = as_s4(pk4(z));
+            if (I == 1) zp01 = cat8(zb[0], zb[1]);
         }
         // The products contract over tokens 32 at a time: lane (col, q) of
         // the 16x16x32 MFMA takes the 8 tokens 32 p + 4 q .. + 3 (block 2 p)

@@ -378,19 +378,26 @@ __global__ __launch_bounds__(NTH, 4) void f3_xfer(F3XferArgs a) {
                 r0[I] -= rr * cr;
             }
         }
+        // blocks (1,0) (2,0) (2,1) (3,0) (3,1) (3,2) of -N: the pieces of
+        // (I, 0) and (I, 1) side by side meet Z's blocks 0 and 1 in one
+        // 32-deep MFMA (pair order), which block 3 issues before Z block 2;
+        // block 3's 16-deep term has an accumulator of its own (an
+        // accumulator handed from a 16x16x32 MFMA straight to a 16x16x16
+        // one is not safe)
+        auto nbp = [&](int blk) { return as_s4(*reinterpret_cast<const uint2 *>(NB[blk] + col * NBP + 4 * kq)); };
         s16x4 zb[4];
+        bf16x8 zp01;
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             f32x4 acc = r0[I];
-#pragma unroll
-            for (int J = 0; J < I; ++J) {
-                const int blk = (I * (I - 1)) / 2 + J;
-                acc = mfma16(as_s4(*reinterpret_cast<const uint2 *>(NB[blk] + col * NBP + 4 * kq)), zb[J], acc);
-            }
+            if (I == 1) acc = mfma16(nbp(0), zb[0], acc);
+            if (I >= 2) acc = mfma(cat8(nbp(I == 2 ? 1 : 3), nbp(I == 2 ? 2 : 4)), zp01, acc);
             const f32x4 z0 = {0.f, 0.f, 0.f, 0.f};
+            if (I == 3) acc += mfma16(nbp(5), zb[2], z0);
             const f32x4 zz = mfma16(as_s4(*reinterpret_cast<const uint2 *>(DB[I] + col * NBP + 4 * kq)),
                                     as_s4(pk4(acc)), z0);
             zb[I] = as_s4(pk4(zz));
+            if (I == 1) zp01 = cat8(zb[0], zb[1]);
         }
         const bf16x8 zp[2] = {cat8(zb[0], zb[1]), cat8(zb[2], zb[3])};
 
