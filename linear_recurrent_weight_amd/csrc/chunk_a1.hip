@@ -535,22 +535,30 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
                 p = mfma32(ld8(xr + 32), q1, p);
                 const f32x4 cl = *reinterpret_cast<const f32x4 *>(&pv[pCol][16 * m + g4]);
                 const f32x4 bh4 = *reinterpret_cast<const f32x4 *>(&pv[pBh][16 * m + g4]);
-                f32x4 sxb;
-                if constexpr (WIN) sxb = *reinterpret_cast<const f32x4 *>(&pv[pSx][16 * m + g4]);
+                // t - j >= 16 (n - m) + OFF - 15 over the tile: every pair of a
+                // tile that far back is past the window (or, with no window,
+                // at or before every token), so it takes the plain factor
+                if (16 * (n - m) + OFF - 15 >= (WIN ? H : 0)) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = 16 * m + g4 + r - OFF;   // pair's token (chunk-local)
-                    // past the window, before the pair (0), or in the band
-                    // (the pair still in the window at t)
-                    float f = (sep ? 1.f : ex2(bq - bh4[r])) * cl[r] * qf;
-                    if constexpr (WIN) {
-                        const int u = tq - j, uc = u < 0 ? 0 : (u < FALCON_MAX_WINDOW - 1 ? u : FALCON_MAX_WINDOW - 2);
-                        const float fb = bf[uc][tq] * sxb[r] * sqq;
-                        f = u >= H ? f : (u < 0 ? 0.f : fb);
-                    } else {
-                        f = tq >= j ? f : 0.f;
+                    for (int r = 0; r < 4; ++r) p[r] *= (sep ? 1.f : ex2(bq - bh4[r])) * cl[r] * qf;
+                } else {
+                    f32x4 sxb;
+                    if constexpr (WIN) sxb = *reinterpret_cast<const f32x4 *>(&pv[pSx][16 * m + g4]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = 16 * m + g4 + r - OFF;   // pair's token (chunk-local)
+                        // past the window, before the pair (0), or in the band
+                        // (the pair still in the window at t)
+                        float f = (sep ? 1.f : ex2(bq - bh4[r])) * cl[r] * qf;
+                        if constexpr (WIN) {
+                            const int u = tq - j, uc = u < 0 ? 0 : (u < FALCON_MAX_WINDOW - 1 ? u : FALCON_MAX_WINDOW - 2);
+                            const float fb = bf[uc][tq] * sxb[r] * sqq;
+                            f = u >= H ? f : (u < 0 ? 0.f : fb);
+                        } else {
+                            f = tq >= j ? f : 0.f;
+                        }
+                        p[r] *= f;
                     }
-                    p[r] *= f;
                 }
                 const s16x4 pt = pk4s(p);
                 o0 = mfma16(ld4(VT + (16 * jt0 + col) * PX + 16 * m + g4), pt, o0);
