@@ -410,8 +410,11 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
         __syncthreads();
 
         // 2. chunk-local prefix b (base 2), lane = token, and the pair
-        //    coefficients; every wave forms the same values (identical LDS
-        //    writes), so no barrier is needed
+        //    coefficients.  Every wave forms b (identical LDS writes).  Without
+        //    a window every wave also forms the pair coefficients, so no
+        //    barrier is needed; with one (band of the mask, 80 pair rows of up
+        //    to W terms each) wave 0 forms the band and waves 1 and 2 the pair
+        //    rows, and a barrier publishes them
         bool sep;
         float bC;
         {
@@ -425,17 +428,19 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
             if constexpr (OUT && WIN) {
                 // band of the mask: bf[u][t] = M_{t, t-u} = sum_{s = max(t-u, 0)}^{t}
                 // e^{b_t - b_s} w_s for u < W - 1 (pairs still in the window at t)
-                float mc = 0.f;
-                for (int u = 0; u < H; ++u) {
-                    const int s = lane - u, sc = s > 0 ? s : 0;
-                    mc += s >= 0 ? ex2(b - tv[kB][sc]) * tv[kW][sc] : 0.f;
-                    bf[u][lane] = mc;
+                if (wave == 0) {
+                    float mc = 0.f;
+                    for (int u = 0; u < H; ++u) {
+                        const int s = lane - u, sc = s > 0 ? s : 0;
+                        mc += s >= 0 ? ex2(b - tv[kB][sc]) * tv[kW][sc] : 0.f;
+                        bf[u][lane] = mc;
+                    }
                 }
             }
 #pragma unroll
             for (int u = 0; u < (NP + 63) / 64; ++u) {
                 const int p = lane + 64 * u;
-                if (p < NP) {
+                if (p < NP && (!WIN || wave == 1 + u)) {
                     const int j = p - OFF;                     // pair's token (chunk-local)
                     const int lo = j > 0 ? j : 0, hi = j + H < C - 1 ? j + H : C - 1;
                     // c'_j: at most W terms (none for rows before the window)
@@ -454,7 +459,8 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
                 }
             }
         }
-        wave_lds_sync();
+        if constexpr (WIN) __syncthreads();
+        else wave_lds_sync();
         bsum += bC;
 
         // 3. transposes, once per block: waves 0-3 the key blocks (scaled by
