@@ -264,16 +264,15 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1XferA
     }
     __syncthreads();
 
-    // 2. chunk-local prefix b (base 2), lane = token; every wave forms the
-    //    same values (identical LDS writes), so no barrier is needed.  The
-    //    decays are separable (2^{b_i} 2^{-b_j}) while 2^{-b} stays in range.
-    bool sep;
-    {
+    // 2. chunk-local prefix b (base 2), lane = token, and the per-token
+    //    factors, formed by wave 0 and published by a barrier.  The decays
+    //    are separable (2^{b_i} 2^{-b_j}) while 2^{-b} stays in range.
+    if (wave == 0) {
         const float lg = sv[kLg][lane];
         const float b = wave_inclusive_scan(lg);
         const float bp = b - lg;
         const float bC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b), 63));
-        sep = bC >= -100.f;
+        const bool sep = bC >= -100.f;
         const float eta = sv[kEta][lane], sx = sv[kSx][lane], sq = sv[kSq][lane];
         sv[kB][lane] = b;
         sv[kBp][lane] = bp;
@@ -282,9 +281,10 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1XferA
         sv[kRs][lane] = eta * ex2(bp) * sx;
         sv[kQs][lane] = ex2(b) * sq;
         sv[kCs][lane] = sep ? ex2(-b) * sx : 0.f;
-        if (wave == 0 && lane == 0) *reinterpret_cast<float *>(rec + f1_xfer_scal_off(DV)) = ex2(bC);
+        if (lane == 0) *reinterpret_cast<float *>(rec + f1_xfer_scal_off(DV)) = ex2(bC);
     }
-    wave_lds_sync();
+    __syncthreads();
+    const bool sep = sv[kB][C - 1] >= -100.f;
 
     // rows (pitch ld) of a 16 x 32 block, 16 of whose columns (block n of
     // 16) come back transposed into the accumulator layout: lane holds

@@ -241,11 +241,12 @@ __global__ __launch_bounds__(NTH, 4) void f3_xfer(F3XferArgs a) {
         }
         __syncthreads();
 
-        // 2. row and token scalars (every wave forms the same values)
+        // 2. row and token scalars, formed by wave 0 and published by a
+        //    barrier
         const float b_e = s > 0 ? cb[s * CT - 1] : 0.f;
         const float b_e2 = cb[s * CT + CT - 1];
         const bool sep = b_e2 >= b_e - 100.f;
-        {
+        if (wave == 0) {
             const int tc = s * CT + lane / W;
             const float w = cw[tc], bt = cb[tc], bp = tc > 0 ? cb[tc - 1] : 0.f, sx = rsx[lane];
             rs[rW][lane] = w;
@@ -265,7 +266,7 @@ __global__ __launch_bounds__(NTH, 4) void f3_xfer(F3XferArgs a) {
                 ts[tSq][lane] = sq;
             }
         }
-        wave_lds_sync();
+        __syncthreads();
 
         // 3. Gram blocks, scores, diagonal inverses, transposes of x
         //    Gram N_ij = w_i 2^{b_{tau_i - 1} - b_tau_j} x_i . x_j for tau_j < tau_i
