@@ -197,7 +197,8 @@ struct A1Rows {
 //
 // Per chunk, after the rows and the step scalars:
 //   - the pair coefficients: c'_j, the chunk write coefficient and the score
-//     column factor of every pair (every wave forms the same values);
+//     column factor of every pair (without a window every wave forms the same
+//     values; with one, two waves form them and a barrier publishes them);
 //   - waves 0-3 transpose the key blocks (scaled by the write coefficients),
 //     XT[d][p], and waves 4-7 the value blocks, VT[j][p], NMT each, on MFMA
 //     into LDS; each block once per chunk;
@@ -214,8 +215,7 @@ struct A1Rows {
 template <bool OUT, bool WIN>
 __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf16_t *QB, bf16_t *XB, bf16_t *VB,
                                         bf16_t *XH, bf16_t *VH, float (*hsx)[16], bf16_t *XT, bf16_t *VT,
-                                        bf16_t *STb, float (*tv)[C], float (*pv)[Geo<WIN>::NP], float (*bf)[C],
-                                        bf16x8 (*IDT)[64]) {
+                                        bf16_t *STb, float (*tv)[C], float (*pv)[Geo<WIN>::NP], float (*bf)[C]) {
     using G = Geo<WIN>;
     constexpr int OFF = G::OFF, NP = G::NP, NMT = G::NMT, PX = G::PX;
     constexpr int NS = 2;             // state tiles per wave
@@ -230,11 +230,24 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
     const int sj = wave & 3;                 // value tile of the state tiles
     const int sd0 = 2 * (wave >> 2);         // first d tile of the state tiles
 
+    // B operands that pick 16 columns (half h) of a 32-wide A block: the MFMA
+    // then hands back that half transposed into the accumulator layout.  Kept
+    // in registers (8 VGPRs): read from LDS by every transpose they were a
+    // third of the transposes' LDS traffic.
+    bf16x8 pick0, pick1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+        u16x8 u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) u[e] = (k8 + e == 16 * h + col) ? 0x3F80 : 0;   // bf16 1.0
+        (h ? pick1 : pick0) = __builtin_bit_cast(bf16x8, u);
+    }
     // a 16-row tile of row-major LDS rows (pitch PK), columns 16 n .. + 15,
     // in the accumulator layout: lane holds rows g4 .. + 3 of column 16 n + col
     auto transposed = [&](const bf16_t *tile, int n) {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        return mfma32(ld8(tile + col * PK + 32 * (n >> 1) + k8), IDT[n & 1][lane], z);
+        return mfma32(ld8(tile + col * PK + 32 * (n >> 1) + k8), (n & 1) ? pick1 : pick0, z);
     };
 
     // first row of pair tile m: the halo tile (WIN, m = 0) of this chunk's
@@ -635,19 +648,6 @@ __device__ __forceinline__ void a1_walk(const ChunkAArgs &a, int seg, int bh, bf
     }
 }
 
-// B operands that pick 16 columns (half h) of a 32-wide A block
-__device__ __forceinline__ void init_pickers(bf16x8 (*IDT)[64]) {
-    const int tid = threadIdx.x, lane = tid & 63;
-    if (tid < 128) {
-        typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
-        const int h = tid >> 6, col = lane & 15, k8 = 8 * (lane >> 4);
-        u16x8 u;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) u[e] = (k8 + e == 16 * h + col) ? 0x3F80 : 0;   // bf16 1.0
-        IDT[h][lane] = __builtin_bit_cast(bf16x8, u);
-    }
-}
-
 template <bool WIN>
 __global__ __launch_bounds__(NTH, 4) void a1_segment(ChunkAArgs a) {
     using G = Geo<WIN>;
@@ -660,10 +660,7 @@ __global__ __launch_bounds__(NTH, 4) void a1_segment(ChunkAArgs a) {
     __shared__ __align__(16) bf16_t VT[D * G::PX];
     __shared__ __align__(16) float tv[kNtv][C];
     __shared__ __align__(16) float pv[kNpv][G::NP];
-    __shared__ __align__(16) bf16x8 IDT[2][64];
-    init_pickers(IDT);
-    __syncthreads();
-    a1_walk<false, WIN>(a, blockIdx.x, blockIdx.y, nullptr, XB, VB, XH, VH, hsx, XT, VT, nullptr, tv, pv, nullptr, IDT);
+    a1_walk<false, WIN>(a, blockIdx.x, blockIdx.y, nullptr, XB, VB, XH, VH, hsx, XT, VT, nullptr, tv, pv, nullptr);
 }
 
 template <bool WIN>
@@ -681,11 +678,9 @@ __global__ __launch_bounds__(NTH, 4) void a1_output(ChunkAArgs a) {
     __shared__ __align__(16) float tv[kNtv][C];
     __shared__ __align__(16) float pv[kNpv][G::NP];
     __shared__ __align__(16) float bf[WIN ? FALCON_MAX_WINDOW - 1 : 1][C];
-    __shared__ __align__(16) bf16x8 IDT[2][64];
-    init_pickers(IDT);
     // (the entry state's bf16 copy is written inside the walk; the first
-    // barrier of the walk orders it and the pickers before their first reads)
-    a1_walk<true, WIN>(a, blockIdx.x, blockIdx.y, QB, XB, VB, XH, VH, hsx, XT, VT, STb, tv, pv, bf, IDT);
+    // barrier of the walk orders it before its first reads)
+    a1_walk<true, WIN>(a, blockIdx.x, blockIdx.y, QB, XB, VB, XH, VH, hsx, XT, VT, STb, tv, pv, bf);
 }
 
 // Falcon-3A window statistic and step scalars of one chunk (one wave): the

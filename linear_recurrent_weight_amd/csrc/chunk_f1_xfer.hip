@@ -156,23 +156,24 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1XferA
     __shared__ __align__(16) bf16_t DB[4][16 * NBP];   // inverses of the diagonal blocks of I + N
     __shared__ __align__(16) float LF[4 * LFB];         // the strictly lower diagonal blocks L_J, fp32 row-major
     __shared__ __align__(16) float sv[kNsv][C];
-    __shared__ __align__(16) bf16x8 IDT[2][64];        // column pickers (see below), per lane
 
     const int nch = a.nchunks, total = nch * a.BH;
     const int T = a.T;
+    bf16x8 pick0, pick1;   // column pickers (see below), in registers
     {
     const int tid = threadIdx.x, lane = tid & 63;
     const int col = lane & 15, k8 = 8 * (lane >> 4);
     // B operands that pick 16 columns (half h) of a 32-wide A block: the MFMA
     // then hands back the block transposed into the accumulator layout (lane
-    // holds 4 consecutive rows of one column).  Kept in LDS, not registers.
-    if (tid < 128) {
+    // holds 4 consecutive rows of one column).  Kept in registers (8 VGPRs):
+    // read from LDS by every transpose they cost as many LDS reads as the rows.
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
         typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
-        const int h = tid >> 6;
         u16x8 u;
 #pragma unroll
         for (int e = 0; e < 8; ++e) u[e] = (k8 + e == 16 * h + col) ? 0x3F80 : 0;   // bf16 1.0
-        IDT[h][lane] = __builtin_bit_cast(bf16x8, u);
+        (h ? pick1 : pick0) = __builtin_bit_cast(bf16x8, u);
     }
     // the score tiles above the diagonal that the paired products read,
     // (0, 1) and (2, 3), stay zero (no chunk writes them)
@@ -291,7 +292,7 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1XferA
     // rows 16 m + 4 (lane / 16) .. + 3 of column 16 n + lane % 16
     auto transposed = [&](const bf16_t *rows, int ld, int m, int n) {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        return mfma(ld8(rows + (16 * m + col) * ld + 32 * (n >> 1) + k8), IDT[n & 1][lane], z);
+        return mfma(ld8(rows + (16 * m + col) * ld + 32 * (n >> 1) + k8), (n & 1) ? pick1 : pick0, z);
     };
     // (diag(e^{b_C-b_t}) x)^T, tile (token block m, feature block n)
     auto transpose_x = [&](int m, int n) {
