@@ -21,10 +21,11 @@
 //   registers), and the four operator products on MFMA; A, G, B^T and H go
 //   to the workspace in bf16 with e^{b_C}.
 // f1_carry: one workgroup per (head, slice of value columns) walks the
-//   chunks: per chunk each compute wave owns 16 state columns x 16 (or 32)
-//   rows (fp32 MFMA accumulators) and issues the MFMAs of its rows of the
-//   carry and of the outputs of its 16 (or 32) tokens, all from one bf16
-//   copy of the entry state (double-buffered in LDS).  Loader waves copy the
+//   chunks: per chunk each compute wave owns 16 (or 32) state rows of every
+//   column tile of the slice (fp32 MFMA accumulators) and issues the MFMAs of
+//   its rows of the carry and of the outputs of its 16 (or 32) tokens, all
+//   from one bf16 copy of the entry state (double-buffered in LDS); a row
+//   tile's operators are read once per step for all column tiles.  Loader waves copy the
 //   operators of later chunks straight from memory into a ring of LDS slots
 //   (global_load_lds), so no register staging sits between memory and the
 //   matrix cores; the records hold their tiles in operand lane order, so
@@ -534,14 +535,14 @@ __device__ __forceinline__ void loader_barrier() {
 // row tiles of the state split over compute waves: each column tile has
 // RS waves (RS = 4 while the workgroup stays within 16 waves)
 template <int DS> constexpr int carry_rs() { return DS == 64 ? 2 : 4; }
-template <int DS> constexpr int carry_threads() { return (DS / 16 * carry_rs<DS>() + 4) * 64; }
+template <int DS> constexpr int carry_threads() { return (carry_rs<DS>() + 4) * 64; }
 
 template <int DS>
 __global__ __launch_bounds__(carry_threads<DS>()) void f1_carry(F1XferArgs a, int nslice, int nbase) {
     constexpr int NCT = DS / 16;                 // column tiles of the slice
     constexpr int RS = carry_rs<DS>();           // row groups per column tile
     constexpr int MT = 4 / RS;                   // row tiles (of 16) per compute wave
-    constexpr int NCW = RS * NCT;                // compute waves
+    constexpr int NCW = RS;                      // compute waves (each takes every column tile)
     constexpr int NLW = 4;                       // loader waves
     constexpr int kA = 0, kG = 8192, kB = 16384, kH = 16384 + 128 * DS, kS = 16384 + 256 * DS;
     constexpr int SB = kS + 256;                 // slot bytes
@@ -633,75 +634,91 @@ __global__ __launch_bounds__(carry_threads<DS>()) void f1_carry(F1XferArgs a, in
         return;
     }
 
-    // ---- compute wave: state columns j0 + 16 ct .. + 15, row tiles
-    //      m = MT mh .. MT mh + MT - 1, and the outputs of the same token
-    //      tiles for those columns ----
-    const int ct = wave % NCT, mh = wave / NCT;
+    // ---- compute wave: row tiles m = MT mh .. MT mh + MT - 1 of every
+    //      column tile ct of the slice, and the outputs of the same token
+    //      tiles for those columns; a row tile's A and G operands are read
+    //      once per step for all column tiles ----
+    const int mh = wave;
     const int col = lane & 15, g4 = 4 * (lane >> 4), k8 = 8 * (lane >> 4);
     // byte offsets inside a slot: the operand pieces of this lane (tiles in
     // lane order), A and G at k half 0 (+ 1024 for half 1), B^T and H tiles
-    // of column tile ct
-    const int ao = 16 * lane, bo = ct * 2048 + 8 * lane;
-    bf16_t *og = static_cast<bf16_t *>(a.o) + size_t(bh) * T * DV + j0 + 16 * ct + g4;
+    // of column tile ct at + ct * 2048
+    const int ao = 16 * lane, bo = 8 * lane;
+    bf16_t *og = static_cast<bf16_t *>(a.o) + size_t(bh) * T * DV + j0 + g4;
 
-    f32x4 S[MT];
+    f32x4 S[NCT][MT];
 #pragma unroll
-    for (int h = 0; h < MT; ++h) {
-        const int m = MT * mh + h;
-        if (g > 0) {
-            S[h] = reinterpret_cast<const f32x4 *>(S0)[(m * (DV / 16) + j0 / 16 + ct) * 64 + lane];
-        } else {
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                S[h][r] = S0 ? S0[(size_t(bh) * DK + 16 * m + g4 + r) * DV + j0 + 16 * ct + col] : 0.f;
+        for (int h = 0; h < MT; ++h) {
+            const int m = MT * mh + h;
+            if (g > 0) {
+                S[ct][h] = reinterpret_cast<const f32x4 *>(S0)[(m * (DV / 16) + j0 / 16 + ct) * 64 + lane];
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    S[ct][h][r] = S0 ? S0[(size_t(bh) * DK + 16 * m + g4 + r) * DV + j0 + 16 * ct + col] : 0.f;
+            }
+            put2(STw[0][ct] + col * PK + 16 * m + g4, pk4(S[ct][h]));
         }
-        put2(STw[0][ct] + col * PK + 16 * m + g4, pk4(S[h]));
-    }
     __syncthreads();
     for (int c = 0; c < nch; ++c) {
         const unsigned char *sl = ring + (c % NB) * SB;
-        const bf16_t *stw = STw[c & 1][ct];
         // every LDS read of the step first, so that one latency covers them
-        const bf16x8 sb0 = ld8(stw + col * PK + k8), sb1 = ld8(stw + col * PK + 32 + k8);
+        bf16x8 sb0[NCT], sb1[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const bf16_t *stw = STw[c & 1][ct];
+            sb0[ct] = ld8(stw + col * PK + k8);
+            sb1[ct] = ld8(stw + col * PK + 32 + k8);
+        }
         const float gC = *reinterpret_cast<const float *>(sl + kS);
-        uint2 bq[MT], hq[MT];
+        uint2 bq[NCT][MT], hq[NCT][MT];
         bf16x8 a0[MT], a1[MT], q0[MT], q1[MT];
 #pragma unroll
         for (int h = 0; h < MT; ++h) {
             const int m = MT * mh + h;
-            bq[h] = *reinterpret_cast<const uint2 *>(sl + kB + bo + m * 512);
-            hq[h] = *reinterpret_cast<const uint2 *>(sl + kH + bo + m * 512);
             a0[h] = ld8(sl + kA + m * 2048 + ao);
             a1[h] = ld8(sl + kA + m * 2048 + 1024 + ao);
             q0[h] = ld8(sl + kG + m * 2048 + ao);
             q1[h] = ld8(sl + kG + m * 2048 + 1024 + ao);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                bq[ct][h] = *reinterpret_cast<const uint2 *>(sl + kB + ct * 2048 + bo + m * 512);
+                hq[ct][h] = *reinterpret_cast<const uint2 *>(sl + kH + ct * 2048 + bo + m * 512);
+            }
         }
-        bf16_t *stn = STw[(c + 1) & 1][ct];
 #pragma unroll
-        for (int h = 0; h < MT; ++h) {
-            const int m = MT * mh + h;
-            // carry: S' = e^{b_C} S + B + A S  (row tile m); the two k halves
-            // accumulate separately (two MFMA chains of one)
-            f32x4 sn = unpk4(bq[h]);
+        for (int ct = 0; ct < NCT; ++ct) {
+            bf16_t *stn = STw[(c + 1) & 1][ct];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sn[r] += gC * S[h][r];
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            sn = mfma(a0[h], sb0, sn);
-            S[h] = sn + mfma(a1[h], sb1, z);
-            put2(stn + col * PK + 16 * m + g4, pk4(S[h]));
-            // outputs: O^T = S^T G^T + H^T (token tile m)
-            const f32x4 o = mfma(sb0, q0[h], unpk4(hq[h])) + mfma(sb1, q1[h], z);
-            const int tg = (c_lo + c) * C + 16 * m + col;
-            if (tg < T) put2(og + size_t(tg) * DV, pk4(o));
+            for (int h = 0; h < MT; ++h) {
+                const int m = MT * mh + h;
+                // carry: S' = e^{b_C} S + B + A S  (row tile m); the two k
+                // halves accumulate separately (two MFMA chains of one)
+                f32x4 sn = unpk4(bq[ct][h]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sn[r] += gC * S[ct][h][r];
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                sn = mfma(a0[h], sb0[ct], sn);
+                S[ct][h] = sn + mfma(a1[h], sb1[ct], z);
+                put2(stn + col * PK + 16 * m + g4, pk4(S[ct][h]));
+                // outputs: O^T = S^T G^T + H^T (token tile m)
+                const f32x4 o = mfma(sb0[ct], q0[h], unpk4(hq[ct][h])) + mfma(sb1[ct], q1[h], z);
+                const int tg = (c_lo + c) * C + 16 * m + col;
+                if (tg < T) put2(og + size_t(tg) * DV + 16 * ct, pk4(o));
+            }
         }
         __syncthreads();
     }
     if (a.S_out && last_seg) {
 #pragma unroll
-        for (int h = 0; h < MT; ++h)
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                a.S_out[(size_t(bh) * DK + 16 * (MT * mh + h) + g4 + r) * DV + j0 + 16 * ct + col] = S[h][r];
+            for (int h = 0; h < MT; ++h)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    a.S_out[(size_t(bh) * DK + 16 * (MT * mh + h) + g4 + r) * DV + j0 + 16 * ct + col] = S[ct][h][r];
     }
 }
 
