@@ -14,9 +14,11 @@
 // elementwise.  The rewrite needs 1/Gamma in range: a chunk in which some
 // column decays below 2^-64 is run token by token instead (exact, slower).
 //
-// One workgroup (4 waves) per (batch*head, slice of up to 32 value columns)
+// One workgroup (8 waves) per (batch*head, slice of up to 32 value columns)
 // walks its chunks in order; the fp32 state slice stays in LDS, and the next
-// chunk's rows load into registers while a chunk is processed.
+// chunk's rows load into registers (first four waves) while a chunk is
+// processed; all eight share the per-column scans, score, output and state
+// tiles.
 #include "chunk_layout.h"
 #include "kernels.h"
 #include "mma.h"
@@ -25,7 +27,8 @@ namespace falcon {
 namespace {
 
 constexpr int C = kChunk;
-constexpr int NT = 256;
+constexpr int NT = 512;   // 8 waves: the row phase takes the first 4 (NR threads)
+constexpr int NR = 256;
 constexpr float kMinLog2Decay = -64.f;
 
 template <class E, int DK, int DS>
@@ -80,7 +83,7 @@ __device__ __forceinline__ void put_row(E *dst, const float *v) {
 }
 
 template <class E, int DK, int DS>
-__global__ __launch_bounds__(NT) void chunk_f2a_kernel(ChunkF2Args a, int nslice) {
+__global__ __launch_bounds__(NT, 4) void chunk_f2a_kernel(ChunkF2Args a, int nslice) {
     using Sh = F2aShared<E, DK, DS>;
     __shared__ __align__(16) Sh sh;
     // workgroup -> (head, slice): the slices of a head share an XCD (block
@@ -103,10 +106,12 @@ __global__ __launch_bounds__(NT) void chunk_f2a_kernel(ChunkF2Args a, int nslice
         st(&sh.ST[j][0], d, s0);
     }
 
-    // rows: thread (row = tid / 4, part = tid % 4) holds DK / 4 features and
-    // DS / 4 values and gains of one token, loaded as 8-byte pieces one chunk
-    // ahead (unconditional loads from rows clamped into [0, T))
-    const int row = tid >> 2, part = tid & 3;
+    // rows: thread (row = tid / 4, part = tid % 4) of the first NR holds
+    // DK / 4 features and DS / 4 values and gains of one token, loaded as
+    // 8-byte pieces one chunk ahead (unconditional loads from rows clamped
+    // into [0, T)); the other waves take part in the later phases only
+    const bool rower = tid < NR;
+    const int row = (tid & (NR - 1)) >> 2, part = tid & 3;
     constexpr int EK = DK / 4, EV = DS / 4;
     constexpr int NQ = EK / Io8<E>::n, NVv = EV / Io8<E>::n;
     static_assert(NQ >= 1 && NVv >= 1 && EV % 4 == 0, "whole 8-byte pieces per thread");
@@ -132,11 +137,11 @@ __global__ __launch_bounds__(NT) void chunk_f2a_kernel(ChunkF2Args a, int nslice
         for (int i = 0; i < EV / 4; ++i) rb[i] = b4[i];
         rlam = a.lambda[size_t(bh) * T + tq];
     };
-    prefetch(0);
+    if (rower) prefetch(0);
 
     for (int c = 0; c < a.nchunks; ++c) {
         __syncthreads();   // the previous chunk's readers are done
-        {
+        if (rower) {
             const int t = c * C + row;
             const bool qok = t < T;
             float q[EK], x[EK], y[EV];
@@ -187,7 +192,7 @@ __global__ __launch_bounds__(NT) void chunk_f2a_kernel(ChunkF2Args a, int nslice
                 sh.lam[row] = rlam;
                 sh.ok[row] = (qok && !(t == 0 && a.fresh)) ? 1.f : 0.f;   // the fresh first step writes nothing
             }
-            if (c + 1 < a.nchunks) prefetch(c + 1);
+            if (c + 1 < a.nchunks) prefetch(c + 1);   // (rower: inside the row phase)
         }
         __syncthreads();
 
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(NT) void chunk_f2a_kernel(ChunkF2Args a, int nslice
 
         if (fast) {
             // L = lower(Qh X^T), 16 x 16 tiles
-            for (int tile = wave; tile < 16; tile += 4) {
+            for (int tile = wave; tile < 16; tile += NT / 64) {
                 const int m = tile >> 2, n = tile & 3;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                 if (n <= m) acc = Mma<E>::run(acc, &sh.Qh[16 * m][0], DK + Sh::PE, &sh.Xr[16 * n][0], DK + Sh::PE, 0, DK);
@@ -227,7 +232,7 @@ __global__ __launch_bounds__(NT) void chunk_f2a_kernel(ChunkF2Args a, int nslice
             }
             __syncthreads();
             // outputs: O = Gamma (Qh S_0 + L yt)
-            for (int tile = wave; tile < 4 * (DS / 16); tile += 4) {
+            for (int tile = wave; tile < 4 * (DS / 16); tile += NT / 64) {
                 const int m = tile / (DS / 16), n = tile % (DS / 16);
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                 acc = Mma<E>::run(acc, &sh.Qh[16 * m][0], DK + Sh::PE, &sh.ST[16 * n][0], DK + Sh::PE, 0, DK);
@@ -241,7 +246,7 @@ __global__ __launch_bounds__(NT) void chunk_f2a_kernel(ChunkF2Args a, int nslice
             }
             __syncthreads();
             // state: S_C = Gamma_C (S_0 + X^T yt)
-            for (int tile = wave; tile < (DK / 16) * (DS / 16); tile += 4) {
+            for (int tile = wave; tile < (DK / 16) * (DS / 16); tile += NT / 64) {
                 const int m = tile / (DS / 16), n = tile % (DS / 16);
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                 acc = Mma<E>::run(acc, &sh.XT[16 * m][0], C + Sh::PE, &sh.YT[16 * n][0], C + Sh::PE, 0, C);
