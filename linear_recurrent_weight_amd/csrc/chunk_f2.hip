@@ -382,12 +382,24 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
             }
         __syncthreads();
 
+        // Chunk frame: while every column of the slice keeps e^{b_C} >=
+        // 2^-100, the writes are kept as e^{-b_l} u_l (chunk-start frame), so
+        // no block rescales the earlier ones and the state update scales once
+        // by e^{b_C}; otherwise each block works in its own frame and rescales
+        // (and a block that decays too far takes the exact form).  Every wave
+        // forms the same flag from the chunk prefix.
+        const bool cframe = __all(lane >= DS || EB[63 * RS + (lane < DS ? lane : 0)] >= 0x1p-100f);
+
         // ---- P3: blocked per-column solve (wave sw: columns 16 sw ..) ----
         if (wave < NCT) {
             const int sw = wave, jj = lane >> 2, q = lane & 3, j = 16 * sw + jj;
             float *H0 = Hs[sw][0], *H1 = Hs[sw][1];
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
+                // e^{b_s} of this lane's column (s: the token before the block)
+                // and its reciprocal, for the chunk frame
+                const float ebs = (cframe && I > 0) ? EB[(16 * I - 1) * RS + j] : 1.f;
+                const float iebs = __builtin_amdgcn_rcpf(ebs);
                 if (I > 0) {
                     const f32x4 h = Mma<E>::run(f32x4{0.f, 0.f, 0.f, 0.f}, GB + 16 * I * LC, LC,
                                                 WT + 16 * sw * LC, LC, 0, kend_for<E>(16 * I));
@@ -395,7 +407,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
                     for (int r = 0; r < 4; ++r) H0[(g4 + r) * 17 + col] = h[r];
                 }
                 const float fblk = SV[j * SVS + 16 * I + 15].w;   // e^{b_end - b_s}
-                const bool sep = __all(fblk >= 0x1p-100f);
+                const bool sep = cframe || __all(fblk >= 0x1p-100f);
                 wave_lds_sync();
                 if (sep) {
                     float w[4] = {0.f, 0.f, 0.f, 0.f};   // w_l = u_l / E_l, l = 4 m + q
@@ -424,7 +436,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
                             if (I > 0) h_n = H0[(i + 1) * 17 + jj];
                         }
                         const float re = __builtin_amdgcn_rcpf(sv.w);
-                        const float ai = sv.x * (sv.y - sv.z * h) * re, ci = sv.x * sv.z * re;
+                        const float ai = sv.x * fmaf(sv.y, iebs, -sv.z * h) * re, ci = sv.x * sv.z * re;
                         const float x = acc[i >> 2];
                         const float s_i = (i & 3) == 0 ? quad_bcast<0x00>(x) : (i & 3) == 1 ? quad_bcast<0x55>(x)
                                         : (i & 3) == 2 ? quad_bcast<0xAA>(x) : quad_bcast<0xFF>(x);
@@ -449,14 +461,15 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int jr = 16 * sw + g4 + r;
-                            ov[r] = OA[t * RS + jr] + SV[jr * SVS + t].w * o[r];
+                            const float eo = (cframe && I > 0) ? EB[(16 * I - 1) * RS + jr] : 1.f;
+                            ov[r] = OA[t * RS + jr] + SV[jr * SVS + t].w * eo * o[r];
                         }
                         if (c0 + t < T) Io<E>::store4(og + size_t(c0 + t) * DV + j0 + 16 * sw + g4, ov);
                     }
                     // rescale W to the block end: the quad of column j takes the
                     // row's 4-element pieces, lane q pieces q, q + 4, .. (every
                     // load before the first store)
-                    {
+                    if (!cframe) {
                         E *wrow = WT + size_t(j) * LC;
                         f32x4 pc[4];
 #pragma unroll
@@ -520,16 +533,21 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
         }
         __syncthreads();
 
-        // ---- P4: S = e^{b_C} S + X^T W (W = writes rescaled to the chunk end) ----
+        // ---- P4: S = e^{b_C} S + X^T W (W = writes rescaled to the chunk end),
+        //      or in the chunk frame S = e^{b_C} (S + X^T W) ----
 #pragma unroll
         for (int m = 0; m < NDT; ++m)
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
                 const int dbase = 16 * (wave + NW * m);
                 const float gC = EB[63 * RS + 16 * ct + col];
+                if (cframe) {
+                    S[m][ct] = Mma<E>::run(S[m][ct], XT + dbase * LC, LC, WT + 16 * ct * LC, LC, 0, C) * gC;
+                } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) S[m][ct][r] *= gC;
-                S[m][ct] = Mma<E>::run(S[m][ct], XT + dbase * LC, LC, WT + 16 * ct * LC, LC, 0, C);
+                    for (int r = 0; r < 4; ++r) S[m][ct][r] *= gC;
+                    S[m][ct] = Mma<E>::run(S[m][ct], XT + dbase * LC, LC, WT + 16 * ct * LC, LC, 0, C);
+                }
                 st4(ST + (16 * ct + col) * LK + dbase + g4, S[m][ct]);
             }
         __syncthreads();
