@@ -452,8 +452,10 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
 #pragma unroll
                     for (int m = 0; m < 4; ++m) st(WT, size_t(j) * LC + 16 * I + 4 * m + q, w[m]);
                     wave_lds_sync();
-                    // outputs of the block: o_t = OA_t + E_t (P0 [W; w])_t, as O^T tiles
-                    {
+                    // outputs of the block: o_t = OA_t + E_t (P0 [W; w])_t, as O^T
+                    // tiles (in the chunk frame every wave forms them after the
+                    // solve, beside the state update)
+                    if (!cframe) {
                         const f32x4 o = Mma<E>::run(f32x4{0.f, 0.f, 0.f, 0.f}, WT + 16 * sw * LC, LC,
                                                     PB + 16 * I * LC, LC, 0, kend_for<E>(16 * I + 16));
                         const int t = 16 * I + col;
@@ -461,8 +463,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int jr = 16 * sw + g4 + r;
-                            const float eo = (cframe && I > 0) ? EB[(16 * I - 1) * RS + jr] : 1.f;
-                            ov[r] = OA[t * RS + jr] + SV[jr * SVS + t].w * eo * o[r];
+                            ov[r] = OA[t * RS + jr] + SV[jr * SVS + t].w * o[r];
                         }
                         if (c0 + t < T) Io<E>::store4(og + size_t(c0 + t) * DV + j0 + 16 * sw + g4, ov);
                     }
@@ -550,6 +551,24 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
                 }
                 st4(ST + (16 * ct + col) * LK + dbase + g4, S[m][ct]);
             }
+        // ---- P3b (chunk frame): the outputs of every block at once,
+        //      o_t = OA_t + e^{b_t} (P0 W)_t with W = e^{-b_l} u_l, one O^T tile
+        //      (columns 16 ct .., tokens 16 I ..) per wave ----
+        if (cframe) {
+            for (int tile = wave; tile < 4 * NCT; tile += NW) {
+                const int ct = tile % NCT, I = tile / NCT;
+                const f32x4 o = Mma<E>::run(f32x4{0.f, 0.f, 0.f, 0.f}, WT + 16 * ct * LC, LC,
+                                            PB + 16 * I * LC, LC, 0, kend_for<E>(16 * I + 16));
+                const int t = 16 * I + col;
+                float ov[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int jr = 16 * ct + g4 + r;
+                    ov[r] = OA[t * RS + jr] + EB[t * RS + jr] * o[r];
+                }
+                if (c0 + t < T) Io<E>::store4(og + size_t(c0 + t) * DV + j0 + 16 * ct + g4, ov);
+            }
+        }
         __syncthreads();
     }
 
