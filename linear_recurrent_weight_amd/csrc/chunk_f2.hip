@@ -424,16 +424,26 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
                     // its owner lane and two multiply-adds.  Operands of step
                     // i + 1 are loaded while step i computes.
                     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-                    float4 sv_n = SV[j * SVS + 16 * I], gu_n = GDu[(I * 16) * 4 + q];
-                    float h_n = I > 0 ? H0[jj] : 0.f;
+                    // operands of steps i .. i + 3 in flight (a rotating
+                    // buffer): the two solving waves run alone on their SIMDs,
+                    // so nothing else hides an LDS round trip per step
+                    constexpr int PF = 4;
+                    float4 svb[PF], gub[PF];
+                    float hb[PF];
+#pragma unroll
+                    for (int u = 0; u < PF; ++u) {
+                        svb[u] = SV[j * SVS + 16 * I + u];
+                        gub[u] = GDu[(I * 16 + u) * 4 + q];
+                        hb[u] = I > 0 ? H0[u * 17 + jj] : 0.f;
+                    }
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        const float4 sv = sv_n, gu = gu_n;
-                        const float h = h_n;
-                        if (i < 15) {
-                            sv_n = SV[j * SVS + 16 * I + i + 1];
-                            gu_n = GDu[(I * 16 + i + 1) * 4 + q];
-                            if (I > 0) h_n = H0[(i + 1) * 17 + jj];
+                        const float4 sv = svb[i % PF], gu = gub[i % PF];
+                        const float h = hb[i % PF];
+                        if (i + PF < 16) {
+                            svb[i % PF] = SV[j * SVS + 16 * I + i + PF];
+                            gub[i % PF] = GDu[(I * 16 + i + PF) * 4 + q];
+                            if (I > 0) hb[i % PF] = H0[(i + PF) * 17 + jj];
                         }
                         const float re = __builtin_amdgcn_rcpf(sv.w);
                         const float ai = sv.x * fmaf(sv.y, iebs, -sv.z * h) * re, ci = sv.x * sv.z * re;
