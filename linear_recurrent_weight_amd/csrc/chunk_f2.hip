@@ -24,6 +24,10 @@
 // When a block decays below 2^-100 (1 / E_l could overflow) it takes the
 // exact form instead: v_l = e^{b_{t-1} - b_l} u_l multiplied by gamma_t at
 // every step, outputs inside the step.  Both leave W rescaled to the block end.
+// While every column of the slice keeps e^{b_C} >= 2^-100 (the usual case),
+// the frame is the chunk start instead (s = -1 for every block: W_l =
+// e^{-b_l} u_l, never rescaled), the outputs of all blocks are one MFMA pass
+// after the solve, and the state update is S_C = e^{b_C} (S_0 + X^T W).
 //
 // Lanes of a solve wave: 4 per column (16 columns per wave), each owning the
 // block positions l = q (mod 4); the in-block sums are quad sums (DPP).
