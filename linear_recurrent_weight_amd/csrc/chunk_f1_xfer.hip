@@ -247,15 +247,11 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1XferA
         } else {
             *reinterpret_cast<uint2 *>(YB + row * YP + VPT * part) = qok ? make_uint2(vr[0].x, vr[0].y) : make_uint2(0, 0);
         }
-        if (part == 0) {
-            float eta = 0.f, alpha = 0.f;
-            if (!(t >= T || (first && a.fresh))) {   // the fresh first step writes nothing
-                const float den = n2 + lam + a.eps;
-                eta = den != 0.f ? beta * __builtin_amdgcn_rcpf(den) : 0.f;
-                alpha = step_alpha(eta, lam, a.eps_gamma);
-            }
-            sv[kEta][row] = eta;
-            sv[kLg][row] = log2_1m(alpha);
+        if (part == 0) {   // the step inputs; wave 0 forms eta and log2 gamma
+            // beta = 0 past the sequence and at a fresh first step (no write)
+            sv[kEta][row] = (t >= T || (first && a.fresh)) ? 0.f : beta;
+            sv[kLg][row] = lam;
+            sv[kB][row] = n2;
             sv[kSx][row] = sck;
             sv[kSq][row] = scq;
         }
@@ -270,12 +266,21 @@ __global__ __launch_bounds__(XW_THREADS, DV == 128 ? 2 : 4) void f1_xfer(F1XferA
     //    factors, formed by wave 0 and published by a barrier.  The decays
     //    are separable (2^{b_i} 2^{-b_j}) while 2^{-b} stays in range.
     if (wave == 0) {
-        const float lg = sv[kLg][lane];
+        // eta and log2 gamma of token `lane` (a zero beta gives eta = 0 and
+        // gamma = 1: no write)
+        float eta;
+        {
+            const float beta = sv[kEta][lane], lam = sv[kLg][lane], n2 = sv[kB][lane];
+            const float den = n2 + lam + a.eps;
+            eta = den != 0.f ? beta * __builtin_amdgcn_rcpf(den) : 0.f;
+        }
+        const float lg = log2_1m(step_alpha(eta, sv[kLg][lane], a.eps_gamma));
+        sv[kEta][lane] = eta;
         const float b = wave_inclusive_scan(lg);
         const float bp = b - lg;
         const float bC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b), 63));
         const bool sep = bC >= -100.f;
-        const float eta = sv[kEta][lane], sx = sv[kSx][lane], sq = sv[kSq][lane];
+        const float sx = sv[kSx][lane], sq = sv[kSq][lane];
         sv[kB][lane] = b;
         sv[kBp][lane] = bp;
         // with the RMS scales of the rows folded in: x = s_x k_{t-1}, qh = s_q q
