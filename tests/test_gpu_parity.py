@@ -788,6 +788,31 @@ def test_chunk_f2_steep_decay_blocks(eps_gamma, lam_hi, dtype):
     assert eo <= tol and es <= tol, (eo, es)
 
 
+@pytest.mark.parametrize("dk,dv,lam_lo,lam_hi", [(128, 64, 100.0, 200.0), (64, 32, 40.0, 80.0)])
+def test_chunk_f2_block_frames(dk, dv, lam_lo, lam_hi):
+    """Chunks that decay below 2^-100 while their 16-token blocks stay above
+    it: the solve keeps a frame per block and rescales the earlier writes (the
+    chunk-start frame needs e^{b_C} >= 2^-100 in every column of a slice).
+    d_k = 128 is the c4 kernel's shape."""
+    w = gu.small("F2", "bf16", B=1, H=2, T=200, dk=dk, dv=dv, chunk=64, lam_lo=lam_lo, lam_hi=lam_hi,
+                 eps_gamma=1e-3, seed=77)
+    inp = gu.make(w)
+    inp["beta"] = (1.0 + inp["beta"]).astype(np.float32)
+    dev = gu.to_device(inp, w)
+    o, st = gu.run_gpu(w, dev)
+    o_ref, st_ref, tr = gu.oracle_heads(w, inp, np.arange(2), trace=True)
+    # per (chunk, column) log2 decay of whole chunks and of 16-token blocks
+    lg = np.log2(np.maximum(1.0 - np.asarray(tr.alpha, np.float64), 1e-300))   # [head, t, column]
+    lg = lg[:, :192].reshape(lg.shape[0], 3, 4, 16, lg.shape[2])   # three whole chunks
+    chunk_decay = lg.sum(axis=(2, 3))
+    block_decay = lg.sum(axis=3)
+    assert (chunk_decay < -100).mean() > 0.5, "most chunks leave the chunk frame"
+    assert (block_decay >= -100).mean() > 0.9, "the blocks stay separable"
+    eo, es = gu.compare(w, np.arange(2), o, st, o_ref, st_ref)
+    tol = gu.tol_for(w)
+    assert eo <= tol and es <= tol, (eo, es)
+
+
 # -- Falcon-2A chunk path -------------------------------------------------------
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
