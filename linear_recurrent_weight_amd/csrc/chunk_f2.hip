@@ -45,6 +45,16 @@ namespace {
 
 constexpr int C = kChunk;
 
+// fp32 -> bf16, rounded to nearest even by the conversion instruction
+// (two values packed in one word, the first in the low half)
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+    typedef float f2v __attribute__((ext_vector_type(2)));
+    typedef __bf16 h2v __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2v{a, b}, h2v));
+}
+__device__ __forceinline__ void sth(bf16_t *p, size_t i, float v) { p[i].bits = __builtin_bit_cast(uint16_t, (__bf16)v); }
+__device__ __forceinline__ void sth(float *p, size_t i, float v) { p[i] = v; }
+
 // 16-byte vectors <-> floats for the io type
 template <class E> struct Io;
 template <> struct Io<bf16_t> {
@@ -57,9 +67,7 @@ template <> struct Io<bf16_t> {
             f[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
         }
     }
-    __device__ static uint32_t p2(float a, float b) {
-        return uint32_t(f32_to_bf16(a)) | (uint32_t(f32_to_bf16(b)) << 16);
-    }
+    __device__ static uint32_t p2(float a, float b) { return bf16x2_rne(a, b); }
     __device__ static uint4 pack(const float *f) {
         return make_uint4(p2(f[0], f[1]), p2(f[2], f[3]), p2(f[4], f[5]), p2(f[6], f[7]));
     }
@@ -86,10 +94,11 @@ template <> struct Io<float> {
 };
 
 // the value of lane h of each lane quad, in every lane of the quad (DPP
-// quad_perm [h, h, h, h], CTRL = 0x55 h)
+// quad_perm [h, h, h, h], CTRL = 0x55 h; every lane is written, so the
+// destination needs no old value)
 template <int CTRL>
 __device__ __forceinline__ float quad_bcast(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 // four consecutive elements of an LDS row (8- or 16-byte aligned) as fp32
 __device__ __forceinline__ f32x4 ld4e(const bf16_t *p) {
@@ -213,8 +222,8 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
     // the tiles above the diagonal are never written but are read (times
     // zero) by the bf16 MFMA k steps of 32: they must hold zeros, not NaNs
     for (int idx = tid; idx < C * LC; idx += NT) {
-        st(GB, idx, 0.f);
-        st(PB, idx, 0.f);
+        sth(GB, idx, 0.f);
+        sth(PB, idx, 0.f);
     }
 
     // ---- state: d tiles {wave, wave + NW, ..} x all column tiles ----
@@ -229,7 +238,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
                 const int d = dbase + g4 + r;
                 S[m][ct][r] = a.S_in ? a.S_in[(size_t(bh) * DK + d) * DV + j0 + 16 * ct + col] : 0.f;
             }
-            st4(ST + (16 * ct + col) * LK + dbase + g4, S[m][ct]);
+            st4e(ST + (16 * ct + col) * LK + dbase + g4, S[m][ct]);
         }
     prefetch(0);
 
@@ -280,7 +289,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
             }
 #pragma unroll
             for (int e = 0; e < EPT; ++e)
-                if constexpr (!kPick) st(XT, size_t(part * EPT + e) * LC + row, xv[e]);
+                if constexpr (!kPick) sth(XT, size_t(part * EPT + e) * LC + row, xv[e]);
             float yv[Io<E>::per16], bv[YE];
             Io<E>::unpack(ry, yv);   // the first YE are this thread's values
 #pragma unroll
@@ -304,7 +313,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
                 GAM[q] = 1.f - alpha;
                 EB[q] = log2_1m(alpha);   // log2 gamma
             }
-            for (int idx = tid; idx < DS * LC; idx += NT) st(WT, idx, 0.f);
+            for (int idx = tid; idx < DS * LC; idx += NT) sth(WT, idx, 0.f);
             if (c + 1 < a.nchunks) prefetch(c + 1);
         }
         __syncthreads();
@@ -333,7 +342,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * I + g4 + r, jn = 16 * J + col;
                 const float v = isG ? (jn < i ? g[r] : 0.f) : (jn <= i ? g[r] : 0.f);
-                st(isG ? GB : PB, size_t(i) * LC + jn, v);
+                sth(isG ? GB : PB, size_t(i) * LC + jn, v);
                 if (I == J) {
                     if (isG) {
                         const int e = ((I * 16 + g4 + r) * 4 + (col & 3)) * 4 + (col >> 2);
@@ -354,7 +363,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
                 const bf16x8 av = *reinterpret_cast<const bf16x8 *>(XB + (16 * m + col) * LK + 32 * (n >> 1) + k8);
                 const f32x4 tb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, IDT[n & 1][lane], f32x4{0.f, 0.f, 0.f, 0.f},
                                                                          0, 0, 0);
-                st4(XT + (16 * n + col) * LC + 16 * m + g4, tb);
+                st4e(XT + (16 * n + col) * LC + 16 * m + g4, tb);
             }
         }
         // X S and Qh S for token rows 16 tw .. + 15: with eight waves, waves
@@ -372,20 +381,6 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
         }
         __syncthreads();
 
-        // ---- P2b: residuals and the state part of the outputs ----
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * tw + g4 + r, j = 16 * ct + col;
-                if (doX) {
-                    const float ebp = t > 0 ? EB[(t - 1) * RS + j] : 1.f;
-                    SV[j * SVS + t].y -= ebp * xs[ct][r];
-                }
-                if (doQ) OA[t * RS + j] = EB[t * RS + j] * qs[ct][r];
-            }
-        __syncthreads();
-
         // Chunk frame: while every column of the slice keeps e^{b_C} >=
         // 2^-100, the writes are kept as e^{-b_l} u_l (chunk-start frame), so
         // no block rescales the earlier ones and the state update scales once
@@ -394,16 +389,107 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
         // forms the same flag from the chunk prefix.
         const bool cframe = __all(lane >= DS || EB[63 * RS + (lane < DS ? lane : 0)] >= 0x1p-100f);
 
+        // ---- P2b: residuals and the state part of the outputs; in the chunk
+        //      frame also the solve's step coefficients (P3) ----
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * tw + g4 + r, j = 16 * ct + col;
+                if (doX) {
+                    const float ebp = t > 0 ? EB[(t - 1) * RS + j] : 1.f;
+                    float4 *sv = SV + j * SVS + t;
+                    const float4 v = *sv;
+                    const float r0 = v.y - ebp * xs[ct][r];
+                    if (cframe) {
+                        // a_t = eta_t R0_t e^{-b_s} / E_t, c_t = eta_t E_{t-1} / E_t
+                        // (s: the token before t's block)
+                        const int s16 = 16 * (t >> 4) - 1;
+                        const float iebs = s16 >= 0 ? __builtin_amdgcn_rcpf(EB[s16 * RS + j]) : 1.f;
+                        const float re = __builtin_amdgcn_rcpf(v.w);
+                        *reinterpret_cast<float2 *>(sv) = make_float2(v.x * r0 * iebs * re, v.x * v.z * re);
+                    } else {
+                        sv->y = r0;
+                    }
+                }
+                if (doQ) OA[t * RS + j] = EB[t * RS + j] * qs[ct][r];
+            }
+        __syncthreads();
+
         // ---- P3: blocked per-column solve (wave sw: columns 16 sw ..) ----
         if (wave < NCT) {
             const int sw = wave, jj = lane >> 2, q = lane & 3, j = 16 * sw + jj;
             float *H0 = Hs[sw][0], *H1 = Hs[sw][1];
+            const float own[4] = {q == 0 ? 1.f : 0.f, q == 1 ? 1.f : 0.f, q == 2 ? 1.f : 0.f,
+                                  q == 3 ? 1.f : 0.f};
+            // operands of steps i .. i + 3 in flight (a rotating buffer): the
+            // two solving waves run alone on their SIMDs, so nothing else
+            // hides an LDS round trip per step
+            constexpr int PF = 4;
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
-                // e^{b_s} of this lane's column (s: the token before the block)
-                // and its reciprocal, for the chunk frame
-                const float ebs = (cframe && I > 0) ? EB[(16 * I - 1) * RS + j] : 1.f;
-                const float iebs = __builtin_amdgcn_rcpf(ebs);
+                // Running in-block sums: acc[m] of lane q holds sum_{l < t}
+                // G_tl w_l for its position t = 4 m + q over the writes known
+                // so far; once w_i is known, every later position adds G_ti w_i
+                // (G_ti = G_it, row i of the upper part).  With a_i = eta_i
+                // (R0_i e^{-b_s} - E_{i-1} h_i) / E_i and c_i = eta_i E_{i-1} /
+                // E_i (neither depends on the writes of the block)
+                //     w_i = a_i - c_i acc_i,
+                // so a step's dependent chain is the broadcast of acc_i from its
+                // owner lane and two multiply-adds.
+                float w[4] = {0.f, 0.f, 0.f, 0.f};   // w_l = u_l / E_l, l = 4 m + q
+                float acc[4] = {0.f, 0.f, 0.f, 0.f};
+                auto step = [&](int i, float ai, float ci, const float4 &gu) {
+                    const float x = acc[i >> 2];
+                    const float s_i = (i & 3) == 0 ? quad_bcast<0x00>(x) : (i & 3) == 1 ? quad_bcast<0x55>(x)
+                                    : (i & 3) == 2 ? quad_bcast<0xAA>(x) : quad_bcast<0xFF>(x);
+                    const float wi = fmaf(-ci, s_i, ai);
+                    // the owner lane of position i keeps w_i (its entry is
+                    // still zero: a multiply-add by a 0/1 lane mask)
+                    w[i >> 2] = fmaf(own[i & 3], wi, w[i >> 2]);
+                    acc[0] = fmaf(gu.x, wi, acc[0]);
+                    acc[1] = fmaf(gu.y, wi, acc[1]);
+                    acc[2] = fmaf(gu.z, wi, acc[2]);
+                    acc[3] = fmaf(gu.w, wi, acc[3]);
+                };
+                if (cframe) {
+                    // chunk frame (s: the token before the block): P2b stored
+                    // (a_i, c_i) without the cross-block term h = G[block, :] W
+                    // of the earlier blocks, which folds in here once per block
+                    if (I > 0) {
+                        const f32x4 h = Mma<E>::run(f32x4{0.f, 0.f, 0.f, 0.f}, GB + 16 * I * LC, LC,
+                                                    WT + 16 * sw * LC, LC, 0, kend_for<E>(16 * I));
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            float2 *p = reinterpret_cast<float2 *>(SV + (16 * sw + col) * SVS + 16 * I + g4 + r);
+                            const float2 ac = *p;
+                            p->x = fmaf(-ac.y, h[r], ac.x);
+                        }
+                    }
+                    wave_lds_sync();
+                    float2 acb[PF];
+                    float4 gub[PF];
+#pragma unroll
+                    for (int u = 0; u < PF; ++u) {
+                        acb[u] = *reinterpret_cast<const float2 *>(SV + j * SVS + 16 * I + u);
+                        gub[u] = GDu[(I * 16 + u) * 4 + q];
+                    }
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const float2 ac = acb[i % PF];
+                        const float4 gu = gub[i % PF];
+                        if (i + PF < 16) {
+                            acb[i % PF] = *reinterpret_cast<const float2 *>(SV + j * SVS + 16 * I + i + PF);
+                            gub[i % PF] = GDu[(I * 16 + i + PF) * 4 + q];
+                        }
+                        step(i, ac.x, ac.y, gu);
+                    }
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) sth(WT, size_t(j) * LC + 16 * I + 4 * m + q, w[m]);
+                    wave_lds_sync();
+                    continue;
+                }
+                // block frame (s = 16 I - 1): SV holds (eta, R0, E_{t-1}, E_t)
                 if (I > 0) {
                     const f32x4 h = Mma<E>::run(f32x4{0.f, 0.f, 0.f, 0.f}, GB + 16 * I * LC, LC,
                                                 WT + 16 * sw * LC, LC, 0, kend_for<E>(16 * I));
@@ -411,27 +497,8 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
                     for (int r = 0; r < 4; ++r) H0[(g4 + r) * 17 + col] = h[r];
                 }
                 const float fblk = SV[j * SVS + 16 * I + 15].w;   // e^{b_end - b_s}
-                const bool sep = cframe || __all(fblk >= 0x1p-100f);
                 wave_lds_sync();
-                if (sep) {
-                    float w[4] = {0.f, 0.f, 0.f, 0.f};   // w_l = u_l / E_l, l = 4 m + q
-                    const float own[4] = {q == 0 ? 1.f : 0.f, q == 1 ? 1.f : 0.f, q == 2 ? 1.f : 0.f,
-                                          q == 3 ? 1.f : 0.f};
-                    // Running in-block sums: acc[m] of lane q holds
-                    // sum_{l < t} G_tl w_l for its position t = 4 m + q over the
-                    // writes known so far; once w_i is known, every later
-                    // position adds G_ti w_i (G_ti = G_it, row i of the upper
-                    // part).  With a_i = eta_i (y_i - E_{i-1} h_i) / E_i and
-                    // c_i = eta_i E_{i-1} / E_i (neither depends on the writes)
-                    //     w_i = a_i - c_i acc_i,
-                    // so a step's dependent chain is the broadcast of acc_i from
-                    // its owner lane and two multiply-adds.  Operands of step
-                    // i + 1 are loaded while step i computes.
-                    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-                    // operands of steps i .. i + 3 in flight (a rotating
-                    // buffer): the two solving waves run alone on their SIMDs,
-                    // so nothing else hides an LDS round trip per step
-                    constexpr int PF = 4;
+                if (__all(fblk >= 0x1p-100f)) {
                     float4 svb[PF], gub[PF];
                     float hb[PF];
 #pragma unroll
@@ -450,26 +517,13 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
                             if (I > 0) hb[i % PF] = H0[(i + PF) * 17 + jj];
                         }
                         const float re = __builtin_amdgcn_rcpf(sv.w);
-                        const float ai = sv.x * fmaf(sv.y, iebs, -sv.z * h) * re, ci = sv.x * sv.z * re;
-                        const float x = acc[i >> 2];
-                        const float s_i = (i & 3) == 0 ? quad_bcast<0x00>(x) : (i & 3) == 1 ? quad_bcast<0x55>(x)
-                                        : (i & 3) == 2 ? quad_bcast<0xAA>(x) : quad_bcast<0xFF>(x);
-                        const float wi = fmaf(-ci, s_i, ai);
-                        // the owner lane of position i keeps w_i (its entry is
-                        // still zero: a multiply-add by a 0/1 lane mask)
-                        w[i >> 2] = fmaf(own[i & 3], wi, w[i >> 2]);
-                        acc[0] = fmaf(gu.x, wi, acc[0]);
-                        acc[1] = fmaf(gu.y, wi, acc[1]);
-                        acc[2] = fmaf(gu.z, wi, acc[2]);
-                        acc[3] = fmaf(gu.w, wi, acc[3]);
+                        step(i, sv.x * (sv.y - sv.z * h) * re, sv.x * sv.z * re, gu);
                     }
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) st(WT, size_t(j) * LC + 16 * I + 4 * m + q, w[m]);
+                    for (int m = 0; m < 4; ++m) sth(WT, size_t(j) * LC + 16 * I + 4 * m + q, w[m]);
                     wave_lds_sync();
-                    // outputs of the block: o_t = OA_t + E_t (P0 [W; w])_t, as O^T
-                    // tiles (in the chunk frame every wave forms them after the
-                    // solve, beside the state update)
-                    if (!cframe) {
+                    // outputs of the block: o_t = OA_t + E_t (P0 [W; w])_t, as O^T tiles
+                    {
                         const f32x4 o = Mma<E>::run(f32x4{0.f, 0.f, 0.f, 0.f}, WT + 16 * sw * LC, LC,
                                                     PB + 16 * I * LC, LC, 0, kend_for<E>(16 * I + 16));
                         const int t = 16 * I + col;
@@ -484,7 +538,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
                     // rescale W to the block end: the quad of column j takes the
                     // row's 4-element pieces, lane q pieces q, q + 4, .. (every
                     // load before the first store)
-                    if (!cframe) {
+                    {
                         E *wrow = WT + size_t(j) * LC;
                         f32x4 pc[4];
 #pragma unroll
@@ -533,15 +587,15 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
                         if (q == 0 && c0 + t < T) {
                             float o = OA[t * RS + j] + oin;
                             if (I > 0) o += pb * H1[i * 17 + jj];
-                            st(og, size_t(c0 + t) * DV + j0 + j, o);
+                            sth(og, size_t(c0 + t) * DV + j0 + j, o);
                         }
                     }
                     for (int l = q; l < 16 * I; l += 4) {
                         const size_t p = size_t(j) * LC + l;
-                        st(WT, p, pb * ld(WT, p));
+                        sth(WT, p, pb * ld(WT, p));
                     }
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) st(WT, size_t(j) * LC + 16 * I + 4 * m + q, v[m]);
+                    for (int m = 0; m < 4; ++m) sth(WT, size_t(j) * LC + 16 * I + 4 * m + q, v[m]);
                     wave_lds_sync();
                 }
             }
@@ -563,7 +617,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
                     for (int r = 0; r < 4; ++r) S[m][ct][r] *= gC;
                     S[m][ct] = Mma<E>::run(S[m][ct], XT + dbase * LC, LC, WT + 16 * ct * LC, LC, 0, C);
                 }
-                st4(ST + (16 * ct + col) * LK + dbase + g4, S[m][ct]);
+                st4e(ST + (16 * ct + col) * LK + dbase + g4, S[m][ct]);
             }
         // ---- P3b (chunk frame): the outputs of every block at once,
         //      o_t = OA_t + e^{b_t} (P0 W)_t with W = e^{-b_l} u_l, one O^T tile
