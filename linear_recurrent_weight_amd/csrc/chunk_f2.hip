@@ -33,9 +33,11 @@
 // block positions l = q (mod 4); the in-block sums are quad sums (DPP).
 // One workgroup owns one (head, DS value columns); the raw rows of the next
 // chunk are prefetched while a chunk is processed.  It has four waves, or
-// eight for bf16 with d_k = 128 and 32 columns (one workgroup fills a CU's
-// LDS there, and the second four waves share the features, step scalars,
+// eight for bf16 with d_k = 128 and 32 columns (only one such workgroup fits
+// a CU's LDS, and the second four waves share the features, step scalars,
 // Gram, scores, X S and Qh S); the solve runs on the first DS / 16 waves.
+// X^T is never stored: the state update reads its operand down the columns
+// of the x rows.
 #include "chunk_layout.h"
 #include "kernels.h"
 #include "mma.h"
@@ -54,6 +56,23 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
 }
 __device__ __forceinline__ void sth(bf16_t *p, size_t i, float v) { p[i].bits = __builtin_bit_cast(uint16_t, (__bf16)v); }
 __device__ __forceinline__ void sth(float *p, size_t i, float v) { p[i] = v; }
+
+// One k step of an MFMA A operand A[m][k] = M[k][m] held down the columns
+// of a row-major [k][m] tile (row stride ld): lane (m = lane % 16, k group)
+// gathers its 8 (bf16) or 1 (fp32) values of k = k0 + ..
+__device__ __forceinline__ bf16x8 col_frag(const bf16_t *M, int ld, int k0) {
+    const int lane = threadIdx.x & 63;
+    const bf16_t *p = M + (k0 + 8 * (lane >> 4)) * ld + (lane & 15);
+    typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+    u16x8 u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u[e] = p[e * ld].bits;
+    return __builtin_bit_cast(bf16x8, u);
+}
+__device__ __forceinline__ float col_frag(const float *M, int ld, int k0) {
+    const int lane = threadIdx.x & 63;
+    return M[(k0 + (lane >> 4)) * ld + (lane & 15)];
+}
 
 // 16-byte vectors <-> floats for the io type
 template <class E> struct Io;
@@ -148,7 +167,6 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
 
     __shared__ __align__(16) E XB[C * LK];     // x rows
     __shared__ __align__(16) E QB[C * LK];     // qh rows
-    __shared__ __align__(16) E XT[DK * LC];    // x^T [d][t]
     __shared__ __align__(16) E GB[C * LC];     // Gram, strictly lower tiles
     __shared__ __align__(16) E PB[C * LC];     // scores, lower incl. diagonal
     __shared__ float4 GDq[4 * 16 * 4];         // diagonal Gram blocks (fp32): [blk][i][q] = G_{i, 4m+q}, m = 0..3
@@ -161,10 +179,6 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
     __shared__ float EB[C * RS];               // log2 gamma, then e^{b_t}
     __shared__ float OA[C * RS];               // e^{b_t} (Qh S_0)_t
     __shared__ float Hs[NCT][2][16 * 17];      // per solve wave: cross sums
-    // bf16: 0/1 B operands that pick 16 columns (half h) of a 32-wide block,
-    // for the MFMA transposes of x into XT
-    constexpr bool kPick = sizeof(E) == 2;
-    __shared__ __align__(16) bf16x8 IDT[kPick ? 2 : 1][64];
 
     const int id = blockIdx.x, u8 = id & 7, rest = id >> 3;
     const int s = rest % nslice;
@@ -209,16 +223,6 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
         rlam = lamg[tq];
     };
 
-    if constexpr (kPick) {
-        if (tid < 128) {
-            typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
-            const int h = tid >> 6, k8 = 8 * (lane >> 4);
-            u16x8 u;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) u[e] = (k8 + e == 16 * h + col) ? 0x3F80 : 0;   // bf16 1.0
-            IDT[h][lane] = __builtin_bit_cast(bf16x8, u);
-        }
-    }
     // the tiles above the diagonal are never written but are read (times
     // zero) by the bf16 MFMA k steps of 32: they must hold zeros, not NaNs
     for (int idx = tid; idx < C * LC; idx += NT) {
@@ -287,9 +291,6 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
                 *reinterpret_cast<uint4 *>(QB + row * LK + part * EPT + v * Io<E>::per16) =
                     Io<E>::pack(qv + v * Io<E>::per16);
             }
-#pragma unroll
-            for (int e = 0; e < EPT; ++e)
-                if constexpr (!kPick) sth(XT, size_t(part * EPT + e) * LC + row, xv[e]);
             float yv[Io<E>::per16], bv[YE];
             Io<E>::unpack(ry, yv);   // the first YE are this thread's values
 #pragma unroll
@@ -351,19 +352,6 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
                     }
                     else PD4[I * 272 + (g4 + r) * 17 + col] = v;
                 }
-            }
-        }
-        // bf16: x^T into XT from the rows, 16 x 16 blocks (token tile m, d tile
-        // n) on MFMA with a column picker; lane holds tokens 16 m + g4 .. + 3
-        // of d = 16 n + col and stores them as 8 bytes (2-byte transposed
-        // stores from the row threads conflict in the LDS banks)
-        if constexpr (kPick) {
-            for (int b = wave; b < 4 * (DK / 16); b += NW) {
-                const int m = b & 3, n = b >> 2, k8 = 8 * (lane >> 4);
-                const bf16x8 av = *reinterpret_cast<const bf16x8 *>(XB + (16 * m + col) * LK + 32 * (n >> 1) + k8);
-                const f32x4 tb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, IDT[n & 1][lane], f32x4{0.f, 0.f, 0.f, 0.f},
-                                                                         0, 0, 0);
-                st4e(XT + (16 * n + col) * LC + 16 * m + g4, tb);
             }
         }
         // X S and Qh S for token rows 16 tw .. + 15: with eight waves, waves
@@ -603,22 +591,32 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
         __syncthreads();
 
         // ---- P4: S = e^{b_C} S + X^T W (W = writes rescaled to the chunk end),
-        //      or in the chunk frame S = e^{b_C} (S + X^T W) ----
+        //      or in the chunk frame S = e^{b_C} (S + X^T W); the X^T operand
+        //      is read down the columns of the x rows, once per k step for
+        //      all column tiles ----
 #pragma unroll
-        for (int m = 0; m < NDT; ++m)
+        for (int m = 0; m < NDT; ++m) {
+            const int dbase = 16 * (wave + NW * m);
+            f32x4 acc[NCT];
+            float gC[NCT];
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                const int dbase = 16 * (wave + NW * m);
-                const float gC = EB[63 * RS + 16 * ct + col];
-                if (cframe) {
-                    S[m][ct] = Mma<E>::run(S[m][ct], XT + dbase * LC, LC, WT + 16 * ct * LC, LC, 0, C) * gC;
-                } else {
+                gC[ct] = EB[63 * RS + 16 * ct + col];
+                acc[ct] = cframe ? S[m][ct] : S[m][ct] * gC[ct];
+            }
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) S[m][ct][r] *= gC;
-                    S[m][ct] = Mma<E>::run(S[m][ct], XT + dbase * LC, LC, WT + 16 * ct * LC, LC, 0, C);
-                }
+            for (int k0 = 0; k0 < C; k0 += MmaFrag<E>::KS) {
+                const auto xa = col_frag(XB + dbase, LK, k0);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+                    acc[ct] = MmaFrag<E>::mma(xa, MmaFrag<E>::load(WT + 16 * ct * LC, LC, k0), acc[ct]);
+            }
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                S[m][ct] = cframe ? acc[ct] * gC[ct] : acc[ct];
                 st4e(ST + (16 * ct + col) * LK + dbase + g4, S[m][ct]);
             }
+        }
         // ---- P3b (chunk frame): the outputs of every block at once,
         //      o_t = OA_t + e^{b_t} (P0 W)_t with W = e^{-b_l} u_l, one O^T tile
         //      (columns 16 ct .., tokens 16 I ..) per wave ----
