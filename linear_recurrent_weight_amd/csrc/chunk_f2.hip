@@ -320,37 +320,47 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
         __syncthreads();
 
         // ---- P2a: per-column prefixes; Gram, scores, XS, Qh S on MFMA ----
+        // Gram G = X X^T (strictly lower) and scores P0 = Qh X^T (lower with
+        // the diagonal), one tile pair (I, J), J <= I, per job: the two share
+        // the x rows of block J as their B operand
+        for (int job = wave; job < 10; job += NW) {
+            const int I = (0xffa94 >> (2 * job)) & 3, J = (0xe4910 >> (2 * job)) & 3;
+            f32x4 g = {0.f, 0.f, 0.f, 0.f}, p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int n = 0; n < DS / NW; ++n) {
-            const int j = wave + NW * n;   // lane = token
-            const float lg = EB[lane * RS + j];
-            EB[lane * RS + j] = __builtin_amdgcn_exp2f(wave_inclusive_scan(lg));
-            const float el = __builtin_amdgcn_exp2f(row_scan(lg));   // block-local E_t
-            SV[j * SVS + lane].w = el;
-            if ((lane & 15) == 0) SV[j * SVS + lane].z = 1.f;
-            if ((lane & 15) != 15) SV[j * SVS + lane + 1].z = el;
-        }
-#pragma unroll
-        for (int m = 0; m < (20 + NW - 1) / NW; ++m) {
-            const int job = wave + NW * m;   // 0-9 Gram tiles, 10-19 score tiles
-            if (job >= 20) break;
-            const bool isG = job < 10;
-            const int tt = isG ? job : job - 10;
-            const int I = (0xffa94 >> (2 * tt)) & 3, J = (0xe4910 >> (2 * tt)) & 3;
-            const f32x4 g = Mma<E>::run(f32x4{0.f, 0.f, 0.f, 0.f}, (isG ? XB : QB) + 16 * I * LK, LK,
-                                        XB + 16 * J * LK, LK, 0, DK);
+            for (int k0 = 0; k0 < DK; k0 += MmaFrag<E>::KS) {
+                const auto xj = MmaFrag<E>::load(XB + 16 * J * LK, LK, k0);
+                g = MmaFrag<E>::mma(MmaFrag<E>::load(XB + 16 * I * LK, LK, k0), xj, g);
+                p = MmaFrag<E>::mma(MmaFrag<E>::load(QB + 16 * I * LK, LK, k0), xj, p);
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * I + g4 + r, jn = 16 * J + col;
-                const float v = isG ? (jn < i ? g[r] : 0.f) : (jn <= i ? g[r] : 0.f);
-                sth(isG ? GB : PB, size_t(i) * LC + jn, v);
+                const float gv = jn < i ? g[r] : 0.f, pv = jn <= i ? p[r] : 0.f;
+                sth(GB, size_t(i) * LC + jn, gv);
+                sth(PB, size_t(i) * LC + jn, pv);
                 if (I == J) {
-                    if (isG) {
-                        const int e = ((I * 16 + g4 + r) * 4 + (col & 3)) * 4 + (col >> 2);
-                        reinterpret_cast<float *>(GDq)[e] = v;
-                        reinterpret_cast<float *>(GDu)[e] = jn > i ? g[r] : 0.f;   // the block is symmetric
-                    }
-                    else PD4[I * 272 + (g4 + r) * 17 + col] = v;
+                    const int e = ((I * 16 + g4 + r) * 4 + (col & 3)) * 4 + (col >> 2);
+                    reinterpret_cast<float *>(GDq)[e] = gv;
+                    reinterpret_cast<float *>(GDu)[e] = jn > i ? g[r] : 0.f;   // the block is symmetric
+                    PD4[I * 272 + (g4 + r) * 17 + col] = pv;
+                }
+            }
+        }
+        // per-column prefixes (lane = token); with eight waves the six that
+        // take one tile pair form them
+        {
+            constexpr int PW0 = NW == 8 ? 10 - NW : 0, NPW = NW - PW0;
+            if (wave >= PW0) {
+#pragma unroll
+                for (int n = 0; n < (DS + NPW - 1) / NPW; ++n) {
+                    const int j = wave - PW0 + NPW * n;
+                    if (j >= DS) break;
+                    const float lg = EB[lane * RS + j];
+                    EB[lane * RS + j] = __builtin_amdgcn_exp2f(wave_inclusive_scan(lg));
+                    const float el = __builtin_amdgcn_exp2f(row_scan(lg));   // block-local E_t
+                    SV[j * SVS + lane].w = el;
+                    if ((lane & 15) == 0) SV[j * SVS + lane].z = 1.f;
+                    if ((lane & 15) != 15) SV[j * SVS + lane + 1].z = el;
                 }
             }
         }
