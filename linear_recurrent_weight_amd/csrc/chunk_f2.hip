@@ -368,14 +368,24 @@ __global__ __launch_bounds__(64 * NW) void chunk_f2(ChunkF2Args a, int nslice) {
         // 0-3 take X S and waves 4-7 Qh S
         const int tw = wave & 3;
         const bool doX = NW == 4 || wave < 4, doQ = NW == 4 || wave >= 4;
+        // (the token rows are read once per k step for every column tile)
         f32x4 xs[NCT], qs[NCT];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            xs[ct] = z;
-            qs[ct] = z;
-            if (doX) xs[ct] = Mma<E>::run(z, XB + 16 * tw * LK, LK, ST + 16 * ct * LK, LK, 0, DK);
-            if (doQ) qs[ct] = Mma<E>::run(z, QB + 16 * tw * LK, LK, ST + 16 * ct * LK, LK, 0, DK);
+            xs[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+            qs[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int k0 = 0; k0 < DK; k0 += MmaFrag<E>::KS) {
+            typename MmaFrag<E>::T ax{}, aq{};
+            if (doX) ax = MmaFrag<E>::load(XB + 16 * tw * LK, LK, k0);
+            if (doQ) aq = MmaFrag<E>::load(QB + 16 * tw * LK, LK, k0);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const auto sb = MmaFrag<E>::load(ST + 16 * ct * LK, LK, k0);
+                if (doX) xs[ct] = MmaFrag<E>::mma(ax, sb, xs[ct]);
+                if (doQ) qs[ct] = MmaFrag<E>::mma(aq, sb, qs[ct]);
+            }
         }
         __syncthreads();
 
